@@ -1,0 +1,333 @@
+"""fp64 CPU oracle for the fused decode-MLP path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  It shares no code with the
+HIP library (``memory_bound_decode_add_amd``): no kernels, no helpers, no constants,
+no pre- or post-processing.  Inputs come from the seeded generators in ``synth``.
+
+Everything is computed in float64 from the same bf16 bit patterns (``uint16``) and
+packed int4 words (``uint32``) the GPU reads.  A bf16 result is produced by rounding
+the float64 value *directly* to bf16 (round to nearest, ties to even), never through
+float32, and only at the points where the GPU path writes a bf16 tensor to memory.
+
+Sources (the pages this follows, cited by title and section):
+
+* [P1] "PyTorch Community Proposes Fusion Fix as Large Intermediate Buffers May Slow
+  Single-Token Decoding in Quantized LLMs" (ainews.surl.tw): the single-row matmul
+  that Inductor turns into a broadcast multiply plus a sum, the (1, K, N) fp32
+  product it can materialise, and the int4 weight-quantised case with a SwiGLU
+  pre-operation.
+* [P3] "PyTorch folds NVFP4 output scaling into NVGEMM candidates for decode
+  workloads" (ainewsletter.today): a zero-dimensional fp32 output-scale multiplier
+  applied to a matmul result, and the fallback that multiplies separately.
+* [P4] "09 - Operator fusion" (infra.pidoku.co.in), section 5 "Technical
+  explanation": the fusion taxonomy (reduction + elementwise, prologue dequant,
+  horizontal gate_up fusion), the residual's two consumers, and the three-kernel
+  layer (add_rmsnorm -> gate_up GEMM -> down GEMM with residual add).
+* [P5] "Kernel Fusion, torch.compile and CUDA Graphs, Measured" (vidyal.ai):
+  "Step 1" (SwiGLU = g / (1 + exp(-g)) * u; RMSNorm as Qwen2 spells it),
+  "Step 2: fusing them by hand in Triton" (add + RMSNorm with two outputs, h kept in
+  bf16), "Step 3: what torch.compile generates" (the down projection computing
+  silu(g) * u while reading the weights), "Step 4" (graph replay of the layer chain).
+
+Readings where the pages are silent (each is also listed in the design notes):
+
+* int4 words: eight weights per uint32 along K, weight k = 8*kb + j in bits
+  [4j, 4j+4), two's-complement nibbles (values -8..7), qweight [K/8, N] row-major.
+* scales: bf16 [K/128, N], group g covering k in [128 g, 128 g + 128).
+* act = silu(g) * u is never rounded on the fused path (it is never written).
+* epilogue: y = bf16(out_scale * acc [+ residual]) with a single rounding.
+* RMSNorm: h = bf16(x + r); mean of h^2 over H; eps inside the square root; one final
+  rounding of h * w / sqrt(ms + eps).
+* Multi-layer chain: each layer's add_rmsnorm adds the previous layer's down output
+  into the residual (the residual add deferred to the next layer's norm).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "GROUP", "bf16_to_f64", "f64_to_bf16", "round_bf16", "w4_unpack", "w4_dequant",
+    "silu", "silu_mul", "swiglu_w4_gemv", "w4_gemv", "add_rmsnorm", "mlp_decode",
+    "mlp_chain", "product_form_gemv", "factored_form_gemv",
+    "product_buffer_bytes", "unfused_act_gemv", "unfused_product_gemv",
+    "add_rmsnorm_eager", "mlp_decode_unfused",
+]
+
+GROUP = 128   # weights per scale group along K (one scale per group per column)
+NIB = 8       # int4 weights per packed uint32
+
+
+# ----------------------------------------------------------------------------
+# bf16 <-> float64
+# ----------------------------------------------------------------------------
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact): the bf16 pattern is the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):                 # NaN patterns stay NaN
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even), in float64.
+
+    bf16 has an 8-bit significand (7 stored bits) and fp32's exponent range.  For a
+    normal result the spacing of bf16 values around x is 2**(e-8) where x = m * 2**e,
+    0.5 <= |m| < 1; below 2**-126 the spacing is fixed at 2**-133 (subnormals).
+    Dividing by the spacing is exact in float64 (a power of two), and ``np.rint``
+    rounds half to even, so this is one correct rounding of the float64 value.
+    Values beyond the largest finite bf16 round to +-inf (as fp32 casting does).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e - 8, -133).astype(np.float64)
+    step = np.exp2(q)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = np.rint(x / step) * step
+    y = np.where(np.isfinite(x), y, x)
+    return y
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    """float64 -> bf16 bit patterns (uint16), one round-to-nearest-even step."""
+    y = round_bf16(x)
+    with np.errstate(over="ignore"):
+        f = y.astype(np.float32)                      # exact: y is a bf16 value (or +-inf)
+    bits = (np.ascontiguousarray(f).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(y)
+    if np.any(nan):
+        bits = np.where(nan, np.uint16(0x7FC0), bits)
+    return bits
+
+
+# ----------------------------------------------------------------------------
+# int4 weights  ([P4] section 5, prologue fusion: dequantise weights as they are read)
+# ----------------------------------------------------------------------------
+def w4_unpack(qweight) -> np.ndarray:
+    """Packed words uint32 [K/8, N] -> int8 weights [K, N].
+
+    Weight k = 8*kb + j of column n is nibble j of word (kb, n), a two's-complement
+    4-bit integer: codes 0..7 are 0..7, codes 8..15 are -8..-1.
+    """
+    w = np.asarray(qweight, dtype=np.uint32)
+    kb, n = w.shape
+    out = np.empty((kb, NIB, n), dtype=np.int8)
+    for j in range(NIB):
+        code = ((w >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.int16)
+        out[:, j, :] = np.where(code >= 8, code - 16, code).astype(np.int8)
+    return out.reshape(kb * NIB, n)
+
+
+def w4_dequant(qweight, scales) -> np.ndarray:
+    """Dequantised weights, float64 [K, N]: w[k, n] = q[k, n] * s[k // 128, n].
+
+    The product of a 4-bit integer and a bf16 scale has at most 12 significant bits,
+    so the same number is obtained exactly in fp32 on the GPU.
+    """
+    q = w4_unpack(qweight).astype(np.float64)
+    s = bf16_to_f64(scales)
+    K = q.shape[0]
+    if s.shape[0] * GROUP != K or s.shape[1] != q.shape[1]:
+        raise ValueError("scales must be [K/128, N]")
+    return q * np.repeat(s, GROUP, axis=0)
+
+
+# ----------------------------------------------------------------------------
+# SwiGLU ([P5] Step 1: silu(g) * u = g / (1 + exp(-g)) * u)
+# ----------------------------------------------------------------------------
+def silu(g) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def silu_mul(g, u) -> np.ndarray:
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+def _epilogue(acc, out_scale, residual):
+    """[P3]: the fp32 output scale multiplies the matmul result; [P4] section 5: the
+    residual add may ride in the same epilogue.  One rounding to bf16."""
+    y = acc * (1.0 if out_scale is None else float(out_scale))
+    if residual is not None:
+        y = y + bf16_to_f64(residual)
+    return y
+
+
+def swiglu_w4_gemv(g, u, qweight, scales, out_scale=1.0, residual=None, *, return_f64=False):
+    """y[m, n] = bf16(out_scale * sum_k silu(g[m,k]) u[m,k] w[k,n] (+ residual[m, n])).
+
+    [P1]: the int4 weight-quantised single-row matmul with a SwiGLU pre-operation,
+    computed without materialising the (M, K, N) product; [P5] Step 3: the down
+    projection computes silu(g) * u while reading its weights; [P3]: the output scale
+    is folded into the same result.  The activation is not rounded (it is never
+    written on the fused path).
+    """
+    act = silu_mul(bf16_to_f64(g), bf16_to_f64(u))
+    acc = act @ w4_dequant(qweight, scales)
+    y = _epilogue(acc, out_scale, residual)
+    return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)
+
+
+def w4_gemv(x, qweight, scales, out_scale=None, *, return_f64=False):
+    """The same GEMV with the identity prologue: y = bf16([out_scale *] x @ dequant(W)).
+
+    Used for the horizontally fused gate_up projection ([P4] section 5, horizontal
+    fusion: gate_proj and up_proj as one matmul, gate columns first).
+    """
+    acc = bf16_to_f64(x) @ w4_dequant(qweight, scales)
+    y = _epilogue(acc, out_scale, None)
+    return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)
+
+
+# ----------------------------------------------------------------------------
+# residual add + RMSNorm ([P5] Step 2; [P4] section 5, reduction + elementwise and
+# the two-output rule for the residual's two consumers)
+# ----------------------------------------------------------------------------
+def add_rmsnorm(x, r, w, eps=1e-6, *, return_f64=False):
+    """(h, y): h = bf16(x + r); y = bf16(h * w / sqrt(mean_H(h^2) + eps)).
+
+    h is the new residual, kept in bf16; the mean is over the H columns of each row;
+    eps sits inside the square root; y is rounded once.
+    """
+    hs = round_bf16(bf16_to_f64(x) + bf16_to_f64(r))        # exact sum, then RNE
+    H = hs.shape[-1]
+    ms = np.sum(hs * hs, axis=-1, keepdims=True) / H
+    y = hs * bf16_to_f64(w) / np.sqrt(ms + float(eps))
+    out = (f64_to_bf16(hs), f64_to_bf16(y))
+    return out + (y,) if return_f64 else out
+
+
+# ----------------------------------------------------------------------------
+# the layer and the chain ([P4] section 5, the fusion boundary problem)
+# ----------------------------------------------------------------------------
+def mlp_decode(x, r, norm_w, gu_q, gu_s, d_q, d_s, out_scale=0.5, eps=1e-6,
+               residual_in_epilogue=True, *, n_chunk=4096):
+    """One decode-MLP layer, three kernels' worth of work.
+
+    1. (h, y) = add_rmsnorm(x, r, norm_w)
+    2. gu = bf16(y @ dequant(W_gate_up)); gate = gu[:, :I], up = gu[:, I:]
+    3. out = bf16(out_scale * silu(gate) * up @ dequant(W_down) [+ h])
+
+    With ``residual_in_epilogue`` the layer's residual add rides in step 3's epilogue
+    (the new residual is h + MLP output); otherwise step 3 writes only the scaled MLP
+    output and the caller adds it into the residual at the next layer's step 1.
+    Dequantisation is done in column chunks of ``n_chunk`` to bound memory.
+    """
+    h, y = add_rmsnorm(x, r, norm_w, eps)
+    gu = _chunked_gemv(bf16_to_f64(y), gu_q, gu_s, n_chunk)
+    gu_b = f64_to_bf16(gu)
+    I = gu_b.shape[1] // 2
+    act = silu_mul(bf16_to_f64(gu_b[:, :I]), bf16_to_f64(gu_b[:, I:]))
+    acc = _chunked_gemv(act, d_q, d_s, n_chunk)
+    out = f64_to_bf16(_epilogue(acc, out_scale, h if residual_in_epilogue else None))
+    return {"h": h, "y": y, "gu": gu_b, "out": out}
+
+
+def _chunked_gemv(a, qweight, scales, n_chunk):
+    N = qweight.shape[1]
+    out = np.empty((a.shape[0], N), dtype=np.float64)
+    for c0 in range(0, N, n_chunk):
+        c1 = min(N, c0 + n_chunk)
+        out[:, c0:c1] = a @ w4_dequant(qweight[:, c0:c1], scales[:, c0:c1])
+    return out
+
+
+def mlp_chain(x0, r0, layers, *, keep=False):
+    """The multi-layer MLP path with the residual add deferred to the next norm.
+
+    For each layer l: (r_{l+1}, y_l) = add_rmsnorm(x_l, r_l); gu_l = bf16(y_l @ W_gu);
+    x_{l+1} = bf16(s_l * silu(g_l) u_l @ W_d).  ``layers`` holds objects with fields
+    ``norm_w, gate_up.qweight, gate_up.scales, down.qweight, down.scales, out_scale,
+    eps``.  Returns (x_L, r_L[, per-layer dicts]).
+    """
+    x, r = x0, r0
+    trace = []
+    for L in layers:
+        d = mlp_decode(x, r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
+                       L.down.qweight, L.down.scales, L.out_scale, L.eps,
+                       residual_in_epilogue=False)
+        if keep:
+            trace.append(d)
+        x, r = d["out"], d["h"]
+    return (x, r, trace) if keep else (x, r)
+
+
+# ----------------------------------------------------------------------------
+# the unfused definitions (self-checks, and references for the unfused GPU sequence)
+# ----------------------------------------------------------------------------
+def product_buffer_bytes(M, K, N) -> int:
+    """Size of the fp32 (M, K, N) broadcast product the unfused form writes ([P1])."""
+    return int(np.empty((0,), dtype=np.float32).itemsize) * int(M) * int(K) * int(N)
+
+
+def product_form_gemv(g, u, qweight, scales, out_scale=1.0, residual=None):
+    """[P1]'s decomposition: P[m, k, n] = act[m, k] * w[k, n] materialised, then summed
+    over k.  Returns the float64 pre-rounding output (for small shapes only)."""
+    act = silu_mul(bf16_to_f64(g), bf16_to_f64(u))
+    W = w4_dequant(qweight, scales)
+    P = act[:, :, None] * W[None, :, :]
+    return _epilogue(P.sum(axis=1), out_scale, residual)
+
+
+def factored_form_gemv(g, u, qweight, scales, out_scale=1.0, residual=None):
+    """Scale factored out of each 128-wide group: sum_g s[g,n] * sum_{k in g} act * q."""
+    act = silu_mul(bf16_to_f64(g), bf16_to_f64(u))
+    q = w4_unpack(qweight).astype(np.float64)
+    s = bf16_to_f64(scales)
+    M, K = act.shape
+    acc = np.zeros((M, q.shape[1]))
+    for gi in range(K // GROUP):
+        ks = slice(gi * GROUP, (gi + 1) * GROUP)
+        acc += s[gi][None, :] * (act[:, ks] @ q[ks, :])
+    return _epilogue(acc, out_scale, residual)
+
+
+def unfused_act_gemv(g, u, qweight, scales, out_scale=1.0, residual=None):
+    """The eager op-by-op sequence with its bf16 round trips ([P5] Step 1, eager SwiGLU
+    as two kernels; [P3] the separate scaling launch; [P4] the separate residual add).
+
+    s1 = bf16(silu(g)); act = bf16(s1 * u); z = bf16(act @ W); y = bf16(out_scale * z);
+    y = bf16(y + residual) if a residual is given.
+    """
+    s1 = round_bf16(silu(bf16_to_f64(g)))
+    act = round_bf16(s1 * bf16_to_f64(u))
+    z = round_bf16(act @ w4_dequant(qweight, scales))
+    y = round_bf16(z * (1.0 if out_scale is None else float(out_scale)))
+    if residual is not None:
+        y = round_bf16(y + bf16_to_f64(residual))
+    return f64_to_bf16(y)
+
+
+def unfused_product_gemv(g, u, qweight, scales, out_scale=1.0):
+    """[P1]'s materialised-product sequence, M = 1: the fp32 product is summed over k
+    and written as bf16, then a separate launch applies the output scale.  The sum is
+    exact here (float64), which the fp32 GPU reduction approximates."""
+    z = round_bf16(silu_mul(bf16_to_f64(g), bf16_to_f64(u)) @ w4_dequant(qweight, scales))
+    return f64_to_bf16(z * (1.0 if out_scale is None else float(out_scale)))
+
+
+def add_rmsnorm_eager(x, r, w, eps=1e-6):
+    """RMSNorm as the Qwen2 model code spells it after the residual add ([P5] Step 1):
+    h = bf16(x + r); rstd = 1/sqrt(mean(h^2) + eps); y = bf16(bf16(h * rstd) * w)."""
+    hs = round_bf16(bf16_to_f64(x) + bf16_to_f64(r))
+    ms = np.mean(hs * hs, axis=-1, keepdims=True)
+    t = round_bf16(hs / np.sqrt(ms + float(eps)))
+    y = round_bf16(t * bf16_to_f64(w))
+    return f64_to_bf16(hs), f64_to_bf16(y)
+
+
+def mlp_decode_unfused(x, r, norm_w, gu_q, gu_s, d_q, d_s, out_scale=0.5, eps=1e-6,
+                       residual_in_epilogue=True, *, n_chunk=4096):
+    """The layer as the unfused sequence computes it: eager norm, gate_up GEMV, eager
+    SwiGLU (two bf16 round trips), down GEMV, separate scale, separate residual add."""
+    h, y = add_rmsnorm_eager(x, r, norm_w, eps)
+    gu_b = f64_to_bf16(_chunked_gemv(bf16_to_f64(y), gu_q, gu_s, n_chunk))
+    I = gu_b.shape[1] // 2
+    s1 = round_bf16(silu(bf16_to_f64(gu_b[:, :I])))
+    act = round_bf16(s1 * bf16_to_f64(gu_b[:, I:]))
+    z = round_bf16(_chunked_gemv(act, d_q, d_s, n_chunk))
+    o = round_bf16(z * float(out_scale))
+    if residual_in_epilogue:
+        o = round_bf16(o + bf16_to_f64(h))
+    return {"h": h, "y": y, "gu": gu_b, "out": f64_to_bf16(o)}
