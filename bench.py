@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused decode-MLP path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only gemv|all] [--cpu-seconds S]
+
+A step is one call of the SwiGLU-prologue int4 GEMV at M=1, K=9216, N=2560 (the
+single-row decode shape whose unfused form writes a 94 MB fp32 product), with its
+fp32 output scale, over one of S rotating sets of seeded synthetic inputs already
+resident in HBM.  The sets total more than twice the 256 MB Infinity Cache, so every
+step streams its weights from HBM.  K steps are captured into hipGraphs (one per
+rotation of the sets) and timed with HIP events on the stream they run on.
+
+The JSON line on stdout reports achieved algorithmic GB/s (the job's bytes over the
+time) and its fraction of MI355X's 8 TB/s HBM peak, the fp64 CPU oracle timed on this
+host on a bounded sample, and, unless --only gemv, the other workloads: residual add +
+RMSNorm at 8192 x 4096, the 16-row Llama-3-8B-sized MLP layer, the 28-layer
+Qwen2.5-1.5B-sized MLP chain (eager and as one hipGraph), the unfused sequences and a
+plain copy kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call + achieved HBM GB/s (% of peak), SwiGLU→W4 GEMV M=1 K=9216 N=2560"
+PEAK_GBPS = 8000.0
+WORKLOAD = "swiglu_w4_gemv_1x9216x2560"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_w4_gemv_1x9216x2560.json")
+KERNEL_SOURCES = ["memory_bound_decode_add_amd/csrc/w4_gemv.hip", "memory_bound_decode_add_amd/csrc/device_common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events recorded on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, reps=1):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        t.cuda.synchronize()
+        return s.elapsed_time(e) / 1e3     # seconds
+
+
+def capture(torch, fns):
+    """Capture a list of launch callables into one CUDA(HIP) graph."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for f in fns:
+                f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+# ----------------------------------------------------------------------------
+# the metric: SwiGLU-prologue W4 GEMV, M=1 K=9216 N=2560
+# ----------------------------------------------------------------------------
+def bench_gemv(torch, F, synth, steps, warmup, n_sets):
+    from memory_bound_decode_add_amd import traffic as T
+    c = synth.CONFIGS[WORKLOAD]
+    M, K, N = c["M"], c["K"], c["N"]
+    log(f"[bench] generating {n_sets} input sets for M={M} K={K} N={N}")
+    sets = []
+    for i in range(n_sets):
+        inp = synth.swiglu_gemv_inputs(M, K, N, seed=i, out_scale=c["out_scale"])
+        sets.append((F.from_bits(inp.g), F.from_bits(inp.u), F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales),
+                     torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    scale = F.scalar(c["out_scale"])
+    ws = F.workspace(F.gemv_workspace_bytes(M, K, N))
+    bytes_per_call = T.swiglu_w4_gemv_bytes(M, K, N)
+
+    def step(i):
+        g, u, W, y = sets[i % n_sets]
+        return lambda: F.swiglu_w4_gemv(g, u, W, scale, None, out=y, ws=ws)
+
+    # graphs: one per rotation of the sets, plus a remainder
+    R = min(steps, n_sets)
+    g_main = capture(torch, [step(i) for i in range(R)])
+    rem = steps % R
+    g_rem = capture(torch, [step(i) for i in range(rem)]) if rem else None
+    # warmup: at least `warmup` steps, and every graph replayed once (uploads it)
+    done = 0
+    while done < max(warmup, 1):
+        g_main.replay()
+        done += R
+    if g_rem is not None:
+        g_rem.replay()
+        done += rem
+    torch.cuda.synchronize()
+
+    timer = Timer(torch)
+
+    def timed():
+        for _ in range(steps // R):
+            g_main.replay()
+        if g_rem is not None:
+            g_rem.replay()
+
+    elapsed = timer(timed)
+    us = elapsed / steps * 1e6
+    gbps = bytes_per_call / (elapsed / steps) / 1e9
+
+    # single eagerly launched call (launch latency included), median of 20
+    lat = []
+    g, u, W, y = sets[0]
+    for _ in range(20):
+        lat.append(timer(lambda: F.swiglu_w4_gemv(g, u, W, scale, None, out=y, ws=ws)))
+    plan = {"workspace_bytes": F.gemv_workspace_bytes(M, K, N)}
+    return {"us_per_call": us, "gbps": gbps, "elapsed_s": elapsed, "bytes_per_call": bytes_per_call,
+            "warmup_steps_run": done, "graph_steps": R, "eager_call_us_median": float(np.median(lat)) * 1e6,
+            **plan}
+
+
+def bench_repeat(torch, timer, fns, n_rep):
+    """Time n_rep replays of a graph of the given launches; seconds per launch list."""
+    g = capture(torch, fns)
+    g.replay()
+    torch.cuda.synchronize()
+    return timer(g.replay, n_rep) / n_rep
+
+
+def bench_extras(torch, F, synth, n_sets_gemv):
+    from memory_bound_decode_add_amd import traffic as T
+    timer = Timer(torch)
+    out = {}
+
+    # a plain copy kernel (torch's elementwise negation: n*4 bytes in, n*4 out), size-matched
+    # to the GEMV's and the norm's traffic, rotating over >= 600 MB of buffers
+    for mb in (12.2, 268.4):
+        n = int(mb * 1e6 / 8)
+        sets = [(torch.randn(n, device="cuda"), torch.empty(n, device="cuda")) for _ in range(max(2, int(600 / mb)))]
+        t = bench_repeat(torch, timer, [lambda s=s: torch.neg(s[0], out=s[1]) for s in sets], 5) / len(sets)
+        out[f"copy_{mb}MB_total"] = {"us": t * 1e6, "gbps_rw": 2 * n * 4 / t / 1e9}
+        del sets
+
+    # residual add + RMSNorm, 8192 x 4096, 4 rotating sets (1.07 GB)
+    c = synth.CONFIGS["add_rmsnorm_8192x4096"]
+    M, H = c["M"], c["H"]
+    log("[bench] add_rmsnorm 8192x4096")
+    sets = []
+    for i in range(4):
+        inp = synth.add_rmsnorm_inputs(M, H, seed=i)
+        sets.append((F.from_bits(inp.x), F.from_bits(inp.r), F.from_bits(inp.w),
+                     torch.empty((M, H), dtype=torch.bfloat16, device="cuda"),
+                     torch.empty((M, H), dtype=torch.bfloat16, device="cuda")))
+    fns = [lambda s=s: F.add_rmsnorm(s[0], s[1], s[2], c["eps"], h_out=s[3], y_out=s[4]) for s in sets]
+    t = bench_repeat(torch, timer, fns, 10) / len(sets)
+    b = T.add_rmsnorm_bytes(M, H)
+    out["add_rmsnorm_8192x4096"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS}
+    wsn = F.workspace(F.unfused_add_rmsnorm_workspace_bytes(M, H))
+    fns = [lambda s=s: F.unfused_add_rmsnorm(s[0], s[1], s[2], c["eps"], h_out=s[3], y_out=s[4], ws=wsn)
+           for s in sets[:2]]
+    t = bench_repeat(torch, timer, fns, 4) / 2
+    out["unfused_add_rmsnorm_8192x4096"] = {"us_per_call": t * 1e6, "kernels": 9,
+                                            "gbps_actual_bytes": T.add_rmsnorm_eager_bytes(M, H) / t / 1e9}
+    del sets, wsn
+
+    # unfused sequences at the metric shape
+    c = synth.CONFIGS[WORKLOAD]
+    Mg, K, N = c["M"], c["K"], c["N"]
+    log("[bench] unfused GEMV sequences")
+    gsets = []
+    for i in range(min(n_sets_gemv, 48)):
+        inp = synth.swiglu_gemv_inputs(Mg, K, N, seed=i, out_scale=c["out_scale"])
+        gsets.append((F.from_bits(inp.g), F.from_bits(inp.u), F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales),
+                      torch.empty((Mg, N), dtype=torch.bfloat16, device="cuda")))
+    scale = F.scalar(c["out_scale"])
+    for mode, name in ((F.UNFUSED_PRODUCT, "product"), (F.UNFUSED_ACT, "act")):
+        wsu = F.workspace(F.unfused_gemv_workspace_bytes(mode, Mg, K, N))
+        fns = [lambda s=s, wsu=wsu, mode=mode: F.unfused_swiglu_w4_gemv(mode, s[0], s[1], s[2], scale, out=s[3],
+                                                                          ws=wsu) for s in gsets]
+        t = bench_repeat(torch, timer, fns, 2) / len(gsets)
+        ab = T.unfused_product_gemv_bytes(K, N) if mode == F.UNFUSED_PRODUCT else T.unfused_act_gemv_bytes(Mg, K, N)
+        out[f"unfused_{name}_1x9216x2560"] = {"us_per_call": t * 1e6, "gbps_actual_bytes": ab / t / 1e9,
+                                              "workspace_bytes": F.unfused_gemv_workspace_bytes(mode, Mg, K, N)}
+        del wsu
+    del gsets
+
+    # Llama-3-8B-sized MLP layer at M=16, 6 rotating weight sets
+    c = synth.CONFIGS["mlp_llama3_8b_m16"]
+    M, H, I = c["M"], c["H"], c["I"]
+    log("[bench] MLP layer M=16 H=4096 I=14336")
+    layers = []
+    for i in range(6):
+        inp = synth.mlp_inputs(M, H, I, 1, seed=i, out_scale=c["out_scale"])
+        L = inp.layers[0]
+        layers.append(F.MlpLayer(F.from_bits(L.norm_w), F.W4Weight.from_numpy(L.gate_up.qweight, L.gate_up.scales),
+                                 F.W4Weight.from_numpy(L.down.qweight, L.down.scales), F.scalar(L.out_scale),
+                                 L.eps, True))
+    bufs = F.MlpBuffers.empty(M, H, I)
+    bufs.x.copy_(F.from_bits(inp.x))
+    bufs.residual.copy_(F.from_bits(inp.r))
+    wsm = F.workspace(F.mlp_workspace_bytes(M, H, I))
+    t = bench_repeat(torch, timer, [lambda L=L: F.mlp_decode(L, bufs, wsm) for L in layers], 5) / len(layers)
+    b = T.mlp_layer_bytes(M, H, I, True)
+    out["mlp_llama3_8b_m16"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS}
+    wsu = F.workspace(F.unfused_mlp_workspace_bytes(M, H, I))
+    t = bench_repeat(torch, timer, [lambda L=L: F.unfused_mlp_decode(L, bufs, wsu) for L in layers[:2]], 3) / 2
+    out["unfused_mlp_llama3_8b_m16"] = {"us_per_call": t * 1e6}
+    del layers, bufs, wsm, wsu
+
+    # Qwen2.5-1.5B-sized MLP chain, 28 layers: eager chain vs one hipGraph
+    c = synth.CONFIGS["mlp_qwen2_5_1_5b_28l"]
+    M, H, I, NL = c["M"], c["H"], c["I"], c["n_layers"]
+    log("[bench] 28-layer MLP chain M=1 H=1536 I=8960")
+    inp = synth.mlp_inputs(M, H, I, NL, seed=0, out_scale=c["out_scale"])
+    layers = [F.MlpLayer(F.from_bits(L.norm_w), F.W4Weight.from_numpy(L.gate_up.qweight, L.gate_up.scales),
+                         F.W4Weight.from_numpy(L.down.qweight, L.down.scales), F.scalar(L.out_scale), L.eps, False)
+              for L in inp.layers]
+    bufs = F.MlpBuffers.empty(M, H, I, out_is_x=True)
+    x0, r0 = F.from_bits(inp.x), F.from_bits(inp.r)
+    wsc = F.workspace(F.mlp_workspace_bytes(M, H, I))
+    graph = F.MlpGraph(layers, bufs, wsc)
+    b = NL * T.mlp_layer_bytes(M, H, I, False)
+
+    def reset():
+        bufs.x.copy_(x0)
+        bufs.residual.copy_(r0)
+
+    reset()
+    graph.launch()
+    torch.cuda.synchronize()
+    tg = timer(graph.launch, 20) / 20
+    reset()
+    F.mlp_chain(layers, bufs, wsc)
+    torch.cuda.synchronize()
+    te = timer(lambda: F.mlp_chain(layers, bufs, wsc), 20) / 20
+    out["mlp_chain_qwen2_5_1_5b_28l"] = {"graph_us_per_step": tg * 1e6, "eager_us_per_step": te * 1e6,
+                                         "kernels_per_step": graph.kernel_count, "bytes_per_step": b,
+                                         "graph_gbps": b / tg / 1e9, "graph_frac_of_peak": b / tg / 1e9 / PEAK_GBPS}
+    graph.close()
+    return out
+
+
+def cpu_baseline(synth, seconds):
+    """The fp64 oracle on the metric's workload, repeated for about `seconds` of CPU time."""
+    import oracle as O
+    from memory_bound_decode_add_amd import traffic as T
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    c = synth.CONFIGS[WORKLOAD]
+    inp = synth.swiglu_gemv_inputs(c["M"], c["K"], c["N"], seed=0, out_scale=c["out_scale"])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, c["out_scale"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 1000:
+            break
+    b = T.swiglu_w4_gemv_bytes(c["M"], c["K"], c["N"])
+    return {"value": b * n / el / 1e9, "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+            "us_per_call": el / n * 1e6,
+            "sample": f"{n} oracle calls on input set 0 of {WORKLOAD} ({el:.1f} s, numpy fp64; elementwise on 1 "
+                      f"thread, the fp64 matmul on {blas} BLAS threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--sets", type=int, default=48, help="rotating input sets (48 x 12.2 MB = 586 MB)")
+    ap.add_argument("--only", choices=["gemv", "all"], default="all")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if a.steps < 1:
+        sys.exit("--steps must be >= 1")
+
+    import torch
+    import memory_bound_decode_add_amd as F
+    import synth
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    F.lib()   # fail loudly if the HIP library is missing
+
+    res = bench_gemv(torch, F, synth, a.steps, a.warmup, a.sets)
+    log(f"[bench] gemv: {res['us_per_call']:.3f} us/call, {res['gbps']:.1f} GB/s")
+    extras = bench_extras(torch, F, synth, a.sets) if a.only == "all" else {}
+    cpu = cpu_baseline(synth, a.cpu_seconds) if a.only == "all" and a.cpu_seconds > 0 else None
+
+    traffic = load_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(res["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": res["us_per_call"] / 1e3,
+        "us_per_call": round(res["us_per_call"], 4),
+        "frac_of_peak": round(res["gbps"] / PEAK_GBPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights, bf16 activations, fp16 dot products, fp32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "M": 1, "K": 9216, "N": 2560, "out_scale": 1.0,
+                   "rotating_input_sets": a.sets, "bytes_per_call": res["bytes_per_call"],
+                   "timing": "hipGraph replays of back-to-back calls, HIP events on the launch stream"},
+        "roofline": {"bound": "hbm", "achieved": round(res["gbps"], 2), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(res["gbps"] / PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "detail": {k: v for k, v in res.items() if k not in ("gbps",)},
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

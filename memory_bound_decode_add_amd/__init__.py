@@ -1,1 +1,482 @@
-"""fdec: fused decode-MLP kernels for MI355X (gfx950), Python binding."""
+"""fdec: fused decode-MLP kernels for AMD MI355X (gfx950) -- the Python binding.
+
+A thin ctypes layer over ``libfdec.so`` (built by ``python -m
+memory_bound_decode_add_amd.build``).  It only marshals arguments: it checks tensor
+dtypes, devices and sizes, passes raw device pointers and the current HIP stream, and
+turns a non-zero status into :class:`FdecError`.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback.  PyTorch provides device memory and
+streams.
+
+bf16 tensors are ``torch.bfloat16``; packed int4 weights are ``torch.int32`` tensors
+of shape ``[K/8, N]`` holding the uint32 words bit for bit (see ``fdec.h``); group
+scales are ``torch.bfloat16`` ``[K/128, N]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import traffic  # noqa: F401  (byte models)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfdec.so")
+
+FDEC_OK = 0
+UNFUSED_PRODUCT = 0
+UNFUSED_ACT = 1
+
+_c_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class FdecError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class FdecNotBuilt(RuntimeError):
+    pass
+
+
+class CW4(ctypes.Structure):
+    _fields_ = [("qweight", _c_p), ("scales", _c_p), ("K", _i32), ("N", _i32)]
+
+
+class CLayer(ctypes.Structure):
+    _fields_ = [("norm_weight", _c_p), ("eps", ctypes.c_float), ("gate_up", CW4), ("down", CW4),
+                ("out_scale", _c_p), ("residual_in_epilogue", _i32)]
+
+
+# name: (restype, argtypes)
+_SIGS = {
+    "fdec_abi_version": (ctypes.c_int, []),
+    "fdec_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "fdec_last_error": (ctypes.c_char_p, []),
+    "fdec_workspace_init": (ctypes.c_int, [_c_p, _sz, _c_p]),
+    "fdec_add_rmsnorm": (ctypes.c_int, [_c_p, _c_p, _c_p, ctypes.c_float, _i32, _i32, _c_p, _c_p, _c_p]),
+    "fdec_w4_gemv_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_swiglu_w4_gemv": (ctypes.c_int, [_c_p, _c_p, _i64, ctypes.POINTER(CW4), _c_p, _c_p, _i32, _c_p,
+                                           _c_p, _sz, _c_p]),
+    "fdec_w4_gemv": (ctypes.c_int, [_c_p, ctypes.POINTER(CW4), _c_p, _i32, _c_p, _c_p, _sz, _c_p]),
+    "fdec_mlp_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_mlp_decode": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
+                                       _c_p]),
+    "fdec_mlp_chain": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
+                                      _c_p]),
+    "fdec_mlp_graph_create": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                             _sz, _c_p, ctypes.POINTER(_c_p)]),
+    "fdec_graph_launch": (ctypes.c_int, [_c_p, _c_p]),
+    "fdec_graph_kernel_count": (ctypes.c_int, [_c_p]),
+    "fdec_graph_destroy": (ctypes.c_int, [_c_p]),
+    "fdec_unfused_gemv_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "fdec_unfused_swiglu_w4_gemv": (ctypes.c_int, [_i32, _c_p, _c_p, _i64, ctypes.POINTER(CW4), _c_p, _c_p, _i32,
+                                                   _c_p, _c_p, _sz, _c_p]),
+    "fdec_unfused_add_rmsnorm_workspace_bytes": (_sz, [_i32, _i32]),
+    "fdec_unfused_add_rmsnorm": (ctypes.c_int, [_c_p, _c_p, _c_p, ctypes.c_float, _i32, _i32, _c_p, _c_p, _c_p,
+                                                _sz, _c_p]),
+    "fdec_unfused_mlp_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_unfused_mlp_decode": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                               _sz, _c_p]),
+    "fdec_w4_unpack": (ctypes.c_int, [ctypes.POINTER(CW4), _c_p, _c_p]),
+    "fdec_w4_dequant": (ctypes.c_int, [ctypes.POINTER(CW4), _c_p, _c_p]),
+    "fdec_set_gemv_split": (None, [_i32]),
+    "fdec_test_fail_launches": (None, [_i32]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises FdecNotBuilt if libfdec.so is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FdecNotBuilt(f"{LIB_PATH} is missing: run `python -m memory_bound_decode_add_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def _check(status: int):
+    if status != FDEC_OK:
+        msg = lib().fdec_last_error().decode(errors="replace")
+        raise FdecError(status, msg or lib().fdec_status_str(status).decode())
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, shape=None, numel=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} is too small")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _rows(t, name, M, K):
+    """A [M, K] bf16 view whose rows may be strided (e.g. a column slice); returns ld."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a bf16 GPU tensor")
+    if t.dim() != 2 or tuple(t.shape) != (M, K) or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a [M, K] = [{M}, {K}] view with unit column stride")
+    return t.stride(0) if M > 1 else max(K, t.stride(0))
+
+
+# ----------------------------------------------------------------------------
+# bf16 bit-pattern helpers (host <-> device)
+# ----------------------------------------------------------------------------
+def from_bits(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """numpy uint16 bf16 bit patterns -> torch.bfloat16 tensor on `device`."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def words_to_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """numpy uint32 packed words -> torch.int32 tensor (same bits) on `device`."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to(device)
+
+
+# ----------------------------------------------------------------------------
+# weights and layers
+# ----------------------------------------------------------------------------
+@dataclass
+class W4Weight:
+    qweight: torch.Tensor   # int32 [K/8, N] (uint32 words)
+    scales: torch.Tensor    # bf16 [K/128, N]
+
+    def __post_init__(self):
+        _need(self.qweight, "qweight", torch.int32)
+        _need(self.scales, "scales", torch.bfloat16)
+        kb, n = self.qweight.shape
+        if tuple(self.scales.shape) != (kb * 8 // 128, n):
+            raise ValueError("scales must be [K/128, N]")
+
+    @property
+    def K(self):
+        return self.qweight.shape[0] * 8
+
+    @property
+    def N(self):
+        return self.qweight.shape[1]
+
+    def c(self) -> CW4:
+        return CW4(self.qweight.data_ptr(), self.scales.data_ptr(), self.K, self.N)
+
+    @classmethod
+    def from_numpy(cls, qweight: np.ndarray, scales: np.ndarray, device="cuda"):
+        return cls(words_to_tensor(qweight, device), from_bits(scales, device))
+
+
+@dataclass
+class MlpLayer:
+    norm_weight: torch.Tensor        # bf16 [H]
+    gate_up: W4Weight                # K = H, N = 2I
+    down: W4Weight                   # K = I, N = H
+    out_scale: torch.Tensor | None   # fp32 0-dim (or 1-element) device tensor, or None
+    eps: float = 1e-6
+    residual_in_epilogue: bool = True
+
+    @property
+    def H(self):
+        return self.gate_up.K
+
+    @property
+    def I(self):  # noqa: E743
+        return self.down.K
+
+    def c(self) -> CLayer:
+        _need(self.norm_weight, "norm_weight", torch.bfloat16, shape=(self.H,))
+        if self.out_scale is not None:
+            _need(self.out_scale, "out_scale", torch.float32, numel=1)
+        return CLayer(self.norm_weight.data_ptr(), float(self.eps), self.gate_up.c(), self.down.c(),
+                      _ptr(self.out_scale), int(bool(self.residual_in_epilogue)))
+
+
+def scalar(v: float, device="cuda") -> torch.Tensor:
+    """A 0-dim fp32 device tensor (the output-scale multiplier)."""
+    return torch.tensor(float(v), dtype=torch.float32, device=device)
+
+
+# ----------------------------------------------------------------------------
+# workspaces
+# ----------------------------------------------------------------------------
+def gemv_workspace_bytes(M, K, N) -> int:
+    return int(lib().fdec_w4_gemv_workspace_bytes(M, K, N))
+
+
+def mlp_workspace_bytes(M, H, I) -> int:
+    return int(lib().fdec_mlp_workspace_bytes(M, H, I))
+
+
+def unfused_gemv_workspace_bytes(mode, M, K, N) -> int:
+    return int(lib().fdec_unfused_gemv_workspace_bytes(mode, M, K, N))
+
+
+def unfused_add_rmsnorm_workspace_bytes(M, H) -> int:
+    return int(lib().fdec_unfused_add_rmsnorm_workspace_bytes(M, H))
+
+
+def unfused_mlp_workspace_bytes(M, H, I) -> int:
+    return int(lib().fdec_unfused_mlp_workspace_bytes(M, H, I))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (its arrival counters must start at zero)."""
+    return torch.zeros(max(16, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+def workspace_init(ws: torch.Tensor):
+    _check(lib().fdec_workspace_init(ws.data_ptr(), ws.numel(), _stream(ws.device)))
+
+
+def _ws(ws, need, device):
+    if ws is None:
+        return workspace(need, device)
+    _need(ws, "ws", torch.uint8)
+    if ws.numel() < need:
+        raise ValueError(f"workspace has {ws.numel()} bytes, {need} required")
+    return ws
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+def add_rmsnorm(x, residual, weight, eps=1e-6, h_out=None, y_out=None, inplace=False):
+    """(h, y) = (bf16(x + residual), bf16(h * weight / rms(h))).  inplace: h_out = residual."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, H]")
+    M, H = x.shape
+    _need(residual, "residual", torch.bfloat16, shape=(M, H))
+    _need(weight, "weight", torch.bfloat16, shape=(H,))
+    h = residual if inplace else (torch.empty_like(x) if h_out is None else h_out)
+    y = torch.empty_like(x) if y_out is None else y_out
+    _need(h, "h_out", torch.bfloat16, shape=(M, H))
+    _need(y, "y_out", torch.bfloat16, shape=(M, H))
+    _check(lib().fdec_add_rmsnorm(x.data_ptr(), residual.data_ptr(), weight.data_ptr(), float(eps), M, H,
+                                  h.data_ptr(), y.data_ptr(), _stream(x.device)))
+    return h, y
+
+
+def swiglu_w4_gemv(g, u, W: W4Weight, out_scale=None, residual=None, out=None, ws=None):
+    """y = bf16(s * (silu(g) * u) @ dequant(W) (+ residual)); g, u are [M, K] views."""
+    M = g.shape[0]
+    ld = _rows(g, "g", M, W.K)
+    ldu = _rows(u, "u", M, W.K)
+    if M > 1 and ldu != ld:
+        raise ValueError("g and u must share a row stride")
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=g.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    ws = _ws(ws, gemv_workspace_bytes(M, W.K, W.N), g.device)
+    cw = W.c()
+    _check(lib().fdec_swiglu_w4_gemv(g.data_ptr(), u.data_ptr(), ld, ctypes.byref(cw), _ptr(out_scale),
+                                     _ptr(residual), M, y.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream(g.device)))
+    return y
+
+
+def w4_gemv(x, W: W4Weight, out_scale=None, out=None, ws=None):
+    """y = bf16(s * x @ dequant(W)) (the identity-prologue GEMV, e.g. gate_up)."""
+    _need(x, "x", torch.bfloat16)
+    M = x.shape[0]
+    _need(x, "x", torch.bfloat16, shape=(M, W.K))
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    ws = _ws(ws, gemv_workspace_bytes(M, W.K, W.N), x.device)
+    cw = W.c()
+    _check(lib().fdec_w4_gemv(x.data_ptr(), ctypes.byref(cw), _ptr(out_scale), M, y.data_ptr(), ws.data_ptr(),
+                              ws.numel(), _stream(x.device)))
+    return y
+
+
+@dataclass
+class MlpBuffers:
+    """Caller-owned activation buffers of one layer (or a chain) at batch M."""
+    x: torch.Tensor          # [M, H]  layer input; with out=x, the layer output
+    residual: torch.Tensor   # [M, H]
+    y_norm: torch.Tensor     # [M, H]
+    gate_up: torch.Tensor    # [M, 2I]
+    out: torch.Tensor        # [M, H]
+
+    @classmethod
+    def empty(cls, M, H, I, device="cuda", out_is_x=False):
+        x = torch.empty((M, H), dtype=torch.bfloat16, device=device)
+        return cls(x, torch.empty_like(x), torch.empty_like(x),
+                   torch.empty((M, 2 * I), dtype=torch.bfloat16, device=device),
+                   x if out_is_x else torch.empty_like(x))
+
+
+def _check_bufs(layer: MlpLayer, b: MlpBuffers):
+    M = b.x.shape[0]
+    for name, t, shp in (("x", b.x, (M, layer.H)), ("residual", b.residual, (M, layer.H)),
+                         ("y_norm", b.y_norm, (M, layer.H)), ("gate_up", b.gate_up, (M, 2 * layer.I)),
+                         ("out", b.out, (M, layer.H))):
+        _need(t, name, torch.bfloat16, shape=shp)
+    return M
+
+
+def mlp_decode(layer: MlpLayer, bufs: MlpBuffers, ws=None):
+    """One layer: residual <- h; y_norm; gate_up; out (see fdec.h)."""
+    M = _check_bufs(layer, bufs)
+    ws = _ws(ws, mlp_workspace_bytes(M, layer.H, layer.I), bufs.x.device)
+    cl = layer.c()
+    _check(lib().fdec_mlp_decode(ctypes.byref(cl), M, bufs.x.data_ptr(), bufs.residual.data_ptr(),
+                                 bufs.y_norm.data_ptr(), bufs.gate_up.data_ptr(), bufs.out.data_ptr(),
+                                 ws.data_ptr(), ws.numel(), _stream(bufs.x.device)))
+    return bufs
+
+
+def _layer_array(layers):
+    arr = (CLayer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = L.c()
+    return arr
+
+
+def mlp_chain(layers, bufs: MlpBuffers, ws=None):
+    """All layers eagerly, x updated in place (out = x), residual <- the last h."""
+    M = _check_bufs(layers[0], bufs)
+    ws = _ws(ws, mlp_workspace_bytes(M, layers[0].H, layers[0].I), bufs.x.device)
+    arr = _layer_array(layers)
+    _check(lib().fdec_mlp_chain(arr, len(layers), M, bufs.x.data_ptr(), bufs.residual.data_ptr(),
+                                bufs.y_norm.data_ptr(), bufs.gate_up.data_ptr(), ws.data_ptr(), ws.numel(),
+                                _stream(bufs.x.device)))
+    return bufs
+
+
+class MlpGraph:
+    """The layer chain captured once into a hipGraph; launch() replays it."""
+
+    def __init__(self, layers, bufs: MlpBuffers, ws=None, stream: torch.cuda.Stream | None = None):
+        M = _check_bufs(layers[0], bufs)
+        self.layers = list(layers)          # keep the tensors alive
+        self.bufs = bufs
+        self.ws = _ws(ws, mlp_workspace_bytes(M, layers[0].H, layers[0].I), bufs.x.device)
+        self._handle = _c_p()
+        cap = stream if stream is not None else torch.cuda.Stream(device=bufs.x.device)
+        cap.wait_stream(torch.cuda.current_stream(bufs.x.device))
+        arr = _layer_array(self.layers)
+        _check(lib().fdec_mlp_graph_create(arr, len(self.layers), M, bufs.x.data_ptr(), bufs.residual.data_ptr(),
+                                           bufs.y_norm.data_ptr(), bufs.gate_up.data_ptr(), self.ws.data_ptr(),
+                                           self.ws.numel(), cap.cuda_stream, ctypes.byref(self._handle)))
+
+    @property
+    def kernel_count(self) -> int:
+        return int(lib().fdec_graph_kernel_count(self._handle))
+
+    def launch(self, stream: torch.cuda.Stream | None = None):
+        s = stream.cuda_stream if stream is not None else _stream(self.bufs.x.device)
+        _check(lib().fdec_graph_launch(self._handle, s))
+
+    def close(self):
+        if self._handle:
+            _check(lib().fdec_graph_destroy(self._handle))
+            self._handle = _c_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def unfused_swiglu_w4_gemv(mode, g, u, W: W4Weight, out_scale=None, residual=None, out=None, ws=None):
+    M = g.shape[0]
+    ld = _rows(g, "g", M, W.K)
+    _rows(u, "u", M, W.K)
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=g.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    need = unfused_gemv_workspace_bytes(mode, M, W.K, W.N)
+    ws = _ws(ws, need, g.device)
+    cw = W.c()
+    _check(lib().fdec_unfused_swiglu_w4_gemv(mode, g.data_ptr(), u.data_ptr(), ld, ctypes.byref(cw),
+                                             _ptr(out_scale), _ptr(residual), M, y.data_ptr(), ws.data_ptr(),
+                                             ws.numel(), _stream(g.device)))
+    return y
+
+
+def unfused_add_rmsnorm(x, residual, weight, eps=1e-6, h_out=None, y_out=None, ws=None):
+    _need(x, "x", torch.bfloat16)
+    M, H = x.shape
+    _need(residual, "residual", torch.bfloat16, shape=(M, H))
+    _need(weight, "weight", torch.bfloat16, shape=(H,))
+    h = torch.empty_like(x) if h_out is None else h_out
+    y = torch.empty_like(x) if y_out is None else y_out
+    ws = _ws(ws, unfused_add_rmsnorm_workspace_bytes(M, H), x.device)
+    _check(lib().fdec_unfused_add_rmsnorm(x.data_ptr(), residual.data_ptr(), weight.data_ptr(), float(eps), M, H,
+                                          h.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)))
+    return h, y
+
+
+def unfused_mlp_decode(layer: MlpLayer, bufs: MlpBuffers, ws=None):
+    M = _check_bufs(layer, bufs)
+    ws = _ws(ws, unfused_mlp_workspace_bytes(M, layer.H, layer.I), bufs.x.device)
+    cl = layer.c()
+    _check(lib().fdec_unfused_mlp_decode(ctypes.byref(cl), M, bufs.x.data_ptr(), bufs.residual.data_ptr(),
+                                         bufs.y_norm.data_ptr(), bufs.gate_up.data_ptr(), bufs.out.data_ptr(),
+                                         ws.data_ptr(), ws.numel(), _stream(bufs.x.device)))
+    return bufs
+
+
+def w4_unpack(W: W4Weight) -> torch.Tensor:
+    q = torch.empty((W.K, W.N), dtype=torch.int8, device=W.qweight.device)
+    cw = W.c()
+    _check(lib().fdec_w4_unpack(ctypes.byref(cw), q.data_ptr(), _stream(q.device)))
+    return q
+
+
+def w4_dequant(W: W4Weight) -> torch.Tensor:
+    w = torch.empty((W.K, W.N), dtype=torch.float32, device=W.qweight.device)
+    cw = W.c()
+    _check(lib().fdec_w4_dequant(ctypes.byref(cw), w.data_ptr(), _stream(w.device)))
+    return w
+
+
+def set_gemv_split(k: int):
+    lib().fdec_set_gemv_split(int(k))
+
+
+def test_fail_launches(on: bool):
+    lib().fdec_test_fail_launches(int(bool(on)))

@@ -1,0 +1,531 @@
+// The C ABI of libfdec: argument validation, workspace sizing, launch sequencing and
+// graph capture.  Every check runs before the first HIP call, so a rejected call
+// enqueues nothing.  Kernels live in the .hip files; see fdec.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "fdec_internal.h"
+
+using namespace fdec;
+
+namespace {
+
+thread_local std::string t_last_error;
+int g_fail_launches = 0;
+
+constexpr size_t kAlign = 256;   // sub-buffer alignment inside workspaces
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    t_last_error = std::string(fdec_status_str(status)) + ": " + buf;
+    return status;
+}
+
+int ok() {
+    t_last_error.clear();
+    return FDEC_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(FDEC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+bool overlap(Span a, Span b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// ---- shared checks ----
+int check_w4(const fdec_w4* W, const char* name) {
+    if (!W) return fail(FDEC_ERR_NULL, "%s is NULL", name);
+    if (!W->qweight || !W->scales) return fail(FDEC_ERR_NULL, "%s.qweight or %s.scales is NULL", name, name);
+    if (W->K <= 0 || W->K % 128) return fail(FDEC_ERR_SHAPE, "%s.K = %d must be a positive multiple of 128", name, W->K);
+    if (W->N <= 0 || W->N % 8) return fail(FDEC_ERR_SHAPE, "%s.N = %d must be a positive multiple of 8", name, W->N);
+    if (!aligned16(W->qweight) || !aligned16(W->scales))
+        return fail(FDEC_ERR_ALIGN, "%s arrays must be 16-byte aligned", name);
+    return FDEC_OK;
+}
+Span w4_qspan(const fdec_w4* W) { return {W->qweight, size_t(W->K) / 8 * W->N * 4}; }
+Span w4_sspan(const fdec_w4* W) { return {W->scales, size_t(W->K) / 128 * W->N * 2}; }
+
+int check_m(int M) {
+    if (M < 1 || M > 16) return fail(FDEC_ERR_SHAPE, "M = %d must be in [1, 16]", M);
+    return FDEC_OK;
+}
+
+int check_norm(const fdec_bf16* x, const fdec_bf16* residual, const fdec_bf16* weight, float eps,
+               int M, int H, const fdec_bf16* h_out, const fdec_bf16* y_out) {
+    if (!x || !residual || !weight || !h_out || !y_out)
+        return fail(FDEC_ERR_NULL, "add_rmsnorm: x, residual, weight, h_out and y_out are required");
+    if (M < 0) return fail(FDEC_ERR_SHAPE, "M = %d must be >= 0", M);
+    if (H < 8 || H > 16384 || H % 8) return fail(FDEC_ERR_SHAPE, "H = %d must be a multiple of 8 in [8, 16384]", H);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(FDEC_ERR_ARG, "eps must be finite and >= 0");
+    if (!aligned16(x) || !aligned16(residual) || !aligned16(weight) || !aligned16(h_out) || !aligned16(y_out))
+        return fail(FDEC_ERR_ALIGN, "add_rmsnorm: every tensor must be 16-byte aligned");
+    const size_t t = size_t(M) * H * 2;
+    const Span X{x, t}, R{residual, t}, W{weight, size_t(H) * 2}, Hs{h_out, t}, Y{y_out, t};
+    if (overlap(Y, X) || overlap(Y, R) || overlap(Y, W) || overlap(Y, Hs))
+        return fail(FDEC_ERR_ALIAS, "y_out overlaps another tensor");
+    if (overlap(Hs, X) || overlap(Hs, W) || (overlap(Hs, R) && h_out != residual))
+        return fail(FDEC_ERR_ALIAS, "h_out may only alias residual exactly");
+    return FDEC_OK;
+}
+
+int check_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_w4* W,
+               const float* out_scale, const fdec_bf16* residual, int M, const fdec_bf16* y,
+               void* ws, size_t ws_bytes, bool swiglu, size_t need_ws) {
+    int st;
+    if ((st = check_w4(W, "W")) != FDEC_OK) return st;
+    if ((st = check_m(M)) != FDEC_OK) return st;
+    if (!g || (swiglu && !u) || !y) return fail(FDEC_ERR_NULL, "activation input and y are required");
+    if (ldgu < W->K || ldgu % 8) return fail(FDEC_ERR_SHAPE, "ld = %lld must be >= K and a multiple of 8", (long long)ldgu);
+    if (!aligned16(g) || (u && !aligned16(u)) || !aligned16(y) || (residual && !aligned16(residual)))
+        return fail(FDEC_ERR_ALIGN, "activation, residual and y must be 16-byte aligned");
+    if (out_scale && !aligned4(out_scale)) return fail(FDEC_ERR_ALIGN, "out_scale must be 4-byte aligned");
+    if (ws_bytes < need_ws) return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, need_ws);
+    if (need_ws > 0 && !ws) return fail(FDEC_ERR_NULL, "workspace is NULL");
+    if (ws && !aligned16(ws)) return fail(FDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t in_bytes = (size_t(M - 1) * ldgu + W->K) * 2;
+    const Span Y{y, size_t(M) * W->N * 2};
+    const Span ins[] = {{g, in_bytes}, {u, in_bytes}, w4_qspan(W), w4_sspan(W), {out_scale, 4}, {ws, ws_bytes}};
+    for (const Span& s : ins)
+        if (overlap(Y, s)) return fail(FDEC_ERR_ALIAS, "y overlaps an input or the workspace");
+    if (residual && overlap(Y, Span{residual, Y.bytes}) && residual != y)
+        return fail(FDEC_ERR_ALIAS, "y may only alias residual exactly");
+    const Span WS{ws, need_ws};
+    const Span others[] = {{g, in_bytes}, {u, in_bytes}, w4_qspan(W), w4_sspan(W), {out_scale, 4}, {residual, Y.bytes}};
+    for (const Span& s : others)
+        if (overlap(WS, s)) return fail(FDEC_ERR_ALIAS, "the workspace overlaps an input");
+    return FDEC_OK;
+}
+
+int injected() { return fail(FDEC_ERR_HIP, "launch failure injected by fdec_test_fail_launches"); }
+
+// ---- the layer ----
+struct LayerDims {
+    int H, I;
+};
+
+int check_layer(const fdec_mlp_layer* L, int M, LayerDims* d) {
+    if (!L) return fail(FDEC_ERR_NULL, "layer is NULL");
+    int st;
+    if ((st = check_m(M)) != FDEC_OK) return st;
+    if ((st = check_w4(&L->gate_up, "gate_up")) != FDEC_OK) return st;
+    if ((st = check_w4(&L->down, "down")) != FDEC_OK) return st;
+    if (!L->norm_weight) return fail(FDEC_ERR_NULL, "norm_weight is NULL");
+    if (!aligned16(L->norm_weight)) return fail(FDEC_ERR_ALIGN, "norm_weight must be 16-byte aligned");
+    if (L->out_scale && !aligned4(L->out_scale)) return fail(FDEC_ERR_ALIGN, "out_scale must be 4-byte aligned");
+    const int H = L->gate_up.K, I = L->down.K;
+    if (L->gate_up.N != 2 * I || L->down.N != H)
+        return fail(FDEC_ERR_SHAPE, "gate_up must be [H, 2I] and down [I, H] (H = %d, I = %d)", H, I);
+    if (H > 16384) return fail(FDEC_ERR_SHAPE, "H = %d exceeds 16384", H);
+    if (!(L->eps >= 0.f) || !std::isfinite(L->eps)) return fail(FDEC_ERR_ARG, "eps must be finite and >= 0");
+    d->H = H;
+    d->I = I;
+    return FDEC_OK;
+}
+
+size_t mlp_ws(int M, int H, int I) {
+    return std::max(gemv_workspace_bytes(M, H, 2 * I), gemv_workspace_bytes(M, I, H));
+}
+
+int check_layer_buffers(const fdec_mlp_layer* L, int M, LayerDims d, const fdec_bf16* x,
+                        const fdec_bf16* residual, const fdec_bf16* y_norm, const fdec_bf16* gate_up,
+                        const fdec_bf16* out, void* ws, size_t ws_bytes, size_t need) {
+    if (!x || !residual || !y_norm || !gate_up || !out)
+        return fail(FDEC_ERR_NULL, "x, residual, y_norm, gate_up and out are required");
+    if (!aligned16(x) || !aligned16(residual) || !aligned16(y_norm) || !aligned16(gate_up) || !aligned16(out))
+        return fail(FDEC_ERR_ALIGN, "every activation buffer must be 16-byte aligned");
+    if (ws_bytes < need) return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);
+    if (need > 0 && !ws) return fail(FDEC_ERR_NULL, "workspace is NULL");
+    if (ws && !aligned16(ws)) return fail(FDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t t = size_t(M) * d.H * 2;
+    const Span X{x, t}, R{residual, t}, Y{y_norm, t}, G{gate_up, size_t(M) * d.I * 4}, O{out, t}, WS{ws, need};
+    const Span wts[] = {w4_qspan(&L->gate_up), w4_sspan(&L->gate_up), w4_qspan(&L->down), w4_sspan(&L->down),
+                        {L->norm_weight, size_t(d.H) * 2}, {L->out_scale, 4}};
+    const Span outs[] = {R, Y, G, O, WS};
+    for (const Span& o : outs)
+        for (const Span& w : wts)
+            if (overlap(o, w)) return fail(FDEC_ERR_ALIAS, "an output buffer overlaps a weight");
+    if (overlap(R, X) || overlap(R, Y) || overlap(R, G) || overlap(R, O) || overlap(R, WS) || overlap(Y, X) ||
+        overlap(Y, G) || overlap(Y, O) || overlap(Y, WS) || overlap(G, X) || overlap(G, O) || overlap(G, WS) ||
+        overlap(O, WS) || overlap(X, WS) || (overlap(O, X) && out != x))
+        return fail(FDEC_ERR_ALIAS, "activation buffers overlap (only out == x is allowed)");
+    return FDEC_OK;
+}
+
+hipError_t enqueue_layer(const fdec_mlp_layer* L, int M, LayerDims d, const fdec_bf16* x,
+                         fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* out,
+                         void* ws, hipStream_t s) {
+    hipError_t e = launch_add_rmsnorm(x, residual, L->norm_weight, L->eps, M, d.H, residual, y_norm, s);
+    if (e != hipSuccess) return e;
+    e = launch_gemv(kIdentity, y_norm, nullptr, d.H, L->gate_up.qweight, L->gate_up.scales, M, d.H, 2 * d.I,
+                    nullptr, nullptr, gate_up, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_gemv(kSwiGLU, gate_up, gate_up + d.I, 2 * int64_t(d.I), L->down.qweight, L->down.scales, M,
+                       d.I, d.H, L->out_scale, L->residual_in_epilogue ? residual : nullptr, out, ws, s);
+}
+
+int check_chain(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d) {
+    if (!layers) return fail(FDEC_ERR_NULL, "layers is NULL");
+    if (n_layers < 1) return fail(FDEC_ERR_SHAPE, "n_layers = %d must be >= 1", n_layers);
+    int st;
+    for (int l = 0; l < n_layers; ++l) {
+        LayerDims dl;
+        if ((st = check_layer(&layers[l], M, &dl)) != FDEC_OK) return st;
+        if (l == 0) *d = dl;
+        if (dl.H != d->H || dl.I != d->I) return fail(FDEC_ERR_SHAPE, "layer %d has different H or I", l);
+        if (l + 1 < n_layers && layers[l].residual_in_epilogue)
+            return fail(FDEC_ERR_ARG, "layer %d: only the last layer may add the residual in its epilogue", l);
+    }
+    return FDEC_OK;
+}
+
+// ---- unfused ----
+size_t unfused_norm_ws(int M, int H) {
+    return 2 * align_up(size_t(M) * H * 4) + align_up(size_t(M) * 3 * 4);
+}
+size_t unfused_act_ws(int M, int K, int N) {
+    return 2 * align_up(size_t(M) * K * 2) + gemv_workspace_bytes(M, K, N);
+}
+
+hipError_t enqueue_unfused_act(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_w4* W,
+                               const float* out_scale, const fdec_bf16* residual, int M, fdec_bf16* y,
+                               void* ws, hipStream_t s) {
+    const int K = W->K, N = W->N;
+    uint16_t* t = static_cast<uint16_t*>(ws);
+    uint16_t* act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align_up(size_t(M) * K * 2));
+    void* gws = static_cast<char*>(ws) + 2 * align_up(size_t(M) * K * 2);
+    hipError_t e;
+    if ((e = launch_silu_bf16(g, ldgu, M, K, t, s)) != hipSuccess) return e;
+    if ((e = launch_mul_bf16(t, K, u, ldgu, M, K, act, s)) != hipSuccess) return e;
+    if ((e = launch_gemv(kIdentity, act, nullptr, K, W->qweight, W->scales, M, K, N, nullptr, nullptr, y, gws, s)) !=
+        hipSuccess)
+        return e;
+    if ((e = launch_scale_bf16(y, int64_t(M) * N, out_scale, s)) != hipSuccess) return e;
+    if (residual) return launch_add_bf16(y, residual, int64_t(M) * N, s);
+    return hipSuccess;
+}
+
+hipError_t enqueue_eager_norm(const fdec_bf16* x, const fdec_bf16* r, const fdec_bf16* w, float eps, int M, int H,
+                              fdec_bf16* h, fdec_bf16* y, void* ws, hipStream_t s) {
+    float* a = static_cast<float*>(ws);
+    float* b = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(size_t(M) * H * 4));
+    float* rows = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * align_up(size_t(M) * H * 4));
+    return launch_eager_rmsnorm(x, r, w, eps, M, H, h, y, a, b, rows, s);
+}
+
+}  // namespace
+
+struct fdec_graph_s {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int kernels = 0;
+};
+
+extern "C" {
+
+FDEC_API int fdec_abi_version(void) { return FDEC_ABI_VERSION; }
+
+FDEC_API const char* fdec_status_str(int status) {
+    switch (status) {
+        case FDEC_OK: return "FDEC_OK";
+        case FDEC_ERR_NULL: return "FDEC_ERR_NULL";
+        case FDEC_ERR_SHAPE: return "FDEC_ERR_SHAPE";
+        case FDEC_ERR_ALIGN: return "FDEC_ERR_ALIGN";
+        case FDEC_ERR_ALIAS: return "FDEC_ERR_ALIAS";
+        case FDEC_ERR_WORKSPACE: return "FDEC_ERR_WORKSPACE";
+        case FDEC_ERR_UNSUPPORTED: return "FDEC_ERR_UNSUPPORTED";
+        case FDEC_ERR_HIP: return "FDEC_ERR_HIP";
+        case FDEC_ERR_ARG: return "FDEC_ERR_ARG";
+        default: return "FDEC_ERR_UNKNOWN";
+    }
+}
+
+FDEC_API const char* fdec_last_error(void) { return t_last_error.c_str(); }
+
+FDEC_API void fdec_set_gemv_split(int32_t k) { g_forced_split = k > 0 ? k : 0; }
+FDEC_API void fdec_test_fail_launches(int32_t on) { g_fail_launches = on ? 1 : 0; }
+
+FDEC_API int fdec_workspace_init(void* ws, size_t ws_bytes, fdec_stream stream) {
+    if (ws_bytes == 0) return ok();
+    if (!ws) return fail(FDEC_ERR_NULL, "workspace is NULL");
+    if (!aligned16(ws)) return fail(FDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (g_fail_launches) return injected();
+    return hip_status(launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)), "fill kernel");
+}
+
+FDEC_API int fdec_add_rmsnorm(const fdec_bf16* x, const fdec_bf16* residual, const fdec_bf16* weight, float eps,
+                              int32_t M, int32_t H, fdec_bf16* h_out, fdec_bf16* y_out, fdec_stream stream) {
+    const int st = check_norm(x, residual, weight, eps, M, H, h_out, y_out);
+    if (st != FDEC_OK) return st;
+    if (g_fail_launches) return injected();
+    return hip_status(launch_add_rmsnorm(x, residual, weight, eps, M, H, h_out, y_out,
+                                         static_cast<hipStream_t>(stream)),
+                      "add_rmsnorm launch");
+}
+
+FDEC_API size_t fdec_w4_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+    if (M < 1 || M > 16 || K <= 0 || K % 128 || N <= 0 || N % 8) return 0;
+    return gemv_workspace_bytes(M, K, N);
+}
+
+FDEC_API int fdec_swiglu_w4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_w4* W,
+                                 const float* out_scale, const fdec_bf16* residual, int32_t M, fdec_bf16* y,
+                                 void* ws, size_t ws_bytes, fdec_stream stream) {
+    if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
+    const size_t need = (M >= 1 && M <= 16 && W->K > 0 && W->K % 128 == 0 && W->N > 0 && W->N % 8 == 0)
+                            ? gemv_workspace_bytes(M, W->K, W->N) : 0;
+    const int st = check_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true, need);
+    if (st != FDEC_OK) return st;
+    if (g_fail_launches) return injected();
+    return hip_status(launch_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual,
+                                  y, ws, static_cast<hipStream_t>(stream)),
+                      "gemv launch");
+}
+
+FDEC_API int fdec_w4_gemv(const fdec_bf16* x, const fdec_w4* W, const float* out_scale, int32_t M, fdec_bf16* y,
+                          void* ws, size_t ws_bytes, fdec_stream stream) {
+    if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
+    const size_t need = (M >= 1 && M <= 16 && W->K > 0 && W->K % 128 == 0 && W->N > 0 && W->N % 8 == 0)
+                            ? gemv_workspace_bytes(M, W->K, W->N) : 0;
+    const int st = check_gemv(x, nullptr, W->K, W, out_scale, nullptr, M, y, ws, ws_bytes, false, need);
+    if (st != FDEC_OK) return st;
+    if (g_fail_launches) return injected();
+    return hip_status(launch_gemv(kIdentity, x, nullptr, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale,
+                                  nullptr, y, ws, static_cast<hipStream_t>(stream)),
+                      "gemv launch");
+}
+
+FDEC_API size_t fdec_mlp_workspace_bytes(int32_t M, int32_t H, int32_t I) {
+    if (M < 1 || M > 16 || H <= 0 || H % 128 || I <= 0 || I % 128) return 0;
+    return mlp_ws(M, H, I);
+}
+
+FDEC_API int fdec_mlp_decode(const fdec_mlp_layer* layer, int32_t M, const fdec_bf16* x, fdec_bf16* residual,
+                             fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* out, void* ws, size_t ws_bytes,
+                             fdec_stream stream) {
+    LayerDims d;
+    int st = check_layer(layer, M, &d);
+    if (st != FDEC_OK) return st;
+    const size_t need = mlp_ws(M, d.H, d.I);
+    st = check_layer_buffers(layer, M, d, x, residual, y_norm, gate_up, out, ws, ws_bytes, need);
+    if (st != FDEC_OK) return st;
+    if (g_fail_launches) return injected();
+    return hip_status(enqueue_layer(layer, M, d, x, residual, y_norm, gate_up, out, ws,
+                                    static_cast<hipStream_t>(stream)),
+                      "layer launch");
+}
+
+FDEC_API int fdec_mlp_chain(const fdec_mlp_layer* layers, int32_t n_layers, int32_t M, fdec_bf16* x,
+                            fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, void* ws, size_t ws_bytes,
+                            fdec_stream stream) {
+    LayerDims d;
+    int st = check_chain(layers, n_layers, M, &d);
+    if (st != FDEC_OK) return st;
+    const size_t need = mlp_ws(M, d.H, d.I);
+    for (int l = 0; l < n_layers; ++l)
+        if ((st = check_layer_buffers(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, ws_bytes, need)) !=
+            FDEC_OK)
+            return st;
+    if (g_fail_launches) return injected();
+    for (int l = 0; l < n_layers; ++l) {
+        const hipError_t e =
+            enqueue_layer(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_status(e, "chain launch");
+    }
+    return ok();
+}
+
+FDEC_API int fdec_mlp_graph_create(const fdec_mlp_layer* layers, int32_t n_layers, int32_t M, fdec_bf16* x,
+                                   fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, void* ws,
+                                   size_t ws_bytes, fdec_stream stream, fdec_graph* out) {
+    if (!out) return fail(FDEC_ERR_NULL, "out is NULL");
+    if (!stream) return fail(FDEC_ERR_ARG, "graph capture needs a non-null stream");
+    LayerDims d;
+    int st = check_chain(layers, n_layers, M, &d);
+    if (st != FDEC_OK) return st;
+    const size_t need = mlp_ws(M, d.H, d.I);
+    for (int l = 0; l < n_layers; ++l)
+        if ((st = check_layer_buffers(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, ws_bytes, need)) !=
+            FDEC_OK)
+            return st;
+    if (g_fail_launches) return injected();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    fdec_graph_s* G = new (std::nothrow) fdec_graph_s;
+    if (!G) return fail(FDEC_ERR_ARG, "out of host memory");
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        delete G;
+        return hip_status(e, "hipStreamBeginCapture");
+    }
+    hipError_t le = hipSuccess;
+    for (int l = 0; l < n_layers && le == hipSuccess; ++l)
+        le = enqueue_layer(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, s);
+    e = hipStreamEndCapture(s, &G->graph);
+    if (le != hipSuccess || e != hipSuccess) {
+        if (G->graph) (void)hipGraphDestroy(G->graph);
+        delete G;
+        return hip_status(le != hipSuccess ? le : e, "graph capture");
+    }
+    size_t nodes = 0;
+    if (hipGraphGetNodes(G->graph, nullptr, &nodes) != hipSuccess) nodes = 0;
+    G->kernels = int(nodes);
+    e = hipGraphInstantiate(&G->exec, G->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(G->graph);
+        delete G;
+        return hip_status(e, "hipGraphInstantiate");
+    }
+    *out = G;
+    return ok();
+}
+
+FDEC_API int fdec_graph_launch(fdec_graph graph, fdec_stream stream) {
+    if (!graph || !graph->exec) return fail(FDEC_ERR_NULL, "graph is NULL");
+    if (g_fail_launches) return injected();
+    return hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)), "hipGraphLaunch");
+}
+
+FDEC_API int fdec_graph_kernel_count(fdec_graph graph) { return graph ? graph->kernels : -1; }
+
+FDEC_API int fdec_graph_destroy(fdec_graph graph) {
+    if (!graph) return ok();
+    hipError_t e1 = graph->exec ? hipGraphExecDestroy(graph->exec) : hipSuccess;
+    hipError_t e2 = graph->graph ? hipGraphDestroy(graph->graph) : hipSuccess;
+    delete graph;
+    return hip_status(e1 != hipSuccess ? e1 : e2, "graph destroy");
+}
+
+FDEC_API size_t fdec_unfused_gemv_workspace_bytes(int32_t mode, int32_t M, int32_t K, int32_t N) {
+    if (M < 1 || M > 16 || K <= 0 || K % 128 || N <= 0 || N % 8) return 0;
+    if (mode == FDEC_UNFUSED_PRODUCT) return M == 1 ? size_t(M) * K * N * 4 : 0;
+    if (mode == FDEC_UNFUSED_ACT) return unfused_act_ws(M, K, N);
+    return 0;
+}
+
+FDEC_API int fdec_unfused_swiglu_w4_gemv(int32_t mode, const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu,
+                                         const fdec_w4* W, const float* out_scale, const fdec_bf16* residual,
+                                         int32_t M, fdec_bf16* y, void* ws, size_t ws_bytes, fdec_stream stream) {
+    if (mode != FDEC_UNFUSED_PRODUCT && mode != FDEC_UNFUSED_ACT) return fail(FDEC_ERR_ARG, "unknown mode %d", mode);
+    if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
+    if (mode == FDEC_UNFUSED_PRODUCT && M != 1)
+        return fail(FDEC_ERR_UNSUPPORTED, "the materialised-product sequence is defined for M == 1 only (M = %d)", M);
+    const bool shape_ok = M >= 1 && M <= 16 && W->K > 0 && W->K % 128 == 0 && W->N > 0 && W->N % 8 == 0;
+    const size_t need = shape_ok ? fdec_unfused_gemv_workspace_bytes(mode, M, W->K, W->N) : 0;
+    const int st = check_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true, need);
+    if (st != FDEC_OK) return st;
+    if (residual == y) return fail(FDEC_ERR_ALIAS, "the unfused sequence needs y distinct from residual");
+    if (g_fail_launches) return injected();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mode == FDEC_UNFUSED_PRODUCT)
+        return hip_status(launch_unfused_product(g, u, W->qweight, W->scales, W->K, W->N, out_scale, residual, y,
+                                                 static_cast<float*>(ws), s),
+                          "unfused product launch");
+    return hip_status(enqueue_unfused_act(g, u, ldgu, W, out_scale, residual, M, y, ws, s), "unfused act launch");
+}
+
+FDEC_API size_t fdec_unfused_add_rmsnorm_workspace_bytes(int32_t M, int32_t H) {
+    if (M < 0 || H < 8 || H > 16384 || H % 8) return 0;
+    return unfused_norm_ws(M, H);
+}
+
+FDEC_API int fdec_unfused_add_rmsnorm(const fdec_bf16* x, const fdec_bf16* residual, const fdec_bf16* weight,
+                                      float eps, int32_t M, int32_t H, fdec_bf16* h_out, fdec_bf16* y_out, void* ws,
+                                      size_t ws_bytes, fdec_stream stream) {
+    int st = check_norm(x, residual, weight, eps, M, H, h_out, y_out);
+    if (st != FDEC_OK) return st;
+    const size_t need = unfused_norm_ws(M, H);
+    if (ws_bytes < need) return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);
+    if (need > 0 && !ws) return fail(FDEC_ERR_NULL, "workspace is NULL");
+    if (ws && !aligned16(ws)) return fail(FDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t t = size_t(M) * H * 2;
+    const Span WS{ws, need};
+    if (overlap(WS, {x, t}) || overlap(WS, {residual, t}) || overlap(WS, {weight, size_t(H) * 2}) ||
+        overlap(WS, {h_out, t}) || overlap(WS, {y_out, t}))
+        return fail(FDEC_ERR_ALIAS, "the workspace overlaps a tensor");
+    if (g_fail_launches) return injected();
+    return hip_status(enqueue_eager_norm(x, residual, weight, eps, M, H, h_out, y_out, ws,
+                                         static_cast<hipStream_t>(stream)),
+                      "eager norm launch");
+}
+
+FDEC_API size_t fdec_unfused_mlp_workspace_bytes(int32_t M, int32_t H, int32_t I) {
+    if (M < 1 || M > 16 || H <= 0 || H % 128 || I <= 0 || I % 128) return 0;
+    return align_up(unfused_norm_ws(M, H)) + align_up(unfused_act_ws(M, I, H)) +
+           align_up(gemv_workspace_bytes(M, H, 2 * I));
+}
+
+FDEC_API int fdec_unfused_mlp_decode(const fdec_mlp_layer* layer, int32_t M, const fdec_bf16* x,
+                                     fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* out,
+                                     void* ws, size_t ws_bytes, fdec_stream stream) {
+    LayerDims d;
+    int st = check_layer(layer, M, &d);
+    if (st != FDEC_OK) return st;
+    const size_t need = fdec_unfused_mlp_workspace_bytes(M, d.H, d.I);
+    st = check_layer_buffers(layer, M, d, x, residual, y_norm, gate_up, out, ws, ws_bytes, need);
+    if (st != FDEC_OK) return st;
+    if (g_fail_launches) return injected();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    void* norm_ws = w;
+    void* act_ws = w + align_up(unfused_norm_ws(M, d.H));
+    void* gu_ws = static_cast<char*>(act_ws) + align_up(unfused_act_ws(M, d.I, d.H));
+    hipError_t e = enqueue_eager_norm(x, residual, layer->norm_weight, layer->eps, M, d.H, residual, y_norm,
+                                      norm_ws, s);
+    if (e == hipSuccess)
+        e = launch_gemv(kIdentity, y_norm, nullptr, d.H, layer->gate_up.qweight, layer->gate_up.scales, M, d.H,
+                        2 * d.I, nullptr, nullptr, gate_up, gu_ws, s);
+    if (e == hipSuccess)
+        e = enqueue_unfused_act(gate_up, gate_up + d.I, 2 * int64_t(d.I), &layer->down, layer->out_scale,
+                                layer->residual_in_epilogue ? residual : nullptr, M, out, act_ws, s);
+    return hip_status(e, "unfused layer launch");
+}
+
+FDEC_API int fdec_w4_unpack(const fdec_w4* W, int8_t* q_out, fdec_stream stream) {
+    int st = check_w4(W, "W");
+    if (st != FDEC_OK) return st;
+    if (!q_out) return fail(FDEC_ERR_NULL, "q_out is NULL");
+    const Span Q{q_out, size_t(W->K) * W->N};
+    if (overlap(Q, w4_qspan(W)) || overlap(Q, w4_sspan(W))) return fail(FDEC_ERR_ALIAS, "q_out overlaps W");
+    if (g_fail_launches) return injected();
+    return hip_status(launch_w4_unpack(W->qweight, W->K, W->N, q_out, static_cast<hipStream_t>(stream)),
+                      "unpack launch");
+}
+
+FDEC_API int fdec_w4_dequant(const fdec_w4* W, float* w_out, fdec_stream stream) {
+    int st = check_w4(W, "W");
+    if (st != FDEC_OK) return st;
+    if (!w_out) return fail(FDEC_ERR_NULL, "w_out is NULL");
+    if (!aligned4(w_out)) return fail(FDEC_ERR_ALIGN, "w_out must be 4-byte aligned");
+    const Span O{w_out, size_t(W->K) * W->N * 4};
+    if (overlap(O, w4_qspan(W)) || overlap(O, w4_sspan(W))) return fail(FDEC_ERR_ALIAS, "w_out overlaps W");
+    if (g_fail_launches) return injected();
+    return hip_status(launch_w4_dequant(W->qweight, W->scales, W->K, W->N, w_out, static_cast<hipStream_t>(stream)),
+                      "dequant launch");
+}
+
+}  // extern "C"

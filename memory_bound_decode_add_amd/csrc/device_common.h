@@ -1,0 +1,86 @@
+// Device helpers shared by the fdec kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fdec {
+
+constexpr int kWave = 64;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  A bf16 pattern is the top half of an fp32 pattern, so widening
+// is a shift; narrowing uses gfx950's v_cvt_pk_bf16_f32 (round to nearest even).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two floats -> one word of two bf16 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// int4 decode.  A packed word holds weights j = 0..7 of one column in bits
+// [4j, 4j+4) as two's-complement nibbles.  XOR with 0x8 per nibble turns the code
+// into q + 8 (offset binary, 0..15).  OR-ing 4-bit fields into the mantissa of the
+// fp16 value 1024 (0x6400) gives exact fp16 numbers:
+//   bits 0..3 of a half  -> 1024 + (q + 8)        -> minus 1032            = q
+//   bits 4..7 of a half  -> 1024 + 16 (q + 8)     -> times 1/16, minus 72  = q
+// so one word becomes four half2 pairs of exact integer weights, ordered
+// (j0, j4), (j1, j5), (j2, j6), (j3, j7).  The activations are stored in the
+// same pair order, so a dot2 of matching pairs sums the right products.
+// ---------------------------------------------------------------------------
+struct Q4x2 { half2_t p04, p15, p26, p37; };
+
+__device__ __forceinline__ Q4x2 decode_int4x8(uint32_t w) {
+    const uint32_t x = w ^ 0x88888888u;
+    const uint32_t t = x >> 8;
+    const half2_t a = __builtin_bit_cast(half2_t, (x & 0x000F000Fu) | 0x64006400u);
+    const half2_t b = __builtin_bit_cast(half2_t, (x & 0x00F000F0u) | 0x64006400u);
+    const half2_t c = __builtin_bit_cast(half2_t, (t & 0x000F000Fu) | 0x64006400u);
+    const half2_t d = __builtin_bit_cast(half2_t, (t & 0x00F000F0u) | 0x64006400u);
+    const half2_t off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half2_t off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    Q4x2 q;
+    q.p04 = a + off_lo;
+    q.p15 = b * sixteenth + off_hi;   // exact: b/16 is an integer in [64, 79]
+    q.p26 = c + off_lo;
+    q.p37 = d * sixteenth + off_hi;
+    return q;
+}
+
+// Position of weight j (0..7) of a word in the pair order above.
+__host__ __device__ constexpr int pair_slot(int j) { return 2 * (j & 3) + (j >> 2); }
+
+__device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions (DPP / permute through the LDS crossbar, no LDS storage)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// SiLU in fp32: v / (1 + exp(-v)).  exp overflows to +inf for v < -88, giving -0.
+__device__ __forceinline__ float silu_f32(float v) {
+    return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+}
+
+}  // namespace fdec

@@ -1,0 +1,251 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects invalid calls before touching HIP.
+
+No call here reaches a kernel launch: every call either fails validation or runs with
+``fdec_test_fail_launches(1)``, which turns the launch into FDEC_ERR_HIP.  Pointers are
+fake device addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_bound_decode_add_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fdec.h")
+
+OK, NULL, SHAPE, ALIGN, ALIAS, WS, UNSUP, HIP, ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+pytestmark = pytest.mark.skipif(not os.path.exists(F.LIB_PATH), reason="libfdec.so not built")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return F.lib()
+
+
+@pytest.fixture
+def inject(L):
+    L.fdec_test_fail_launches(1)
+    yield
+    L.fdec_test_fail_launches(0)
+
+
+class Fake:
+    """Disjoint, 4 KB-aligned fake device addresses."""
+
+    def __init__(self):
+        self.next = 0x7F0000000000
+
+    def __call__(self, nbytes=1 << 20):
+        p = self.next
+        self.next += ((nbytes + 4095) // 4096 + 1) * 4096
+        return p
+
+
+def header_symbols():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"FDEC_API\s+[\w\s\*]+?\b(fdec_\w+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported_and_bound(L):
+    syms = header_symbols()
+    assert len(syms) >= 25
+    for s in syms:
+        assert hasattr(L, s), s
+    assert sorted(F.exported_symbols()) == syms
+
+
+def test_abi_version_matches_header(L):
+    v = int(re.search(r"#define FDEC_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.fdec_abi_version() == v
+
+
+def test_status_strings(L):
+    assert L.fdec_status_str(0) == b"FDEC_OK"
+    assert L.fdec_status_str(-5) == b"FDEC_ERR_WORKSPACE"
+    assert L.fdec_status_str(-99) == b"FDEC_ERR_UNKNOWN"
+
+
+def test_workspace_queries(L):
+    # the unfused product buffer: exactly M*K*N*4 bytes (about 94 MB at K=9216, N=2560)
+    assert L.fdec_unfused_gemv_workspace_bytes(0, 1, 9216, 2560) == 94_371_840
+    assert L.fdec_unfused_gemv_workspace_bytes(0, 2, 9216, 2560) == 0     # M > 1 unsupported
+    assert L.fdec_unfused_gemv_workspace_bytes(1, 1, 9216, 2560) >= 2 * 9216 * 2
+    assert L.fdec_w4_gemv_workspace_bytes(17, 1024, 512) == 0            # invalid shape
+    assert L.fdec_w4_gemv_workspace_bytes(1, 1000, 512) == 0
+    # the fused GEMV's own workspace stays far below the product it avoids
+    assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) < 0.02 * 94_371_840
+    for M in (1, 16):
+        assert L.fdec_mlp_workspace_bytes(M, 4096, 14336) >= max(
+            L.fdec_w4_gemv_workspace_bytes(M, 4096, 28672), L.fdec_w4_gemv_workspace_bytes(M, 14336, 4096))
+    assert L.fdec_unfused_add_rmsnorm_workspace_bytes(8192, 4096) >= 2 * 8192 * 4096 * 4
+
+
+def _norm(L, fake, x=None, r=None, w=None, eps=1e-6, M=4, H=512, h=None, y=None):
+    x = fake() if x is None else x
+    r = fake() if r is None else r
+    w = fake() if w is None else w
+    h = fake() if h is None else h
+    y = fake() if y is None else y
+    return L.fdec_add_rmsnorm(x, r, w, eps, M, H, h, y, None)
+
+
+def test_add_rmsnorm_validation(L, inject):
+    f = Fake()
+    assert _norm(L, f, x=0) == NULL
+    assert _norm(L, f, H=12) == SHAPE
+    assert _norm(L, f, H=16392) == SHAPE
+    assert _norm(L, f, M=-1) == SHAPE
+    assert _norm(L, f, eps=-1.0) == ARG
+    assert _norm(L, f, eps=float("nan")) == ARG
+    assert _norm(L, f, x=f() + 8) == ALIGN
+    x = f()
+    assert _norm(L, f, x=x, y=x) == ALIAS
+    r = f()
+    assert _norm(L, f, r=r, h=r + 256) == ALIAS           # partial overlap
+    assert _norm(L, f, r=r, h=r) == HIP                    # exact alias allowed -> reaches the launch
+    assert b"injected" in L.fdec_last_error()
+    assert _norm(L, f) == HIP
+
+
+def test_add_rmsnorm_empty_batch_enqueues_nothing(L):
+    f = Fake()
+    assert _norm(L, f, M=0) == OK
+
+
+def _w4(fake, K=1024, N=512, q=None, s=None):
+    return F.CW4(fake() if q is None else q, fake() if s is None else s, K, N)
+
+
+def _gemv(L, fake, W=None, g=None, u=None, ld=None, scale=None, res=None, M=1, y=None, ws=None, wsb=None):
+    W = _w4(fake) if W is None else W
+    need = L.fdec_w4_gemv_workspace_bytes(M, W.K, W.N)
+    g = fake() if g is None else g
+    u = fake() if u is None else u
+    y = fake() if y is None else y
+    ws = fake(max(need, 16)) if ws is None else ws
+    wsb = need if wsb is None else wsb
+    return L.fdec_swiglu_w4_gemv(g, u, W.K if ld is None else ld, ctypes.byref(W), scale, res, M, y, ws, wsb, None)
+
+
+def test_gemv_validation(L, inject):
+    f = Fake()
+    assert L.fdec_swiglu_w4_gemv(f(), f(), 1024, None, None, None, 1, f(), f(), 1 << 20, None) == NULL
+    assert _gemv(L, f, W=_w4(f, K=1000)) == SHAPE
+    assert _gemv(L, f, W=_w4(f, N=500)) == SHAPE
+    assert _gemv(L, f, W=_w4(f, q=0)) == NULL
+    assert _gemv(L, f, M=0) == SHAPE
+    assert _gemv(L, f, M=17) == SHAPE
+    assert _gemv(L, f, ld=1000) == SHAPE
+    assert _gemv(L, f, ld=1028) == SHAPE
+    assert _gemv(L, f, g=f() + 2) == ALIGN
+    assert _gemv(L, f, scale=f() + 2) == ALIGN
+    assert _gemv(L, f, g=0) == NULL
+    g = f()
+    assert _gemv(L, f, g=g, y=g + 16) == ALIAS
+    W = _w4(f)
+    assert _gemv(L, f, W=W, y=W.scales) == ALIAS
+    r = f()
+    assert _gemv(L, f, res=r, y=r + 32) == ALIAS
+    assert _gemv(L, f, res=r, y=r) == HIP                   # y == residual allowed
+    # workspace checks (a split-K shape)
+    need = L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560)
+    if need:
+        assert _gemv(L, f, W=_w4(f, K=9216, N=2560), wsb=need - 1) == WS
+        assert _gemv(L, f, W=_w4(f, K=9216, N=2560), ws=0) == NULL
+    assert _gemv(L, f) == HIP
+    assert _gemv(L, f, M=16, ld=2048) == HIP
+
+
+def test_gemv_split_override_changes_workspace(L):
+    base = L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560)
+    try:
+        L.fdec_set_gemv_split(1)
+        assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) < base or base == 0
+        L.fdec_set_gemv_split(18)
+        assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) > 0
+    finally:
+        L.fdec_set_gemv_split(0)
+    assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) == base
+
+
+def test_unfused_validation(L, inject):
+    f = Fake()
+    W = _w4(f, K=1024, N=512)
+    ws = f(1024 * 512 * 4)
+    assert L.fdec_unfused_swiglu_w4_gemv(0, f(), f(), 1024, ctypes.byref(W), None, None, 2, f(), ws,
+                                         1 << 30, None) == UNSUP
+    assert L.fdec_unfused_swiglu_w4_gemv(7, f(), f(), 1024, ctypes.byref(W), None, None, 1, f(), ws,
+                                         1 << 30, None) == ARG
+    assert L.fdec_unfused_swiglu_w4_gemv(0, f(), f(), 1024, ctypes.byref(W), None, None, 1, f(), ws,
+                                         1024 * 512 * 4 - 1, None) == WS
+    assert L.fdec_unfused_swiglu_w4_gemv(0, f(), f(), 1024, ctypes.byref(W), None, None, 1, f(), ws,
+                                         1024 * 512 * 4, None) == HIP
+    need = L.fdec_unfused_add_rmsnorm_workspace_bytes(4, 512)
+    assert L.fdec_unfused_add_rmsnorm(f(), f(), f(), 1e-6, 4, 512, f(), f(), f(need), need - 1, None) == WS
+    assert L.fdec_unfused_add_rmsnorm(f(), f(), f(), 1e-6, 4, 512, f(), f(), f(need), need, None) == HIP
+
+
+def _layer(f, H=512, I=1024, **kw):
+    return F.CLayer(f(), kw.get("eps", 1e-6), F.CW4(f(), f(), H, 2 * I), F.CW4(f(), f(), I, H),
+                    kw.get("scale", f()), kw.get("resid", 1))
+
+
+def test_layer_validation(L, inject):
+    f = Fake()
+    M, H, I = 2, 512, 1024
+    need = L.fdec_mlp_workspace_bytes(M, H, I)
+    lay = _layer(f, H, I)
+
+    def call(layer=lay, x=None, r=None, yn=None, gu=None, out=None, ws=None, wsb=None, m=M):
+        x = f() if x is None else x
+        return L.fdec_mlp_decode(ctypes.byref(layer), m, x, f() if r is None else r, f() if yn is None else yn,
+                                 f() if gu is None else gu, f() if out is None else out,
+                                 f(max(16, need)) if ws is None else ws, need if wsb is None else wsb, None)
+
+    assert call() == HIP
+    x = f()
+    assert call(x=x, out=x) == HIP                      # out == x allowed
+    assert call(x=x, out=x + 16) == ALIAS
+    bad = F.CLayer(f(), 1e-6, F.CW4(f(), f(), H, 2 * I), F.CW4(f(), f(), I, H + 128), None, 1)
+    assert call(layer=bad) == SHAPE
+    bad = F.CLayer(0, 1e-6, F.CW4(f(), f(), H, 2 * I), F.CW4(f(), f(), I, H), None, 1)
+    assert call(layer=bad) == NULL
+    if need:
+        assert call(wsb=need - 1) == WS
+    assert call(m=17) == SHAPE
+    # chains: only the last layer may add the residual
+    arr = (F.CLayer * 2)(_layer(f, H, I, resid=1), _layer(f, H, I, resid=0))
+    assert L.fdec_mlp_chain(arr, 2, M, f(), f(), f(), f(), f(max(16, need)), need, None) == ARG
+    arr = (F.CLayer * 2)(_layer(f, H, I, resid=0), _layer(f, H, I, resid=1))
+    assert L.fdec_mlp_chain(arr, 2, M, f(), f(), f(), f(), f(max(16, need)), need, None) == HIP
+    g = ctypes.c_void_p()
+    assert L.fdec_mlp_graph_create(arr, 2, M, f(), f(), f(), f(), f(max(16, need)), need, None,
+                                   ctypes.byref(g)) == ARG      # null stream cannot be captured
+    assert L.fdec_mlp_graph_create(arr, 0, M, f(), f(), f(), f(), f(max(16, need)), need, f(),
+                                   ctypes.byref(g)) == SHAPE
+
+
+def test_hooks_validation(L, inject):
+    f = Fake()
+    W = _w4(f)
+    assert L.fdec_w4_unpack(ctypes.byref(W), 0, None) == NULL
+    assert L.fdec_w4_unpack(ctypes.byref(W), W.qweight + 64, None) == ALIAS
+    assert L.fdec_w4_dequant(ctypes.byref(W), f() + 2, None) == ALIGN
+    assert L.fdec_w4_dequant(ctypes.byref(W), f(), None) == HIP
+    assert L.fdec_workspace_init(0, 64, None) == NULL
+    assert L.fdec_workspace_init(0, 0, None) == OK
+    assert L.fdec_graph_launch(None, None) == NULL
+    assert L.fdec_graph_destroy(None) == OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        F.add_rmsnorm(x, x.clone(), torch.ones(512, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        F.add_rmsnorm(x.float(), x.clone(), torch.ones(512, dtype=torch.bfloat16))

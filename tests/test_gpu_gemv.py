@@ -1,0 +1,187 @@
+"""GPU parity of the int4 decode and the SwiGLU-prologue / identity GEMVs against the
+fp64 oracle (through the C ABI, via the ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_decode_add_amd as F
+import oracle as O
+import synth
+from helpers import assert_bits_equal, assert_close, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def to_dev(inp: synth.GemvInputs):
+    return (F.from_bits(inp.g), F.from_bits(inp.u), F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales),
+            None if inp.residual is None else F.from_bits(inp.residual))
+
+
+def run_gemv(inp, out_scale=None, residual=True, ws=None):
+    g, u, W, res = to_dev(inp)
+    s = None if out_scale is None else F.scalar(out_scale)
+    y = F.swiglu_w4_gemv(g, u, W, s, res if residual else None, ws=ws)
+    torch.cuda.synchronize()
+    return F.to_bits(y)
+
+
+# ---------------------------------------------------------------------------
+# int4 decode: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("K,N", [(1024, 512), (9216, 2560), (256, 8)])
+def test_unpack_and_dequant_bit_exact(K, N):
+    say(f"[unpack/dequant] K={K} N={N}")
+    W = synth.w4_weight(np.random.default_rng(K + N), K, N)
+    Wd = F.W4Weight.from_numpy(W.qweight, W.scales)
+    q = F.w4_unpack(Wd).cpu().numpy()
+    w = F.w4_dequant(Wd).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(q, O.w4_unpack(W.qweight))
+    ref = O.w4_dequant(W.qweight, W.scales)
+    assert np.array_equal(w.astype(np.float64), ref)
+
+
+def test_unpack_every_code_in_every_position():
+    say("[unpack] all codes")
+    k, n = np.meshgrid(np.arange(128), np.arange(64), indexing="ij")
+    q = (((k + n) % 16) - 8).astype(np.int8)          # every code at every nibble position
+    words = synth.pack_int4(q)
+    sc = np.full((1, 64), 0x3F80, dtype=np.uint16)
+    Wd = F.W4Weight.from_numpy(words, sc)
+    got = F.w4_unpack(Wd).cpu().numpy()
+    assert np.array_equal(got, q)
+
+
+# ---------------------------------------------------------------------------
+# the SwiGLU GEMV
+# ---------------------------------------------------------------------------
+def test_swiglu_gemv_small_config():
+    say("[gemv] M=1 K=1024 N=512 scale 0.5 seed 0")
+    inp = synth.make("swiglu_w4_gemv_1x1024x512")
+    y = run_gemv(inp, inp.out_scale)
+    ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, inp.out_scale)
+    say("  worst err/bound", assert_close(y, ref, "C1"))
+
+
+def test_swiglu_gemv_decode_shape_full():
+    say("[gemv] M=1 K=9216 N=2560 scale 1.0 seed 0 (default split)")
+    inp = synth.make("swiglu_w4_gemv_1x9216x2560")
+    y = run_gemv(inp, inp.out_scale)
+    ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, inp.out_scale)
+    say("  worst err/bound", assert_close(y, ref, "C2"))
+    y2 = run_gemv(inp, inp.out_scale)
+    assert_bits_equal(y, y2, "C2 repeat (determinism)")
+
+
+@pytest.mark.parametrize("split", [1, 2, 5, 9, 18, 72])
+def test_swiglu_gemv_every_split(split):
+    say(f"[gemv] M=1 K=9216 N=2560 forced split {split}")
+    inp = synth.make("swiglu_w4_gemv_1x9216x2560")
+    ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 1.0)
+    try:
+        F.set_gemv_split(split)
+        y = run_gemv(inp, 1.0)
+        y2 = run_gemv(inp, 1.0)
+    finally:
+        F.set_gemv_split(0)
+    assert_close(y, ref, f"split {split}")
+    assert_bits_equal(y, y2, f"split {split} repeat")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 8), (3, 384, 520), (5, 1280, 136), (16, 2048, 1032),
+                                   (2, 256, 4104), (8, 4096, 776), (16, 14336, 128)])
+def test_swiglu_gemv_ragged_shapes_with_residual(M, K, N):
+    say(f"[gemv] ragged M={M} K={K} N={N} with residual")
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=M * 7 + K + N, out_scale=0.75, with_residual=True)
+    y = run_gemv(inp, 0.75, residual=True)
+    ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 0.75, inp.residual)
+    assert_close(y, ref, f"M={M} K={K} N={N}")
+
+
+def test_swiglu_gemv_strided_rows_and_null_scale():
+    say("[gemv] g, u as halves of one [M, 2K] buffer; out_scale NULL")
+    M, K, N = 4, 1024, 264
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=3)
+    gu = np.concatenate([inp.g, inp.u], axis=1)
+    t = F.from_bits(gu)
+    W = F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales)
+    y = F.to_bits(F.swiglu_w4_gemv(t[:, :K], t[:, K:], W, None))
+    ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 1.0)
+    assert_close(y, ref, "strided")
+
+
+def test_swiglu_gemv_output_scale_matrix():
+    """The folded scale: a value changed in device memory is read at launch."""
+    say("[gemv] output-scale matrix")
+    inp = synth.swiglu_gemv_inputs(1, 2048, 512, seed=5)
+    g, u, W, _ = to_dev(inp)
+    s = F.scalar(1.0)
+    for v in (0.0, 2.0**-3, 0.5, 1.0, 3.7):
+        s.fill_(v)
+        y = F.to_bits(F.swiglu_w4_gemv(g, u, W, s))
+        ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, v)
+        if v == 0.0:
+            assert np.all(O.bf16_to_f64(y) == 0)
+        else:
+            assert_close(y, ref, f"scale {v}")
+
+
+def _exact_case(M, K, N, seed):
+    """g in {0, 32}, u in {-1, 0, 1}, power-of-two scales: every partial sum is exact in
+    fp32 (see the bound below), so the GPU must match exact rational arithmetic."""
+    rng = np.random.default_rng(seed)
+    g = rng.choice([0.0, 32.0], size=(M, K)).astype(np.float32)
+    u = rng.integers(-1, 2, size=(M, K)).astype(np.float32)
+    q = rng.integers(-8, 8, size=(K, N)).astype(np.int8)
+    s = rng.choice([2.0**-6, 2.0**-7], size=(K // 128, N)).astype(np.float32)
+    exact = (g.astype(np.float64) * u) @ (q.astype(np.float64) * np.repeat(s, 128, axis=0))
+    # silu(32) = 32 and silu(0) = 0 exactly in fp32.  A group's largest |act| = 32 is stored
+    # as 2^14 (scale 2^-9), so every per-lane dot is a multiple of 2^14 below 2^22, and every
+    # scaled partial sum a multiple of 2^14 * 2^-7 * 2^-9 = 2^-2 bounded by
+    # sum |act q s| <= 32 * 8 * 2^-6 * K = 4K.  fp32 holds all of them exactly if 4K / 2^-2 < 2^24.
+    assert 16 * K < 2**24
+    return (synth.f32_to_bf16_bits(g), synth.f32_to_bf16_bits(u), synth.pack_int4(q),
+            synth.f32_to_bf16_bits(s), exact)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 512), (1, 9216, 2560), (4, 2048, 256)])
+def test_swiglu_gemv_exact_special_cases_bit_exact(M, K, N):
+    say(f"[gemv] exact special case M={M} K={K} N={N}")
+    gb, ub, qw, sb, exact = _exact_case(M, K, N, seed=K + N)
+    W = F.W4Weight.from_numpy(qw, sb)
+    for scale in (0.5, 1.0):
+        y = F.to_bits(F.swiglu_w4_gemv(F.from_bits(gb), F.from_bits(ub), W, F.scalar(scale)))
+        want = O.f64_to_bf16(exact * scale)     # exact value, one rounding
+        assert_bits_equal(y, want, f"exact scale={scale}")
+
+
+# ---------------------------------------------------------------------------
+# the identity-prologue GEMV (gate_up)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", [(1, 1536, 17920), (16, 4096, 28672), (3, 640, 392)])
+def test_w4_gemv_identity(M, K, N):
+    say(f"[gemv identity] M={M} K={K} N={N}")
+    rng = np.random.default_rng(M + K + N)
+    x = synth._normal_bf16(rng, (M, K))
+    W = synth.w4_weight(rng, K, N)
+    y = F.to_bits(F.w4_gemv(F.from_bits(x), F.W4Weight.from_numpy(W.qweight, W.scales)))
+    torch.cuda.synchronize()
+    ref = O.f64_to_bf16(O._chunked_gemv(O.bf16_to_f64(x), W.qweight, W.scales, 4096))
+    assert_close(y, ref, "identity")
+
+
+def test_w4_gemv_identity_large_dynamic_range():
+    """Activations far outside fp16's range still work (per-group power-of-two scaling)."""
+    say("[gemv identity] large dynamic range")
+    M, K, N = 2, 1024, 256
+    rng = np.random.default_rng(11)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    xf[0] *= 1e6          # beyond fp16's 65504
+    xf[1] *= 1e-6         # deep in fp16's subnormal range
+    x = synth.f32_to_bf16_bits(xf)
+    W = synth.w4_weight(rng, K, N)
+    y = F.to_bits(F.w4_gemv(F.from_bits(x), F.W4Weight.from_numpy(W.qweight, W.scales)))
+    ref = O.w4_gemv(x, W.qweight, W.scales)
+    for m in range(M):
+        assert_close(y[m:m + 1], ref[m:m + 1], f"row {m}")

@@ -1,0 +1,147 @@
+"""GPU parity of the three-kernel decode-MLP layer, the multi-layer chain and its
+hipGraph capture, against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_decode_add_amd as F
+import oracle as O
+import synth
+from helpers import assert_bits_equal, assert_close, say
+
+pytestmark = pytest.mark.gpu
+
+
+def dev_layers(inp: synth.MlpInputs, residual_in_epilogue):
+    out = []
+    for L in inp.layers:
+        out.append(F.MlpLayer(F.from_bits(L.norm_w), F.W4Weight.from_numpy(L.gate_up.qweight, L.gate_up.scales),
+                              F.W4Weight.from_numpy(L.down.qweight, L.down.scales), F.scalar(L.out_scale),
+                              L.eps, residual_in_epilogue))
+    return out
+
+
+def check_layer(L, x, r, got, resid):
+    """Oracle for one layer fed with the same bf16 inputs the GPU layer read."""
+    ref = O.mlp_decode(x, r, L.norm_w, L.gate_up.qweight, L.gate_up.scales, L.down.qweight, L.down.scales,
+                       L.out_scale, L.eps, residual_in_epilogue=resid)
+    assert_bits_equal(got["h"], ref["h"], "h")
+    w = [assert_close(got["y"], ref["y"], "y"), assert_close(got["gu"], ref["gu"], "gate_up"),
+         assert_close(got["out"], ref["out"], "out")]
+    return w
+
+
+def test_mlp_layer_llama3_8b_m16():
+    say("[mlp] M=16 H=4096 I=14336, residual in the epilogue")
+    inp = synth.make("mlp_llama3_8b_m16")
+    layer = dev_layers(inp, True)[0]
+    b = F.MlpBuffers.empty(16, 4096, 14336)
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    F.mlp_decode(layer, b)
+    torch.cuda.synchronize()
+    got = {"h": F.to_bits(b.residual), "y": F.to_bits(b.y_norm), "gu": F.to_bits(b.gate_up),
+           "out": F.to_bits(b.out)}
+    say("  worst err/bound (y, gu, out)", check_layer(inp.layers[0], inp.x, inp.r, got, True))
+
+
+@pytest.mark.parametrize("M,H,I", [(1, 256, 384), (3, 512, 640), (16, 384, 256)])
+def test_mlp_layer_small_shapes_both_residual_modes(M, H, I):
+    say(f"[mlp] M={M} H={H} I={I}")
+    inp = synth.mlp_inputs(M, H, I, n_layers=1, seed=M + H + I)
+    for resid in (True, False):
+        layer = dev_layers(inp, resid)[0]
+        b = F.MlpBuffers.empty(M, H, I)
+        b.x.copy_(F.from_bits(inp.x))
+        b.residual.copy_(F.from_bits(inp.r))
+        F.mlp_decode(layer, b)
+        got = {"h": F.to_bits(b.residual), "y": F.to_bits(b.y_norm), "gu": F.to_bits(b.gate_up),
+               "out": F.to_bits(b.out)}
+        check_layer(inp.layers[0], inp.x, inp.r, got, resid)
+
+
+def test_chain_small_matches_oracle_chain():
+    say("[chain] M=1 H=256 I=512, 4 layers, eager and graph")
+    inp = synth.mlp_inputs(1, 256, 512, n_layers=4, seed=21)
+    layers = dev_layers(inp, False)
+    xr, rr = O.mlp_chain(inp.x, inp.r, inp.layers)
+    b = F.MlpBuffers.empty(1, 256, 512, out_is_x=True)
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    F.mlp_chain(layers, b)
+    assert_close(F.to_bits(b.x), xr, "x_L")
+    assert_close(F.to_bits(b.residual), rr, "r_L")
+
+
+def run_layers_eagerly(inp, layers, M, H, I):
+    """Run the chain layer by layer, keeping every layer's inputs and outputs."""
+    b = F.MlpBuffers.empty(M, H, I, out_is_x=True)
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    ws = F.workspace(F.mlp_workspace_bytes(M, H, I))
+    trace = []
+    for L in layers:
+        xin, rin = F.to_bits(b.x), F.to_bits(b.residual)
+        F.mlp_decode(L, b, ws)
+        torch.cuda.synchronize()
+        trace.append({"x": xin, "r": rin, "h": F.to_bits(b.residual), "y": F.to_bits(b.y_norm),
+                      "gu": F.to_bits(b.gate_up), "out": F.to_bits(b.x)})
+    return trace
+
+
+def test_chain_qwen2_5_1_5b_28_layers_graph():
+    say("[chain] M=1 H=1536 I=8960, 28 layers: per-layer parity, graph == eager")
+    inp = synth.make("mlp_qwen2_5_1_5b_28l")
+    M, H, I = 1, 1536, 8960
+    layers = dev_layers(inp, False)
+    trace = run_layers_eagerly(inp, layers, M, H, I)
+    for l in (0, 1, 13, 27):
+        say(f"  layer {l}")
+        t = trace[l]
+        check_layer(inp.layers[l], t["x"], t["r"], t, False)
+
+    # the same chain through one eager call and through a captured graph
+    b = F.MlpBuffers.empty(M, H, I, out_is_x=True)
+    ws = F.workspace(F.mlp_workspace_bytes(M, H, I))
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    F.mlp_chain(layers, b, ws)
+    torch.cuda.synchronize()
+    assert_bits_equal(F.to_bits(b.x), trace[-1]["out"], "chain x")
+    assert_bits_equal(F.to_bits(b.residual), trace[-1]["h"], "chain r")
+
+    graph = F.MlpGraph(layers, b, ws)
+    assert graph.kernel_count == 3 * 28
+    for rep in range(3):
+        b.x.copy_(F.from_bits(inp.x))
+        b.residual.copy_(F.from_bits(inp.r))
+        graph.launch()
+        torch.cuda.synchronize()
+        assert_bits_equal(F.to_bits(b.x), trace[-1]["out"], f"graph replay {rep} x")
+        assert_bits_equal(F.to_bits(b.residual), trace[-1]["h"], f"graph replay {rep} r")
+        # unrelated eager work between replays
+        torch.randn(1 << 20, device="cuda").sum().item()
+    graph.close()
+
+
+def test_graph_reads_scale_at_replay():
+    say("[graph] out_scale changed in device memory between replays")
+    inp = synth.mlp_inputs(1, 256, 384, n_layers=2, seed=31)
+    layers = dev_layers(inp, False)
+    b = F.MlpBuffers.empty(1, 256, 384, out_is_x=True)
+    graph = F.MlpGraph(layers, b)
+    outs = {}
+    for v in (0.5, 2.0):
+        for L in layers:
+            L.out_scale.fill_(v)
+        b.x.copy_(F.from_bits(inp.x))
+        b.residual.copy_(F.from_bits(inp.r))
+        graph.launch()
+        torch.cuda.synchronize()
+        outs[v] = F.to_bits(b.x)
+        for L in inp.layers:
+            L.out_scale = v
+        xr, _ = O.mlp_chain(inp.x, inp.r, inp.layers)
+        assert_close(outs[v], xr, f"scale {v}")
+    assert not np.array_equal(outs[0.5], outs[2.0])
+    graph.close()

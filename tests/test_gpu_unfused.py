@@ -1,0 +1,66 @@
+"""GPU parity of the unfused reference sequences against the oracle's unfused forms."""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_decode_add_amd as F
+import oracle as O
+import synth
+from helpers import assert_close, assert_bits_equal, say
+from test_gpu_mlp import dev_layers
+
+pytestmark = pytest.mark.gpu
+
+
+def test_unfused_product_decode_shape():
+    say("[unfused product] M=1 K=9216 N=2560")
+    inp = synth.make("swiglu_w4_gemv_1x9216x2560")
+    g, u = F.from_bits(inp.g), F.from_bits(inp.u)
+    W = F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales)
+    assert F.unfused_gemv_workspace_bytes(F.UNFUSED_PRODUCT, 1, 9216, 2560) == 94_371_840
+    y = F.to_bits(F.unfused_swiglu_w4_gemv(F.UNFUSED_PRODUCT, g, u, W, F.scalar(1.0)))
+    torch.cuda.synchronize()
+    assert_close(y, O.unfused_product_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 1.0), "product")
+    # and against the fused definition
+    assert_close(y, O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 1.0), "product vs fused")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 512), (4, 2048, 264)])
+def test_unfused_act(M, K, N):
+    say(f"[unfused act] M={M} K={K} N={N}")
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=2, with_residual=True)
+    g, u = F.from_bits(inp.g), F.from_bits(inp.u)
+    W = F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales)
+    res = F.from_bits(inp.residual)
+    y = F.to_bits(F.unfused_swiglu_w4_gemv(F.UNFUSED_ACT, g, u, W, F.scalar(0.5), res))
+    torch.cuda.synchronize()
+    ref = O.unfused_act_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 0.5, inp.residual)
+    assert_close(y, ref, "act")
+
+
+def test_unfused_add_rmsnorm():
+    say("[unfused norm] M=256 H=4096")
+    inp = synth.add_rmsnorm_inputs(256, 4096, seed=3)
+    h, y = F.unfused_add_rmsnorm(F.from_bits(inp.x), F.from_bits(inp.r), F.from_bits(inp.w), inp.eps)
+    torch.cuda.synchronize()
+    rh, ry = O.add_rmsnorm_eager(inp.x, inp.r, inp.w, inp.eps)
+    assert_bits_equal(F.to_bits(h), rh, "h")
+    assert_close(F.to_bits(y), ry, "y")
+
+
+def test_unfused_mlp_layer():
+    say("[unfused mlp] M=4 H=512 I=1024")
+    inp = synth.mlp_inputs(4, 512, 1024, n_layers=1, seed=4)
+    layer = dev_layers(inp, True)[0]
+    b = F.MlpBuffers.empty(4, 512, 1024)
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    F.unfused_mlp_decode(layer, b)
+    torch.cuda.synchronize()
+    L = inp.layers[0]
+    ref = O.mlp_decode_unfused(inp.x, inp.r, L.norm_w, L.gate_up.qweight, L.gate_up.scales, L.down.qweight,
+                               L.down.scales, L.out_scale, L.eps, residual_in_epilogue=True)
+    assert_bits_equal(F.to_bits(b.residual), ref["h"], "h")
+    assert_close(F.to_bits(b.y_norm), ref["y"], "y")
+    assert_close(F.to_bits(b.gate_up), ref["gu"], "gu")
+    assert_close(F.to_bits(b.out), ref["out"], "out")
