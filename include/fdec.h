@@ -130,7 +130,8 @@ FDEC_API int fdec_workspace_init(void* ws, size_t ws_bytes, fdec_stream stream);
  *   h = bf16(x + residual)                                   (the new residual)
  *   y = bf16(h * weight / sqrt(mean_H(h * h) + eps))          (computed in fp32)
  *   x, residual, h_out, y_out: bf16 [M][H];  weight: bf16 [H].
- *   M >= 0 (M == 0 enqueues nothing);  8 <= H <= 16384, H % 8 == 0;  eps >= 0, finite.
+ *   M >= 0 (M == 0 enqueues nothing, and x, residual, h_out, y_out may then be NULL);
+ *   8 <= H <= 16384, H % 8 == 0;  eps >= 0, finite.
  *   h_out may equal residual (in-place residual update); no other overlap allowed.
  */
 FDEC_API int fdec_add_rmsnorm(const fdec_bf16* x, const fdec_bf16* residual,

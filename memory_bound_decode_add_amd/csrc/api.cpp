@@ -78,11 +78,13 @@ int check_m(int M) {
 
 int check_norm(const fdec_bf16* x, const fdec_bf16* residual, const fdec_bf16* weight, float eps,
                int M, int H, const fdec_bf16* h_out, const fdec_bf16* y_out) {
-    if (!x || !residual || !weight || !h_out || !y_out)
-        return fail(FDEC_ERR_NULL, "add_rmsnorm: x, residual, weight, h_out and y_out are required");
     if (M < 0) return fail(FDEC_ERR_SHAPE, "M = %d must be >= 0", M);
     if (H < 8 || H > 16384 || H % 8) return fail(FDEC_ERR_SHAPE, "H = %d must be a multiple of 8 in [8, 16384]", H);
     if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(FDEC_ERR_ARG, "eps must be finite and >= 0");
+    if (!weight) return fail(FDEC_ERR_NULL, "add_rmsnorm: weight is required");
+    if (M == 0) return FDEC_OK;   // empty batch: the [0, H] tensors may be NULL
+    if (!x || !residual || !h_out || !y_out)
+        return fail(FDEC_ERR_NULL, "add_rmsnorm: x, residual, h_out and y_out are required");
     if (!aligned16(x) || !aligned16(residual) || !aligned16(weight) || !aligned16(h_out) || !aligned16(y_out))
         return fail(FDEC_ERR_ALIGN, "add_rmsnorm: every tensor must be 16-byte aligned");
     const size_t t = size_t(M) * H * 2;

@@ -39,13 +39,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ---------------------------------------------------------------------------
 struct Q4x2 { half2_t p04, p15, p26, p37; };
 
+// (x & mask) | bits in one VOP3 instruction.  CDNA's VOP3 encoding takes no literal
+// constants and at most one scalar operand, so the mask comes from a scalar register
+// and the OR-ed bits from a vector register (left to the compiler to materialise once).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));
+    return r;
+}
+
+// w ^ bits, kept opaque to the optimiser: a plain XOR of a conditionally loaded word
+// gets folded into the load's branch, which forces a wait for the load right there.
+__device__ __forceinline__ uint32_t xor_opaque(uint32_t w, uint32_t bits) {
+    uint32_t r;
+    asm("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(bits), "v"(w));
+    return r;
+}
+
 __device__ __forceinline__ Q4x2 decode_int4x8(uint32_t w) {
-    const uint32_t x = w ^ 0x88888888u;
+    const uint32_t x = xor_opaque(w, 0x88888888u);
     const uint32_t t = x >> 8;
-    const half2_t a = __builtin_bit_cast(half2_t, (x & 0x000F000Fu) | 0x64006400u);
-    const half2_t b = __builtin_bit_cast(half2_t, (x & 0x00F000F0u) | 0x64006400u);
-    const half2_t c = __builtin_bit_cast(half2_t, (t & 0x000F000Fu) | 0x64006400u);
-    const half2_t d = __builtin_bit_cast(half2_t, (t & 0x00F000F0u) | 0x64006400u);
+    const uint32_t one024 = 0x64006400u;
+    const half2_t a = __builtin_bit_cast(half2_t, and_or(x, 0x000F000Fu, one024));
+    const half2_t b = __builtin_bit_cast(half2_t, and_or(x, 0x00F000F0u, one024));
+    const half2_t c = __builtin_bit_cast(half2_t, and_or(t, 0x000F000Fu, one024));
+    const half2_t d = __builtin_bit_cast(half2_t, and_or(t, 0x00F000F0u, one024));
     const half2_t off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const half2_t off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
     const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
@@ -76,6 +94,38 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
     return v;
+}
+
+// DPP lane moves (gfx9 encodings): quad permutations and rotations within a row of 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+
+// Sum over the four lanes of each quad; every lane of the quad gets the sum.
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp<kQuadSwap1>(v);
+    v += dpp<kQuadSwap2>(v);
+    return v;
+}
+
+// Maximum over a full wave (all 64 lanes active), returned uniform: DPP within each row
+// of 16 lanes, then the four row results read as scalars.
+__device__ __forceinline__ float wave_max_uniform(float v) {
+    v = fmaxf(v, dpp<kQuadSwap1>(v));
+    v = fmaxf(v, dpp<kQuadSwap2>(v));
+    v = fmaxf(v, dpp<kRowRor4>(v));
+    v = fmaxf(v, dpp<kRowRor8>(v));
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // SiLU in fp32: v / (1 + exp(-v)).  exp overflows to +inf for v < -88, giving -0.

@@ -11,7 +11,7 @@
 //
 // Work decomposition.  A 256-thread workgroup owns a 64-column tile and a slice of
 // whole 128-wide K groups (a "split").  Wave w of the workgroup owns groups
-// w, w+4, ... of the slice.  Lane (cq = lane % 16, kr = lane / 16) owns columns
+// w, w+4, ... of the slice.  Lane (kr = lane % 4, cq = lane / 4) owns columns
 // 4cq..4cq+3 and packed rows 4kr..4kr+3 of each of its wave's groups, loading each
 // packed row of its four columns with one 16-byte load: one load instruction of a
 // wave covers four 256-byte runs of the weight matrix.  Every weight load of the
@@ -30,12 +30,13 @@
 // against the activations in fp32.  The group scale (times 2^E) multiplies the
 // lane's 32-element partial sum once per group.
 //
-// Reduction.  Lanes sharing columns are summed with cross-lane shuffles, waves through
-// LDS.  With one split the workgroup applies the epilogue directly.  With several,
-// each workgroup writes fp32 partial sums for its tile to the workspace, then bumps
-// the tile's arrival counter (device-scope atomic after a device-scope release
-// fence); the last workgroup to arrive sums the partials in split order (so results
-// do not depend on arrival order), applies the epilogue and resets the counter.
+// Reduction.  The four lanes sharing columns form a quad and are summed with DPP; the
+// four waves through LDS.  With one split the workgroup applies the epilogue directly.  With several,
+// each workgroup writes fp32 partial sums for its tile to the workspace with
+// device-scope atomic stores, waits for them to complete, then bumps the tile's
+// arrival counter; the last workgroup to arrive reads the partials back with
+// device-scope atomic loads, sums them in split order (so results do not depend on
+// arrival order), applies the epilogue and resets the counter.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -84,8 +85,8 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
     const int split = blockIdx.x / a.tiles;
     const int g0 = split * a.gps;
     const int ng = min(a.gps, a.groups - g0);
-    const int cq = lane & 15;
-    const int kr = lane >> 4;
+    const int kr = lane & 3;          // the four lanes of a quad share columns
+    const int cq = lane >> 2;
     const int col = tile * kGemvCols + cq * 4;
     const bool col_ok = col < a.N;
     const int nq = a.N >> 2;
@@ -94,19 +95,19 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
     constexpr int T = MR * GW;
     constexpr int B = T < 8 ? T : 8;
     uint32_t ga[B], ua[B];
+    // Every load below is unconditional, from an address clamped into the tensor: a
+    // task or group outside the slice re-reads a valid location and its value is never
+    // used.  Without branches around the loads, the compiler's wait counting can let
+    // the prologue start as soon as its own (first-issued) loads arrive.
     auto load_batch = [&](int b0) {
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             const int t = b0 + b;
-            const int i = t / MR, m = t % MR;
-            const int lg = wave + 4 * i;
-            ga[b] = 0u;
-            ua[b] = 0u;
-            if (t < T && lg < ng && m < a.M) {
-                const size_t off = size_t(m) * a.lda + size_t(g0 + lg) * kGroup + 2 * lane;
-                ga[b] = *reinterpret_cast<const uint32_t*>(a.a0 + off);
-                if (PRO == kSwiGLU) ua[b] = *reinterpret_cast<const uint32_t*>(a.a1 + off);
-            }
+            const int i = t / MR, m = min(t % MR, a.M - 1);
+            const int lg = min(wave + 4 * i, ng - 1);
+            const size_t off = size_t(m) * a.lda + size_t(g0 + lg) * kGroup + 2 * lane;
+            ga[b] = *reinterpret_cast<const uint32_t*>(a.a0 + off);
+            ua[b] = PRO == kSwiGLU ? *reinterpret_cast<const uint32_t*>(a.a1 + off) : 0u;
         }
     };
     load_batch(0);
@@ -114,23 +115,20 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
     // ---- weights and scales of this wave's groups, all in flight at once ----
     uint4 wv[GW][4];
     uint2 sv[GW];
+    const int colc = col_ok ? col : 0;
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
-        const int lg = wave + 4 * i;
-        if (lg < ng && col_ok) {
-            const int g = g0 + lg;
+        const int g = g0 + min(wave + 4 * i, ng - 1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const size_t kb = size_t(g) * 16 + kr * 4 + j;
-                wv[i][j] = a.qw[kb * nq + (col >> 2)];
-            }
-            sv[i] = *reinterpret_cast<const uint2*>(a.sc + size_t(g) * a.N + col);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wv[i][j] = make_uint4(0u, 0u, 0u, 0u);   // code 0 = weight 0
-            sv[i] = make_uint2(0u, 0u);
+        for (int j = 0; j < 4; ++j) {
+            const size_t kb = size_t(g) * 16 + kr * 4 + j;
+            wv[i][j] = a.qw[kb * nq + (colc >> 2)];
         }
+        sv[i] = *reinterpret_cast<const uint2*>(a.sc + size_t(g) * a.N + colc);
     }
+    // Keep the weight decode below the prologue: the prologue needs only the (earlier)
+    // activation loads, so the weights stay in flight while it runs.
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- prologue: activations to LDS as block-scaled fp16 ----
 #pragma unroll
@@ -142,15 +140,17 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
             const int i = t / MR, m = t % MR;
             const int lg = wave + 4 * i;
             if (t >= T || lg >= ng) continue;          // uniform across the wave
-            float v0, v1;
-            if (PRO == kSwiGLU) {
-                v0 = silu_f32(bf16_lo(ga[b])) * bf16_lo(ua[b]);
-                v1 = silu_f32(bf16_hi(ga[b])) * bf16_hi(ua[b]);
-            } else {
-                v0 = bf16_lo(ga[b]);
-                v1 = bf16_hi(ga[b]);
+            float v0 = 0.f, v1 = 0.f;
+            if (m < a.M) {                                // uniform; rows past M stay zero
+                if (PRO == kSwiGLU) {
+                    v0 = silu_f32(bf16_lo(ga[b])) * bf16_lo(ua[b]);
+                    v1 = silu_f32(bf16_hi(ga[b])) * bf16_hi(ua[b]);
+                } else {
+                    v0 = bf16_lo(ga[b]);
+                    v1 = bf16_hi(ga[b]);
+                }
             }
-            const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+            const float mx = wave_max_uniform(fmaxf(fabsf(v0), fabsf(v1)));
             int e = 0;
             (void)__builtin_frexpf(mx, &e);
             const int E = min(max(e - 15, -126), 127);
@@ -162,7 +162,10 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
             if (lane == 0) esc_s[lg * MR + m] = __builtin_ldexpf(1.0f, E);
         }
     }
-    __syncthreads();
+    // Each wave reads back only the groups it wrote; LDS operations of one wave complete
+    // in order, so a wave-level scheduling barrier suffices.
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- dot products ----
     float acc[MR][4];
@@ -214,16 +217,11 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
         }
     }
 
-    // ---- reduce: lanes with the same columns, then the four waves ----
+    // ---- reduce: the quad's lanes (same columns), then the four waves ----
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float v = acc[m][c];
-            v += __shfl_xor(v, 16, kWave);
-            v += __shfl_xor(v, 32, kWave);
-            acc[m][c] = v;
-        }
+        for (int c = 0; c < 4; ++c) acc[m][c] = quad_sum(acc[m][c]);
     if (kr == 0) {
 #pragma unroll
         for (int m = 0; m < MR; ++m)
@@ -244,32 +242,74 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
             const size_t o = size_t(m) * a.N + n;
             a.y[o] = f32_to_bf16(epilogue(v, s, a.residual, o));
         } else {
-            a.partial[(size_t(split) * a.M + m) * npad + n] = v;
+            __hip_atomic_store(a.partial + (size_t(split) * a.M + m) * npad + n, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     if (a.splits == 1) return;
 
     // ---- split-K: the last workgroup of the tile to arrive finishes it ----
-    __threadfence();
+    // The partials were written with device-scope atomic stores, which are coherent
+    // across the XCDs' L2 caches (they write through).  Waiting for their completion
+    // before the arrival counter is bumped orders them before it without a release
+    // fence, which on this part would write back the whole L2 once per workgroup.
+    // The finishing workgroup reads them back with device-scope atomic loads.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const unsigned old = atomicAdd(&a.counters[tile], 1u);
+        const unsigned old = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
         last_flag = (old == unsigned(a.splits - 1));
     }
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
-    for (int idx = tid; idx < MR * kGemvCols; idx += kGemvThreads) {
-        const int m = idx / kGemvCols, cc = idx % kGemvCols;
+
+    // P threads per output, each summing every P-th split with all its loads issued
+    // before the first add; the P sums are then added in a fixed order through LDS.
+    constexpr int OUTS = MR * kGemvCols;
+    constexpr int P = OUTS >= kGemvThreads ? 1 : kGemvThreads / OUTS;
+    constexpr int BATCH = 16;
+    for (int o = tid % OUTS; o < OUTS; o += (P == 1 ? kGemvThreads : OUTS)) {
+        const int p = P == 1 ? 0 : tid / OUTS;
+        const int m = o / kGemvCols, cc = o % kGemvCols;
         const int n = tile * kGemvCols + cc;
-        if (m >= a.M || n >= a.N) continue;
+        const bool live = m < a.M && n < a.N;
         float v = 0.f;
-        for (int sp = 0; sp < a.splits; ++sp)
-            v += __builtin_nontemporal_load(a.partial + (size_t(sp) * a.M + m) * npad + n);
-        const size_t o = size_t(m) * a.N + n;
-        a.y[o] = f32_to_bf16(epilogue(v, s, a.residual, o));
+        for (int s0 = p; s0 < a.splits; s0 += P * BATCH) {
+            float t[BATCH];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+                const int sp = s0 + b * P;
+                t[b] = (live && sp < a.splits)
+                           ? __hip_atomic_load(a.partial + (size_t(sp) * a.M + m) * npad + n, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+            }
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) v += t[b];
+        }
+        if (P == 1) {
+            if (live) {
+                const size_t oo = size_t(m) * a.N + n;
+                a.y[oo] = f32_to_bf16(epilogue(v, s, a.residual, oo));
+            }
+        } else {
+            red_s[p * OUTS + o] = v;
+        }
     }
-    if (tid == 0) a.counters[tile] = 0u;
+    if (P > 1) {
+        __syncthreads();
+        for (int o = tid; o < OUTS; o += kGemvThreads) {
+            const int m = o / kGemvCols, cc = o % kGemvCols;
+            const int n = tile * kGemvCols + cc;
+            if (m >= a.M || n >= a.N) continue;
+            float v = 0.f;
+            for (int p = 0; p < P; ++p) v += red_s[p * OUTS + o];
+            const size_t oo = size_t(m) * a.N + n;
+            a.y[oo] = f32_to_bf16(epilogue(v, s, a.residual, oo));
+        }
+    }
+    if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Kernels that need more than 64 KB of dynamic LDS must say so once before launch.

@@ -164,7 +164,7 @@ def swiglu_w4_gemv(g, u, qweight, scales, out_scale=1.0, residual=None, *, retur
     written on the fused path).
     """
     act = silu_mul(bf16_to_f64(g), bf16_to_f64(u))
-    acc = act @ w4_dequant(qweight, scales)
+    acc = _chunked_gemv(act, qweight, scales)
     y = _epilogue(acc, out_scale, residual)
     return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)
 
@@ -175,7 +175,7 @@ def w4_gemv(x, qweight, scales, out_scale=None, *, return_f64=False):
     Used for the horizontally fused gate_up projection ([P4] section 5, horizontal
     fusion: gate_proj and up_proj as one matmul, gate columns first).
     """
-    acc = bf16_to_f64(x) @ w4_dequant(qweight, scales)
+    acc = _chunked_gemv(bf16_to_f64(x), qweight, scales)
     y = _epilogue(acc, out_scale, None)
     return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)
 
@@ -224,7 +224,8 @@ def mlp_decode(x, r, norm_w, gu_q, gu_s, d_q, d_s, out_scale=0.5, eps=1e-6,
     return {"h": h, "y": y, "gu": gu_b, "out": out}
 
 
-def _chunked_gemv(a, qweight, scales, n_chunk):
+def _chunked_gemv(a, qweight, scales, n_chunk=4096):
+    """a @ dequant(W), dequantising ``n_chunk`` columns at a time to bound memory."""
     N = qweight.shape[1]
     out = np.empty((a.shape[0], N), dtype=np.float64)
     for c0 in range(0, N, n_chunk):

@@ -114,6 +114,8 @@ def test_add_rmsnorm_validation(L, inject):
 def test_add_rmsnorm_empty_batch_enqueues_nothing(L):
     f = Fake()
     assert _norm(L, f, M=0) == OK
+    assert L.fdec_add_rmsnorm(0, 0, f(), 1e-6, 0, 512, 0, 0, None) == OK   # empty tensors may be NULL
+    assert L.fdec_add_rmsnorm(0, 0, 0, 1e-6, 0, 512, 0, 0, None) == NULL
 
 
 def _w4(fake, K=1024, N=512, q=None, s=None):

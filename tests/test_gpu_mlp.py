@@ -22,12 +22,18 @@ def dev_layers(inp: synth.MlpInputs, residual_in_epilogue):
 
 
 def check_layer(L, x, r, got, resid):
-    """Oracle for one layer fed with the same bf16 inputs the GPU layer read."""
-    ref = O.mlp_decode(x, r, L.norm_w, L.gate_up.qweight, L.gate_up.scales, L.down.qweight, L.down.scales,
-                       L.out_scale, L.eps, residual_in_epilogue=resid)
-    assert_bits_equal(got["h"], ref["h"], "h")
-    w = [assert_close(got["y"], ref["y"], "y"), assert_close(got["gu"], ref["gu"], "gate_up"),
-         assert_close(got["out"], ref["out"], "out")]
+    """Each of the layer's three kernels against the oracle fed the bf16 inputs that
+    kernel read (the per-call tolerance applies per call; an oracle chaining its own
+    intermediates would also measure how rounding differences propagate)."""
+    h, y = O.add_rmsnorm(x, r, L.norm_w, L.eps)
+    assert_bits_equal(got["h"], h, "h")
+    w = [assert_close(got["y"], y, "y")]
+    gu = O.w4_gemv(got["y"], L.gate_up.qweight, L.gate_up.scales)
+    w.append(assert_close(got["gu"], gu, "gate_up"))
+    I = L.down.qweight.shape[0] * 8
+    out = O.swiglu_w4_gemv(got["gu"][:, :I], got["gu"][:, I:], L.down.qweight, L.down.scales, L.out_scale,
+                           got["h"] if resid else None)
+    w.append(assert_close(got["out"], out, "out"))
     return w
 
 
@@ -60,17 +66,30 @@ def test_mlp_layer_small_shapes_both_residual_modes(M, H, I):
         check_layer(inp.layers[0], inp.x, inp.r, got, resid)
 
 
-def test_chain_small_matches_oracle_chain():
-    say("[chain] M=1 H=256 I=512, 4 layers, eager and graph")
+def test_chain_small_per_layer_and_chain_calls():
+    """Chains are checked layer by layer: each layer's outputs against the oracle fed the
+    bf16 inputs that layer read.  Comparing the last layer against the oracle's own chain
+    is not a parity test: two correct roundings of a layer differ by a bf16 step here and
+    there, and later layers amplify the difference past the per-call tolerance."""
+    say("[chain] M=1 H=256 I=512, 4 layers: per layer, eager chain, graph")
     inp = synth.mlp_inputs(1, 256, 512, n_layers=4, seed=21)
     layers = dev_layers(inp, False)
-    xr, rr = O.mlp_chain(inp.x, inp.r, inp.layers)
+    trace = run_layers_eagerly(inp, layers, 1, 256, 512)
+    for l, t in enumerate(trace):
+        check_layer(inp.layers[l], t["x"], t["r"], t, False)
     b = F.MlpBuffers.empty(1, 256, 512, out_is_x=True)
     b.x.copy_(F.from_bits(inp.x))
     b.residual.copy_(F.from_bits(inp.r))
     F.mlp_chain(layers, b)
-    assert_close(F.to_bits(b.x), xr, "x_L")
-    assert_close(F.to_bits(b.residual), rr, "r_L")
+    assert_bits_equal(F.to_bits(b.x), trace[-1]["out"], "chain x")
+    assert_bits_equal(F.to_bits(b.residual), trace[-1]["h"], "chain r")
+    g = F.MlpGraph(layers, b)
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    g.launch()
+    torch.cuda.synchronize()
+    assert_bits_equal(F.to_bits(b.x), trace[-1]["out"], "graph x")
+    g.close()
 
 
 def run_layers_eagerly(inp, layers, M, H, I):
@@ -141,7 +160,9 @@ def test_graph_reads_scale_at_replay():
         outs[v] = F.to_bits(b.x)
         for L in inp.layers:
             L.out_scale = v
-        xr, _ = O.mlp_chain(inp.x, inp.r, inp.layers)
-        assert_close(outs[v], xr, f"scale {v}")
+        trace = run_layers_eagerly(inp, layers, 1, 256, 384)
+        assert_bits_equal(outs[v], trace[-1]["out"], f"graph vs eager, scale {v}")
+        for l, t in enumerate(trace):
+            check_layer(inp.layers[l], t["x"], t["r"], t, False)
     assert not np.array_equal(outs[0.5], outs[2.0])
     graph.close()
