@@ -101,9 +101,11 @@ typedef enum {
 
 /*
  * int4 group-quantised weight matrix W [K, N] ([P1]; [P4] section 5, prologue fusion).
- *   qweight: uint32 [K/8][N], row-major.  Word (kb, n) holds the weights
- *            k = 8*kb + j, j = 0..7, of column n; weight j sits in bits [4j, 4j+4)
- *            as a two's-complement nibble (values -8..7, symmetric, no zero point).
+ *   qweight: uint32 [N][K/8], row-major (a linear layer's [out_features,
+ *            in_features] orientation: the K values of one output column are
+ *            contiguous).  Word (n, kb) holds the weights k = 8*kb + j, j = 0..7, of
+ *            column n; weight j sits in bits [4j, 4j+4) as a two's-complement nibble
+ *            (values -8..7, symmetric, no zero point).
  *   scales:  bf16 [K/128][N], row-major.  Scale (g, n) multiplies the weights
  *            k in [128 g, 128 g + 128) of column n:  W[k, n] = q[k, n] * s[k/128, n].
  *   Requirements: K a positive multiple of 128, N a positive multiple of 8.
@@ -289,13 +291,18 @@ FDEC_API int fdec_w4_dequant(const fdec_w4* W, float* w_out, fdec_stream stream)
 
 /*
  * Tuning and test controls (process-wide, not thread-safe; not for production use).
- * fdec_set_gemv_split(k): force the GEMV's split of K into k parts per column tile
- *   (0 restores the built-in choice; values that do not fit the shape are clamped).
+ * fdec_set_gemv_split(k): force the split-K GEMV kernel with K split into about k
+ *   parts per column tile (0 restores the built-in choice of kernel and split; values
+ *   that do not fit the shape are clamped).
+ * fdec_set_gemv_tiling(waves, cols_per_wave): force the column-owning GEMV kernel's
+ *   workgroup shape (waves in 1..8, columns per wave in {1, 2, 4}); (0, 0) restores
+ *   the built-in choice.  Shapes the kernel cannot take fall back to the built-in one.
  * fdec_test_fail_launches(on): while on, every compute call validates its arguments
  *   and then returns FDEC_ERR_HIP without touching the GPU (exercises the error path
  *   on machines without a GPU).
  */
 FDEC_API void fdec_set_gemv_split(int32_t k);
+FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_wave);
 FDEC_API void fdec_test_fail_launches(int32_t on);
 
 #ifdef __cplusplus

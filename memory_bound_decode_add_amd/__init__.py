@@ -8,7 +8,7 @@ the library's HIP kernels; there is no fallback.  PyTorch provides device memory
 streams.
 
 bf16 tensors are ``torch.bfloat16``; packed int4 weights are ``torch.int32`` tensors
-of shape ``[K/8, N]`` holding the uint32 words bit for bit (see ``fdec.h``); group
+of shape ``[N, K/8]`` holding the uint32 words bit for bit (see ``fdec.h``); group
 scales are ``torch.bfloat16`` ``[K/128, N]``.
 """
 from __future__ import annotations
@@ -87,6 +87,7 @@ _SIGS = {
     "fdec_w4_unpack": (ctypes.c_int, [ctypes.POINTER(CW4), _c_p, _c_p]),
     "fdec_w4_dequant": (ctypes.c_int, [ctypes.POINTER(CW4), _c_p, _c_p]),
     "fdec_set_gemv_split": (None, [_i32]),
+    "fdec_set_gemv_tiling": (None, [_i32, _i32]),
     "fdec_test_fail_launches": (None, [_i32]),
 }
 
@@ -173,23 +174,23 @@ def words_to_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
 # ----------------------------------------------------------------------------
 @dataclass
 class W4Weight:
-    qweight: torch.Tensor   # int32 [K/8, N] (uint32 words)
+    qweight: torch.Tensor   # int32 [N, K/8] (uint32 words)
     scales: torch.Tensor    # bf16 [K/128, N]
 
     def __post_init__(self):
         _need(self.qweight, "qweight", torch.int32)
         _need(self.scales, "scales", torch.bfloat16)
-        kb, n = self.qweight.shape
+        n, kb = self.qweight.shape
         if tuple(self.scales.shape) != (kb * 8 // 128, n):
             raise ValueError("scales must be [K/128, N]")
 
     @property
     def K(self):
-        return self.qweight.shape[0] * 8
+        return self.qweight.shape[1] * 8
 
     @property
     def N(self):
-        return self.qweight.shape[1]
+        return self.qweight.shape[0]
 
     def c(self) -> CW4:
         return CW4(self.qweight.data_ptr(), self.scales.data_ptr(), self.K, self.N)
@@ -476,6 +477,10 @@ def w4_dequant(W: W4Weight) -> torch.Tensor:
 
 def set_gemv_split(k: int):
     lib().fdec_set_gemv_split(int(k))
+
+
+def set_gemv_tiling(waves: int, cols_per_wave: int):
+    lib().fdec_set_gemv_tiling(int(waves), int(cols_per_wave))
 
 
 def test_fail_launches(on: bool):

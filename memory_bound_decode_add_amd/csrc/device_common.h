@@ -75,6 +75,20 @@ __device__ __forceinline__ Q4x2 decode_int4x8(uint32_t w) {
     return q;
 }
 
+// The same pairs with the offsets left in: 1032 + q at even positions (j0, j4, j2, j6),
+// 1152 + 16 q at odd positions (j1, j5, j3, j7).  Six integer ops per word.
+__device__ __forceinline__ Q4x2 decode_int4x8_biased(uint32_t w) {
+    const uint32_t x = xor_opaque(w, 0x88888888u);
+    const uint32_t t = x >> 8;
+    const uint32_t one024 = 0x64006400u;
+    Q4x2 q;
+    q.p04 = __builtin_bit_cast(half2_t, and_or(x, 0x000F000Fu, one024));
+    q.p15 = __builtin_bit_cast(half2_t, and_or(x, 0x00F000F0u, one024));
+    q.p26 = __builtin_bit_cast(half2_t, and_or(t, 0x000F000Fu, one024));
+    q.p37 = __builtin_bit_cast(half2_t, and_or(t, 0x00F000F0u, one024));
+    return q;
+}
+
 // Position of weight j (0..7) of a word in the pair order above.
 __host__ __device__ constexpr int pair_slot(int j) { return 2 * (j & 3) + (j >> 2); }
 

@@ -9,19 +9,36 @@
 
 namespace fdec {
 
-// Tile geometry of the int4 GEMV: a workgroup of 4 waves covers 64 columns; each
-// wave covers whole 128-wide K groups of those columns.
+// The int4 GEMV has two kernels.
+//  * Column-owning (M <= 4, K <= 16384): each wave owns whole output columns over the
+//    full K, each workgroup stages the activation of the full K once in LDS; no
+//    cross-workgroup reduction and no workspace.
+//  * Split-K (any M <= 16, any K): a 256-thread workgroup owns a 64-column tile and a
+//    slice of K; slices are combined by the last workgroup of the tile to arrive.
 constexpr int kGemvThreads = 256;
 constexpr int kGemvCols = 64;
 constexpr int kGroup = 128;
+constexpr int kColMaxTasks = 8;      // activation tasks (row, 512-wide block) per wave, column kernel
+constexpr int kColMaxWaves = 8;      // waves per workgroup, column kernel (256 VGPRs per lane)
+constexpr int kColMaxChunks = 8;     // 32-wide K chunks per lane, column kernel
+constexpr size_t kMaxLds = 160 * 1024;
+
+enum GemvKind { kColumnOwning = 0, kSplitK = 1 };
 
 struct GemvPlan {
-    int tiles;        // ceil(N / 64)
+    int kind;
+    int mr;           // rows the kernel is compiled for
     int groups;       // K / 128
+    // column-owning kernel
+    int waves;        // waves per workgroup
+    int cpw;          // columns per wave (1 or 4)
+    int ni;           // 32-wide K chunks per lane
+    int wgs;          // workgroups
+    // split-K kernel
+    int tiles;        // ceil(N / 64)
     int gw;           // groups per wave (1, 2 or 4)
     int gps;          // groups per split = 4 * gw
     int splits;       // ceil(groups / gps)
-    int mr;           // rows the kernel is compiled for (1, 2, 4, 8, 16)
     size_t partial_bytes;   // splits * M * tiles * 64 * 4 (0 when splits == 1)
     size_t counter_bytes;   // tiles * 4, rounded up to 256 (0 when splits == 1)
     size_t lds_bytes;       // dynamic LDS per workgroup
@@ -62,5 +79,7 @@ hipError_t launch_eager_rmsnorm(const uint16_t* x, const uint16_t* r, const uint
                                 float* f32a, float* f32b, float* rowbuf, hipStream_t s);
 
 extern int g_forced_split;   // fdec_set_gemv_split
+extern int g_col_waves;      // fdec_set_gemv_tiling
+extern int g_col_cpw;
 
 }  // namespace fdec

@@ -43,7 +43,7 @@ __global__ void product_kernel(const uint16_t* __restrict__ g, const uint16_t* _
         act[2 * j] = silu_f32(bf16_lo(ga[j])) * bf16_lo(ua[j]);
         act[2 * j + 1] = silu_f32(bf16_hi(ga[j])) * bf16_hi(ua[j]);
     }
-    const Q4x2 d = decode_int4x8(qw[i]);
+    const Q4x2 d = decode_int4x8(qw[int64_t(n) * KB + kb]);      // word (n, kb) of [N][K/8]
     const half2_t p[4] = {d.p04, d.p15, d.p26, d.p37};
     const float s = bf16_to_f32(sc[int64_t(kb / 16) * N + n]);
 #pragma unroll

@@ -9,34 +9,43 @@
 // with act = silu(g) * u (SwiGLU prologue) or act = x (identity prologue).  The
 // activation exists only in LDS and registers; the (M, K, N) product never exists.
 //
-// Work decomposition.  A 256-thread workgroup owns a 64-column tile and a slice of
-// whole 128-wide K groups (a "split").  Wave w of the workgroup owns groups
-// w, w+4, ... of the slice.  Lane (kr = lane % 4, cq = lane / 4) owns columns
-// 4cq..4cq+3 and packed rows 4kr..4kr+3 of each of its wave's groups, loading each
-// packed row of its four columns with one 16-byte load: one load instruction of a
-// wave covers four 256-byte runs of the weight matrix.  Every weight load of the
-// workgroup is issued before any arithmetic, so the whole slice is in flight at once.
+// Weights: qweight uint32 [N][K/8] (the K values of a column are contiguous, 8 per
+// word), scales bf16 [K/128][N].
 //
-// Prologue.  Each wave computes the activation of its own groups (2 values per lane
-// per group and row) in fp32, then stores it to LDS as fp16 scaled by a power of two
-// 2^-E chosen per (row, group) from the group's largest magnitude, so the largest
-// value lands in [2^14, 2^15): any finite fp32 activation fits fp16 with an 11-bit
-// significand relative to its group's maximum.  The factor 2^E is folded back in
-// with the group scale.  Activation values are stored in the pair order of the int4
-// decode (see decode_int4x8), so four dot2 instructions consume one packed word.
+// Shared by both kernels:
+//  * Prologue.  A wave computes the activation of one 128-wide K group of one row
+//    (2 values per lane) in fp32 and stores it to LDS as fp16 scaled by a power of two
+//    2^-E chosen from the group's largest magnitude, so the largest value lands in
+//    [2^14, 2^15): any finite fp32 activation fits fp16 with an 11-bit significand
+//    relative to its group's maximum.  2^E is folded back in with the group scale.
+//    Values are stored in the pair order of the int4 decode (decode_int4x8), so four
+//    v_dot2_f32_f16 consume one packed word.
+//  * Dot.  Per packed word: XOR, shift, four AND-OR and four packed fp16 ops give four
+//    exact fp16 pairs of weights; four dot2 accumulate them in fp32.  The group scale
+//    times 2^E multiplies each 32-wide partial sum once.
+//  * Every global load is issued before any arithmetic, from addresses clamped into
+//    the tensors (no branches around loads), activation inputs first, so the prologue
+//    runs while the weights are still in flight.
 //
-// Dot.  Per packed word: one XOR, one shift, four AND-OR and four packed fp16 ops turn
-// eight nibbles into four exact fp16 pairs; four v_dot2_f32_f16 accumulate them
-// against the activations in fp32.  The group scale (times 2^E) multiplies the
-// lane's 32-element partial sum once per group.
+// Column-owning kernel (M <= 4, K <= 16384).  A workgroup of W waves owns W*CPW
+// consecutive columns; each wave owns CPW of them over the whole K.  Lane l loads the
+// 16-byte chunks (32 consecutive k) l, l+64, ... of each of the wave's columns, so one
+// load instruction reads 1 KB of contiguous weights, and one read of the staged
+// activation of a chunk (64 bytes, conflict-free layout) serves all CPW columns.  The
+// workgroup stages the activation of the full K and the group scales of its columns
+// in LDS once.  A column's sum is reduced across the wave with DPP and scalar lane
+// reads, and one lane applies the epilogue.  There is no cross-workgroup step and no
+// workspace; results do not depend on scheduling.
 //
-// Reduction.  The four lanes sharing columns form a quad and are summed with DPP; the
-// four waves through LDS.  With one split the workgroup applies the epilogue directly.  With several,
-// each workgroup writes fp32 partial sums for its tile to the workspace with
-// device-scope atomic stores, waits for them to complete, then bumps the tile's
-// arrival counter; the last workgroup to arrive reads the partials back with
-// device-scope atomic loads, sums them in split order (so results do not depend on
-// arrival order), applies the epilogue and resets the counter.
+// Split-K kernel (M <= 16, any K).  A 256-thread workgroup owns a 64-column tile and
+// a slice of whole 128-wide groups; wave w owns groups w, w+4, ... of the slice; lane
+// (kr = lane % 4, cq = lane / 4) owns columns 4cq..4cq+3 and packed words 4kr..4kr+3
+// of each group of those columns.  The quad of lanes sharing columns reduces with DPP,
+// the waves through LDS.  With several slices each workgroup writes fp32 partials to
+// the workspace with device-scope atomic stores, waits for them to complete, then bumps
+// the tile's arrival counter; the last to arrive reads the partials back with
+// device-scope atomic loads, sums them in slice order, applies the epilogue and resets
+// the counter.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -45,16 +54,301 @@
 namespace fdec {
 
 int g_forced_split = 0;
+int g_col_waves = 0;
+int g_col_cpw = 0;
 
 namespace {
 
-struct GemvArgs {
+__device__ __forceinline__ float epilogue(float v, float s, const uint16_t* res, size_t idx) {
+    v *= s;
+    if (res) v += bf16_to_f32(res[idx]);
+    return v;
+}
+
+// Activation of one (row, group) task, 2 values per lane, to LDS as block-scaled fp16.
+// Must be called by a full wave (wave-uniform control flow).
+template <int PRO>
+__device__ __forceinline__ void stage_act(uint32_t ga, uint32_t ua, bool live, int lane, _Float16* dst128,
+                                          float* esc) {
+    float v0 = 0.f, v1 = 0.f;
+    if (live) {
+        if (PRO == kSwiGLU) {
+            v0 = silu_f32(bf16_lo(ga)) * bf16_lo(ua);
+            v1 = silu_f32(bf16_hi(ga)) * bf16_hi(ua);
+        } else {
+            v0 = bf16_lo(ga);
+            v1 = bf16_hi(ga);
+        }
+    }
+    const float mx = wave_max_uniform(fmaxf(fabsf(v0), fabsf(v1)));
+    int e = 0;
+    (void)__builtin_frexpf(mx, &e);
+    const int E = min(max(e - 15, -126), 127);
+    const int k0 = 2 * lane;                      // k within the group
+    _Float16* dst = dst128 + (k0 >> 3) * 8;
+    dst[pair_slot(k0 & 7)] = (_Float16)__builtin_ldexpf(v0, -E);
+    dst[pair_slot((k0 & 7) + 1)] = (_Float16)__builtin_ldexpf(v1, -E);
+    if (lane == 0) *esc = __builtin_ldexpf(1.0f, E);
+}
+
+// sum over 32 k: four packed words against 64 bytes of staged activation
+__device__ __forceinline__ float dot32(const uint4 w, const _Float16* act) {
+    const uint4 a0 = *reinterpret_cast<const uint4*>(act);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(act + 8);
+    const uint4 a2 = *reinterpret_cast<const uint4*>(act + 16);
+    const uint4 a3 = *reinterpret_cast<const uint4*>(act + 24);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    const uint4 av[4] = {a0, a1, a2, a3};
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const Q4x2 q = decode_int4x8(wd[j]);
+        v = dot2(q.p04, __builtin_bit_cast(half2_t, av[j].x), v);
+        v = dot2(q.p15, __builtin_bit_cast(half2_t, av[j].y), v);
+        v = dot2(q.p26, __builtin_bit_cast(half2_t, av[j].z), v);
+        v = dot2(q.p37, __builtin_bit_cast(half2_t, av[j].w), v);
+    }
+    return v;
+}
+
+// ===========================================================================
+// column-owning kernel
+// ===========================================================================
+struct ColArgs {
     const uint16_t* a0;     // g (SwiGLU) or x (identity), row stride lda
     const uint16_t* a1;     // u (SwiGLU) or unused
     int64_t lda;
-    const uint4* qw;        // packed words viewed as uint4: [K/8][N/4]
+    const uint4* qw;        // [N][K/32] chunks of 4 words
     const uint16_t* sc;     // bf16 scales [K/128][N]
     int M, K, N;
+    int nch;                // K / 32
+    int groups;             // K / 128
+    const float* out_scale;
+    const uint16_t* residual;
+    uint16_t* y;
+};
+
+// Staged activation of the column kernel, per row: fp16 in the layout [quarter q][chunk
+// c][8] with a quarter stride of 8*nch + 32 halves; quarter q of chunk c holds k = 32c +
+// 8q .. 32c + 8q + 7 in the decode's pair order.  A wave reading quarter q of chunks l,
+// l+1, ... (one per lane) touches consecutive 16-byte blocks, and the 64-byte pad
+// spreads the staging writes of a quad (one chunk, four quarters) over distinct banks.
+//
+// The weights are decoded without removing their offsets: a nibble at an even position
+// j (bits 0..3 of a half) decodes to 1032 + q, at an odd position (bits 4..7) to
+// 1152 + 16 q.  Odd-position activations are staged divided by 16, so each product is
+// a*q plus a per-k offset 1032*a or 72*a that does not depend on the weight; the
+// staging phase sums those offsets per chunk (bias_s) and the dot phase subtracts them.
+// Every staged value and every product is exact; what changes is that the fp32 sums
+// now also carry the offset terms, about 1032/|q| times larger than the wanted ones,
+// so a chunk's dot keeps roughly 10 fewer significant bits (relative error ~1e-4).
+//
+// Staging task: one row and 512 consecutive k; lane l takes the 8 values of packed word
+// l of the block (16-byte loads of g and u), writes them as one 16-byte LDS store, and
+// the quad of lanes holding one chunk sums its offsets.  The block's power-of-two scale
+// 2^E puts its largest magnitude in [2^14, 2^15).
+__device__ __forceinline__ int col_quarter_stride(int nch) { return nch * 8 + 32; }
+
+template <int PRO>
+__device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, bool live, bool in_k,
+                                               int lane, _Float16* dst, float* esc, float* bias_dst) {
+    float v[8];                                    // k = 8w + j, j = 0..7
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        if (PRO == kSwiGLU) {
+            v[2 * h] = silu_f32(bf16_lo(gw[h])) * bf16_lo(uw[h]);
+            v[2 * h + 1] = silu_f32(bf16_hi(gw[h])) * bf16_hi(uw[h]);
+        } else {
+            v[2 * h] = bf16_lo(gw[h]);
+            v[2 * h + 1] = bf16_hi(gw[h]);
+        }
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        v[j] = live ? v[j] : 0.f;
+        mx = fmaxf(mx, fabsf(v[j]));
+    }
+    mx = wave_max_uniform(mx);
+    int e = 0;
+    (void)__builtin_frexpf(mx, &e);
+    const int E = min(max(e - 15, -126), 127);
+    const float down = __builtin_ldexpf(1.0f, -E);
+    const float down16 = down * 0.0625f;
+    // slot order (j0, j4, j1, j5, j2, j6, j3, j7); odd j stored divided by 16
+    const _Float16 h0 = (_Float16)(v[0] * down), h4 = (_Float16)(v[4] * down);
+    const _Float16 h1 = (_Float16)(v[1] * down16), h5 = (_Float16)(v[5] * down16);
+    const _Float16 h2 = (_Float16)(v[2] * down), h6 = (_Float16)(v[6] * down);
+    const _Float16 h3 = (_Float16)(v[3] * down16), h7 = (_Float16)(v[7] * down16);
+    typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+    const half8_t pk = {h0, h4, h1, h5, h2, h6, h3, h7};
+    if (in_k) *reinterpret_cast<half8_t*>(dst) = pk;
+    if (lane == 0) *esc = __builtin_ldexpf(1.0f, E);
+    float b = 1032.0f * ((float(h0) + float(h4)) + (float(h2) + float(h6))) +
+              1152.0f * ((float(h1) + float(h5)) + (float(h3) + float(h7)));
+    b += dpp<kQuadSwap1>(b);
+    b += dpp<kQuadSwap2>(b);                       // the chunk's four words are one quad
+    if ((lane & 3) == 0 && in_k) *bias_dst = b;
+}
+
+template <int MR, int CPW, int NI, int PRO>
+__global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int W = blockDim.x >> 6;
+    const int C = W * CPW;                         // columns per workgroup
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int nblk = (a.K + 511) >> 9;             // 512-wide staging blocks
+    const int qs = col_quarter_stride(a.nch);      // halves
+    const int kw = a.K >> 3;                       // packed words per row
+    _Float16* act_s = reinterpret_cast<_Float16*>(smem);                          // [MR][4][qs]
+    float* esc_s = reinterpret_cast<float*>(smem + size_t(MR) * 4 * qs * 2);      // [MR][nblk]
+    float* bias_s = esc_s + MR * nblk;                                             // [MR][nch]
+    float* sc_s = bias_s + MR * a.nch;                                             // [groups][C]
+
+    const int col0 = blockIdx.x * C;
+    const int nw = col0 + wave * CPW;              // this wave's first column
+
+    // ---- 1. activation inputs: task t = wave + W * ti -> (row t % MR, block t / MR) ----
+    const int ntask = MR * nblk;
+    uint4 ga[kColMaxTasks], ua[kColMaxTasks];
+#pragma unroll
+    for (int ti = 0; ti < kColMaxTasks; ++ti) {
+        const int t = wave + W * ti;
+        if (t >= ntask) break;                     // uniform across the wave
+        const int m = min(t % MR, a.M - 1), b = t / MR;
+        const int k = min(b * 64 + lane, kw - 1) * 8;
+        ga[ti] = *reinterpret_cast<const uint4*>(a.a0 + size_t(m) * a.lda + k);
+        ua[ti] = PRO == kSwiGLU ? *reinterpret_cast<const uint4*>(a.a1 + size_t(m) * a.lda + k) : make_uint4(0, 0, 0, 0);
+    }
+    // ---- 2. group scales of this workgroup's columns, epilogue inputs ----
+    constexpr int kScPer = 8;
+    const int nsc = a.groups * C;
+    uint16_t sraw[kScPer];
+#pragma unroll
+    for (int r = 0; r < kScPer; ++r) {
+        if (r * int(blockDim.x) >= nsc) break;     // uniform
+        const int idx = min(tid + r * int(blockDim.x), nsc - 1);
+        const int g = idx / C, cc = idx % C;
+        sraw[r] = a.sc[size_t(g) * a.N + min(col0 + cc, a.N - 1)];
+    }
+    // lane l < MR*CPW finishes output (row l / CPW, column nw + l % CPW)
+    const int em = lane / CPW, en = nw + lane % CPW;
+    const bool owner = lane < MR * CPW && em < a.M && en < a.N;
+    float res = 0.f;
+    if (a.residual) res = bf16_to_f32(a.residual[size_t(min(em, a.M - 1)) * a.N + min(en, a.N - 1)]);
+    const float os = a.out_scale ? *a.out_scale : 1.0f;
+    // ---- 3. weight chunks: lane l takes chunks l, l+64, ... of each of the wave's columns ----
+    uint4 wv[NI][CPW];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < CPW; ++j)
+            wv[i][j] = a.qw[size_t(min(nw + j, a.N - 1)) * a.nch + min(lane + kWave * i, a.nch - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 4. prologue: activations, per-chunk offsets and scales to LDS ----
+    // word wi = 64 b + lane: chunk wi / 4, quarter wi % 4
+    const int lofs = (lane & 3) * qs + (lane >> 2) * 8;
+#pragma unroll
+    for (int ti = 0; ti < kColMaxTasks; ++ti) {
+        const int t = wave + W * ti;
+        if (t >= ntask) break;                     // uniform across the wave
+        const int m = t % MR, b = t / MR;
+        const bool in_k = b * 64 + lane < kw;      // a chunk lies wholly inside or outside K
+        stage_word_col<PRO>(ga[ti], ua[ti], in_k && m < a.M, in_k, lane,
+                            act_s + size_t(m) * 4 * qs + lofs + b * 128, esc_s + m * nblk + b,
+                            bias_s + m * a.nch + b * 16 + (lane >> 2));
+    }
+#pragma unroll
+    for (int r = 0; r < kScPer; ++r) {
+        const int idx = tid + r * int(blockDim.x);
+        if (r * int(blockDim.x) >= nsc) break;
+        if (idx < nsc) sc_s[idx] = bf16_to_f32(sraw[r]);
+    }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 5. dot products: one activation read per chunk serves the wave's CPW columns ----
+    float acc[MR][CPW];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) acc[m][j] = 0.f;
+    const int cw = wave * CPW;                     // first column index within the workgroup
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int c = lane + kWave * i;
+        if (c < a.nch) {
+            float s[CPW];
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) s[j] = sc_s[(c >> 2) * C + cw + j];
+            Q4x2 q[CPW][4];
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) {
+                const uint32_t wd[4] = {wv[i][j].x, wv[i][j].y, wv[i][j].z, wv[i][j].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) q[j][h] = decode_int4x8_biased(wd[h]);
+            }
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const _Float16* arow = act_s + size_t(m) * 4 * qs + c * 8;
+                uint4 av[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) av[h] = *reinterpret_cast<const uint4*>(arow + h * qs);
+                const float bias = bias_s[m * a.nch + c];
+                const float e = esc_s[m * nblk + (c >> 4)];
+#pragma unroll
+                for (int j = 0; j < CPW; ++j) {
+                    float d = -bias;
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        d = dot2(q[j][h].p04, __builtin_bit_cast(half2_t, av[h].x), d);
+                        d = dot2(q[j][h].p15, __builtin_bit_cast(half2_t, av[h].y), d);
+                        d = dot2(q[j][h].p26, __builtin_bit_cast(half2_t, av[h].z), d);
+                        d = dot2(q[j][h].p37, __builtin_bit_cast(half2_t, av[h].w), d);
+                    }
+                    acc[m][j] = fmaf(d, s[j] * e, acc[m][j]);
+                }
+            }
+        }
+    }
+
+    // ---- 6. reduce each column over the wave; the owning lane applies the epilogue ----
+    float mine = 0.f;
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            float v = acc[m][j];
+            v += dpp<kQuadSwap1>(v);
+            v += dpp<kQuadSwap2>(v);
+            v += dpp<kRowRor4>(v);
+            v += dpp<kRowRor8>(v);                 // every lane holds its row-of-16 sum
+            const int b = __builtin_bit_cast(int, v);
+            v = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+                (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+            mine = lane == m * CPW + j ? v : mine;
+        }
+    if (owner) a.y[size_t(em) * a.N + en] = f32_to_bf16(fmaf(mine, os, res));
+}
+
+// ===========================================================================
+// split-K kernel
+// ===========================================================================
+struct SplitArgs {
+    const uint16_t* a0;
+    const uint16_t* a1;
+    int64_t lda;
+    const uint4* qw;        // [N][K/32] chunks of 4 words
+    const uint16_t* sc;
+    int M, K, N;
+    int nch;
     int groups, gps, splits, tiles;
     const float* out_scale;
     const uint16_t* residual;
@@ -63,14 +357,8 @@ struct GemvArgs {
     unsigned* counters;     // [tiles]
 };
 
-__device__ __forceinline__ float epilogue(float v, float s, const uint16_t* res, size_t idx) {
-    v *= s;
-    if (res) v += bf16_to_f32(res[idx]);
-    return v;
-}
-
 template <int MR, int GW, int PRO>
-__global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(256) void w4_gemv_split_kernel(SplitArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int GPS = 4 * GW;
     _Float16* act_s = reinterpret_cast<_Float16*>(smem);                 // [GPS][MR][128]
@@ -89,16 +377,11 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
     const int cq = lane >> 2;
     const int col = tile * kGemvCols + cq * 4;
     const bool col_ok = col < a.N;
-    const int nq = a.N >> 2;
 
     // ---- activation inputs: tasks (i, m) = (this wave's i-th group, row m) ----
     constexpr int T = MR * GW;
     constexpr int B = T < 8 ? T : 8;
     uint32_t ga[B], ua[B];
-    // Every load below is unconditional, from an address clamped into the tensor: a
-    // task or group outside the slice re-reads a valid location and its value is never
-    // used.  Without branches around the loads, the compiler's wait counting can let
-    // the prologue start as soon as its own (first-issued) loads arrive.
     auto load_batch = [&](int b0) {
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -112,7 +395,8 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
     };
     load_batch(0);
 
-    // ---- weights and scales of this wave's groups, all in flight at once ----
+    // ---- weights and scales of this wave's groups: per column one 16-byte load of the
+    // lane's four words ----
     uint4 wv[GW][4];
     uint2 sv[GW];
     const int colc = col_ok ? col : 0;
@@ -120,17 +404,12 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
     for (int i = 0; i < GW; ++i) {
         const int g = g0 + min(wave + 4 * i, ng - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const size_t kb = size_t(g) * 16 + kr * 4 + j;
-            wv[i][j] = a.qw[kb * nq + (colc >> 2)];
-        }
+        for (int c = 0; c < 4; ++c) wv[i][c] = a.qw[size_t(colc + c) * a.nch + g * 4 + kr];
         sv[i] = *reinterpret_cast<const uint2*>(a.sc + size_t(g) * a.N + colc);
     }
-    // Keep the weight decode below the prologue: the prologue needs only the (earlier)
-    // activation loads, so the weights stay in flight while it runs.
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- prologue: activations to LDS as block-scaled fp16 ----
+    // ---- prologue ----
 #pragma unroll
     for (int b0 = 0; b0 < T; b0 += B) {
         if (b0 > 0) load_batch(b0);
@@ -140,26 +419,7 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
             const int i = t / MR, m = t % MR;
             const int lg = wave + 4 * i;
             if (t >= T || lg >= ng) continue;          // uniform across the wave
-            float v0 = 0.f, v1 = 0.f;
-            if (m < a.M) {                                // uniform; rows past M stay zero
-                if (PRO == kSwiGLU) {
-                    v0 = silu_f32(bf16_lo(ga[b])) * bf16_lo(ua[b]);
-                    v1 = silu_f32(bf16_hi(ga[b])) * bf16_hi(ua[b]);
-                } else {
-                    v0 = bf16_lo(ga[b]);
-                    v1 = bf16_hi(ga[b]);
-                }
-            }
-            const float mx = wave_max_uniform(fmaxf(fabsf(v0), fabsf(v1)));
-            int e = 0;
-            (void)__builtin_frexpf(mx, &e);
-            const int E = min(max(e - 15, -126), 127);
-            const int k0 = 2 * lane;                      // k within the group
-            const int r = k0 >> 3, j0 = k0 & 7;
-            _Float16* dst = act_s + (lg * MR + m) * kGroup + r * 8;
-            dst[pair_slot(j0)] = (_Float16)__builtin_ldexpf(v0, -E);
-            dst[pair_slot(j0 + 1)] = (_Float16)__builtin_ldexpf(v1, -E);
-            if (lane == 0) esc_s[lg * MR + m] = __builtin_ldexpf(1.0f, E);
+            stage_act<PRO>(ga[b], ua[b], m < a.M, lane, act_s + (lg * MR + m) * kGroup, esc_s + lg * MR + m);
         }
     }
     // Each wave reads back only the groups it wrote; LDS operations of one wave complete
@@ -178,42 +438,13 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
     for (int i = 0; i < GW; ++i) {
         const int lg = wave + 4 * i;
         if (lg >= ng) break;                              // uniform across the wave
-        float gs[MR][4];
-#pragma unroll
-        for (int m = 0; m < MR; ++m)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) gs[m][c] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = kr * 4 + j;
-            const uint32_t wd[4] = {wv[i][j].x, wv[i][j].y, wv[i][j].z, wv[i][j].w};
-            Q4x2 q[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) q[c] = decode_int4x8(wd[c]);
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                const uint4 av = *reinterpret_cast<const uint4*>(act_s + (lg * MR + m) * kGroup + r * 8);
-                const half2_t a04 = __builtin_bit_cast(half2_t, av.x);
-                const half2_t a15 = __builtin_bit_cast(half2_t, av.y);
-                const half2_t a26 = __builtin_bit_cast(half2_t, av.z);
-                const half2_t a37 = __builtin_bit_cast(half2_t, av.w);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    float v = gs[m][c];
-                    v = dot2(q[c].p04, a04, v);
-                    v = dot2(q[c].p15, a15, v);
-                    v = dot2(q[c].p26, a26, v);
-                    v = dot2(q[c].p37, a37, v);
-                    gs[m][c] = v;
-                }
-            }
-        }
         const float s4[4] = {bf16_lo(sv[i].x), bf16_hi(sv[i].x), bf16_lo(sv[i].y), bf16_hi(sv[i].y)};
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
+            const _Float16* act = act_s + (lg * MR + m) * kGroup + kr * 32;
             const float e = esc_s[lg * MR + m];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[m][c] = fmaf(gs[m][c], s4[c] * e, acc[m][c]);
+            for (int c = 0; c < 4; ++c) acc[m][c] = fmaf(dot32(wv[i][c], act), s4[c] * e, acc[m][c]);
         }
     }
 
@@ -248,7 +479,7 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
     }
     if (a.splits == 1) return;
 
-    // ---- split-K: the last workgroup of the tile to arrive finishes it ----
+    // ---- the last workgroup of the tile to arrive finishes it ----
     // The partials were written with device-scope atomic stores, which are coherent
     // across the XCDs' L2 caches (they write through).  Waiting for their completion
     // before the arrival counter is bumped orders them before it without a release
@@ -312,7 +543,10 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemvArgs a) {
     if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Kernels that need more than 64 KB of dynamic LDS must say so once before launch.
+// ===========================================================================
+// launch plumbing
+// ===========================================================================
+// Kernels that need more than 64 KB of dynamic LDS must say so before launch.
 template <typename Kern>
 hipError_t allow_lds(Kern k, size_t bytes) {
     if (bytes <= 65536) return hipSuccess;
@@ -320,26 +554,67 @@ hipError_t allow_lds(Kern k, size_t bytes) {
                                int(bytes));
 }
 
-template <int MR, int GW>
-hipError_t launch_mr_gw(Prologue pro, const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
-    const dim3 grid(p.tiles * p.splits);
-    hipError_t e;
-    if (pro == kSwiGLU) {
-        if ((e = allow_lds(w4_gemv_kernel<MR, GW, kSwiGLU>, p.lds_bytes)) != hipSuccess) return e;
-        w4_gemv_kernel<MR, GW, kSwiGLU><<<grid, kGemvThreads, p.lds_bytes, s>>>(a);
-    } else {
-        if ((e = allow_lds(w4_gemv_kernel<MR, GW, kIdentity>, p.lds_bytes)) != hipSuccess) return e;
-        w4_gemv_kernel<MR, GW, kIdentity><<<grid, kGemvThreads, p.lds_bytes, s>>>(a);
-    }
+template <typename Args, typename Kern>
+hipError_t launch(Kern k, dim3 grid, int threads, size_t lds, hipStream_t s, const Args& a) {
+    hipError_t e = allow_lds(k, lds);
+    if (e != hipSuccess) return e;
+    k<<<grid, threads, lds, s>>>(a);
     return hipGetLastError();
 }
 
+template <int MR, int CPW, int NI>
+hipError_t launch_col3(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStream_t s) {
+    if (pro == kSwiGLU)
+        return launch(w4_gemv_col_kernel<MR, CPW, NI, kSwiGLU>, dim3(p.wgs), p.waves * kWave, p.lds_bytes, s, a);
+    return launch(w4_gemv_col_kernel<MR, CPW, NI, kIdentity>, dim3(p.wgs), p.waves * kWave, p.lds_bytes, s, a);
+}
+
+// Only the (CPW, NI) pairs plan_column can choose are instantiated: CPW = 4 with NI <= 3,
+// CPW = 2 with NI <= 6, CPW = 1 with NI <= 8 (the weight registers of a lane).
 template <int MR>
-hipError_t launch_mr(Prologue pro, const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
+hipError_t launch_col(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStream_t s) {
+    if (p.cpw == 4) {
+        switch (p.ni) {
+            case 1: return launch_col3<MR, 4, 1>(pro, a, p, s);
+            case 2: return launch_col3<MR, 4, 2>(pro, a, p, s);
+            default: return launch_col3<MR, 4, 3>(pro, a, p, s);
+        }
+    }
+    if (p.cpw == 2) {
+        switch (p.ni) {
+            case 1: return launch_col3<MR, 2, 1>(pro, a, p, s);
+            case 2: return launch_col3<MR, 2, 2>(pro, a, p, s);
+            case 3: return launch_col3<MR, 2, 3>(pro, a, p, s);
+            case 4: return launch_col3<MR, 2, 4>(pro, a, p, s);
+            case 5: return launch_col3<MR, 2, 5>(pro, a, p, s);
+            default: return launch_col3<MR, 2, 6>(pro, a, p, s);
+        }
+    }
+    switch (p.ni) {
+        case 1: return launch_col3<MR, 1, 1>(pro, a, p, s);
+        case 2: return launch_col3<MR, 1, 2>(pro, a, p, s);
+        case 3: return launch_col3<MR, 1, 3>(pro, a, p, s);
+        case 4: return launch_col3<MR, 1, 4>(pro, a, p, s);
+        case 5: return launch_col3<MR, 1, 5>(pro, a, p, s);
+        case 6: return launch_col3<MR, 1, 6>(pro, a, p, s);
+        case 7: return launch_col3<MR, 1, 7>(pro, a, p, s);
+        default: return launch_col3<MR, 1, 8>(pro, a, p, s);
+    }
+}
+
+template <int MR, int GW>
+hipError_t launch_split2(Prologue pro, const SplitArgs& a, const GemvPlan& p, hipStream_t s) {
+    const dim3 grid(p.tiles * p.splits);
+    if (pro == kSwiGLU) return launch(w4_gemv_split_kernel<MR, GW, kSwiGLU>, grid, kGemvThreads, p.lds_bytes, s, a);
+    return launch(w4_gemv_split_kernel<MR, GW, kIdentity>, grid, kGemvThreads, p.lds_bytes, s, a);
+}
+
+template <int MR>
+hipError_t launch_split(Prologue pro, const SplitArgs& a, const GemvPlan& p, hipStream_t s) {
     switch (p.gw) {
-        case 1: return launch_mr_gw<MR, 1>(pro, a, p, s);
-        case 2: return launch_mr_gw<MR, 2>(pro, a, p, s);
-        default: return launch_mr_gw<MR, 4>(pro, a, p, s);
+        case 1: return launch_split2<MR, 1>(pro, a, p, s);
+        case 2: return launch_split2<MR, 2>(pro, a, p, s);
+        default: return launch_split2<MR, 4>(pro, a, p, s);
     }
 }
 
@@ -347,9 +622,9 @@ int round_gw(int gw) { return gw <= 1 ? 1 : (gw <= 2 ? 2 : 4); }
 
 // ---- test hooks: the same in-register decode, written out ----
 __global__ void w4_unpack_kernel(const uint32_t* __restrict__ qw, int KB, int N, int8_t* __restrict__ q) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;     // word (n, kb)
     if (i >= int64_t(KB) * N) return;
-    const int kb = int(i / N), n = int(i % N);
+    const int n = int(i / KB), kb = int(i % KB);
     const Q4x2 d = decode_int4x8(qw[i]);
     const half2_t p[4] = {d.p04, d.p15, d.p26, d.p37};
 #pragma unroll
@@ -363,7 +638,7 @@ __global__ void w4_dequant_kernel(const uint32_t* __restrict__ qw, const uint16_
                                   int KB, int N, float* __restrict__ w) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= int64_t(KB) * N) return;
-    const int kb = int(i / N), n = int(i % N);
+    const int n = int(i / KB), kb = int(i % KB);
     const Q4x2 d = decode_int4x8(qw[i]);
     const half2_t p[4] = {d.p04, d.p15, d.p26, d.p37};
     const float s = bf16_to_f32(sc[int64_t(kb / 16) * N + n]);
@@ -380,12 +655,46 @@ __global__ void fill_zero_kernel(uint4* p, int64_t n16, unsigned char* tail, int
     if (i < ntail) tail[i] = 0;
 }
 
+bool plan_column(int M, int K, int N, GemvPlan& p) {
+    if (M > 4 || K > 32 * kColMaxChunks * kWave) return false;
+    const int nch = K / 32;
+    const int nblk = (K + 511) / 512;
+    p.mr = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+    p.ni = (nch + kWave - 1) / kWave;
+    const int ntask = p.mr * nblk;
+    const int wmin = (ntask + kColMaxTasks - 1) / kColMaxTasks;
+    if (wmin > kColMaxWaves) return false;
+    // Columns per wave: as many as the weight registers allow (CPW * NI chunks of 16
+    // bytes per lane), since each staged activation read then serves CPW columns.
+    const int want = std::max(1, (N + 255) / 256);                 // columns per workgroup for ~256 workgroups
+    p.cpw = (p.ni <= 3 && want >= 4 && p.mr <= 2) ? 4 : (p.ni <= 6 && want >= 2) ? 2 : 1;
+    p.waves = std::min(kColMaxWaves, std::max((want + p.cpw - 1) / p.cpw, wmin));
+    // a forced shape replaces the choice when the kernel has a variant for it
+    const int fc = g_col_cpw;
+    if (g_col_waves > 0 && (fc == 1 || (fc == 2 && p.ni <= 6) || (fc == 4 && p.ni <= 3))) {
+        p.cpw = fc;
+        p.waves = std::min(kColMaxWaves, std::max(g_col_waves, wmin));
+    }
+    const int C = p.waves * p.cpw;
+    if (p.groups * C > 8 * p.waves * kWave) return false;    // scale staging capacity
+    p.wgs = (N + C - 1) / C;
+    p.lds_bytes = size_t(p.mr) * 4 * (nch * 8 + 32) * 2 + size_t(p.mr) * nblk * 4 + size_t(p.mr) * nch * 4 +
+                  size_t(p.groups) * C * 4;
+    if (p.lds_bytes > kMaxLds) return false;
+    p.kind = kColumnOwning;
+    return true;
+}
+
 }  // namespace
 
 GemvPlan plan_gemv(int M, int K, int N) {
     GemvPlan p{};
-    p.tiles = (N + kGemvCols - 1) / kGemvCols;
     p.groups = K / kGroup;
+    if (g_forced_split == 0 && plan_column(M, K, N, p)) return p;
+    p = GemvPlan{};
+    p.kind = kSplitK;
+    p.groups = K / kGroup;
+    p.tiles = (N + kGemvCols - 1) / kGemvCols;
     p.mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     int gw;
     if (g_forced_split > 0) {
@@ -420,7 +729,28 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
                        void* ws, hipStream_t s) {
     const GemvPlan p = plan_gemv(M, K, N);
-    GemvArgs a{};
+    if (p.kind == kColumnOwning) {
+        ColArgs a{};
+        a.a0 = a0;
+        a.a1 = a1;
+        a.lda = lda;
+        a.qw = reinterpret_cast<const uint4*>(qw);
+        a.sc = sc;
+        a.M = M;
+        a.K = K;
+        a.N = N;
+        a.nch = K / 32;
+        a.groups = p.groups;
+        a.out_scale = out_scale;
+        a.residual = residual;
+        a.y = y;
+        switch (p.mr) {
+            case 1: return launch_col<1>(pro, a, p, s);
+            case 2: return launch_col<2>(pro, a, p, s);
+            default: return launch_col<4>(pro, a, p, s);
+        }
+    }
+    SplitArgs a{};
     a.a0 = a0;
     a.a1 = a1;
     a.lda = lda;
@@ -429,6 +759,7 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     a.M = M;
     a.K = K;
     a.N = N;
+    a.nch = K / 32;
     a.groups = p.groups;
     a.gps = p.gps;
     a.splits = p.splits;
@@ -439,11 +770,11 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     a.counters = p.splits > 1 ? static_cast<unsigned*>(ws) : nullptr;
     a.partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes) : nullptr;
     switch (p.mr) {
-        case 1: return launch_mr<1>(pro, a, p, s);
-        case 2: return launch_mr<2>(pro, a, p, s);
-        case 4: return launch_mr<4>(pro, a, p, s);
-        case 8: return launch_mr<8>(pro, a, p, s);
-        default: return launch_mr<16>(pro, a, p, s);
+        case 1: return launch_split<1>(pro, a, p, s);
+        case 2: return launch_split<2>(pro, a, p, s);
+        case 4: return launch_split<4>(pro, a, p, s);
+        case 8: return launch_split<8>(pro, a, p, s);
+        default: return launch_split<16>(pro, a, p, s);
     }
 }
 

@@ -33,7 +33,8 @@ Sources (the pages this follows, cited by title and section):
 Readings where the pages are silent (each is also listed in the design notes):
 
 * int4 words: eight weights per uint32 along K, weight k = 8*kb + j in bits
-  [4j, 4j+4), two's-complement nibbles (values -8..7), qweight [K/8, N] row-major.
+  [4j, 4j+4), two's-complement nibbles (values -8..7), qweight [N, K/8] row-major
+  (a linear layer's [out_features, in_features] orientation).
 * scales: bf16 [K/128, N], group g covering k in [128 g, 128 g + 128).
 * act = silu(g) * u is never rounded on the fused path (it is never written).
 * epilogue: y = bf16(out_scale * acc [+ residual]) with a single rounding.
@@ -104,17 +105,17 @@ def f64_to_bf16(x) -> np.ndarray:
 # int4 weights  ([P4] section 5, prologue fusion: dequantise weights as they are read)
 # ----------------------------------------------------------------------------
 def w4_unpack(qweight) -> np.ndarray:
-    """Packed words uint32 [K/8, N] -> int8 weights [K, N].
+    """Packed words uint32 [N, K/8] -> int8 weights [K, N].
 
-    Weight k = 8*kb + j of column n is nibble j of word (kb, n), a two's-complement
+    Weight k = 8*kb + j of column n is nibble j of word (n, kb), a two's-complement
     4-bit integer: codes 0..7 are 0..7, codes 8..15 are -8..-1.
     """
     w = np.asarray(qweight, dtype=np.uint32)
-    kb, n = w.shape
+    n, kb = w.shape
     out = np.empty((kb, NIB, n), dtype=np.int8)
     for j in range(NIB):
-        code = ((w >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.int16)
-        out[:, j, :] = np.where(code >= 8, code - 16, code).astype(np.int8)
+        code = ((w >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.int16)   # [n, kb]
+        out[:, j, :] = np.where(code >= 8, code - 16, code).astype(np.int8).T
     return out.reshape(kb * NIB, n)
 
 
@@ -226,11 +227,11 @@ def mlp_decode(x, r, norm_w, gu_q, gu_s, d_q, d_s, out_scale=0.5, eps=1e-6,
 
 def _chunked_gemv(a, qweight, scales, n_chunk=4096):
     """a @ dequant(W), dequantising ``n_chunk`` columns at a time to bound memory."""
-    N = qweight.shape[1]
+    N = qweight.shape[0]
     out = np.empty((a.shape[0], N), dtype=np.float64)
     for c0 in range(0, N, n_chunk):
         c1 = min(N, c0 + n_chunk)
-        out[:, c0:c1] = a @ w4_dequant(qweight[:, c0:c1], scales[:, c0:c1])
+        out[:, c0:c1] = a @ w4_dequant(qweight[c0:c1], scales[:, c0:c1])
     return out
 
 

@@ -10,12 +10,13 @@ Storage formats produced here:
 * bf16 tensors are ``numpy.uint16`` arrays of bf16 bit patterns.  Values are drawn in
   fp32 and rounded to bf16 (round to nearest, ties to even) by PyTorch's own
   ``float32 -> bfloat16`` conversion.
-* int4 weights are ``numpy.uint32`` arrays of shape ``[K/8, N]`` (row-major, N
-  contiguous).  Word ``(kb, n)`` holds the eight weights ``k = 8*kb + j`` (j = 0..7)
-  of column ``n``; weight ``j`` sits in bits ``[4j, 4j+4)`` as a two's-complement
-  nibble, so values span ``[-8, 7]``.  Drawing every word uniformly over all 2**32
-  patterns draws every nibble independently and uniformly over its 16 codes, i.e.
-  every weight uniformly over ``[-8, 7]``.
+* int4 weights are ``numpy.uint32`` arrays of shape ``[N, K/8]`` (row-major, the
+  orientation of a linear layer's ``[out_features, in_features]`` weight, so the K
+  values of one output column are contiguous).  Word ``(n, kb)`` holds the eight
+  weights ``k = 8*kb + j`` (j = 0..7) of column ``n``; weight ``j`` sits in bits
+  ``[4j, 4j+4)`` as a two's-complement nibble, so values span ``[-8, 7]``.  Drawing
+  every word uniformly over all 2**32 patterns draws every nibble independently and
+  uniformly over its 16 codes, i.e. every weight uniformly over ``[-8, 7]``.
 * group scales are bf16 ``[K/128, N]`` (row-major), scale ``(g, n)`` applying to
   ``k`` in ``[128 g, 128 g + 128)``, drawn uniformly from ``[0.005, 0.02)``.
 
@@ -54,7 +55,7 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 
 def pack_int4(q: np.ndarray) -> np.ndarray:
-    """Pack int values in [-8, 7], shape [K, N] with K % 8 == 0, into uint32 [K/8, N].
+    """Pack int values in [-8, 7], shape [K, N] with K % 8 == 0, into uint32 [N, K/8].
 
     Used to build hand-made weight matrices for tests; random workloads draw the
     packed words directly.
@@ -65,10 +66,10 @@ def pack_int4(q: np.ndarray) -> np.ndarray:
     if q.min(initial=0) < -8 or q.max(initial=0) > 7:
         raise ValueError("int4 values must lie in [-8, 7]")
     codes = (q.astype(np.int64) & 0xF).astype(np.uint32)          # two's complement nibble
-    codes = codes.reshape(q.shape[0] // PACK, PACK, q.shape[1])
-    words = np.zeros((q.shape[0] // PACK, q.shape[1]), dtype=np.uint32)
+    codes = codes.reshape(q.shape[0] // PACK, PACK, q.shape[1])    # [kb, j, n]
+    words = np.zeros((q.shape[1], q.shape[0] // PACK), dtype=np.uint32)
     for j in range(PACK):
-        words |= codes[:, j, :] << np.uint32(4 * j)
+        words |= codes[:, j, :].T << np.uint32(4 * j)
     return words
 
 
@@ -89,7 +90,7 @@ def _scales_bf16(rng, shape):
 
 
 def _qweight(rng, K, N):
-    return rng.integers(0, 2**32, size=(K // PACK, N), dtype=np.uint32)
+    return rng.integers(0, 2**32, size=(N, K // PACK), dtype=np.uint32)
 
 
 # ----------------------------------------------------------------------------
@@ -97,16 +98,16 @@ def _qweight(rng, K, N):
 # ----------------------------------------------------------------------------
 @dataclass
 class W4:
-    qweight: np.ndarray   # uint32 [K/8, N]
+    qweight: np.ndarray   # uint32 [N, K/8]
     scales: np.ndarray    # uint16 (bf16 bits) [K/128, N]
 
     @property
     def K(self):
-        return self.qweight.shape[0] * PACK
+        return self.qweight.shape[1] * PACK
 
     @property
     def N(self):
-        return self.qweight.shape[1]
+        return self.qweight.shape[0]
 
 
 def w4_weight(rng, K, N) -> W4:

@@ -30,7 +30,7 @@ def check_layer(L, x, r, got, resid):
     w = [assert_close(got["y"], y, "y")]
     gu = O.w4_gemv(got["y"], L.gate_up.qweight, L.gate_up.scales)
     w.append(assert_close(got["gu"], gu, "gate_up"))
-    I = L.down.qweight.shape[0] * 8
+    I = L.down.qweight.shape[1] * 8
     out = O.swiglu_w4_gemv(got["gu"][:, :I], got["gu"][:, I:], L.down.qweight, L.down.scales, L.out_scale,
                            got["h"] if resid else None)
     w.append(assert_close(got["out"], out, "out"))

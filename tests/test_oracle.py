@@ -74,7 +74,7 @@ def from_bits_t(t):
 
 def brute_force_gemv(g, u, qw, sc, out_scale, residual=None):
     M, K = g.shape
-    N = qw.shape[1]
+    N = qw.shape[0]
     out = np.zeros((M, N))
     for m in range(M):
         for n in range(N):
@@ -82,7 +82,7 @@ def brute_force_gemv(g, u, qw, sc, out_scale, residual=None):
             for k in range(K):
                 gv, uv = bf16_bits_to_float(g[m, k]), bf16_bits_to_float(u[m, k])
                 a = gv / (1.0 + math.exp(-gv)) * uv
-                code = (int(qw[k // 8, n]) >> (4 * (k % 8))) & 0xF
+                code = (int(qw[n, k // 8]) >> (4 * (k % 8))) & 0xF
                 qv = code - 16 if code >= 8 else code
                 tot += a * qv * bf16_bits_to_float(sc[k // 128, n])
             v = tot * out_scale
@@ -151,8 +151,8 @@ def test_bf16_round_matches_bitwise_rounding_on_random_f64():
 def test_unpack_every_code_every_position():
     for j in range(8):
         for code in range(16):
-            w = np.zeros((1, 3), dtype=np.uint32)
-            w[0, 1] = np.uint32(code << (4 * j))
+            w = np.zeros((3, 1), dtype=np.uint32)          # [N = 3, K/8 = 1]
+            w[1, 0] = np.uint32(code << (4 * j))
             q = O.w4_unpack(w)
             want = code - 16 if code >= 8 else code
             assert q.shape == (8, 3)
@@ -166,7 +166,7 @@ def test_pack_unpack_round_trip():
     rng = np.random.default_rng(3)
     q = rng.integers(-8, 8, size=(256, 24)).astype(np.int8)
     assert np.array_equal(O.w4_unpack(synth.pack_int4(q)), q)
-    words = rng.integers(0, 2**32, size=(16, 5), dtype=np.uint32)
+    words = rng.integers(0, 2**32, size=(5, 16), dtype=np.uint32)
     assert np.array_equal(synth.pack_int4(O.w4_unpack(words)), words)
 
 
@@ -354,10 +354,10 @@ def _py_round(x):
 
 def _py_layer(x, r, nw, guq, gus, dq, ds, s, eps, residual_in_epilogue):
     M, H = x.shape
-    I = guq.shape[1] // 2
+    I = guq.shape[0] // 2
 
     def wq(qw, sc, k, n):
-        code = (int(qw[k // 8, n]) >> (4 * (k % 8))) & 0xF
+        code = (int(qw[n, k // 8]) >> (4 * (k % 8))) & 0xF
         return (code - 16 if code >= 8 else code) * bf16_bits_to_float(sc[k // 128, n])
 
     outs = {"h": [], "y": [], "gu": [], "out": []}
