@@ -294,15 +294,15 @@ FDEC_API int fdec_w4_dequant(const fdec_w4* W, float* w_out, fdec_stream stream)
  * fdec_set_gemv_split(k): force the split-K GEMV kernel with K split into about k
  *   parts per column tile (0 restores the built-in choice of kernel and split; values
  *   that do not fit the shape are clamped).
- * fdec_set_gemv_tiling(waves, cols_per_wave): force the column-owning GEMV kernel's
- *   workgroup shape (waves in 1..8, columns per wave in {1, 2, 4}); (0, 0) restores
- *   the built-in choice.  Shapes the kernel cannot take fall back to the built-in one.
+ * fdec_set_gemv_tiling(waves, cols_per_workgroup): force the column-owning GEMV
+ *   kernel's workgroup shape (1..8 waves, each owning at most 4 columns); (0, 0)
+ *   restores the built-in choice.  Shapes the kernel cannot take fall back to it.
  * fdec_test_fail_launches(on): while on, every compute call validates its arguments
  *   and then returns FDEC_ERR_HIP without touching the GPU (exercises the error path
  *   on machines without a GPU).
  */
 FDEC_API void fdec_set_gemv_split(int32_t k);
-FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_wave);
+FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_workgroup);
 FDEC_API void fdec_test_fail_launches(int32_t on);
 
 #ifdef __cplusplus

@@ -479,8 +479,8 @@ def set_gemv_split(k: int):
     lib().fdec_set_gemv_split(int(k))
 
 
-def set_gemv_tiling(waves: int, cols_per_wave: int):
-    lib().fdec_set_gemv_tiling(int(waves), int(cols_per_wave))
+def set_gemv_tiling(waves: int, cols_per_workgroup: int):
+    lib().fdec_set_gemv_tiling(int(waves), int(cols_per_workgroup))
 
 
 def test_fail_launches(on: bool):

@@ -270,9 +270,9 @@ FDEC_API const char* fdec_status_str(int status) {
 FDEC_API const char* fdec_last_error(void) { return t_last_error.c_str(); }
 
 FDEC_API void fdec_set_gemv_split(int32_t k) { g_forced_split = k > 0 ? k : 0; }
-FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_wave) {
+FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_workgroup) {
     g_col_waves = waves > 0 ? waves : 0;
-    g_col_cpw = cols_per_wave > 0 ? cols_per_wave : 0;
+    g_col_cols = cols_per_workgroup > 0 ? cols_per_workgroup : 0;
 }
 FDEC_API void fdec_test_fail_launches(int32_t on) { g_fail_launches = on ? 1 : 0; }
 

@@ -89,6 +89,11 @@ __device__ __forceinline__ Q4x2 decode_int4x8_biased(uint32_t w) {
     return q;
 }
 
+// Two fp32 values to one packed fp16 pair, rounding toward zero (one instruction).
+__device__ __forceinline__ half2_t pk_f16_rtz(float a, float b) {
+    return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
 // Position of weight j (0..7) of a word in the pair order above.
 __host__ __device__ constexpr int pair_slot(int j) { return 2 * (j & 3) + (j >> 2); }
 

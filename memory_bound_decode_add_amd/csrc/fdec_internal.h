@@ -20,7 +20,8 @@ constexpr int kGemvCols = 64;
 constexpr int kGroup = 128;
 constexpr int kColMaxTasks = 8;      // activation tasks (row, 512-wide block) per wave, column kernel
 constexpr int kColMaxWaves = 8;      // waves per workgroup, column kernel (256 VGPRs per lane)
-constexpr int kColMaxChunks = 8;     // 32-wide K chunks per lane, column kernel
+constexpr int kColMaxChunks = 8;
+constexpr int kColScLoads = 4;       // 16-byte scale loads per thread, column kernel     // 32-wide K chunks per lane, column kernel
 constexpr size_t kMaxLds = 160 * 1024;
 
 enum GemvKind { kColumnOwning = 0, kSplitK = 1 };
@@ -31,7 +32,8 @@ struct GemvPlan {
     int groups;       // K / 128
     // column-owning kernel
     int waves;        // waves per workgroup
-    int cpw;          // columns per wave (1 or 4)
+    int cpw;          // most columns any wave owns (1..4)
+    int cols;         // columns per workgroup
     int ni;           // 32-wide K chunks per lane
     int wgs;          // workgroups
     // split-K kernel
@@ -80,6 +82,6 @@ hipError_t launch_eager_rmsnorm(const uint16_t* x, const uint16_t* r, const uint
 
 extern int g_forced_split;   // fdec_set_gemv_split
 extern int g_col_waves;      // fdec_set_gemv_tiling
-extern int g_col_cpw;
+extern int g_col_cols;
 
 }  // namespace fdec

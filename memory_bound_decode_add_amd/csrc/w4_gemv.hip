@@ -12,40 +12,37 @@
 // Weights: qweight uint32 [N][K/8] (the K values of a column are contiguous, 8 per
 // word), scales bf16 [K/128][N].
 //
-// Shared by both kernels:
-//  * Prologue.  A wave computes the activation of one 128-wide K group of one row
-//    (2 values per lane) in fp32 and stores it to LDS as fp16 scaled by a power of two
-//    2^-E chosen from the group's largest magnitude, so the largest value lands in
-//    [2^14, 2^15): any finite fp32 activation fits fp16 with an 11-bit significand
-//    relative to its group's maximum.  2^E is folded back in with the group scale.
-//    Values are stored in the pair order of the int4 decode (decode_int4x8), so four
-//    v_dot2_f32_f16 consume one packed word.
-//  * Dot.  Per packed word: XOR, shift, four AND-OR and four packed fp16 ops give four
-//    exact fp16 pairs of weights; four dot2 accumulate them in fp32.  The group scale
-//    times 2^E multiplies each 32-wide partial sum once.
-//  * Every global load is issued before any arithmetic, from addresses clamped into
-//    the tensors (no branches around loads), activation inputs first, so the prologue
-//    runs while the weights are still in flight.
+// Both kernels stage the activation in LDS as block-scaled fp16: a block of values is
+// multiplied by a power of two 2^-E chosen from its largest magnitude so that this
+// magnitude lands in [2^14, 2^15) (any finite fp32 activation then fits fp16 with an
+// 11-bit significand relative to its block's maximum), and 2^E is folded back in with
+// the group scale.  Values are stored in the pair order of the int4 decode, so four
+// v_dot2_f32_f16 consume one packed word with fp32 accumulation.  Every global load is
+// issued before any arithmetic, from addresses clamped into the tensors, activation
+// inputs first, so the prologue runs while the weights are still in flight.
 //
-// Column-owning kernel (M <= 4, K <= 16384).  A workgroup of W waves owns W*CPW
-// consecutive columns; each wave owns CPW of them over the whole K.  Lane l loads the
-// 16-byte chunks (32 consecutive k) l, l+64, ... of each of the wave's columns, so one
-// load instruction reads 1 KB of contiguous weights, and one read of the staged
-// activation of a chunk (64 bytes, conflict-free layout) serves all CPW columns.  The
-// workgroup stages the activation of the full K and the group scales of its columns
-// in LDS once.  A column's sum is reduced across the wave with DPP and scalar lane
-// reads, and one lane applies the epilogue.  There is no cross-workgroup step and no
-// workspace; results do not depend on scheduling.
+// Column-owning kernel (M <= 4, K <= 16384).  A workgroup of W waves owns C consecutive
+// columns; wave w owns columns w, w + W, ... (at most CPW) over the whole K.  Lane l
+// loads the 16-byte chunks (32 consecutive k) l, l+64, ... of each of the wave's
+// columns, so one load instruction reads 1 KB of contiguous weights, and one read of
+// the staged activation of a chunk serves all of the wave's columns.  The workgroup
+// stages the activation of the full K (fp16 blocks of 32, offsets folded per chunk,
+// see stage_word_col) and the group scales of its columns in LDS once.  A column's
+// sum is reduced across the wave with DPP and scalar lane reads, and one lane applies
+// the epilogue.  There is no cross-workgroup step and no workspace; results do not
+// depend on scheduling.
 //
 // Split-K kernel (M <= 16, any K).  A 256-thread workgroup owns a 64-column tile and
 // a slice of whole 128-wide groups; wave w owns groups w, w+4, ... of the slice; lane
 // (kr = lane % 4, cq = lane / 4) owns columns 4cq..4cq+3 and packed words 4kr..4kr+3
-// of each group of those columns.  The quad of lanes sharing columns reduces with DPP,
-// the waves through LDS.  With several slices each workgroup writes fp32 partials to
-// the workspace with device-scope atomic stores, waits for them to complete, then bumps
-// the tile's arrival counter; the last to arrive reads the partials back with
-// device-scope atomic loads, sums them in slice order, applies the epilogue and resets
-// the counter.
+// of each group of those columns.  The activation of a group is staged in blocks of
+// 128 (2 values per lane) and the weights are decoded to exact fp16 (XOR, shift, four
+// AND-OR and four packed fp16 ops per word).  The quad of lanes sharing columns reduces
+// with DPP, the waves through LDS.  With several slices each workgroup writes fp32
+// partials to the workspace with device-scope atomic stores, waits for them to
+// complete, then bumps the tile's arrival counter; the last to arrive reads the partials
+// back with device-scope atomic loads, sums them in slice order, applies the epilogue
+// and resets the counter.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -55,7 +52,7 @@ namespace fdec {
 
 int g_forced_split = 0;
 int g_col_waves = 0;
-int g_col_cpw = 0;
+int g_col_cols = 0;
 
 namespace {
 
@@ -123,6 +120,7 @@ struct ColArgs {
     int M, K, N;
     int nch;                // K / 32
     int groups;             // K / 128
+    int cols;               // columns per workgroup (column kernel)
     const float* out_scale;
     const uint16_t* residual;
     uint16_t* y;
@@ -138,20 +136,23 @@ struct ColArgs {
 // j (bits 0..3 of a half) decodes to 1032 + q, at an odd position (bits 4..7) to
 // 1152 + 16 q.  Odd-position activations are staged divided by 16, so each product is
 // a*q plus a per-k offset 1032*a or 72*a that does not depend on the weight; the
-// staging phase sums those offsets per chunk (bias_s) and the dot phase subtracts them.
-// Every staged value and every product is exact; what changes is that the fp32 sums
-// now also carry the offset terms, about 1032/|q| times larger than the wanted ones,
-// so a chunk's dot keeps roughly 10 fewer significant bits (relative error ~1e-4).
+// staging phase sums those offsets per chunk and the dot phase subtracts them.  Every
+// staged value and every product is exact; what changes is that the fp32 sums now also
+// carry the offset terms, about 1032/|q| times larger than the wanted ones, so a
+// chunk's dot keeps roughly 10 fewer significant bits (relative error ~1e-4).
 //
 // Staging task: one row and 512 consecutive k; lane l takes the 8 values of packed word
-// l of the block (16-byte loads of g and u), writes them as one 16-byte LDS store, and
-// the quad of lanes holding one chunk sums its offsets.  The block's power-of-two scale
-// 2^E puts its largest magnitude in [2^14, 2^15).
+// l of the block (16-byte loads of g and u) and writes them as one 16-byte LDS store.
+// The four lanes of a quad hold one 32-wide chunk: they share the chunk's power-of-two
+// scale 2^E (its largest magnitude lands in [2^14, 2^15), so no value overflows fp16)
+// and sum its offsets; lane 0 of the quad stores (2^E, offset sum) for the chunk.
+// fp32 -> fp16 rounds toward zero (one packed conversion per pair); the offsets are
+// summed from the rounded values, so they cancel exactly whatever the rounding.
 __device__ __forceinline__ int col_quarter_stride(int nch) { return nch * 8 + 32; }
 
 template <int PRO>
 __device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, bool live, bool in_k,
-                                               int lane, _Float16* dst, float* esc, float* bias_dst) {
+                                               bool quad_lead, _Float16* dst, float2* eb_dst) {
     float v[8];                                    // k = 8w + j, j = 0..7
     const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
     const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
@@ -171,33 +172,41 @@ __device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, b
         v[j] = live ? v[j] : 0.f;
         mx = fmaxf(mx, fabsf(v[j]));
     }
-    mx = wave_max_uniform(mx);
+    mx = fmaxf(mx, dpp<kQuadSwap1>(mx));
+    mx = fmaxf(mx, dpp<kQuadSwap2>(mx));           // the chunk's largest magnitude
     int e = 0;
     (void)__builtin_frexpf(mx, &e);
     const int E = min(max(e - 15, -126), 127);
     const float down = __builtin_ldexpf(1.0f, -E);
     const float down16 = down * 0.0625f;
     // slot order (j0, j4, j1, j5, j2, j6, j3, j7); odd j stored divided by 16
-    const _Float16 h0 = (_Float16)(v[0] * down), h4 = (_Float16)(v[4] * down);
-    const _Float16 h1 = (_Float16)(v[1] * down16), h5 = (_Float16)(v[5] * down16);
-    const _Float16 h2 = (_Float16)(v[2] * down), h6 = (_Float16)(v[6] * down);
-    const _Float16 h3 = (_Float16)(v[3] * down16), h7 = (_Float16)(v[7] * down16);
-    typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-    const half8_t pk = {h0, h4, h1, h5, h2, h6, h3, h7};
-    if (in_k) *reinterpret_cast<half8_t*>(dst) = pk;
-    if (lane == 0) *esc = __builtin_ldexpf(1.0f, E);
-    float b = 1032.0f * ((float(h0) + float(h4)) + (float(h2) + float(h6))) +
-              1152.0f * ((float(h1) + float(h5)) + (float(h3) + float(h7)));
+    const half2_t p0 = pk_f16_rtz(v[0] * down, v[4] * down);
+    const half2_t p1 = pk_f16_rtz(v[1] * down16, v[5] * down16);
+    const half2_t p2 = pk_f16_rtz(v[2] * down, v[6] * down);
+    const half2_t p3 = pk_f16_rtz(v[3] * down16, v[7] * down16);
+    if (in_k)
+        *reinterpret_cast<uint4*>(dst) = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+    const half2_t even = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2_t odd = {(_Float16)1152.0f, (_Float16)1152.0f};
+    float b = dot2(p0, even, 0.f);
+    b = dot2(p2, even, b);
+    b = dot2(p1, odd, b);
+    b = dot2(p3, odd, b);
     b += dpp<kQuadSwap1>(b);
-    b += dpp<kQuadSwap2>(b);                       // the chunk's four words are one quad
-    if ((lane & 3) == 0 && in_k) *bias_dst = b;
+    b += dpp<kQuadSwap2>(b);
+    if (quad_lead && in_k) *eb_dst = make_float2(__builtin_ldexpf(1.0f, E), b);
 }
 
+// Wave w of a W-wave workgroup owning C columns handles the columns w, w + W, w + 2W,
+// ... below C (at most CPW of them), so the columns spread over the four SIMDs as
+// evenly as C allows; staging tasks go to the waves in reverse order, the waves with
+// fewer columns taking the extra tasks.
 template <int MR, int CPW, int NI, int PRO>
 __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int W = blockDim.x >> 6;
-    const int C = W * CPW;                         // columns per workgroup
+    const int C = a.cols;                          // columns per workgroup
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -205,19 +214,18 @@ __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColAr
     const int qs = col_quarter_stride(a.nch);      // halves
     const int kw = a.K >> 3;                       // packed words per row
     _Float16* act_s = reinterpret_cast<_Float16*>(smem);                          // [MR][4][qs]
-    float* esc_s = reinterpret_cast<float*>(smem + size_t(MR) * 4 * qs * 2);      // [MR][nblk]
-    float* bias_s = esc_s + MR * nblk;                                             // [MR][nch]
-    float* sc_s = bias_s + MR * a.nch;                                             // [groups][C]
+    float2* eb_s = reinterpret_cast<float2*>(smem + size_t(MR) * 4 * qs * 2);     // [MR][nch]
+    float* sc_s = reinterpret_cast<float*>(eb_s + MR * a.nch);                     // [groups][C]
 
     const int col0 = blockIdx.x * C;
-    const int nw = col0 + wave * CPW;              // this wave's first column
 
-    // ---- 1. activation inputs: task t = wave + W * ti -> (row t % MR, block t / MR) ----
+    // ---- 1. activation inputs: task t -> (row t % MR, block t / MR), wave W-1 - t % W ----
     const int ntask = MR * nblk;
+    const int tw = W - 1 - wave;
     uint4 ga[kColMaxTasks], ua[kColMaxTasks];
 #pragma unroll
     for (int ti = 0; ti < kColMaxTasks; ++ti) {
-        const int t = wave + W * ti;
+        const int t = tw + W * ti;
         if (t >= ntask) break;                     // uniform across the wave
         const int m = min(t % MR, a.M - 1), b = t / MR;
         const int k = min(b * 64 + lane, kw - 1) * 8;
@@ -225,93 +233,107 @@ __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColAr
         ua[ti] = PRO == kSwiGLU ? *reinterpret_cast<const uint4*>(a.a1 + size_t(m) * a.lda + k) : make_uint4(0, 0, 0, 0);
     }
     // ---- 2. group scales of this workgroup's columns, epilogue inputs ----
-    constexpr int kScPer = 8;
-    const int nsc = a.groups * C;
-    uint16_t sraw[kScPer];
+    // the scales of columns [col0, col0 + C) are read as aligned 8-column pieces of each
+    // group's row: item (g, p) is the piece (col0 / 8 + p) of group g
+    const int p0 = col0 >> 3;
+    const int npc = ((min(col0 + C, a.N) - 1) >> 3) - p0 + 1;
+    const int nsc = a.groups * npc;
+    uint4 sraw[kColScLoads];
 #pragma unroll
-    for (int r = 0; r < kScPer; ++r) {
+    for (int r = 0; r < kColScLoads; ++r) {
         if (r * int(blockDim.x) >= nsc) break;     // uniform
         const int idx = min(tid + r * int(blockDim.x), nsc - 1);
-        const int g = idx / C, cc = idx % C;
-        sraw[r] = a.sc[size_t(g) * a.N + min(col0 + cc, a.N - 1)];
+        const int g = idx / npc, pc = p0 + idx % npc;
+        sraw[r] = *reinterpret_cast<const uint4*>(a.sc + size_t(g) * a.N + pc * 8);
     }
-    // lane l < MR*CPW finishes output (row l / CPW, column nw + l % CPW)
-    const int em = lane / CPW, en = nw + lane % CPW;
-    const bool owner = lane < MR * CPW && em < a.M && en < a.N;
-    float res = 0.f;
-    if (a.residual) res = bf16_to_f32(a.residual[size_t(min(em, a.M - 1)) * a.N + min(en, a.N - 1)]);
+    // lane l < MR*CPW finishes output (row l / CPW, column col0 + wave + W * (l % CPW))
+    const int em = lane / CPW, ecc = wave + W * (lane % CPW), en = col0 + ecc;
+    const bool owner = lane < MR * CPW && em < a.M && ecc < C && en < a.N;
+    const uint16_t* rsrc = a.residual ? a.residual : a.y;   // y: a readable stand-in, value unused
+    const uint16_t rraw = rsrc[size_t(min(em, a.M - 1)) * a.N + min(en, a.N - 1)];
     const float os = a.out_scale ? *a.out_scale : 1.0f;
     // ---- 3. weight chunks: lane l takes chunks l, l+64, ... of each of the wave's columns ----
+    // (unconditional: a slot the wave does not own re-reads its first column, so the
+    // number of loads in flight is the same on every path and the prologue's waits for
+    // the activation loads never wait for weights)
     uint4 wv[NI][CPW];
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+    for (int j = 0; j < CPW; ++j) {
+        const int cj = wave + W * j < C ? wave + W * j : wave;
+        const uint4* colp = a.qw + size_t(min(col0 + cj, a.N - 1)) * a.nch;
 #pragma unroll
-        for (int j = 0; j < CPW; ++j)
-            wv[i][j] = a.qw[size_t(min(nw + j, a.N - 1)) * a.nch + min(lane + kWave * i, a.nch - 1)];
+        for (int i = 0; i < NI; ++i) wv[i][j] = colp[min(lane + kWave * i, a.nch - 1)];
+    }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 4. prologue: activations, per-chunk offsets and scales to LDS ----
+    // ---- 4. prologue: activations, per-chunk scale and offsets, group scales to LDS ----
     // word wi = 64 b + lane: chunk wi / 4, quarter wi % 4
     const int lofs = (lane & 3) * qs + (lane >> 2) * 8;
 #pragma unroll
     for (int ti = 0; ti < kColMaxTasks; ++ti) {
-        const int t = wave + W * ti;
+        const int t = tw + W * ti;
         if (t >= ntask) break;                     // uniform across the wave
         const int m = t % MR, b = t / MR;
         const bool in_k = b * 64 + lane < kw;      // a chunk lies wholly inside or outside K
-        stage_word_col<PRO>(ga[ti], ua[ti], in_k && m < a.M, in_k, lane,
-                            act_s + size_t(m) * 4 * qs + lofs + b * 128, esc_s + m * nblk + b,
-                            bias_s + m * a.nch + b * 16 + (lane >> 2));
+        stage_word_col<PRO>(ga[ti], ua[ti], in_k && m < a.M, in_k, (lane & 3) == 0,
+                            act_s + size_t(m) * 4 * qs + lofs + b * 128,
+                            eb_s + m * a.nch + b * 16 + (lane >> 2));
     }
 #pragma unroll
-    for (int r = 0; r < kScPer; ++r) {
-        const int idx = tid + r * int(blockDim.x);
+    for (int r = 0; r < kColScLoads; ++r) {
         if (r * int(blockDim.x) >= nsc) break;
-        if (idx < nsc) sc_s[idx] = bf16_to_f32(sraw[r]);
+        const int idx = tid + r * int(blockDim.x);
+        if (idx < nsc) {
+            const int g = idx / npc, cc0 = (p0 + idx % npc) * 8 - col0;
+            const uint32_t wd[4] = {sraw[r].x, sraw[r].y, sraw[r].z, sraw[r].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int cc = cc0 + e;
+                if (cc >= 0 && cc < C) sc_s[g * C + cc] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+            }
+        }
     }
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 5. dot products: one activation read per chunk serves the wave's CPW columns ----
+    // ---- 5. dot products: one activation read per chunk serves the wave's columns ----
     float acc[MR][CPW];
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int j = 0; j < CPW; ++j) acc[m][j] = 0.f;
-    const int cw = wave * CPW;                     // first column index within the workgroup
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int c = lane + kWave * i;
         if (c < a.nch) {
-            float s[CPW];
-#pragma unroll
-            for (int j = 0; j < CPW; ++j) s[j] = sc_s[(c >> 2) * C + cw + j];
-            Q4x2 q[CPW][4];
-#pragma unroll
-            for (int j = 0; j < CPW; ++j) {
-                const uint32_t wd[4] = {wv[i][j].x, wv[i][j].y, wv[i][j].z, wv[i][j].w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) q[j][h] = decode_int4x8_biased(wd[h]);
-            }
+            uint4 av[MR][4];
+            float2 eb[MR];
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 const _Float16* arow = act_s + size_t(m) * 4 * qs + c * 8;
-                uint4 av[4];
 #pragma unroll
-                for (int h = 0; h < 4; ++h) av[h] = *reinterpret_cast<const uint4*>(arow + h * qs);
-                const float bias = bias_s[m * a.nch + c];
-                const float e = esc_s[m * nblk + (c >> 4)];
+                for (int h = 0; h < 4; ++h) av[m][h] = *reinterpret_cast<const uint4*>(arow + h * qs);
+                eb[m] = eb_s[m * a.nch + c];
+            }
 #pragma unroll
-                for (int j = 0; j < CPW; ++j) {
-                    float d = -bias;
+            for (int j = 0; j < CPW; ++j) {
+                if (wave + W * j >= C) break;      // uniform
+                const float s = sc_s[(c >> 2) * C + wave + W * j];
+                const uint32_t wd[4] = {wv[i][j].x, wv[i][j].y, wv[i][j].z, wv[i][j].w};
+                Q4x2 q[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) q[h] = decode_int4x8_biased(wd[h]);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    float d = -eb[m].y;
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
-                        d = dot2(q[j][h].p04, __builtin_bit_cast(half2_t, av[h].x), d);
-                        d = dot2(q[j][h].p15, __builtin_bit_cast(half2_t, av[h].y), d);
-                        d = dot2(q[j][h].p26, __builtin_bit_cast(half2_t, av[h].z), d);
-                        d = dot2(q[j][h].p37, __builtin_bit_cast(half2_t, av[h].w), d);
+                        d = dot2(q[h].p04, __builtin_bit_cast(half2_t, av[m][h].x), d);
+                        d = dot2(q[h].p15, __builtin_bit_cast(half2_t, av[m][h].y), d);
+                        d = dot2(q[h].p26, __builtin_bit_cast(half2_t, av[m][h].z), d);
+                        d = dot2(q[h].p37, __builtin_bit_cast(half2_t, av[m][h].w), d);
                     }
-                    acc[m][j] = fmaf(d, s[j] * e, acc[m][j]);
+                    acc[m][j] = fmaf(d, s * eb[m].x, acc[m][j]);
                 }
             }
         }
@@ -320,9 +342,10 @@ __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColAr
     // ---- 6. reduce each column over the wave; the owning lane applies the epilogue ----
     float mine = 0.f;
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
+    for (int j = 0; j < CPW; ++j) {
+        if (wave + W * j >= C) break;              // uniform
 #pragma unroll
-        for (int j = 0; j < CPW; ++j) {
+        for (int m = 0; m < MR; ++m) {
             float v = acc[m][j];
             v += dpp<kQuadSwap1>(v);
             v += dpp<kQuadSwap2>(v);
@@ -335,6 +358,8 @@ __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColAr
                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
             mine = lane == m * CPW + j ? v : mine;
         }
+    }
+    const float res = a.residual ? bf16_to_f32(rraw) : 0.f;
     if (owner) a.y[size_t(em) * a.N + en] = f32_to_bf16(fmaf(mine, os, res));
 }
 
@@ -569,36 +594,43 @@ hipError_t launch_col3(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStr
     return launch(w4_gemv_col_kernel<MR, CPW, NI, kIdentity>, dim3(p.wgs), p.waves * kWave, p.lds_bytes, s, a);
 }
 
-// Only the (CPW, NI) pairs plan_column can choose are instantiated: CPW = 4 with NI <= 3,
-// CPW = 2 with NI <= 6, CPW = 1 with NI <= 8 (the weight registers of a lane).
+// Only the (CPW, NI) pairs col_cpw_max allows are instantiated.
 template <int MR>
 hipError_t launch_col(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStream_t s) {
-    if (p.cpw == 4) {
-        switch (p.ni) {
-            case 1: return launch_col3<MR, 4, 1>(pro, a, p, s);
-            case 2: return launch_col3<MR, 4, 2>(pro, a, p, s);
-            default: return launch_col3<MR, 4, 3>(pro, a, p, s);
-        }
-    }
-    if (p.cpw == 2) {
-        switch (p.ni) {
-            case 1: return launch_col3<MR, 2, 1>(pro, a, p, s);
-            case 2: return launch_col3<MR, 2, 2>(pro, a, p, s);
-            case 3: return launch_col3<MR, 2, 3>(pro, a, p, s);
-            case 4: return launch_col3<MR, 2, 4>(pro, a, p, s);
-            case 5: return launch_col3<MR, 2, 5>(pro, a, p, s);
-            default: return launch_col3<MR, 2, 6>(pro, a, p, s);
-        }
-    }
-    switch (p.ni) {
-        case 1: return launch_col3<MR, 1, 1>(pro, a, p, s);
-        case 2: return launch_col3<MR, 1, 2>(pro, a, p, s);
-        case 3: return launch_col3<MR, 1, 3>(pro, a, p, s);
-        case 4: return launch_col3<MR, 1, 4>(pro, a, p, s);
-        case 5: return launch_col3<MR, 1, 5>(pro, a, p, s);
-        case 6: return launch_col3<MR, 1, 6>(pro, a, p, s);
-        case 7: return launch_col3<MR, 1, 7>(pro, a, p, s);
-        default: return launch_col3<MR, 1, 8>(pro, a, p, s);
+    switch (p.cpw) {
+        case 4:
+            switch (p.ni) {
+                case 1: return launch_col3<MR, 4, 1>(pro, a, p, s);
+                case 2: return launch_col3<MR, 4, 2>(pro, a, p, s);
+                default: return launch_col3<MR, 4, 3>(pro, a, p, s);
+            }
+        case 3:
+            switch (p.ni) {
+                case 1: return launch_col3<MR, 3, 1>(pro, a, p, s);
+                case 2: return launch_col3<MR, 3, 2>(pro, a, p, s);
+                case 3: return launch_col3<MR, 3, 3>(pro, a, p, s);
+                default: return launch_col3<MR, 3, 4>(pro, a, p, s);
+            }
+        case 2:
+            switch (p.ni) {
+                case 1: return launch_col3<MR, 2, 1>(pro, a, p, s);
+                case 2: return launch_col3<MR, 2, 2>(pro, a, p, s);
+                case 3: return launch_col3<MR, 2, 3>(pro, a, p, s);
+                case 4: return launch_col3<MR, 2, 4>(pro, a, p, s);
+                case 5: return launch_col3<MR, 2, 5>(pro, a, p, s);
+                default: return launch_col3<MR, 2, 6>(pro, a, p, s);
+            }
+        default:
+            switch (p.ni) {
+                case 1: return launch_col3<MR, 1, 1>(pro, a, p, s);
+                case 2: return launch_col3<MR, 1, 2>(pro, a, p, s);
+                case 3: return launch_col3<MR, 1, 3>(pro, a, p, s);
+                case 4: return launch_col3<MR, 1, 4>(pro, a, p, s);
+                case 5: return launch_col3<MR, 1, 5>(pro, a, p, s);
+                case 6: return launch_col3<MR, 1, 6>(pro, a, p, s);
+                case 7: return launch_col3<MR, 1, 7>(pro, a, p, s);
+                default: return launch_col3<MR, 1, 8>(pro, a, p, s);
+            }
     }
 }
 
@@ -655,6 +687,10 @@ __global__ void fill_zero_kernel(uint4* p, int64_t n16, unsigned char* tail, int
     if (i < ntail) tail[i] = 0;
 }
 
+// Largest columns-per-wave the weight registers allow (CPW * NI chunks of 16 bytes
+// per lane); only these (CPW, NI) pairs are instantiated.
+int col_cpw_max(int ni) { return ni <= 3 ? 4 : ni <= 4 ? 3 : ni <= 6 ? 2 : 1; }
+
 bool plan_column(int M, int K, int N, GemvPlan& p) {
     if (M > 4 || K > 32 * kColMaxChunks * kWave) return false;
     const int nch = K / 32;
@@ -662,24 +698,27 @@ bool plan_column(int M, int K, int N, GemvPlan& p) {
     p.mr = M <= 1 ? 1 : M <= 2 ? 2 : 4;
     p.ni = (nch + kWave - 1) / kWave;
     const int ntask = p.mr * nblk;
-    const int wmin = (ntask + kColMaxTasks - 1) / kColMaxTasks;
-    if (wmin > kColMaxWaves) return false;
-    // Columns per wave: as many as the weight registers allow (CPW * NI chunks of 16
-    // bytes per lane), since each staged activation read then serves CPW columns.
-    const int want = std::max(1, (N + 255) / 256);                 // columns per workgroup for ~256 workgroups
-    p.cpw = (p.ni <= 3 && want >= 4 && p.mr <= 2) ? 4 : (p.ni <= 6 && want >= 2) ? 2 : 1;
-    p.waves = std::min(kColMaxWaves, std::max((want + p.cpw - 1) / p.cpw, wmin));
+    if (ntask > kColMaxWaves * kColMaxTasks) return false;
+    const int cmax = col_cpw_max(p.ni);
+    // Eight waves (two per SIMD: one wave per SIMD issues VALU work at about half rate)
+    // and about N / 256 columns per workgroup, so that every CU gets one workgroup.
+    p.waves = kColMaxWaves;
+    int C = std::min(std::max(1, (N + 255) / 256), p.waves * cmax);
     // a forced shape replaces the choice when the kernel has a variant for it
-    const int fc = g_col_cpw;
-    if (g_col_waves > 0 && (fc == 1 || (fc == 2 && p.ni <= 6) || (fc == 4 && p.ni <= 3))) {
-        p.cpw = fc;
-        p.waves = std::min(kColMaxWaves, std::max(g_col_waves, wmin));
+    if (g_col_waves > 0 && g_col_cols > 0) {
+        const int w = std::min(g_col_waves, kColMaxWaves);
+        if (w * kColMaxTasks >= ntask && (g_col_cols + w - 1) / w <= cmax) {
+            p.waves = w;
+            C = g_col_cols;
+        }
     }
-    const int C = p.waves * p.cpw;
-    if (p.groups * C > 8 * p.waves * kWave) return false;    // scale staging capacity
+    p.cols = C;
+    p.cpw = (C + p.waves - 1) / p.waves;
+    if (p.cpw < 1 || p.cpw > cmax || p.waves * kColMaxTasks < ntask) return false;
+    const int pieces = (C + 7) / 8 + 1;                       // 8-column scale pieces per group, at most
+    if (p.groups * pieces > kColScLoads * p.waves * kWave) return false;   // scale staging capacity
     p.wgs = (N + C - 1) / C;
-    p.lds_bytes = size_t(p.mr) * 4 * (nch * 8 + 32) * 2 + size_t(p.mr) * nblk * 4 + size_t(p.mr) * nch * 4 +
-                  size_t(p.groups) * C * 4;
+    p.lds_bytes = size_t(p.mr) * 4 * (nch * 8 + 32) * 2 + size_t(p.mr) * nch * 8 + size_t(p.groups) * C * 4;
     if (p.lds_bytes > kMaxLds) return false;
     p.kind = kColumnOwning;
     return true;
@@ -741,6 +780,7 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
         a.N = N;
         a.nch = K / 32;
         a.groups = p.groups;
+        a.cols = p.cols;
         a.out_scale = out_scale;
         a.residual = residual;
         a.y = y;
