@@ -9,7 +9,7 @@
 
 namespace fdec {
 
-// The int4 GEMV has two kernels.
+// The int4 GEMV has three kernels.
 //  * Column-owning (M <= 4, K <= 16384): each wave owns whole output columns over the
 //    full K, each workgroup stages the activation of the full K once in LDS; no
 //    cross-workgroup reduction and no workspace.
@@ -24,7 +24,9 @@ constexpr int kColMaxChunks = 8;
 constexpr int kColScLoads = 4;       // 16-byte scale loads per thread, column kernel     // 32-wide K chunks per lane, column kernel
 constexpr size_t kMaxLds = 160 * 1024;
 
-enum GemvKind { kColumnOwning = 0, kSplitK = 1 };
+enum GemvKind { kColumnOwning = 0, kSplitK = 1, kMfma = 2 };
+constexpr int kMfmaWaves = 8;       // waves per workgroup, matrix-core kernel
+constexpr int kMfmaMaxSliceGroups = 36;   // 128-wide groups per K slice (LDS: 4 KB each)
 
 struct GemvPlan {
     int kind;
@@ -36,7 +38,8 @@ struct GemvPlan {
     int cols;         // columns per workgroup
     int ni;           // 32-wide K chunks per lane
     int wgs;          // workgroups
-    // split-K kernel
+    // split-K kernel (the matrix-core kernel reuses tiles = column ranges, gps = groups
+    // per K slice, splits, cpw = 16-column tiles per wave, waves)
     int tiles;        // ceil(N / 64)
     int gw;           // groups per wave (1, 2 or 4)
     int gps;          // groups per split = 4 * gw
@@ -60,6 +63,10 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
                        void* ws, hipStream_t s);
+hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
+                       const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
+                       const float* out_scale, const uint16_t* residual, uint16_t* y,
+                       void* ws, const GemvPlan& p, hipStream_t s);
 hipError_t launch_w4_unpack(const uint32_t* qw, int K, int N, int8_t* q, hipStream_t s);
 hipError_t launch_w4_dequant(const uint32_t* qw, const uint16_t* sc, int K, int N,
                              float* w, hipStream_t s);

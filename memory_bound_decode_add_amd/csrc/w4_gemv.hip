@@ -726,10 +726,36 @@ bool plan_column(int M, int K, int N, GemvPlan& p) {
 
 }  // namespace
 
+// Matrix-core kernel: 8 waves of one 16-column tile each, K split into slices until
+// there are about 200 workgroups (and each slice's activation fits LDS).
+bool plan_mfma(int M, int K, int N, GemvPlan& p) {
+    if (M <= 4 || M > 16) return false;
+    p.kind = kMfma;
+    p.mr = 16;
+    p.groups = K / kGroup;
+    p.waves = kMfmaWaves;
+    p.cpw = 1;
+    const int ncol = p.waves * p.cpw * 16;
+    p.tiles = (N + ncol - 1) / ncol;
+    int S = std::max((p.groups + kMfmaMaxSliceGroups - 1) / kMfmaMaxSliceGroups,
+                     std::min(p.groups, (200 + p.tiles - 1) / p.tiles));
+    p.gps = (p.groups + S - 1) / S;
+    p.splits = (p.groups + p.gps - 1) / p.gps;
+    if (p.splits > 1) {
+        p.counter_bytes = (size_t(p.tiles) * 4 + 255) / 256 * 256;
+        p.partial_bytes = size_t(p.splits) * 16 * p.tiles * ncol * 4;
+    }
+    p.lds_bytes = size_t(16) * (size_t(p.gps) * 16 + 1) * 16 + size_t(16) * p.gps * 4;
+    return true;
+}
+
 GemvPlan plan_gemv(int M, int K, int N) {
     GemvPlan p{};
     p.groups = K / kGroup;
     if (g_forced_split == 0 && plan_column(M, K, N, p)) return p;
+    p = GemvPlan{};
+    if (g_forced_split == 0 && plan_mfma(M, K, N, p)) return p;
+    p = GemvPlan{};
     p = GemvPlan{};
     p.kind = kSplitK;
     p.groups = K / kGroup;
@@ -790,6 +816,7 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
             default: return launch_col<4>(pro, a, p, s);
         }
     }
+    if (p.kind == kMfma) return launch_mfma(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
     SplitArgs a{};
     a.a0 = a0;
     a.a1 = a1;

@@ -1,0 +1,345 @@
+// int4 group-quantised GEMV for 5..16 rows on the matrix cores, gfx950.
+//
+// Same operation as the VALU kernels ("PyTorch Community Proposes Fusion Fix as Large
+// Intermediate Buffers May Slow Single-Token Decoding in Quantized LLMs"; "Kernel
+// Fusion, torch.compile and CUDA Graphs, Measured", Step 3):
+//     y[m, n] = bf16( s * sum_k act[m, k] * q[k, n] * scale[k/128, n]  (+ res[m, n]) )
+// with act = silu(g) * u (SwiGLU prologue) or act = x (identity prologue).  At 16 rows
+// every weight byte feeds 16 rows of products, which the VALU cannot keep up with at
+// HBM speed; v_mfma_f32_16x16x32_f16 does the products, the VALU only decodes.
+//
+// Tiling.  A tile is 16 consecutive columns.  A workgroup of W waves owns W * TPW
+// tiles (each wave TPW of them) over a slice of whole 128-wide groups of K; with
+// several slices per column range, slices are combined through the workspace by the
+// last workgroup to arrive (the split-K protocol of the VALU split kernel).
+//
+// MFMA mapping (16x16x32, checked on the hardware for the f16 and bf16 forms: lane l
+// supplies A[l%16][8(l/16) + e],
+// B[8(l/16) + e][l%16] and receives D[4(l/16) + r][l%16]).  A is a tile's weights (row
+// = column n of the tile), B the activation (column = row m), D[n][m].  Lane l loads
+// the 16-byte chunk (4 packed words, 32 consecutive k) number 4g + l/16 of column
+// l%16 of the tile, for group g; word j of it is its A operand in the j-th MFMA of the
+// group, so MFMA j of group g covers the k-blocks (8 k each) 16g + 4s + j, s = 0..3.
+//
+// Decode.  The packed words are decoded as in the VALU column kernel, with their fp16
+// offsets left in (1032 + q at even nibble positions, 1152 + 16 q at odd ones, six
+// integer ops per word), in the pair order (j0, j4, j1, j5, j2, j6, j3, j7).  The
+// offsets are removed inside the matrix core: each group's accumulation starts from
+// the product of a constant matrix of -1032 / -1152 with the same activation operands.
+//
+// Activation.  The workgroup stages its slice of act (16 rows, zero beyond M) in LDS as
+// block-scaled fp16 with the odd positions divided by 16 (so each product is a * q plus
+// a weight-independent offset): per (row, 128-wide group) a power of two 2^-E puts the
+// largest magnitude in [2^14, 2^15); 2^E is folded back in with the group scale.  The
+// layout is [row][k-block][8] with a 16-byte pad per row, so the B operands of one MFMA
+// (16 rows of one k-block per k-slot) are spread over all LDS banks.  With the SwiGLU
+// prologue silu(g) * u is computed in fp32; fp32 -> fp16 rounds toward zero.
+#include "device_common.h"
+#include "fdec_internal.h"
+
+#include <algorithm>
+
+namespace fdec {
+namespace {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaP = 4;          // groups per batch of weight loads
+
+struct MfmaArgs {
+    const uint16_t* a0;     // g (SwiGLU) or x (identity), row stride lda
+    const uint16_t* a1;     // u (SwiGLU) or unused
+    int64_t lda;
+    const uint4* qw;        // [N][K/32] chunks of 4 words
+    const uint16_t* sc;     // bf16 scales [K/128][N]
+    int M, K, N;
+    int nch;                // K / 32
+    int groups;             // K / 128
+    int kgroups;            // groups per K slice
+    int splits;             // K slices
+    int cgroups;            // column ranges (workgroups per slice)
+    int npad;               // cgroups * columns per workgroup
+    const float* out_scale;
+    const uint16_t* residual;
+    uint16_t* y;
+    float* partial;         // [splits][16][npad]
+    unsigned* counters;     // [cgroups]
+};
+
+// One packed word -> 8 fp16 values with their offsets, in pair order.
+__device__ __forceinline__ f16x8_t decode_f16x8_biased(uint32_t w) {
+    const Q4x2 q = decode_int4x8_biased(w);
+    return __builtin_bit_cast(f16x8_t, make_uint4(__builtin_bit_cast(uint32_t, q.p04), __builtin_bit_cast(uint32_t, q.p15),
+                                                  __builtin_bit_cast(uint32_t, q.p26), __builtin_bit_cast(uint32_t, q.p37)));
+}
+
+// One staging item: 8 consecutive activation values of one row.  The 16 lanes of a
+// DPP row hold the 16 k-blocks of one 128-wide group of that row and share its scale.
+// Must be called with the whole wave active.  Returns the fp16 words in pair order;
+// *esc = 2^E of the group.
+template <int PRO>
+__device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, bool live, float* esc) {
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        if (PRO == kSwiGLU) {
+            v[2 * h] = silu_f32(bf16_lo(gw[h])) * bf16_lo(uw[h]);
+            v[2 * h + 1] = silu_f32(bf16_hi(gw[h])) * bf16_hi(uw[h]);
+        } else {
+            v[2 * h] = bf16_lo(gw[h]);
+            v[2 * h + 1] = bf16_hi(gw[h]);
+        }
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        v[j] = live ? v[j] : 0.f;
+        mx = fmaxf(mx, fabsf(v[j]));
+    }
+    mx = fmaxf(mx, dpp<kQuadSwap1>(mx));
+    mx = fmaxf(mx, dpp<kQuadSwap2>(mx));
+    mx = fmaxf(mx, dpp<kRowRor4>(mx));
+    mx = fmaxf(mx, dpp<kRowRor8>(mx));             // the group's largest magnitude
+    int e = 0;
+    (void)__builtin_frexpf(mx, &e);
+    const int E = min(max(e - 15, -126), 127);
+    const float down = __builtin_ldexpf(1.0f, -E);
+    const float down16 = down * 0.0625f;
+    *esc = __builtin_ldexpf(1.0f, E);
+    return make_uint4(__builtin_bit_cast(uint32_t, pk_f16_rtz(v[0] * down, v[4] * down)),
+                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[1] * down16, v[5] * down16)),
+                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2] * down, v[6] * down)),
+                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[3] * down16, v[7] * down16)));
+}
+
+template <int TPW, int PRO>
+__global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int last_flag;
+    const int W = blockDim.x >> 6;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int ls = lane >> 4, lm = lane & 15;          // k-slot, row / column-in-tile
+    const int cg = blockIdx.x % a.cgroups, split = blockIdx.x / a.cgroups;
+    const int g0 = split * a.kgroups;
+    const int ng = min(a.kgroups, a.groups - g0);      // groups in this slice
+    const int nkb = ng * 16;                           // 8-wide k-blocks in this slice
+    const int ncol = W * TPW * 16;                     // columns per workgroup
+    const int nw0 = cg * ncol + wave * TPW * 16;       // first column of this wave's tiles
+    const int rs = nkb + 1;                            // row stride of act_s, in 16-byte blocks
+    uint4* act_s = reinterpret_cast<uint4*>(smem);     // [16 rows][rs] of 8 fp16
+    float* esc_s = reinterpret_cast<float*>(act_s + 16 * rs);   // [16 rows][ng]
+
+    // ---- weight and scale loads of one batch of groups (addresses clamped) ----
+    auto load_batch = [&](int b, uint4 (&w)[kMfmaP][TPW], uint2 (&sv)[kMfmaP][TPW]) {
+#pragma unroll
+        for (int p = 0; p < kMfmaP; ++p) {
+            const int g = g0 + min(b * kMfmaP + p, ng - 1);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int n = min(nw0 + t * 16 + lm, a.N - 1);
+                w[p][t] = a.qw[size_t(n) * a.nch + 4 * g + ls];
+                const int ns = min(nw0 + t * 16 + 4 * ls, a.N - 4);
+                sv[p][t] = *reinterpret_cast<const uint2*>(a.sc + size_t(g) * a.N + ns);
+            }
+        }
+    };
+
+    uint4 wA[kMfmaP][TPW], wB[kMfmaP][TPW];
+    uint2 sA[kMfmaP][TPW], sB[kMfmaP][TPW];
+    load_batch(0, wA, sA);
+    // epilogue inputs: 4 consecutive columns of row lm per tile
+    uint2 rraw[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const uint16_t* rsrc = a.residual ? a.residual : a.y;   // y: a readable stand-in, value unused
+        rraw[t] = *reinterpret_cast<const uint2*>(rsrc + size_t(min(lm, a.M - 1)) * a.N +
+                                                  min(nw0 + t * 16 + 4 * ls, a.N - 4));
+    }
+    const float os = a.out_scale ? *a.out_scale : 1.0f;
+
+    // ---- stage the activation slice: item i = (row i / nkb, k-block i % nkb) ----
+    const int nitems = nkb * 16;
+    const int kbase = g0 * 128;
+    constexpr int U = 4;
+    for (int i0 = tid; i0 - tid < nitems; i0 += U * int(blockDim.x)) {   // uniform trip count
+        uint4 gv[U], uv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int it = min(i0 + u * int(blockDim.x), nitems - 1);
+            const int m = min(it / nkb, a.M - 1);
+            const size_t off = size_t(m) * a.lda + kbase + (it % nkb) * 8;
+            gv[u] = *reinterpret_cast<const uint4*>(a.a0 + off);
+            uv[u] = PRO == kSwiGLU ? *reinterpret_cast<const uint4*>(a.a1 + off) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int it = i0 + u * int(blockDim.x);
+            const int m = it / nkb, kb = it % nkb;
+            float esc;
+            const uint4 h = stage_item_mfma<PRO>(gv[u], uv[u], it < nitems && m < a.M, &esc);
+            if (it < nitems) {
+                act_s[m * rs + kb] = h;
+                if ((kb & 15) == 0) esc_s[m * ng + (kb >> 4)] = esc;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- main loop: batches of kMfmaP groups, next batch's loads in flight ----
+    f32x4_t out[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) out[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // -offset of each pair-order slot: (-1032, -1032), (-1152, -1152), ...
+    const uint32_t o_even = 0xE408E408u, o_odd = 0xE480E480u;
+    const f16x8_t negoff = __builtin_bit_cast(f16x8_t, make_uint4(o_even, o_odd, o_even, o_odd));
+
+    auto compute_batch = [&](int b, const uint4 (&w)[kMfmaP][TPW], const uint2 (&sv)[kMfmaP][TPW]) {
+#pragma unroll
+        for (int p = 0; p < kMfmaP; ++p) {
+            const int gl = b * kMfmaP + p;
+            if (gl >= ng) break;                       // uniform
+            f16x8_t bop[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(f16x8_t, act_s[lm * rs + 16 * gl + 4 * ls + j]);
+            const float e = esc_s[lm * ng + gl];
+            f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bias = __builtin_amdgcn_mfma_f32_16x16x32_f16(negoff, bop[j], bias, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const uint32_t wd[4] = {w[p][t].x, w[p][t].y, w[p][t].z, w[p][t].w};
+                f32x4_t d = bias;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode_f16x8_biased(wd[j]), bop[j], d, 0, 0, 0);
+                out[t][0] = fmaf(bf16_lo(sv[p][t].x) * e, d[0], out[t][0]);
+                out[t][1] = fmaf(bf16_hi(sv[p][t].x) * e, d[1], out[t][1]);
+                out[t][2] = fmaf(bf16_lo(sv[p][t].y) * e, d[2], out[t][2]);
+                out[t][3] = fmaf(bf16_hi(sv[p][t].y) * e, d[3], out[t][3]);
+            }
+        }
+    };
+
+    const int nbatch = (ng + kMfmaP - 1) / kMfmaP;
+    for (int b = 0; b < nbatch; b += 2) {
+        load_batch(b + 1, wB, sB);                     // clamped: harmless past the end
+        compute_batch(b, wA, sA);
+        load_batch(b + 2, wA, sA);
+        compute_batch(b + 1, wB, sB);
+    }
+
+    // ---- epilogue: lane holds D[column 4 ls + r][row lm] of each tile ----
+    if (a.splits == 1) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int n = nw0 + t * 16 + 4 * ls;
+            if (lm < a.M && n < a.N) {
+                const float r0 = a.residual ? bf16_lo(rraw[t].x) : 0.f, r1 = a.residual ? bf16_hi(rraw[t].x) : 0.f;
+                const float r2 = a.residual ? bf16_lo(rraw[t].y) : 0.f, r3 = a.residual ? bf16_hi(rraw[t].y) : 0.f;
+                uint2 o;
+                o.x = pack_bf16x2(fmaf(out[t][0], os, r0), fmaf(out[t][1], os, r1));
+                o.y = pack_bf16x2(fmaf(out[t][2], os, r2), fmaf(out[t][3], os, r3));
+                *reinterpret_cast<uint2*>(a.y + size_t(lm) * a.N + n) = o;
+            }
+        }
+        return;
+    }
+
+    // ---- several K slices: partials, then the last workgroup of the range finishes ----
+    // Partials go out as device-scope atomic stores (coherent across the XCDs' L2s);
+    // waiting for their completion before bumping the arrival counter orders them
+    // before it.  The finishing workgroup reads them back with device-scope atomic loads.
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int nc = (nw0 - cg * ncol) + t * 16 + 4 * ls;          // column within the range
+        float* dst = a.partial + (size_t(split) * 16 + lm) * a.npad + cg * ncol + nc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, out[t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned old = __hip_atomic_fetch_add(&a.counters[cg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (old == unsigned(a.splits - 1));
+    }
+    __syncthreads();
+    if (!last_flag) return;
+
+    // each thread finishes outputs o = tid, tid + blockDim, ... of the range's 16 x ncol,
+    // summing the slices in order with all loads of a batch issued before the adds
+    constexpr int SB = 8;
+    for (int o = tid; o < 16 * ncol; o += blockDim.x) {
+        const int m = o / ncol, nc = o % ncol, n = cg * ncol + nc;
+        const bool live = m < a.M && n < a.N;
+        float v = 0.f;
+        for (int s0 = 0; s0 < a.splits; s0 += SB) {
+            float t[SB];
+#pragma unroll
+            for (int b = 0; b < SB; ++b)
+                t[b] = (live && s0 + b < a.splits)
+                           ? __hip_atomic_load(a.partial + (size_t(s0 + b) * 16 + m) * a.npad + n, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+#pragma unroll
+            for (int b = 0; b < SB; ++b) v += t[b];
+        }
+        if (live) {
+            const size_t oo = size_t(m) * a.N + n;
+            const float r = a.residual ? bf16_to_f32(a.residual[oo]) : 0.f;
+            a.y[oo] = f32_to_bf16(fmaf(v, os, r));
+        }
+    }
+    if (tid == 0) __hip_atomic_store(&a.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename Kern>
+hipError_t launch_k(Kern k, dim3 grid, int threads, size_t lds, hipStream_t s, const MfmaArgs& a) {
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k, grid, dim3(threads), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
+                       const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
+                       const float* out_scale, const uint16_t* residual, uint16_t* y,
+                       void* ws, const GemvPlan& p, hipStream_t s) {
+    MfmaArgs a{};
+    a.a0 = a0;
+    a.a1 = a1;
+    a.lda = lda;
+    a.qw = reinterpret_cast<const uint4*>(qw);
+    a.sc = sc;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.nch = K / 32;
+    a.groups = p.groups;
+    a.kgroups = p.gps;
+    a.splits = p.splits;
+    a.cgroups = p.tiles;
+    a.npad = p.tiles * p.waves * p.cpw * 16;
+    a.out_scale = out_scale;
+    a.residual = residual;
+    a.y = y;
+    a.counters = p.splits > 1 ? static_cast<unsigned*>(ws) : nullptr;
+    a.partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes) : nullptr;
+    const dim3 grid(p.tiles * p.splits);
+    const int threads = p.waves * kWave;
+    if (p.cpw == 2) {
+        return pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<2, kSwiGLU>, grid, threads, p.lds_bytes, s, a)
+                              : launch_k(w4_gemv_mfma_kernel<2, kIdentity>, grid, threads, p.lds_bytes, s, a);
+    }
+    return pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU>, grid, threads, p.lds_bytes, s, a)
+                          : launch_k(w4_gemv_mfma_kernel<1, kIdentity>, grid, threads, p.lds_bytes, s, a);
+}
+
+}  // namespace fdec

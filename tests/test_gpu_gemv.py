@@ -145,7 +145,8 @@ def _exact_case(M, K, N, seed):
             synth.f32_to_bf16_bits(s), exact)
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 1024, 512), (1, 9216, 2560), (4, 2048, 256)])
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 512), (1, 9216, 2560), (4, 2048, 256), (8, 1024, 136),
+                                   (16, 2048, 264), (16, 14336, 520)])
 def test_swiglu_gemv_exact_special_cases_bit_exact(M, K, N):
     say(f"[gemv] exact special case M={M} K={K} N={N}")
     gb, ub, qw, sb, exact = _exact_case(M, K, N, seed=K + N)
