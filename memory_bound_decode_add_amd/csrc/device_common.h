@@ -89,6 +89,17 @@ __device__ __forceinline__ Q4x2 decode_int4x8_biased(uint32_t w) {
     return q;
 }
 
+// Workgroups are dispatched to the eight XCDs round-robin (workgroup b runs on XCD
+// b % 8), and each XCD has its own L2.  Renumbering b so that the workgroups of one XCD
+// get consecutive logical indices (XCD x takes a contiguous range) makes neighbouring
+// tiles, which share cache lines of the scales and of the activation, meet in one L2
+// instead of being fetched from HBM once per XCD.  A bijection on [0, n) for any n.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+    const int x = b % kXcds, q = n / kXcds, r = n % kXcds;
+    return x * q + min(x, r) + b / kXcds;
+}
+
 // Two fp32 values to one packed fp16 pair, rounding toward zero (one instruction).
 __device__ __forceinline__ half2_t pk_f16_rtz(float a, float b) {
     return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a, b));

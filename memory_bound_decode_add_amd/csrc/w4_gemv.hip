@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColAr
     float2* eb_s = reinterpret_cast<float2*>(smem + size_t(MR) * 4 * qs * 2);     // [MR][nch]
     float* sc_s = reinterpret_cast<float*>(eb_s + MR * a.nch);                     // [groups][C]
 
-    const int col0 = blockIdx.x * C;
+    const int col0 = xcd_remap(blockIdx.x, gridDim.x) * C;
 
     // ---- 1. activation inputs: task t -> (row t % MR, block t / MR), wave W-1 - t % W ----
     const int ntask = MR * nblk;

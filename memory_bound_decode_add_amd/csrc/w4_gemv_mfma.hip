@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     const int W = blockDim.x >> 6;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ls = lane >> 4, lm = lane & 15;          // k-slot, row / column-in-tile
-    const int cg = blockIdx.x % a.cgroups, split = blockIdx.x / a.cgroups;
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int cg = lb % a.cgroups, split = lb / a.cgroups;
     const int g0 = split * a.kgroups;
     const int ng = min(a.kgroups, a.groups - g0);      // groups in this slice
     const int nkb = ng * 16;                           // 8-wide k-blocks in this slice
