@@ -100,6 +100,17 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return x * q + min(x, r) + b / kXcds;
 }
 
+// 16-byte loads and stores marked non-temporal (streamed data that is not re-read).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_load(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void nt_store(uint4 v, uint4* p) {
+    const u32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Two fp32 values to one packed fp16 pair, rounding toward zero (one instruction).
 __device__ __forceinline__ half2_t pk_f16_rtz(float a, float b) {
     return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
