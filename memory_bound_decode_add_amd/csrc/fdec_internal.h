@@ -19,7 +19,7 @@ constexpr int kGemvThreads = 256;
 constexpr int kGemvCols = 64;
 constexpr int kGroup = 128;
 constexpr int kColMaxTasks = 8;      // activation tasks (row, 512-wide block) per wave, column kernel
-constexpr int kColMaxWaves = 8;      // waves per workgroup, column kernel (256 VGPRs per lane)
+constexpr int kColMaxWaves = 8;      // dot waves (and staging waves) per workgroup, column kernel
 constexpr int kColMaxChunks = 8;
 constexpr int kColScLoads = 4;       // 16-byte scale loads per thread, column kernel     // 32-wide K chunks per lane, column kernel
 constexpr size_t kMaxLds = 160 * 1024;
@@ -36,6 +36,7 @@ struct GemvPlan {
     int waves;        // waves per workgroup
     int cpw;          // most columns any wave owns (1..4)
     int cols;         // columns per workgroup
+    int stagers;      // staging waves per workgroup
     int ni;           // 32-wide K chunks per lane
     int wgs;          // workgroups
     // split-K kernel (the matrix-core kernel reuses tiles = column ranges, gps = groups

@@ -121,6 +121,7 @@ struct ColArgs {
     int nch;                // K / 32
     int groups;             // K / 128
     int cols;               // columns per workgroup (column kernel)
+    int stagers;            // staging waves per workgroup (column kernel)
     const float* out_scale;
     const uint16_t* residual;
     uint16_t* y;
@@ -198,14 +199,21 @@ __device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, b
     if (quad_lead && in_k) *eb_dst = make_float2(__builtin_ldexpf(1.0f, E), b);
 }
 
-// Wave w of a W-wave workgroup owning C columns handles the columns w, w + W, w + 2W,
-// ... below C (at most CPW of them), so the columns spread over the four SIMDs as
-// evenly as C allows; staging tasks go to the waves in reverse order, the waves with
-// fewer columns taking the extra tasks.
+// The workgroup has S + W waves in two roles.
+//  * Staging waves 0..S-1: they load the activation inputs and the group scales, stage
+//    them in LDS and retire at the barrier.  They are the older waves, so their loads
+//    are issued ahead of the weight loads.
+//  * Dot waves S..S+W-1: dot wave w owns columns w, w + W, ... below C (at most CPW of
+//    them).  It issues its weight loads first thing and, after the barrier, runs the dot.
+// Measured on MI355X: a wave that issues many loads stalls at issue behind the CU's
+// outstanding requests, and one wave per SIMD issues VALU work at about half rate.
+// Split roles keep the staging waves' issue free of weight loads, and give every SIMD
+// two waves in each phase.
 template <int MR, int CPW, int NI, int PRO>
-__global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColArgs a) {
+__global__ __launch_bounds__(2 * kColMaxWaves * kWave) void w4_gemv_col_kernel(ColArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int W = blockDim.x >> 6;
+    const int S = a.stagers;                       // staging waves
+    const int W = (blockDim.x >> 6) - S;           // dot waves
     const int C = a.cols;                          // columns per workgroup
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -219,43 +227,78 @@ __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColAr
 
     const int col0 = xcd_remap(blockIdx.x, gridDim.x) * C;
 
-    // ---- 1. activation inputs: task t -> (row t % MR, block t / MR), wave W-1 - t % W ----
-    const int ntask = MR * nblk;
-    const int tw = W - 1 - wave;
-    uint4 ga[kColMaxTasks], ua[kColMaxTasks];
+    if (wave < S) {
+        // ================= staging waves =================
+        const int sw = wave, stid = tid, nst = S * kWave;
+        // ---- activation inputs: task t = sw + S * ti -> (row t % MR, block t / MR) ----
+        const int ntask = MR * nblk;
+        uint4 ga[kColMaxTasks], ua[kColMaxTasks];
 #pragma unroll
-    for (int ti = 0; ti < kColMaxTasks; ++ti) {
-        const int t = tw + W * ti;
-        if (t >= ntask) break;                     // uniform across the wave
-        const int m = min(t % MR, a.M - 1), b = t / MR;
-        const int k = min(b * 64 + lane, kw - 1) * 8;
-        ga[ti] = *reinterpret_cast<const uint4*>(a.a0 + size_t(m) * a.lda + k);
-        ua[ti] = PRO == kSwiGLU ? *reinterpret_cast<const uint4*>(a.a1 + size_t(m) * a.lda + k) : make_uint4(0, 0, 0, 0);
-    }
-    // ---- 2. group scales of this workgroup's columns, epilogue inputs ----
-    // the scales of columns [col0, col0 + C) are read as aligned 8-column pieces of each
-    // group's row: item (g, p) is the piece (col0 / 8 + p) of group g
-    const int p0 = col0 >> 3;
-    const int npc = ((min(col0 + C, a.N) - 1) >> 3) - p0 + 1;
-    const int nsc = a.groups * npc;
-    uint4 sraw[kColScLoads];
+        for (int ti = 0; ti < kColMaxTasks; ++ti) {
+            const int t = sw + S * ti;
+            if (t >= ntask) break;                 // uniform across the wave
+            const int m = min(t % MR, a.M - 1), b = t / MR;
+            const int k = min(b * 64 + lane, kw - 1) * 8;
+            ga[ti] = *reinterpret_cast<const uint4*>(a.a0 + size_t(m) * a.lda + k);
+            ua[ti] = PRO == kSwiGLU ? *reinterpret_cast<const uint4*>(a.a1 + size_t(m) * a.lda + k)
+                                    : make_uint4(0, 0, 0, 0);
+        }
+        // ---- group scales of columns [col0, col0 + C), as aligned 8-column pieces of
+        // each group's row: item (g, p) is the piece (col0 / 8 + p) of group g ----
+        const int p0 = col0 >> 3;
+        const int npc = ((min(col0 + C, a.N) - 1) >> 3) - p0 + 1;
+        const int nsc = a.groups * npc;
+        uint4 sraw[kColScLoads];
 #pragma unroll
-    for (int r = 0; r < kColScLoads; ++r) {
-        if (r * int(blockDim.x) >= nsc) break;     // uniform
-        const int idx = min(tid + r * int(blockDim.x), nsc - 1);
-        const int g = idx / npc, pc = p0 + idx % npc;
-        sraw[r] = *reinterpret_cast<const uint4*>(a.sc + size_t(g) * a.N + pc * 8);
+        for (int r = 0; r < kColScLoads; ++r) {
+            if (r * nst >= nsc) break;             // uniform
+            const int idx = min(stid + r * nst, nsc - 1);
+            const int g = idx / npc, pc = p0 + idx % npc;
+            sraw[r] = *reinterpret_cast<const uint4*>(a.sc + size_t(g) * a.N + pc * 8);
+        }
+        // ---- activations, per-chunk scale and offsets, group scales to LDS ----
+        // word wi = 64 b + lane: chunk wi / 4, quarter wi % 4
+        const int lofs = (lane & 3) * qs + (lane >> 2) * 8;
+#pragma unroll
+        for (int ti = 0; ti < kColMaxTasks; ++ti) {
+            const int t = sw + S * ti;
+            if (t >= ntask) break;                 // uniform across the wave
+            const int m = t % MR, b = t / MR;
+            const bool in_k = b * 64 + lane < kw;  // a chunk lies wholly inside or outside K
+            stage_word_col<PRO>(ga[ti], ua[ti], in_k && m < a.M, in_k, (lane & 3) == 0,
+                                act_s + size_t(m) * 4 * qs + lofs + b * 128,
+                                eb_s + m * a.nch + b * 16 + (lane >> 2));
+        }
+#pragma unroll
+        for (int r = 0; r < kColScLoads; ++r) {
+            if (r * nst >= nsc) break;
+            const int idx = stid + r * nst;
+            if (idx < nsc) {
+                const int g = idx / npc, cc0 = (p0 + idx % npc) * 8 - col0;
+                const uint32_t wd[4] = {sraw[r].x, sraw[r].y, sraw[r].z, sraw[r].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int cc = cc0 + e;
+                    if (cc >= 0 && cc < C) sc_s[g * C + cc] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+                }
+            }
+        }
+        __syncthreads();
+        return;
     }
+
+    // ================= dot waves =================
+    const int wave_all = wave;
+    {
+    const int wave = wave_all - S;
     // lane l < MR*CPW finishes output (row l / CPW, column col0 + wave + W * (l % CPW))
     const int em = lane / CPW, ecc = wave + W * (lane % CPW), en = col0 + ecc;
     const bool owner = lane < MR * CPW && em < a.M && ecc < C && en < a.N;
     const uint16_t* rsrc = a.residual ? a.residual : a.y;   // y: a readable stand-in, value unused
     const uint16_t rraw = rsrc[size_t(min(em, a.M - 1)) * a.N + min(en, a.N - 1)];
     const float os = a.out_scale ? *a.out_scale : 1.0f;
-    // ---- 3. weight chunks: lane l takes chunks l, l+64, ... of each of the wave's columns ----
-    // (unconditional: a slot the wave does not own re-reads its first column, so the
-    // number of loads in flight is the same on every path and the prologue's waits for
-    // the activation loads never wait for weights)
+    // weight chunks: lane l takes chunks l, l+64, ... of each of the wave's columns (a
+    // slot the wave does not own re-reads its first column: the loads stay unconditional)
     uint4 wv[NI][CPW];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
@@ -264,39 +307,10 @@ __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColAr
 #pragma unroll
         for (int i = 0; i < NI; ++i) wv[i][j] = colp[min(lane + kWave * i, a.nch - 1)];
     }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- 4. prologue: activations, per-chunk scale and offsets, group scales to LDS ----
-    // word wi = 64 b + lane: chunk wi / 4, quarter wi % 4
-    const int lofs = (lane & 3) * qs + (lane >> 2) * 8;
-#pragma unroll
-    for (int ti = 0; ti < kColMaxTasks; ++ti) {
-        const int t = tw + W * ti;
-        if (t >= ntask) break;                     // uniform across the wave
-        const int m = t % MR, b = t / MR;
-        const bool in_k = b * 64 + lane < kw;      // a chunk lies wholly inside or outside K
-        stage_word_col<PRO>(ga[ti], ua[ti], in_k && m < a.M, in_k, (lane & 3) == 0,
-                            act_s + size_t(m) * 4 * qs + lofs + b * 128,
-                            eb_s + m * a.nch + b * 16 + (lane >> 2));
-    }
-#pragma unroll
-    for (int r = 0; r < kColScLoads; ++r) {
-        if (r * int(blockDim.x) >= nsc) break;
-        const int idx = tid + r * int(blockDim.x);
-        if (idx < nsc) {
-            const int g = idx / npc, cc0 = (p0 + idx % npc) * 8 - col0;
-            const uint32_t wd[4] = {sraw[r].x, sraw[r].y, sraw[r].z, sraw[r].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int cc = cc0 + e;
-                if (cc >= 0 && cc < C) sc_s[g * C + cc] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
-            }
-        }
-    }
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 5. dot products: one activation read per chunk serves the wave's columns ----
+    // ---- dot products: one activation read per chunk serves the wave's columns ----
     float acc[MR][CPW];
 #pragma unroll
     for (int m = 0; m < MR; ++m)
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColAr
         }
     }
 
-    // ---- 6. reduce each column over the wave; the owning lane applies the epilogue ----
+    // ---- reduce each column over the wave; the owning lane applies the epilogue ----
     float mine = 0.f;
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
@@ -361,6 +375,7 @@ __global__ __launch_bounds__(kColMaxWaves * kWave) void w4_gemv_col_kernel(ColAr
     }
     const float res = a.residual ? bf16_to_f32(rraw) : 0.f;
     if (owner) a.y[size_t(em) * a.N + en] = f32_to_bf16(fmaf(mine, os, res));
+    }
 }
 
 // ===========================================================================
@@ -590,11 +605,13 @@ hipError_t launch(Kern k, dim3 grid, int threads, size_t lds, hipStream_t s, con
 template <int MR, int CPW, int NI>
 hipError_t launch_col3(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStream_t s) {
     if (pro == kSwiGLU)
-        return launch(w4_gemv_col_kernel<MR, CPW, NI, kSwiGLU>, dim3(p.wgs), p.waves * kWave, p.lds_bytes, s, a);
-    return launch(w4_gemv_col_kernel<MR, CPW, NI, kIdentity>, dim3(p.wgs), p.waves * kWave, p.lds_bytes, s, a);
+        return launch(w4_gemv_col_kernel<MR, CPW, NI, kSwiGLU>, dim3(p.wgs), (p.stagers + p.waves) * kWave, p.lds_bytes,
+                      s, a);
+    return launch(w4_gemv_col_kernel<MR, CPW, NI, kIdentity>, dim3(p.wgs), (p.stagers + p.waves) * kWave, p.lds_bytes,
+                  s, a);
 }
 
-// Only the (CPW, NI) pairs col_cpw_max allows are instantiated.
+// The (CPW, NI) pairs col_cpw_max allows (for some row count) are instantiated.
 template <int MR>
 hipError_t launch_col(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStream_t s) {
     switch (p.cpw) {
@@ -688,8 +705,12 @@ __global__ void fill_zero_kernel(uint4* p, int64_t n16, unsigned char* tail, int
 }
 
 // Largest columns-per-wave the weight registers allow (CPW * NI chunks of 16 bytes
-// per lane); only these (CPW, NI) pairs are instantiated.
-int col_cpw_max(int ni) { return ni <= 3 ? 4 : ni <= 4 ? 3 : ni <= 6 ? 2 : 1; }
+// per lane, at most 128 VGPRs with 16 waves) without spilling; only these (CPW, NI)
+// pairs are instantiated.
+int col_cpw_max(int ni, int mr) {
+    if (mr >= 4) return ni <= 1 ? 4 : ni <= 3 ? 2 : 1;
+    return ni <= 3 ? 4 : ni <= 4 ? 3 : ni <= 6 ? 2 : 1;
+}
 
 bool plan_column(int M, int K, int N, GemvPlan& p) {
     if (M > 4 || K > 32 * kColMaxChunks * kWave) return false;
@@ -699,24 +720,26 @@ bool plan_column(int M, int K, int N, GemvPlan& p) {
     p.ni = (nch + kWave - 1) / kWave;
     const int ntask = p.mr * nblk;
     if (ntask > kColMaxWaves * kColMaxTasks) return false;
-    const int cmax = col_cpw_max(p.ni);
-    // Eight waves (two per SIMD: one wave per SIMD issues VALU work at about half rate)
-    // and about N / 256 columns per workgroup, so that every CU gets one workgroup.
+    // staging waves: two per SIMD when there is enough staging work, fewer for short K
+    p.stagers = std::min(kColMaxWaves, std::max(2, ntask));
+    const int cmax = col_cpw_max(p.ni, p.mr);
+    // Eight dot waves (two per SIMD: one wave per SIMD issues VALU work at about half
+    // rate) and about N / 256 columns per workgroup, so that every CU gets one workgroup.
     p.waves = kColMaxWaves;
     int C = std::min(std::max(1, (N + 255) / 256), p.waves * cmax);
     // a forced shape replaces the choice when the kernel has a variant for it
     if (g_col_waves > 0 && g_col_cols > 0) {
         const int w = std::min(g_col_waves, kColMaxWaves);
-        if (w * kColMaxTasks >= ntask && (g_col_cols + w - 1) / w <= cmax) {
+        if ((g_col_cols + w - 1) / w <= cmax) {
             p.waves = w;
             C = g_col_cols;
         }
     }
     p.cols = C;
     p.cpw = (C + p.waves - 1) / p.waves;
-    if (p.cpw < 1 || p.cpw > cmax || p.waves * kColMaxTasks < ntask) return false;
+    if (p.cpw < 1 || p.cpw > cmax || p.stagers * kColMaxTasks < ntask) return false;
     const int pieces = (C + 7) / 8 + 1;                       // 8-column scale pieces per group, at most
-    if (p.groups * pieces > kColScLoads * p.waves * kWave) return false;   // scale staging capacity
+    if (p.groups * pieces > kColScLoads * p.stagers * kWave) return false;   // staging waves' scale capacity
     p.wgs = (N + C - 1) / C;
     p.lds_bytes = size_t(p.mr) * 4 * (nch * 8 + 32) * 2 + size_t(p.mr) * nch * 8 + size_t(p.groups) * C * 4;
     if (p.lds_bytes > kMaxLds) return false;
@@ -807,6 +830,7 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
         a.nch = K / 32;
         a.groups = p.groups;
         a.cols = p.cols;
+        a.stagers = p.stagers;
         a.out_scale = out_scale;
         a.residual = residual;
         a.y = y;
