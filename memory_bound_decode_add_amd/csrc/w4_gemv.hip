@@ -749,19 +749,34 @@ bool plan_column(int M, int K, int N, GemvPlan& p) {
 
 }  // namespace
 
-// Matrix-core kernel: 8 waves of one 16-column tile each, K split into slices until
-// there are about 200 workgroups (and each slice's activation fits LDS).
+// Matrix-core kernel: 6..8 waves of one 16-column tile each, K split into slices
+// until there are about 200 workgroups (and each slice's activation fits LDS); of the
+// wave counts, the one whose workgroups fill the 256 CUs best (fewest idle slots in
+// the last round of workgroups), ties to more waves.
+int mfma_splits(int groups, int tiles) {
+    const int S = std::max((groups + kMfmaMaxSliceGroups - 1) / kMfmaMaxSliceGroups,
+                           std::min(groups, (200 + tiles - 1) / tiles));
+    const int gps = (groups + S - 1) / S;
+    return (groups + gps - 1) / gps;
+}
+
 bool plan_mfma(int M, int K, int N, GemvPlan& p) {
     if (M <= 4 || M > 16) return false;
     p.kind = kMfma;
     p.mr = 16;
     p.groups = K / kGroup;
-    p.waves = kMfmaWaves;
     p.cpw = 1;
+    p.waves = kMfmaWaves;
+    double best = 1e30;
+    for (int w = kMfmaWaves; w >= 6; --w) {
+        const int tiles = (N + 16 * p.cpw * w - 1) / (16 * p.cpw * w);
+        const int wgs = tiles * mfma_splits(p.groups, tiles);
+        const double fill = double((wgs + 255) / 256 * 256) / wgs;
+        if (fill < best - 1e-9) { best = fill; p.waves = w; }
+    }
     const int ncol = p.waves * p.cpw * 16;
     p.tiles = (N + ncol - 1) / ncol;
-    int S = std::max((p.groups + kMfmaMaxSliceGroups - 1) / kMfmaMaxSliceGroups,
-                     std::min(p.groups, (200 + p.tiles - 1) / p.tiles));
+    int S = mfma_splits(p.groups, p.tiles);
     p.gps = (p.groups + S - 1) / S;
     p.splits = (p.groups + p.gps - 1) / p.gps;
     if (p.splits > 1) {

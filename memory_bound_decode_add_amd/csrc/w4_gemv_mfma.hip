@@ -26,6 +26,8 @@
 // integer ops per word), in the pair order (j0, j4, j1, j5, j2, j6, j3, j7).  The
 // offsets are removed inside the matrix core: each group's accumulation starts from
 // the product of a constant matrix of -1032 / -1152 with the same activation operands.
+// (A bf16 operand path was measured slower in the main loop, and bf16 loses 3 bits of
+// the fp32 SwiGLU activation, which failed the parity bound at K = 14336.)
 //
 // Activation.  The workgroup stages its slice of act (16 rows, zero beyond M) in LDS as
 // block-scaled fp16 with the odd positions divided by 16 (so each product is a * q plus
@@ -150,7 +152,6 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
 
     uint4 wA[kMfmaP][TPW], wB[kMfmaP][TPW];
     uint2 sA[kMfmaP][TPW], sB[kMfmaP][TPW];
-    load_batch(0, wA, sA);
     // epilogue inputs: 4 consecutive columns of row lm per tile
     uint2 rraw[TPW];
 #pragma unroll
@@ -162,22 +163,29 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     const float os = a.out_scale ? *a.out_scale : 1.0f;
 
     // ---- stage the activation slice: item i = (row i / nkb, k-block i % nkb) ----
+    // All of a thread's items (up to UMAX of them) are loaded before the first is
+    // converted, so the staging waits for one L2 round trip, not one per item.
     const int nitems = nkb * 16;
     const int kbase = g0 * 128;
-    constexpr int U = 4;
-    for (int i0 = tid; i0 - tid < nitems; i0 += U * int(blockDim.x)) {   // uniform trip count
-        uint4 gv[U], uv[U];
+    constexpr int UMAX = PRO == kSwiGLU ? 12 : 24;
+    const int nthr = blockDim.x;
+    uint4 gv[UMAX], uv[UMAX];
+    auto load_items = [&](int base) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int it = min(i0 + u * int(blockDim.x), nitems - 1);
+        for (int u = 0; u < UMAX; ++u) {
+            if (base + u * nthr >= nitems) break;                   // uniform
+            const int it = min(base + u * nthr + tid, nitems - 1);
             const int m = min(it / nkb, a.M - 1);
             const size_t off = size_t(m) * a.lda + kbase + (it % nkb) * 8;
             gv[u] = *reinterpret_cast<const uint4*>(a.a0 + off);
             uv[u] = PRO == kSwiGLU ? *reinterpret_cast<const uint4*>(a.a1 + off) : make_uint4(0, 0, 0, 0);
         }
+    };
+    auto stage_items = [&](int base) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int it = i0 + u * int(blockDim.x);
+        for (int u = 0; u < UMAX; ++u) {
+            if (base + u * nthr >= nitems) break;                   // uniform: the whole wave stays active
+            const int it = base + u * nthr + tid;
             const int m = it / nkb, kb = it % nkb;
             float esc;
             const uint4 h = stage_item_mfma<PRO>(gv[u], uv[u], it < nitems && m < a.M, &esc);
@@ -186,7 +194,14 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
                 if ((kb & 15) == 0) esc_s[m * ng + (kb >> 4)] = esc;
             }
         }
+    };
+    for (int base = 0; base < nitems; base += UMAX * nthr) {       // uniform trip count
+        load_items(base);
+        stage_items(base);
     }
+    // the first weights are requested only now: issued earlier, they would sit ahead of
+    // the activation loads in the CU's memory queue and every staging wait would cover them
+    load_batch(0, wA, sA);
     __syncthreads();
 
     // ---- main loop: batches of kMfmaP groups, next batch's loads in flight ----
@@ -197,29 +212,45 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     const uint32_t o_even = 0xE408E408u, o_odd = 0xE480E480u;
     const f16x8_t negoff = __builtin_bit_cast(f16x8_t, make_uint4(o_even, o_odd, o_even, o_odd));
 
+    // The kMfmaP groups of a batch are independent accumulation chains; their MFMAs are
+    // interleaved so that no MFMA waits on the one issued just before it.  A group past
+    // the slice's end re-reads the last group and contributes with weight 0.
     auto compute_batch = [&](int b, const uint4 (&w)[kMfmaP][TPW], const uint2 (&sv)[kMfmaP][TPW]) {
+        f16x8_t bop[kMfmaP][4];
+        float e[kMfmaP];
 #pragma unroll
         for (int p = 0; p < kMfmaP; ++p) {
-            const int gl = b * kMfmaP + p;
-            if (gl >= ng) break;                       // uniform
-            f16x8_t bop[4];
+            const int gl = min(b * kMfmaP + p, ng - 1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(f16x8_t, act_s[lm * rs + 16 * gl + 4 * ls + j]);
-            const float e = esc_s[lm * ng + gl];
-            f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 4; ++j) bop[p][j] = __builtin_bit_cast(f16x8_t, act_s[lm * rs + 16 * gl + 4 * ls + j]);
+            e[p] = b * kMfmaP + p < ng ? esc_s[lm * ng + gl] : 0.f;
+        }
+        f32x4_t bias[kMfmaP];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bias = __builtin_amdgcn_mfma_f32_16x16x32_f16(negoff, bop[j], bias, 0, 0, 0);
+        for (int p = 0; p < kMfmaP; ++p) bias[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const uint32_t wd[4] = {w[p][t].x, w[p][t].y, w[p][t].z, w[p][t].w};
-                f32x4_t d = bias;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode_f16x8_biased(wd[j]), bop[j], d, 0, 0, 0);
-                out[t][0] = fmaf(bf16_lo(sv[p][t].x) * e, d[0], out[t][0]);
-                out[t][1] = fmaf(bf16_hi(sv[p][t].x) * e, d[1], out[t][1]);
-                out[t][2] = fmaf(bf16_lo(sv[p][t].y) * e, d[2], out[t][2]);
-                out[t][3] = fmaf(bf16_hi(sv[p][t].y) * e, d[3], out[t][3]);
+            for (int p = 0; p < kMfmaP; ++p)
+                bias[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(negoff, bop[p][j], bias[p], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            f32x4_t d[kMfmaP];
+#pragma unroll
+            for (int p = 0; p < kMfmaP; ++p) d[p] = bias[p];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int p = 0; p < kMfmaP; ++p) {
+                    const uint32_t wd = j == 0 ? w[p][t].x : j == 1 ? w[p][t].y : j == 2 ? w[p][t].z : w[p][t].w;
+                    d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode_f16x8_biased(wd), bop[p][j], d[p], 0, 0, 0);
+                }
+#pragma unroll
+            for (int p = 0; p < kMfmaP; ++p) {
+                out[t][0] = fmaf(bf16_lo(sv[p][t].x) * e[p], d[p][0], out[t][0]);
+                out[t][1] = fmaf(bf16_hi(sv[p][t].x) * e[p], d[p][1], out[t][1]);
+                out[t][2] = fmaf(bf16_lo(sv[p][t].y) * e[p], d[p][2], out[t][2]);
+                out[t][3] = fmaf(bf16_hi(sv[p][t].y) * e[p], d[p][3], out[t][3]);
             }
         }
     };
@@ -335,10 +366,8 @@ hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     a.partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes) : nullptr;
     const dim3 grid(p.tiles * p.splits);
     const int threads = p.waves * kWave;
-    if (p.cpw == 2) {
-        return pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<2, kSwiGLU>, grid, threads, p.lds_bytes, s, a)
-                              : launch_k(w4_gemv_mfma_kernel<2, kIdentity>, grid, threads, p.lds_bytes, s, a);
-    }
+    // one 16-column tile per wave (two per wave measured slower: more registers and a
+    // K split for the same workgroup count)
     return pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU>, grid, threads, p.lds_bytes, s, a)
                           : launch_k(w4_gemv_mfma_kernel<1, kIdentity>, grid, threads, p.lds_bytes, s, a);
 }
