@@ -295,8 +295,9 @@ FDEC_API int fdec_w4_dequant(const fdec_w4* W, float* w_out, fdec_stream stream)
  *   parts per column tile (0 restores the built-in choice of kernel and split; values
  *   that do not fit the shape are clamped).
  * fdec_set_gemv_tiling(waves, cols_per_workgroup): force the column-owning GEMV
- *   kernel's workgroup shape (1..8 waves, each owning at most 4 columns); (0, 0)
- *   restores the built-in choice.  Shapes the kernel cannot take fall back to it.
+ *   kernel's workgroup shape (1..14 dot waves, each owning at most 4 columns, next to
+ *   the staging waves, 16 waves in all); (0, 0) restores the built-in choice.  Shapes
+ *   the kernel cannot take fall back to it.
  * fdec_test_fail_launches(on): while on, every compute call validates its arguments
  *   and then returns FDEC_ERR_HIP without touching the GPU (exercises the error path
  *   on machines without a GPU).

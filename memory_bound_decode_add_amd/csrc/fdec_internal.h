@@ -19,7 +19,7 @@ constexpr int kGemvThreads = 256;
 constexpr int kGemvCols = 64;
 constexpr int kGroup = 128;
 constexpr int kColMaxTasks = 8;      // activation tasks (row, 512-wide block) per wave, column kernel
-constexpr int kColMaxWaves = 8;      // dot waves (and staging waves) per workgroup, column kernel
+constexpr int kColMaxWaves = 14;     // dot waves per workgroup, column kernel (with the staging waves, 16 at most)
 constexpr int kColMaxChunks = 8;
 constexpr int kColScLoads = 4;       // 16-byte scale loads per thread, column kernel     // 32-wide K chunks per lane, column kernel
 constexpr size_t kMaxLds = 160 * 1024;

@@ -210,7 +210,7 @@ __device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, b
 // Split roles keep the staging waves' issue free of weight loads, and give every SIMD
 // two waves in each phase.
 template <int MR, int CPW, int NI, int PRO>
-__global__ __launch_bounds__(2 * kColMaxWaves * kWave) void w4_gemv_col_kernel(ColArgs a) {
+__global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int S = a.stagers;                       // staging waves
     const int W = (blockDim.x >> 6) - S;           // dot waves
@@ -298,7 +298,8 @@ __global__ __launch_bounds__(2 * kColMaxWaves * kWave) void w4_gemv_col_kernel(C
     const uint16_t rraw = rsrc[size_t(min(em, a.M - 1)) * a.N + min(en, a.N - 1)];
     const float os = a.out_scale ? *a.out_scale : 1.0f;
     // weight chunks: lane l takes chunks l, l+64, ... of each of the wave's columns (a
-    // slot the wave does not own re-reads its first column: the loads stay unconditional)
+    // slot the wave does not own re-reads its first column: the loads stay unconditional,
+    // so every wait in the dot is exact; skipping them measured slower)
     uint4 wv[NI][CPW];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
@@ -719,19 +720,22 @@ bool plan_column(int M, int K, int N, GemvPlan& p) {
     p.mr = M <= 1 ? 1 : M <= 2 ? 2 : 4;
     p.ni = (nch + kWave - 1) / kWave;
     const int ntask = p.mr * nblk;
-    if (ntask > kColMaxWaves * kColMaxTasks) return false;
+    if (ntask > 8 * kColMaxTasks) return false;             // at most 8 staging waves
     // staging waves: two per SIMD when there is enough staging work, fewer for short K
-    p.stagers = std::min(kColMaxWaves, std::max(2, ntask));
+    p.stagers = std::min(8, std::max(2, ntask));
     const int cmax = col_cpw_max(p.ni, p.mr);
     // Eight dot waves (two per SIMD: one wave per SIMD issues VALU work at about half
     // rate) and about N / 256 columns per workgroup, so that every CU gets one workgroup.
-    p.waves = kColMaxWaves;
+    p.waves = 8;
     int C = std::min(std::max(1, (N + 255) / 256), p.waves * cmax);
-    // a forced shape replaces the choice when the kernel has a variant for it
+    // a forced shape replaces the choice when the kernel has a variant for it; more dot
+    // waves than 8 take slots from the staging waves (16 waves in all)
     if (g_col_waves > 0 && g_col_cols > 0) {
         const int w = std::min(g_col_waves, kColMaxWaves);
-        if ((g_col_cols + w - 1) / w <= cmax) {
+        const int st = std::min(p.stagers, 16 - w);
+        if ((g_col_cols + w - 1) / w <= cmax && st * kColMaxTasks >= ntask && st >= 1) {
             p.waves = w;
+            p.stagers = st;
             C = g_col_cols;
         }
     }
