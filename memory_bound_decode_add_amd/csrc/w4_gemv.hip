@@ -616,6 +616,8 @@ hipError_t launch_col3(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStr
 template <int MR>
 hipError_t launch_col(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStream_t s) {
     switch (p.cpw) {
+        case 8: return launch_col3<MR, 8, 1>(pro, a, p, s);
+        case 6: return launch_col3<MR, 6, 1>(pro, a, p, s);
         case 4:
             switch (p.ni) {
                 case 1: return launch_col3<MR, 4, 1>(pro, a, p, s);
@@ -710,8 +712,12 @@ __global__ void fill_zero_kernel(uint4* p, int64_t n16, unsigned char* tail, int
 // pairs are instantiated.
 int col_cpw_max(int ni, int mr) {
     if (mr >= 4) return ni <= 1 ? 4 : ni <= 3 ? 2 : 1;
-    return ni <= 3 ? 4 : ni <= 4 ? 3 : ni <= 6 ? 2 : 1;
+    return ni <= 1 ? 8 : ni <= 3 ? 4 : ni <= 4 ? 3 : ni <= 6 ? 2 : 1;
 }
+
+// Columns per wave as instantiated: 5 and 7 round up to 6 and 8 (only for one chunk
+// per lane); the extra slots are skipped.
+int col_cpw_round(int cpw) { return cpw <= 4 ? cpw : cpw <= 6 ? 6 : 8; }
 
 bool plan_column(int M, int K, int N, GemvPlan& p) {
     if (M > 4 || K > 32 * kColMaxChunks * kWave) return false;
@@ -726,8 +732,15 @@ bool plan_column(int M, int K, int N, GemvPlan& p) {
     const int cmax = col_cpw_max(p.ni, p.mr);
     // Eight dot waves (two per SIMD: one wave per SIMD issues VALU work at about half
     // rate) and about N / 256 columns per workgroup, so that every CU gets one workgroup.
+    // When eight waves cannot hold that many columns, the fewest waves (at most
+    // 16 - stagers) that reach the smallest columns-per-wave variant.
+    const int cwant = std::max(1, (N + 255) / 256);
     p.waves = 8;
-    int C = std::min(std::max(1, (N + 255) / 256), p.waves * cmax);
+    if (cwant > 8 * cmax) {
+        const int cpw = std::min(cmax, col_cpw_round((cwant + 15 - p.stagers) / (16 - p.stagers)));
+        p.waves = std::max(8, std::min(16 - p.stagers, (cwant + cpw - 1) / cpw));
+    }
+    int C = std::min(cwant, p.waves * cmax);
     // a forced shape replaces the choice when the kernel has a variant for it; more dot
     // waves than 8 take slots from the staging waves (16 waves in all)
     if (g_col_waves > 0 && g_col_cols > 0) {
@@ -740,7 +753,7 @@ bool plan_column(int M, int K, int N, GemvPlan& p) {
         }
     }
     p.cols = C;
-    p.cpw = (C + p.waves - 1) / p.waves;
+    p.cpw = col_cpw_round((C + p.waves - 1) / p.waves);
     if (p.cpw < 1 || p.cpw > cmax || p.stagers * kColMaxTasks < ntask) return false;
     const int pieces = (C + 7) / 8 + 1;                       // 8-column scale pieces per group, at most
     if (p.groups * pieces > kColScLoads * p.stagers * kWave) return false;   // staging waves' scale capacity

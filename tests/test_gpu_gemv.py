@@ -90,7 +90,8 @@ def test_swiglu_gemv_every_split(split):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 8), (3, 384, 520), (5, 1280, 136), (16, 2048, 1032),
-                                   (2, 256, 4104), (8, 4096, 776), (16, 14336, 128)])
+                                   (2, 256, 4104), (8, 4096, 776), (16, 14336, 128),
+                                   (1, 1920, 17928), (2, 1024, 20480)])
 def test_swiglu_gemv_ragged_shapes_with_residual(M, K, N):
     say(f"[gemv] ragged M={M} K={K} N={N} with residual")
     inp = synth.swiglu_gemv_inputs(M, K, N, seed=M * 7 + K + N, out_scale=0.75, with_residual=True)
@@ -146,7 +147,7 @@ def _exact_case(M, K, N, seed):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 512), (1, 9216, 2560), (4, 2048, 256), (8, 1024, 136),
-                                   (16, 2048, 264), (16, 14336, 520)])
+                                   (16, 2048, 264), (16, 14336, 520), (1, 1536, 17920), (2, 1024, 20488)])
 def test_swiglu_gemv_exact_special_cases_bit_exact(M, K, N):
     say(f"[gemv] exact special case M={M} K={K} N={N}")
     gb, ub, qw, sb, exact = _exact_case(M, K, N, seed=K + N)
