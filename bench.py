@@ -276,6 +276,32 @@ def bench_extras(torch, F, synth, n_sets_gemv):
                                          "kernels_per_step": graph.kernel_count, "bytes_per_step": b,
                                          "graph_gbps": b / tg / 1e9, "graph_frac_of_peak": b / tg / 1e9 / PEAK_GBPS}
     graph.close()
+
+    # the same chain with the two-kernel layer (norm as the gate_up prologue, SwiGLU as
+    # its epilogue)
+    log("[bench] 28-layer two-kernel MLP chain M=1 H=1536 I=8960")
+    bufs2 = F.Mlp2Buffers.empty(M, H, I, out_is_x=True)
+    ws2 = F.workspace(F.mlp2_workspace_bytes(M, H, I))
+    graph2 = F.Mlp2Graph(layers, bufs2, ws2)
+    b2 = NL * T.mlp2_layer_bytes(M, H, I, False)
+
+    def reset2():
+        bufs2.x.copy_(x0)
+        bufs2.residual.copy_(r0)
+
+    reset2()
+    graph2.launch()
+    torch.cuda.synchronize()
+    tg2 = timer(graph2.launch, 20) / 20
+    reset2()
+    F.mlp_chain2(layers, bufs2, ws2)
+    torch.cuda.synchronize()
+    te2 = timer(lambda: F.mlp_chain2(layers, bufs2, ws2), 20) / 20
+    out["mlp2_chain_qwen2_5_1_5b_28l"] = {"graph_us_per_step": tg2 * 1e6, "eager_us_per_step": te2 * 1e6,
+                                          "kernels_per_step": graph2.kernel_count, "bytes_per_step": b2,
+                                          "graph_gbps": b2 / tg2 / 1e9,
+                                          "graph_frac_of_peak": b2 / tg2 / 1e9 / PEAK_GBPS}
+    graph2.close()
     return out
 
 

@@ -231,6 +231,50 @@ FDEC_API int fdec_graph_kernel_count(fdec_graph graph);
 FDEC_API int fdec_graph_destroy(fdec_graph graph);
 
 /*
+ * The layer as two kernels: the other fusion placement of [P4] section 5 ("the fusion
+ * boundary problem": the gate_up GEMM with a silu * up epilogue writing act, the
+ * GEMM-with-prologue and reduction-with-consumer rows of its fusion list), taken one
+ * step further by running the add + RMSNorm as that GEMM's prologue.
+ *
+ * fdec_add_rmsnorm_w4_gemv_swiglu: one kernel computing
+ *     h   = bf16(x + residual)                                   -> h_out [M][H]
+ *     y   = h * norm_weight / sqrt(mean_H(h^2) + eps)            (fp32, never written)
+ *     g   = y @ dequant(gate_up)[:, :I],  u = y @ dequant(gate_up)[:, I:]   (fp32)
+ *     act = bf16(silu(g) * u)                                    -> act_out [M][I]
+ *   Every workgroup reads the whole rows of x and residual, so h_out may alias neither
+ *   (nor any other input); act_out may not overlap anything.  H = gate_up.K,
+ *   gate_up.N = 2I with I a multiple of 8.  Implemented for the column GEMV only
+ *   (M <= 4 and H small enough for its register budget: H <= 16384 / ceil-pow2(M) and
+ *   about I / 256 pairs per workgroup); otherwise FDEC_ERR_UNSUPPORTED.
+ *
+ * fdec_mlp_decode2: the layer of fdec_mlp_decode in two kernels, same results up to
+ * the roundings the three-kernel form adds (y_norm and gate_up are not written):
+ *   1. fdec_add_rmsnorm_w4_gemv_swiglu(x, residual) -> h (into ws), act;
+ *   2. out = bf16(out_scale * act @ dequant(down) [+ h]); the same kernel copies h into
+ *      residual, so afterwards residual = h as with fdec_mlp_decode.
+ *   act: bf16 [M][I] (caller-owned scratch).  out may equal x.  ws: at least
+ *   fdec_mlp2_workspace_bytes(M, H, I) bytes (it holds h between the kernels).
+ *   FDEC_ERR_UNSUPPORTED where either projection does not fit the column GEMV.
+ * fdec_mlp_chain2 / fdec_mlp_graph_create2: the chain of fdec_mlp_chain and
+ * fdec_mlp_graph_create built from the two-kernel layer (2 * n_layers kernels).
+ */
+FDEC_API int fdec_add_rmsnorm_w4_gemv_swiglu(const fdec_bf16* x, const fdec_bf16* residual,
+                                             const fdec_bf16* norm_weight, float eps,
+                                             const fdec_w4* gate_up, int32_t M, fdec_bf16* h_out,
+                                             fdec_bf16* act_out, fdec_stream stream);
+FDEC_API size_t fdec_mlp2_workspace_bytes(int32_t M, int32_t H, int32_t I);
+FDEC_API int fdec_mlp_decode2(const fdec_mlp_layer* layer, int32_t M, const fdec_bf16* x,
+                              fdec_bf16* residual, fdec_bf16* act, fdec_bf16* out, void* ws,
+                              size_t ws_bytes, fdec_stream stream);
+FDEC_API int fdec_mlp_chain2(const fdec_mlp_layer* layers, int32_t n_layers, int32_t M,
+                             fdec_bf16* x, fdec_bf16* residual, fdec_bf16* act, void* ws,
+                             size_t ws_bytes, fdec_stream stream);
+FDEC_API int fdec_mlp_graph_create2(const fdec_mlp_layer* layers, int32_t n_layers,
+                                    int32_t M, fdec_bf16* x, fdec_bf16* residual,
+                                    fdec_bf16* act, void* ws, size_t ws_bytes,
+                                    fdec_stream stream, fdec_graph* out);
+
+/*
  * The unfused sequences the fused kernels replace, kept for comparison.
  *
  * FDEC_UNFUSED_PRODUCT ([P1], the materialised broadcast product; M == 1 only,

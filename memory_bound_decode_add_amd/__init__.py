@@ -72,6 +72,13 @@ _SIGS = {
                                       _c_p]),
     "fdec_mlp_graph_create": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p,
                                              _sz, _c_p, ctypes.POINTER(_c_p)]),
+    "fdec_add_rmsnorm_w4_gemv_swiglu": (ctypes.c_int, [_c_p, _c_p, _c_p, ctypes.c_float, ctypes.POINTER(CW4), _i32,
+                                                       _c_p, _c_p, _c_p]),
+    "fdec_mlp2_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_mlp_decode2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "fdec_mlp_chain2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "fdec_mlp_graph_create2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _sz,
+                                              _c_p, ctypes.POINTER(_c_p)]),
     "fdec_graph_launch": (ctypes.c_int, [_c_p, _c_p]),
     "fdec_graph_kernel_count": (ctypes.c_int, [_c_p]),
     "fdec_graph_destroy": (ctypes.c_int, [_c_p]),
@@ -417,6 +424,92 @@ class MlpGraph:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------------------------------------
+# the two-kernel layer: add + RMSNorm as the gate_up prologue, SwiGLU as its epilogue
+# ---------------------------------------------------------------------------
+def add_rmsnorm_w4_gemv_swiglu(x, residual, weight, W_gu: W4Weight, eps=1e-6, h_out=None, act_out=None):
+    """(h, act): h = bf16(x + residual); act = bf16(silu(g) * u) with [g, u] = rmsnorm(h) @ W_gu."""
+    M, H = x.shape
+    I = W_gu.N // 2
+    _need(x, "x", torch.bfloat16, shape=(M, H))
+    _need(residual, "residual", torch.bfloat16, shape=(M, H))
+    _need(weight, "weight", torch.bfloat16, shape=(H,))
+    h = h_out if h_out is not None else torch.empty_like(x)
+    act = act_out if act_out is not None else torch.empty((M, I), dtype=torch.bfloat16, device=x.device)
+    _need(h, "h_out", torch.bfloat16, shape=(M, H))
+    _need(act, "act_out", torch.bfloat16, shape=(M, I))
+    cw = W_gu.c()
+    _check(lib().fdec_add_rmsnorm_w4_gemv_swiglu(x.data_ptr(), residual.data_ptr(), weight.data_ptr(), float(eps),
+                                                 ctypes.byref(cw), M, h.data_ptr(), act.data_ptr(),
+                                                 _stream(x.device)))
+    return h, act
+
+
+def mlp2_workspace_bytes(M, H, I) -> int:
+    return int(lib().fdec_mlp2_workspace_bytes(M, H, I))
+
+
+@dataclass
+class Mlp2Buffers:
+    """Caller-owned activation buffers of the two-kernel layer (or chain) at batch M."""
+    x: torch.Tensor          # [M, H]  layer input; with out=x, the layer output
+    residual: torch.Tensor   # [M, H]
+    act: torch.Tensor        # [M, I]  silu(gate) * up, written by the first kernel
+    out: torch.Tensor        # [M, H]
+
+    @classmethod
+    def empty(cls, M, H, I, device="cuda", out_is_x=False):
+        x = torch.empty((M, H), dtype=torch.bfloat16, device=device)
+        return cls(x, torch.empty_like(x), torch.empty((M, I), dtype=torch.bfloat16, device=device),
+                   x if out_is_x else torch.empty_like(x))
+
+
+def _check_bufs2(layer: MlpLayer, b: Mlp2Buffers):
+    M = b.x.shape[0]
+    for name, t, shp in (("x", b.x, (M, layer.H)), ("residual", b.residual, (M, layer.H)),
+                         ("act", b.act, (M, layer.I)), ("out", b.out, (M, layer.H))):
+        _need(t, name, torch.bfloat16, shape=shp)
+    return M
+
+
+def mlp_decode2(layer: MlpLayer, bufs: Mlp2Buffers, ws=None):
+    """One two-kernel layer: residual <- h; act; out (see fdec.h)."""
+    M = _check_bufs2(layer, bufs)
+    ws = _ws(ws, mlp2_workspace_bytes(M, layer.H, layer.I), bufs.x.device)
+    cl = layer.c()
+    _check(lib().fdec_mlp_decode2(ctypes.byref(cl), M, bufs.x.data_ptr(), bufs.residual.data_ptr(),
+                                  bufs.act.data_ptr(), bufs.out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  _stream(bufs.x.device)))
+    return bufs
+
+
+def mlp_chain2(layers, bufs: Mlp2Buffers, ws=None):
+    """All layers eagerly, two kernels each, x updated in place, residual <- the last h."""
+    M = _check_bufs2(layers[0], bufs)
+    ws = _ws(ws, mlp2_workspace_bytes(M, layers[0].H, layers[0].I), bufs.x.device)
+    arr = _layer_array(layers)
+    _check(lib().fdec_mlp_chain2(arr, len(layers), M, bufs.x.data_ptr(), bufs.residual.data_ptr(),
+                                 bufs.act.data_ptr(), ws.data_ptr(), ws.numel(), _stream(bufs.x.device)))
+    return bufs
+
+
+class Mlp2Graph(MlpGraph):
+    """The two-kernel layer chain captured once into a hipGraph; launch() replays it."""
+
+    def __init__(self, layers, bufs: Mlp2Buffers, ws=None, stream: torch.cuda.Stream | None = None):
+        M = _check_bufs2(layers[0], bufs)
+        self.layers = list(layers)
+        self.bufs = bufs
+        self.ws = _ws(ws, mlp2_workspace_bytes(M, layers[0].H, layers[0].I), bufs.x.device)
+        self._handle = _c_p()
+        cap = stream if stream is not None else torch.cuda.Stream(device=bufs.x.device)
+        cap.wait_stream(torch.cuda.current_stream(bufs.x.device))
+        arr = _layer_array(self.layers)
+        _check(lib().fdec_mlp_graph_create2(arr, len(self.layers), M, bufs.x.data_ptr(), bufs.residual.data_ptr(),
+                                            bufs.act.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+                                            cap.cuda_stream, ctypes.byref(self._handle)))
 
 
 def unfused_swiglu_w4_gemv(mode, g, u, W: W4Weight, out_scale=None, residual=None, out=None, ws=None):

@@ -206,6 +206,60 @@ int check_chain(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d)
     return FDEC_OK;
 }
 
+// ---- the two-kernel layer ----
+// Workspace: h (the new residual) staged between the two kernels.  The first kernel
+// cannot write h into the residual buffer itself: every workgroup of it reads that buffer.
+size_t mlp2_ws(int M, int H) { return align_up(size_t(M) * H * 2); }
+
+int check_layer2(const fdec_mlp_layer* L, int M, LayerDims* d) {
+    int st = check_layer(L, M, d);
+    if (st != FDEC_OK) return st;
+    if (!norm_gemv_swiglu_supported(M, d->H, d->I) || !gemv_column_supported(M, d->I, d->H))
+        return fail(FDEC_ERR_UNSUPPORTED,
+                    "the two-kernel layer needs the column GEMV for both projections (M = %d, H = %d, I = %d)", M,
+                    d->H, d->I);
+    return FDEC_OK;
+}
+
+int check_layer2_buffers(const fdec_mlp_layer* L, int M, LayerDims d, const fdec_bf16* x,
+                         const fdec_bf16* residual, const fdec_bf16* act, const fdec_bf16* out, void* ws,
+                         size_t ws_bytes, size_t need) {
+    if (!x || !residual || !act || !out) return fail(FDEC_ERR_NULL, "x, residual, act and out are required");
+    if (!aligned16(x) || !aligned16(residual) || !aligned16(act) || !aligned16(out))
+        return fail(FDEC_ERR_ALIGN, "every activation buffer must be 16-byte aligned");
+    if (ws_bytes < need) return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);
+    if (!ws) return fail(FDEC_ERR_NULL, "workspace is NULL");
+    if (!aligned16(ws)) return fail(FDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t t = size_t(M) * d.H * 2;
+    const Span X{x, t}, R{residual, t}, A{act, size_t(M) * d.I * 2}, O{out, t}, WS{ws, need};
+    const Span wts[] = {w4_qspan(&L->gate_up), w4_sspan(&L->gate_up), w4_qspan(&L->down), w4_sspan(&L->down),
+                        {L->norm_weight, size_t(d.H) * 2}, {L->out_scale, 4}};
+    const Span outs[] = {R, A, O, WS};
+    for (const Span& o : outs)
+        for (const Span& w : wts)
+            if (overlap(o, w)) return fail(FDEC_ERR_ALIAS, "an output buffer overlaps a weight");
+    if (overlap(R, X) || overlap(R, A) || overlap(R, O) || overlap(R, WS) || overlap(A, X) || overlap(A, O) ||
+        overlap(A, WS) || overlap(O, WS) || overlap(X, WS) || (overlap(O, X) && out != x))
+        return fail(FDEC_ERR_ALIAS, "activation buffers overlap (only out == x is allowed)");
+    return FDEC_OK;
+}
+
+hipError_t enqueue_layer2(const fdec_mlp_layer* L, int M, LayerDims d, const fdec_bf16* x, fdec_bf16* residual,
+                          fdec_bf16* act, fdec_bf16* out, void* ws, hipStream_t s) {
+    uint16_t* h = static_cast<uint16_t*>(ws);
+    hipError_t e = launch_norm_gemv_swiglu(x, residual, L->norm_weight, L->eps, L->gate_up.qweight,
+                                           L->gate_up.scales, M, d.H, d.I, h, act, s);
+    if (e != hipSuccess) return e;
+    return launch_gemv_copy(kIdentity, act, d.I, L->down.qweight, L->down.scales, M, d.I, d.H, L->out_scale,
+                            L->residual_in_epilogue ? h : nullptr, out, h, residual, size_t(M) * d.H * 2, s);
+}
+
+int check_chain2(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d) {
+    int st = check_chain(layers, n_layers, M, d);
+    if (st != FDEC_OK) return st;
+    return check_layer2(&layers[0], M, d);
+}
+
 // ---- unfused ----
 size_t unfused_norm_ws(int M, int H) {
     return 2 * align_up(size_t(M) * H * 4) + align_up(size_t(M) * 3 * 4);
@@ -424,6 +478,110 @@ FDEC_API int fdec_graph_destroy(fdec_graph graph) {
     hipError_t e2 = graph->graph ? hipGraphDestroy(graph->graph) : hipSuccess;
     delete graph;
     return hip_status(e1 != hipSuccess ? e1 : e2, "graph destroy");
+}
+
+FDEC_API int fdec_add_rmsnorm_w4_gemv_swiglu(const fdec_bf16* x, const fdec_bf16* residual,
+                                             const fdec_bf16* norm_weight, float eps, const fdec_w4* gate_up,
+                                             int32_t M, fdec_bf16* h_out, fdec_bf16* act_out, fdec_stream stream) {
+    int st;
+    if ((st = check_w4(gate_up, "gate_up")) != FDEC_OK) return st;
+    if ((st = check_m(M)) != FDEC_OK) return st;
+    const int H = gate_up->K;
+    if (gate_up->N % 16) return fail(FDEC_ERR_SHAPE, "gate_up.N = %d must be 2I with I a multiple of 8", gate_up->N);
+    const int I = gate_up->N / 2;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(FDEC_ERR_ARG, "eps must be finite and >= 0");
+    if (!x || !residual || !norm_weight || !h_out || !act_out)
+        return fail(FDEC_ERR_NULL, "x, residual, norm_weight, h_out and act_out are required");
+    if (!aligned16(x) || !aligned16(residual) || !aligned16(norm_weight) || !aligned16(h_out) || !aligned16(act_out))
+        return fail(FDEC_ERR_ALIGN, "every tensor must be 16-byte aligned");
+    const size_t t = size_t(M) * H * 2;
+    const Span X{x, t}, R{residual, t}, NW{norm_weight, size_t(H) * 2}, Hs{h_out, t}, A{act_out, size_t(M) * I * 2};
+    const Span ins[] = {X, R, NW, w4_qspan(gate_up), w4_sspan(gate_up)};
+    for (const Span& in : ins)
+        if (overlap(Hs, in) || overlap(A, in)) return fail(FDEC_ERR_ALIAS, "h_out or act_out overlaps an input");
+    if (overlap(Hs, A)) return fail(FDEC_ERR_ALIAS, "h_out overlaps act_out");
+    if (!norm_gemv_swiglu_supported(M, H, I))
+        return fail(FDEC_ERR_UNSUPPORTED, "no column-kernel variant for M = %d, H = %d, I = %d", M, H, I);
+    if (g_fail_launches) return injected();
+    return hip_status(launch_norm_gemv_swiglu(x, residual, norm_weight, eps, gate_up->qweight, gate_up->scales, M, H,
+                                              I, h_out, act_out, static_cast<hipStream_t>(stream)),
+                      "fused gate_up launch");
+}
+
+FDEC_API size_t fdec_mlp2_workspace_bytes(int32_t M, int32_t H, int32_t I) {
+    if (M < 1 || M > 16 || H <= 0 || H % 128 || I <= 0 || I % 128) return 0;
+    return mlp2_ws(M, H);
+}
+
+FDEC_API int fdec_mlp_decode2(const fdec_mlp_layer* layer, int32_t M, const fdec_bf16* x, fdec_bf16* residual,
+                              fdec_bf16* act, fdec_bf16* out, void* ws, size_t ws_bytes, fdec_stream stream) {
+    LayerDims d;
+    int st = check_layer2(layer, M, &d);
+    if (st != FDEC_OK) return st;
+    st = check_layer2_buffers(layer, M, d, x, residual, act, out, ws, ws_bytes, mlp2_ws(M, d.H));
+    if (st != FDEC_OK) return st;
+    if (g_fail_launches) return injected();
+    return hip_status(enqueue_layer2(layer, M, d, x, residual, act, out, ws, static_cast<hipStream_t>(stream)),
+                      "layer launch");
+}
+
+FDEC_API int fdec_mlp_chain2(const fdec_mlp_layer* layers, int32_t n_layers, int32_t M, fdec_bf16* x,
+                             fdec_bf16* residual, fdec_bf16* act, void* ws, size_t ws_bytes, fdec_stream stream) {
+    LayerDims d;
+    int st = check_chain2(layers, n_layers, M, &d);
+    if (st != FDEC_OK) return st;
+    for (int l = 0; l < n_layers; ++l)
+        if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, mlp2_ws(M, d.H))) !=
+            FDEC_OK)
+            return st;
+    if (g_fail_launches) return injected();
+    for (int l = 0; l < n_layers; ++l) {
+        const hipError_t e = enqueue_layer2(&layers[l], M, d, x, residual, act, x, ws, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_status(e, "chain launch");
+    }
+    return ok();
+}
+
+FDEC_API int fdec_mlp_graph_create2(const fdec_mlp_layer* layers, int32_t n_layers, int32_t M, fdec_bf16* x,
+                                    fdec_bf16* residual, fdec_bf16* act, void* ws, size_t ws_bytes,
+                                    fdec_stream stream, fdec_graph* out) {
+    if (!out) return fail(FDEC_ERR_NULL, "out is NULL");
+    if (!stream) return fail(FDEC_ERR_ARG, "graph capture needs a non-null stream");
+    LayerDims d;
+    int st = check_chain2(layers, n_layers, M, &d);
+    if (st != FDEC_OK) return st;
+    for (int l = 0; l < n_layers; ++l)
+        if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, mlp2_ws(M, d.H))) !=
+            FDEC_OK)
+            return st;
+    if (g_fail_launches) return injected();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    fdec_graph_s* G = new (std::nothrow) fdec_graph_s;
+    if (!G) return fail(FDEC_ERR_ARG, "out of host memory");
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        delete G;
+        return hip_status(e, "hipStreamBeginCapture");
+    }
+    hipError_t le = hipSuccess;
+    for (int l = 0; l < n_layers && le == hipSuccess; ++l) le = enqueue_layer2(&layers[l], M, d, x, residual, act, x, ws, s);
+    e = hipStreamEndCapture(s, &G->graph);
+    if (le != hipSuccess || e != hipSuccess) {
+        if (G->graph) (void)hipGraphDestroy(G->graph);
+        delete G;
+        return hip_status(le != hipSuccess ? le : e, "graph capture");
+    }
+    size_t nodes = 0;
+    if (hipGraphGetNodes(G->graph, nullptr, &nodes) != hipSuccess) nodes = 0;
+    G->kernels = int(nodes);
+    e = hipGraphInstantiate(&G->exec, G->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(G->graph);
+        delete G;
+        return hip_status(e, "hipGraphInstantiate");
+    }
+    *out = G;
+    return ok();
 }
 
 FDEC_API size_t fdec_unfused_gemv_workspace_bytes(int32_t mode, int32_t M, int32_t K, int32_t N) {

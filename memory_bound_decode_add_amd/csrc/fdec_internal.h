@@ -19,6 +19,7 @@ constexpr int kGemvThreads = 256;
 constexpr int kGemvCols = 64;
 constexpr int kGroup = 128;
 constexpr int kColMaxTasks = 8;      // activation tasks (row, 512-wide block) per wave, column kernel
+constexpr int kColMaxTasksNorm = 4;  // the same with the add + RMSNorm prologue (three loads per task)
 constexpr int kColMaxWaves = 14;     // dot waves per workgroup, column kernel (with the staging waves, 16 at most)
 constexpr int kColMaxChunks = 8;
 constexpr int kColScLoads = 4;       // 16-byte scale loads per thread, column kernel     // 32-wide K chunks per lane, column kernel
@@ -53,7 +54,9 @@ struct GemvPlan {
 GemvPlan plan_gemv(int M, int K, int N);
 size_t gemv_workspace_bytes(int M, int K, int N);
 
-enum Prologue { kIdentity = 0, kSwiGLU = 1 };
+// kAddRmsNorm: the activation is rmsnorm(x + r) * w over the whole row (the fused
+// layer's gate_up), and the epilogue writes silu(gate) * up of column pairs (i, I + i).
+enum Prologue { kIdentity = 0, kSwiGLU = 1, kAddRmsNorm = 2 };
 
 // Launchers: arguments are validated by the caller; they return the HIP error of the
 // launch (hipSuccess on success).
@@ -64,6 +67,15 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
                        void* ws, hipStream_t s);
+// The fused layer's two kernels (column kernel only).
+bool norm_gemv_swiglu_supported(int M, int K, int I);
+hipError_t launch_norm_gemv_swiglu(const uint16_t* x, const uint16_t* r, const uint16_t* nw, float eps,
+                                   const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
+                                   uint16_t* h_out, uint16_t* act, hipStream_t s);
+bool gemv_column_supported(int M, int K, int N);
+hipError_t launch_gemv_copy(Prologue pro, const uint16_t* a0, int64_t lda, const uint32_t* qw, const uint16_t* sc,
+                            int M, int K, int N, const float* out_scale, const uint16_t* residual, uint16_t* y,
+                            const void* cp_src, void* cp_dst, size_t cp_bytes, hipStream_t s);
 hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,

@@ -125,6 +125,16 @@ struct ColArgs {
     const float* out_scale;
     const uint16_t* residual;
     uint16_t* y;
+    // add + RMSNorm prologue with the SwiGLU pair epilogue (prologue kAddRmsNorm)
+    const uint16_t* nw;     // RMSNorm weight [K]
+    float eps;
+    uint16_t* h_out;        // h = bf16(x + r) [M][K], written by workgroup 0
+    int pairs;              // gate/up column pairs per workgroup (cols = 2 * pairs)
+    int half_n;             // I = N / 2: column i pairs with column I + i; y is [M][I]
+    // side copy of cp_n16 16-byte words, spread over the grid's dot waves
+    const uint4* cp_src;
+    uint4* cp_dst;
+    int cp_n16;
 };
 
 // Staged activation of the column kernel, per row: fp16 in the layout [quarter q][chunk
@@ -151,22 +161,9 @@ struct ColArgs {
 // summed from the rounded values, so they cancel exactly whatever the rounding.
 __device__ __forceinline__ int col_quarter_stride(int nch) { return nch * 8 + 32; }
 
-template <int PRO>
-__device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, bool live, bool in_k,
-                                               bool quad_lead, _Float16* dst, float2* eb_dst) {
-    float v[8];                                    // k = 8w + j, j = 0..7
-    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-    const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        if (PRO == kSwiGLU) {
-            v[2 * h] = silu_f32(bf16_lo(gw[h])) * bf16_lo(uw[h]);
-            v[2 * h + 1] = silu_f32(bf16_hi(gw[h])) * bf16_hi(uw[h]);
-        } else {
-            v[2 * h] = bf16_lo(gw[h]);
-            v[2 * h + 1] = bf16_hi(gw[h]);
-        }
-    }
+// Eight activation values k = 8w + j (j = 0..7) of one lane -> LDS (see above).
+__device__ __forceinline__ void stage_values_col(float (&v)[8], bool live, bool in_k, bool quad_lead,
+                                                 _Float16* dst, float2* eb_dst) {
     float mx = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -199,6 +196,38 @@ __device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, b
     if (quad_lead && in_k) *eb_dst = make_float2(__builtin_ldexpf(1.0f, E), b);
 }
 
+template <int PRO>
+__device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, bool live, bool in_k,
+                                               bool quad_lead, _Float16* dst, float2* eb_dst) {
+    float v[8];                                    // k = 8w + j, j = 0..7
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        if (PRO == kSwiGLU) {
+            v[2 * h] = silu_f32(bf16_lo(gw[h])) * bf16_lo(uw[h]);
+            v[2 * h + 1] = silu_f32(bf16_hi(gw[h])) * bf16_hi(uw[h]);
+        } else {
+            v[2 * h] = bf16_lo(gw[h]);
+            v[2 * h + 1] = bf16_hi(gw[h]);
+        }
+    }
+    stage_values_col(v, live, in_k, quad_lead, dst, eb_dst);
+}
+
+// Sum over a full wave (all 64 lanes active), returned uniform, in a fixed order.
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+    v += dpp<kQuadSwap1>(v);
+    v += dpp<kQuadSwap2>(v);
+    v += dpp<kRowRor4>(v);
+    v += dpp<kRowRor8>(v);
+    const int b = __builtin_bit_cast(int, v);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+}
+
 // The workgroup has S + W waves in two roles.
 //  * Staging waves 0..S-1: they load the activation inputs and the group scales, stage
 //    them in LDS and retire at the barrier.  They are the older waves, so their loads
@@ -212,9 +241,13 @@ __device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, b
 template <int MR, int CPW, int NI, int PRO>
 __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
+    // With the add + RMSNorm prologue the workgroup owns column pairs (i, I + i): gate
+    // and up of the same i, so the epilogue can form silu(gate) * up.
+    constexpr bool PAIR = PRO == kAddRmsNorm;
+    constexpr int TMAX = PAIR ? kColMaxTasksNorm : kColMaxTasks;
     const int S = a.stagers;                       // staging waves
     const int W = (blockDim.x >> 6) - S;           // dot waves
-    const int C = a.cols;                          // columns per workgroup
+    const int C = a.cols;                          // columns per workgroup (2 * pairs with PAIR)
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -224,62 +257,144 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     _Float16* act_s = reinterpret_cast<_Float16*>(smem);                          // [MR][4][qs]
     float2* eb_s = reinterpret_cast<float2*>(smem + size_t(MR) * 4 * qs * 2);     // [MR][nch]
     float* sc_s = reinterpret_cast<float*>(eb_s + MR * a.nch);                     // [groups][C]
+    float* ss_s = sc_s + a.groups * C;                                             // [S][MR]
 
-    const int col0 = xcd_remap(blockIdx.x, gridDim.x) * C;
+    // first column (pair) of the workgroup; column of local column slot cj in [0, C)
+    const int cbase = xcd_remap(blockIdx.x, gridDim.x) * (PAIR ? a.pairs : C);
+    auto column = [&](int cj) {
+        if (PAIR) return cj < a.pairs ? cbase + cj : a.half_n + cbase + (cj - a.pairs);
+        return cbase + cj;
+    };
 
     if (wave < S) {
         // ================= staging waves =================
         const int sw = wave, stid = tid, nst = S * kWave;
         // ---- activation inputs: task t = sw + S * ti -> (row t % MR, block t / MR) ----
         const int ntask = MR * nblk;
-        uint4 ga[kColMaxTasks], ua[kColMaxTasks];
+        uint4 ga[TMAX], ua[TMAX], wa[PAIR ? TMAX : 1];
 #pragma unroll
-        for (int ti = 0; ti < kColMaxTasks; ++ti) {
+        for (int ti = 0; ti < TMAX; ++ti) {
             const int t = sw + S * ti;
             if (t >= ntask) break;                 // uniform across the wave
             const int m = min(t % MR, a.M - 1), b = t / MR;
             const int k = min(b * 64 + lane, kw - 1) * 8;
             ga[ti] = *reinterpret_cast<const uint4*>(a.a0 + size_t(m) * a.lda + k);
-            ua[ti] = PRO == kSwiGLU ? *reinterpret_cast<const uint4*>(a.a1 + size_t(m) * a.lda + k)
-                                    : make_uint4(0, 0, 0, 0);
+            ua[ti] = PRO != kIdentity ? *reinterpret_cast<const uint4*>(a.a1 + size_t(m) * a.lda + k)
+                                      : make_uint4(0, 0, 0, 0);
+            if (PAIR) wa[ti] = *reinterpret_cast<const uint4*>(a.nw + k);
         }
-        // ---- group scales of columns [col0, col0 + C), as aligned 8-column pieces of
-        // each group's row: item (g, p) is the piece (col0 / 8 + p) of group g ----
-        const int p0 = col0 >> 3;
-        const int npc = ((min(col0 + C, a.N) - 1) >> 3) - p0 + 1;
-        const int nsc = a.groups * npc;
+        // ---- group scales of the workgroup's columns, as aligned 8-column pieces of
+        // each group's row.  One column range, or two with PAIR (gate i.., up I + i..):
+        // range r covers columns [cb_r, cb_r + n_r) and LDS slots [o_r, o_r + n_r). ----
+        const int n0 = PAIR ? a.pairs : C;
+        const int cb0 = cbase, cb1 = PAIR ? a.half_n + cbase : 0;
+        const int p00 = cb0 >> 3, npc0 = ((min(cb0 + n0, a.N) - 1) >> 3) - p00 + 1;
+        const int p01 = cb1 >> 3, npc1 = PAIR ? ((min(cb1 + n0, a.N) - 1) >> 3) - p01 + 1 : 0;
+        const int nsc0 = a.groups * npc0, nsc = nsc0 + a.groups * npc1;
         uint4 sraw[kColScLoads];
 #pragma unroll
         for (int r = 0; r < kColScLoads; ++r) {
             if (r * nst >= nsc) break;             // uniform
             const int idx = min(stid + r * nst, nsc - 1);
-            const int g = idx / npc, pc = p0 + idx % npc;
+            const bool hi = idx >= nsc0;
+            const int j = hi ? idx - nsc0 : idx, npc = hi ? npc1 : npc0;
+            const int g = j / npc, pc = (hi ? p01 : p00) + j % npc;
             sraw[r] = *reinterpret_cast<const uint4*>(a.sc + size_t(g) * a.N + pc * 8);
         }
         // ---- activations, per-chunk scale and offsets, group scales to LDS ----
         // word wi = 64 b + lane: chunk wi / 4, quarter wi % 4
         const int lofs = (lane & 3) * qs + (lane >> 2) * 8;
+        if (PAIR) {
+            // h = bf16(x + r) (written out by workgroup 0), then the mean of h^2 over the
+            // row: per-wave sums meet in LDS, and every staging wave adds them up in the
+            // same order.
+            float ssr[MR];
 #pragma unroll
-        for (int ti = 0; ti < kColMaxTasks; ++ti) {
-            const int t = sw + S * ti;
-            if (t >= ntask) break;                 // uniform across the wave
-            const int m = t % MR, b = t / MR;
-            const bool in_k = b * 64 + lane < kw;  // a chunk lies wholly inside or outside K
-            stage_word_col<PRO>(ga[ti], ua[ti], in_k && m < a.M, in_k, (lane & 3) == 0,
-                                act_s + size_t(m) * 4 * qs + lofs + b * 128,
-                                eb_s + m * a.nch + b * 16 + (lane >> 2));
+            for (int m = 0; m < MR; ++m) ssr[m] = 0.f;
+#pragma unroll
+            for (int ti = 0; ti < TMAX; ++ti) {
+                const int t = sw + S * ti;
+                if (t >= ntask) break;             // uniform
+                const int m = t % MR, b = t / MR;
+                const bool in_k = b * 64 + lane < kw;
+                const bool live = in_k && m < a.M;
+                const uint32_t xw[4] = {ga[ti].x, ga[ti].y, ga[ti].z, ga[ti].w};
+                const uint32_t rw[4] = {ua[ti].x, ua[ti].y, ua[ti].z, ua[ti].w};
+                uint32_t hw[4];
+                float ss = 0.f;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    hw[h] = pack_bf16x2(bf16_lo(xw[h]) + bf16_lo(rw[h]), bf16_hi(xw[h]) + bf16_hi(rw[h]));
+                    const float lo = bf16_lo(hw[h]), hi = bf16_hi(hw[h]);
+                    ss = fmaf(lo, lo, ss);
+                    ss = fmaf(hi, hi, ss);
+                }
+                ga[ti] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+#pragma unroll
+                for (int mm = 0; mm < MR; ++mm) ssr[mm] += (mm == m && live) ? ss : 0.f;
+                if (blockIdx.x == 0 && live)
+                    *reinterpret_cast<uint4*>(a.h_out + size_t(m) * a.K + (b * 64 + lane) * 8) = ga[ti];
+            }
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float tot = wave_sum_uniform(ssr[m]);
+                if (lane == 0) ss_s[sw * MR + m] = tot;
+            }
+            __syncthreads();                       // row sums of squares in LDS
+            float rstd[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                float tot = 0.f;
+                for (int w = 0; w < S; ++w) tot += ss_s[w * MR + m];
+                rstd[m] = __builtin_amdgcn_rsqf(fmaf(tot, 1.0f / float(a.K), a.eps));
+            }
+#pragma unroll
+            for (int ti = 0; ti < TMAX; ++ti) {
+                const int t = sw + S * ti;
+                if (t >= ntask) break;             // uniform
+                const int m = t % MR, b = t / MR;
+                const bool in_k = b * 64 + lane < kw;
+                float rs = rstd[0];
+#pragma unroll
+                for (int mm = 1; mm < MR; ++mm) rs = mm == m ? rstd[mm] : rs;
+                const uint32_t hw[4] = {ga[ti].x, ga[ti].y, ga[ti].z, ga[ti].w};
+                const uint32_t ww[4] = {wa[ti].x, wa[ti].y, wa[ti].z, wa[ti].w};
+                float v[8];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    v[2 * h] = bf16_lo(hw[h]) * rs * bf16_lo(ww[h]);
+                    v[2 * h + 1] = bf16_hi(hw[h]) * rs * bf16_hi(ww[h]);
+                }
+                stage_values_col(v, in_k && m < a.M, in_k, (lane & 3) == 0,
+                                 act_s + size_t(m) * 4 * qs + lofs + b * 128,
+                                 eb_s + m * a.nch + b * 16 + (lane >> 2));
+            }
+        } else {
+#pragma unroll
+            for (int ti = 0; ti < TMAX; ++ti) {
+                const int t = sw + S * ti;
+                if (t >= ntask) break;             // uniform across the wave
+                const int m = t % MR, b = t / MR;
+                const bool in_k = b * 64 + lane < kw;  // a chunk lies wholly inside or outside K
+                stage_word_col<PRO>(ga[ti], ua[ti], in_k && m < a.M, in_k, (lane & 3) == 0,
+                                    act_s + size_t(m) * 4 * qs + lofs + b * 128,
+                                    eb_s + m * a.nch + b * 16 + (lane >> 2));
+            }
         }
 #pragma unroll
         for (int r = 0; r < kColScLoads; ++r) {
             if (r * nst >= nsc) break;
             const int idx = stid + r * nst;
             if (idx < nsc) {
-                const int g = idx / npc, cc0 = (p0 + idx % npc) * 8 - col0;
+                const bool hi = idx >= nsc0;
+                const int j = hi ? idx - nsc0 : idx, npc = hi ? npc1 : npc0;
+                const int g = j / npc;
+                const int cc0 = ((hi ? p01 : p00) + j % npc) * 8 - (hi ? cb1 : cb0), o = hi ? n0 : 0;
                 const uint32_t wd[4] = {sraw[r].x, sraw[r].y, sraw[r].z, sraw[r].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int cc = cc0 + e;
-                    if (cc >= 0 && cc < C) sc_s[g * C + cc] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+                    if (cc >= 0 && cc < n0) sc_s[g * C + o + cc] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
                 }
             }
         }
@@ -291,11 +406,18 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     const int wave_all = wave;
     {
     const int wave = wave_all - S;
-    // lane l < MR*CPW finishes output (row l / CPW, column col0 + wave + W * (l % CPW))
-    const int em = lane / CPW, ecc = wave + W * (lane % CPW), en = col0 + ecc;
-    const bool owner = lane < MR * CPW && em < a.M && ecc < C && en < a.N;
+    // The wave's slots j = 0..CPW-1.  Plain: slot j is column slot wave + W j.  PAIR:
+    // slots 2p and 2p+1 are the gate and up columns of pair wave + W p.
+    auto slot_unit = [&](int j) { return wave + W * (PAIR ? (j >> 1) : j); };
+    auto slot_ok = [&](int j) { return slot_unit(j) < (PAIR ? a.pairs : C); };
+    auto slot_cj = [&](int j) { return PAIR && (j & 1) ? a.pairs + slot_unit(j) : slot_unit(j); };
+    // output of lane l < MR * OPW: row l / OPW, unit (column or pair) wave + W * (l % OPW)
+    constexpr int OPW = PAIR ? CPW / 2 : CPW;
+    const int ldy = PAIR ? a.half_n : a.N;
+    const int em = lane / OPW, eu = wave + W * (lane % OPW), en = cbase + eu;
+    const bool owner = lane < MR * OPW && em < a.M && eu < (PAIR ? a.pairs : C) && en < ldy;
     const uint16_t* rsrc = a.residual ? a.residual : a.y;   // y: a readable stand-in, value unused
-    const uint16_t rraw = rsrc[size_t(min(em, a.M - 1)) * a.N + min(en, a.N - 1)];
+    const uint16_t rraw = rsrc[size_t(min(em, a.M - 1)) * ldy + min(en, ldy - 1)];
     const float os = a.out_scale ? *a.out_scale : 1.0f;
     // weight chunks: lane l takes chunks l, l+64, ... of each of the wave's columns (a
     // slot the wave does not own re-reads its first column: the loads stay unconditional,
@@ -303,11 +425,12 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     uint4 wv[NI][CPW];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-        const int cj = wave + W * j < C ? wave + W * j : wave;
-        const uint4* colp = a.qw + size_t(min(col0 + cj, a.N - 1)) * a.nch;
+        const int cj = slot_ok(j) ? slot_cj(j) : slot_cj(0);
+        const uint4* colp = a.qw + size_t(min(column(cj), a.N - 1)) * a.nch;
 #pragma unroll
         for (int i = 0; i < NI; ++i) wv[i][j] = colp[min(lane + kWave * i, a.nch - 1)];
     }
+    if (PAIR) __syncthreads();                     // the staging waves' row sums
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -332,8 +455,8 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
             }
 #pragma unroll
             for (int j = 0; j < CPW; ++j) {
-                if (wave + W * j >= C) break;      // uniform
-                const float s = sc_s[(c >> 2) * C + wave + W * j];
+                if (!slot_ok(j)) break;            // uniform
+                const float s = sc_s[(c >> 2) * C + slot_cj(j)];
                 const uint32_t wd[4] = {wv[i][j].x, wv[i][j].y, wv[i][j].z, wv[i][j].w};
                 Q4x2 q[4];
 #pragma unroll
@@ -355,27 +478,45 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     }
 
     // ---- reduce each column over the wave; the owning lane applies the epilogue ----
-    float mine = 0.f;
+    float tot[MR][CPW];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-        if (wave + W * j >= C) break;              // uniform
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
+            tot[m][j] = 0.f;
+            if (!slot_ok(j)) continue;             // uniform
             float v = acc[m][j];
             v += dpp<kQuadSwap1>(v);
             v += dpp<kQuadSwap2>(v);
             v += dpp<kRowRor4>(v);
             v += dpp<kRowRor8>(v);                 // every lane holds its row-of-16 sum
             const int b = __builtin_bit_cast(int, v);
-            v = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
-                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
-                (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
-                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
-            mine = lane == m * CPW + j ? v : mine;
+            tot[m][j] = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+                        (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
         }
     }
-    const float res = a.residual ? bf16_to_f32(rraw) : 0.f;
-    if (owner) a.y[size_t(em) * a.N + en] = f32_to_bf16(fmaf(mine, os, res));
+    float mine = 0.f;
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int o = 0; o < OPW; ++o) {
+            // PAIR: silu(gate) * up of the pair's fp32 sums, rounded once
+            const float v = PAIR ? silu_f32(tot[m][2 * o]) * tot[m][2 * o + 1] : tot[m][o];
+            mine = lane == m * OPW + o ? v : mine;
+        }
+    if (PAIR) {
+        if (owner) a.y[size_t(em) * ldy + en] = f32_to_bf16(mine);
+    } else {
+        const float res = a.residual ? bf16_to_f32(rraw) : 0.f;
+        if (owner) a.y[size_t(em) * ldy + en] = f32_to_bf16(fmaf(mine, os, res));
+    }
+    // ---- side copy (the fused layer's residual update), spread over the grid ----
+    if (a.cp_n16 > 0) {
+        const int nt = W * kWave;
+        for (int i = blockIdx.x * nt + (tid - S * kWave); i < a.cp_n16; i += gridDim.x * nt) a.cp_dst[i] = a.cp_src[i];
+    }
     }
 }
 
@@ -654,6 +795,36 @@ hipError_t launch_col(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStre
     }
 }
 
+// Pair mode (add + RMSNorm prologue, SwiGLU pair epilogue): even slot counts only.
+template <int MR, int CPW, int NI>
+hipError_t launch_pair3(const ColArgs& a, const GemvPlan& p, hipStream_t s) {
+    return launch(w4_gemv_col_kernel<MR, CPW, NI, kAddRmsNorm>, dim3(p.wgs), (p.stagers + p.waves) * kWave,
+                  p.lds_bytes, s, a);
+}
+
+template <int MR>
+hipError_t launch_pair(const ColArgs& a, const GemvPlan& p, hipStream_t s) {
+    switch (p.cpw) {
+        case 8: return launch_pair3<MR, 8, 1>(a, p, s);
+        case 6: return launch_pair3<MR, 6, 1>(a, p, s);
+        case 4:
+            switch (p.ni) {
+                case 1: return launch_pair3<MR, 4, 1>(a, p, s);
+                case 2: return launch_pair3<MR, 4, 2>(a, p, s);
+                default: return launch_pair3<MR, 4, 3>(a, p, s);
+            }
+        default:
+            switch (p.ni) {
+                case 1: return launch_pair3<MR, 2, 1>(a, p, s);
+                case 2: return launch_pair3<MR, 2, 2>(a, p, s);
+                case 3: return launch_pair3<MR, 2, 3>(a, p, s);
+                case 4: return launch_pair3<MR, 2, 4>(a, p, s);
+                case 5: return launch_pair3<MR, 2, 5>(a, p, s);
+                default: return launch_pair3<MR, 2, 6>(a, p, s);
+            }
+    }
+}
+
 template <int MR, int GW>
 hipError_t launch_split2(Prologue pro, const SplitArgs& a, const GemvPlan& p, hipStream_t s) {
     const dim3 grid(p.tiles * p.splits);
@@ -759,6 +930,42 @@ bool plan_column(int M, int K, int N, GemvPlan& p) {
     if (p.groups * pieces > kColScLoads * p.stagers * kWave) return false;   // staging waves' scale capacity
     p.wgs = (N + C - 1) / C;
     p.lds_bytes = size_t(p.mr) * 4 * (nch * 8 + 32) * 2 + size_t(p.mr) * nch * 8 + size_t(p.groups) * C * 4;
+    if (p.lds_bytes > kMaxLds) return false;
+    p.kind = kColumnOwning;
+    return true;
+}
+
+// The fused layer's gate_up: column kernel in pair mode over K = H, N = 2I.  The
+// workgroup owns about I / 256 pairs (so every CU gets one workgroup), with slots
+// (two per pair) spread over 8..16 - stagers dot waves.
+bool plan_column_pair(int M, int K, int I, GemvPlan& p) {
+    p = GemvPlan{};
+    p.groups = K / kGroup;
+    if (M > 4 || K > 32 * kColMaxChunks * kWave || I < 1) return false;
+    const int nch = K / 32;
+    const int nblk = (K + 511) / 512;
+    p.mr = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+    p.ni = (nch + kWave - 1) / kWave;
+    if (p.ni > 6) return false;
+    const int ntask = p.mr * nblk;
+    if (ntask > 8 * kColMaxTasksNorm) return false;
+    p.stagers = std::min(8, std::max(2, ntask));
+    if (p.stagers * kColMaxTasksNorm < ntask) return false;
+    const int cmax = col_cpw_max(p.ni, p.mr) & ~1;            // slots per wave, even
+    if (cmax < 2) return false;
+    const int ppw = cmax / 2;                                  // pairs per wave, at most
+    const int pwant = std::max(1, (I + 255) / 256);
+    p.waves = 8;
+    if (pwant > 8 * ppw) p.waves = std::min(16 - p.stagers, (pwant + ppw - 1) / ppw);
+    const int pairs = std::min(pwant, p.waves * ppw);
+    p.cpw = 2 * ((pairs + p.waves - 1) / p.waves);
+    if (p.cpw > cmax) return false;
+    p.cols = 2 * pairs;
+    const int pieces = 2 * ((pairs + 7) / 8 + 1);
+    if (p.groups * pieces > kColScLoads * p.stagers * kWave) return false;
+    p.wgs = (I + pairs - 1) / pairs;
+    p.lds_bytes = size_t(p.mr) * 4 * (nch * 8 + 32) * 2 + size_t(p.mr) * nch * 8 + size_t(p.groups) * p.cols * 4 +
+                  size_t(p.stagers) * p.mr * 4;
     if (p.lds_bytes > kMaxLds) return false;
     p.kind = kColumnOwning;
     return true;
@@ -922,6 +1129,79 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
     const int64_t threads = std::max<int64_t>(n16, ntail);
     fill_zero_kernel<<<dim3((threads + 255) / 256), 256, 0, s>>>(static_cast<uint4*>(p), n16, tail, ntail);
     return hipGetLastError();
+}
+
+bool norm_gemv_swiglu_supported(int M, int K, int I) {
+    GemvPlan p;
+    return plan_column_pair(M, K, I, p);
+}
+
+hipError_t launch_norm_gemv_swiglu(const uint16_t* x, const uint16_t* r, const uint16_t* nw, float eps,
+                                   const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
+                                   uint16_t* h_out, uint16_t* act, hipStream_t s) {
+    GemvPlan p;
+    if (!plan_column_pair(M, K, I, p)) return hipErrorInvalidValue;
+    ColArgs a{};
+    a.a0 = x;
+    a.a1 = r;
+    a.lda = K;
+    a.qw = reinterpret_cast<const uint4*>(qw);
+    a.sc = sc;
+    a.M = M;
+    a.K = K;
+    a.N = 2 * I;
+    a.nch = K / 32;
+    a.groups = p.groups;
+    a.cols = p.cols;
+    a.stagers = p.stagers;
+    a.y = act;
+    a.nw = nw;
+    a.eps = eps;
+    a.h_out = h_out;
+    a.pairs = p.cols / 2;
+    a.half_n = I;
+    switch (p.mr) {
+        case 1: return launch_pair<1>(a, p, s);
+        case 2: return launch_pair<2>(a, p, s);
+        default: return launch_pair<4>(a, p, s);
+    }
+}
+
+bool gemv_column_supported(int M, int K, int N) {
+    GemvPlan p{};
+    p.groups = K / kGroup;
+    return plan_column(M, K, N, p);
+}
+
+hipError_t launch_gemv_copy(Prologue pro, const uint16_t* a0, int64_t lda, const uint32_t* qw, const uint16_t* sc,
+                            int M, int K, int N, const float* out_scale, const uint16_t* residual, uint16_t* y,
+                            const void* cp_src, void* cp_dst, size_t cp_bytes, hipStream_t s) {
+    GemvPlan p{};
+    p.groups = K / kGroup;
+    if (pro != kIdentity || !plan_column(M, K, N, p) || cp_bytes % 16) return hipErrorInvalidValue;
+    ColArgs a{};
+    a.a0 = a0;
+    a.lda = lda;
+    a.qw = reinterpret_cast<const uint4*>(qw);
+    a.sc = sc;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.nch = K / 32;
+    a.groups = p.groups;
+    a.cols = p.cols;
+    a.stagers = p.stagers;
+    a.out_scale = out_scale;
+    a.residual = residual;
+    a.y = y;
+    a.cp_src = static_cast<const uint4*>(cp_src);
+    a.cp_dst = static_cast<uint4*>(cp_dst);
+    a.cp_n16 = int(cp_bytes / 16);
+    switch (p.mr) {
+        case 1: return launch_col<1>(kIdentity, a, p, s);
+        case 2: return launch_col<2>(kIdentity, a, p, s);
+        default: return launch_col<4>(kIdentity, a, p, s);
+    }
 }
 
 }  // namespace fdec

@@ -63,6 +63,17 @@ def mlp_layer_bytes(M: int, H: int, I: int, residual_in_epilogue: bool) -> int:
             + swiglu_w4_gemv_bytes(M, I, H, residual=residual_in_epilogue))
 
 
+def mlp2_layer_bytes(M: int, H: int, I: int, residual_in_epilogue: bool) -> int:
+    """The two-kernel layer.  Kernel 1: x, residual and the norm weight in, gate_up
+    weights, h and act out.  Kernel 2: act in, down weights, out out (+ h in for the
+    residual add), the fp32 scalar, and the residual update (h in, residual out)."""
+    k1 = 2 * M * H * BF16 + H * BF16 + w4_weight_bytes(H, 2 * I) + M * H * BF16 + M * I * BF16
+    k2 = M * I * BF16 + w4_weight_bytes(I, H) + M * H * BF16 + F32 + 2 * M * H * BF16
+    if residual_in_epilogue:
+        k2 += M * H * BF16
+    return k1 + k2
+
+
 def product_bytes(M: int, K: int, N: int) -> int:
     """The fp32 (M, K, N) broadcast product the unfused single-row path materialises."""
     return M * K * N * F32

@@ -53,6 +53,7 @@ __all__ = [
     "mlp_chain", "product_form_gemv", "factored_form_gemv",
     "product_buffer_bytes", "unfused_act_gemv", "unfused_product_gemv",
     "add_rmsnorm_eager", "mlp_decode_unfused",
+    "add_rmsnorm_gemv_swiglu", "mlp_decode2", "mlp_chain2",
 ]
 
 GROUP = 128   # weights per scale group along K (one scale per group per column)
@@ -249,6 +250,54 @@ def mlp_chain(x0, r0, layers, *, keep=False):
         d = mlp_decode(x, r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
                        L.down.qweight, L.down.scales, L.out_scale, L.eps,
                        residual_in_epilogue=False)
+        if keep:
+            trace.append(d)
+        x, r = d["out"], d["h"]
+    return (x, r, trace) if keep else (x, r)
+
+
+# ----------------------------------------------------------------------------
+# the two-kernel layer ([P4] section 5, "the fusion boundary problem": the gate_up GEMM
+# with a silu * up epilogue writing act; here the add + RMSNorm also runs as that GEMM's
+# prologue, so y_norm and the gate/up pair are never written)
+# ----------------------------------------------------------------------------
+def add_rmsnorm_gemv_swiglu(x, r, norm_w, gu_q, gu_s, eps=1e-6, *, n_chunk=4096):
+    """(h, act): h = bf16(x + r); y = h * w / sqrt(mean_H(h^2) + eps) (not rounded);
+    [g, u] = y @ dequant(W_gate_up) (not rounded); act = bf16(silu(g) * u).
+
+    h and act are the only tensors this step writes, so they are the only roundings.
+    """
+    hs = round_bf16(bf16_to_f64(x) + bf16_to_f64(r))
+    H = hs.shape[-1]
+    ms = np.sum(hs * hs, axis=-1, keepdims=True) / H
+    y = hs * bf16_to_f64(norm_w) / np.sqrt(ms + float(eps))
+    gu = _chunked_gemv(y, gu_q, gu_s, n_chunk)
+    I = gu.shape[1] // 2
+    act = silu_mul(gu[:, :I], gu[:, I:])
+    return f64_to_bf16(hs), f64_to_bf16(act)
+
+
+def mlp_decode2(x, r, norm_w, gu_q, gu_s, d_q, d_s, out_scale=0.5, eps=1e-6,
+                residual_in_epilogue=True, *, n_chunk=4096):
+    """The layer of ``mlp_decode`` as two kernels' worth of work:
+
+    1. (h, act) = add_rmsnorm_gemv_swiglu(x, r, norm_w, W_gate_up)
+    2. out = bf16(out_scale * act @ dequant(W_down) [+ h])
+    """
+    h, act = add_rmsnorm_gemv_swiglu(x, r, norm_w, gu_q, gu_s, eps, n_chunk=n_chunk)
+    acc = _chunked_gemv(bf16_to_f64(act), d_q, d_s, n_chunk)
+    out = f64_to_bf16(_epilogue(acc, out_scale, h if residual_in_epilogue else None))
+    return {"h": h, "act": act, "out": out}
+
+
+def mlp_chain2(x0, r0, layers, *, keep=False):
+    """``mlp_chain`` built from the two-kernel layer (residual add deferred)."""
+    x, r = x0, r0
+    trace = []
+    for L in layers:
+        d = mlp_decode2(x, r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
+                        L.down.qweight, L.down.scales, L.out_scale, L.eps,
+                        residual_in_epilogue=False)
         if keep:
             trace.append(d)
         x, r = d["out"], d["h"]

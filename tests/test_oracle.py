@@ -409,6 +409,90 @@ def test_mlp_chain_defers_residual():
 
 
 # ----------------------------------------------------------------------------
+# the two-kernel layer (norm as the gate_up prologue, SwiGLU as its epilogue)
+# ----------------------------------------------------------------------------
+def _py_layer2(x, r, nw, guq, gus, dq, ds, s, eps, residual_in_epilogue):
+    """Pure-Python loops: y and gate/up are not rounded (never written), act is."""
+    M, H = x.shape
+    I = guq.shape[0] // 2
+
+    def wq(qw, sc, k, n):
+        code = (int(qw[n, k // 8]) >> (4 * (k % 8))) & 0xF
+        return (code - 16 if code >= 8 else code) * bf16_bits_to_float(sc[k // 128, n])
+
+    outs = {"h": [], "act": [], "out": []}
+    for m in range(M):
+        h = [_py_round(bf16_bits_to_float(x[m, j]) + bf16_bits_to_float(r[m, j])) for j in range(H)]
+        inv = 1.0 / math.sqrt(sum(v * v for v in h) / H + eps)
+        y = [h[j] * inv * bf16_bits_to_float(nw[j]) for j in range(H)]
+        g = [sum(y[k] * wq(guq, gus, k, n) for k in range(H)) for n in range(I)]
+        u = [sum(y[k] * wq(guq, gus, k, I + n) for k in range(H)) for n in range(I)]
+        act = [_py_round(g[n] / (1.0 + math.exp(-g[n])) * u[n]) for n in range(I)]
+        out = []
+        for n in range(H):
+            v = s * sum(act[k] * wq(dq, ds, k, n) for k in range(I))
+            out.append(_py_round(v + (h[n] if residual_in_epilogue else 0.0)))
+        outs["h"].append(h); outs["act"].append(act); outs["out"].append(out)
+    return {k: np.array(v) for k, v in outs.items()}
+
+
+@pytest.mark.parametrize("resid", [True, False])
+def test_mlp_layer2_matches_brute_force(resid):
+    inp = synth.mlp_inputs(2, 128, 128, n_layers=1, seed=17, out_scale=0.5)
+    L = inp.layers[0]
+    d = O.mlp_decode2(inp.x, inp.r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
+                      L.down.qweight, L.down.scales, L.out_scale, L.eps, residual_in_epilogue=resid)
+    ref = _py_layer2(inp.x, inp.r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
+                     L.down.qweight, L.down.scales, L.out_scale, L.eps, resid)
+    for k in ("h", "act", "out"):
+        ours = O.bf16_to_f64(d[k])
+        mism = ours != ref[k]
+        assert mism.mean() < 0.02, k
+        assert np.all(np.abs(ours - ref[k])[mism] <= np.abs(ref[k][mism]) * 2.0**-7), k
+
+
+def test_layer2_gate_up_is_norm_invariant_to_input_scale():
+    # RMSNorm with eps = 0 divides out any common factor of the row: doubling x and r
+    # (exact in bf16) doubles h and leaves y, and so act, bit-identical.
+    inp = synth.mlp_inputs(2, 256, 128, n_layers=1, seed=18)
+    L = inp.layers[0]
+    x2 = O.f64_to_bf16(2.0 * O.bf16_to_f64(inp.x))
+    r2 = O.f64_to_bf16(2.0 * O.bf16_to_f64(inp.r))
+    h1, a1 = O.add_rmsnorm_gemv_swiglu(inp.x, inp.r, L.norm_w, L.gate_up.qweight, L.gate_up.scales, 0.0)
+    h2, a2 = O.add_rmsnorm_gemv_swiglu(x2, r2, L.norm_w, L.gate_up.qweight, L.gate_up.scales, 0.0)
+    assert np.array_equal(O.bf16_to_f64(h2), 2.0 * O.bf16_to_f64(h1))
+    assert np.array_equal(a1, a2)
+
+
+def test_layer2_h_equals_add_rmsnorm_h_and_act_close_to_three_kernel_form():
+    inp = synth.mlp_inputs(4, 512, 256, n_layers=1, seed=19)
+    L = inp.layers[0]
+    d3 = O.mlp_decode(inp.x, inp.r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
+                      L.down.qweight, L.down.scales, 0.5, 1e-6)
+    d2 = O.mlp_decode2(inp.x, inp.r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
+                       L.down.qweight, L.down.scales, 0.5, 1e-6)
+    assert np.array_equal(d2["h"], d3["h"])
+    I = 256
+    act3 = O.silu_mul(O.bf16_to_f64(d3["gu"][:, :I]), O.bf16_to_f64(d3["gu"][:, I:]))
+    a2 = O.bf16_to_f64(d2["act"])
+    # the three-kernel form rounds y and gate/up to bf16; the two-kernel form does not
+    assert np.max(np.abs(a2 - act3)) <= 0.05 * np.max(np.abs(act3))
+    o2, o3 = O.bf16_to_f64(d2["out"]), O.bf16_to_f64(d3["out"])
+    assert np.max(np.abs(o2 - o3)) <= 0.05 * np.max(np.abs(o3))
+
+
+def test_mlp_chain2_defers_residual():
+    inp = synth.mlp_inputs(1, 128, 128, n_layers=2, seed=20)
+    x2, r2, tr = O.mlp_chain2(inp.x, inp.r, inp.layers, keep=True)
+    L0, L1 = inp.layers
+    d0 = O.mlp_decode2(inp.x, inp.r, L0.norm_w, L0.gate_up.qweight, L0.gate_up.scales,
+                       L0.down.qweight, L0.down.scales, 0.5, 1e-6, residual_in_epilogue=False)
+    h1, _ = O.add_rmsnorm(d0["out"], d0["h"], L1.norm_w, 1e-6)
+    assert np.array_equal(r2, h1)
+    assert np.array_equal(tr[0]["out"], d0["out"])
+
+
+# ----------------------------------------------------------------------------
 # the unfused references
 # ----------------------------------------------------------------------------
 def test_unfused_act_matches_torch_eager_silu_mul():

@@ -60,3 +60,7 @@ def test_config_byte_totals():
     assert T.mlp_layer_bytes(16, 4096, 14336, True) == 93_593_604
     assert T.mlp_layer_bytes(1, 1536, 8960, False) == 21_382_148
     assert 28 * T.mlp_layer_bytes(1, 1536, 8960, False) == 598_700_144
+    # two-kernel layer, by hand: kernel 1 = x, r (6,144) + norm weight (3,072) + gate_up
+    # (13,762,560 + 430,080) + h (3,072) + act (17,920); kernel 2 = act (17,920) + down
+    # (6,881,280 + 215,040) + out (3,072) + scale (4) + h -> residual (6,144)
+    assert T.mlp2_layer_bytes(1, 1536, 8960, False) == 14_222_848 + 7_123_460
