@@ -227,6 +227,28 @@ FDEC_API int fdec_mlp_graph_create(const fdec_mlp_layer* layers, int32_t n_layer
                                    fdec_bf16* y_norm, fdec_bf16* gate_up, void* ws,
                                    size_t ws_bytes, fdec_stream stream, fdec_graph* out);
 FDEC_API int fdec_graph_launch(fdec_graph graph, fdec_stream stream);
+
+/*
+ * fdec_mlp_graph_update: re-points a graph made by fdec_mlp_graph_create at other
+ * layers (weights, scales, norm weights, out_scale pointers, residual flags) and other
+ * buffers (x, residual, y_norm, gate_up, ws), without a new instantiation.  [P5]
+ * section "In the real world" describes this for llama.cpp: changed kernel parameters
+ * are patched into the graph instead of capturing it again.  The chain is captured on
+ * `stream` (not the null stream; nothing runs) and its kernel arguments are written
+ * into the existing executable graph with hipGraphExecUpdate.
+ *   Same argument checks as fdec_mlp_graph_create.  The update must keep the graph's
+ *   launch shapes: the same form (three-kernel layers), n_layers, M, H and I, else
+ *   FDEC_ERR_UNSUPPORTED and the graph is unchanged.  If HIP refuses the update, the
+ *   call returns FDEC_ERR_UNSUPPORTED and the handle keeps replaying what it replayed
+ *   before.  No launch of the graph may be pending when it is called (synchronise the
+ *   stream it was launched on first).  The old buffers may be freed once it returns
+ *   FDEC_OK.
+ * fdec_mlp_graph_update2: the same for a graph made by fdec_mlp_graph_create2.
+ */
+FDEC_API int fdec_mlp_graph_update(fdec_graph graph, const fdec_mlp_layer* layers, int32_t n_layers,
+                                   int32_t M, fdec_bf16* x, fdec_bf16* residual,
+                                   fdec_bf16* y_norm, fdec_bf16* gate_up, void* ws,
+                                   size_t ws_bytes, fdec_stream stream);
 FDEC_API int fdec_graph_kernel_count(fdec_graph graph);
 FDEC_API int fdec_graph_destroy(fdec_graph graph);
 
@@ -273,6 +295,10 @@ FDEC_API int fdec_mlp_graph_create2(const fdec_mlp_layer* layers, int32_t n_laye
                                     int32_t M, fdec_bf16* x, fdec_bf16* residual,
                                     fdec_bf16* act, void* ws, size_t ws_bytes,
                                     fdec_stream stream, fdec_graph* out);
+FDEC_API int fdec_mlp_graph_update2(fdec_graph graph, const fdec_mlp_layer* layers,
+                                    int32_t n_layers, int32_t M, fdec_bf16* x,
+                                    fdec_bf16* residual, fdec_bf16* act, void* ws,
+                                    size_t ws_bytes, fdec_stream stream);
 
 /*
  * The unfused sequences the fused kernels replace, kept for comparison.

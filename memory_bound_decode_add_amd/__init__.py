@@ -79,6 +79,10 @@ _SIGS = {
     "fdec_mlp_chain2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "fdec_mlp_graph_create2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _sz,
                                               _c_p, ctypes.POINTER(_c_p)]),
+    "fdec_mlp_graph_update": (ctypes.c_int, [_c_p, ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p,
+                                             _c_p, _sz, _c_p]),
+    "fdec_mlp_graph_update2": (ctypes.c_int, [_c_p, ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p,
+                                              _sz, _c_p]),
     "fdec_graph_launch": (ctypes.c_int, [_c_p, _c_p]),
     "fdec_graph_kernel_count": (ctypes.c_int, [_c_p]),
     "fdec_graph_destroy": (ctypes.c_int, [_c_p]),
@@ -406,6 +410,20 @@ class MlpGraph:
                                            bufs.y_norm.data_ptr(), bufs.gate_up.data_ptr(), self.ws.data_ptr(),
                                            self.ws.numel(), cap.cuda_stream, ctypes.byref(self._handle)))
 
+    def update(self, layers, bufs: MlpBuffers, ws=None, stream: torch.cuda.Stream | None = None):
+        """Point the graph at other layers and buffers of the same shapes, without a new
+        instantiation (fdec_mlp_graph_update).  Waits for pending work on the device first."""
+        M = _check_bufs(layers[0], bufs)
+        ws = _ws(ws, mlp_workspace_bytes(M, layers[0].H, layers[0].I), bufs.x.device)
+        torch.cuda.synchronize(bufs.x.device)
+        cap = stream if stream is not None else torch.cuda.Stream(device=bufs.x.device)
+        layers = list(layers)
+        arr = _layer_array(layers)
+        _check(lib().fdec_mlp_graph_update(self._handle, arr, len(layers), M, bufs.x.data_ptr(),
+                                           bufs.residual.data_ptr(), bufs.y_norm.data_ptr(), bufs.gate_up.data_ptr(),
+                                           ws.data_ptr(), ws.numel(), cap.cuda_stream))
+        self.layers, self.bufs, self.ws = layers, bufs, ws
+
     @property
     def kernel_count(self) -> int:
         return int(lib().fdec_graph_kernel_count(self._handle))
@@ -510,6 +528,20 @@ class Mlp2Graph(MlpGraph):
         _check(lib().fdec_mlp_graph_create2(arr, len(self.layers), M, bufs.x.data_ptr(), bufs.residual.data_ptr(),
                                             bufs.act.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
                                             cap.cuda_stream, ctypes.byref(self._handle)))
+
+    def update(self, layers, bufs: Mlp2Buffers, ws=None, stream: torch.cuda.Stream | None = None):
+        """Point the graph at other layers and buffers of the same shapes, without a new
+        instantiation (fdec_mlp_graph_update2).  Waits for pending work on the device first."""
+        M = _check_bufs2(layers[0], bufs)
+        ws = _ws(ws, mlp2_workspace_bytes(M, layers[0].H, layers[0].I), bufs.x.device)
+        torch.cuda.synchronize(bufs.x.device)
+        cap = stream if stream is not None else torch.cuda.Stream(device=bufs.x.device)
+        layers = list(layers)
+        arr = _layer_array(layers)
+        _check(lib().fdec_mlp_graph_update2(self._handle, arr, len(layers), M, bufs.x.data_ptr(),
+                                            bufs.residual.data_ptr(), bufs.act.data_ptr(), ws.data_ptr(), ws.numel(),
+                                            cap.cuda_stream))
+        self.layers, self.bufs, self.ws = layers, bufs, ws
 
 
 def unfused_swiglu_w4_gemv(mode, g, u, W: W4Weight, out_scale=None, residual=None, out=None, ws=None):

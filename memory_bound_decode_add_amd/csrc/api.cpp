@@ -297,10 +297,100 @@ hipError_t enqueue_eager_norm(const fdec_bf16* x, const fdec_bf16* r, const fdec
 }  // namespace
 
 struct fdec_graph_s {
-    hipGraph_t graph = nullptr;
+    hipGraph_t graph = nullptr;       // the captured graph the executable was made from
     hipGraphExec_t exec = nullptr;
     int kernels = 0;
+    int form = 0;                     // 1: three-kernel layers, 2: two-kernel layers
+    int n_layers = 0, M = 0, H = 0, I = 0;
 };
+
+namespace {
+
+// Captures the chain of the given form on s into *out; nothing runs.  Form 1 uses
+// y_norm and gate_up, form 2 uses act.
+hipError_t capture_chain(int form, const fdec_mlp_layer* layers, int n_layers, int M, LayerDims d, fdec_bf16* x,
+                         fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* act, void* ws,
+                         hipStream_t s, hipGraph_t* out) {
+    *out = nullptr;
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return e;
+    hipError_t le = hipSuccess;
+    for (int l = 0; l < n_layers && le == hipSuccess; ++l)
+        le = form == 1 ? enqueue_layer(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, s)
+                       : enqueue_layer2(&layers[l], M, d, x, residual, act, x, ws, s);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(s, &g);
+    if (le != hipSuccess || e != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return le != hipSuccess ? le : e;
+    }
+    *out = g;
+    return hipSuccess;
+}
+
+int make_graph(int form, const fdec_mlp_layer* layers, int n_layers, int M, LayerDims d, fdec_bf16* x,
+               fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* act, void* ws, hipStream_t s,
+               fdec_graph* out) {
+    fdec_graph_s* G = new (std::nothrow) fdec_graph_s;
+    if (!G) return fail(FDEC_ERR_ARG, "out of host memory");
+    hipError_t e = capture_chain(form, layers, n_layers, M, d, x, residual, y_norm, gate_up, act, ws, s, &G->graph);
+    if (e != hipSuccess) {
+        delete G;
+        return hip_status(e, "graph capture");
+    }
+    size_t nodes = 0;
+    if (hipGraphGetNodes(G->graph, nullptr, &nodes) != hipSuccess) nodes = 0;
+    G->kernels = int(nodes);
+    e = hipGraphInstantiate(&G->exec, G->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(G->graph);
+        delete G;
+        return hip_status(e, "hipGraphInstantiate");
+    }
+    G->form = form;
+    G->n_layers = n_layers;
+    G->M = M;
+    G->H = d.H;
+    G->I = d.I;
+    *out = G;
+    return ok();
+}
+
+// Re-captures the chain with new layers and buffers and writes the new kernel
+// arguments into the existing executable graph (hipGraphExecUpdate): the launch
+// shapes are those of the graph, so no re-instantiation is needed.
+int update_graph(fdec_graph G, int form, const fdec_mlp_layer* layers, int n_layers, int M, LayerDims d,
+                 fdec_bf16* x, fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* act, void* ws,
+                 hipStream_t s) {
+    if (G->form != form || G->n_layers != n_layers || G->M != M || G->H != d.H || G->I != d.I)
+        return fail(FDEC_ERR_UNSUPPORTED,
+                    "an update keeps the graph's form and shapes (form %d, %d layers, M = %d, H = %d, I = %d); "
+                    "got form %d, %d layers, M = %d, H = %d, I = %d",
+                    G->form, G->n_layers, G->M, G->H, G->I, form, n_layers, M, d.H, d.I);
+    hipGraph_t ng = nullptr;
+    hipError_t e = capture_chain(form, layers, n_layers, M, d, x, residual, y_norm, gate_up, act, ws, s, &ng);
+    if (e != hipSuccess) return hip_status(e, "graph capture");
+    hipGraphNode_t err_node = nullptr;
+    hipGraphExecUpdateResult res = hipGraphExecUpdateSuccess;
+    e = hipGraphExecUpdate(G->exec, ng, &err_node, &res);
+    if (e != hipSuccess || res != hipGraphExecUpdateSuccess) {
+        (void)hipGetLastError();
+        // keep the handle on the graph it had: a fresh executable from the kept graph
+        hipGraphExec_t fresh = nullptr;
+        if (hipGraphInstantiate(&fresh, G->graph, nullptr, nullptr, 0) == hipSuccess) {
+            (void)hipGraphExecDestroy(G->exec);
+            G->exec = fresh;
+        }
+        (void)hipGraphDestroy(ng);
+        return fail(FDEC_ERR_UNSUPPORTED, "hipGraphExecUpdate refused the update (%s, result %d)",
+                    hipGetErrorString(e), int(res));
+    }
+    (void)hipGraphDestroy(G->graph);
+    G->graph = ng;
+    return ok();
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -434,34 +524,26 @@ FDEC_API int fdec_mlp_graph_create(const fdec_mlp_layer* layers, int32_t n_layer
             FDEC_OK)
             return st;
     if (g_fail_launches) return injected();
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    fdec_graph_s* G = new (std::nothrow) fdec_graph_s;
-    if (!G) return fail(FDEC_ERR_ARG, "out of host memory");
-    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
-    if (e != hipSuccess) {
-        delete G;
-        return hip_status(e, "hipStreamBeginCapture");
-    }
-    hipError_t le = hipSuccess;
-    for (int l = 0; l < n_layers && le == hipSuccess; ++l)
-        le = enqueue_layer(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, s);
-    e = hipStreamEndCapture(s, &G->graph);
-    if (le != hipSuccess || e != hipSuccess) {
-        if (G->graph) (void)hipGraphDestroy(G->graph);
-        delete G;
-        return hip_status(le != hipSuccess ? le : e, "graph capture");
-    }
-    size_t nodes = 0;
-    if (hipGraphGetNodes(G->graph, nullptr, &nodes) != hipSuccess) nodes = 0;
-    G->kernels = int(nodes);
-    e = hipGraphInstantiate(&G->exec, G->graph, nullptr, nullptr, 0);
-    if (e != hipSuccess) {
-        (void)hipGraphDestroy(G->graph);
-        delete G;
-        return hip_status(e, "hipGraphInstantiate");
-    }
-    *out = G;
-    return ok();
+    return make_graph(1, layers, n_layers, M, d, x, residual, y_norm, gate_up, nullptr, ws,
+                      static_cast<hipStream_t>(stream), out);
+}
+
+FDEC_API int fdec_mlp_graph_update(fdec_graph graph, const fdec_mlp_layer* layers, int32_t n_layers, int32_t M,
+                                   fdec_bf16* x, fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up,
+                                   void* ws, size_t ws_bytes, fdec_stream stream) {
+    if (!graph || !graph->exec) return fail(FDEC_ERR_NULL, "graph is NULL");
+    if (!stream) return fail(FDEC_ERR_ARG, "graph capture needs a non-null stream");
+    LayerDims d;
+    int st = check_chain(layers, n_layers, M, &d);
+    if (st != FDEC_OK) return st;
+    const size_t need = mlp_ws(M, d.H, d.I);
+    for (int l = 0; l < n_layers; ++l)
+        if ((st = check_layer_buffers(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, ws_bytes, need)) !=
+            FDEC_OK)
+            return st;
+    if (g_fail_launches) return injected();
+    return update_graph(graph, 1, layers, n_layers, M, d, x, residual, y_norm, gate_up, nullptr, ws,
+                        static_cast<hipStream_t>(stream));
 }
 
 FDEC_API int fdec_graph_launch(fdec_graph graph, fdec_stream stream) {
@@ -555,33 +637,25 @@ FDEC_API int fdec_mlp_graph_create2(const fdec_mlp_layer* layers, int32_t n_laye
             FDEC_OK)
             return st;
     if (g_fail_launches) return injected();
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    fdec_graph_s* G = new (std::nothrow) fdec_graph_s;
-    if (!G) return fail(FDEC_ERR_ARG, "out of host memory");
-    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
-    if (e != hipSuccess) {
-        delete G;
-        return hip_status(e, "hipStreamBeginCapture");
-    }
-    hipError_t le = hipSuccess;
-    for (int l = 0; l < n_layers && le == hipSuccess; ++l) le = enqueue_layer2(&layers[l], M, d, x, residual, act, x, ws, s);
-    e = hipStreamEndCapture(s, &G->graph);
-    if (le != hipSuccess || e != hipSuccess) {
-        if (G->graph) (void)hipGraphDestroy(G->graph);
-        delete G;
-        return hip_status(le != hipSuccess ? le : e, "graph capture");
-    }
-    size_t nodes = 0;
-    if (hipGraphGetNodes(G->graph, nullptr, &nodes) != hipSuccess) nodes = 0;
-    G->kernels = int(nodes);
-    e = hipGraphInstantiate(&G->exec, G->graph, nullptr, nullptr, 0);
-    if (e != hipSuccess) {
-        (void)hipGraphDestroy(G->graph);
-        delete G;
-        return hip_status(e, "hipGraphInstantiate");
-    }
-    *out = G;
-    return ok();
+    return make_graph(2, layers, n_layers, M, d, x, residual, nullptr, nullptr, act, ws,
+                      static_cast<hipStream_t>(stream), out);
+}
+
+FDEC_API int fdec_mlp_graph_update2(fdec_graph graph, const fdec_mlp_layer* layers, int32_t n_layers, int32_t M,
+                                    fdec_bf16* x, fdec_bf16* residual, fdec_bf16* act, void* ws, size_t ws_bytes,
+                                    fdec_stream stream) {
+    if (!graph || !graph->exec) return fail(FDEC_ERR_NULL, "graph is NULL");
+    if (!stream) return fail(FDEC_ERR_ARG, "graph capture needs a non-null stream");
+    LayerDims d;
+    int st = check_chain2(layers, n_layers, M, &d);
+    if (st != FDEC_OK) return st;
+    for (int l = 0; l < n_layers; ++l)
+        if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, mlp2_ws(M, d.H))) !=
+            FDEC_OK)
+            return st;
+    if (g_fail_launches) return injected();
+    return update_graph(graph, 2, layers, n_layers, M, d, x, residual, nullptr, nullptr, act, ws,
+                        static_cast<hipStream_t>(stream));
 }
 
 FDEC_API size_t fdec_unfused_gemv_workspace_bytes(int32_t mode, int32_t M, int32_t K, int32_t N) {

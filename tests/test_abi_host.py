@@ -229,6 +229,9 @@ def test_layer_validation(L, inject):
                                    ctypes.byref(g)) == ARG      # null stream cannot be captured
     assert L.fdec_mlp_graph_create(arr, 0, M, f(), f(), f(), f(), f(max(16, need)), need, f(),
                                    ctypes.byref(g)) == SHAPE
+    # graph updates check the handle first
+    assert L.fdec_mlp_graph_update(None, arr, 2, M, f(), f(), f(), f(), f(max(16, need)), need, f()) == NULL
+    assert L.fdec_mlp_graph_update2(None, arr, 2, M, f(), f(), f(), f(max(16, need)), need, f()) == NULL
 
 
 def test_hooks_validation(L, inject):
