@@ -221,6 +221,25 @@ def bench_extras(torch, F, synth, n_sets_gemv):
         out[f"unfused_{name}_1x9216x2560"] = {"us_per_call": t * 1e6, "gbps_actual_bytes": ab / t / 1e9,
                                               "workspace_bytes": F.unfused_gemv_workspace_bytes(mode, Mg, K, N)}
         del wsu
+
+    # batch sweep at the metric's K and N: the same 48 rotating weight sets, M rows of
+    # seeded N(0,1) activations, one graph per batch size; M <= 4 runs the column kernel,
+    # 5 <= M <= 16 the matrix-core kernel
+    log("[bench] batch sweep M=1..16 at K=9216 N=2560")
+    gen = torch.Generator().manual_seed(1234)
+    sweep = {}
+    for Mb in (1, 2, 3, 4, 5, 8, 12, 16):
+        gb = torch.randn(Mb, K, generator=gen).to(torch.bfloat16).cuda()
+        ub = torch.randn(Mb, K, generator=gen).to(torch.bfloat16).cuda()
+        ys = [torch.empty((Mb, N), dtype=torch.bfloat16, device="cuda") for _ in gsets]
+        wsb = F.workspace(F.gemv_workspace_bytes(Mb, K, N))
+        fns = [lambda s=s, y=y: F.swiglu_w4_gemv(gb, ub, s[2], scale, out=y, ws=wsb) for s, y in zip(gsets, ys)]
+        t = bench_repeat(torch, timer, fns, 5) / len(gsets)
+        b = T.swiglu_w4_gemv_bytes(Mb, K, N)
+        sweep[f"M{Mb}"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS,
+                           "kernel": "column" if Mb <= 4 else "matrix-core"}
+        del gb, ub, ys, wsb
+    out["batch_sweep_swiglu_w4_gemv_9216x2560"] = sweep
     del gsets
 
     # Llama-3-8B-sized MLP layer at M=16, 6 rotating weight sets
@@ -301,6 +320,31 @@ def bench_extras(torch, F, synth, n_sets_gemv):
                                           "kernels_per_step": graph2.kernel_count, "bytes_per_step": b2,
                                           "graph_gbps": b2 / tg2 / 1e9,
                                           "graph_frac_of_peak": b2 / tg2 / 1e9 / PEAK_GBPS}
+
+    # re-pointing the captured graph at a second set of buffers (same shapes): the
+    # in-place parameter update against a fresh capture + instantiation, host time
+    bufs2b = F.Mlp2Buffers.empty(M, H, I, out_is_x=True)
+    ws2b = F.workspace(F.mlp2_workspace_bytes(M, H, I))
+    cap = torch.cuda.Stream()
+    t_upd, t_new = [], []
+    for i in range(6):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph2.update(layers, bufs2b if i % 2 == 0 else bufs2, ws2b if i % 2 == 0 else ws2, stream=cap)
+        t_upd.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        gfresh = F.Mlp2Graph(layers, bufs2b, ws2b, stream=cap)
+        t_new.append(time.perf_counter() - t0)
+        gfresh.close()
+    bufs2.x.copy_(x0)
+    bufs2.residual.copy_(r0)
+    graph2.launch()
+    torch.cuda.synchronize()
+    tg2u = timer(graph2.launch, 20) / 20
+    out["mlp2_chain_qwen2_5_1_5b_28l"].update({
+        "graph_update_ms_median": float(np.median(t_upd)) * 1e3,
+        "graph_create_ms_median": float(np.median(t_new)) * 1e3,
+        "graph_us_per_step_after_update": tg2u * 1e6})
     graph2.close()
     return out
 
