@@ -42,6 +42,11 @@ Readings where the pages are silent (each is also listed in the design notes):
   rounding of h * w / sqrt(ms + eps).
 * Multi-layer chain: each layer's add_rmsnorm adds the previous layer's down output
   into the residual (the residual add deferred to the next layer's norm).
+* FP4 weights ([P3]'s packed FP4 with E4M3 1x16 block scales and an fp32 output
+  multiplier) are read as weight-only quantisation: the activation stays the unrounded
+  SwiGLU prologue value.  E2M1 codes are packed like the int4 nibbles (code of k = 8*kb
+  + j in bits [4j, 4j+4) of word (n, kb)); block scales are E4M3 ('fn': no infinities)
+  bytes [K/16, N], scale (b, n) applying to k in [16 b, 16 b + 16).
 """
 from __future__ import annotations
 
@@ -54,6 +59,7 @@ __all__ = [
     "product_buffer_bytes", "unfused_act_gemv", "unfused_product_gemv",
     "add_rmsnorm_eager", "mlp_decode_unfused",
     "add_rmsnorm_gemv_swiglu", "mlp_decode2", "mlp_chain2",
+    "FP4_BLOCK", "e2m1_decode", "e4m3_decode", "fp4_unpack", "fp4_dequant", "swiglu_fp4_gemv", "fp4_gemv",
 ]
 
 GROUP = 128   # weights per scale group along K (one scale per group per column)
@@ -382,3 +388,86 @@ def mlp_decode_unfused(x, r, norm_w, gu_q, gu_s, d_q, d_s, out_scale=0.5, eps=1e
     if residual_in_epilogue:
         o = round_bf16(o + bf16_to_f64(h))
     return {"h": h, "y": y, "gu": gu_b, "out": f64_to_bf16(o)}
+
+
+# ----------------------------------------------------------------------------
+# FP4 weights with E4M3 block scales ([P3]: packed FP4 inputs with E4M3 1x16 block
+# scales and a zero-dimensional fp32 output multiplier folded into the GEMM)
+# ----------------------------------------------------------------------------
+FP4_BLOCK = 16    # weights per E4M3 block scale along K
+
+# E2M1: one sign bit, two exponent bits, one mantissa bit.  The magnitudes of codes
+# 0..7 (sign bit clear), in code order: exponent field 0 holds zero and the single
+# subnormal 0.5; fields 1..3 hold 1, 1.5, 2, 3, 4, 6.
+_E2M1_MAGNITUDE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 codes 0..15 -> float64; bit 3 is the sign (code 8 is -0)."""
+    c = np.asarray(codes).astype(np.int64)
+    mag = _E2M1_MAGNITUDE[c & 7]
+    return np.where((c & 8) != 0, -mag, mag)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 byte codes -> float64.  Sign bit 7, exponent bits 6..3 (bias 7), mantissa
+    bits 2..0.  Exponent field 0: subnormal m/8 * 2**-6.  No infinities: exponent 15
+    with mantissa 7 is NaN, every other code is finite (largest 448)."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where((c & 0x80) != 0, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((e == 15) & (c & 7 == 7), np.nan, val)
+    return sign * val
+
+
+def fp4_unpack(qweight) -> np.ndarray:
+    """Packed words uint32 [N, K/8] -> E2M1 codes uint8 [K, N] (code of k = 8*kb + j in
+    bits [4j, 4j+4) of word (n, kb))."""
+    w = np.asarray(qweight, dtype=np.uint32)
+    n, kb = w.shape
+    out = np.empty((kb, NIB, n), dtype=np.uint8)
+    for j in range(NIB):
+        out[:, j, :] = ((w >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8).T
+    return out.reshape(kb * NIB, n)
+
+
+def fp4_dequant(qweight, scales) -> np.ndarray:
+    """Dequantised weights, float64 [K, N]: w[k, n] = e2m1(code[k, n]) * e4m3(s[k // 16, n]).
+
+    An E2M1 value has 2 significant bits and an E4M3 value 4, so the product is exact in
+    fp32 (and in fp16 up to the range) on the GPU."""
+    v = e2m1_decode(fp4_unpack(qweight))
+    s = e4m3_decode(scales)
+    K = v.shape[0]
+    if s.shape[0] * FP4_BLOCK != K or s.shape[1] != v.shape[1]:
+        raise ValueError("scales must be [K/16, N]")
+    return v * np.repeat(s, FP4_BLOCK, axis=0)
+
+
+def _chunked_fp4_gemv(a, qweight, scales, n_chunk=2048):
+    """a [M, K] float64 times fp4_dequant(W) [K, N], N in chunks (bounded memory)."""
+    N = qweight.shape[0]
+    sc = np.asarray(scales)
+    out = np.empty((a.shape[0], N), dtype=np.float64)
+    for n0 in range(0, N, n_chunk):
+        n1 = min(N, n0 + n_chunk)
+        out[:, n0:n1] = a @ fp4_dequant(qweight[n0:n1], sc[:, n0:n1])
+    return out
+
+
+def swiglu_fp4_gemv(g, u, qweight, scales, out_scale=1.0, residual=None, *, return_f64=False):
+    """y[m, n] = bf16(out_scale * sum_k silu(g[m,k]) u[m,k] w[k,n] (+ residual[m, n]))
+    with FP4 weights w = e2m1 * e4m3 block scale ([P3]); the activation is unrounded."""
+    act = silu_mul(bf16_to_f64(g), bf16_to_f64(u))
+    acc = _chunked_fp4_gemv(act, qweight, scales)
+    y = _epilogue(acc, out_scale, residual)
+    return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)
+
+
+def fp4_gemv(x, qweight, scales, out_scale=None, residual=None, *, return_f64=False):
+    """The same GEMV with the identity prologue: y = bf16([out_scale *] x @ W (+ residual))."""
+    acc = _chunked_fp4_gemv(bf16_to_f64(x), qweight, scales)
+    y = _epilogue(acc, out_scale, residual)
+    return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)

@@ -137,6 +137,63 @@ def swiglu_gemv_inputs(M: int, K: int, N: int, seed: int = 0, out_scale: float =
     return GemvInputs(g, u, W, float(out_scale), res)
 
 
+# ----------------------------------------------------------------------------
+# FP4 weights with E4M3 block scales
+# ----------------------------------------------------------------------------
+FP4_BLOCK = 16       # FP4 weights per E4M3 block scale along K
+
+
+def f32_to_e4m3_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> E4M3 ('fn': no infinities) byte codes via PyTorch's RNE conversion."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+@dataclass
+class FP4:
+    qweight: np.ndarray   # uint32 [N, K/8]: eight E2M1 codes per word, code j in bits [4j, 4j+4)
+    scales: np.ndarray    # uint8 (E4M3 codes) [K/16, N]
+
+    @property
+    def K(self):
+        return self.qweight.shape[1] * PACK
+
+    @property
+    def N(self):
+        return self.qweight.shape[0]
+
+
+def fp4_weight(rng, K, N) -> FP4:
+    """One FP4 matrix: words uniform over all 2**32 patterns (every E2M1 code, -0
+    included, equally likely), then block scales drawn from U[0.005, 0.02) and rounded
+    to E4M3, from the same generator."""
+    if K % 32 or N <= 0:
+        raise ValueError("K must be a multiple of 32")
+    q = _qweight(rng, K, N)
+    sc = f32_to_e4m3_bits(rng.uniform(SCALE_LO, SCALE_HI, size=(K // FP4_BLOCK, N)).astype(np.float32))
+    return FP4(q, sc)
+
+
+@dataclass
+class Fp4GemvInputs:
+    g: np.ndarray          # bf16 bits [M, K]
+    u: np.ndarray          # bf16 bits [M, K]
+    W: FP4
+    out_scale: float
+    residual: np.ndarray | None = None   # bf16 bits [M, N]
+
+
+def swiglu_fp4_gemv_inputs(M: int, K: int, N: int, seed: int = 0, out_scale: float = 1.0,
+                           with_residual: bool = False) -> Fp4GemvInputs:
+    """Children in order: g, u, weights (words then block scales), residual."""
+    rg, ru, rw, rr = _children(seed, 4)
+    g = _normal_bf16(rg, (M, K))
+    u = _normal_bf16(ru, (M, K))
+    W = fp4_weight(rw, K, N)
+    res = _normal_bf16(rr, (M, N)) if with_residual else None
+    return Fp4GemvInputs(g, u, W, float(out_scale), res)
+
+
 @dataclass
 class NormInputs:
     x: np.ndarray          # bf16 bits [M, H]
