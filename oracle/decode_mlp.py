@@ -434,16 +434,16 @@ def fp4_unpack(qweight) -> np.ndarray:
 
 
 def fp4_dequant(qweight, scales) -> np.ndarray:
-    """Dequantised weights, float64 [K, N]: w[k, n] = e2m1(code[k, n]) * e4m3(s[k // 16, n]).
+    """Dequantised weights, float64 [K, N]: w[k, n] = e2m1(code[k, n]) * e4m3(s[n, k // 16]).
 
     An E2M1 value has 2 significant bits and an E4M3 value 4, so the product is exact in
     fp32 (and in fp16 up to the range) on the GPU."""
     v = e2m1_decode(fp4_unpack(qweight))
     s = e4m3_decode(scales)
     K = v.shape[0]
-    if s.shape[0] * FP4_BLOCK != K or s.shape[1] != v.shape[1]:
-        raise ValueError("scales must be [K/16, N]")
-    return v * np.repeat(s, FP4_BLOCK, axis=0)
+    if s.shape[1] * FP4_BLOCK != K or s.shape[0] != v.shape[1]:
+        raise ValueError("scales must be [N, K/16]")
+    return v * np.repeat(s.T, FP4_BLOCK, axis=0)
 
 
 def _chunked_fp4_gemv(a, qweight, scales, n_chunk=2048):
@@ -453,7 +453,7 @@ def _chunked_fp4_gemv(a, qweight, scales, n_chunk=2048):
     out = np.empty((a.shape[0], N), dtype=np.float64)
     for n0 in range(0, N, n_chunk):
         n1 = min(N, n0 + n_chunk)
-        out[:, n0:n1] = a @ fp4_dequant(qweight[n0:n1], sc[:, n0:n1])
+        out[:, n0:n1] = a @ fp4_dequant(qweight[n0:n1], sc[n0:n1])
     return out
 
 

@@ -152,7 +152,7 @@ def f32_to_e4m3_bits(a: np.ndarray) -> np.ndarray:
 @dataclass
 class FP4:
     qweight: np.ndarray   # uint32 [N, K/8]: eight E2M1 codes per word, code j in bits [4j, 4j+4)
-    scales: np.ndarray    # uint8 (E4M3 codes) [K/16, N]
+    scales: np.ndarray    # uint8 (E4M3 codes) [N, K/16]: the scales of a column are contiguous
 
     @property
     def K(self):
@@ -170,7 +170,7 @@ def fp4_weight(rng, K, N) -> FP4:
     if K % 32 or N <= 0:
         raise ValueError("K must be a multiple of 32")
     q = _qweight(rng, K, N)
-    sc = f32_to_e4m3_bits(rng.uniform(SCALE_LO, SCALE_HI, size=(K // FP4_BLOCK, N)).astype(np.float32))
+    sc = f32_to_e4m3_bits(rng.uniform(SCALE_LO, SCALE_HI, size=(N, K // FP4_BLOCK)).astype(np.float32))
     return FP4(q, sc)
 
 

@@ -58,9 +58,9 @@ def test_fp4_dequant_block_layout():
     K, N = 64, 3
     codes = np.full((K, N), 2)                       # E2M1 code 2 = 1.0
     words = synth.pack_int4(codes)
-    sc = np.zeros((K // 16, N), dtype=np.uint8)
+    sc = np.zeros((N, K // 16), dtype=np.uint8)
     for b in range(K // 16):
-        sc[b] = 0x38 + b                             # E4M3 1.0, 1.125, 1.25, 1.375
+        sc[:, b] = 0x38 + b                          # E4M3 1.0, 1.125, 1.25, 1.375
     w = O.fp4_dequant(words, sc)
     for k in range(K):
         assert np.all(w[k] == 1.0 + (k // 16) / 8)
@@ -77,7 +77,7 @@ def brute_fp4(g, u, words, sc, out_scale, residual=None):
             acc = 0.0
             for k in range(K):
                 code = (int(words[n, k // 8]) >> (4 * (k % 8))) & 0xF
-                sb = int(sc[k // 16, n])
+                sb = int(sc[n, k // 16])
                 e, mm = (sb >> 3) & 0xF, sb & 7
                 s = (mm / 8 * 2.0 ** -6 if e == 0 else (1 + mm / 8) * 2.0 ** (e - 7)) * (-1 if sb & 0x80 else 1)
                 a = gf[m, k] / (1 + math.exp(-gf[m, k])) * uf[m, k]
@@ -107,7 +107,7 @@ def test_fp4_gemv_exact_rational():
     for n in range(N):
         exact = Fraction(0)
         for k in range(K):
-            s = Fraction(float(O.e4m3_decode(W.scales[k // 16, n])))
+            s = Fraction(float(O.e4m3_decode(W.scales[n, k // 16])))
             exact += Fraction(float(O.bf16_to_f64(x[0, k]))) * Fraction(e2m1_from_fields(int(codes[k, n]))) * s
         assert Fraction(float(got[0, n])) == exact / 2
 
