@@ -301,6 +301,40 @@ FDEC_API int fdec_mlp_graph_update2(fdec_graph graph, const fdec_mlp_layer* laye
                                     size_t ws_bytes, fdec_stream stream);
 
 /*
+ * FP4 weights: [P3] ("PyTorch folds NVFP4 output scaling into NVGEMM candidates for
+ * decode workloads") restricts its fold to packed FP4 inputs with E4M3 1x16 block scales
+ * and a zero-dimensional fp32 multiplier.  Read here as weight-only quantisation behind
+ * the same SwiGLU (or identity) prologue: the activation stays the unrounded prologue
+ * value, as on the int4 path.
+ *   qweight: uint32 [N][K/8]; the E2M1 code of weight k = 8 kb + j of column n sits in
+ *            bits [4j, 4j+4) of word (n, kb): bit 3 sign, bits 2..1 exponent (bias 1),
+ *            bit 0 mantissa; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives.
+ *   scales:  E4M3 ('fn', no infinities) bytes [N][K/16]; byte (n, b) scales k in
+ *            [16 b, 16 b + 16) of column n.  NaN scales are outside the contract.
+ *   K % 32 == 0, N % 8 == 0; both arrays 16-byte aligned.
+ *
+ * fdec_swiglu_fp4_gemv: y[m, n] = bf16(s * sum_k silu(g[m,k]) u[m,k] w[k,n] (+ residual)),
+ *   w = e2m1 * e4m3 block scale; arguments, aliasing and errors as fdec_swiglu_w4_gemv,
+ *   without a workspace.  Implemented for M <= 4 and K <= 16384 (FDEC_ERR_UNSUPPORTED
+ *   otherwise, FDEC_ERR_SHAPE outside [1, 16]).
+ * fdec_fp4_gemv: the identity prologue, y = bf16(s * x @ w (+ residual)); x [M][K].
+ * fdec_fp4_dequant: test hook; writes w as fp32 [K][N] (exact).
+ */
+typedef struct {
+    const uint32_t* qweight;
+    const uint8_t* scales;
+    int32_t K, N;
+} fdec_fp4;
+FDEC_API int fdec_swiglu_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu,
+                                  const fdec_fp4* W, const float* out_scale,
+                                  const fdec_bf16* residual, int32_t M, fdec_bf16* y,
+                                  fdec_stream stream);
+FDEC_API int fdec_fp4_gemv(const fdec_bf16* x, const fdec_fp4* W, const float* out_scale,
+                           const fdec_bf16* residual, int32_t M, fdec_bf16* y,
+                           fdec_stream stream);
+FDEC_API int fdec_fp4_dequant(const fdec_fp4* W, float* w_out, fdec_stream stream);
+
+/*
  * The unfused sequences the fused kernels replace, kept for comparison.
  *
  * FDEC_UNFUSED_PRODUCT ([P1], the materialised broadcast product; M == 1 only,

@@ -49,6 +49,10 @@ class CW4(ctypes.Structure):
     _fields_ = [("qweight", _c_p), ("scales", _c_p), ("K", _i32), ("N", _i32)]
 
 
+class CFP4(ctypes.Structure):
+    _fields_ = [("qweight", _c_p), ("scales", _c_p), ("K", _i32), ("N", _i32)]
+
+
 class CLayer(ctypes.Structure):
     _fields_ = [("norm_weight", _c_p), ("eps", ctypes.c_float), ("gate_up", CW4), ("down", CW4),
                 ("out_scale", _c_p), ("residual_in_epilogue", _i32)]
@@ -97,6 +101,10 @@ _SIGS = {
                                                _sz, _c_p]),
     "fdec_w4_unpack": (ctypes.c_int, [ctypes.POINTER(CW4), _c_p, _c_p]),
     "fdec_w4_dequant": (ctypes.c_int, [ctypes.POINTER(CW4), _c_p, _c_p]),
+    "fdec_swiglu_fp4_gemv": (ctypes.c_int, [_c_p, _c_p, _i64, ctypes.POINTER(CFP4), _c_p, _c_p, _i32, _c_p,
+                                            _c_p]),
+    "fdec_fp4_gemv": (ctypes.c_int, [_c_p, ctypes.POINTER(CFP4), _c_p, _c_p, _i32, _c_p, _c_p]),
+    "fdec_fp4_dequant": (ctypes.c_int, [ctypes.POINTER(CFP4), _c_p, _c_p]),
     "fdec_set_gemv_split": (None, [_i32]),
     "fdec_set_gemv_tiling": (None, [_i32, _i32]),
     "fdec_test_fail_launches": (None, [_i32]),
@@ -597,6 +605,81 @@ def w4_dequant(W: W4Weight) -> torch.Tensor:
     w = torch.empty((W.K, W.N), dtype=torch.float32, device=W.qweight.device)
     cw = W.c()
     _check(lib().fdec_w4_dequant(ctypes.byref(cw), w.data_ptr(), _stream(w.device)))
+    return w
+
+
+# ---------------------------------------------------------------------------
+# FP4 (E2M1) weights with E4M3 1x16 block scales
+# ---------------------------------------------------------------------------
+@dataclass
+class FP4Weight:
+    qweight: torch.Tensor   # int32 [N, K/8] (uint32 words of eight E2M1 codes)
+    scales: torch.Tensor    # uint8 [N, K/16] (E4M3 codes)
+
+    def __post_init__(self):
+        _need(self.qweight, "qweight", torch.int32)
+        _need(self.scales, "scales", torch.uint8)
+        n, kb = self.qweight.shape
+        if tuple(self.scales.shape) != (n, kb * 8 // 16):
+            raise ValueError("scales must be [N, K/16]")
+
+    @property
+    def K(self):
+        return self.qweight.shape[1] * 8
+
+    @property
+    def N(self):
+        return self.qweight.shape[0]
+
+    def c(self) -> CFP4:
+        return CFP4(self.qweight.data_ptr(), self.scales.data_ptr(), self.K, self.N)
+
+    @classmethod
+    def from_numpy(cls, qweight: np.ndarray, scales: np.ndarray, device="cuda"):
+        return cls(words_to_tensor(qweight, device),
+                   torch.from_numpy(np.ascontiguousarray(scales, dtype=np.uint8)).to(device))
+
+
+def swiglu_fp4_gemv(g, u, W: FP4Weight, out_scale=None, residual=None, out=None):
+    """y = bf16(s * (silu(g) * u) @ W (+ residual)) with FP4 weights; g, u are [M, K] views."""
+    M = g.shape[0]
+    ld = _rows(g, "g", M, W.K)
+    ldu = _rows(u, "u", M, W.K)
+    if M > 1 and ldu != ld:
+        raise ValueError("g and u must share a row stride")
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=g.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    cw = W.c()
+    _check(lib().fdec_swiglu_fp4_gemv(g.data_ptr(), u.data_ptr(), ld, ctypes.byref(cw), _ptr(out_scale),
+                                      _ptr(residual), M, y.data_ptr(), _stream(g.device)))
+    return y
+
+
+def fp4_gemv(x, W: FP4Weight, out_scale=None, residual=None, out=None):
+    """y = bf16(s * x @ W (+ residual)) with FP4 weights (identity prologue)."""
+    _need(x, "x", torch.bfloat16)
+    M = x.shape[0]
+    _need(x, "x", torch.bfloat16, shape=(M, W.K))
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    cw = W.c()
+    _check(lib().fdec_fp4_gemv(x.data_ptr(), ctypes.byref(cw), _ptr(out_scale), _ptr(residual), M, y.data_ptr(),
+                               _stream(x.device)))
+    return y
+
+
+def fp4_dequant(W: FP4Weight) -> torch.Tensor:
+    w = torch.empty((W.K, W.N), dtype=torch.float32, device=W.qweight.device)
+    cw = W.c()
+    _check(lib().fdec_fp4_dequant(ctypes.byref(cw), w.data_ptr(), _stream(w.device)))
     return w
 
 

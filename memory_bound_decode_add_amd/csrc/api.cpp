@@ -126,6 +126,40 @@ int check_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_
 
 int injected() { return fail(FDEC_ERR_HIP, "launch failure injected by fdec_test_fail_launches"); }
 
+// ---- FP4 weights ----
+int check_fp4(const fdec_fp4* W) {
+    if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
+    if (!W->qweight || !W->scales) return fail(FDEC_ERR_NULL, "W.qweight or W.scales is NULL");
+    if (W->K <= 0 || W->K % 32) return fail(FDEC_ERR_SHAPE, "W.K = %d must be a positive multiple of 32", W->K);
+    if (W->N <= 0 || W->N % 8) return fail(FDEC_ERR_SHAPE, "W.N = %d must be a positive multiple of 8", W->N);
+    if (!aligned16(W->qweight) || !aligned16(W->scales)) return fail(FDEC_ERR_ALIGN, "W arrays must be 16-byte aligned");
+    return FDEC_OK;
+}
+Span fp4_qspan(const fdec_fp4* W) { return {W->qweight, size_t(W->K) / 8 * W->N * 4}; }
+Span fp4_sspan(const fdec_fp4* W) { return {W->scales, size_t(W->K) / 16 * W->N}; }
+
+int check_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_fp4* W, const float* out_scale,
+                   const fdec_bf16* residual, int M, const fdec_bf16* y, bool swiglu) {
+    int st;
+    if ((st = check_fp4(W)) != FDEC_OK) return st;
+    if ((st = check_m(M)) != FDEC_OK) return st;
+    if (!g || (swiglu && !u) || !y) return fail(FDEC_ERR_NULL, "activation input and y are required");
+    if (ldgu < W->K || ldgu % 8) return fail(FDEC_ERR_SHAPE, "ld = %lld must be >= K and a multiple of 8", (long long)ldgu);
+    if (!aligned16(g) || (u && !aligned16(u)) || !aligned16(y) || (residual && !aligned16(residual)))
+        return fail(FDEC_ERR_ALIGN, "activation, residual and y must be 16-byte aligned");
+    if (out_scale && !aligned4(out_scale)) return fail(FDEC_ERR_ALIGN, "out_scale must be 4-byte aligned");
+    const size_t in_bytes = (size_t(M - 1) * ldgu + W->K) * 2;
+    const Span Y{y, size_t(M) * W->N * 2};
+    const Span ins[] = {{g, in_bytes}, {u, in_bytes}, fp4_qspan(W), fp4_sspan(W), {out_scale, 4}};
+    for (const Span& sp : ins)
+        if (overlap(Y, sp)) return fail(FDEC_ERR_ALIAS, "y overlaps an input");
+    if (residual && overlap(Y, Span{residual, Y.bytes}) && residual != y)
+        return fail(FDEC_ERR_ALIAS, "y may only alias residual exactly");
+    if (!fp4_gemv_supported(M, W->K, W->N))
+        return fail(FDEC_ERR_UNSUPPORTED, "the FP4 GEMV takes M <= 4 and K <= 16384 (M = %d, K = %d)", M, W->K);
+    return FDEC_OK;
+}
+
 // ---- the layer ----
 struct LayerDims {
     int H, I;
@@ -741,6 +775,40 @@ FDEC_API int fdec_unfused_mlp_decode(const fdec_mlp_layer* layer, int32_t M, con
         e = enqueue_unfused_act(gate_up, gate_up + d.I, 2 * int64_t(d.I), &layer->down, layer->out_scale,
                                 layer->residual_in_epilogue ? residual : nullptr, M, out, act_ws, s);
     return hip_status(e, "unfused layer launch");
+}
+
+FDEC_API int fdec_swiglu_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_fp4* W,
+                                  const float* out_scale, const fdec_bf16* residual, int32_t M, fdec_bf16* y,
+                                  fdec_stream stream) {
+    const int st = check_fp4_gemv(g, u, ldgu, W, out_scale, residual, M, y, true);
+    if (st != FDEC_OK) return st;
+    if (g_fail_launches) return injected();
+    return hip_status(launch_fp4_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual,
+                                      y, static_cast<hipStream_t>(stream)),
+                      "fp4 gemv launch");
+}
+
+FDEC_API int fdec_fp4_gemv(const fdec_bf16* x, const fdec_fp4* W, const float* out_scale, const fdec_bf16* residual,
+                           int32_t M, fdec_bf16* y, fdec_stream stream) {
+    if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
+    const int st = check_fp4_gemv(x, nullptr, W->K, W, out_scale, residual, M, y, false);
+    if (st != FDEC_OK) return st;
+    if (g_fail_launches) return injected();
+    return hip_status(launch_fp4_gemv(kIdentity, x, nullptr, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale,
+                                      residual, y, static_cast<hipStream_t>(stream)),
+                      "fp4 gemv launch");
+}
+
+FDEC_API int fdec_fp4_dequant(const fdec_fp4* W, float* w_out, fdec_stream stream) {
+    int st = check_fp4(W);
+    if (st != FDEC_OK) return st;
+    if (!w_out) return fail(FDEC_ERR_NULL, "w_out is NULL");
+    if (!aligned4(w_out)) return fail(FDEC_ERR_ALIGN, "w_out must be 4-byte aligned");
+    const Span O{w_out, size_t(W->K) * W->N * 4};
+    if (overlap(O, fp4_qspan(W)) || overlap(O, fp4_sspan(W))) return fail(FDEC_ERR_ALIAS, "w_out overlaps W");
+    if (g_fail_launches) return injected();
+    return hip_status(launch_fp4_dequant(W->qweight, W->scales, W->K, W->N, w_out, static_cast<hipStream_t>(stream)),
+                      "fp4 dequant launch");
 }
 
 FDEC_API int fdec_w4_unpack(const fdec_w4* W, int8_t* q_out, fdec_stream stream) {

@@ -1,0 +1,332 @@
+// FP4 (E2M1) weight GEMV with E4M3 block scales of 16 along K, a SwiGLU (or identity)
+// prologue and an fp32 output-scale + residual epilogue, M = 1..4, gfx950.
+//
+// What it computes ("PyTorch folds NVFP4 output scaling into NVGEMM candidates for
+// decode workloads": packed FP4 weights with E4M3 1x16 block scales and a
+// zero-dimensional fp32 output multiplier applied inside the GEMM):
+//     y[m, n] = bf16( s * sum_k act[m, k] * e2m1(q[k, n]) * e4m3(scale[n, k/16])  (+ res[m, n]) )
+// with act = silu(g) * u or act = x.  The activation exists only in registers.
+//
+// Weights: qweight uint32 [N][K/8], E2M1 code of k = 8 kb + j in bits [4j, 4j+4) of word
+// (n, kb); scales E4M3 bytes [N][K/16], so the two scales of a 32-wide chunk of a column
+// are one 16-bit word.
+//
+// Work assignment.  A workgroup owns C = 2 CH consecutive columns and has ceil(K/1024)
+// waves; wave w covers the 32-wide K chunks 32 w .. 32 w + 31.  Lane (h = lane / 32, cl =
+// lane % 32) owns chunk c = 32 w + cl and columns h CH .. h CH + CH - 1 of the workgroup:
+//  * it loads half of the chunk's activation inputs (k = 32 c + 16 h .. + 15), forms
+//    those 16 activation values in fp32, and the two lanes of the chunk (l, l ^ 32)
+//    exchange their halves as block-scaled fp16: one power of two per chunk puts the
+//    chunk's largest magnitude in [2^14, 2^15), so every value fits fp16 with an 11-bit
+//    significand relative to it.  Each activation value is computed once per workgroup.
+//  * for each of its CH columns it loads the chunk's 16 bytes of weights (a half-wave
+//    reads 512 contiguous bytes of one column) and the chunk's two block scales.  gfx950's
+//    v_cvt_scalef32_pk_f16_fp4 turns a byte of two E2M1 codes into two exact fp16 values;
+//    it is run with scale 1, because it applies only the exponent of its fp32 scale
+//    operand (the power-of-two scales of the MX formats; measured: an E4M3 scale's
+//    mantissa is dropped).  Eight v_dot2_f32_f16 sum each 16-wide block in fp32, and the
+//    two block sums are multiplied by their E4M3 scales.
+// A column's 32-lane sums are reduced with DPP and lane reads, the per-wave results meet
+// in LDS, and one lane per output sums them in wave order and applies the epilogue.  No
+// workspace, no cross-workgroup step; results do not depend on scheduling.
+#include "device_common.h"
+#include "fdec_internal.h"
+
+#include <algorithm>
+
+namespace fdec {
+
+namespace {
+
+constexpr int kFp4MaxWaves = 16;
+
+// E4M3 ('fn': no infinities) byte -> fp32 from its fields: sign bit 7, exponent bits
+// 6..3 (bias 7), mantissa bits 2..0; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+    float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;
+    v = (e == 15u && m == 7u) ? __builtin_nanf("") : v;
+    return (b & 0x80u) ? -v : v;
+}
+
+// The two E2M1 codes of byte B of w (the lower-k code in the low nibble) as exact fp16
+// values: (w[k = 2B], w[k = 2B + 1]).
+template <int B>
+__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B);
+}
+
+// The eight weights of one packed word, in k order.
+__device__ __forceinline__ void fp4x8(uint32_t w, half2_t* q) {
+    q[0] = fp4x2<0>(w);
+    q[1] = fp4x2<1>(w);
+    q[2] = fp4x2<2>(w);
+    q[3] = fp4x2<3>(w);
+}
+
+__device__ __forceinline__ float xchg32(float v) { return __shfl_xor(v, 32, kWave); }
+__device__ __forceinline__ uint32_t xchg32u(uint32_t v) {
+    return __builtin_bit_cast(uint32_t, __shfl_xor(__builtin_bit_cast(int, v), 32, kWave));
+}
+
+struct Fp4Args {
+    const uint16_t* a0;     // g (SwiGLU) or x (identity), row stride lda
+    const uint16_t* a1;     // u (SwiGLU) or unused
+    int64_t lda;
+    const uint4* qw;        // [N][K/32] chunks of four words
+    const uint16_t* sc;     // [N][K/32] pairs of E4M3 block scales
+    int M, K, N;
+    int nch;                // K / 32
+    int cols;               // columns per workgroup (2 CH)
+    const float* out_scale;
+    const uint16_t* residual;
+    uint16_t* y;
+};
+
+template <int MR, int CH, int PRO>
+__global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args a) {
+    __shared__ float red[kFp4MaxWaves][MR][2 * CH];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int h = lane >> 5, cl = lane & 31;
+    const int cbase = xcd_remap(blockIdx.x, gridDim.x) * a.cols;
+    const int c = wave * 32 + cl;
+    const bool valid = c < a.nch;
+    const int cc = min(c, a.nch - 1);          // loads stay inside the tensors
+
+    // ---- every global load first: activation inputs, then weights and scales ----
+    uint4 ga[MR][2], ua[MR][2];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const uint16_t* p = a.a0 + size_t(min(m, a.M - 1)) * a.lda + size_t(cc) * 32 + 16 * h;
+        ga[m][0] = *reinterpret_cast<const uint4*>(p);
+        ga[m][1] = *reinterpret_cast<const uint4*>(p + 8);
+        if (PRO == kSwiGLU) {
+            const uint16_t* q = a.a1 + size_t(min(m, a.M - 1)) * a.lda + size_t(cc) * 32 + 16 * h;
+            ua[m][0] = *reinterpret_cast<const uint4*>(q);
+            ua[m][1] = *reinterpret_cast<const uint4*>(q + 8);
+        }
+    }
+    uint4 wv[CH];
+    uint32_t sp[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const size_t n = size_t(min(cbase + h * CH + j, a.N - 1));
+        wv[j] = a.qw[n * a.nch + cc];
+        sp[j] = a.sc[n * a.nch + cc];
+    }
+
+    // ---- the chunk's activation, block-scaled fp16, both halves in every lane ----
+    uint32_t act[MR][16];                      // the chunk's 32 values as 16 pairs, k order
+    float e2[MR];                              // the chunk's power of two
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const bool live = valid && m < a.M;
+        const uint32_t gw[8] = {ga[m][0].x, ga[m][0].y, ga[m][0].z, ga[m][0].w,
+                                ga[m][1].x, ga[m][1].y, ga[m][1].z, ga[m][1].w};
+        uint32_t uw[8] = {};
+        if (PRO == kSwiGLU) {
+            const uint32_t t[8] = {ua[m][0].x, ua[m][0].y, ua[m][0].z, ua[m][0].w,
+                                   ua[m][1].x, ua[m][1].y, ua[m][1].z, ua[m][1].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) uw[i] = t[i];
+        }
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (PRO == kSwiGLU) {
+                v[2 * i] = silu_f32(bf16_lo(gw[i])) * bf16_lo(uw[i]);
+                v[2 * i + 1] = silu_f32(bf16_hi(gw[i])) * bf16_hi(uw[i]);
+            } else {
+                v[2 * i] = bf16_lo(gw[i]);
+                v[2 * i + 1] = bf16_hi(gw[i]);
+            }
+        }
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            v[i] = live ? v[i] : 0.f;
+            mx = fmaxf(mx, fabsf(v[i]));
+        }
+        mx = fmaxf(mx, xchg32(mx));            // the chunk's largest magnitude
+        int e = 0;
+        (void)__builtin_frexpf(mx, &e);
+        const int E = min(max(e - 15, -126), 127);
+        const float down = __builtin_ldexpf(1.0f, -E);
+        e2[m] = __builtin_ldexpf(1.0f, E);
+        uint32_t own[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            own[i] = __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2 * i] * down, v[2 * i + 1] * down));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t oth = xchg32u(own[i]);
+            act[m][i] = h ? oth : own[i];      // k = 32 c + 0 .. 15 come from half 0
+            act[m][8 + i] = h ? own[i] : oth;  // k = 32 c + 16 .. 31 from half 1
+        }
+    }
+
+    // ---- the chunk's dot product for each of the lane's columns ----
+    float part[MR][CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const float s0 = e4m3_to_f32(sp[j] & 0xFFu), s1 = e4m3_to_f32(sp[j] >> 8);
+        half2_t q[16];
+        fp4x8(wv[j].x, q);
+        fp4x8(wv[j].y, q + 4);
+        fp4x8(wv[j].z, q + 8);
+        fp4x8(wv[j].w, q + 12);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            float d0 = 0.f, d1 = 0.f;          // the chunk's two 16-wide blocks
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                d0 = dot2(q[i], __builtin_bit_cast(half2_t, act[m][i]), d0);
+                d1 = dot2(q[8 + i], __builtin_bit_cast(half2_t, act[m][8 + i]), d1);
+            }
+            part[m][j] = valid ? fmaf(d0, s0, d1 * s1) * e2[m] : 0.f;
+        }
+    }
+
+    // ---- per column: the 32 lanes of each half, then the waves ----
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            float t = part[m][j];
+            t += dpp<kQuadSwap1>(t);
+            t += dpp<kQuadSwap2>(t);
+            t += dpp<kRowRor4>(t);
+            t += dpp<kRowRor8>(t);             // every lane holds its row-of-16 sum
+            const int b = __builtin_bit_cast(int, t);
+            const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+            const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+            if (lane == 0) {
+                red[wave][m][j] = s0;
+                red[wave][m][CH + j] = s1;
+            }
+        }
+    __syncthreads();
+    if (wave == 0 && lane < MR * 2 * CH) {
+        const int m = lane / (2 * CH), col = lane % (2 * CH), n = cbase + col;
+        const int nw = blockDim.x >> 6;
+        float t = 0.f;
+        for (int w = 0; w < nw; ++w) t += red[w][m][col];
+        if (m < a.M && col < a.cols && n < a.N) {
+            const float os = a.out_scale ? *a.out_scale : 1.0f;
+            const float res = a.residual ? bf16_to_f32(a.residual[size_t(m) * a.N + n]) : 0.f;
+            a.y[size_t(m) * a.N + n] = f32_to_bf16(fmaf(t, os, res));
+        }
+    }
+}
+
+// Test hook: the same decode, written out as fp32 w[k][n].
+__global__ void fp4_dequant_kernel(const uint32_t* __restrict__ qw, const uint8_t* __restrict__ sc, int KB, int N,
+                                   float* __restrict__ w) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;     // word (n, kb)
+    if (i >= int64_t(KB) * N) return;
+    const int n = int(i / KB), kb = int(i % KB);
+    const float s = e4m3_to_f32(sc[int64_t(n) * (KB / 2) + kb / 2]);
+    half2_t q[4];
+    fp4x8(qw[i], q);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        w[(int64_t(kb) * 8 + 2 * p) * N + n] = float(q[p][0]) * s;
+        w[(int64_t(kb) * 8 + 2 * p + 1) * N + n] = float(q[p][1]) * s;
+    }
+}
+
+struct Fp4Plan {
+    int mr, ch, cols, waves, wgs;
+};
+
+// Columns per lane: about N / 512, so that C = 2 CH columns per workgroup gives one
+// workgroup per CU; capped by the registers the rows need (8, 6 and 2 for 1, 2 and 4 rows).
+constexpr int kFp4Ch[] = {1, 2, 3, 4, 5, 6, 8};
+
+bool fp4_plan(int M, int K, int N, Fp4Plan& p) {
+    if (M < 1 || M > 4 || K <= 0 || K % 32 || K > 32 * 32 * kFp4MaxWaves || N <= 0) return false;
+    p.mr = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+    const int chmax = p.mr == 1 ? 8 : p.mr == 2 ? 6 : 2;
+    const int want = std::min(chmax, std::max(1, (N + 511) / 512));
+    p.ch = chmax;
+    for (int c : kFp4Ch)
+        if (c >= want && c <= chmax) { p.ch = c; break; }
+    p.cols = 2 * p.ch;
+    p.waves = (K / 32 + 31) / 32;
+    p.wgs = (N + p.cols - 1) / p.cols;
+    return true;
+}
+
+template <int MR, int CH>
+hipError_t launch_fp4_2(Prologue pro, const Fp4Args& a, const Fp4Plan& p, hipStream_t s) {
+    if (pro == kSwiGLU)
+        fp4_gemv_kernel<MR, CH, kSwiGLU><<<dim3(p.wgs), p.waves * kWave, 0, s>>>(a);
+    else
+        fp4_gemv_kernel<MR, CH, kIdentity><<<dim3(p.wgs), p.waves * kWave, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+// Instantiated: CH in {1, 2} for every MR, 3..6 for MR <= 2, 8 for MR == 1 (the
+// register budget: no spills); fp4_plan only picks these.
+template <int MR>
+hipError_t launch_fp4_1(Prologue pro, const Fp4Args& a, const Fp4Plan& p, hipStream_t s) {
+    if constexpr (MR == 1)
+        if (p.ch == 8) return launch_fp4_2<MR, 8>(pro, a, p, s);
+    if constexpr (MR <= 2) {
+        switch (p.ch) {
+            case 6: return launch_fp4_2<MR, 6>(pro, a, p, s);
+            case 5: return launch_fp4_2<MR, 5>(pro, a, p, s);
+            case 4: return launch_fp4_2<MR, 4>(pro, a, p, s);
+            case 3: return launch_fp4_2<MR, 3>(pro, a, p, s);
+            default: break;
+        }
+    }
+    switch (p.ch) {
+        case 1: return launch_fp4_2<MR, 1>(pro, a, p, s);
+        case 2: return launch_fp4_2<MR, 2>(pro, a, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool fp4_gemv_supported(int M, int K, int N) {
+    Fp4Plan p;
+    return fp4_plan(M, K, N, p);
+}
+
+hipError_t launch_fp4_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
+                           const uint8_t* sc, int M, int K, int N, const float* out_scale, const uint16_t* residual,
+                           uint16_t* y, hipStream_t s) {
+    Fp4Plan p;
+    if (!fp4_plan(M, K, N, p)) return hipErrorInvalidValue;
+    Fp4Args a{};
+    a.a0 = a0;
+    a.a1 = a1;
+    a.lda = lda;
+    a.qw = reinterpret_cast<const uint4*>(qw);
+    a.sc = reinterpret_cast<const uint16_t*>(sc);
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.nch = K / 32;
+    a.cols = p.cols;
+    a.out_scale = out_scale;
+    a.residual = residual;
+    a.y = y;
+    switch (p.mr) {
+        case 1: return launch_fp4_1<1>(pro, a, p, s);
+        case 2: return launch_fp4_1<2>(pro, a, p, s);
+        default: return launch_fp4_1<4>(pro, a, p, s);
+    }
+}
+
+hipError_t launch_fp4_dequant(const uint32_t* qw, const uint8_t* sc, int K, int N, float* w, hipStream_t s) {
+    const int64_t n = int64_t(K / 8) * N;
+    fp4_dequant_kernel<<<dim3((n + 255) / 256), 256, 0, s>>>(qw, sc, K / 8, N, w);
+    return hipGetLastError();
+}
+
+}  // namespace fdec
