@@ -242,6 +242,21 @@ def bench_extras(torch, F, synth, n_sets_gemv):
     out["batch_sweep_swiglu_w4_gemv_9216x2560"] = sweep
     del gsets
 
+    # the same SwiGLU GEMV with FP4 weights (E2M1 + E4M3 1x16 block scales), 48
+    # rotating sets (13.3 MB each, 639 MB in all)
+    log("[bench] FP4 SwiGLU GEMV M=1 K=9216 N=2560")
+    fsets = []
+    for i in range(min(n_sets_gemv, 48)):
+        inp = synth.swiglu_fp4_gemv_inputs(Mg, K, N, seed=i, out_scale=c["out_scale"])
+        fsets.append((F.from_bits(inp.g), F.from_bits(inp.u), F.FP4Weight.from_numpy(inp.W.qweight, inp.W.scales),
+                      torch.empty((Mg, N), dtype=torch.bfloat16, device="cuda")))
+    fns = [lambda s=s: F.swiglu_fp4_gemv(s[0], s[1], s[2], scale, out=s[3]) for s in fsets]
+    t = bench_repeat(torch, timer, fns, 5) / len(fsets)
+    b = T.swiglu_fp4_gemv_bytes(Mg, K, N)
+    out["swiglu_fp4_gemv_1x9216x2560"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9,
+                                          "frac_of_peak": b / t / 1e9 / PEAK_GBPS, "bytes_per_call": b}
+    del fsets
+
     # Llama-3-8B-sized MLP layer at M=16, 6 rotating weight sets
     c = synth.CONFIGS["mlp_llama3_8b_m16"]
     M, H, I = c["M"], c["H"], c["I"]

@@ -41,6 +41,22 @@ def w4_gemv_bytes(M: int, K: int, N: int, out_scale: bool = False) -> int:
     return w4_weight_bytes(K, N) + M * K * BF16 + M * N * BF16 + (F32 if out_scale else 0)
 
 
+def fp4_weight_bytes(K: int, N: int) -> int:
+    """Packed E2M1 weights (K*N/2) plus E4M3 block scales, one byte per 16 along K."""
+    return K * N // 2 + (K // 16) * N
+
+
+def swiglu_fp4_gemv_bytes(M: int, K: int, N: int, residual: bool = False, out_scale: bool = True) -> int:
+    """The SwiGLU-prologue GEMV with FP4 weights: g and u in, y out (+ residual), weights,
+    and the fp32 scalar."""
+    b = fp4_weight_bytes(K, N) + 2 * M * K * BF16 + M * N * BF16
+    if residual:
+        b += M * N * BF16
+    if out_scale:
+        b += F32
+    return b
+
+
 def add_rmsnorm_bytes(M: int, H: int) -> int:
     """x and residual in, h and y out (8 bytes per element), plus the weight vector."""
     return 4 * M * H * BF16 + H * BF16

@@ -64,3 +64,10 @@ def test_config_byte_totals():
     # (13,762,560 + 430,080) + h (3,072) + act (17,920); kernel 2 = act (17,920) + down
     # (6,881,280 + 215,040) + out (3,072) + scale (4) + h -> residual (6,144)
     assert T.mlp2_layer_bytes(1, 1536, 8960, False) == 14_222_848 + 7_123_460
+
+
+def test_fp4_gemv_bytes():
+    # E2M1 codes (K*N/2) + one E4M3 byte per 16 weights + g, u in + y out + the scalar
+    assert T.fp4_weight_bytes(9216, 2560) == 11_796_480 + 1_474_560
+    assert T.swiglu_fp4_gemv_bytes(1, 9216, 2560) == 11_796_480 + 1_474_560 + 36_864 + 5_120 + 4
+    assert T.swiglu_fp4_gemv_bytes(1, 9216, 2560) - T.swiglu_w4_gemv_bytes(1, 9216, 2560) == 1_474_560 - 368_640
