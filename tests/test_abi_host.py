@@ -162,6 +162,46 @@ def test_gemv_validation(L, inject):
     assert _gemv(L, f, M=16, ld=2048) == HIP
 
 
+def _fp4(f, K=1024, N=512, q=None, s=None):
+    return F.CFP4(f(K * N // 2) if q is None else q, f(K * N // 16) if s is None else s, K, N)
+
+
+def test_fp4_gemv_validation(L, inject):
+    f = Fake()
+
+    def call(W=None, g=None, u=None, ld=None, scale=None, res=None, M=1, y=None):
+        W = _fp4(f) if W is None else W
+        return L.fdec_swiglu_fp4_gemv(f() if g is None else g, f() if u is None else u, W.K if ld is None else ld,
+                                      ctypes.byref(W), scale, res, M, f() if y is None else y, None)
+
+    assert L.fdec_swiglu_fp4_gemv(f(), f(), 1024, None, None, None, 1, f(), None) == NULL
+    assert call(W=_fp4(f, K=1000)) == SHAPE              # K % 32
+    assert call(W=_fp4(f, N=500)) == SHAPE               # N % 8
+    assert call(W=_fp4(f, q=0)) == NULL
+    assert call(W=_fp4(f, s=f() + 2)) == ALIGN
+    assert call(M=0) == SHAPE
+    assert call(M=17) == SHAPE
+    assert call(M=5) == UNSUP                            # the FP4 kernel takes M <= 4
+    assert call(W=_fp4(f, K=16416, N=8)) == UNSUP        # and K <= 16384
+    assert call(ld=1000) == SHAPE
+    assert call(g=f() + 2) == ALIGN
+    assert call(u=0) == NULL
+    W = _fp4(f)
+    assert call(W=W, y=W.scales) == ALIAS
+    r = f()
+    assert call(res=r, y=r + 32) == ALIAS
+    assert call(res=r, y=r) == HIP                       # y == residual allowed
+    assert call() == HIP
+    assert call(M=4, ld=2048) == HIP
+    # identity prologue and the decode hook
+    W = _fp4(f, K=96, N=8)
+    assert L.fdec_fp4_gemv(f(), ctypes.byref(W), None, None, 1, f(), None) == HIP
+    assert L.fdec_fp4_gemv(f(), None, None, None, 1, f(), None) == NULL
+    assert L.fdec_fp4_dequant(ctypes.byref(W), 0, None) == NULL
+    assert L.fdec_fp4_dequant(ctypes.byref(W), W.qweight + 64, None) == ALIAS
+    assert L.fdec_fp4_dequant(ctypes.byref(W), f(), None) == HIP
+
+
 def test_gemv_split_override_changes_workspace(L):
     base = L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560)
     try:
