@@ -39,6 +39,8 @@ namespace fdec {
 namespace {
 
 constexpr int kFp4MaxWaves = 16;
+constexpr int kFp4MaxCh = 8;                                  // columns per lane, at most
+constexpr int kFp4ScBytes = 2 * kFp4MaxCh * 32 * kFp4MaxWaves * 2 + 32;   // a workgroup's scales + alignment slack
 
 // E4M3 ('fn': no infinities) byte -> fp32 from its fields: sign bit 7, exponent bits
 // 6..3 (bias 7), mantissa bits 2..0; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN.
@@ -74,7 +76,7 @@ struct Fp4Args {
     const uint16_t* a1;     // u (SwiGLU) or unused
     int64_t lda;
     const uint4* qw;        // [N][K/32] chunks of four words
-    const uint16_t* sc;     // [N][K/32] pairs of E4M3 block scales
+    const uint8_t* sc;      // [N][K/16] E4M3 block scales
     int M, K, N;
     int nch;                // K / 32
     int cols;               // columns per workgroup (2 CH)
@@ -86,6 +88,7 @@ struct Fp4Args {
 template <int MR, int CH, int PRO>
 __global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args a) {
     __shared__ float red[kFp4MaxWaves][MR][2 * CH];
+    __shared__ __align__(16) unsigned char sc_s[kFp4ScBytes];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h = lane >> 5, cl = lane & 31;
     const int cbase = xcd_remap(blockIdx.x, gridDim.x) * a.cols;
@@ -107,12 +110,25 @@ __global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args 
         }
     }
     uint4 wv[CH];
-    uint32_t sp[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
         const size_t n = size_t(min(cbase + h * CH + j, a.N - 1));
         wv[j] = a.qw[n * a.nch + cc];
-        sp[j] = a.sc[n * a.nch + cc];
+    }
+    // The workgroup's block scales are one contiguous run of cols * K/16 bytes (its
+    // columns are consecutive rows of [N][K/16]).  Threads load it in 16-byte pieces from
+    // the 16-byte boundary at or below its start; the tensor's size is a multiple of 16
+    // (N % 8 == 0, K/16 even), so no piece reads past its end.
+    const size_t sb = size_t(a.K) / 16;                      // scale bytes per column
+    const int ncols = min(a.cols, a.N - cbase);              // columns that exist
+    const size_t s0 = size_t(cbase) * sb, s1 = s0 + size_t(ncols) * sb;
+    const size_t a0 = s0 & ~size_t(15);
+    const int npieces = int((s1 - a0 + 15) >> 4);
+    uint4 spc[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int t = min(tid + r * int(blockDim.x), npieces - 1);
+        spc[r] = *reinterpret_cast<const uint4*>(a.sc + a0 + size_t(t) * 16);
     }
 
     // ---- the chunk's activation, block-scaled fp16, both halves in every lane ----
@@ -165,11 +181,22 @@ __global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args 
         }
     }
 
+    // ---- scales to LDS: piece t at sc_s[16 t], so byte i of the run is at sc_s[s0 - a0 + i]
+    // (s0 - a0 is even: cbase and K/16 are) ----
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int t = tid + r * int(blockDim.x);
+        if (t < npieces) *reinterpret_cast<uint4*>(sc_s + size_t(t) * 16) = spc[r];
+    }
+    __syncthreads();
+
     // ---- the chunk's dot product for each of the lane's columns ----
     float part[MR][CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        const float s0 = e4m3_to_f32(sp[j] & 0xFFu), s1 = e4m3_to_f32(sp[j] >> 8);
+        const int col = min(h * CH + j, ncols - 1);
+        const uint32_t sp = *reinterpret_cast<const uint16_t*>(sc_s + (s0 - a0) + size_t(col) * sb + 2 * cc);
+        const float s0 = e4m3_to_f32(sp & 0xFFu), s1 = e4m3_to_f32(sp >> 8);
         half2_t q[16];
         fp4x8(wv[j].x, q);
         fp4x8(wv[j].y, q + 4);
@@ -246,7 +273,7 @@ struct Fp4Plan {
 constexpr int kFp4Ch[] = {1, 2, 3, 4, 5, 6, 8};
 
 bool fp4_plan(int M, int K, int N, Fp4Plan& p) {
-    if (M < 1 || M > 4 || K <= 0 || K % 32 || K > 32 * 32 * kFp4MaxWaves || N <= 0) return false;
+    if (M < 1 || M > 4 || K <= 0 || K % 32 || K > 32 * 32 * kFp4MaxWaves || N <= 0 || N % 8) return false;
     p.mr = M <= 1 ? 1 : M <= 2 ? 2 : 4;
     const int chmax = p.mr == 1 ? 8 : p.mr == 2 ? 6 : 2;
     const int want = std::min(chmax, std::max(1, (N + 511) / 512));
@@ -307,7 +334,7 @@ hipError_t launch_fp4_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1,
     a.a1 = a1;
     a.lda = lda;
     a.qw = reinterpret_cast<const uint4*>(qw);
-    a.sc = reinterpret_cast<const uint16_t*>(sc);
+    a.sc = sc;
     a.M = M;
     a.K = K;
     a.N = N;

@@ -117,3 +117,36 @@ def test_graph_update_refuses_the_other_layer_form():
     want = eager_chain(inp, layers, M, H, I, False)
     replay_and_check(graph, b, inp, want, "after a refused form change")
     graph.close()
+
+
+def test_graph_update_with_other_kernels_keeps_a_consistent_graph():
+    """Forcing the split-K GEMV makes the re-captured chain use other kernel functions.
+    Either HIP takes the update (the graph then replays the split-K chain on the new
+    buffers) or it refuses (FDEC_ERR_UNSUPPORTED, and the graph keeps replaying the old
+    chain on the old buffers); both are checked bit for bit against eager chains."""
+    say("[graph update] re-captured chain with other kernel functions")
+    M, H, I = 1, 256, 512
+    inp_a = synth.mlp_inputs(M, H, I, n_layers=2, seed=404)
+    inp_b = synth.mlp_inputs(M, H, I, n_layers=2, seed=505)
+    lay_a, lay_b = dev_layers(inp_a, False), dev_layers(inp_b, False)
+    want_a = eager_chain(inp_a, lay_a, M, H, I, False)
+    ba, bb = F.MlpBuffers.empty(M, H, I, out_is_x=True), F.MlpBuffers.empty(M, H, I, out_is_x=True)
+    graph = F.MlpGraph(lay_a, ba)
+    replay_and_check(graph, ba, inp_a, want_a, "before")
+    F.set_gemv_split(2)
+    try:
+        want_b_split = eager_chain(inp_b, lay_b, M, H, I, False)
+        try:
+            graph.update(lay_b, bb)
+            took = True
+        except F.FdecError as e:
+            assert e.status == UNSUP
+            took = False
+    finally:
+        F.set_gemv_split(0)
+    say(f"  update {'taken' if took else 'refused'}")
+    if took:
+        replay_and_check(graph, bb, inp_b, want_b_split, "after a taken update")
+    else:
+        replay_and_check(graph, ba, inp_a, want_a, "after a refused update")
+    graph.close()
