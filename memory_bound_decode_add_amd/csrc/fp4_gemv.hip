@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args 
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
         const size_t n = size_t(min(cbase + h * CH + j, a.N - 1));
-        wv[j] = a.qw[n * a.nch + cc];
+        wv[j] = nt_load(a.qw + n * a.nch + cc);
     }
     // The workgroup's block scales are one contiguous run of cols * K/16 bytes (its
     // columns are consecutive rows of [N][K/16]).  Threads load it in 16-byte pieces from

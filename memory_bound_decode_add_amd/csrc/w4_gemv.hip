@@ -428,7 +428,7 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
         const int cj = slot_ok(j) ? slot_cj(j) : slot_cj(0);
         const uint4* colp = a.qw + size_t(min(column(cj), a.N - 1)) * a.nch;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) wv[i][j] = colp[min(lane + kWave * i, a.nch - 1)];
+        for (int i = 0; i < NI; ++i) wv[i][j] = nt_load(colp + min(lane + kWave * i, a.nch - 1));
     }
     if (PAIR) __syncthreads();                     // the staging waves' row sums
     __syncthreads();
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(256) void w4_gemv_split_kernel(SplitArgs a) {
     for (int i = 0; i < GW; ++i) {
         const int g = g0 + min(wave + 4 * i, ng - 1);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) wv[i][c] = a.qw[size_t(colc + c) * a.nch + g * 4 + kr];
+        for (int c = 0; c < 4; ++c) wv[i][c] = nt_load(a.qw + size_t(colc + c) * a.nch + g * 4 + kr);
         sv[i] = *reinterpret_cast<const uint2*>(a.sc + size_t(g) * a.N + colc);
     }
     __builtin_amdgcn_sched_barrier(0);
