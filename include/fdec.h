@@ -59,11 +59,14 @@
  *              stores); out_scale must be 4-byte aligned.
  *   Aliasing.  Outputs must not overlap inputs, except where a parameter says so.
  *   Workspace. Entry points that reduce across workgroups take a workspace of at
- *              least the size their *_workspace_bytes query returns.  It holds
- *              per-tile arrival counters that must be zero when the workspace is
- *              first used: allocate it zero-filled or call fdec_workspace_init once.
- *              Each call leaves the counters at zero again.  One workspace serves one
- *              call at a time: calls that may run concurrently (different streams)
+ *              least the size their *_workspace_bytes query returns.  It holds fp32
+ *              partial sums of K slices, and for the VALU split-K kernel (M <= 4 with
+ *              K > 16384) per-tile arrival counters that must be zero when the
+ *              workspace is first used: allocate it zero-filled or call
+ *              fdec_workspace_init once; each call leaves the counters at zero again.
+ *              (The matrix-core kernel, 5 <= M <= 16, sums its slices in a second
+ *              kernel on the same stream and needs no counters.)  One workspace serves
+ *              one call at a time: calls that may run concurrently (different streams)
  *              need different workspaces.
  */
 #ifndef FDEC_H

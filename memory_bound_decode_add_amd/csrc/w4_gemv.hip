@@ -1003,10 +1003,7 @@ bool plan_mfma(int M, int K, int N, GemvPlan& p) {
     int S = mfma_splits(p.groups, p.tiles);
     p.gps = (p.groups + S - 1) / S;
     p.splits = (p.groups + p.gps - 1) / p.gps;
-    if (p.splits > 1) {
-        p.counter_bytes = (size_t(p.tiles) * 4 + 255) / 256 * 256;
-        p.partial_bytes = size_t(p.splits) * 16 * p.tiles * ncol * 4;
-    }
+    if (p.splits > 1) p.partial_bytes = size_t(p.splits) * 16 * p.tiles * ncol * 4;   // no counters: a second kernel sums
     p.lds_bytes = size_t(16) * (size_t(p.gps) * 16 + 1) * 16 + size_t(16) * p.gps * 4;
     return true;
 }

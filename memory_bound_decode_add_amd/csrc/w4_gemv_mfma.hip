@@ -9,9 +9,13 @@
 // HBM speed; v_mfma_f32_16x16x32_f16 does the products, the VALU only decodes.
 //
 // Tiling.  A tile is 16 consecutive columns.  A workgroup of W waves owns W * TPW
-// tiles (each wave TPW of them) over a slice of whole 128-wide groups of K; with
-// several slices per column range, slices are combined through the workspace by the
-// last workgroup to arrive (the split-K protocol of the VALU split kernel).
+// tiles (each wave TPW of them) over a slice of whole 128-wide groups of K.  With
+// several slices per column range, each workgroup writes its fp32 partial sums to the
+// workspace with plain stores, and a second kernel on the same stream sums the slices in
+// order and applies the epilogue: the kernel boundary makes the partials visible.  (A
+// last-workgroup-to-arrive finish inside the kernel, with device-scope atomic stores, an
+// arrival counter and device-scope loads, measured about 5 us slower per call: device-
+// scope operations go past the XCDs' L2s.)
 //
 // MFMA mapping (16x16x32, checked on the hardware for the f16 and bf16 forms: lane l
 // supplies A[l%16][8(l/16) + e],
@@ -66,7 +70,6 @@ struct MfmaArgs {
     const uint16_t* residual;
     uint16_t* y;
     float* partial;         // [splits][16][npad]
-    unsigned* counters;     // [cgroups]
 };
 
 // One packed word -> 8 fp16 values with their offsets, in pair order.
@@ -120,7 +123,6 @@ __device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, bool live, 
 template <int TPW, int PRO>
 __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int last_flag;
     const int W = blockDim.x >> 6;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ls = lane >> 4, lm = lane & 15;          // k-slot, row / column-in-tile
@@ -280,51 +282,36 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
         return;
     }
 
-    // ---- several K slices: partials, then the last workgroup of the range finishes ----
-    // Partials go out as device-scope atomic stores (coherent across the XCDs' L2s);
-    // waiting for their completion before bumping the arrival counter orders them
-    // before it.  The finishing workgroup reads them back with device-scope atomic loads.
+    // ---- several K slices: this slice's partial sums, plain stores ----
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int nc = (nw0 - cg * ncol) + t * 16 + 4 * ls;          // column within the range
         float* dst = a.partial + (size_t(split) * 16 + lm) * a.npad + cg * ncol + nc;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, out[t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *reinterpret_cast<float4*>(dst) = make_float4(out[t][0], out[t][1], out[t][2], out[t][3]);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned old = __hip_atomic_fetch_add(&a.counters[cg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (old == unsigned(a.splits - 1));
-    }
-    __syncthreads();
-    if (!last_flag) return;
+}
 
-    // each thread finishes outputs o = tid, tid + blockDim, ... of the range's 16 x ncol,
-    // summing the slices in order with all loads of a batch issued before the adds
+// y[m, n] = bf16(s * sum over slices, in slice order, of partial[slice][m][n] (+ res)).
+__global__ __launch_bounds__(256) void mfma_splitk_finish_kernel(const float* __restrict__ partial, int splits,
+                                                                int npad, int M, int N, const float* out_scale,
+                                                                const uint16_t* residual, uint16_t* y) {
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= M * N) return;
+    const int m = o / N, n = o % N;
+    const float* p = partial + size_t(m) * npad + n;
+    const size_t stride = size_t(16) * npad;
     constexpr int SB = 8;
-    for (int o = tid; o < 16 * ncol; o += blockDim.x) {
-        const int m = o / ncol, nc = o % ncol, n = cg * ncol + nc;
-        const bool live = m < a.M && n < a.N;
-        float v = 0.f;
-        for (int s0 = 0; s0 < a.splits; s0 += SB) {
-            float t[SB];
+    float v = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += SB) {
+        float t[SB];
 #pragma unroll
-            for (int b = 0; b < SB; ++b)
-                t[b] = (live && s0 + b < a.splits)
-                           ? __hip_atomic_load(a.partial + (size_t(s0 + b) * 16 + m) * a.npad + n, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT)
-                           : 0.f;
+        for (int b = 0; b < SB; ++b) t[b] = s0 + b < splits ? p[size_t(s0 + b) * stride] : 0.f;
 #pragma unroll
-            for (int b = 0; b < SB; ++b) v += t[b];
-        }
-        if (live) {
-            const size_t oo = size_t(m) * a.N + n;
-            const float r = a.residual ? bf16_to_f32(a.residual[oo]) : 0.f;
-            a.y[oo] = f32_to_bf16(fmaf(v, os, r));
-        }
+        for (int b = 0; b < SB; ++b) v += t[b];
     }
-    if (tid == 0) __hip_atomic_store(&a.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float os = out_scale ? *out_scale : 1.0f;
+    const float r = residual ? bf16_to_f32(residual[o]) : 0.f;
+    y[o] = f32_to_bf16(fmaf(v, os, r));
 }
 
 template <typename Kern>
@@ -362,14 +349,17 @@ hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     a.out_scale = out_scale;
     a.residual = residual;
     a.y = y;
-    a.counters = p.splits > 1 ? static_cast<unsigned*>(ws) : nullptr;
     a.partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes) : nullptr;
     const dim3 grid(p.tiles * p.splits);
     const int threads = p.waves * kWave;
     // one 16-column tile per wave (two per wave measured slower: more registers and a
     // K split for the same workgroup count)
-    return pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU>, grid, threads, p.lds_bytes, s, a)
-                          : launch_k(w4_gemv_mfma_kernel<1, kIdentity>, grid, threads, p.lds_bytes, s, a);
+    hipError_t e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU>, grid, threads, p.lds_bytes, s, a)
+                                  : launch_k(w4_gemv_mfma_kernel<1, kIdentity>, grid, threads, p.lds_bytes, s, a);
+    if (e != hipSuccess || p.splits == 1) return e;
+    mfma_splitk_finish_kernel<<<dim3((M * N + 255) / 256), 256, 0, s>>>(a.partial, p.splits, a.npad, M, N, out_scale,
+                                                                       residual, y);
+    return hipGetLastError();
 }
 
 }  // namespace fdec
