@@ -974,12 +974,12 @@ bool plan_column_pair(int M, int K, int I, GemvPlan& p) {
 }  // namespace
 
 // Matrix-core kernel: 6..8 waves of one 16-column tile each, K split into slices
-// until there are about 200 workgroups (and each slice's activation fits LDS); of the
-// wave counts, the one whose workgroups fill the 256 CUs best (fewest idle slots in
-// the last round of workgroups), ties to more waves.
+// until there are about 256 workgroups, one per CU (and each slice's activation fits
+// LDS); of the wave counts, the one whose workgroups fill the 256 CUs best (fewest idle
+// slots in the last round of workgroups), ties to more waves.
 int mfma_splits(int groups, int tiles) {
     const int S = std::max((groups + kMfmaMaxSliceGroups - 1) / kMfmaMaxSliceGroups,
-                           std::min(groups, (200 + tiles - 1) / tiles));
+                           std::min(groups, (256 + tiles - 1) / tiles));
     const int gps = (groups + S - 1) / S;
     return (groups + gps - 1) / gps;
 }
