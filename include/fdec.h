@@ -59,15 +59,11 @@
  *              stores); out_scale must be 4-byte aligned.
  *   Aliasing.  Outputs must not overlap inputs, except where a parameter says so.
  *   Workspace. Entry points that reduce across workgroups take a workspace of at
- *              least the size their *_workspace_bytes query returns.  It holds fp32
- *              partial sums of K slices, and for the VALU split-K kernel (M <= 4 with
- *              K > 16384) per-tile arrival counters that must be zero when the
- *              workspace is first used: allocate it zero-filled or call
- *              fdec_workspace_init once; each call leaves the counters at zero again.
- *              (The matrix-core kernel, 5 <= M <= 16, sums its slices in a second
- *              kernel on the same stream and needs no counters.)  One workspace serves
- *              one call at a time: calls that may run concurrently (different streams)
- *              need different workspaces.
+ *              least the size their *_workspace_bytes query returns.  It holds the fp32
+ *              partial sums of K slices, which a second kernel on the same stream sums;
+ *              its contents need no initialisation.  One workspace serves one call at
+ *              a time: calls that may run concurrently (different streams) need
+ *              different workspaces.
  */
 #ifndef FDEC_H
 #define FDEC_H
@@ -126,7 +122,9 @@ FDEC_API const char* fdec_status_str(int status);
 FDEC_API const char* fdec_last_error(void);
 
 /* Zero-fill a workspace on `stream` (a fill kernel, not a memset node, so it may be
- * captured).  ws may be NULL only if ws_bytes is 0.  ws must be 16-byte aligned. */
+ * captured).  ws may be NULL only if ws_bytes is 0.  ws must be 16-byte aligned.  No
+ * entry point needs it (workspaces need no initialisation); it is kept for callers that
+ * want a defined workspace content. */
 FDEC_API int fdec_workspace_init(void* ws, size_t ws_bytes, fdec_stream stream);
 
 /*

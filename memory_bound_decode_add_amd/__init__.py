@@ -273,7 +273,7 @@ def unfused_mlp_workspace_bytes(M, H, I) -> int:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace (its arrival counters must start at zero)."""
+    """A workspace of at least 16 bytes (zero-filled; the kernels need no initial content)."""
     return torch.zeros(max(16, int(nbytes)), dtype=torch.uint8, device=device)
 
 

@@ -14,7 +14,7 @@ namespace fdec {
 //    full K, each workgroup stages the activation of the full K once in LDS; no
 //    cross-workgroup reduction and no workspace.
 //  * Split-K (any M <= 16, any K): a 256-thread workgroup owns a 64-column tile and a
-//    slice of K; slices are combined by the last workgroup of the tile to arrive.
+//    slice of K; a second kernel sums the slices.
 constexpr int kGemvThreads = 256;
 constexpr int kGemvCols = 64;
 constexpr int kGroup = 128;
@@ -46,12 +46,16 @@ struct GemvPlan {
     int gw;           // groups per wave (1, 2 or 4)
     int gps;          // groups per split = 4 * gw
     int splits;       // ceil(groups / gps)
-    size_t partial_bytes;   // splits * M * tiles * 64 * 4 (0 when splits == 1)
-    size_t counter_bytes;   // tiles * 4, rounded up to 256 (0 when splits == 1)
+    size_t partial_bytes;   // fp32 partial sums of the K slices (0 when splits == 1)
     size_t lds_bytes;       // dynamic LDS per workgroup
 };
 
 GemvPlan plan_gemv(int M, int K, int N);
+// Sums the fp32 partials of K slices (slice j of row m at partial + j * split_stride +
+// m * row_stride) in slice order and applies the epilogue; launched after the kernel
+// that wrote them, on the same stream.
+hipError_t launch_splitk_finish(const float* partial, int splits, int64_t split_stride, int64_t row_stride, int M,
+                                int N, const float* out_scale, const uint16_t* residual, uint16_t* y, hipStream_t s);
 size_t gemv_workspace_bytes(int M, int K, int N);
 
 // kAddRmsNorm: the activation is rmsnorm(x + r) * w over the whole row (the fused

@@ -38,11 +38,9 @@
 // of each group of those columns.  The activation of a group is staged in blocks of
 // 128 (2 values per lane) and the weights are decoded to exact fp16 (XOR, shift, four
 // AND-OR and four packed fp16 ops per word).  The quad of lanes sharing columns reduces
-// with DPP, the waves through LDS.  With several slices each workgroup writes fp32
-// partials to the workspace with device-scope atomic stores, waits for them to
-// complete, then bumps the tile's arrival counter; the last to arrive reads the partials
-// back with device-scope atomic loads, sums them in slice order, applies the epilogue
-// and resets the counter.
+// with DPP, the waves through LDS.  With several slices each workgroup writes its fp32
+// partials to the workspace with plain stores, and splitk_finish_kernel, launched next
+// on the same stream, sums them in slice order and applies the epilogue.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -536,7 +534,6 @@ struct SplitArgs {
     const uint16_t* residual;
     uint16_t* y;
     float* partial;         // [splits][M][tiles*64]
-    unsigned* counters;     // [tiles]
 };
 
 template <int MR, int GW, int PRO>
@@ -546,7 +543,6 @@ __global__ __launch_bounds__(256) void w4_gemv_split_kernel(SplitArgs a) {
     _Float16* act_s = reinterpret_cast<_Float16*>(smem);                 // [GPS][MR][128]
     float* esc_s = reinterpret_cast<float*>(smem + GPS * MR * 128 * 2);   // [GPS][MR]
     float* red_s = esc_s + GPS * MR;                                      // [4][MR][64]
-    __shared__ int last_flag;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -655,74 +651,37 @@ __global__ __launch_bounds__(256) void w4_gemv_split_kernel(SplitArgs a) {
             const size_t o = size_t(m) * a.N + n;
             a.y[o] = f32_to_bf16(epilogue(v, s, a.residual, o));
         } else {
-            __hip_atomic_store(a.partial + (size_t(split) * a.M + m) * npad + n, v, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            a.partial[(size_t(split) * a.M + m) * npad + n] = v;   // summed by splitk_finish_kernel
         }
     }
-    if (a.splits == 1) return;
+}
 
-    // ---- the last workgroup of the tile to arrive finishes it ----
-    // The partials were written with device-scope atomic stores, which are coherent
-    // across the XCDs' L2 caches (they write through).  Waiting for their completion
-    // before the arrival counter is bumped orders them before it without a release
-    // fence, which on this part would write back the whole L2 once per workgroup.
-    // The finishing workgroup reads them back with device-scope atomic loads.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned old = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (old == unsigned(a.splits - 1));
-    }
-    __syncthreads();
-    if (!last_flag) return;
-
-    // P threads per output, each summing every P-th split with all its loads issued
-    // before the first add; the P sums are then added in a fixed order through LDS.
-    constexpr int OUTS = MR * kGemvCols;
-    constexpr int P = OUTS >= kGemvThreads ? 1 : kGemvThreads / OUTS;
-    constexpr int BATCH = 16;
-    for (int o = tid % OUTS; o < OUTS; o += (P == 1 ? kGemvThreads : OUTS)) {
-        const int p = P == 1 ? 0 : tid / OUTS;
-        const int m = o / kGemvCols, cc = o % kGemvCols;
-        const int n = tile * kGemvCols + cc;
-        const bool live = m < a.M && n < a.N;
-        float v = 0.f;
-        for (int s0 = p; s0 < a.splits; s0 += P * BATCH) {
-            float t[BATCH];
+// y[m, n] = bf16(s * sum over slices, in slice order, of partial[slice][m][n] (+ res)),
+// slice j of row m at partial + j * split_stride + m * row_stride.  Runs after the
+// kernel that wrote the partials, on the same stream: the kernel boundary makes them
+// visible.  (Summing inside that kernel, by the last workgroup to arrive, needs
+// device-scope atomic stores and loads and an arrival counter, which go past the XCDs'
+// L2s: measured about 5 us slower per call.)
+__global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restrict__ partial, int splits,
+                                                           int64_t split_stride, int64_t row_stride, int M, int N,
+                                                           const float* out_scale, const uint16_t* residual,
+                                                           uint16_t* y) {
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= M * N) return;
+    const int m = o / N, n = o % N;
+    const float* p = partial + m * row_stride + n;
+    constexpr int SB = 8;
+    float v = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += SB) {
+        float t[SB];
 #pragma unroll
-            for (int b = 0; b < BATCH; ++b) {
-                const int sp = s0 + b * P;
-                t[b] = (live && sp < a.splits)
-                           ? __hip_atomic_load(a.partial + (size_t(sp) * a.M + m) * npad + n, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT)
-                           : 0.f;
-            }
+        for (int b = 0; b < SB; ++b) t[b] = s0 + b < splits ? p[(s0 + b) * split_stride] : 0.f;
 #pragma unroll
-            for (int b = 0; b < BATCH; ++b) v += t[b];
-        }
-        if (P == 1) {
-            if (live) {
-                const size_t oo = size_t(m) * a.N + n;
-                a.y[oo] = f32_to_bf16(epilogue(v, s, a.residual, oo));
-            }
-        } else {
-            red_s[p * OUTS + o] = v;
-        }
+        for (int b = 0; b < SB; ++b) v += t[b];
     }
-    if (P > 1) {
-        __syncthreads();
-        for (int o = tid; o < OUTS; o += kGemvThreads) {
-            const int m = o / kGemvCols, cc = o % kGemvCols;
-            const int n = tile * kGemvCols + cc;
-            if (m >= a.M || n >= a.N) continue;
-            float v = 0.f;
-            for (int p = 0; p < P; ++p) v += red_s[p * OUTS + o];
-            const size_t oo = size_t(m) * a.N + n;
-            a.y[oo] = f32_to_bf16(epilogue(v, s, a.residual, oo));
-        }
-    }
-    if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float os = out_scale ? *out_scale : 1.0f;
+    const float r = residual ? bf16_to_f32(residual[o]) : 0.f;
+    y[o] = f32_to_bf16(fmaf(v, os, r));
 }
 
 // ===========================================================================
@@ -1003,7 +962,7 @@ bool plan_mfma(int M, int K, int N, GemvPlan& p) {
     int S = mfma_splits(p.groups, p.tiles);
     p.gps = (p.groups + S - 1) / S;
     p.splits = (p.groups + p.gps - 1) / p.gps;
-    if (p.splits > 1) p.partial_bytes = size_t(p.splits) * 16 * p.tiles * ncol * 4;   // no counters: a second kernel sums
+    if (p.splits > 1) p.partial_bytes = size_t(p.splits) * 16 * p.tiles * ncol * 4;
     p.lds_bytes = size_t(16) * (size_t(p.gps) * 16 + 1) * 16 + size_t(16) * p.gps * 4;
     return true;
 }
@@ -1034,10 +993,7 @@ GemvPlan plan_gemv(int M, int K, int N) {
     p.gw = gw;
     p.gps = 4 * gw;
     p.splits = (p.groups + p.gps - 1) / p.gps;
-    if (p.splits > 1) {
-        p.counter_bytes = (size_t(p.tiles) * 4 + 255) / 256 * 256;
-        p.partial_bytes = size_t(p.splits) * M * p.tiles * kGemvCols * 4;
-    }
+    if (p.splits > 1) p.partial_bytes = size_t(p.splits) * M * p.tiles * kGemvCols * 4;
     p.lds_bytes = size_t(p.gps) * p.mr * kGroup * 2 + size_t(p.gps) * p.mr * 4 +
                   size_t(4) * p.mr * kGemvCols * 4;
     return p;
@@ -1045,7 +1001,14 @@ GemvPlan plan_gemv(int M, int K, int N) {
 
 size_t gemv_workspace_bytes(int M, int K, int N) {
     const GemvPlan p = plan_gemv(M, K, N);
-    return p.counter_bytes + p.partial_bytes;
+    return p.partial_bytes;
+}
+
+hipError_t launch_splitk_finish(const float* partial, int splits, int64_t split_stride, int64_t row_stride, int M,
+                                int N, const float* out_scale, const uint16_t* residual, uint16_t* y, hipStream_t s) {
+    splitk_finish_kernel<<<dim3((M * N + 255) / 256), 256, 0, s>>>(partial, splits, split_stride, row_stride, M, N,
+                                                                 out_scale, residual, y);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
@@ -1094,15 +1057,18 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     a.out_scale = out_scale;
     a.residual = residual;
     a.y = y;
-    a.counters = p.splits > 1 ? static_cast<unsigned*>(ws) : nullptr;
-    a.partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes) : nullptr;
+    a.partial = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
+    hipError_t e;
     switch (p.mr) {
-        case 1: return launch_split<1>(pro, a, p, s);
-        case 2: return launch_split<2>(pro, a, p, s);
-        case 4: return launch_split<4>(pro, a, p, s);
-        case 8: return launch_split<8>(pro, a, p, s);
-        default: return launch_split<16>(pro, a, p, s);
+        case 1: e = launch_split<1>(pro, a, p, s); break;
+        case 2: e = launch_split<2>(pro, a, p, s); break;
+        case 4: e = launch_split<4>(pro, a, p, s); break;
+        case 8: e = launch_split<8>(pro, a, p, s); break;
+        default: e = launch_split<16>(pro, a, p, s); break;
     }
+    if (e != hipSuccess || p.splits == 1) return e;
+    const int64_t npad = int64_t(p.tiles) * kGemvCols;
+    return launch_splitk_finish(a.partial, p.splits, int64_t(M) * npad, npad, M, N, out_scale, residual, y, s);
 }
 
 hipError_t launch_w4_unpack(const uint32_t* qw, int K, int N, int8_t* q, hipStream_t s) {

@@ -12,10 +12,8 @@
 // tiles (each wave TPW of them) over a slice of whole 128-wide groups of K.  With
 // several slices per column range, each workgroup writes its fp32 partial sums to the
 // workspace with plain stores, and a second kernel on the same stream sums the slices in
-// order and applies the epilogue: the kernel boundary makes the partials visible.  (A
-// last-workgroup-to-arrive finish inside the kernel, with device-scope atomic stores, an
-// arrival counter and device-scope loads, measured about 5 us slower per call: device-
-// scope operations go past the XCDs' L2s.)
+// order and applies the epilogue (splitk_finish_kernel): the kernel boundary makes the
+// partials visible.
 //
 // MFMA mapping (16x16x32, checked on the hardware for the f16 and bf16 forms: lane l
 // supplies A[l%16][8(l/16) + e],
@@ -291,29 +289,6 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     }
 }
 
-// y[m, n] = bf16(s * sum over slices, in slice order, of partial[slice][m][n] (+ res)).
-__global__ __launch_bounds__(256) void mfma_splitk_finish_kernel(const float* __restrict__ partial, int splits,
-                                                                int npad, int M, int N, const float* out_scale,
-                                                                const uint16_t* residual, uint16_t* y) {
-    const int o = blockIdx.x * 256 + threadIdx.x;
-    if (o >= M * N) return;
-    const int m = o / N, n = o % N;
-    const float* p = partial + size_t(m) * npad + n;
-    const size_t stride = size_t(16) * npad;
-    constexpr int SB = 8;
-    float v = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += SB) {
-        float t[SB];
-#pragma unroll
-        for (int b = 0; b < SB; ++b) t[b] = s0 + b < splits ? p[size_t(s0 + b) * stride] : 0.f;
-#pragma unroll
-        for (int b = 0; b < SB; ++b) v += t[b];
-    }
-    const float os = out_scale ? *out_scale : 1.0f;
-    const float r = residual ? bf16_to_f32(residual[o]) : 0.f;
-    y[o] = f32_to_bf16(fmaf(v, os, r));
-}
-
 template <typename Kern>
 hipError_t launch_k(Kern k, dim3 grid, int threads, size_t lds, hipStream_t s, const MfmaArgs& a) {
     if (lds > 65536) {
@@ -349,7 +324,7 @@ hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     a.out_scale = out_scale;
     a.residual = residual;
     a.y = y;
-    a.partial = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes) : nullptr;
+    a.partial = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
     const dim3 grid(p.tiles * p.splits);
     const int threads = p.waves * kWave;
     // one 16-column tile per wave (two per wave measured slower: more registers and a
@@ -357,9 +332,7 @@ hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     hipError_t e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU>, grid, threads, p.lds_bytes, s, a)
                                   : launch_k(w4_gemv_mfma_kernel<1, kIdentity>, grid, threads, p.lds_bytes, s, a);
     if (e != hipSuccess || p.splits == 1) return e;
-    mfma_splitk_finish_kernel<<<dim3((M * N + 255) / 256), 256, 0, s>>>(a.partial, p.splits, a.npad, M, N, out_scale,
-                                                                       residual, y);
-    return hipGetLastError();
+    return launch_splitk_finish(a.partial, p.splits, int64_t(16) * a.npad, a.npad, M, N, out_scale, residual, y, s);
 }
 
 }  // namespace fdec
