@@ -187,3 +187,25 @@ def test_w4_gemv_identity_large_dynamic_range():
     ref = O.w4_gemv(x, W.qweight, W.scales)
     for m in range(M):
         assert_close(y[m:m + 1], ref[m:m + 1], f"row {m}")
+
+
+@pytest.mark.parametrize("M,K,N,split", [(16, 14336, 4096, 0), (8, 9216, 2560, 0), (5, 4096, 1000, 0),
+                                         (1, 9216, 2560, 7), (3, 2048, 520, 4)])
+def test_split_k_ignores_workspace_contents(M, K, N, split):
+    """K-sliced GEMVs (the matrix-core kernel at 5..16 rows, the VALU split kernel when
+    forced) write every partial they read back: a workspace full of NaN patterns, reused
+    for two different inputs in a row, gives the oracle's result both times."""
+    say(f"[split-K] M={M} K={K} N={N} forced split={split}: workspace filled with NaN patterns")
+    if split:
+        F.set_gemv_split(split)
+    try:
+        need = F.gemv_workspace_bytes(M, K, N)
+        assert need > 0
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+        for seed in (1, 2):
+            inp = synth.swiglu_gemv_inputs(M, K, N, seed=seed * 100 + M, out_scale=0.5, with_residual=True)
+            got = run_gemv(inp, 0.5, True, ws=ws)
+            ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 0.5, inp.residual)
+            say(f"  seed {seed}: worst err/bound {assert_close(got, ref, 'y'):.3f}")
+    finally:
+        F.set_gemv_split(0)
