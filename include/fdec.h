@@ -315,9 +315,11 @@ FDEC_API int fdec_mlp_graph_update2(fdec_graph graph, const fdec_mlp_layer* laye
  *   K % 32 == 0, N % 8 == 0; both arrays 16-byte aligned.
  *
  * fdec_swiglu_fp4_gemv: y[m, n] = bf16(s * sum_k silu(g[m,k]) u[m,k] w[k,n] (+ residual)),
- *   w = e2m1 * e4m3 block scale; arguments, aliasing and errors as fdec_swiglu_w4_gemv,
- *   without a workspace.  Implemented for M <= 4 and K <= 16384 (FDEC_ERR_UNSUPPORTED
- *   otherwise, FDEC_ERR_SHAPE outside [1, 16]).
+ *   w = e2m1 * e4m3 block scale; arguments, aliasing and errors as fdec_swiglu_w4_gemv.
+ *   Implemented for M <= 4 with K <= 16384 (a chunk-owning VALU kernel, no workspace),
+ *   and for 5 <= M <= 16 with K % 128 == 0 (the matrix-core kernel, whose K slices use
+ *   a workspace of fdec_fp4_gemv_workspace_bytes(M, K, N) bytes, 0 when not needed);
+ *   FDEC_ERR_UNSUPPORTED otherwise, FDEC_ERR_SHAPE outside [1, 16].
  * fdec_fp4_gemv: the identity prologue, y = bf16(s * x @ w (+ residual)); x [M][K].
  * fdec_fp4_dequant: test hook; writes w as fp32 [K][N] (exact).
  */
@@ -326,13 +328,14 @@ typedef struct {
     const uint8_t* scales;
     int32_t K, N;
 } fdec_fp4;
+FDEC_API size_t fdec_fp4_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N);
 FDEC_API int fdec_swiglu_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu,
                                   const fdec_fp4* W, const float* out_scale,
                                   const fdec_bf16* residual, int32_t M, fdec_bf16* y,
-                                  fdec_stream stream);
+                                  void* ws, size_t ws_bytes, fdec_stream stream);
 FDEC_API int fdec_fp4_gemv(const fdec_bf16* x, const fdec_fp4* W, const float* out_scale,
-                           const fdec_bf16* residual, int32_t M, fdec_bf16* y,
-                           fdec_stream stream);
+                           const fdec_bf16* residual, int32_t M, fdec_bf16* y, void* ws,
+                           size_t ws_bytes, fdec_stream stream);
 FDEC_API int fdec_fp4_dequant(const fdec_fp4* W, float* w_out, fdec_stream stream);
 
 /*

@@ -101,9 +101,10 @@ _SIGS = {
                                                _sz, _c_p]),
     "fdec_w4_unpack": (ctypes.c_int, [ctypes.POINTER(CW4), _c_p, _c_p]),
     "fdec_w4_dequant": (ctypes.c_int, [ctypes.POINTER(CW4), _c_p, _c_p]),
+    "fdec_fp4_gemv_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "fdec_swiglu_fp4_gemv": (ctypes.c_int, [_c_p, _c_p, _i64, ctypes.POINTER(CFP4), _c_p, _c_p, _i32, _c_p,
-                                            _c_p]),
-    "fdec_fp4_gemv": (ctypes.c_int, [_c_p, ctypes.POINTER(CFP4), _c_p, _c_p, _i32, _c_p, _c_p]),
+                                            _c_p, _sz, _c_p]),
+    "fdec_fp4_gemv": (ctypes.c_int, [_c_p, ctypes.POINTER(CFP4), _c_p, _c_p, _i32, _c_p, _c_p, _sz, _c_p]),
     "fdec_fp4_dequant": (ctypes.c_int, [ctypes.POINTER(CFP4), _c_p, _c_p]),
     "fdec_set_gemv_split": (None, [_i32]),
     "fdec_set_gemv_tiling": (None, [_i32, _i32]),
@@ -281,9 +282,24 @@ def workspace_init(ws: torch.Tensor):
     _check(lib().fdec_workspace_init(ws.data_ptr(), ws.numel(), _stream(ws.device)))
 
 
+class _NoWorkspace:
+    """Stands for 'no workspace' (a NULL pointer and 0 bytes) where a call needs none, so
+    that no tensor is allocated per call (inside a graph capture an allocation records a
+    fill kernel)."""
+
+    def data_ptr(self):
+        return 0
+
+    def numel(self):
+        return 0
+
+
+_NO_WS = _NoWorkspace()
+
+
 def _ws(ws, need, device):
     if ws is None:
-        return workspace(need, device)
+        return _NO_WS if need == 0 else workspace(need, device)
     _need(ws, "ws", torch.uint8)
     if ws.numel() < need:
         raise ValueError(f"workspace has {ws.numel()} bytes, {need} required")
@@ -640,7 +656,11 @@ class FP4Weight:
                    torch.from_numpy(np.ascontiguousarray(scales, dtype=np.uint8)).to(device))
 
 
-def swiglu_fp4_gemv(g, u, W: FP4Weight, out_scale=None, residual=None, out=None):
+def fp4_gemv_workspace_bytes(M, K, N) -> int:
+    return int(lib().fdec_fp4_gemv_workspace_bytes(M, K, N))
+
+
+def swiglu_fp4_gemv(g, u, W: FP4Weight, out_scale=None, residual=None, out=None, ws=None):
     """y = bf16(s * (silu(g) * u) @ W (+ residual)) with FP4 weights; g, u are [M, K] views."""
     M = g.shape[0]
     ld = _rows(g, "g", M, W.K)
@@ -653,13 +673,15 @@ def swiglu_fp4_gemv(g, u, W: FP4Weight, out_scale=None, residual=None, out=None)
         _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
     y = torch.empty((M, W.N), dtype=torch.bfloat16, device=g.device) if out is None else out
     _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    ws = _ws(ws, fp4_gemv_workspace_bytes(M, W.K, W.N), g.device)
     cw = W.c()
     _check(lib().fdec_swiglu_fp4_gemv(g.data_ptr(), u.data_ptr(), ld, ctypes.byref(cw), _ptr(out_scale),
-                                      _ptr(residual), M, y.data_ptr(), _stream(g.device)))
+                                      _ptr(residual), M, y.data_ptr(), ws.data_ptr(), ws.numel(),
+                                      _stream(g.device)))
     return y
 
 
-def fp4_gemv(x, W: FP4Weight, out_scale=None, residual=None, out=None):
+def fp4_gemv(x, W: FP4Weight, out_scale=None, residual=None, out=None, ws=None):
     """y = bf16(s * x @ W (+ residual)) with FP4 weights (identity prologue)."""
     _need(x, "x", torch.bfloat16)
     M = x.shape[0]
@@ -670,9 +692,10 @@ def fp4_gemv(x, W: FP4Weight, out_scale=None, residual=None, out=None):
         _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
     y = torch.empty((M, W.N), dtype=torch.bfloat16, device=x.device) if out is None else out
     _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    ws = _ws(ws, fp4_gemv_workspace_bytes(M, W.K, W.N), x.device)
     cw = W.c()
     _check(lib().fdec_fp4_gemv(x.data_ptr(), ctypes.byref(cw), _ptr(out_scale), _ptr(residual), M, y.data_ptr(),
-                               _stream(x.device)))
+                               ws.data_ptr(), ws.numel(), _stream(x.device)))
     return y
 
 

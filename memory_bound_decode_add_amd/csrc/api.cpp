@@ -139,7 +139,7 @@ Span fp4_qspan(const fdec_fp4* W) { return {W->qweight, size_t(W->K) / 8 * W->N 
 Span fp4_sspan(const fdec_fp4* W) { return {W->scales, size_t(W->K) / 16 * W->N}; }
 
 int check_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_fp4* W, const float* out_scale,
-                   const fdec_bf16* residual, int M, const fdec_bf16* y, bool swiglu) {
+                   const fdec_bf16* residual, int M, const fdec_bf16* y, void* ws, size_t ws_bytes, bool swiglu) {
     int st;
     if ((st = check_fp4(W)) != FDEC_OK) return st;
     if ((st = check_m(M)) != FDEC_OK) return st;
@@ -156,7 +156,18 @@ int check_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const f
     if (residual && overlap(Y, Span{residual, Y.bytes}) && residual != y)
         return fail(FDEC_ERR_ALIAS, "y may only alias residual exactly");
     if (!fp4_gemv_supported(M, W->K, W->N))
-        return fail(FDEC_ERR_UNSUPPORTED, "the FP4 GEMV takes M <= 4 and K <= 16384 (M = %d, K = %d)", M, W->K);
+        return fail(FDEC_ERR_UNSUPPORTED,
+                    "the FP4 GEMV takes M <= 4 with K <= 16384, or M <= 16 with K %% 128 == 0 (M = %d, K = %d)", M,
+                    W->K);
+    const size_t need = fp4_gemv_workspace_bytes(M, W->K, W->N);
+    if (ws_bytes < need) return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);
+    if (need > 0 && !ws) return fail(FDEC_ERR_NULL, "workspace is NULL");
+    if (ws && !aligned16(ws)) return fail(FDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const Span WS{ws, need};
+    const Span others[] = {{g, in_bytes}, {u, in_bytes}, fp4_qspan(W), fp4_sspan(W), {out_scale, 4}, {residual, Y.bytes},
+                           Y};
+    for (const Span& sp : others)
+        if (overlap(WS, sp)) return fail(FDEC_ERR_ALIAS, "the workspace overlaps an input or y");
     return FDEC_OK;
 }
 
@@ -777,25 +788,30 @@ FDEC_API int fdec_unfused_mlp_decode(const fdec_mlp_layer* layer, int32_t M, con
     return hip_status(e, "unfused layer launch");
 }
 
+FDEC_API size_t fdec_fp4_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+    if (M < 1 || M > 16 || K <= 0 || K % 32 || N <= 0 || N % 8) return 0;
+    return fp4_gemv_workspace_bytes(M, K, N);
+}
+
 FDEC_API int fdec_swiglu_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_fp4* W,
                                   const float* out_scale, const fdec_bf16* residual, int32_t M, fdec_bf16* y,
-                                  fdec_stream stream) {
-    const int st = check_fp4_gemv(g, u, ldgu, W, out_scale, residual, M, y, true);
+                                  void* ws, size_t ws_bytes, fdec_stream stream) {
+    const int st = check_fp4_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true);
     if (st != FDEC_OK) return st;
     if (g_fail_launches) return injected();
     return hip_status(launch_fp4_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual,
-                                      y, static_cast<hipStream_t>(stream)),
+                                      y, ws, static_cast<hipStream_t>(stream)),
                       "fp4 gemv launch");
 }
 
 FDEC_API int fdec_fp4_gemv(const fdec_bf16* x, const fdec_fp4* W, const float* out_scale, const fdec_bf16* residual,
-                           int32_t M, fdec_bf16* y, fdec_stream stream) {
+                           int32_t M, fdec_bf16* y, void* ws, size_t ws_bytes, fdec_stream stream) {
     if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
-    const int st = check_fp4_gemv(x, nullptr, W->K, W, out_scale, residual, M, y, false);
+    const int st = check_fp4_gemv(x, nullptr, W->K, W, out_scale, residual, M, y, ws, ws_bytes, false);
     if (st != FDEC_OK) return st;
     if (g_fail_launches) return injected();
     return hip_status(launch_fp4_gemv(kIdentity, x, nullptr, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale,
-                                      residual, y, static_cast<hipStream_t>(stream)),
+                                      residual, y, ws, static_cast<hipStream_t>(stream)),
                       "fp4 gemv launch");
 }
 

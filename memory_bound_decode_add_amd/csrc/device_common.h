@@ -116,6 +116,36 @@ __device__ __forceinline__ half2_t pk_f16_rtz(float a, float b) {
     return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
+// ---------------------------------------------------------------------------
+// FP4 weights: E2M1 codes (bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa)
+// with E4M3 block scales.
+// ---------------------------------------------------------------------------
+// E4M3 ('fn': no infinities) byte -> fp32 from its fields: sign bit 7, exponent bits
+// 6..3 (bias 7), mantissa bits 2..0; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+    float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;
+    v = (e == 15u && m == 7u) ? __builtin_nanf("") : v;
+    return (b & 0x80u) ? -v : v;
+}
+
+// The two E2M1 codes of byte B of w (the lower-k code in the low nibble) as exact fp16
+// values: (w[k = 2B], w[k = 2B + 1]).  gfx950's v_cvt_scalef32_pk_f16_fp4 applies only
+// the exponent of its fp32 scale operand (the power-of-two scales of the MX formats), so
+// it runs with scale 1 and E4M3 block scales are applied separately.
+template <int B>
+__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B);
+}
+
+// The eight weights of one packed word, in k order.
+__device__ __forceinline__ void fp4x8(uint32_t w, half2_t* q) {
+    q[0] = fp4x2<0>(w);
+    q[1] = fp4x2<1>(w);
+    q[2] = fp4x2<2>(w);
+    q[3] = fp4x2<3>(w);
+}
+
 // Position of weight j (0..7) of a word in the pair order above.
 __host__ __device__ constexpr int pair_slot(int j) { return 2 * (j & 3) + (j >> 2); }
 

@@ -51,6 +51,7 @@ struct GemvPlan {
 };
 
 GemvPlan plan_gemv(int M, int K, int N);
+bool plan_mfma(int M, int K, int N, GemvPlan& p);   // 5 <= M <= 16
 // Sums the fp32 partials of K slices (slice j of row m at partial + j * split_stride +
 // m * row_stride) in slice order and applies the epilogue; launched after the kernel
 // that wrote them, on the same stream.
@@ -84,11 +85,17 @@ hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
                        void* ws, const GemvPlan& p, hipStream_t s);
-// FP4 (E2M1) weights with E4M3 1x16 block scales: M = 1..4, K % 32 == 0, K <= 16384.
+// FP4 (E2M1) weights with E4M3 1x16 block scales: M = 1..4 (K % 32 == 0, K <= 16384)
+// on the chunk-owning kernel, M = 5..16 (K % 128 == 0) on the matrix-core kernel.
 bool fp4_gemv_supported(int M, int K, int N);
+size_t fp4_gemv_workspace_bytes(int M, int K, int N);
 hipError_t launch_fp4_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
                            const uint8_t* sc, int M, int K, int N, const float* out_scale, const uint16_t* residual,
-                           uint16_t* y, hipStream_t s);
+                           uint16_t* y, void* ws, hipStream_t s);
+hipError_t launch_mfma_fp4(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
+                           const uint32_t* qw, const uint8_t* sc8, int M, int K, int N,
+                           const float* out_scale, const uint16_t* residual, uint16_t* y,
+                           void* ws, const GemvPlan& p, hipStream_t s);
 hipError_t launch_fp4_dequant(const uint32_t* qw, const uint8_t* sc, int K, int N, float* w, hipStream_t s);
 hipError_t launch_w4_unpack(const uint32_t* qw, int K, int N, int8_t* q, hipStream_t s);
 hipError_t launch_w4_dequant(const uint32_t* qw, const uint16_t* sc, int K, int N,

@@ -42,30 +42,6 @@ constexpr int kFp4MaxWaves = 16;
 constexpr int kFp4MaxCh = 8;                                  // columns per lane, at most
 constexpr int kFp4ScBytes = 2 * kFp4MaxCh * 32 * kFp4MaxWaves * 2 + 32;   // a workgroup's scales + alignment slack
 
-// E4M3 ('fn': no infinities) byte -> fp32 from its fields: sign bit 7, exponent bits
-// 6..3 (bias 7), mantissa bits 2..0; exponent 0 is subnormal m * 2^-9; S.1111.111 is NaN.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    const uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
-    float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;
-    v = (e == 15u && m == 7u) ? __builtin_nanf("") : v;
-    return (b & 0x80u) ? -v : v;
-}
-
-// The two E2M1 codes of byte B of w (the lower-k code in the low nibble) as exact fp16
-// values: (w[k = 2B], w[k = 2B + 1]).
-template <int B>
-__device__ __forceinline__ half2_t fp4x2(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B);
-}
-
-// The eight weights of one packed word, in k order.
-__device__ __forceinline__ void fp4x8(uint32_t w, half2_t* q) {
-    q[0] = fp4x2<0>(w);
-    q[1] = fp4x2<1>(w);
-    q[2] = fp4x2<2>(w);
-    q[3] = fp4x2<3>(w);
-}
-
 __device__ __forceinline__ float xchg32(float v) { return __shfl_xor(v, 32, kWave); }
 __device__ __forceinline__ uint32_t xchg32u(uint32_t v) {
     return __builtin_bit_cast(uint32_t, __shfl_xor(__builtin_bit_cast(int, v), 32, kWave));
@@ -319,14 +295,32 @@ hipError_t launch_fp4_1(Prologue pro, const Fp4Args& a, const Fp4Plan& p, hipStr
 
 }  // namespace
 
+// 1..4 rows: the chunk-owning kernel above.  5..16 rows: the matrix-core kernel with
+// the FP4 weight format (K % 128 == 0), whose K slices need a workspace.
 bool fp4_gemv_supported(int M, int K, int N) {
     Fp4Plan p;
-    return fp4_plan(M, K, N, p);
+    if (M <= 4) return fp4_plan(M, K, N, p);
+    GemvPlan g{};
+    return M <= 16 && K > 0 && K % 128 == 0 && N > 0 && N % 8 == 0 && plan_mfma(M, K, N, g);
+}
+
+size_t fp4_gemv_workspace_bytes(int M, int K, int N) {
+    if (M <= 4 || !fp4_gemv_supported(M, K, N)) return 0;
+    GemvPlan g{};
+    g.groups = K / kGroup;
+    plan_mfma(M, K, N, g);
+    return g.partial_bytes;
 }
 
 hipError_t launch_fp4_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
                            const uint8_t* sc, int M, int K, int N, const float* out_scale, const uint16_t* residual,
-                           uint16_t* y, hipStream_t s) {
+                           uint16_t* y, void* ws, hipStream_t s) {
+    if (M > 4) {
+        GemvPlan g{};
+        g.groups = K / kGroup;
+        if (!fp4_gemv_supported(M, K, N) || !plan_mfma(M, K, N, g)) return hipErrorInvalidValue;
+        return launch_mfma_fp4(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, g, s);
+    }
     Fp4Plan p;
     if (!fp4_plan(M, K, N, p)) return hipErrorInvalidValue;
     Fp4Args a{};

@@ -38,6 +38,13 @@
 // layout is [row][k-block][8] with a 16-byte pad per row, so the B operands of one MFMA
 // (16 rows of one k-block per k-slot) are spread over all LDS banks.  With the SwiGLU
 // prologue silu(g) * u is computed in fp32; fp32 -> fp16 rounds toward zero.
+//
+// FP4 weights (E2M1 codes with E4M3 block scales of 16 along K; template WF = kWFp4).
+// The same tiling and staging, with three differences: the activation is staged in k
+// order without the 1/16 at odd positions; the A operand of MFMA j is the word's eight
+// E2M1 values (v_cvt_scalef32_pk_f16_fp4) times its block scale in fp16 (exact: an E2M1
+// value has 2 significant bits, an E4M3 value 4, and every product is a normal fp16
+// number), so there are no offsets to remove; and there is no group scale to apply.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -50,13 +57,16 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaP = 4;          // groups per batch of weight loads
+constexpr int kWInt4 = 0;          // weight formats
+constexpr int kWFp4 = 1;
 
 struct MfmaArgs {
     const uint16_t* a0;     // g (SwiGLU) or x (identity), row stride lda
     const uint16_t* a1;     // u (SwiGLU) or unused
     int64_t lda;
     const uint4* qw;        // [N][K/32] chunks of 4 words
-    const uint16_t* sc;     // bf16 scales [K/128][N]
+    const uint16_t* sc;     // bf16 scales [K/128][N] (int4)
+    const uint8_t* sc8;     // E4M3 block scales [N][K/16] (FP4)
     int M, K, N;
     int nch;                // K / 32
     int groups;             // K / 128
@@ -81,7 +91,7 @@ __device__ __forceinline__ f16x8_t decode_f16x8_biased(uint32_t w) {
 // DPP row hold the 16 k-blocks of one 128-wide group of that row and share its scale.
 // Must be called with the whole wave active.  Returns the fp16 words in pair order;
 // *esc = 2^E of the group.
-template <int PRO>
+template <int PRO, int WF>
 __device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, bool live, float* esc) {
     const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
     const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
@@ -112,13 +122,30 @@ __device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, bool live, 
     const float down = __builtin_ldexpf(1.0f, -E);
     const float down16 = down * 0.0625f;
     *esc = __builtin_ldexpf(1.0f, E);
+    if (WF == kWFp4)   // k order, as v_cvt_scalef32_pk_f16_fp4 produces the weights
+        return make_uint4(__builtin_bit_cast(uint32_t, pk_f16_rtz(v[0] * down, v[1] * down)),
+                          __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2] * down, v[3] * down)),
+                          __builtin_bit_cast(uint32_t, pk_f16_rtz(v[4] * down, v[5] * down)),
+                          __builtin_bit_cast(uint32_t, pk_f16_rtz(v[6] * down, v[7] * down)));
     return make_uint4(__builtin_bit_cast(uint32_t, pk_f16_rtz(v[0] * down, v[4] * down)),
                       __builtin_bit_cast(uint32_t, pk_f16_rtz(v[1] * down16, v[5] * down16)),
                       __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2] * down, v[6] * down)),
                       __builtin_bit_cast(uint32_t, pk_f16_rtz(v[3] * down16, v[7] * down16)));
 }
 
-template <int TPW, int PRO>
+// The A operand of one MFMA for FP4 weights: the eight values of word w times the
+// block scale s (fp16, exact).
+__device__ __forceinline__ f16x8_t fp4_operand(uint32_t w, _Float16 s) {
+    half2_t q[4];
+    fp4x8(w, q);
+    const half2_t s2 = {s, s};
+    return __builtin_bit_cast(f16x8_t, make_uint4(__builtin_bit_cast(uint32_t, q[0] * s2),
+                                                  __builtin_bit_cast(uint32_t, q[1] * s2),
+                                                  __builtin_bit_cast(uint32_t, q[2] * s2),
+                                                  __builtin_bit_cast(uint32_t, q[3] * s2)));
+}
+
+template <int TPW, int PRO, int WF>
 __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int W = blockDim.x >> 6;
@@ -144,8 +171,14 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
             for (int t = 0; t < TPW; ++t) {
                 const int n = min(nw0 + t * 16 + lm, a.N - 1);
                 w[p][t] = a.qw[size_t(n) * a.nch + 4 * g + ls];
-                const int ns = min(nw0 + t * 16 + 4 * ls, a.N - 4);
-                sv[p][t] = *reinterpret_cast<const uint2*>(a.sc + size_t(g) * a.N + ns);
+                if (WF == kWFp4) {
+                    // the two E4M3 scales of this lane's chunk (column n, chunk 4g + ls)
+                    sv[p][t].x = *reinterpret_cast<const uint16_t*>(a.sc8 + size_t(n) * (a.K / 16) + 2 * (4 * g + ls));
+                    sv[p][t].y = 0;
+                } else {
+                    const int ns = min(nw0 + t * 16 + 4 * ls, a.N - 4);
+                    sv[p][t] = *reinterpret_cast<const uint2*>(a.sc + size_t(g) * a.N + ns);
+                }
             }
         }
     };
@@ -188,7 +221,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
             const int it = base + u * nthr + tid;
             const int m = it / nkb, kb = it % nkb;
             float esc;
-            const uint4 h = stage_item_mfma<PRO>(gv[u], uv[u], it < nitems && m < a.M, &esc);
+            const uint4 h = stage_item_mfma<PRO, WF>(gv[u], uv[u], it < nitems && m < a.M, &esc);
             if (it < nitems) {
                 act_s[m * rs + kb] = h;
                 if ((kb & 15) == 0) esc_s[m * ng + (kb >> 4)] = esc;
@@ -228,29 +261,45 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
         f32x4_t bias[kMfmaP];
 #pragma unroll
         for (int p = 0; p < kMfmaP; ++p) bias[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (WF == kWInt4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int p = 0; p < kMfmaP; ++p)
-                bias[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(negoff, bop[p][j], bias[p], 0, 0, 0);
+                for (int p = 0; p < kMfmaP; ++p)
+                    bias[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(negoff, bop[p][j], bias[p], 0, 0, 0);
+        }
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             f32x4_t d[kMfmaP];
 #pragma unroll
             for (int p = 0; p < kMfmaP; ++p) d[p] = bias[p];
+            _Float16 fs[kMfmaP][2];
+            if (WF == kWFp4) {
+#pragma unroll
+                for (int p = 0; p < kMfmaP; ++p) {
+                    fs[p][0] = (_Float16)e4m3_to_f32(sv[p][t].x & 0xFFu);
+                    fs[p][1] = (_Float16)e4m3_to_f32(sv[p][t].x >> 8);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int p = 0; p < kMfmaP; ++p) {
                     const uint32_t wd = j == 0 ? w[p][t].x : j == 1 ? w[p][t].y : j == 2 ? w[p][t].z : w[p][t].w;
-                    d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(decode_f16x8_biased(wd), bop[p][j], d[p], 0, 0, 0);
+                    const f16x8_t aop = WF == kWFp4 ? fp4_operand(wd, fs[p][j >> 1]) : decode_f16x8_biased(wd);
+                    d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[p][j], d[p], 0, 0, 0);
                 }
 #pragma unroll
             for (int p = 0; p < kMfmaP; ++p) {
-                out[t][0] = fmaf(bf16_lo(sv[p][t].x) * e[p], d[p][0], out[t][0]);
-                out[t][1] = fmaf(bf16_hi(sv[p][t].x) * e[p], d[p][1], out[t][1]);
-                out[t][2] = fmaf(bf16_lo(sv[p][t].y) * e[p], d[p][2], out[t][2]);
-                out[t][3] = fmaf(bf16_hi(sv[p][t].y) * e[p], d[p][3], out[t][3]);
+                if (WF == kWFp4) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) out[t][r] = fmaf(e[p], d[p][r], out[t][r]);
+                } else {
+                    out[t][0] = fmaf(bf16_lo(sv[p][t].x) * e[p], d[p][0], out[t][0]);
+                    out[t][1] = fmaf(bf16_hi(sv[p][t].x) * e[p], d[p][1], out[t][1]);
+                    out[t][2] = fmaf(bf16_lo(sv[p][t].y) * e[p], d[p][2], out[t][2]);
+                    out[t][3] = fmaf(bf16_hi(sv[p][t].y) * e[p], d[p][3], out[t][3]);
+                }
             }
         }
     };
@@ -302,16 +351,19 @@ hipError_t launch_k(Kern k, dim3 grid, int threads, size_t lds, hipStream_t s, c
 
 }  // namespace
 
-hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
-                       const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
-                       const float* out_scale, const uint16_t* residual, uint16_t* y,
-                       void* ws, const GemvPlan& p, hipStream_t s) {
+namespace {
+
+template <int WF>
+hipError_t launch_mfma_wf(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
+                          const uint16_t* sc, const uint8_t* sc8, int M, int K, int N, const float* out_scale,
+                          const uint16_t* residual, uint16_t* y, void* ws, const GemvPlan& p, hipStream_t s) {
     MfmaArgs a{};
     a.a0 = a0;
     a.a1 = a1;
     a.lda = lda;
     a.qw = reinterpret_cast<const uint4*>(qw);
     a.sc = sc;
+    a.sc8 = sc8;
     a.M = M;
     a.K = K;
     a.N = N;
@@ -329,10 +381,26 @@ hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     const int threads = p.waves * kWave;
     // one 16-column tile per wave (two per wave measured slower: more registers and a
     // K split for the same workgroup count)
-    hipError_t e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU>, grid, threads, p.lds_bytes, s, a)
-                                  : launch_k(w4_gemv_mfma_kernel<1, kIdentity>, grid, threads, p.lds_bytes, s, a);
+    hipError_t e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF>, grid, threads, p.lds_bytes, s, a)
+                                  : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF>, grid, threads, p.lds_bytes, s, a);
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_splitk_finish(a.partial, p.splits, int64_t(16) * a.npad, a.npad, M, N, out_scale, residual, y, s);
+}
+
+}  // namespace
+
+hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
+                       const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
+                       const float* out_scale, const uint16_t* residual, uint16_t* y,
+                       void* ws, const GemvPlan& p, hipStream_t s) {
+    return launch_mfma_wf<kWInt4>(pro, a0, a1, lda, qw, sc, nullptr, M, K, N, out_scale, residual, y, ws, p, s);
+}
+
+hipError_t launch_mfma_fp4(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
+                           const uint32_t* qw, const uint8_t* sc8, int M, int K, int N,
+                           const float* out_scale, const uint16_t* residual, uint16_t* y,
+                           void* ws, const GemvPlan& p, hipStream_t s) {
+    return launch_mfma_wf<kWFp4>(pro, a0, a1, lda, qw, nullptr, sc8, M, K, N, out_scale, residual, y, ws, p, s);
 }
 
 }  // namespace fdec

@@ -169,20 +169,30 @@ def _fp4(f, K=1024, N=512, q=None, s=None):
 def test_fp4_gemv_validation(L, inject):
     f = Fake()
 
-    def call(W=None, g=None, u=None, ld=None, scale=None, res=None, M=1, y=None):
+    def call(W=None, g=None, u=None, ld=None, scale=None, res=None, M=1, y=None, ws=None, wsb=None):
         W = _fp4(f) if W is None else W
+        need = L.fdec_fp4_gemv_workspace_bytes(M, W.K, W.N)
         return L.fdec_swiglu_fp4_gemv(f() if g is None else g, f() if u is None else u, W.K if ld is None else ld,
-                                      ctypes.byref(W), scale, res, M, f() if y is None else y, None)
+                                      ctypes.byref(W), scale, res, M, f() if y is None else y,
+                                      f(max(need, 16)) if ws is None else ws, need if wsb is None else wsb, None)
 
-    assert L.fdec_swiglu_fp4_gemv(f(), f(), 1024, None, None, None, 1, f(), None) == NULL
+    assert L.fdec_swiglu_fp4_gemv(f(), f(), 1024, None, None, None, 1, f(), 0, 0, None) == NULL
     assert call(W=_fp4(f, K=1000)) == SHAPE              # K % 32
     assert call(W=_fp4(f, N=500)) == SHAPE               # N % 8
     assert call(W=_fp4(f, q=0)) == NULL
     assert call(W=_fp4(f, s=f() + 2)) == ALIGN
     assert call(M=0) == SHAPE
     assert call(M=17) == SHAPE
-    assert call(M=5) == UNSUP                            # the FP4 kernel takes M <= 4
-    assert call(W=_fp4(f, K=16416, N=8)) == UNSUP        # and K <= 16384
+    assert call(W=_fp4(f, K=16416, N=8)) == UNSUP        # M <= 4 takes K <= 16384
+    assert call(M=5, W=_fp4(f, K=96, N=8)) == UNSUP      # M > 4 takes K % 128 == 0
+    assert L.fdec_fp4_gemv_workspace_bytes(1, 9216, 2560) == 0
+    need = L.fdec_fp4_gemv_workspace_bytes(16, 9216, 2560)
+    assert need > 0                                      # the matrix-core kernel's K slices
+    W = _fp4(f, K=9216, N=2560)
+    assert call(M=16, W=W, ld=9216, wsb=need - 1) == WS
+    assert call(M=16, W=W, ld=9216, ws=0) == NULL
+    assert call(M=16, W=W, ld=9216, ws=f() + 8) == ALIGN
+    assert call(M=16, W=W, ld=9216) == HIP
     assert call(ld=1000) == SHAPE
     assert call(g=f() + 2) == ALIGN
     assert call(u=0) == NULL
@@ -195,8 +205,8 @@ def test_fp4_gemv_validation(L, inject):
     assert call(M=4, ld=2048) == HIP
     # identity prologue and the decode hook
     W = _fp4(f, K=96, N=8)
-    assert L.fdec_fp4_gemv(f(), ctypes.byref(W), None, None, 1, f(), None) == HIP
-    assert L.fdec_fp4_gemv(f(), None, None, None, 1, f(), None) == NULL
+    assert L.fdec_fp4_gemv(f(), ctypes.byref(W), None, None, 1, f(), 0, 0, None) == HIP
+    assert L.fdec_fp4_gemv(f(), None, None, None, 1, f(), 0, 0, None) == NULL
     assert L.fdec_fp4_dequant(ctypes.byref(W), 0, None) == NULL
     assert L.fdec_fp4_dequant(ctypes.byref(W), W.qweight + 64, None) == ALIAS
     assert L.fdec_fp4_dequant(ctypes.byref(W), f(), None) == HIP

@@ -98,7 +98,7 @@ def test_fp4_gemv_exact_case_and_repeatability():
 
 
 def test_fp4_gemv_rejects_what_it_cannot_do():
-    inp = synth.swiglu_fp4_gemv_inputs(5, 256, 64, seed=1)
+    inp = synth.swiglu_fp4_gemv_inputs(5, 96, 64, seed=1)          # 5..16 rows need K % 128 == 0
     g, u, W = F.from_bits(inp.g), F.from_bits(inp.u), dev_w(inp.W)
     with pytest.raises(F.FdecError) as e:
         F.swiglu_fp4_gemv(g, u, W)
@@ -107,3 +107,34 @@ def test_fp4_gemv_rejects_what_it_cannot_do():
     with pytest.raises(F.FdecError) as e:
         F.swiglu_fp4_gemv(F.from_bits(inp.g), F.from_bits(inp.u), dev_w(inp.W))
     assert e.value.status == UNSUP
+
+
+
+# ---------------------------------------------------------------------------
+# 5..16 rows: the matrix-core kernel with FP4 weights
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", [(16, 14336, 4096), (16, 9216, 2560), (8, 4096, 1000), (5, 256, 24),
+                                   (12, 1024, 512), (16, 4096, 28672)])
+def test_fp4_gemv_matrix_core_shapes(M, K, N):
+    say(f"[fp4 gemv, matrix cores] M={M} K={K} N={N}")
+    inp = synth.swiglu_fp4_gemv_inputs(M, K, N, seed=M * 5 + K + N, out_scale=0.5, with_residual=True)
+    w = assert_close(run(inp, 0.5, True), want(inp, 0.5, True), "y with residual")
+    say(f"  worst err/bound {w:.3f}")
+    assert_close(run(inp, None, False), want(inp, None, False), "y, NULL scale")
+    if K <= 4096:
+        assert_close(run(inp, 0.5, False, swiglu=False), want(inp, 0.5, False, swiglu=False), "identity prologue")
+
+
+def test_fp4_gemv_matrix_core_exact_case():
+    say("[fp4 gemv, matrix cores] integer activations, power-of-two scales, M=16: bit-exact")
+    rng = np.random.default_rng(13)
+    M, K, N = 16, 9216, 264
+    x = synth.f32_to_bf16_bits(rng.integers(-3, 4, size=(M, K)).astype(np.float32))
+    sc = rng.choice(np.array([0x20, 0x28, 0x30], dtype=np.uint8), size=(N, K // 16))   # 2^-3, 2^-2, 2^-1
+    W = synth.FP4(rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint32), sc)
+    xd, Wd, s = F.from_bits(x), dev_w(W), F.scalar(0.5)
+    y1 = F.fp4_gemv(xd, Wd, s)
+    y2 = F.fp4_gemv(xd, Wd, s)
+    torch.cuda.synchronize()
+    assert_bits_equal(F.to_bits(y1), O.fp4_gemv(x, W.qweight, W.scales, 0.5), "exact case")
+    assert_bits_equal(F.to_bits(y1), F.to_bits(y2), "repeat")
