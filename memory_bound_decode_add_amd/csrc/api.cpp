@@ -432,6 +432,8 @@ int update_graph(fdec_graph G, int form, const fdec_mlp_layer* layers, int n_lay
     }
     (void)hipGraphDestroy(G->graph);
     G->graph = ng;
+    size_t nodes = 0;                  // HIP may take a chain with other kernels (and nodes)
+    if (hipGraphGetNodes(ng, nullptr, &nodes) == hipSuccess) G->kernels = int(nodes);
     return ok();
 }
 

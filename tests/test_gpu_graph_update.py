@@ -146,6 +146,14 @@ def test_graph_update_with_other_kernels_keeps_a_consistent_graph():
         F.set_gemv_split(0)
     say(f"  update {'taken' if took else 'refused'}")
     if took:
+        # the split-K chain has a finish kernel after each K-sliced GEMV
+        F.set_gemv_split(2)
+        try:
+            fresh = F.MlpGraph(lay_b, F.MlpBuffers.empty(M, H, I, out_is_x=True))
+            assert graph.kernel_count == fresh.kernel_count
+            fresh.close()
+        finally:
+            F.set_gemv_split(0)
         replay_and_check(graph, bb, inp_b, want_b_split, "after a taken update")
     else:
         replay_and_check(graph, ba, inp_a, want_a, "after a refused update")
