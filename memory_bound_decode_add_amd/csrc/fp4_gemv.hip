@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args 
     for (int j = 0; j < CH; ++j) {
         const int col = min(h * CH + j, ncols - 1);
         const uint32_t sp = *reinterpret_cast<const uint16_t*>(sc_s + (s0 - a0) + size_t(col) * sb + 2 * cc);
-        const float s0 = e4m3_to_f32(sp & 0xFFu), s1 = e4m3_to_f32(sp >> 8);
+        const float bs0 = e4m3_to_f32(sp & 0xFFu), bs1 = e4m3_to_f32(sp >> 8);   // block scales
         half2_t q[16];
         fp4x8(wv[j].x, q);
         fp4x8(wv[j].y, q + 4);
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args 
                 d0 = dot2(q[i], __builtin_bit_cast(half2_t, act[m][i]), d0);
                 d1 = dot2(q[8 + i], __builtin_bit_cast(half2_t, act[m][8 + i]), d1);
             }
-            part[m][j] = valid ? fmaf(d0, s0, d1 * s1) * e2[m] : 0.f;
+            part[m][j] = valid ? fmaf(d0, bs0, d1 * bs1) * e2[m] : 0.f;
         }
     }
 
