@@ -9,7 +9,7 @@
 // read once and h and y written once (8 bytes per element, the minimum).  A row is
 // spread over 1 to 8 waves so that no lane holds more than 4 chunks of 16 bytes (8
 // bf16) of each of x, r and w, which keeps registers low enough for 5-8 waves per
-// SIMD to hide HBM latency.  Lane chunks are strided by 64 so every load and store
+// SIMD to hide HBM latency (rows of 449..512 chunks take eight waves of one chunk).  Lane chunks are strided by 64 so every load and store
 // instruction of a wave touches 1 KB of contiguous memory.  The sum of squares is
 // reduced with cross-lane shuffles, and across the waves of a row through LDS.
 // h may alias r (in-place residual update): each lane reads its chunks of r before it
@@ -118,7 +118,9 @@ hipError_t launch_add_rmsnorm(const uint16_t* x, const uint16_t* r, const uint16
         case 3: return launch_nc<3, 1>(x, r, w, eps, M, H, h, y, s);
         case 4: return launch_nc<4, 1>(x, r, w, eps, M, H, h, y, s);
         case 5: case 6: return launch_nc<3, 2>(x, r, w, eps, M, H, h, y, s);
-        case 7: case 8: return launch_nc<4, 2>(x, r, w, eps, M, H, h, y, s);
+        // 449..512 chunks (H = 4096): eight waves of one chunk per lane measured 3 % faster
+        // at 8192 x 4096 than two waves of four
+        case 7: case 8: return launch_nc<1, 8>(x, r, w, eps, M, H, h, y, s);
         case 9: case 10: case 11: case 12: return launch_nc<3, 4>(x, r, w, eps, M, H, h, y, s);
         case 13: case 14: case 15: case 16: return launch_nc<4, 4>(x, r, w, eps, M, H, h, y, s);
         default: return launch_nc<4, 8>(x, r, w, eps, M, H, h, y, s);
