@@ -112,6 +112,16 @@ hipError_t launch_add_rmsnorm(const uint16_t* x, const uint16_t* r, const uint16
     if (M == 0) return hipSuccess;
     // at most 4 chunks per lane (x, r and w in registers), more waves per row beyond that
     const int per_lane = (H / 8 + kWave - 1) / kWave;   // 1..32 for H <= 16384
+    if (M <= 64 && per_lane <= 8) {
+        // a few rows (decode): one chunk per lane, the row spread over up to eight waves,
+        // so that a row's loads are spread over as many waves as possible
+        switch (per_lane) {
+            case 1: return launch_nc<1, 1>(x, r, w, eps, M, H, h, y, s);
+            case 2: return launch_nc<1, 2>(x, r, w, eps, M, H, h, y, s);
+            case 3: case 4: return launch_nc<1, 4>(x, r, w, eps, M, H, h, y, s);
+            default: return launch_nc<1, 8>(x, r, w, eps, M, H, h, y, s);
+        }
+    }
     switch (per_lane) {
         case 1: return launch_nc<1, 1>(x, r, w, eps, M, H, h, y, s);
         case 2: return launch_nc<2, 1>(x, r, w, eps, M, H, h, y, s);

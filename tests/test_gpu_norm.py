@@ -42,6 +42,18 @@ def test_add_rmsnorm_shapes(M, H):
     assert_close(y, ry, "y")
 
 
+@pytest.mark.parametrize("M", [1, 3, 64, 65])
+@pytest.mark.parametrize("H", [8, 512, 1032, 1536, 2048, 3072, 3592, 4096])
+def test_add_rmsnorm_decode_batches(M, H):
+    """Up to 64 rows use one chunk per lane with the row over 1..8 waves; 65 rows the
+    general shapes: every row width class on both sides of the switch."""
+    inp = synth.add_rmsnorm_inputs(M, H, seed=7 * M + H)
+    h, y = run(inp)
+    rh, ry = O.add_rmsnorm(inp.x, inp.r, inp.w, inp.eps)
+    assert_bits_equal(h, rh, f"h M={M} H={H}")
+    assert_close(y, ry, f"y M={M} H={H}")
+
+
 def test_add_rmsnorm_in_place_residual():
     say("[norm] in place")
     inp = synth.add_rmsnorm_inputs(33, 2048, seed=4)
