@@ -139,6 +139,19 @@ def bench_gemv(torch, F, synth, steps, warmup, n_sets):
     us = elapsed / steps * 1e6
     gbps = bytes_per_call / (elapsed / steps) / 1e9
 
+    # the spread: 20 separately timed rounds of R back-to-back calls, each followed by an
+    # untimed 12 MB copy (so that clock and cache drift hit every round alike)
+    cpy_src = torch.randn(int(12.2e6 / 8), device="cuda")
+    cpy_dst = torch.empty_like(cpy_src)
+    rounds = []
+    for _ in range(20):
+        rounds.append(timer(g_main.replay) / R * 1e6)
+        torch.neg(cpy_src, out=cpy_dst)
+    torch.cuda.synchronize()
+    del cpy_src, cpy_dst
+    spread = {"rounds": len(rounds), "calls_per_round": R, "median_us": float(np.median(rounds)),
+              "p10_us": float(np.percentile(rounds, 10)), "p90_us": float(np.percentile(rounds, 90))}
+
     # a plain copy kernel of known size, for scaling the HBM byte counters of a profiled run
     src = torch.randn(CALIB_FLOATS, device="cuda")
     dst = torch.empty_like(src)
@@ -155,7 +168,7 @@ def bench_gemv(torch, F, synth, steps, warmup, n_sets):
     plan = {"workspace_bytes": F.gemv_workspace_bytes(M, K, N)}
     return {"us_per_call": us, "gbps": gbps, "elapsed_s": elapsed, "bytes_per_call": bytes_per_call,
             "warmup_steps_run": done, "graph_steps": R, "eager_call_us_median": float(np.median(lat)) * 1e6,
-            **plan}
+            "rounds": spread, **plan}
 
 
 def bench_repeat(torch, timer, fns, n_rep):
