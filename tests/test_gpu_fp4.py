@@ -138,3 +138,15 @@ def test_fp4_gemv_matrix_core_exact_case():
     torch.cuda.synchronize()
     assert_bits_equal(F.to_bits(y1), O.fp4_gemv(x, W.qweight, W.scales, 0.5), "exact case")
     assert_bits_equal(F.to_bits(y1), F.to_bits(y2), "repeat")
+
+
+@pytest.mark.parametrize("M,K,N", [(3, 1536, 264), (8, 1024, 512)])
+def test_fp4_gemv_strided_gate_up_halves(M, K, N):
+    """g and u as the two halves of one [M, 2K] gate_up output (row stride 2K), on the
+    chunk-owning kernel (M = 3) and the matrix-core kernel (M = 8)."""
+    say(f"[fp4 gemv] strided g/u, M={M} K={K} N={N}")
+    inp = synth.swiglu_fp4_gemv_inputs(M, K, N, seed=91 + M, out_scale=0.5)
+    gu = torch.cat([F.from_bits(inp.g), F.from_bits(inp.u)], dim=1)      # [M, 2K]
+    y = F.swiglu_fp4_gemv(gu[:, :K], gu[:, K:], dev_w(inp.W), F.scalar(0.5))
+    torch.cuda.synchronize()
+    assert_close(F.to_bits(y), want(inp, 0.5, False), "y")
