@@ -414,13 +414,46 @@ def cpu_baseline(synth, seconds):
                       f"thread, the fp64 matmul on {blas} BLAS threads)"}
 
 
+def profile_calls(torch, F, synth):
+    """A few eager calls of each GEMV kernel family, for hardware-counter runs: the column
+    kernel at the metric's shape, the matrix-core kernel on the Llama-3-8B-sized M=16
+    projections (gate_up identity, down SwiGLU with its finish kernel), and the FP4 kernels."""
+    sc = F.scalar(0.5)
+    for M, K, N, pro, n in ((1, 9216, 2560, "swiglu", 24), (16, 4096, 28672, "id", 4), (16, 14336, 4096, "swiglu", 4)):
+        sets = []
+        for i in range(n):
+            inp = synth.swiglu_gemv_inputs(M, K, N, seed=i)
+            sets.append((F.from_bits(inp.g), F.from_bits(inp.u), F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales),
+                         torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+        ws = F.workspace(F.gemv_workspace_bytes(M, K, N))
+        for _ in range(2):
+            for g, u, W, y in sets:
+                if pro == "swiglu":
+                    F.swiglu_w4_gemv(g, u, W, sc, out=y, ws=ws)
+                else:
+                    F.w4_gemv(g, W, sc, out=y, ws=ws)
+        torch.cuda.synchronize()
+        del sets, ws
+    for M in (1, 16):
+        inp = synth.swiglu_fp4_gemv_inputs(M, 9216, 2560, seed=M)
+        g, u = F.from_bits(inp.g), F.from_bits(inp.u)
+        W = F.FP4Weight.from_numpy(inp.W.qweight, inp.W.scales)
+        y = torch.empty((M, 2560), dtype=torch.bfloat16, device="cuda")
+        ws = F.workspace(F.fp4_gemv_workspace_bytes(M, 9216, 2560))
+        for _ in range(8):
+            F.swiglu_fp4_gemv(g, u, W, sc, out=y, ws=ws)
+    torch.cuda.synchronize()
+    log("[bench] profile calls done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--sets", type=int, default=48, help="rotating input sets (48 x 12.2 MB = 586 MB)")
-    ap.add_argument("--only", choices=["gemv", "all"], default="all")
+    ap.add_argument("--only", choices=["gemv", "all", "profile"], default="all",
+                    help="profile: a few calls of each GEMV kernel family and exit (for counter runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -435,6 +468,9 @@ def main():
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
     F.lib()   # fail loudly if the HIP library is missing
+    if a.only == "profile":
+        profile_calls(torch, F, synth)
+        return
 
     res = bench_gemv(torch, F, synth, a.steps, a.warmup, a.sets)
     log(f"[bench] gemv: {res['us_per_call']:.3f} us/call, {res['gbps']:.1f} GB/s")
