@@ -202,30 +202,44 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     const int kbase = g0 * 128;
     constexpr int UMAX = PRO == kSwiGLU ? 12 : 24;
     const int nthr = blockDim.x;
+    // Item it has row it / nkb and k-block it % nkb.  A thread's items are nthr apart, so
+    // after one division per round the pair is advanced by the (uniform) quotient and
+    // remainder of nthr / nkb.
+    const int qn = nthr / nkb, rn = nthr - qn * nkb;
+    auto advance = [&](int& m, int& kb) {
+        kb += rn;
+        m += qn;
+        if (kb >= nkb) {
+            kb -= nkb;
+            ++m;
+        }
+    };
     uint4 gv[UMAX], uv[UMAX];
     auto load_items = [&](int base) {
+        int m = (base + tid) / nkb, kb = base + tid - m * nkb;
 #pragma unroll
         for (int u = 0; u < UMAX; ++u) {
             if (base + u * nthr >= nitems) break;                   // uniform
-            const int it = min(base + u * nthr + tid, nitems - 1);
-            const int m = min(it / nkb, a.M - 1);
-            const size_t off = size_t(m) * a.lda + kbase + (it % nkb) * 8;
+            // rows past M (and items past the end) read row M - 1: in bounds, value unused
+            const size_t off = size_t(min(m, a.M - 1)) * a.lda + kbase + kb * 8;
             gv[u] = *reinterpret_cast<const uint4*>(a.a0 + off);
             uv[u] = PRO == kSwiGLU ? *reinterpret_cast<const uint4*>(a.a1 + off) : make_uint4(0, 0, 0, 0);
+            advance(m, kb);
         }
     };
     auto stage_items = [&](int base) {
+        int m = (base + tid) / nkb, kb = base + tid - m * nkb;
 #pragma unroll
         for (int u = 0; u < UMAX; ++u) {
             if (base + u * nthr >= nitems) break;                   // uniform: the whole wave stays active
-            const int it = base + u * nthr + tid;
-            const int m = it / nkb, kb = it % nkb;
+            const bool in = base + u * nthr + tid < nitems;
             float esc;
-            const uint4 h = stage_item_mfma<PRO, WF>(gv[u], uv[u], it < nitems && m < a.M, &esc);
-            if (it < nitems) {
+            const uint4 h = stage_item_mfma<PRO, WF>(gv[u], uv[u], in && m < a.M, &esc);
+            if (in) {
                 act_s[m * rs + kb] = h;
                 if ((kb & 15) == 0) esc_s[m * ng + (kb >> 4)] = esc;
             }
+            advance(m, kb);
         }
     };
     for (int base = 0; base < nitems; base += UMAX * nthr) {       // uniform trip count
