@@ -172,6 +172,10 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
 constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;

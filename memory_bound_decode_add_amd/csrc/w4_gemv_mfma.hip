@@ -90,9 +90,10 @@ __device__ __forceinline__ f16x8_t decode_f16x8_biased(uint32_t w) {
 // One staging item: 8 consecutive activation values of one row.  The 16 lanes of a
 // DPP row hold the 16 k-blocks of one 128-wide group of that row and share its scale.
 // Must be called with the whole wave active.  Returns the fp16 words in pair order;
-// *esc = 2^E of the group.
+// *esc = 2^E of the group.  Rows past M need no zeroing: row m of the activation only
+// reaches output row m, which is never stored.
 template <int PRO, int WF>
-__device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, bool live, float* esc) {
+__device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, float* esc) {
     const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
     const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
     float v[8];
@@ -108,16 +109,15 @@ __device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, bool live, 
     }
     float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        v[j] = live ? v[j] : 0.f;
-        mx = fmaxf(mx, fabsf(v[j]));
-    }
-    mx = fmaxf(mx, dpp<kQuadSwap1>(mx));
-    mx = fmaxf(mx, dpp<kQuadSwap2>(mx));
-    mx = fmaxf(mx, dpp<kRowRor4>(mx));
-    mx = fmaxf(mx, dpp<kRowRor8>(mx));             // the group's largest magnitude
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+    // magnitudes order as their bit patterns do, so the group max is an unsigned max
+    uint32_t mb = __builtin_bit_cast(uint32_t, mx);
+    mb = max(mb, dpp_u32<kQuadSwap1>(mb));
+    mb = max(mb, dpp_u32<kQuadSwap2>(mb));
+    mb = max(mb, dpp_u32<kRowRor4>(mb));
+    mb = max(mb, dpp_u32<kRowRor8>(mb));           // the group's largest magnitude
     int e = 0;
-    (void)__builtin_frexpf(mx, &e);
+    (void)__builtin_frexpf(__builtin_bit_cast(float, mb), &e);
     const int E = min(max(e - 15, -126), 127);
     const float down = __builtin_ldexpf(1.0f, -E);
     const float down16 = down * 0.0625f;
@@ -232,10 +232,9 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
 #pragma unroll
         for (int u = 0; u < UMAX; ++u) {
             if (base + u * nthr >= nitems) break;                   // uniform: the whole wave stays active
-            const bool in = base + u * nthr + tid < nitems;
             float esc;
-            const uint4 h = stage_item_mfma<PRO, WF>(gv[u], uv[u], in && m < a.M, &esc);
-            if (in) {
+            const uint4 h = stage_item_mfma<PRO, WF>(gv[u], uv[u], &esc);
+            if (base + u * nthr + tid < nitems) {
                 act_s[m * rs + kb] = h;
                 if ((kb & 15) == 0) esc_s[m * ng + (kb >> 4)] = esc;
             }
