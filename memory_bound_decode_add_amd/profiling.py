@@ -81,28 +81,39 @@ def write_trace_text(entries, command: str, out: str, top: int = 25):
 
 
 def counter_means(path: str, counter: str):
+    """Mean counter value per (kernel name, grid size): one kernel launched at several
+    sizes gives several entries."""
     rows = list(csv.DictReader(open(path)))
     acc = defaultdict(list)
     for r in rows:
         if r["Counter_Name"] == counter:
-            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+            acc[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
     return {k: statistics.mean(v) for k, v in acc.items()}
 
 
 def _pick(means: dict, sub: str):
-    hits = [(k, v) for k, v in means.items() if sub in k]
+    hits = [(k, v) for k, v in means.items() if sub in k[0]]
     if len(hits) != 1:
-        raise SystemExit(f"'{sub}' matches {len(hits)} kernels: {[k[:80] for k, _ in hits]}")
+        raise SystemExit(f"'{sub}' matches {len(hits)} kernel shapes: {[(k[0][:80], k[1]) for k, _ in hits]}")
     return hits[0]
+
+
+def _pick_largest(means: dict, sub: str):
+    """The largest-grid launch of the kernels matching sub: the calibration copy is the
+    largest copy a profiled run makes (smaller copies of the same kernel may run too)."""
+    hits = [(k, v) for k, v in means.items() if sub in k[0]]
+    if not hits:
+        raise SystemExit(f"'{sub}' matches no kernel")
+    return max(hits, key=lambda kv: kv[0][1])
 
 
 def traffic(a):
     fetch = counter_means(a.fetch, "FETCH_SIZE")
     write = counter_means(a.write, "WRITE_SIZE")
-    kf, f_k = _pick(fetch, a.kernel)
-    kw, w_k = _pick(write, a.kernel)
-    _, f_c = _pick(fetch, a.copy)
-    _, w_c = _pick(write, a.copy)
+    (kf, _), f_k = _pick(fetch, a.kernel)
+    _, w_k = _pick(write, a.kernel)
+    _, f_c = _pick_largest(fetch, a.copy)
+    _, w_c = _pick_largest(write, a.copy)
     ff = a.copy_read_bytes / (f_c * 1024.0)
     fw = a.copy_write_bytes / (w_c * 1024.0)
     hbm = f_k * 1024.0 * ff + w_k * 1024.0 * fw
