@@ -237,11 +237,11 @@ def bench_extras(torch, F, synth, n_sets_gemv):
 
     # batch sweep at the metric's K and N: the same 48 rotating weight sets, M rows of
     # seeded N(0,1) activations, one graph per batch size; M <= 4 runs the column kernel,
-    # 5 <= M <= 16 the matrix-core kernel
-    log("[bench] batch sweep M=1..16 at K=9216 N=2560")
+    # 5 <= M <= 16 the matrix-core kernel, M = 32 and 64 two and four 16-row blocks of it
+    log("[bench] batch sweep M=1..64 at K=9216 N=2560")
     gen = torch.Generator().manual_seed(1234)
     sweep = {}
-    for Mb in (1, 2, 3, 4, 5, 8, 12, 16):
+    for Mb in (1, 2, 3, 4, 5, 8, 12, 16, 32, 64):
         gb = torch.randn(Mb, K, generator=gen).to(torch.bfloat16).cuda()
         ub = torch.randn(Mb, K, generator=gen).to(torch.bfloat16).cuda()
         ys = [torch.empty((Mb, N), dtype=torch.bfloat16, device="cuda") for _ in gsets]
@@ -250,7 +250,8 @@ def bench_extras(torch, F, synth, n_sets_gemv):
         t = bench_repeat(torch, timer, fns, 5) / len(gsets)
         b = T.swiglu_w4_gemv_bytes(Mb, K, N)
         sweep[f"M{Mb}"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS,
-                           "kernel": "column" if Mb <= 4 else "matrix-core"}
+                           "kernel": "column" if Mb <= 4 else "matrix-core" if Mb <= 16 else
+                           f"matrix-core x {(Mb + 15) // 16} row blocks"}
         del gb, ub, ys, wsb
     out["batch_sweep_swiglu_w4_gemv_9216x2560"] = sweep
     del gsets

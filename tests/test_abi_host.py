@@ -74,7 +74,12 @@ def test_workspace_queries(L):
     assert L.fdec_unfused_gemv_workspace_bytes(0, 1, 9216, 2560) == 94_371_840
     assert L.fdec_unfused_gemv_workspace_bytes(0, 2, 9216, 2560) == 0     # M > 1 unsupported
     assert L.fdec_unfused_gemv_workspace_bytes(1, 1, 9216, 2560) >= 2 * 9216 * 2
-    assert L.fdec_w4_gemv_workspace_bytes(17, 1024, 512) == 0            # invalid shape
+    assert L.fdec_w4_gemv_workspace_bytes(65, 1024, 512) == 0            # invalid shape
+    assert L.fdec_w4_gemv_workspace_bytes(0, 1024, 512) == 0
+    # above 16 rows the blocks of 16 share one workspace: the largest block's
+    for M in (17, 32, 40, 64):
+        assert L.fdec_w4_gemv_workspace_bytes(M, 9216, 2560) == max(
+            L.fdec_w4_gemv_workspace_bytes(16, 9216, 2560), L.fdec_w4_gemv_workspace_bytes(M % 16 or 16, 9216, 2560))
     assert L.fdec_w4_gemv_workspace_bytes(1, 1000, 512) == 0
     # the fused GEMV's own workspace stays far below the product it avoids
     assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) < 0.02 * 94_371_840
@@ -140,7 +145,7 @@ def test_gemv_validation(L, inject):
     assert _gemv(L, f, W=_w4(f, N=500)) == SHAPE
     assert _gemv(L, f, W=_w4(f, q=0)) == NULL
     assert _gemv(L, f, M=0) == SHAPE
-    assert _gemv(L, f, M=17) == SHAPE
+    assert _gemv(L, f, M=65) == SHAPE
     assert _gemv(L, f, ld=1000) == SHAPE
     assert _gemv(L, f, ld=1028) == SHAPE
     assert _gemv(L, f, g=f() + 2) == ALIGN

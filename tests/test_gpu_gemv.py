@@ -100,6 +100,27 @@ def test_swiglu_gemv_ragged_shapes_with_residual(M, K, N):
     assert_close(y, ref, f"M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N", [(17, 1024, 520), (32, 9216, 2560), (40, 2048, 1032), (64, 4096, 776)])
+def test_swiglu_gemv_row_blocks_with_residual(M, K, N):
+    # above 16 rows the call runs blocks of 16 rows (the last one shorter); each block
+    # must equal the same rows run on their own, and the whole must match the oracle
+    say(f"[gemv] row blocks M={M} K={K} N={N} with residual")
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=M * 11 + K + N, out_scale=0.5, with_residual=True)
+    g, u, W, res = to_dev(inp)
+    s = F.scalar(0.5)
+    y = F.to_bits(F.swiglu_w4_gemv(g, u, W, s, res))
+    ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 0.5, inp.residual)
+    assert_close(y, ref, f"M={M} K={K} N={N}")
+    for m0 in range(0, M, 16):
+        m1 = min(M, m0 + 16)
+        yb = F.to_bits(F.swiglu_w4_gemv(g[m0:m1], u[m0:m1], W, s, res[m0:m1].contiguous()))
+        assert_bits_equal(y[m0:m1], yb, f"rows {m0}..{m1 - 1}")
+    # in place: y is the residual
+    F.swiglu_w4_gemv(g, u, W, s, res, out=res)
+    torch.cuda.synchronize()
+    assert_bits_equal(F.to_bits(res), y, "in place")
+
+
 def test_swiglu_gemv_strided_rows_and_null_scale():
     say("[gemv] g, u as halves of one [M, 2K] buffer; out_scale NULL")
     M, K, N = 4, 1024, 264
@@ -161,7 +182,8 @@ def test_swiglu_gemv_exact_special_cases_bit_exact(M, K, N):
 # ---------------------------------------------------------------------------
 # the identity-prologue GEMV (gate_up)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("M,K,N", [(1, 1536, 17920), (16, 4096, 28672), (3, 640, 392)])
+@pytest.mark.parametrize("M,K,N", [(1, 1536, 17920), (16, 4096, 28672), (3, 640, 392), (64, 1024, 2056),
+                                   (21, 4096, 1024)])
 def test_w4_gemv_identity(M, K, N):
     say(f"[gemv identity] M={M} K={K} N={N}")
     rng = np.random.default_rng(M + K + N)
