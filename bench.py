@@ -237,7 +237,8 @@ def bench_extras(torch, F, synth, n_sets_gemv):
 
     # batch sweep at the metric's K and N: the same 48 rotating weight sets, M rows of
     # seeded N(0,1) activations, one graph per batch size; M <= 4 runs the column kernel,
-    # 5 <= M <= 16 the matrix-core kernel, M = 32 and 64 two and four 16-row blocks of it
+    # 5 <= M <= 16 the matrix-core kernel, M = 32 and 64 the same kernel with two and four
+    # 16-row blocks per weight load
     log("[bench] batch sweep M=1..64 at K=9216 N=2560")
     gen = torch.Generator().manual_seed(1234)
     sweep = {}
@@ -251,7 +252,7 @@ def bench_extras(torch, F, synth, n_sets_gemv):
         b = T.swiglu_w4_gemv_bytes(Mb, K, N)
         sweep[f"M{Mb}"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS,
                            "kernel": "column" if Mb <= 4 else "matrix-core" if Mb <= 16 else
-                           f"matrix-core x {(Mb + 15) // 16} row blocks"}
+                           f"matrix-core, {(Mb + 15) // 16} row blocks"}
         del gb, ub, ys, wsb
     out["batch_sweep_swiglu_w4_gemv_9216x2560"] = sweep
     del gsets

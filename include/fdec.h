@@ -152,9 +152,8 @@ FDEC_API int fdec_add_rmsnorm(const fdec_bf16* x, const fdec_bf16* residual,
  *   W:        K x N int4 weights (fdec_w4).
  *   residual: bf16 [M][N] or NULL.
  *   y:        bf16 [M][N].  May not overlap g, u, W or out_scale; may equal residual.
- *   1 <= M <= 64;  ldgu >= K, ldgu % 8 == 0.  Rows past 16 run as consecutive blocks
- *   of 16 (the last one shorter), each a full pass over W, in order on the stream; the
- *   decode batch sizes of the matrix-core kernel stop at 16 rows.
+ *   1 <= M <= 64;  ldgu >= K, ldgu % 8 == 0.  17..64 rows run on the matrix cores as
+ *   two or four blocks of 16 rows that share every weight load (W is read once).
  *   The activation silu(g) * u is formed in registers and is never written; the
  *   (M, K, N) product is never formed.
  *   ws: at least fdec_w4_gemv_workspace_bytes(M, K, N) bytes (see Workspace above).
@@ -169,8 +168,8 @@ FDEC_API int fdec_swiglu_w4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t
  * The same GEMV with the identity prologue: y = bf16( s * x @ W ), s as above
  * (NULL = 1).  Used for the horizontally fused gate_up projection ([P4] section 5,
  * horizontal fusion), whose columns [0, I) are gate_proj and [I, 2I) up_proj.
- *   x: bf16 [M][K];  y: bf16 [M][N], no overlap with x.  1 <= M <= 64 (row blocks of
- *   16 as above).
+ *   x: bf16 [M][K];  y: bf16 [M][N], no overlap with x.  1 <= M <= 64 (row blocks as
+ *   above).
  */
 FDEC_API int fdec_w4_gemv(const fdec_bf16* x, const fdec_w4* W, const float* out_scale,
                           int32_t M, fdec_bf16* y, void* ws, size_t ws_bytes,

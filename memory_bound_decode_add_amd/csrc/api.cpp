@@ -76,35 +76,12 @@ int check_m(int M, int max_m = 16) {
     return FDEC_OK;
 }
 
-// The W4 GEMV entry points take up to kMaxGemvRows rows: above 16 the rows are run as
-// consecutive blocks of 16 (the last one shorter) on the caller's stream, each block a
-// full GEMV over the weights.
-constexpr int kMaxGemvRows = 64;
-constexpr int kRowBlock = 16;
+// The W4 GEMV entry points take up to kMaxGemvRows rows: past 16 the matrix-core kernel
+// stages 32 or 64 rows and feeds each weight load to two or four 16-row MFMA blocks.
+constexpr int kMaxGemvRows = kMfmaMaxRows;
 
 bool w4_gemv_shape_ok(int M, int K, int N) {
     return M >= 1 && M <= kMaxGemvRows && K > 0 && K % 128 == 0 && N > 0 && N % 8 == 0;
-}
-
-// Blocks run in stream order and each finishes with its partials before the next starts,
-// so one workspace sized for the largest block serves them all.
-size_t w4_gemv_ws(int M, int K, int N) {
-    if (M <= kRowBlock) return gemv_workspace_bytes(M, K, N);
-    const int tail = M % kRowBlock;
-    return std::max(gemv_workspace_bytes(kRowBlock, K, N), tail ? gemv_workspace_bytes(tail, K, N) : size_t(0));
-}
-
-hipError_t launch_gemv_rows(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const fdec_w4* W,
-                            int M, const float* out_scale, const uint16_t* residual, uint16_t* y, void* ws,
-                            hipStream_t s) {
-    for (int m0 = 0; m0 < M; m0 += kRowBlock) {
-        const int mb = std::min(kRowBlock, M - m0);
-        const hipError_t e = launch_gemv(pro, a0 + m0 * lda, a1 ? a1 + m0 * lda : nullptr, lda, W->qweight, W->scales,
-                                         mb, W->K, W->N, out_scale, residual ? residual + size_t(m0) * W->N : nullptr,
-                                         y + size_t(m0) * W->N, ws, s);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
 }
 
 int check_norm(const fdec_bf16* x, const fdec_bf16* residual, const fdec_bf16* weight, float eps,
@@ -517,31 +494,31 @@ FDEC_API int fdec_add_rmsnorm(const fdec_bf16* x, const fdec_bf16* residual, con
 }
 
 FDEC_API size_t fdec_w4_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
-    return w4_gemv_shape_ok(M, K, N) ? w4_gemv_ws(M, K, N) : 0;
+    return w4_gemv_shape_ok(M, K, N) ? gemv_workspace_bytes(M, K, N) : 0;
 }
 
 FDEC_API int fdec_swiglu_w4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_w4* W,
                                  const float* out_scale, const fdec_bf16* residual, int32_t M, fdec_bf16* y,
                                  void* ws, size_t ws_bytes, fdec_stream stream) {
     if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
-    const size_t need = w4_gemv_shape_ok(M, W->K, W->N) ? w4_gemv_ws(M, W->K, W->N) : 0;
+    const size_t need = w4_gemv_shape_ok(M, W->K, W->N) ? gemv_workspace_bytes(M, W->K, W->N) : 0;
     const int st = check_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true, need, kMaxGemvRows);
     if (st != FDEC_OK) return st;
     if (g_fail_launches) return injected();
-    return hip_status(launch_gemv_rows(kSwiGLU, g, u, ldgu, W, M, out_scale, residual, y, ws,
-                                       static_cast<hipStream_t>(stream)),
+    return hip_status(launch_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual,
+                                  y, ws, static_cast<hipStream_t>(stream)),
                       "gemv launch");
 }
 
 FDEC_API int fdec_w4_gemv(const fdec_bf16* x, const fdec_w4* W, const float* out_scale, int32_t M, fdec_bf16* y,
                           void* ws, size_t ws_bytes, fdec_stream stream) {
     if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
-    const size_t need = w4_gemv_shape_ok(M, W->K, W->N) ? w4_gemv_ws(M, W->K, W->N) : 0;
+    const size_t need = w4_gemv_shape_ok(M, W->K, W->N) ? gemv_workspace_bytes(M, W->K, W->N) : 0;
     const int st = check_gemv(x, nullptr, W->K, W, out_scale, nullptr, M, y, ws, ws_bytes, false, need, kMaxGemvRows);
     if (st != FDEC_OK) return st;
     if (g_fail_launches) return injected();
-    return hip_status(launch_gemv_rows(kIdentity, x, nullptr, W->K, W, M, out_scale, nullptr, y, ws,
-                                       static_cast<hipStream_t>(stream)),
+    return hip_status(launch_gemv(kIdentity, x, nullptr, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale,
+                                  nullptr, y, ws, static_cast<hipStream_t>(stream)),
                       "gemv launch");
 }
 

@@ -27,7 +27,8 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 enum GemvKind { kColumnOwning = 0, kSplitK = 1, kMfma = 2 };
 constexpr int kMfmaWaves = 8;       // waves per workgroup, matrix-core kernel
-constexpr int kMfmaMaxSliceGroups = 36;   // 128-wide groups per K slice (LDS: 4 KB each)
+constexpr int kMfmaMaxSliceGroups = 36;   // 128-wide groups per K slice at 16 rows (LDS: 4 KB each)
+constexpr int kMfmaMaxRows = 64;          // four row blocks of 16
 
 struct GemvPlan {
     int kind;

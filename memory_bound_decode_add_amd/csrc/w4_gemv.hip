@@ -936,40 +936,46 @@ bool plan_column_pair(int M, int K, int I, GemvPlan& p) {
 // until there are about 256 workgroups, one per CU (and each slice's activation fits
 // LDS); of the wave counts, the one whose workgroups fill the 256 CUs best (fewest idle
 // slots in the last round of workgroups), ties to more waves.
-int mfma_splits(int groups, int tiles) {
-    const int S = std::max((groups + kMfmaMaxSliceGroups - 1) / kMfmaMaxSliceGroups,
+int mfma_splits(int groups, int tiles, int max_slice = kMfmaMaxSliceGroups) {
+    const int S = std::max((groups + max_slice - 1) / max_slice,
                            std::min(groups, (256 + tiles - 1) / tiles));
     const int gps = (groups + S - 1) / S;
     return (groups + gps - 1) / gps;
 }
 
 bool plan_mfma(int M, int K, int N, GemvPlan& p) {
-    if (M <= 4 || M > 16) return false;
+    if (M <= 4 || M > kMfmaMaxRows) return false;
+    const int rb = M <= 16 ? 1 : M <= 32 ? 2 : 4;     // row blocks of 16
+    const int max_slice = kMfmaMaxSliceGroups / rb;   // LDS holds 16 rb rows of the slice
     p.kind = kMfma;
-    p.mr = 16;
+    p.mr = 16 * rb;
     p.groups = K / kGroup;
     p.cpw = 1;
     p.waves = kMfmaWaves;
     double best = 1e30;
     for (int w = kMfmaWaves; w >= 6; --w) {
         const int tiles = (N + 16 * p.cpw * w - 1) / (16 * p.cpw * w);
-        const int wgs = tiles * mfma_splits(p.groups, tiles);
+        const int wgs = tiles * mfma_splits(p.groups, tiles, max_slice);
         const double fill = double((wgs + 255) / 256 * 256) / wgs;
         if (fill < best - 1e-9) { best = fill; p.waves = w; }
     }
     const int ncol = p.waves * p.cpw * 16;
     p.tiles = (N + ncol - 1) / ncol;
-    int S = mfma_splits(p.groups, p.tiles);
+    int S = mfma_splits(p.groups, p.tiles, max_slice);
     p.gps = (p.groups + S - 1) / S;
     p.splits = (p.groups + p.gps - 1) / p.gps;
-    if (p.splits > 1) p.partial_bytes = size_t(p.splits) * 16 * p.tiles * ncol * 4;
-    p.lds_bytes = size_t(16) * (size_t(p.gps) * 16 + 1) * 16 + size_t(16) * p.gps * 4;
+    if (p.splits > 1) p.partial_bytes = size_t(p.splits) * p.mr * p.tiles * ncol * 4;
+    p.lds_bytes = size_t(p.mr) * (size_t(p.gps) * 16 + 1) * 16 + size_t(p.mr) * p.gps * 4;
     return true;
 }
 
 GemvPlan plan_gemv(int M, int K, int N) {
     GemvPlan p{};
     p.groups = K / kGroup;
+    if (M > 16) {                 // only the matrix-core kernel takes more than 16 rows
+        plan_mfma(M, K, N, p);
+        return p;
+    }
     if (g_forced_split == 0 && plan_column(M, K, N, p)) return p;
     p = GemvPlan{};
     if (g_forced_split == 0 && plan_mfma(M, K, N, p)) return p;

@@ -8,6 +8,11 @@
 // every weight byte feeds 16 rows of products, which the VALU cannot keep up with at
 // HBM speed; v_mfma_f32_16x16x32_f16 does the products, the VALU only decodes.
 //
+// Row blocks.  A batch of 17..64 rows is RB = 2 or 4 blocks of 16 (int4 weights): the
+// workgroup stages all 16 RB rows, and each weight word, decoded once per block, feeds
+// RB MFMAs, so the weights are read once for the whole batch.  The K slices shrink by RB
+// so the staged activation still fits LDS.
+//
 // Tiling.  A tile is 16 consecutive columns.  A workgroup of W waves owns W * TPW
 // tiles (each wave TPW of them) over a slice of whole 128-wide groups of K.  With
 // several slices per column range, each workgroup writes its fp32 partial sums to the
@@ -31,7 +36,8 @@
 // (A bf16 operand path was measured slower in the main loop, and bf16 loses 3 bits of
 // the fp32 SwiGLU activation, which failed the parity bound at K = 14336.)
 //
-// Activation.  The workgroup stages its slice of act (16 rows, zero beyond M) in LDS as
+// Activation.  The workgroup stages its slice of act (16 RB rows; rows past M repeat row
+// M - 1 and are never stored) in LDS as
 // block-scaled fp16 with the odd positions divided by 16 (so each product is a * q plus
 // a weight-independent offset): per (row, 128-wide group) a power of two 2^-E puts the
 // largest magnitude in [2^14, 2^15); 2^E is folded back in with the group scale.  The
@@ -80,11 +86,18 @@ struct MfmaArgs {
     float* partial;         // [splits][16][npad]
 };
 
-// One packed word -> 8 fp16 values with their offsets, in pair order.
+// One packed word -> 8 fp16 values with their offsets, in pair order: the decode of
+// the VALU kernels (offset binary OR-ed into the mantissa of 1024, 1032 + q at even and
+// 1152 + 16 q at odd positions), written as plain integer code.  The compiler spaces an
+// MFMA and a later instruction that writes the registers the MFMA still reads (its
+// accumulator input is read over several passes) only for instructions it can see; an
+// inline-asm decode next to MFMAs can overwrite an accumulator in flight.
 __device__ __forceinline__ f16x8_t decode_f16x8_biased(uint32_t w) {
-    const Q4x2 q = decode_int4x8_biased(w);
-    return __builtin_bit_cast(f16x8_t, make_uint4(__builtin_bit_cast(uint32_t, q.p04), __builtin_bit_cast(uint32_t, q.p15),
-                                                  __builtin_bit_cast(uint32_t, q.p26), __builtin_bit_cast(uint32_t, q.p37)));
+    const uint32_t x = w ^ 0x88888888u;
+    const uint32_t t = x >> 8;
+    const uint32_t one024 = 0x64006400u;
+    return __builtin_bit_cast(f16x8_t, make_uint4((x & 0x000F000Fu) | one024, (x & 0x00F000F0u) | one024,
+                                                  (t & 0x000F000Fu) | one024, (t & 0x00F000F0u) | one024));
 }
 
 // One staging item: 8 consecutive activation values of one row.  The 16 lanes of a
@@ -145,8 +158,12 @@ __device__ __forceinline__ f16x8_t fp4_operand(uint32_t w, _Float16 s) {
                                                   __builtin_bit_cast(uint32_t, q[3] * s2)));
 }
 
-template <int TPW, int PRO, int WF>
+template <int TPW, int PRO, int WF, int RB>
 __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaArgs a) {
+    constexpr int kRows = 16 * RB;                     // activation rows staged: RB blocks of 16
+    // groups per batch of weight loads: several row blocks already give the matrix cores
+    // independent chains, and four groups of them would not fit the register file
+    constexpr int kP = RB > 1 ? 2 : kMfmaP;
     extern __shared__ __align__(16) unsigned char smem[];
     const int W = blockDim.x >> 6;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -159,14 +176,14 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     const int ncol = W * TPW * 16;                     // columns per workgroup
     const int nw0 = cg * ncol + wave * TPW * 16;       // first column of this wave's tiles
     const int rs = nkb + 1;                            // row stride of act_s, in 16-byte blocks
-    uint4* act_s = reinterpret_cast<uint4*>(smem);     // [16 rows][rs] of 8 fp16
-    float* esc_s = reinterpret_cast<float*>(act_s + 16 * rs);   // [16 rows][ng]
+    uint4* act_s = reinterpret_cast<uint4*>(smem);     // [kRows][rs] of 8 fp16
+    float* esc_s = reinterpret_cast<float*>(act_s + kRows * rs);   // [kRows][ng]
 
     // ---- weight and scale loads of one batch of groups (addresses clamped) ----
-    auto load_batch = [&](int b, uint4 (&w)[kMfmaP][TPW], uint2 (&sv)[kMfmaP][TPW]) {
+    auto load_batch = [&](int b, uint4 (&w)[kP][TPW], uint2 (&sv)[kP][TPW]) {
 #pragma unroll
-        for (int p = 0; p < kMfmaP; ++p) {
-            const int g = g0 + min(b * kMfmaP + p, ng - 1);
+        for (int p = 0; p < kP; ++p) {
+            const int g = g0 + min(b * kP + p, ng - 1);
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int n = min(nw0 + t * 16 + lm, a.N - 1);
@@ -183,22 +200,24 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
         }
     };
 
-    uint4 wA[kMfmaP][TPW], wB[kMfmaP][TPW];
-    uint2 sA[kMfmaP][TPW], sB[kMfmaP][TPW];
-    // epilogue inputs: 4 consecutive columns of row lm per tile
-    uint2 rraw[TPW];
+    uint4 wA[kP][TPW], wB[kP][TPW];
+    uint2 sA[kP][TPW], sB[kP][TPW];
+    // epilogue inputs: 4 consecutive columns of row 16 r + lm per tile
+    uint2 rraw[RB][TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const uint16_t* rsrc = a.residual ? a.residual : a.y;   // y: a readable stand-in, value unused
-        rraw[t] = *reinterpret_cast<const uint2*>(rsrc + size_t(min(lm, a.M - 1)) * a.N +
-                                                  min(nw0 + t * 16 + 4 * ls, a.N - 4));
-    }
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const uint16_t* rsrc = a.residual ? a.residual : a.y;   // y: a readable stand-in, value unused
+            rraw[r][t] = *reinterpret_cast<const uint2*>(rsrc + size_t(min(16 * r + lm, a.M - 1)) * a.N +
+                                                         min(nw0 + t * 16 + 4 * ls, a.N - 4));
+        }
     const float os = a.out_scale ? *a.out_scale : 1.0f;
 
     // ---- stage the activation slice: item i = (row i / nkb, k-block i % nkb) ----
     // All of a thread's items (up to UMAX of them) are loaded before the first is
     // converted, so the staging waits for one L2 round trip, not one per item.
-    const int nitems = nkb * 16;
+    const int nitems = nkb * kRows;
     const int kbase = g0 * 128;
     constexpr int UMAX = PRO == kSwiGLU ? 12 : 24;
     const int nthr = blockDim.x;
@@ -250,46 +269,52 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     load_batch(0, wA, sA);
     __syncthreads();
 
-    // ---- main loop: batches of kMfmaP groups, next batch's loads in flight ----
-    f32x4_t out[TPW];
+    // ---- main loop: batches of kP groups, next batch's loads in flight ----
+    f32x4_t out[RB][TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) out[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) out[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // -offset of each pair-order slot: (-1032, -1032), (-1152, -1152), ...
     const uint32_t o_even = 0xE408E408u, o_odd = 0xE480E480u;
     const f16x8_t negoff = __builtin_bit_cast(f16x8_t, make_uint4(o_even, o_odd, o_even, o_odd));
 
-    // The kMfmaP groups of a batch are independent accumulation chains; their MFMAs are
+    // The kP groups of a batch are independent accumulation chains; their MFMAs are
     // interleaved so that no MFMA waits on the one issued just before it.  A group past
-    // the slice's end re-reads the last group and contributes with weight 0.
-    auto compute_batch = [&](int b, const uint4 (&w)[kMfmaP][TPW], const uint2 (&sv)[kMfmaP][TPW]) {
-        f16x8_t bop[kMfmaP][4];
-        float e[kMfmaP];
+    // the slice's end re-reads the last group and contributes with weight 0.  With
+    // several row blocks the same weight registers feed each block's MFMAs in turn.
+    auto compute_batch = [&](int b, const uint4 (&w)[kP][TPW], const uint2 (&sv)[kP][TPW]) {
 #pragma unroll
-        for (int p = 0; p < kMfmaP; ++p) {
-            const int gl = min(b * kMfmaP + p, ng - 1);
+      for (int r = 0; r < RB; ++r) {
+        const int row = 16 * r + lm;
+        f16x8_t bop[kP][4];
+        float e[kP];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bop[p][j] = __builtin_bit_cast(f16x8_t, act_s[lm * rs + 16 * gl + 4 * ls + j]);
-            e[p] = b * kMfmaP + p < ng ? esc_s[lm * ng + gl] : 0.f;
+        for (int p = 0; p < kP; ++p) {
+            const int gl = min(b * kP + p, ng - 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bop[p][j] = __builtin_bit_cast(f16x8_t, act_s[row * rs + 16 * gl + 4 * ls + j]);
+            e[p] = b * kP + p < ng ? esc_s[row * ng + gl] : 0.f;
         }
-        f32x4_t bias[kMfmaP];
+        f32x4_t bias[kP];
 #pragma unroll
-        for (int p = 0; p < kMfmaP; ++p) bias[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < kP; ++p) bias[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (WF == kWInt4) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int p = 0; p < kMfmaP; ++p)
+                for (int p = 0; p < kP; ++p)
                     bias[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(negoff, bop[p][j], bias[p], 0, 0, 0);
         }
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            f32x4_t d[kMfmaP];
+            f32x4_t d[kP];
 #pragma unroll
-            for (int p = 0; p < kMfmaP; ++p) d[p] = bias[p];
-            _Float16 fs[kMfmaP][2];
+            for (int p = 0; p < kP; ++p) d[p] = bias[p];
+            _Float16 fs[kP][2];
             if (WF == kWFp4) {
 #pragma unroll
-                for (int p = 0; p < kMfmaP; ++p) {
+                for (int p = 0; p < kP; ++p) {
                     fs[p][0] = (_Float16)e4m3_to_f32(sv[p][t].x & 0xFFu);
                     fs[p][1] = (_Float16)e4m3_to_f32(sv[p][t].x >> 8);
                 }
@@ -297,27 +322,28 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int p = 0; p < kMfmaP; ++p) {
+                for (int p = 0; p < kP; ++p) {
                     const uint32_t wd = j == 0 ? w[p][t].x : j == 1 ? w[p][t].y : j == 2 ? w[p][t].z : w[p][t].w;
                     const f16x8_t aop = WF == kWFp4 ? fp4_operand(wd, fs[p][j >> 1]) : decode_f16x8_biased(wd);
                     d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[p][j], d[p], 0, 0, 0);
                 }
 #pragma unroll
-            for (int p = 0; p < kMfmaP; ++p) {
+            for (int p = 0; p < kP; ++p) {
                 if (WF == kWFp4) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) out[t][r] = fmaf(e[p], d[p][r], out[t][r]);
+                    for (int q = 0; q < 4; ++q) out[r][t][q] = fmaf(e[p], d[p][q], out[r][t][q]);
                 } else {
-                    out[t][0] = fmaf(bf16_lo(sv[p][t].x) * e[p], d[p][0], out[t][0]);
-                    out[t][1] = fmaf(bf16_hi(sv[p][t].x) * e[p], d[p][1], out[t][1]);
-                    out[t][2] = fmaf(bf16_lo(sv[p][t].y) * e[p], d[p][2], out[t][2]);
-                    out[t][3] = fmaf(bf16_hi(sv[p][t].y) * e[p], d[p][3], out[t][3]);
+                    out[r][t][0] = fmaf(bf16_lo(sv[p][t].x) * e[p], d[p][0], out[r][t][0]);
+                    out[r][t][1] = fmaf(bf16_hi(sv[p][t].x) * e[p], d[p][1], out[r][t][1]);
+                    out[r][t][2] = fmaf(bf16_lo(sv[p][t].y) * e[p], d[p][2], out[r][t][2]);
+                    out[r][t][3] = fmaf(bf16_hi(sv[p][t].y) * e[p], d[p][3], out[r][t][3]);
                 }
             }
         }
+      }
     };
 
-    const int nbatch = (ng + kMfmaP - 1) / kMfmaP;
+    const int nbatch = (ng + kP - 1) / kP;
     for (int b = 0; b < nbatch; b += 2) {
         load_batch(b + 1, wB, sB);                     // clamped: harmless past the end
         compute_batch(b, wA, sA);
@@ -325,30 +351,36 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
         compute_batch(b + 1, wB, sB);
     }
 
-    // ---- epilogue: lane holds D[column 4 ls + r][row lm] of each tile ----
+    // ---- epilogue: lane holds D[column 4 ls + q][row 16 r + lm] of each tile ----
     if (a.splits == 1) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int n = nw0 + t * 16 + 4 * ls;
-            if (lm < a.M && n < a.N) {
-                const float r0 = a.residual ? bf16_lo(rraw[t].x) : 0.f, r1 = a.residual ? bf16_hi(rraw[t].x) : 0.f;
-                const float r2 = a.residual ? bf16_lo(rraw[t].y) : 0.f, r3 = a.residual ? bf16_hi(rraw[t].y) : 0.f;
-                uint2 o;
-                o.x = pack_bf16x2(fmaf(out[t][0], os, r0), fmaf(out[t][1], os, r1));
-                o.y = pack_bf16x2(fmaf(out[t][2], os, r2), fmaf(out[t][3], os, r3));
-                *reinterpret_cast<uint2*>(a.y + size_t(lm) * a.N + n) = o;
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int n = nw0 + t * 16 + 4 * ls;
+                const int row = 16 * r + lm;
+                if (row < a.M && n < a.N) {
+                    const uint2 rr = rraw[r][t];
+                    const float r0 = a.residual ? bf16_lo(rr.x) : 0.f, r1 = a.residual ? bf16_hi(rr.x) : 0.f;
+                    const float r2 = a.residual ? bf16_lo(rr.y) : 0.f, r3 = a.residual ? bf16_hi(rr.y) : 0.f;
+                    uint2 o;
+                    o.x = pack_bf16x2(fmaf(out[r][t][0], os, r0), fmaf(out[r][t][1], os, r1));
+                    o.y = pack_bf16x2(fmaf(out[r][t][2], os, r2), fmaf(out[r][t][3], os, r3));
+                    *reinterpret_cast<uint2*>(a.y + size_t(row) * a.N + n) = o;
+                }
             }
-        }
         return;
     }
 
-    // ---- several K slices: this slice's partial sums, plain stores ----
+    // ---- several K slices: this slice's partial sums (all kRows rows), plain stores ----
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int nc = (nw0 - cg * ncol) + t * 16 + 4 * ls;          // column within the range
-        float* dst = a.partial + (size_t(split) * 16 + lm) * a.npad + cg * ncol + nc;
-        *reinterpret_cast<float4*>(dst) = make_float4(out[t][0], out[t][1], out[t][2], out[t][3]);
-    }
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int nc = (nw0 - cg * ncol) + t * 16 + 4 * ls;          // column within the range
+            float* dst = a.partial + (size_t(split) * kRows + 16 * r + lm) * a.npad + cg * ncol + nc;
+            *reinterpret_cast<float4*>(dst) = make_float4(out[r][t][0], out[r][t][1], out[r][t][2], out[r][t][3]);
+        }
 }
 
 template <typename Kern>
@@ -393,11 +425,25 @@ hipError_t launch_mfma_wf(Prologue pro, const uint16_t* a0, const uint16_t* a1, 
     const dim3 grid(p.tiles * p.splits);
     const int threads = p.waves * kWave;
     // one 16-column tile per wave (two per wave measured slower: more registers and a
-    // K split for the same workgroup count)
-    hipError_t e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF>, grid, threads, p.lds_bytes, s, a)
-                                  : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF>, grid, threads, p.lds_bytes, s, a);
+    // K split for the same workgroup count); p.mr / 16 row blocks (int4 weights only)
+    const int rb = p.mr / 16;
+    if (M > p.mr || (rb != 1 && rb != 2 && rb != 4) || (WF == kWFp4 && rb != 1)) return hipErrorInvalidValue;
+    hipError_t e;
+    if (rb == 1)
+        e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF, 1>, grid, threads, p.lds_bytes, s, a)
+                           : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF, 1>, grid, threads, p.lds_bytes, s, a);
+    else if constexpr (WF == kWInt4) {
+        if (rb == 2)
+            e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF, 2>, grid, threads, p.lds_bytes, s, a)
+                               : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF, 2>, grid, threads, p.lds_bytes, s, a);
+        else
+            e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF, 4>, grid, threads, p.lds_bytes, s, a)
+                               : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF, 4>, grid, threads, p.lds_bytes, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     if (e != hipSuccess || p.splits == 1) return e;
-    return launch_splitk_finish(a.partial, p.splits, int64_t(16) * a.npad, a.npad, M, N, out_scale, residual, y, s);
+    return launch_splitk_finish(a.partial, p.splits, int64_t(p.mr) * a.npad, a.npad, M, N, out_scale, residual, y, s);
 }
 
 }  // namespace

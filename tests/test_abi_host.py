@@ -76,10 +76,12 @@ def test_workspace_queries(L):
     assert L.fdec_unfused_gemv_workspace_bytes(1, 1, 9216, 2560) >= 2 * 9216 * 2
     assert L.fdec_w4_gemv_workspace_bytes(65, 1024, 512) == 0            # invalid shape
     assert L.fdec_w4_gemv_workspace_bytes(0, 1024, 512) == 0
-    # above 16 rows the blocks of 16 share one workspace: the largest block's
-    for M in (17, 32, 40, 64):
-        assert L.fdec_w4_gemv_workspace_bytes(M, 9216, 2560) == max(
-            L.fdec_w4_gemv_workspace_bytes(16, 9216, 2560), L.fdec_w4_gemv_workspace_bytes(M % 16 or 16, 9216, 2560))
+    # 17..64 rows: the matrix-core kernel's partial sums hold 32 or 64 rows per K slice,
+    # and its K slices shrink with the rows, so the workspace grows with the row blocks
+    w16, w32, w64 = (L.fdec_w4_gemv_workspace_bytes(M, 9216, 2560) for M in (16, 32, 64))
+    assert 0 < w16 < w32 < w64
+    assert L.fdec_w4_gemv_workspace_bytes(17, 9216, 2560) == w32
+    assert L.fdec_w4_gemv_workspace_bytes(33, 9216, 2560) == w64
     assert L.fdec_w4_gemv_workspace_bytes(1, 1000, 512) == 0
     # the fused GEMV's own workspace stays far below the product it avoids
     assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) < 0.02 * 94_371_840
