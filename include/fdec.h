@@ -5,7 +5,7 @@
  * LLM's MLP half:
  *   - a residual add fused with RMSNorm, writing both the new residual and the
  *     normalised activations from one kernel;
- *   - a single-row (M = 1..16) GEMV over int4 group-quantised weights, with the
+ *   - a decode-batch (M = 1..64) GEMV over int4 group-quantised weights, with the
  *     SwiGLU activation silu(g) * u computed in the GEMV's prologue (the activation
  *     and the (M, K, N) broadcast product are never written to memory) and an fp32
  *     output scale (and optional residual add) folded into its epilogue;
