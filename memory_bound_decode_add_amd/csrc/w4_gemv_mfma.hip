@@ -83,7 +83,8 @@ struct MfmaArgs {
     const float* out_scale;
     const uint16_t* residual;
     uint16_t* y;
-    float* partial;         // [splits][16][npad]
+    float* partial;         // [splits][16 RB][npad]
+    uint32_t m_lo, m_hi;    // int4 decode field masks 0x000F000F and 0x00F000F0
 };
 
 // One packed word -> 8 fp16 values with their offsets, in pair order: the decode of
@@ -92,12 +93,19 @@ struct MfmaArgs {
 // MFMA and a later instruction that writes the registers the MFMA still reads (its
 // accumulator input is read over several passes) only for instructions it can see; an
 // inline-asm decode next to MFMAs can overwrite an accumulator in flight.
-__device__ __forceinline__ f16x8_t decode_f16x8_biased(uint32_t w) {
-    const uint32_t x = w ^ 0x88888888u;
-    const uint32_t t = x >> 8;
-    const uint32_t one024 = 0x64006400u;
-    return __builtin_bit_cast(f16x8_t, make_uint4((x & 0x000F000Fu) | one024, (x & 0x00F000F0u) | one024,
-                                                  (t & 0x000F000Fu) | one024, (t & 0x00F000F0u) | one024));
+//
+// Each field is K ^ (v & m): inside the mask m the nibble is XOR-ed with 8 (two's
+// complement -> offset binary), outside it are the bits of 1024, which share none with
+// m, so K = 1024's bits | 8 in each masked nibble (0x64086408 for the low nibbles of
+// both halves, 0x64806480 for the high ones).  The XOR commutes with the shift by 8, so
+// the fields of w >> 8 use the same constants.  The masks come in the kernel arguments
+// (scalar registers), which lets each field compile to one v_bitop3_b32.
+struct DecodeMasks { uint32_t lo, hi; };
+__device__ __forceinline__ f16x8_t decode_f16x8_biased(uint32_t w, DecodeMasks dm) {
+    const uint32_t t = w >> 8;
+    const uint32_t k_lo = 0x64086408u, k_hi = 0x64806480u;
+    return __builtin_bit_cast(f16x8_t, make_uint4(k_lo ^ (w & dm.lo), k_hi ^ (w & dm.hi),
+                                                  k_lo ^ (t & dm.lo), k_hi ^ (t & dm.hi)));
 }
 
 // One staging item: 8 consecutive activation values of one row.  The 16 lanes of a
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
 #pragma unroll
                 for (int p = 0; p < kP; ++p) {
                     const uint32_t wd = j == 0 ? w[p][t].x : j == 1 ? w[p][t].y : j == 2 ? w[p][t].z : w[p][t].w;
-                    const f16x8_t aop = WF == kWFp4 ? fp4_operand(wd, fs[p][j >> 1]) : decode_f16x8_biased(wd);
+                    const f16x8_t aop = WF == kWFp4 ? fp4_operand(wd, fs[p][j >> 1]) : decode_f16x8_biased(wd, DecodeMasks{a.m_lo, a.m_hi});
                     d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[p][j], d[p], 0, 0, 0);
                 }
 #pragma unroll
@@ -422,6 +430,8 @@ hipError_t launch_mfma_wf(Prologue pro, const uint16_t* a0, const uint16_t* a1, 
     a.residual = residual;
     a.y = y;
     a.partial = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
+    a.m_lo = 0x000F000Fu;
+    a.m_hi = 0x00F000F0u;
     const dim3 grid(p.tiles * p.splits);
     const int threads = p.waves * kWave;
     // one 16-column tile per wave (two per wave measured slower: more registers and a
