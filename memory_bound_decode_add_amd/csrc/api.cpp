@@ -150,7 +150,7 @@ int check_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const f
                    const fdec_bf16* residual, int M, const fdec_bf16* y, void* ws, size_t ws_bytes, bool swiglu) {
     int st;
     if ((st = check_fp4(W)) != FDEC_OK) return st;
-    if ((st = check_m(M)) != FDEC_OK) return st;
+    if ((st = check_m(M, kMaxGemvRows)) != FDEC_OK) return st;
     if (!g || (swiglu && !u) || !y) return fail(FDEC_ERR_NULL, "activation input and y are required");
     if (ldgu < W->K || ldgu % 8) return fail(FDEC_ERR_SHAPE, "ld = %lld must be >= K and a multiple of 8", (long long)ldgu);
     if (!aligned16(g) || (u && !aligned16(u)) || !aligned16(y) || (residual && !aligned16(residual)))
@@ -796,7 +796,7 @@ FDEC_API int fdec_unfused_mlp_decode(const fdec_mlp_layer* layer, int32_t M, con
 }
 
 FDEC_API size_t fdec_fp4_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
-    if (M < 1 || M > 16 || K <= 0 || K % 32 || N <= 0 || N % 8) return 0;
+    if (M < 1 || M > kMaxGemvRows || K <= 0 || K % 32 || N <= 0 || N % 8) return 0;
     return fp4_gemv_workspace_bytes(M, K, N);
 }
 

@@ -295,13 +295,14 @@ hipError_t launch_fp4_1(Prologue pro, const Fp4Args& a, const Fp4Plan& p, hipStr
 
 }  // namespace
 
-// 1..4 rows: the chunk-owning kernel above.  5..16 rows: the matrix-core kernel with
-// the FP4 weight format (K % 128 == 0), whose K slices need a workspace.
+// 1..4 rows: the chunk-owning kernel above.  5..64 rows: the matrix-core kernel with
+// the FP4 weight format (K % 128 == 0; two or four 16-row blocks past 16 rows), whose K
+// slices need a workspace.
 bool fp4_gemv_supported(int M, int K, int N) {
     Fp4Plan p;
     if (M <= 4) return fp4_plan(M, K, N, p);
     GemvPlan g{};
-    return M <= 16 && K > 0 && K % 128 == 0 && N > 0 && N % 8 == 0 && plan_mfma(M, K, N, g);
+    return M <= kMfmaMaxRows && K > 0 && K % 128 == 0 && N > 0 && N % 8 == 0 && plan_mfma(M, K, N, g);
 }
 
 size_t fp4_gemv_workspace_bytes(int M, int K, int N) {

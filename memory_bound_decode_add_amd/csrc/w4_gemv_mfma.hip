@@ -8,7 +8,7 @@
 // every weight byte feeds 16 rows of products, which the VALU cannot keep up with at
 // HBM speed; v_mfma_f32_16x16x32_f16 does the products, the VALU only decodes.
 //
-// Row blocks.  A batch of 17..64 rows is RB = 2 or 4 blocks of 16 (int4 weights): the
+// Row blocks.  A batch of 17..64 rows is RB = 2 or 4 blocks of 16 (either weight format): the
 // workgroup stages all 16 RB rows, and each weight word, decoded once per block, feeds
 // RB MFMAs, so the weights are read once for the whole batch.  The K slices shrink by RB
 // so the staged activation still fits LDS.
@@ -435,23 +435,19 @@ hipError_t launch_mfma_wf(Prologue pro, const uint16_t* a0, const uint16_t* a1, 
     const dim3 grid(p.tiles * p.splits);
     const int threads = p.waves * kWave;
     // one 16-column tile per wave (two per wave measured slower: more registers and a
-    // K split for the same workgroup count); p.mr / 16 row blocks (int4 weights only)
+    // K split for the same workgroup count); p.mr / 16 row blocks
     const int rb = p.mr / 16;
-    if (M > p.mr || (rb != 1 && rb != 2 && rb != 4) || (WF == kWFp4 && rb != 1)) return hipErrorInvalidValue;
+    if (M > p.mr || (rb != 1 && rb != 2 && rb != 4)) return hipErrorInvalidValue;
     hipError_t e;
     if (rb == 1)
         e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF, 1>, grid, threads, p.lds_bytes, s, a)
                            : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF, 1>, grid, threads, p.lds_bytes, s, a);
-    else if constexpr (WF == kWInt4) {
-        if (rb == 2)
-            e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF, 2>, grid, threads, p.lds_bytes, s, a)
-                               : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF, 2>, grid, threads, p.lds_bytes, s, a);
-        else
-            e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF, 4>, grid, threads, p.lds_bytes, s, a)
-                               : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF, 4>, grid, threads, p.lds_bytes, s, a);
-    } else {
-        return hipErrorInvalidValue;
-    }
+    else if (rb == 2)
+        e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF, 2>, grid, threads, p.lds_bytes, s, a)
+                           : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF, 2>, grid, threads, p.lds_bytes, s, a);
+    else
+        e = pro == kSwiGLU ? launch_k(w4_gemv_mfma_kernel<1, kSwiGLU, WF, 4>, grid, threads, p.lds_bytes, s, a)
+                           : launch_k(w4_gemv_mfma_kernel<1, kIdentity, WF, 4>, grid, threads, p.lds_bytes, s, a);
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_splitk_finish(a.partial, p.splits, int64_t(p.mr) * a.npad, a.npad, M, N, out_scale, residual, y, s);
 }

@@ -189,7 +189,7 @@ def test_fp4_gemv_validation(L, inject):
     assert call(W=_fp4(f, q=0)) == NULL
     assert call(W=_fp4(f, s=f() + 2)) == ALIGN
     assert call(M=0) == SHAPE
-    assert call(M=17) == SHAPE
+    assert call(M=65) == SHAPE
     assert call(W=_fp4(f, K=16416, N=8)) == UNSUP        # M <= 4 takes K <= 16384
     assert call(M=5, W=_fp4(f, K=96, N=8)) == UNSUP      # M > 4 takes K % 128 == 0
     assert L.fdec_fp4_gemv_workspace_bytes(1, 9216, 2560) == 0

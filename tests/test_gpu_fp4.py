@@ -111,10 +111,12 @@ def test_fp4_gemv_rejects_what_it_cannot_do():
 
 
 # ---------------------------------------------------------------------------
-# 5..16 rows: the matrix-core kernel with FP4 weights
+# 5..64 rows: the matrix-core kernel with FP4 weights (two or four 16-row blocks
+# per weight load past 16 rows)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("M,K,N", [(16, 14336, 4096), (16, 9216, 2560), (8, 4096, 1000), (5, 256, 24),
-                                   (12, 1024, 512), (16, 4096, 28672)])
+                                   (12, 1024, 512), (16, 4096, 28672), (17, 1024, 512), (32, 9216, 2560),
+                                   (40, 256, 24), (64, 4096, 1000)])
 def test_fp4_gemv_matrix_core_shapes(M, K, N):
     say(f"[fp4 gemv, matrix cores] M={M} K={K} N={N}")
     inp = synth.swiglu_fp4_gemv_inputs(M, K, N, seed=M * 5 + K + N, out_scale=0.5, with_residual=True)
@@ -125,10 +127,11 @@ def test_fp4_gemv_matrix_core_shapes(M, K, N):
         assert_close(run(inp, 0.5, False, swiglu=False), want(inp, 0.5, False, swiglu=False), "identity prologue")
 
 
-def test_fp4_gemv_matrix_core_exact_case():
-    say("[fp4 gemv, matrix cores] integer activations, power-of-two scales, M=16: bit-exact")
+@pytest.mark.parametrize("M", [16, 64])
+def test_fp4_gemv_matrix_core_exact_case(M):
+    say(f"[fp4 gemv, matrix cores] integer activations, power-of-two scales, M={M}: bit-exact")
     rng = np.random.default_rng(13)
-    M, K, N = 16, 9216, 264
+    K, N = 9216, 264
     x = synth.f32_to_bf16_bits(rng.integers(-3, 4, size=(M, K)).astype(np.float32))
     sc = rng.choice(np.array([0x20, 0x28, 0x30], dtype=np.uint8), size=(N, K // 16))   # 2^-3, 2^-2, 2^-1
     W = synth.FP4(rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint32), sc)
