@@ -270,18 +270,21 @@ def bench_extras(torch, F, synth, n_sets_gemv):
     b = T.swiglu_fp4_gemv_bytes(Mg, K, N)
     out["swiglu_fp4_gemv_1x9216x2560"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9,
                                           "frac_of_peak": b / t / 1e9 / PEAK_GBPS, "bytes_per_call": b}
-    # the same weights at 16 rows (the matrix-core kernel with FP4 weights)
+    # the same weights at 16 and 64 rows (the matrix-core kernel with FP4 weights; 64 rows
+    # as four 16-row blocks per weight load)
     gen = torch.Generator().manual_seed(4321)
-    g16 = torch.randn(16, K, generator=gen).to(torch.bfloat16).cuda()
-    u16 = torch.randn(16, K, generator=gen).to(torch.bfloat16).cuda()
-    ys = [torch.empty((16, N), dtype=torch.bfloat16, device="cuda") for _ in fsets]
-    ws16 = F.workspace(F.fp4_gemv_workspace_bytes(16, K, N))
-    fns = [lambda s=s, y=y: F.swiglu_fp4_gemv(g16, u16, s[2], scale, out=y, ws=ws16) for s, y in zip(fsets, ys)]
-    t = bench_repeat(torch, timer, fns, 5) / len(fsets)
-    b = T.swiglu_fp4_gemv_bytes(16, K, N)
-    out["swiglu_fp4_gemv_16x9216x2560"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9,
-                                           "frac_of_peak": b / t / 1e9 / PEAK_GBPS, "bytes_per_call": b}
-    del fsets, ys, ws16
+    for Mb in (16, 64):
+        gb = torch.randn(Mb, K, generator=gen).to(torch.bfloat16).cuda()
+        ub = torch.randn(Mb, K, generator=gen).to(torch.bfloat16).cuda()
+        ys = [torch.empty((Mb, N), dtype=torch.bfloat16, device="cuda") for _ in fsets]
+        wsb = F.workspace(F.fp4_gemv_workspace_bytes(Mb, K, N))
+        fns = [lambda s=s, y=y: F.swiglu_fp4_gemv(gb, ub, s[2], scale, out=y, ws=wsb) for s, y in zip(fsets, ys)]
+        t = bench_repeat(torch, timer, fns, 5) / len(fsets)
+        b = T.swiglu_fp4_gemv_bytes(Mb, K, N)
+        out[f"swiglu_fp4_gemv_{Mb}x9216x2560"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9,
+                                                  "frac_of_peak": b / t / 1e9 / PEAK_GBPS, "bytes_per_call": b}
+        del gb, ub, ys, wsb
+    del fsets
 
     # Llama-3-8B-sized MLP layer at M=16, 6 rotating weight sets
     c = synth.CONFIGS["mlp_llama3_8b_m16"]
