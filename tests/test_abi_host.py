@@ -311,3 +311,17 @@ def test_python_binding_rejects_cpu_tensors():
         F.add_rmsnorm(x, x.clone(), torch.ones(512, dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         F.add_rmsnorm(x.float(), x.clone(), torch.ones(512, dtype=torch.bfloat16))
+
+
+def test_matrix_core_kernel_has_no_inline_asm():
+    # The compiler inserts the wait states between an MFMA and a later instruction that
+    # writes the registers the MFMA still reads only for instructions it can see; an
+    # inline-asm decode next to MFMAs overwrote an accumulator in flight.  The
+    # matrix-core source must stay asm-free.
+    src = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "memory_bound_decode_add_amd", "csrc", "w4_gemv_mfma.hip")
+    text = open(src).read()
+    code = re.sub(r"//[^\n]*", "", text)
+    assert not re.search(r"\basm\b|__asm__", code), "inline asm in the matrix-core kernel source"
+    # the int4 decode it uses is its own, not the asm helpers of the VALU kernels
+    assert "decode_int4x8_biased(" not in code and "and_or(" not in code and "xor_opaque(" not in code
