@@ -404,7 +404,8 @@ FDEC_API int fdec_w4_dequant(const fdec_w4* W, float* w_out, fdec_stream stream)
  * Tuning and test controls (process-wide, not thread-safe; not for production use).
  * fdec_set_gemv_split(k): force the split-K GEMV kernel with K split into about k
  *   parts per column tile (0 restores the built-in choice of kernel and split; values
- *   that do not fit the shape are clamped).
+ *   that do not fit the shape are clamped).  Calls with more than 16 rows ignore it:
+ *   only the matrix-core kernel takes them.
  * fdec_set_gemv_tiling(waves, cols_per_workgroup): force the column-owning GEMV
  *   kernel's workgroup shape (1..14 dot waves, each owning at most 4 columns, next to
  *   the staging waves, 16 waves in all); (0, 0) restores the built-in choice.  Shapes
