@@ -116,6 +116,13 @@ def test_swiglu_gemv_row_blocks_with_residual(M, K, N):
     ws.fill_(0xFF)
     y2 = F.to_bits(F.swiglu_w4_gemv(g, u, W, s, res, ws=ws))
     assert_bits_equal(y, y2, "repeat")
+    # a forced split-K (a 16-row VALU kernel) does not apply past 16 rows
+    try:
+        F.set_gemv_split(4)
+        y3 = F.to_bits(F.swiglu_w4_gemv(g, u, W, s, res))
+    finally:
+        F.set_gemv_split(0)
+    assert_bits_equal(y, y3, "forced split ignored")
     # in place: y is the residual
     F.swiglu_w4_gemv(g, u, W, s, res, out=res)
     torch.cuda.synchronize()
