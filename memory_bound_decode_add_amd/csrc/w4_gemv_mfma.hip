@@ -29,8 +29,8 @@
 // group, so MFMA j of group g covers the k-blocks (8 k each) 16g + 4s + j, s = 0..3.
 //
 // Decode.  The packed words are decoded as in the VALU column kernel, with their fp16
-// offsets left in (1032 + q at even nibble positions, 1152 + 16 q at odd ones, six
-// integer ops per word), in the pair order (j0, j4, j1, j5, j2, j6, j3, j7).  The
+// offsets left in (1032 + q at even nibble positions, 1152 + 16 q at odd ones, five
+// integer ops per word here), in the pair order (j0, j4, j1, j5, j2, j6, j3, j7).  The
 // offsets are removed inside the matrix core: each group's accumulation starts from
 // the product of a constant matrix of -1032 / -1152 with the same activation operands.
 // (A bf16 operand path was measured slower in the main loop, and bf16 loses 3 bits of
