@@ -239,3 +239,35 @@ def test_split_k_ignores_workspace_contents(M, K, N, split):
             say(f"  seed {seed}: worst err/bound {assert_close(got, ref, 'y'):.3f}")
     finally:
         F.set_gemv_split(0)
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 9216, 2560), (16, 14336, 4096)])
+def test_gemv_graph_replays_match_eager(M, K, N):
+    # the split-K GEMV (main kernel + finish kernel) captured once and replayed several
+    # times, with other eager work and synchronisations between the replays
+    say(f"[gemv] graph replays M={M} K={K} N={N}")
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=M + K + N, out_scale=0.5, with_residual=True)
+    g, u, W, res = to_dev(inp)
+    s = F.scalar(0.5)
+    ws = F.workspace(F.gemv_workspace_bytes(M, K, N))
+    ref = F.to_bits(F.swiglu_w4_gemv(g, u, W, s, res, ws=ws))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        F.swiglu_w4_gemv(g, u, W, s, res, out=y, ws=ws)          # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        F.swiglu_w4_gemv(g, u, W, s, res, out=y, ws=ws)
+    for i in range(3):
+        y.fill_(0)
+        ws.fill_(0xFF)                                            # workspace contents must not matter
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(F.to_bits(y), ref, f"replay {i}")
+        F.swiglu_w4_gemv(g, u, W, s, res, ws=ws)                  # eager work between replays
+        torch.cuda.synchronize()
+    assert_close(ref, O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 0.5, inp.residual), "eager vs oracle")
