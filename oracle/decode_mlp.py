@@ -46,7 +46,7 @@ Readings where the pages are silent (each is also listed in the design notes):
   multiplier) are read as weight-only quantisation: the activation stays the unrounded
   SwiGLU prologue value.  E2M1 codes are packed like the int4 nibbles (code of k = 8*kb
   + j in bits [4j, 4j+4) of word (n, kb)); block scales are E4M3 ('fn': no infinities)
-  bytes [K/16, N], scale (b, n) applying to k in [16 b, 16 b + 16).
+  bytes [N, K/16], scale (n, b) applying to k in [16 b, 16 b + 16) of column n.
 """
 from __future__ import annotations
 
@@ -57,7 +57,7 @@ __all__ = [
     "silu", "silu_mul", "swiglu_w4_gemv", "w4_gemv", "add_rmsnorm", "mlp_decode",
     "mlp_chain", "product_form_gemv", "factored_form_gemv",
     "product_buffer_bytes", "unfused_act_gemv", "unfused_product_gemv",
-    "add_rmsnorm_eager", "mlp_decode_unfused",
+    "add_rmsnorm_eager",
     "add_rmsnorm_gemv_swiglu", "mlp_decode2", "mlp_chain2",
     "FP4_BLOCK", "e2m1_decode", "e4m3_decode", "fp4_unpack", "fp4_dequant", "swiglu_fp4_gemv", "fp4_gemv",
 ]
@@ -372,22 +372,6 @@ def add_rmsnorm_eager(x, r, w, eps=1e-6):
     t = round_bf16(hs / np.sqrt(ms + float(eps)))
     y = round_bf16(t * bf16_to_f64(w))
     return f64_to_bf16(hs), f64_to_bf16(y)
-
-
-def mlp_decode_unfused(x, r, norm_w, gu_q, gu_s, d_q, d_s, out_scale=0.5, eps=1e-6,
-                       residual_in_epilogue=True, *, n_chunk=4096):
-    """The layer as the unfused sequence computes it: eager norm, gate_up GEMV, eager
-    SwiGLU (two bf16 round trips), down GEMV, separate scale, separate residual add."""
-    h, y = add_rmsnorm_eager(x, r, norm_w, eps)
-    gu_b = f64_to_bf16(_chunked_gemv(bf16_to_f64(y), gu_q, gu_s, n_chunk))
-    I = gu_b.shape[1] // 2
-    s1 = round_bf16(silu(bf16_to_f64(gu_b[:, :I])))
-    act = round_bf16(s1 * bf16_to_f64(gu_b[:, I:]))
-    z = round_bf16(_chunked_gemv(act, d_q, d_s, n_chunk))
-    o = round_bf16(z * float(out_scale))
-    if residual_in_epilogue:
-        o = round_bf16(o + bf16_to_f64(h))
-    return {"h": h, "y": y, "gu": gu_b, "out": f64_to_bf16(o)}
 
 
 # ----------------------------------------------------------------------------
