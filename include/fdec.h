@@ -393,8 +393,10 @@ FDEC_API int fdec_unfused_mlp_decode(const fdec_mlp_layer* layer, int32_t M,
                                      fdec_stream stream);
 
 /*
- * Test hooks: run the GEMV's in-register int4 decode on the whole matrix and write
- * the result ([P4] section 5, prologue fusion).  q_out: int8 [K][N] (the integer
+ * Test hooks: run the in-register int4 decode on the whole matrix and write the result
+ * ([P4] section 5, prologue fusion).  The column, split-K and matrix-core GEMV kernels
+ * all decode with this one routine (packed word -> fp16 values that keep a known
+ * offset); the hooks run it and remove the offsets.  q_out: int8 [K][N] (the integer
  * weights); w_out: fp32 [K][N] (q * scale, exact).  Output may not overlap W.
  */
 FDEC_API int fdec_w4_unpack(const fdec_w4* W, int8_t* q_out, fdec_stream stream);

@@ -27,65 +27,55 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
-// int4 decode.  A packed word holds weights j = 0..7 of one column in bits
-// [4j, 4j+4) as two's-complement nibbles.  XOR with 0x8 per nibble turns the code
-// into q + 8 (offset binary, 0..15).  OR-ing 4-bit fields into the mantissa of the
-// fp16 value 1024 (0x6400) gives exact fp16 numbers:
-//   bits 0..3 of a half  -> 1024 + (q + 8)        -> minus 1032            = q
-//   bits 4..7 of a half  -> 1024 + 16 (q + 8)     -> times 1/16, minus 72  = q
-// so one word becomes four half2 pairs of exact integer weights, ordered
-// (j0, j4), (j1, j5), (j2, j6), (j3, j7).  The activations are stored in the
-// same pair order, so a dot2 of matching pairs sums the right products.
+// int4 decode, shared by every int4 kernel (column, split-K, matrix-core) and by the
+// unpack/dequant test hooks.  A packed word holds weights j = 0..7 of one column in
+// bits [4j, 4j+4) as two's-complement nibbles.  XOR-ing a nibble with 8 turns its code
+// into q + 8 (offset binary, 0..15); placing that 4-bit field in the mantissa of the
+// fp16 value 1024 (0x6400) gives an exact fp16 number:
+//   field in bits 0..3 of a half  -> 1024 + (q + 8)     = 1032 + q
+//   field in bits 4..7 of a half  -> 1024 + 16 (q + 8)  = 1152 + 16 q
+// One word becomes four half2 pairs ordered (j0, j4), (j1, j5), (j2, j6), (j3, j7)
+// ("pair order"); the activations are stored in the same order, so a dot2 (or an MFMA
+// k-slot) of matching pairs sums the right products.  The kernels keep the offsets in
+// and remove them once per chunk or group; decode_int4x8 removes them per value.
+//
+// Each field is K ^ (v & m): inside the nibble mask m the XOR flips the code to offset
+// binary, outside it are the bits of 1024, which share none with m, so K holds 1024's
+// bits and an 8 in each masked nibble (0x64086408 for the low nibbles of both halves,
+// 0x64806480 for the high ones).  The XOR commutes with the shift by 8, so the fields of
+// w >> 8 use the same constants.  With the masks in scalar registers (kernel arguments:
+// a VOP3 instruction takes no literal constant on this target) each field is one
+// v_bitop3_b32, five VALU instructions per word, all visible to the compiler, which
+// therefore places the wait states an MFMA still reading its operands requires.
 // ---------------------------------------------------------------------------
 struct Q4x2 { half2_t p04, p15, p26, p37; };
 
-// (x & mask) | bits in one VOP3 instruction.  CDNA's VOP3 encoding takes no literal
-// constants and at most one scalar operand, so the mask comes from a scalar register
-// and the OR-ed bits from a vector register (left to the compiler to materialise once).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));
-    return r;
-}
+struct DecodeMasks { uint32_t lo, hi; };        // 0x000F000F and 0x00F000F0, from the host
+constexpr uint32_t kDecodeMaskLo = 0x000F000Fu;
+constexpr uint32_t kDecodeMaskHi = 0x00F000F0u;
 
-// w ^ bits, kept opaque to the optimiser: a plain XOR of a conditionally loaded word
-// gets folded into the load's branch, which forces a wait for the load right there.
-__device__ __forceinline__ uint32_t xor_opaque(uint32_t w, uint32_t bits) {
-    uint32_t r;
-    asm("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(bits), "v"(w));
-    return r;
-}
-
-__device__ __forceinline__ Q4x2 decode_int4x8(uint32_t w) {
-    const uint32_t x = xor_opaque(w, 0x88888888u);
-    const uint32_t t = x >> 8;
-    const uint32_t one024 = 0x64006400u;
-    const half2_t a = __builtin_bit_cast(half2_t, and_or(x, 0x000F000Fu, one024));
-    const half2_t b = __builtin_bit_cast(half2_t, and_or(x, 0x00F000F0u, one024));
-    const half2_t c = __builtin_bit_cast(half2_t, and_or(t, 0x000F000Fu, one024));
-    const half2_t d = __builtin_bit_cast(half2_t, and_or(t, 0x00F000F0u, one024));
-    const half2_t off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const half2_t off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
-    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+__device__ __forceinline__ Q4x2 decode_int4x8_biased(uint32_t w, DecodeMasks dm) {
+    const uint32_t t = w >> 8;
+    const uint32_t k_lo = 0x64086408u, k_hi = 0x64806480u;
     Q4x2 q;
-    q.p04 = a + off_lo;
-    q.p15 = b * sixteenth + off_hi;   // exact: b/16 is an integer in [64, 79]
-    q.p26 = c + off_lo;
-    q.p37 = d * sixteenth + off_hi;
+    q.p04 = __builtin_bit_cast(half2_t, k_lo ^ (w & dm.lo));
+    q.p15 = __builtin_bit_cast(half2_t, k_hi ^ (w & dm.hi));
+    q.p26 = __builtin_bit_cast(half2_t, k_lo ^ (t & dm.lo));
+    q.p37 = __builtin_bit_cast(half2_t, k_hi ^ (t & dm.hi));
     return q;
 }
 
-// The same pairs with the offsets left in: 1032 + q at even positions (j0, j4, j2, j6),
-// 1152 + 16 q at odd positions (j1, j5, j3, j7).  Six integer ops per word.
-__device__ __forceinline__ Q4x2 decode_int4x8_biased(uint32_t w) {
-    const uint32_t x = xor_opaque(w, 0x88888888u);
-    const uint32_t t = x >> 8;
-    const uint32_t one024 = 0x64006400u;
-    Q4x2 q;
-    q.p04 = __builtin_bit_cast(half2_t, and_or(x, 0x000F000Fu, one024));
-    q.p15 = __builtin_bit_cast(half2_t, and_or(x, 0x00F000F0u, one024));
-    q.p26 = __builtin_bit_cast(half2_t, and_or(t, 0x000F000Fu, one024));
-    q.p37 = __builtin_bit_cast(half2_t, and_or(t, 0x00F000F0u, one024));
+// The same pairs as exact integer weights q (offsets removed: v - 1032 at even
+// positions, v / 16 - 72 at odd ones; every step is exact in fp16).
+__device__ __forceinline__ Q4x2 decode_int4x8(uint32_t w, DecodeMasks dm) {
+    Q4x2 q = decode_int4x8_biased(w, dm);
+    const half2_t off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half2_t off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    q.p04 = q.p04 + off_lo;
+    q.p15 = q.p15 * sixteenth + off_hi;   // b / 16 is an integer in [64, 79]
+    q.p26 = q.p26 + off_lo;
+    q.p37 = q.p37 * sixteenth + off_hi;
     return q;
 }
 

@@ -29,7 +29,7 @@ inline dim3 grid_for(int64_t n, int per_block = 256) {
 // P[8kb + j][n] = act[8kb + j] * q * scale, fp32
 __global__ void product_kernel(const uint16_t* __restrict__ g, const uint16_t* __restrict__ u,
                                const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
-                               int KB, int N, float* __restrict__ P) {
+                               int KB, int N, float* __restrict__ P, DecodeMasks dm) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= int64_t(KB) * N) return;
     const int kb = int(i / N), n = int(i % N);
@@ -43,7 +43,7 @@ __global__ void product_kernel(const uint16_t* __restrict__ g, const uint16_t* _
         act[2 * j] = silu_f32(bf16_lo(ga[j])) * bf16_lo(ua[j]);
         act[2 * j + 1] = silu_f32(bf16_hi(ga[j])) * bf16_hi(ua[j]);
     }
-    const Q4x2 d = decode_int4x8(qw[int64_t(n) * KB + kb]);      // word (n, kb) of [N][K/8]
+    const Q4x2 d = decode_int4x8(qw[int64_t(n) * KB + kb], dm);      // word (n, kb) of [N][K/8]
     const half2_t p[4] = {d.p04, d.p15, d.p26, d.p37};
     const float s = bf16_to_f32(sc[int64_t(kb / 16) * N + n]);
 #pragma unroll
@@ -246,7 +246,8 @@ hipError_t launch_unfused_product(const uint16_t* g, const uint16_t* u, const ui
                                   const uint16_t* residual, uint16_t* y, float* P,
                                   hipStream_t s) {
     const int KB = K / 8;
-    product_kernel<<<grid_for(int64_t(KB) * N), 256, 0, s>>>(g, u, qw, sc, KB, N, P);
+    product_kernel<<<grid_for(int64_t(KB) * N), 256, 0, s>>>(g, u, qw, sc, KB, N, P,
+                                                            DecodeMasks{kDecodeMaskLo, kDecodeMaskHi});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int tiles = (N + 63) / 64, chunks = (K + kProdChunk - 1) / kProdChunk;

@@ -87,7 +87,7 @@ __device__ __forceinline__ void stage_act(uint32_t ga, uint32_t ua, bool live, i
 }
 
 // sum over 32 k: four packed words against 64 bytes of staged activation
-__device__ __forceinline__ float dot32(const uint4 w, const _Float16* act) {
+__device__ __forceinline__ float dot32(const uint4 w, const _Float16* act, DecodeMasks dm) {
     const uint4 a0 = *reinterpret_cast<const uint4*>(act);
     const uint4 a1 = *reinterpret_cast<const uint4*>(act + 8);
     const uint4 a2 = *reinterpret_cast<const uint4*>(act + 16);
@@ -97,7 +97,7 @@ __device__ __forceinline__ float dot32(const uint4 w, const _Float16* act) {
     float v = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const Q4x2 q = decode_int4x8(wd[j]);
+        const Q4x2 q = decode_int4x8(wd[j], dm);
         v = dot2(q.p04, __builtin_bit_cast(half2_t, av[j].x), v);
         v = dot2(q.p15, __builtin_bit_cast(half2_t, av[j].y), v);
         v = dot2(q.p26, __builtin_bit_cast(half2_t, av[j].z), v);
@@ -133,6 +133,7 @@ struct ColArgs {
     const uint4* cp_src;
     uint4* cp_dst;
     int cp_n16;
+    DecodeMasks dm;         // int4 decode field masks (scalar registers)
 };
 
 // Staged activation of the column kernel, per row: fp16 in the layout [quarter q][chunk
@@ -458,7 +459,7 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
                 const uint32_t wd[4] = {wv[i][j].x, wv[i][j].y, wv[i][j].z, wv[i][j].w};
                 Q4x2 q[4];
 #pragma unroll
-                for (int h = 0; h < 4; ++h) q[h] = decode_int4x8_biased(wd[h]);
+                for (int h = 0; h < 4; ++h) q[h] = decode_int4x8_biased(wd[h], a.dm);
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     float d = -eb[m].y;
@@ -534,6 +535,7 @@ struct SplitArgs {
     const uint16_t* residual;
     uint16_t* y;
     float* partial;         // [splits][M][tiles*64]
+    DecodeMasks dm;         // int4 decode field masks (scalar registers)
 };
 
 template <int MR, int GW, int PRO>
@@ -622,7 +624,7 @@ __global__ __launch_bounds__(256) void w4_gemv_split_kernel(SplitArgs a) {
             const _Float16* act = act_s + (lg * MR + m) * kGroup + kr * 32;
             const float e = esc_s[lg * MR + m];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[m][c] = fmaf(dot32(wv[i][c], act), s4[c] * e, acc[m][c]);
+            for (int c = 0; c < 4; ++c) acc[m][c] = fmaf(dot32(wv[i][c], act, a.dm), s4[c] * e, acc[m][c]);
         }
     }
 
@@ -802,12 +804,14 @@ hipError_t launch_split(Prologue pro, const SplitArgs& a, const GemvPlan& p, hip
 
 int round_gw(int gw) { return gw <= 1 ? 1 : (gw <= 2 ? 2 : 4); }
 
-// ---- test hooks: the same in-register decode, written out ----
-__global__ void w4_unpack_kernel(const uint32_t* __restrict__ qw, int KB, int N, int8_t* __restrict__ q) {
+// ---- test hooks: the decode every int4 kernel runs (decode_int4x8_biased), with its
+// offsets removed (decode_int4x8), written out ----
+__global__ void w4_unpack_kernel(const uint32_t* __restrict__ qw, int KB, int N, int8_t* __restrict__ q,
+                                 DecodeMasks dm) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;     // word (n, kb)
     if (i >= int64_t(KB) * N) return;
     const int n = int(i / KB), kb = int(i % KB);
-    const Q4x2 d = decode_int4x8(qw[i]);
+    const Q4x2 d = decode_int4x8(qw[i], dm);
     const half2_t p[4] = {d.p04, d.p15, d.p26, d.p37};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -817,11 +821,11 @@ __global__ void w4_unpack_kernel(const uint32_t* __restrict__ qw, int KB, int N,
 }
 
 __global__ void w4_dequant_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
-                                  int KB, int N, float* __restrict__ w) {
+                                  int KB, int N, float* __restrict__ w, DecodeMasks dm) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= int64_t(KB) * N) return;
     const int n = int(i / KB), kb = int(i % KB);
-    const Q4x2 d = decode_int4x8(qw[i]);
+    const Q4x2 d = decode_int4x8(qw[i], dm);
     const half2_t p[4] = {d.p04, d.p15, d.p26, d.p37};
     const float s = bf16_to_f32(sc[int64_t(kb / 16) * N + n]);
 #pragma unroll
@@ -1024,6 +1028,7 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     const GemvPlan p = plan_gemv(M, K, N);
     if (p.kind == kColumnOwning) {
         ColArgs a{};
+        a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};
         a.a0 = a0;
         a.a1 = a1;
         a.lda = lda;
@@ -1047,6 +1052,7 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     }
     if (p.kind == kMfma) return launch_mfma(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
     SplitArgs a{};
+    a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};
     a.a0 = a0;
     a.a1 = a1;
     a.lda = lda;
@@ -1079,14 +1085,15 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
 
 hipError_t launch_w4_unpack(const uint32_t* qw, int K, int N, int8_t* q, hipStream_t s) {
     const int64_t n = int64_t(K / 8) * N;
-    w4_unpack_kernel<<<dim3((n + 255) / 256), 256, 0, s>>>(qw, K / 8, N, q);
+    w4_unpack_kernel<<<dim3((n + 255) / 256), 256, 0, s>>>(qw, K / 8, N, q, DecodeMasks{kDecodeMaskLo, kDecodeMaskHi});
     return hipGetLastError();
 }
 
 hipError_t launch_w4_dequant(const uint32_t* qw, const uint16_t* sc, int K, int N, float* w,
                              hipStream_t s) {
     const int64_t n = int64_t(K / 8) * N;
-    w4_dequant_kernel<<<dim3((n + 255) / 256), 256, 0, s>>>(qw, sc, K / 8, N, w);
+    w4_dequant_kernel<<<dim3((n + 255) / 256), 256, 0, s>>>(qw, sc, K / 8, N, w,
+                                                             DecodeMasks{kDecodeMaskLo, kDecodeMaskHi});
     return hipGetLastError();
 }
 
@@ -1111,6 +1118,7 @@ hipError_t launch_norm_gemv_swiglu(const uint16_t* x, const uint16_t* r, const u
     GemvPlan p;
     if (!plan_column_pair(M, K, I, p)) return hipErrorInvalidValue;
     ColArgs a{};
+    a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};
     a.a0 = x;
     a.a1 = r;
     a.lda = K;
@@ -1149,6 +1157,7 @@ hipError_t launch_gemv_copy(Prologue pro, const uint16_t* a0, int64_t lda, const
     p.groups = K / kGroup;
     if (pro != kIdentity || !plan_column(M, K, N, p) || cp_bytes % 16) return hipErrorInvalidValue;
     ColArgs a{};
+    a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};
     a.a0 = a0;
     a.lda = lda;
     a.qw = reinterpret_cast<const uint4*>(qw);

@@ -87,25 +87,11 @@ struct MfmaArgs {
     uint32_t m_lo, m_hi;    // int4 decode field masks 0x000F000F and 0x00F000F0
 };
 
-// One packed word -> 8 fp16 values with their offsets, in pair order: the decode of
-// the VALU kernels (offset binary OR-ed into the mantissa of 1024, 1032 + q at even and
-// 1152 + 16 q at odd positions), written as plain integer code.  The compiler spaces an
-// MFMA and a later instruction that writes the registers the MFMA still reads (its
-// accumulator input is read over several passes) only for instructions it can see; an
-// inline-asm decode next to MFMAs can overwrite an accumulator in flight.
-//
-// Each field is K ^ (v & m): inside the mask m the nibble is XOR-ed with 8 (two's
-// complement -> offset binary), outside it are the bits of 1024, which share none with
-// m, so K = 1024's bits | 8 in each masked nibble (0x64086408 for the low nibbles of
-// both halves, 0x64806480 for the high ones).  The XOR commutes with the shift by 8, so
-// the fields of w >> 8 use the same constants.  The masks come in the kernel arguments
-// (scalar registers), which lets each field compile to one v_bitop3_b32.
-struct DecodeMasks { uint32_t lo, hi; };
+// One packed word -> 8 fp16 values with their offsets, in pair order: the decode every
+// int4 kernel runs (decode_int4x8_biased, plain integer code the compiler sees, so it
+// spaces an MFMA and a later instruction that writes registers the MFMA still reads).
 __device__ __forceinline__ f16x8_t decode_f16x8_biased(uint32_t w, DecodeMasks dm) {
-    const uint32_t t = w >> 8;
-    const uint32_t k_lo = 0x64086408u, k_hi = 0x64806480u;
-    return __builtin_bit_cast(f16x8_t, make_uint4(k_lo ^ (w & dm.lo), k_hi ^ (w & dm.hi),
-                                                  k_lo ^ (t & dm.lo), k_hi ^ (t & dm.hi)));
+    return __builtin_bit_cast(f16x8_t, decode_int4x8_biased(w, dm));
 }
 
 // One staging item: 8 consecutive activation values of one row.  The 16 lanes of a
@@ -430,8 +416,8 @@ hipError_t launch_mfma_wf(Prologue pro, const uint16_t* a0, const uint16_t* a1, 
     a.residual = residual;
     a.y = y;
     a.partial = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
-    a.m_lo = 0x000F000Fu;
-    a.m_hi = 0x00F000F0u;
+    a.m_lo = kDecodeMaskLo;
+    a.m_hi = kDecodeMaskHi;
     const dim3 grid(p.tiles * p.splits);
     const int threads = p.waves * kWave;
     // one 16-column tile per wave (two per wave measured slower: more registers and a

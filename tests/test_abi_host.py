@@ -313,15 +313,19 @@ def test_python_binding_rejects_cpu_tensors():
         F.add_rmsnorm(x.float(), x.clone(), torch.ones(512, dtype=torch.bfloat16))
 
 
-def test_matrix_core_kernel_has_no_inline_asm():
+def test_kernel_sources_have_no_inline_asm():
     # The compiler inserts the wait states between an MFMA and a later instruction that
     # writes the registers the MFMA still reads only for instructions it can see; an
-    # inline-asm decode next to MFMAs overwrote an accumulator in flight.  The
-    # matrix-core source must stay asm-free.
-    src = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                       "memory_bound_decode_add_amd", "csrc", "w4_gemv_mfma.hip")
-    text = open(src).read()
-    code = re.sub(r"//[^\n]*", "", text)
-    assert not re.search(r"\basm\b|__asm__", code), "inline asm in the matrix-core kernel source"
-    # the int4 decode it uses is its own, not the asm helpers of the VALU kernels
-    assert "decode_int4x8_biased(" not in code and "and_or(" not in code and "xor_opaque(" not in code
+    # inline-asm decode next to MFMAs overwrote an accumulator in flight.  Every device
+    # source stays asm-free, and the int4 kernels share one compiler-visible decoder.
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "memory_bound_decode_add_amd", "csrc")
+    names = [n for n in os.listdir(csrc) if n.endswith((".hip", ".h", ".cpp"))]
+    assert "w4_gemv_mfma.hip" in names and "device_common.h" in names
+    for n in names:
+        code = re.sub(r"//[^\n]*", "", open(os.path.join(csrc, n)).read())
+        assert not re.search(r"\basm\b|__asm__", code), f"inline asm in {n}"
+    for n in ("w4_gemv.hip", "w4_gemv_mfma.hip", "unfused.hip"):
+        code = open(os.path.join(csrc, n)).read()
+        assert "decode_int4x8" in code, n
+        assert not re.search(r"__device__[^;{]*\bdecode_int4x8", code), f"{n} defines its own int4 decode"
