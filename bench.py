@@ -112,26 +112,29 @@ def bench_gemv(torch, F, synth, steps, warmup, n_sets):
         g, u, W, y = sets[i % n_sets]
         return lambda: F.swiglu_w4_gemv(g, u, W, scale, None, out=y, ws=ws)
 
-    # graphs: one per rotation of the sets, plus a remainder
-    R = min(steps, n_sets)
-    g_main = capture(torch, [step(i) for i in range(R)])
-    rem = steps % R
+    # One graph of a full rotation (every set once, in order) and one of the first
+    # `steps mod n_sets` sets.  The timed region is floor(steps / n_sets) full rotations and
+    # then the remainder, right after a full rotation: whatever `steps` is, a timed call's
+    # set was last read n_sets calls earlier, with n_sets * bytes_per_call (more than twice
+    # the Infinity Cache) read in between.
+    g_full = capture(torch, [step(i) for i in range(n_sets)])
+    rem = steps % n_sets
     g_rem = capture(torch, [step(i) for i in range(rem)]) if rem else None
-    # warmup: at least `warmup` steps, and every graph replayed once (uploads it)
     done = 0
-    while done < max(warmup, 1):
-        g_main.replay()
-        done += R
-    if g_rem is not None:
+    while done < max(warmup, n_sets):
+        g_full.replay()
+        done += n_sets
+    if g_rem is not None:                  # upload it, then a full rotation again
         g_rem.replay()
-        done += rem
+        g_full.replay()
+        done += rem + n_sets
     torch.cuda.synchronize()
 
     timer = Timer(torch)
 
     def timed():
-        for _ in range(steps // R):
-            g_main.replay()
+        for _ in range(steps // n_sets):
+            g_full.replay()
         if g_rem is not None:
             g_rem.replay()
 
@@ -139,18 +142,23 @@ def bench_gemv(torch, F, synth, steps, warmup, n_sets):
     us = elapsed / steps * 1e6
     gbps = bytes_per_call / (elapsed / steps) / 1e9
 
-    # the spread: 20 separately timed rounds of R back-to-back calls, each followed by an
-    # untimed 12 MB copy (so that clock and cache drift hit every round alike)
+    # the spread: 20 separately timed rotations, each followed by an untimed 12 MB copy (so
+    # that clock and cache drift hit every round alike)
     cpy_src = torch.randn(int(12.2e6 / 8), device="cuda")
     cpy_dst = torch.empty_like(cpy_src)
     rounds = []
     for _ in range(20):
-        rounds.append(timer(g_main.replay) / R * 1e6)
+        rounds.append(timer(g_full.replay) / n_sets * 1e6)
         torch.neg(cpy_src, out=cpy_dst)
     torch.cuda.synchronize()
     del cpy_src, cpy_dst
-    spread = {"rounds": len(rounds), "calls_per_round": R, "median_us": float(np.median(rounds)),
+    spread = {"rounds": len(rounds), "calls_per_round": n_sets, "median_us": float(np.median(rounds)),
               "p10_us": float(np.percentile(rounds, 10)), "p90_us": float(np.percentile(rounds, 90))}
+
+    ceiling = measured_ceiling(torch, F, timer, sets, n_sets, K, N)
+    ceiling["gemv_frac_of_read_only"] = ceiling["read_only_us"] / us
+    ceiling["gemv_us_above_floor"] = us - ceiling["empty_kernel_us"]
+    ceiling["read_only_us_above_floor"] = ceiling["read_only_us"] - ceiling["empty_kernel_us"]
 
     # a plain copy kernel of known size, for scaling the HBM byte counters of a profiled run
     src = torch.randn(CALIB_FLOATS, device="cuda")
@@ -166,9 +174,37 @@ def bench_gemv(torch, F, synth, steps, warmup, n_sets):
     for _ in range(20):
         lat.append(timer(lambda: F.swiglu_w4_gemv(g, u, W, scale, None, out=y, ws=ws)))
     plan = {"workspace_bytes": F.gemv_workspace_bytes(M, K, N)}
+    timed_sets = min(steps, n_sets)
     return {"us_per_call": us, "gbps": gbps, "elapsed_s": elapsed, "bytes_per_call": bytes_per_call,
-            "warmup_steps_run": done, "graph_steps": R, "eager_call_us_median": float(np.median(lat)) * 1e6,
-            "rounds": spread, **plan}
+            "warmup_steps_run": done, "timed_steps": steps, "rotating_input_sets": n_sets,
+            "distinct_sets_timed": timed_sets, "bytes_read_between_reuses_of_a_set": n_sets * bytes_per_call,
+            "eager_call_us_median": float(np.median(lat)) * 1e6, "rounds": spread, "measured_ceiling": ceiling,
+            **plan}
+
+
+def measured_ceiling(torch, F, timer, sets, n_sets, K, N):
+    """The per-call floor and ceiling the GEMV is measured against, timed like it (one
+    graph of n_sets back-to-back launches, replayed): an empty kernel on the GEMV's grid,
+    and a kernel that only reads the GEMV's bytes in the column kernel's order (its
+    workgroup's columns' packed weights, all of g and u, its columns' group scales) over
+    the same rotating sets, writing one word per workgroup."""
+    wgs = 256
+    cols = N // wgs
+    per_wg = cols * (K // 32)                 # 16-byte chunks of the workgroup's columns
+    sink = torch.empty(wgs, dtype=torch.int32, device="cuda")
+    g_empty = capture(torch, [lambda: F.empty_kernel(wgs, 1024) for _ in range(n_sets)])
+    g_read = capture(torch, [lambda s=s: F.read_ceiling(s[2].qweight, per_wg, s[0], s[1], s[2].scales, K // 128,
+                                                        2 * N, 2 * cols, wgs, sink) for s in sets])
+    for g in (g_empty, g_read, g_read):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = 10
+    t_empty = timer(g_empty.replay, reps) / (reps * n_sets)
+    t_read = timer(g_read.replay, reps) / (reps * n_sets)
+    del g_empty, g_read
+    return {"empty_kernel_us": t_empty * 1e6, "read_only_us": t_read * 1e6,
+            "read_only_bytes": K * N // 2 + 2 * K * 2 + (K // 128) * 2 * N,
+            "timing": f"graph of {n_sets} back-to-back launches over the rotating sets, {reps} replays"}
 
 
 def bench_repeat(torch, timer, fns, n_rep):
@@ -393,15 +429,43 @@ def bench_extras(torch, F, synth, n_sets_gemv):
     return out
 
 
+def host_info():
+    """The host the CPU baseline runs on: core counts, affinity, CPU model, BLAS."""
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        info["affinity_cpus"] = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    info["cpu_model"] = model
+    blas_threads, blas_lib = 1, None
+    try:
+        from threadpoolctl import threadpool_info
+        for d in threadpool_info():
+            if d.get("user_api") == "blas":
+                blas_threads = max(blas_threads, int(d.get("num_threads", 1)))
+                blas_lib = f"{d.get('internal_api')} {d.get('version')} ({os.path.basename(d.get('filepath', ''))})"
+    except Exception:
+        pass
+    info["blas"] = blas_lib
+    info["blas_threads"] = blas_threads
+    return info
+
+
 def cpu_baseline(synth, seconds):
     """The fp64 oracle on the metric's workload, repeated for about `seconds` of CPU time."""
     import oracle as O
     from memory_bound_decode_add_amd import traffic as T
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
-    except Exception:
-        blas = 1
+    host = host_info()
+    blas = host["blas_threads"]
     c = synth.CONFIGS[WORKLOAD]
     inp = synth.swiglu_gemv_inputs(c["M"], c["K"], c["N"], seed=0, out_scale=c["out_scale"])
     n = 0
@@ -414,7 +478,7 @@ def cpu_baseline(synth, seconds):
             break
     b = T.swiglu_w4_gemv_bytes(c["M"], c["K"], c["N"])
     return {"value": b * n / el / 1e9, "unit": "GB/s", "cores": int(blas), "kind": "oracle",
-            "us_per_call": el / n * 1e6,
+            "us_per_call": el / n * 1e6, "host": host,
             "sample": f"{n} oracle calls on input set 0 of {WORKLOAD} ({el:.1f} s, numpy fp64; elementwise on 1 "
                       f"thread, the fp64 matmul on {blas} BLAS threads)"}
 
@@ -466,6 +530,8 @@ def main():
         sys.exit(2)
     if a.steps < 1:
         sys.exit("--steps must be >= 1")
+    if a.sets < 2:
+        sys.exit("--sets must be >= 2")
 
     import torch
     import memory_bound_decode_add_amd as F
@@ -480,6 +546,8 @@ def main():
     res = bench_gemv(torch, F, synth, a.steps, a.warmup, a.sets)
     log(f"[bench] gemv: {res['us_per_call']:.3f} us/call, {res['gbps']:.1f} GB/s")
     extras = bench_extras(torch, F, synth, a.sets) if a.only == "all" else {}
+    if extras:
+        extras[f"measured_ceiling_{WORKLOAD}"] = res["measured_ceiling"]
     cpu = cpu_baseline(synth, a.cpu_seconds) if a.only == "all" and a.cpu_seconds > 0 else None
 
     traffic = load_traffic()
@@ -499,8 +567,11 @@ def main():
         "dtype": "f16*i4->f32",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "M": 1, "K": 9216, "N": 2560, "out_scale": 1.0,
-                   "rotating_input_sets": a.sets, "bytes_per_call": res["bytes_per_call"],
-                   "timing": "hipGraph replays of back-to-back calls, HIP events on the launch stream"},
+                   "rotating_input_sets": a.sets, "distinct_sets_timed": res["distinct_sets_timed"],
+                   "bytes_read_between_reuses_of_a_set": res["bytes_read_between_reuses_of_a_set"],
+                   "bytes_per_call": res["bytes_per_call"],
+                   "timing": "hipGraph replays of back-to-back calls after a full rotation of the sets, "
+                             "HIP events on the launch stream"},
         "roofline": {"bound": "hbm", "achieved": round(res["gbps"], 2), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(res["gbps"] / PEAK_GBPS, 4),
                      "traffic": traffic},

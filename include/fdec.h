@@ -402,23 +402,8 @@ FDEC_API int fdec_unfused_mlp_decode(const fdec_mlp_layer* layer, int32_t M,
 FDEC_API int fdec_w4_unpack(const fdec_w4* W, int8_t* q_out, fdec_stream stream);
 FDEC_API int fdec_w4_dequant(const fdec_w4* W, float* w_out, fdec_stream stream);
 
-/*
- * Tuning and test controls (process-wide, not thread-safe; not for production use).
- * fdec_set_gemv_split(k): force the split-K GEMV kernel with K split into about k
- *   parts per column tile (0 restores the built-in choice of kernel and split; values
- *   that do not fit the shape are clamped).  Calls with more than 16 rows ignore it:
- *   only the matrix-core kernel takes them.
- * fdec_set_gemv_tiling(waves, cols_per_workgroup): force the column-owning GEMV
- *   kernel's workgroup shape (1..14 dot waves, each owning at most 4 columns, next to
- *   the staging waves, 16 waves in all); (0, 0) restores the built-in choice.  Shapes
- *   the kernel cannot take fall back to it.
- * fdec_test_fail_launches(on): while on, every compute call validates its arguments
- *   and then returns FDEC_ERR_HIP without touching the GPU (exercises the error path
- *   on machines without a GPU).
- */
-FDEC_API void fdec_set_gemv_split(int32_t k);
-FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_workgroup);
-FDEC_API void fdec_test_fail_launches(int32_t on);
+/* Test, tuning and measurement controls are declared in fdec_test.h (not for production
+ * use). */
 
 #ifdef __cplusplus
 }

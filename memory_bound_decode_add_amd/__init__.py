@@ -106,9 +106,15 @@ _SIGS = {
                                             _c_p, _sz, _c_p]),
     "fdec_fp4_gemv": (ctypes.c_int, [_c_p, ctypes.POINTER(CFP4), _c_p, _c_p, _i32, _c_p, _c_p, _sz, _c_p]),
     "fdec_fp4_dequant": (ctypes.c_int, [ctypes.POINTER(CFP4), _c_p, _c_p]),
+    # include/fdec_test.h
     "fdec_set_gemv_split": (None, [_i32]),
     "fdec_set_gemv_tiling": (None, [_i32, _i32]),
     "fdec_test_fail_launches": (None, [_i32]),
+    "fdec_test_gemv_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_test_mlp_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_test_empty_kernel": (ctypes.c_int, [_i32, _i32, _c_p]),
+    "fdec_test_read_ceiling": (ctypes.c_int, [_c_p, _sz, _i32, _c_p, _c_p, _sz, _c_p, _sz, _i32, _i32, _i32, _i32,
+                                              _c_p, _c_p]),
 }
 
 _lib = None
@@ -254,10 +260,17 @@ def scalar(v: float, device="cuda") -> torch.Tensor:
 # workspaces
 # ----------------------------------------------------------------------------
 def gemv_workspace_bytes(M, K, N) -> int:
+    """Workspace of fdec_swiglu_w4_gemv / fdec_w4_gemv.  While a test override set through
+    this module (set_gemv_split, set_gemv_tiling) is active, the size under it."""
+    if _overrides_active:
+        return int(lib().fdec_test_gemv_workspace_bytes(M, K, N))
     return int(lib().fdec_w4_gemv_workspace_bytes(M, K, N))
 
 
 def mlp_workspace_bytes(M, H, I) -> int:
+    """Workspace of the three-kernel layer, chain and graph calls (override-aware as above)."""
+    if _overrides_active:
+        return int(lib().fdec_test_mlp_workspace_bytes(M, H, I))
     return int(lib().fdec_mlp_workspace_bytes(M, H, I))
 
 
@@ -706,13 +719,52 @@ def fp4_dequant(W: FP4Weight) -> torch.Tensor:
     return w
 
 
+# ----------------------------------------------------------------------------
+# test, tuning and measurement controls (include/fdec_test.h; not for production use)
+# ----------------------------------------------------------------------------
+_overrides_active = False
+_override_state = {"split": 0, "tiling": (0, 0)}
+
+
+def _note_overrides():
+    global _overrides_active
+    _overrides_active = _override_state["split"] != 0 or _override_state["tiling"] != (0, 0)
+
+
 def set_gemv_split(k: int):
     lib().fdec_set_gemv_split(int(k))
+    _override_state["split"] = max(0, int(k))
+    _note_overrides()
 
 
 def set_gemv_tiling(waves: int, cols_per_workgroup: int):
     lib().fdec_set_gemv_tiling(int(waves), int(cols_per_workgroup))
+    _override_state["tiling"] = (max(0, int(waves)), max(0, int(cols_per_workgroup)))
+    _note_overrides()
 
 
 def test_fail_launches(on: bool):
     lib().fdec_test_fail_launches(int(bool(on)))
+
+
+def empty_kernel(wgs=256, threads=256):
+    """One launch of a kernel that does nothing (the per-launch floor)."""
+    _check(lib().fdec_test_empty_kernel(int(wgs), int(threads), _stream()))
+
+
+def read_ceiling(stream_buf, per_wg, g, u, pieces, rows, row_bytes, piece_bytes, wgs, sink):
+    """One launch of the read-only probe (fdec_test.h): workgroup b reads chunks
+    [b * per_wg, (b + 1) * per_wg) of stream_buf, all of g and u, and its pieces of each of
+    `rows` rows of `pieces`; writes one word per workgroup to sink (int32 [wgs])."""
+    for t, name in ((stream_buf, "stream_buf"), (g, "g"), (u, "u"), (pieces, "pieces"), (sink, "sink")):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if g.numel() * g.element_size() != u.numel() * u.element_size():
+        raise ValueError("g and u must have the same size")
+    if sink.numel() * sink.element_size() < 4 * wgs:
+        raise ValueError("sink is too small")
+    nb = lambda t: t.numel() * t.element_size()  # noqa: E731
+    _check(lib().fdec_test_read_ceiling(stream_buf.data_ptr(), nb(stream_buf), int(per_wg), g.data_ptr(),
+                                        u.data_ptr(), nb(g), pieces.data_ptr(), nb(pieces), int(rows),
+                                        int(row_bytes), int(piece_bytes), int(wgs), sink.data_ptr(),
+                                        _stream(stream_buf.device)))

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -19,7 +20,12 @@ using namespace fdec;
 namespace {
 
 thread_local std::string t_last_error;
-int g_fail_launches = 0;
+
+// Test and tuning controls (include/fdec_test.h): read once per call.
+std::atomic<int> g_fail_launches{0};
+std::atomic<int> g_forced_split{0};
+std::atomic<int> g_col_waves{0};
+std::atomic<int> g_col_cols{0};
 
 constexpr size_t kAlign = 256;   // sub-buffer alignment inside workspaces
 
@@ -203,9 +209,20 @@ int check_layer(const fdec_mlp_layer* L, int M, LayerDims* d) {
     return FDEC_OK;
 }
 
-size_t mlp_ws(int M, int H, int I) {
-    return std::max(gemv_workspace_bytes(M, H, 2 * I), gemv_workspace_bytes(M, I, H));
+// The two GEMV plans of a layer, made once per call: the workspace is checked against
+// them and they are what gets launched.
+struct LayerPlan {
+    GemvPlan gu, dn;
+    size_t ws;
+};
+LayerPlan plan_layer(int M, int H, int I, const Overrides& ov) {
+    LayerPlan lp;
+    lp.gu = plan_gemv(M, H, 2 * I, ov);
+    lp.dn = plan_gemv(M, I, H, ov);
+    lp.ws = std::max(lp.gu.partial_bytes, lp.dn.partial_bytes);
+    return lp;
 }
+size_t mlp_ws(int M, int H, int I) { return plan_layer(M, H, I, Overrides{}).ws; }
 
 int check_layer_buffers(const fdec_mlp_layer* L, int M, LayerDims d, const fdec_bf16* x,
                         const fdec_bf16* residual, const fdec_bf16* y_norm, const fdec_bf16* gate_up,
@@ -232,16 +249,16 @@ int check_layer_buffers(const fdec_mlp_layer* L, int M, LayerDims d, const fdec_
     return FDEC_OK;
 }
 
-hipError_t enqueue_layer(const fdec_mlp_layer* L, int M, LayerDims d, const fdec_bf16* x,
+hipError_t enqueue_layer(const fdec_mlp_layer* L, int M, LayerDims d, const LayerPlan& lp, const fdec_bf16* x,
                          fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* out,
                          void* ws, hipStream_t s) {
     hipError_t e = launch_add_rmsnorm(x, residual, L->norm_weight, L->eps, M, d.H, residual, y_norm, s);
     if (e != hipSuccess) return e;
     e = launch_gemv(kIdentity, y_norm, nullptr, d.H, L->gate_up.qweight, L->gate_up.scales, M, d.H, 2 * d.I,
-                    nullptr, nullptr, gate_up, ws, s);
+                    nullptr, nullptr, gate_up, ws, lp.gu, s);
     if (e != hipSuccess) return e;
     return launch_gemv(kSwiGLU, gate_up, gate_up + d.I, 2 * int64_t(d.I), L->down.qweight, L->down.scales, M,
-                       d.I, d.H, L->out_scale, L->residual_in_epilogue ? residual : nullptr, out, ws, s);
+                       d.I, d.H, L->out_scale, L->residual_in_epilogue ? residual : nullptr, out, ws, lp.dn, s);
 }
 
 int check_chain(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d) {
@@ -264,10 +281,10 @@ int check_chain(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d)
 // cannot write h into the residual buffer itself: every workgroup of it reads that buffer.
 size_t mlp2_ws(int M, int H) { return align_up(size_t(M) * H * 2); }
 
-int check_layer2(const fdec_mlp_layer* L, int M, LayerDims* d) {
+int check_layer2(const fdec_mlp_layer* L, int M, LayerDims* d, const Overrides& ov) {
     int st = check_layer(L, M, d);
     if (st != FDEC_OK) return st;
-    if (!norm_gemv_swiglu_supported(M, d->H, d->I) || !gemv_column_supported(M, d->I, d->H))
+    if (!norm_gemv_swiglu_supported(M, d->H, d->I) || !gemv_column_supported(M, d->I, d->H, ov))
         return fail(FDEC_ERR_UNSUPPORTED,
                     "the two-kernel layer needs the column GEMV for both projections (M = %d, H = %d, I = %d)", M,
                     d->H, d->I);
@@ -297,33 +314,32 @@ int check_layer2_buffers(const fdec_mlp_layer* L, int M, LayerDims d, const fdec
     return FDEC_OK;
 }
 
-hipError_t enqueue_layer2(const fdec_mlp_layer* L, int M, LayerDims d, const fdec_bf16* x, fdec_bf16* residual,
-                          fdec_bf16* act, fdec_bf16* out, void* ws, hipStream_t s) {
+hipError_t enqueue_layer2(const fdec_mlp_layer* L, int M, LayerDims d, const Overrides& ov, const fdec_bf16* x,
+                          fdec_bf16* residual, fdec_bf16* act, fdec_bf16* out, void* ws, hipStream_t s) {
     uint16_t* h = static_cast<uint16_t*>(ws);
     hipError_t e = launch_norm_gemv_swiglu(x, residual, L->norm_weight, L->eps, L->gate_up.qweight,
                                            L->gate_up.scales, M, d.H, d.I, h, act, s);
     if (e != hipSuccess) return e;
     return launch_gemv_copy(kIdentity, act, d.I, L->down.qweight, L->down.scales, M, d.I, d.H, L->out_scale,
-                            L->residual_in_epilogue ? h : nullptr, out, h, residual, size_t(M) * d.H * 2, s);
+                            L->residual_in_epilogue ? h : nullptr, out, h, residual, size_t(M) * d.H * 2, ov, s);
 }
 
-int check_chain2(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d) {
+int check_chain2(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d, const Overrides& ov) {
     int st = check_chain(layers, n_layers, M, d);
     if (st != FDEC_OK) return st;
-    return check_layer2(&layers[0], M, d);
+    return check_layer2(&layers[0], M, d, ov);
 }
 
 // ---- unfused ----
 size_t unfused_norm_ws(int M, int H) {
     return 2 * align_up(size_t(M) * H * 4) + align_up(size_t(M) * 3 * 4);
 }
-size_t unfused_act_ws(int M, int K, int N) {
-    return 2 * align_up(size_t(M) * K * 2) + gemv_workspace_bytes(M, K, N);
-}
+// p: the plan of the sequence's identity-prologue GEMV (M, K, N)
+size_t unfused_act_ws(int M, int K, const GemvPlan& p) { return 2 * align_up(size_t(M) * K * 2) + p.partial_bytes; }
 
 hipError_t enqueue_unfused_act(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_w4* W,
                                const float* out_scale, const fdec_bf16* residual, int M, fdec_bf16* y,
-                               void* ws, hipStream_t s) {
+                               void* ws, const GemvPlan& p, hipStream_t s) {
     const int K = W->K, N = W->N;
     uint16_t* t = static_cast<uint16_t*>(ws);
     uint16_t* act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align_up(size_t(M) * K * 2));
@@ -331,8 +347,8 @@ hipError_t enqueue_unfused_act(const fdec_bf16* g, const fdec_bf16* u, int64_t l
     hipError_t e;
     if ((e = launch_silu_bf16(g, ldgu, M, K, t, s)) != hipSuccess) return e;
     if ((e = launch_mul_bf16(t, K, u, ldgu, M, K, act, s)) != hipSuccess) return e;
-    if ((e = launch_gemv(kIdentity, act, nullptr, K, W->qweight, W->scales, M, K, N, nullptr, nullptr, y, gws, s)) !=
-        hipSuccess)
+    if ((e = launch_gemv(kIdentity, act, nullptr, K, W->qweight, W->scales, M, K, N, nullptr, nullptr, y, gws, p,
+                         s)) != hipSuccess)
         return e;
     if ((e = launch_scale_bf16(y, int64_t(M) * N, out_scale, s)) != hipSuccess) return e;
     if (residual) return launch_add_bf16(y, residual, int64_t(M) * N, s);
@@ -349,6 +365,16 @@ hipError_t enqueue_eager_norm(const fdec_bf16* x, const fdec_bf16* r, const fdec
 
 }  // namespace
 
+namespace fdec {
+Overrides current_overrides() {
+    Overrides ov;
+    ov.split = g_forced_split.load();
+    ov.col_waves = g_col_waves.load();
+    ov.col_cols = g_col_cols.load();
+    return ov;
+}
+}  // namespace fdec
+
 struct fdec_graph_s {
     hipGraph_t graph = nullptr;       // the captured graph the executable was made from
     hipGraphExec_t exec = nullptr;
@@ -361,16 +387,22 @@ namespace {
 
 // Captures the chain of the given form on s into *out; nothing runs.  Form 1 uses
 // y_norm and gate_up, form 2 uses act.
-hipError_t capture_chain(int form, const fdec_mlp_layer* layers, int n_layers, int M, LayerDims d, fdec_bf16* x,
-                         fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* act, void* ws,
-                         hipStream_t s, hipGraph_t* out) {
+// The plans and overrides were taken once by the entry point (they fixed the workspace).
+struct ChainPlan {
+    LayerPlan lp;      // form 1
+    Overrides ov;      // form 2
+};
+
+hipError_t capture_chain(int form, const ChainPlan& cp, const fdec_mlp_layer* layers, int n_layers, int M,
+                         LayerDims d, fdec_bf16* x, fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up,
+                         fdec_bf16* act, void* ws, hipStream_t s, hipGraph_t* out) {
     *out = nullptr;
     hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return e;
     hipError_t le = hipSuccess;
     for (int l = 0; l < n_layers && le == hipSuccess; ++l)
-        le = form == 1 ? enqueue_layer(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, s)
-                       : enqueue_layer2(&layers[l], M, d, x, residual, act, x, ws, s);
+        le = form == 1 ? enqueue_layer(&layers[l], M, d, cp.lp, x, residual, y_norm, gate_up, x, ws, s)
+                       : enqueue_layer2(&layers[l], M, d, cp.ov, x, residual, act, x, ws, s);
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(s, &g);
     if (le != hipSuccess || e != hipSuccess) {
@@ -381,12 +413,13 @@ hipError_t capture_chain(int form, const fdec_mlp_layer* layers, int n_layers, i
     return hipSuccess;
 }
 
-int make_graph(int form, const fdec_mlp_layer* layers, int n_layers, int M, LayerDims d, fdec_bf16* x,
-               fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* act, void* ws, hipStream_t s,
-               fdec_graph* out) {
+int make_graph(int form, const ChainPlan& cp, const fdec_mlp_layer* layers, int n_layers, int M, LayerDims d,
+               fdec_bf16* x, fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* act, void* ws,
+               hipStream_t s, fdec_graph* out) {
     fdec_graph_s* G = new (std::nothrow) fdec_graph_s;
     if (!G) return fail(FDEC_ERR_ARG, "out of host memory");
-    hipError_t e = capture_chain(form, layers, n_layers, M, d, x, residual, y_norm, gate_up, act, ws, s, &G->graph);
+    hipError_t e =
+        capture_chain(form, cp, layers, n_layers, M, d, x, residual, y_norm, gate_up, act, ws, s, &G->graph);
     if (e != hipSuccess) {
         delete G;
         return hip_status(e, "graph capture");
@@ -412,16 +445,16 @@ int make_graph(int form, const fdec_mlp_layer* layers, int n_layers, int M, Laye
 // Re-captures the chain with new layers and buffers and writes the new kernel
 // arguments into the existing executable graph (hipGraphExecUpdate): the launch
 // shapes are those of the graph, so no re-instantiation is needed.
-int update_graph(fdec_graph G, int form, const fdec_mlp_layer* layers, int n_layers, int M, LayerDims d,
-                 fdec_bf16* x, fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* act, void* ws,
-                 hipStream_t s) {
+int update_graph(fdec_graph G, int form, const ChainPlan& cp, const fdec_mlp_layer* layers, int n_layers, int M,
+                 LayerDims d, fdec_bf16* x, fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up,
+                 fdec_bf16* act, void* ws, hipStream_t s) {
     if (G->form != form || G->n_layers != n_layers || G->M != M || G->H != d.H || G->I != d.I)
         return fail(FDEC_ERR_UNSUPPORTED,
                     "an update keeps the graph's form and shapes (form %d, %d layers, M = %d, H = %d, I = %d); "
                     "got form %d, %d layers, M = %d, H = %d, I = %d",
                     G->form, G->n_layers, G->M, G->H, G->I, form, n_layers, M, d.H, d.I);
     hipGraph_t ng = nullptr;
-    hipError_t e = capture_chain(form, layers, n_layers, M, d, x, residual, y_norm, gate_up, act, ws, s, &ng);
+    hipError_t e = capture_chain(form, cp, layers, n_layers, M, d, x, residual, y_norm, gate_up, act, ws, s, &ng);
     if (e != hipSuccess) return hip_status(e, "graph capture");
     hipGraphNode_t err_node = nullptr;
     hipGraphExecUpdateResult res = hipGraphExecUpdateSuccess;
@@ -468,18 +501,57 @@ FDEC_API const char* fdec_status_str(int status) {
 
 FDEC_API const char* fdec_last_error(void) { return t_last_error.c_str(); }
 
-FDEC_API void fdec_set_gemv_split(int32_t k) { g_forced_split = k > 0 ? k : 0; }
+FDEC_API void fdec_set_gemv_split(int32_t k) { g_forced_split.store(k > 0 ? k : 0); }
 FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_workgroup) {
-    g_col_waves = waves > 0 ? waves : 0;
-    g_col_cols = cols_per_workgroup > 0 ? cols_per_workgroup : 0;
+    g_col_waves.store(waves > 0 ? waves : 0);
+    g_col_cols.store(cols_per_workgroup > 0 ? cols_per_workgroup : 0);
 }
-FDEC_API void fdec_test_fail_launches(int32_t on) { g_fail_launches = on ? 1 : 0; }
+FDEC_API void fdec_test_fail_launches(int32_t on) { g_fail_launches.store(on ? 1 : 0); }
+
+FDEC_API size_t fdec_test_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+    return w4_gemv_shape_ok(M, K, N) ? plan_gemv(M, K, N, current_overrides()).partial_bytes : 0;
+}
+
+FDEC_API size_t fdec_test_mlp_workspace_bytes(int32_t M, int32_t H, int32_t I) {
+    if (M < 1 || M > 16 || H <= 0 || H % 128 || I <= 0 || I % 128) return 0;
+    return plan_layer(M, H, I, current_overrides()).ws;
+}
+
+FDEC_API int fdec_test_empty_kernel(int32_t wgs, int32_t threads, fdec_stream stream) {
+    if (wgs < 1 || wgs > 65536 || threads < 64 || threads > 1024 || threads % 64)
+        return fail(FDEC_ERR_SHAPE, "empty kernel: wgs = %d, threads = %d out of range", wgs, threads);
+    if (g_fail_launches.load()) return injected();
+    return hip_status(launch_empty(wgs, threads, static_cast<hipStream_t>(stream)), "empty kernel launch");
+}
+
+FDEC_API int fdec_test_read_ceiling(const void* stream_buf, size_t stream_bytes, int32_t per_wg, const void* bcast0,
+                                    const void* bcast1, size_t bcast_bytes, const void* pieces, size_t pieces_bytes,
+                                    int32_t rows, int32_t row_bytes, int32_t piece_bytes, int32_t wgs, uint32_t* sink,
+                                    fdec_stream stream) {
+    if (!stream_buf || !bcast0 || !bcast1 || !pieces || !sink) return fail(FDEC_ERR_NULL, "read ceiling: NULL buffer");
+    if (!aligned16(stream_buf) || !aligned16(bcast0) || !aligned16(bcast1) || !aligned16(pieces) || !aligned4(sink) ||
+        row_bytes % 16)
+        return fail(FDEC_ERR_ALIGN, "read ceiling: buffers must be 16-byte aligned and row_bytes a multiple of 16");
+    if (wgs < 1 || wgs > 65536 || bcast_bytes % 16 || !read_ceiling_fits(per_wg, int(bcast_bytes / 16), rows, piece_bytes))
+        return fail(FDEC_ERR_SHAPE, "read ceiling: sizes outside the probe's limits");
+    if (uint64_t(wgs) * uint64_t(per_wg) * 16 > stream_bytes)
+        return fail(FDEC_ERR_SHAPE, "read ceiling: wgs * per_wg chunks exceed the stream buffer");
+    // the last workgroup's last piece of the last row ends inside `pieces`
+    const uint64_t last_end = uint64_t(rows - 1) * uint64_t(row_bytes) +
+                              ((uint64_t(wgs) * uint64_t(piece_bytes) - 1) / 16 + 1) * 16;
+    if (last_end > pieces_bytes || uint64_t(wgs) * uint64_t(piece_bytes) > uint64_t(row_bytes))
+        return fail(FDEC_ERR_SHAPE, "read ceiling: the pieces exceed their rows or buffer");
+    if (g_fail_launches.load()) return injected();
+    return hip_status(launch_read_ceiling(stream_buf, per_wg, bcast0, bcast1, int(bcast_bytes / 16), pieces, rows,
+                                          row_bytes, piece_bytes, wgs, sink, static_cast<hipStream_t>(stream)),
+                      "read ceiling launch");
+}
 
 FDEC_API int fdec_workspace_init(void* ws, size_t ws_bytes, fdec_stream stream) {
     if (ws_bytes == 0) return ok();
     if (!ws) return fail(FDEC_ERR_NULL, "workspace is NULL");
     if (!aligned16(ws)) return fail(FDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)), "fill kernel");
 }
 
@@ -487,7 +559,7 @@ FDEC_API int fdec_add_rmsnorm(const fdec_bf16* x, const fdec_bf16* residual, con
                               int32_t M, int32_t H, fdec_bf16* h_out, fdec_bf16* y_out, fdec_stream stream) {
     const int st = check_norm(x, residual, weight, eps, M, H, h_out, y_out);
     if (st != FDEC_OK) return st;
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_add_rmsnorm(x, residual, weight, eps, M, H, h_out, y_out,
                                          static_cast<hipStream_t>(stream)),
                       "add_rmsnorm launch");
@@ -501,24 +573,28 @@ FDEC_API int fdec_swiglu_w4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t
                                  const float* out_scale, const fdec_bf16* residual, int32_t M, fdec_bf16* y,
                                  void* ws, size_t ws_bytes, fdec_stream stream) {
     if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
-    const size_t need = w4_gemv_shape_ok(M, W->K, W->N) ? gemv_workspace_bytes(M, W->K, W->N) : 0;
-    const int st = check_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true, need, kMaxGemvRows);
+    const bool shape_ok = w4_gemv_shape_ok(M, W->K, W->N);
+    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides()) : GemvPlan{};
+    const int st = check_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true, p.partial_bytes,
+                              kMaxGemvRows);
     if (st != FDEC_OK) return st;
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual,
-                                  y, ws, static_cast<hipStream_t>(stream)),
+                                  y, ws, p, static_cast<hipStream_t>(stream)),
                       "gemv launch");
 }
 
 FDEC_API int fdec_w4_gemv(const fdec_bf16* x, const fdec_w4* W, const float* out_scale, int32_t M, fdec_bf16* y,
                           void* ws, size_t ws_bytes, fdec_stream stream) {
     if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
-    const size_t need = w4_gemv_shape_ok(M, W->K, W->N) ? gemv_workspace_bytes(M, W->K, W->N) : 0;
-    const int st = check_gemv(x, nullptr, W->K, W, out_scale, nullptr, M, y, ws, ws_bytes, false, need, kMaxGemvRows);
+    const bool shape_ok = w4_gemv_shape_ok(M, W->K, W->N);
+    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides()) : GemvPlan{};
+    const int st = check_gemv(x, nullptr, W->K, W, out_scale, nullptr, M, y, ws, ws_bytes, false, p.partial_bytes,
+                              kMaxGemvRows);
     if (st != FDEC_OK) return st;
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_gemv(kIdentity, x, nullptr, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale,
-                                  nullptr, y, ws, static_cast<hipStream_t>(stream)),
+                                  nullptr, y, ws, p, static_cast<hipStream_t>(stream)),
                       "gemv launch");
 }
 
@@ -533,11 +609,11 @@ FDEC_API int fdec_mlp_decode(const fdec_mlp_layer* layer, int32_t M, const fdec_
     LayerDims d;
     int st = check_layer(layer, M, &d);
     if (st != FDEC_OK) return st;
-    const size_t need = mlp_ws(M, d.H, d.I);
-    st = check_layer_buffers(layer, M, d, x, residual, y_norm, gate_up, out, ws, ws_bytes, need);
+    const LayerPlan lp = plan_layer(M, d.H, d.I, current_overrides());
+    st = check_layer_buffers(layer, M, d, x, residual, y_norm, gate_up, out, ws, ws_bytes, lp.ws);
     if (st != FDEC_OK) return st;
-    if (g_fail_launches) return injected();
-    return hip_status(enqueue_layer(layer, M, d, x, residual, y_norm, gate_up, out, ws,
+    if (g_fail_launches.load()) return injected();
+    return hip_status(enqueue_layer(layer, M, d, lp, x, residual, y_norm, gate_up, out, ws,
                                     static_cast<hipStream_t>(stream)),
                       "layer launch");
 }
@@ -548,15 +624,15 @@ FDEC_API int fdec_mlp_chain(const fdec_mlp_layer* layers, int32_t n_layers, int3
     LayerDims d;
     int st = check_chain(layers, n_layers, M, &d);
     if (st != FDEC_OK) return st;
-    const size_t need = mlp_ws(M, d.H, d.I);
+    const LayerPlan lp = plan_layer(M, d.H, d.I, current_overrides());
     for (int l = 0; l < n_layers; ++l)
-        if ((st = check_layer_buffers(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, ws_bytes, need)) !=
+        if ((st = check_layer_buffers(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, ws_bytes, lp.ws)) !=
             FDEC_OK)
             return st;
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     for (int l = 0; l < n_layers; ++l) {
-        const hipError_t e =
-            enqueue_layer(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, static_cast<hipStream_t>(stream));
+        const hipError_t e = enqueue_layer(&layers[l], M, d, lp, x, residual, y_norm, gate_up, x, ws,
+                                           static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return hip_status(e, "chain launch");
     }
     return ok();
@@ -570,13 +646,15 @@ FDEC_API int fdec_mlp_graph_create(const fdec_mlp_layer* layers, int32_t n_layer
     LayerDims d;
     int st = check_chain(layers, n_layers, M, &d);
     if (st != FDEC_OK) return st;
-    const size_t need = mlp_ws(M, d.H, d.I);
+    ChainPlan cp;
+    cp.ov = current_overrides();
+    cp.lp = plan_layer(M, d.H, d.I, cp.ov);
     for (int l = 0; l < n_layers; ++l)
-        if ((st = check_layer_buffers(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, ws_bytes, need)) !=
+        if ((st = check_layer_buffers(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, ws_bytes, cp.lp.ws)) !=
             FDEC_OK)
             return st;
-    if (g_fail_launches) return injected();
-    return make_graph(1, layers, n_layers, M, d, x, residual, y_norm, gate_up, nullptr, ws,
+    if (g_fail_launches.load()) return injected();
+    return make_graph(1, cp, layers, n_layers, M, d, x, residual, y_norm, gate_up, nullptr, ws,
                       static_cast<hipStream_t>(stream), out);
 }
 
@@ -588,19 +666,21 @@ FDEC_API int fdec_mlp_graph_update(fdec_graph graph, const fdec_mlp_layer* layer
     LayerDims d;
     int st = check_chain(layers, n_layers, M, &d);
     if (st != FDEC_OK) return st;
-    const size_t need = mlp_ws(M, d.H, d.I);
+    ChainPlan cp;
+    cp.ov = current_overrides();
+    cp.lp = plan_layer(M, d.H, d.I, cp.ov);
     for (int l = 0; l < n_layers; ++l)
-        if ((st = check_layer_buffers(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, ws_bytes, need)) !=
+        if ((st = check_layer_buffers(&layers[l], M, d, x, residual, y_norm, gate_up, x, ws, ws_bytes, cp.lp.ws)) !=
             FDEC_OK)
             return st;
-    if (g_fail_launches) return injected();
-    return update_graph(graph, 1, layers, n_layers, M, d, x, residual, y_norm, gate_up, nullptr, ws,
+    if (g_fail_launches.load()) return injected();
+    return update_graph(graph, 1, cp, layers, n_layers, M, d, x, residual, y_norm, gate_up, nullptr, ws,
                         static_cast<hipStream_t>(stream));
 }
 
 FDEC_API int fdec_graph_launch(fdec_graph graph, fdec_stream stream) {
     if (!graph || !graph->exec) return fail(FDEC_ERR_NULL, "graph is NULL");
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)), "hipGraphLaunch");
 }
 
@@ -636,7 +716,7 @@ FDEC_API int fdec_add_rmsnorm_w4_gemv_swiglu(const fdec_bf16* x, const fdec_bf16
     if (overlap(Hs, A)) return fail(FDEC_ERR_ALIAS, "h_out overlaps act_out");
     if (!norm_gemv_swiglu_supported(M, H, I))
         return fail(FDEC_ERR_UNSUPPORTED, "no column-kernel variant for M = %d, H = %d, I = %d", M, H, I);
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_norm_gemv_swiglu(x, residual, norm_weight, eps, gate_up->qweight, gate_up->scales, M, H,
                                               I, h_out, act_out, static_cast<hipStream_t>(stream)),
                       "fused gate_up launch");
@@ -650,27 +730,30 @@ FDEC_API size_t fdec_mlp2_workspace_bytes(int32_t M, int32_t H, int32_t I) {
 FDEC_API int fdec_mlp_decode2(const fdec_mlp_layer* layer, int32_t M, const fdec_bf16* x, fdec_bf16* residual,
                               fdec_bf16* act, fdec_bf16* out, void* ws, size_t ws_bytes, fdec_stream stream) {
     LayerDims d;
-    int st = check_layer2(layer, M, &d);
+    const Overrides ov = current_overrides();
+    int st = check_layer2(layer, M, &d, ov);
     if (st != FDEC_OK) return st;
     st = check_layer2_buffers(layer, M, d, x, residual, act, out, ws, ws_bytes, mlp2_ws(M, d.H));
     if (st != FDEC_OK) return st;
-    if (g_fail_launches) return injected();
-    return hip_status(enqueue_layer2(layer, M, d, x, residual, act, out, ws, static_cast<hipStream_t>(stream)),
+    if (g_fail_launches.load()) return injected();
+    return hip_status(enqueue_layer2(layer, M, d, ov, x, residual, act, out, ws, static_cast<hipStream_t>(stream)),
                       "layer launch");
 }
 
 FDEC_API int fdec_mlp_chain2(const fdec_mlp_layer* layers, int32_t n_layers, int32_t M, fdec_bf16* x,
                              fdec_bf16* residual, fdec_bf16* act, void* ws, size_t ws_bytes, fdec_stream stream) {
     LayerDims d;
-    int st = check_chain2(layers, n_layers, M, &d);
+    const Overrides ov = current_overrides();
+    int st = check_chain2(layers, n_layers, M, &d, ov);
     if (st != FDEC_OK) return st;
     for (int l = 0; l < n_layers; ++l)
         if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, mlp2_ws(M, d.H))) !=
             FDEC_OK)
             return st;
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     for (int l = 0; l < n_layers; ++l) {
-        const hipError_t e = enqueue_layer2(&layers[l], M, d, x, residual, act, x, ws, static_cast<hipStream_t>(stream));
+        const hipError_t e =
+            enqueue_layer2(&layers[l], M, d, ov, x, residual, act, x, ws, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return hip_status(e, "chain launch");
     }
     return ok();
@@ -682,14 +765,16 @@ FDEC_API int fdec_mlp_graph_create2(const fdec_mlp_layer* layers, int32_t n_laye
     if (!out) return fail(FDEC_ERR_NULL, "out is NULL");
     if (!stream) return fail(FDEC_ERR_ARG, "graph capture needs a non-null stream");
     LayerDims d;
-    int st = check_chain2(layers, n_layers, M, &d);
+    ChainPlan cp;
+    cp.ov = current_overrides();
+    int st = check_chain2(layers, n_layers, M, &d, cp.ov);
     if (st != FDEC_OK) return st;
     for (int l = 0; l < n_layers; ++l)
         if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, mlp2_ws(M, d.H))) !=
             FDEC_OK)
             return st;
-    if (g_fail_launches) return injected();
-    return make_graph(2, layers, n_layers, M, d, x, residual, nullptr, nullptr, act, ws,
+    if (g_fail_launches.load()) return injected();
+    return make_graph(2, cp, layers, n_layers, M, d, x, residual, nullptr, nullptr, act, ws,
                       static_cast<hipStream_t>(stream), out);
 }
 
@@ -699,21 +784,23 @@ FDEC_API int fdec_mlp_graph_update2(fdec_graph graph, const fdec_mlp_layer* laye
     if (!graph || !graph->exec) return fail(FDEC_ERR_NULL, "graph is NULL");
     if (!stream) return fail(FDEC_ERR_ARG, "graph capture needs a non-null stream");
     LayerDims d;
-    int st = check_chain2(layers, n_layers, M, &d);
+    ChainPlan cp;
+    cp.ov = current_overrides();
+    int st = check_chain2(layers, n_layers, M, &d, cp.ov);
     if (st != FDEC_OK) return st;
     for (int l = 0; l < n_layers; ++l)
         if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, mlp2_ws(M, d.H))) !=
             FDEC_OK)
             return st;
-    if (g_fail_launches) return injected();
-    return update_graph(graph, 2, layers, n_layers, M, d, x, residual, nullptr, nullptr, act, ws,
+    if (g_fail_launches.load()) return injected();
+    return update_graph(graph, 2, cp, layers, n_layers, M, d, x, residual, nullptr, nullptr, act, ws,
                         static_cast<hipStream_t>(stream));
 }
 
 FDEC_API size_t fdec_unfused_gemv_workspace_bytes(int32_t mode, int32_t M, int32_t K, int32_t N) {
     if (M < 1 || M > 16 || K <= 0 || K % 128 || N <= 0 || N % 8) return 0;
     if (mode == FDEC_UNFUSED_PRODUCT) return M == 1 ? size_t(M) * K * N * 4 : 0;
-    if (mode == FDEC_UNFUSED_ACT) return unfused_act_ws(M, K, N);
+    if (mode == FDEC_UNFUSED_ACT) return unfused_act_ws(M, K, plan_gemv(M, K, N, Overrides{}));
     return 0;
 }
 
@@ -725,17 +812,20 @@ FDEC_API int fdec_unfused_swiglu_w4_gemv(int32_t mode, const fdec_bf16* g, const
     if (mode == FDEC_UNFUSED_PRODUCT && M != 1)
         return fail(FDEC_ERR_UNSUPPORTED, "the materialised-product sequence is defined for M == 1 only (M = %d)", M);
     const bool shape_ok = M >= 1 && M <= 16 && W->K > 0 && W->K % 128 == 0 && W->N > 0 && W->N % 8 == 0;
-    const size_t need = shape_ok ? fdec_unfused_gemv_workspace_bytes(mode, M, W->K, W->N) : 0;
+    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides()) : GemvPlan{};
+    const size_t need = !shape_ok ? 0
+                        : mode == FDEC_UNFUSED_PRODUCT ? size_t(M) * W->K * W->N * 4
+                                                       : unfused_act_ws(M, W->K, p);
     const int st = check_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true, need);
     if (st != FDEC_OK) return st;
     if (residual == y) return fail(FDEC_ERR_ALIAS, "the unfused sequence needs y distinct from residual");
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (mode == FDEC_UNFUSED_PRODUCT)
         return hip_status(launch_unfused_product(g, u, W->qweight, W->scales, W->K, W->N, out_scale, residual, y,
                                                  static_cast<float*>(ws), s),
                           "unfused product launch");
-    return hip_status(enqueue_unfused_act(g, u, ldgu, W, out_scale, residual, M, y, ws, s), "unfused act launch");
+    return hip_status(enqueue_unfused_act(g, u, ldgu, W, out_scale, residual, M, y, ws, p, s), "unfused act launch");
 }
 
 FDEC_API size_t fdec_unfused_add_rmsnorm_workspace_bytes(int32_t M, int32_t H) {
@@ -757,16 +847,23 @@ FDEC_API int fdec_unfused_add_rmsnorm(const fdec_bf16* x, const fdec_bf16* resid
     if (overlap(WS, {x, t}) || overlap(WS, {residual, t}) || overlap(WS, {weight, size_t(H) * 2}) ||
         overlap(WS, {h_out, t}) || overlap(WS, {y_out, t}))
         return fail(FDEC_ERR_ALIAS, "the workspace overlaps a tensor");
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(enqueue_eager_norm(x, residual, weight, eps, M, H, h_out, y_out, ws,
                                          static_cast<hipStream_t>(stream)),
                       "eager norm launch");
 }
 
+namespace {
+// norm scratch, then the ACT sequence's scratch (its down GEMV plan lp.dn), then the
+// gate_up GEMV's workspace (plan lp.gu)
+size_t unfused_mlp_ws(int M, int H, int I, const LayerPlan& lp) {
+    return align_up(unfused_norm_ws(M, H)) + align_up(unfused_act_ws(M, I, lp.dn)) + align_up(lp.gu.partial_bytes);
+}
+}  // namespace
+
 FDEC_API size_t fdec_unfused_mlp_workspace_bytes(int32_t M, int32_t H, int32_t I) {
     if (M < 1 || M > 16 || H <= 0 || H % 128 || I <= 0 || I % 128) return 0;
-    return align_up(unfused_norm_ws(M, H)) + align_up(unfused_act_ws(M, I, H)) +
-           align_up(gemv_workspace_bytes(M, H, 2 * I));
+    return unfused_mlp_ws(M, H, I, plan_layer(M, H, I, Overrides{}));
 }
 
 FDEC_API int fdec_unfused_mlp_decode(const fdec_mlp_layer* layer, int32_t M, const fdec_bf16* x,
@@ -775,23 +872,24 @@ FDEC_API int fdec_unfused_mlp_decode(const fdec_mlp_layer* layer, int32_t M, con
     LayerDims d;
     int st = check_layer(layer, M, &d);
     if (st != FDEC_OK) return st;
-    const size_t need = fdec_unfused_mlp_workspace_bytes(M, d.H, d.I);
+    const LayerPlan lp = plan_layer(M, d.H, d.I, current_overrides());
+    const size_t need = unfused_mlp_ws(M, d.H, d.I, lp);
     st = check_layer_buffers(layer, M, d, x, residual, y_norm, gate_up, out, ws, ws_bytes, need);
     if (st != FDEC_OK) return st;
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(ws);
     void* norm_ws = w;
     void* act_ws = w + align_up(unfused_norm_ws(M, d.H));
-    void* gu_ws = static_cast<char*>(act_ws) + align_up(unfused_act_ws(M, d.I, d.H));
+    void* gu_ws = static_cast<char*>(act_ws) + align_up(unfused_act_ws(M, d.I, lp.dn));
     hipError_t e = enqueue_eager_norm(x, residual, layer->norm_weight, layer->eps, M, d.H, residual, y_norm,
                                       norm_ws, s);
     if (e == hipSuccess)
         e = launch_gemv(kIdentity, y_norm, nullptr, d.H, layer->gate_up.qweight, layer->gate_up.scales, M, d.H,
-                        2 * d.I, nullptr, nullptr, gate_up, gu_ws, s);
+                        2 * d.I, nullptr, nullptr, gate_up, gu_ws, lp.gu, s);
     if (e == hipSuccess)
         e = enqueue_unfused_act(gate_up, gate_up + d.I, 2 * int64_t(d.I), &layer->down, layer->out_scale,
-                                layer->residual_in_epilogue ? residual : nullptr, M, out, act_ws, s);
+                                layer->residual_in_epilogue ? residual : nullptr, M, out, act_ws, lp.dn, s);
     return hip_status(e, "unfused layer launch");
 }
 
@@ -805,7 +903,7 @@ FDEC_API int fdec_swiglu_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_
                                   void* ws, size_t ws_bytes, fdec_stream stream) {
     const int st = check_fp4_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true);
     if (st != FDEC_OK) return st;
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_fp4_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual,
                                       y, ws, static_cast<hipStream_t>(stream)),
                       "fp4 gemv launch");
@@ -816,7 +914,7 @@ FDEC_API int fdec_fp4_gemv(const fdec_bf16* x, const fdec_fp4* W, const float* o
     if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
     const int st = check_fp4_gemv(x, nullptr, W->K, W, out_scale, residual, M, y, ws, ws_bytes, false);
     if (st != FDEC_OK) return st;
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_fp4_gemv(kIdentity, x, nullptr, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale,
                                       residual, y, ws, static_cast<hipStream_t>(stream)),
                       "fp4 gemv launch");
@@ -829,7 +927,7 @@ FDEC_API int fdec_fp4_dequant(const fdec_fp4* W, float* w_out, fdec_stream strea
     if (!aligned4(w_out)) return fail(FDEC_ERR_ALIGN, "w_out must be 4-byte aligned");
     const Span O{w_out, size_t(W->K) * W->N * 4};
     if (overlap(O, fp4_qspan(W)) || overlap(O, fp4_sspan(W))) return fail(FDEC_ERR_ALIAS, "w_out overlaps W");
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_fp4_dequant(W->qweight, W->scales, W->K, W->N, w_out, static_cast<hipStream_t>(stream)),
                       "fp4 dequant launch");
 }
@@ -840,7 +938,7 @@ FDEC_API int fdec_w4_unpack(const fdec_w4* W, int8_t* q_out, fdec_stream stream)
     if (!q_out) return fail(FDEC_ERR_NULL, "q_out is NULL");
     const Span Q{q_out, size_t(W->K) * W->N};
     if (overlap(Q, w4_qspan(W)) || overlap(Q, w4_sspan(W))) return fail(FDEC_ERR_ALIAS, "q_out overlaps W");
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_w4_unpack(W->qweight, W->K, W->N, q_out, static_cast<hipStream_t>(stream)),
                       "unpack launch");
 }
@@ -852,7 +950,7 @@ FDEC_API int fdec_w4_dequant(const fdec_w4* W, float* w_out, fdec_stream stream)
     if (!aligned4(w_out)) return fail(FDEC_ERR_ALIGN, "w_out must be 4-byte aligned");
     const Span O{w_out, size_t(W->K) * W->N * 4};
     if (overlap(O, w4_qspan(W)) || overlap(O, w4_sspan(W))) return fail(FDEC_ERR_ALIAS, "w_out overlaps W");
-    if (g_fail_launches) return injected();
+    if (g_fail_launches.load()) return injected();
     return hip_status(launch_w4_dequant(W->qweight, W->scales, W->K, W->N, w_out, static_cast<hipStream_t>(stream)),
                       "dequant launch");
 }

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/fdec.h"
+#include "../../include/fdec_test.h"
 
 namespace fdec {
 
@@ -51,14 +52,23 @@ struct GemvPlan {
     size_t lds_bytes;       // dynamic LDS per workgroup
 };
 
-GemvPlan plan_gemv(int M, int K, int N);
+// Test/tuning overrides of the GEMV plan (include/fdec_test.h).  Every compute call
+// takes one snapshot at entry and plans, checks and launches with it.
+struct Overrides {
+    int split = 0;        // fdec_set_gemv_split
+    int col_waves = 0;    // fdec_set_gemv_tiling
+    int col_cols = 0;
+};
+Overrides current_overrides();
+
+GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov = Overrides{});
 bool plan_mfma(int M, int K, int N, GemvPlan& p);   // 5 <= M <= 16
 // Sums the fp32 partials of K slices (slice j of row m at partial + j * split_stride +
 // m * row_stride) in slice order and applies the epilogue; launched after the kernel
 // that wrote them, on the same stream.
 hipError_t launch_splitk_finish(const float* partial, int splits, int64_t split_stride, int64_t row_stride, int M,
                                 int N, const float* out_scale, const uint16_t* residual, uint16_t* y, hipStream_t s);
-size_t gemv_workspace_bytes(int M, int K, int N);
+size_t gemv_workspace_bytes(int M, int K, int N);   // the built-in plan (no overrides)
 
 // kAddRmsNorm: the activation is rmsnorm(x + r) * w over the whole row (the fused
 // layer's gate_up), and the epilogue writes silu(gate) * up of column pairs (i, I + i).
@@ -69,19 +79,20 @@ enum Prologue { kIdentity = 0, kSwiGLU = 1, kAddRmsNorm = 2 };
 hipError_t launch_add_rmsnorm(const uint16_t* x, const uint16_t* r, const uint16_t* w,
                               float eps, int M, int H, uint16_t* h, uint16_t* y,
                               hipStream_t s);
+// Launches plan p, which the caller made with plan_gemv(M, K, N, ...) and checked ws for.
 hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
-                       void* ws, hipStream_t s);
+                       void* ws, const GemvPlan& p, hipStream_t s);
 // The fused layer's two kernels (column kernel only).
 bool norm_gemv_swiglu_supported(int M, int K, int I);
 hipError_t launch_norm_gemv_swiglu(const uint16_t* x, const uint16_t* r, const uint16_t* nw, float eps,
                                    const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
                                    uint16_t* h_out, uint16_t* act, hipStream_t s);
-bool gemv_column_supported(int M, int K, int N);
+bool gemv_column_supported(int M, int K, int N, const Overrides& ov);
 hipError_t launch_gemv_copy(Prologue pro, const uint16_t* a0, int64_t lda, const uint32_t* qw, const uint16_t* sc,
                             int M, int K, int N, const float* out_scale, const uint16_t* residual, uint16_t* y,
-                            const void* cp_src, void* cp_dst, size_t cp_bytes, hipStream_t s);
+                            const void* cp_src, void* cp_dst, size_t cp_bytes, const Overrides& ov, hipStream_t s);
 hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
@@ -118,8 +129,11 @@ hipError_t launch_eager_rmsnorm(const uint16_t* x, const uint16_t* r, const uint
                                 float eps, int M, int H, uint16_t* h, uint16_t* y,
                                 float* f32a, float* f32b, float* rowbuf, hipStream_t s);
 
-extern int g_forced_split;   // fdec_set_gemv_split
-extern int g_col_waves;      // fdec_set_gemv_tiling
-extern int g_col_cols;
+// measurement probes
+hipError_t launch_empty(int wgs, int threads, hipStream_t s);
+bool read_ceiling_fits(int per_wg, int bcast16, int rows, int piece_bytes);
+hipError_t launch_read_ceiling(const void* stream_buf, int per_wg, const void* b0, const void* b1, int bcast16,
+                               const void* pieces, int rows, int row_bytes, int piece_bytes, int wgs,
+                               uint32_t* sink, hipStream_t s);
 
 }  // namespace fdec

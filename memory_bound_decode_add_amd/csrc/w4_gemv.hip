@@ -48,10 +48,6 @@
 
 namespace fdec {
 
-int g_forced_split = 0;
-int g_col_waves = 0;
-int g_col_cols = 0;
-
 namespace {
 
 __device__ __forceinline__ float epilogue(float v, float s, const uint16_t* res, size_t idx) {
@@ -853,7 +849,7 @@ int col_cpw_max(int ni, int mr) {
 // per lane); the extra slots are skipped.
 int col_cpw_round(int cpw) { return cpw <= 4 ? cpw : cpw <= 6 ? 6 : 8; }
 
-bool plan_column(int M, int K, int N, GemvPlan& p) {
+bool plan_column(int M, int K, int N, GemvPlan& p, const Overrides& ov) {
     if (M > 4 || K > 32 * kColMaxChunks * kWave) return false;
     const int nch = K / 32;
     const int nblk = (K + 511) / 512;
@@ -877,13 +873,13 @@ bool plan_column(int M, int K, int N, GemvPlan& p) {
     int C = std::min(cwant, p.waves * cmax);
     // a forced shape replaces the choice when the kernel has a variant for it; more dot
     // waves than 8 take slots from the staging waves (16 waves in all)
-    if (g_col_waves > 0 && g_col_cols > 0) {
-        const int w = std::min(g_col_waves, kColMaxWaves);
+    if (ov.col_waves > 0 && ov.col_cols > 0) {
+        const int w = std::min(ov.col_waves, kColMaxWaves);
         const int st = std::min(p.stagers, 16 - w);
-        if ((g_col_cols + w - 1) / w <= cmax && st * kColMaxTasks >= ntask && st >= 1) {
+        if ((ov.col_cols + w - 1) / w <= cmax && st * kColMaxTasks >= ntask && st >= 1) {
             p.waves = w;
             p.stagers = st;
-            C = g_col_cols;
+            C = ov.col_cols;
         }
     }
     p.cols = C;
@@ -973,25 +969,24 @@ bool plan_mfma(int M, int K, int N, GemvPlan& p) {
     return true;
 }
 
-GemvPlan plan_gemv(int M, int K, int N) {
+GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov) {
     GemvPlan p{};
     p.groups = K / kGroup;
     if (M > 16) {                 // only the matrix-core kernel takes more than 16 rows
         plan_mfma(M, K, N, p);
         return p;
     }
-    if (g_forced_split == 0 && plan_column(M, K, N, p)) return p;
+    if (ov.split == 0 && plan_column(M, K, N, p, ov)) return p;
     p = GemvPlan{};
-    if (g_forced_split == 0 && plan_mfma(M, K, N, p)) return p;
-    p = GemvPlan{};
+    if (ov.split == 0 && plan_mfma(M, K, N, p)) return p;
     p = GemvPlan{};
     p.kind = kSplitK;
     p.groups = K / kGroup;
     p.tiles = (N + kGemvCols - 1) / kGemvCols;
     p.mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     int gw;
-    if (g_forced_split > 0) {
-        const int k = std::min(g_forced_split, p.groups);
+    if (ov.split > 0) {
+        const int k = std::min(ov.split, p.groups);
         const int gps = (p.groups + k - 1) / k;
         gw = round_gw((gps + 3) / 4);
     } else if (p.tiles >= 192 && p.groups <= 16) {
@@ -1010,7 +1005,7 @@ GemvPlan plan_gemv(int M, int K, int N) {
 }
 
 size_t gemv_workspace_bytes(int M, int K, int N) {
-    const GemvPlan p = plan_gemv(M, K, N);
+    const GemvPlan p = plan_gemv(M, K, N, Overrides{});
     return p.partial_bytes;
 }
 
@@ -1024,8 +1019,7 @@ hipError_t launch_splitk_finish(const float* partial, int splits, int64_t split_
 hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
-                       void* ws, hipStream_t s) {
-    const GemvPlan p = plan_gemv(M, K, N);
+                       void* ws, const GemvPlan& p, hipStream_t s) {
     if (p.kind == kColumnOwning) {
         ColArgs a{};
         a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};
@@ -1144,18 +1138,18 @@ hipError_t launch_norm_gemv_swiglu(const uint16_t* x, const uint16_t* r, const u
     }
 }
 
-bool gemv_column_supported(int M, int K, int N) {
+bool gemv_column_supported(int M, int K, int N, const Overrides& ov) {
     GemvPlan p{};
     p.groups = K / kGroup;
-    return plan_column(M, K, N, p);
+    return plan_column(M, K, N, p, ov);
 }
 
 hipError_t launch_gemv_copy(Prologue pro, const uint16_t* a0, int64_t lda, const uint32_t* qw, const uint16_t* sc,
                             int M, int K, int N, const float* out_scale, const uint16_t* residual, uint16_t* y,
-                            const void* cp_src, void* cp_dst, size_t cp_bytes, hipStream_t s) {
+                            const void* cp_src, void* cp_dst, size_t cp_bytes, const Overrides& ov, hipStream_t s) {
     GemvPlan p{};
     p.groups = K / kGroup;
-    if (pro != kIdentity || !plan_column(M, K, N, p) || cp_bytes % 16) return hipErrorInvalidValue;
+    if (pro != kIdentity || !plan_column(M, K, N, p, ov) || cp_bytes % 16) return hipErrorInvalidValue;
     ColArgs a{};
     a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};
     a.a0 = a0;

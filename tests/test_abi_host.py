@@ -18,6 +18,8 @@ HEADER = os.path.join(ROOT, "include", "fdec.h")
 
 OK, NULL, SHAPE, ALIGN, ALIAS, WS, UNSUP, HIP, ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
+CW4 = F.CW4
+
 pytestmark = pytest.mark.skipif(not os.path.exists(F.LIB_PATH), reason="libfdec.so not built")
 
 
@@ -33,6 +35,11 @@ def inject(L):
     L.fdec_test_fail_launches(0)
 
 
+@pytest.fixture
+def fake():
+    return Fake()
+
+
 class Fake:
     """Disjoint, 4 KB-aligned fake device addresses."""
 
@@ -46,7 +53,9 @@ class Fake:
 
 
 def header_symbols():
-    txt = open(HEADER).read()
+    """Every entry point declared in include/*.h (fdec.h and the test-only fdec_test.h)."""
+    inc = os.path.dirname(HEADER)
+    txt = "".join(open(os.path.join(inc, n)).read() for n in sorted(os.listdir(inc)) if n.endswith(".h"))
     return sorted(set(re.findall(r"FDEC_API\s+[\w\s\*]+?\b(fdec_\w+)\s*\(", txt)))
 
 
@@ -219,16 +228,54 @@ def test_fp4_gemv_validation(L, inject):
     assert L.fdec_fp4_dequant(ctypes.byref(W), f(), None) == HIP
 
 
-def test_gemv_split_override_changes_workspace(L):
+def test_gemv_split_override_changes_only_the_test_queries(L):
     base = L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560)
+    mlp = L.fdec_mlp_workspace_bytes(1, 1536, 8960)
+    assert L.fdec_test_gemv_workspace_bytes(1, 9216, 2560) == base
+    assert L.fdec_test_mlp_workspace_bytes(1, 1536, 8960) == mlp
     try:
-        L.fdec_set_gemv_split(1)
-        assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) < base or base == 0
         L.fdec_set_gemv_split(18)
-        assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) > 0
+        # the production queries are pure functions of the shapes
+        assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) == base
+        assert L.fdec_mlp_workspace_bytes(1, 1536, 8960) == mlp
+        assert L.fdec_test_gemv_workspace_bytes(1, 9216, 2560) > base
+        assert L.fdec_test_mlp_workspace_bytes(1, 1536, 8960) > mlp
+        # more than 16 rows: only the matrix-core kernel, whatever the override
+        assert L.fdec_test_gemv_workspace_bytes(32, 9216, 2560) == L.fdec_w4_gemv_workspace_bytes(32, 9216, 2560)
     finally:
         L.fdec_set_gemv_split(0)
-    assert L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560) == base
+    assert L.fdec_test_gemv_workspace_bytes(1, 9216, 2560) == base
+
+
+def test_forced_split_needs_the_larger_workspace(L, fake, inject):
+    # planned once at entry: a call under an override is checked against that plan's workspace
+    W = CW4(fake(1 << 24), fake(1 << 20), 9216, 2560)
+    g, u, y = fake(), fake(), fake()
+    try:
+        L.fdec_set_gemv_split(18)
+        need = L.fdec_test_gemv_workspace_bytes(1, 9216, 2560)
+        assert L.fdec_swiglu_w4_gemv(g, u, 9216, ctypes.byref(W), None, None, 1, y, None, 0, None) == -5
+        assert L.fdec_swiglu_w4_gemv(g, u, 9216, ctypes.byref(W), None, None, 1, y, fake(need), need, None) == HIP
+    finally:
+        L.fdec_set_gemv_split(0)
+    assert L.fdec_swiglu_w4_gemv(g, u, 9216, ctypes.byref(W), None, None, 1, y, None, 0, None) == HIP
+
+
+def test_probe_validation(L, fake, inject):
+    assert L.fdec_test_empty_kernel(256, 256, None) == HIP
+    assert L.fdec_test_empty_kernel(0, 256, None) == SHAPE
+    assert L.fdec_test_empty_kernel(1, 96, None) == SHAPE
+    wb, gb, sb = 11_796_480, 18_432, 368_640
+    args = lambda wbytes=wb, per=2880, rows=72, rowb=5120, pb=20, wgs=256, sink=None: (  # noqa: E731
+        fake(wbytes), wbytes, per, fake(gb), fake(gb), gb, fake(sb), sb, rows, rowb, pb, wgs,
+        fake() if sink is None else sink, None)
+    assert L.fdec_test_read_ceiling(*args()) == HIP
+    assert L.fdec_test_read_ceiling(*args(per=2881)) == SHAPE          # past the weights
+    assert L.fdec_test_read_ceiling(*args(rows=73)) == SHAPE           # past the scales
+    assert L.fdec_test_read_ceiling(*args(pb=21)) == SHAPE             # past a scale row
+    assert L.fdec_test_read_ceiling(*args(per=9000, wbytes=9000 * 256 * 16)) == SHAPE   # beyond the probe
+    assert L.fdec_test_read_ceiling(*args(rowb=5128)) == ALIGN
+    assert L.fdec_test_read_ceiling(*args(sink=0)) == NULL
 
 
 def test_unfused_validation(L, inject):
