@@ -59,7 +59,7 @@ FDEC_API size_t fdec_test_mlp_workspace_bytes(int32_t M, int32_t H, int32_t I);
  *       16-byte pieces covering bytes [b * piece_bytes, (b + 1) * piece_bytes) of the
  *       row (the group scales of its columns);
  *     - sink[b] = a checksum of what it read (uint32 [wgs]).
- *   Limits: per_wg <= 8192, bcast16 <= 8192, rows * ceil(piece_bytes / 16 + 1) <= 8192,
+ *   Limits: per_wg <= 4096, bcast16 <= 2048, rows * (piece_bytes / 16 + 2) <= 1024,
  *   every range inside its buffer (the caller passes the byte sizes; they are checked),
  *   16-byte aligned pointers and row_bytes % 16 == 0.
  */

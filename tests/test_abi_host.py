@@ -273,7 +273,7 @@ def test_probe_validation(L, fake, inject):
     assert L.fdec_test_read_ceiling(*args(per=2881)) == SHAPE          # past the weights
     assert L.fdec_test_read_ceiling(*args(rows=73)) == SHAPE           # past the scales
     assert L.fdec_test_read_ceiling(*args(pb=21)) == SHAPE             # past a scale row
-    assert L.fdec_test_read_ceiling(*args(per=9000, wbytes=9000 * 256 * 16)) == SHAPE   # beyond the probe
+    assert L.fdec_test_read_ceiling(*args(per=4097, wbytes=4097 * 256 * 16)) == SHAPE   # beyond the probe
     assert L.fdec_test_read_ceiling(*args(rowb=5128)) == ALIGN
     assert L.fdec_test_read_ceiling(*args(sink=0)) == NULL
 
