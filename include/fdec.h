@@ -165,6 +165,29 @@ FDEC_API int fdec_swiglu_w4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t
                                  void* ws, size_t ws_bytes, fdec_stream stream);
 
 /*
+ * fdec_swiglu_w4_gemv_noalloc: fdec_swiglu_w4_gemv for callers that cannot allocate
+ * device memory or pass a workspace (code under graph capture that must not allocate,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments, results
+ * (bit for bit: the same kernels and plan), checks and errors, without ws/ws_bytes: the
+ * K-slice partial sums go to a static device array of FDEC_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that each GPU holds from the library's load until the process ends.  No
+ * hipMalloc, hipFree or other allocation happens in the call.
+ *   A shape whose plan needs more partial-sum space than the scratch holds returns
+ *   FDEC_ERR_WORKSPACE (use fdec_swiglu_w4_gemv with a workspace).  The stream must
+ *   belong to the current device.  The first call on a device that needs the scratch
+ *   looks up its device address (hipGetSymbolAddress, once per device); make that first
+ *   call outside graph capture.
+ *   Every call on a GPU shares that GPU's one scratch: calls that may overlap in time on
+ *   one GPU (different streams, or graphs replayed concurrently) race and must not be
+ *   issued.  The kernels write every partial they read, so no clearing is needed.
+ */
+#define FDEC_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+FDEC_API int fdec_swiglu_w4_gemv_noalloc(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu,
+                                         const fdec_w4* W, const float* out_scale,
+                                         const fdec_bf16* residual, int32_t M, fdec_bf16* y,
+                                         fdec_stream stream);
+
+/*
  * The same GEMV with the identity prologue: y = bf16( s * x @ W ), s as above
  * (NULL = 1).  Used for the horizontally fused gate_up projection ([P4] section 5,
  * horizontal fusion), whose columns [0, I) are gate_proj and [I, 2I) up_proj.

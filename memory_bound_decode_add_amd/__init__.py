@@ -69,6 +69,8 @@ _SIGS = {
     "fdec_swiglu_w4_gemv": (ctypes.c_int, [_c_p, _c_p, _i64, ctypes.POINTER(CW4), _c_p, _c_p, _i32, _c_p,
                                            _c_p, _sz, _c_p]),
     "fdec_w4_gemv": (ctypes.c_int, [_c_p, ctypes.POINTER(CW4), _c_p, _i32, _c_p, _c_p, _sz, _c_p]),
+    "fdec_swiglu_w4_gemv_noalloc": (ctypes.c_int, [_c_p, _c_p, _i64, ctypes.POINTER(CW4), _c_p, _c_p, _i32, _c_p,
+                                                   _c_p]),
     "fdec_mlp_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "fdec_mlp_decode": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
                                        _c_p]),
@@ -357,6 +359,27 @@ def swiglu_w4_gemv(g, u, W: W4Weight, out_scale=None, residual=None, out=None, w
     _check(lib().fdec_swiglu_w4_gemv(g.data_ptr(), u.data_ptr(), ld, ctypes.byref(cw), _ptr(out_scale),
                                      _ptr(residual), M, y.data_ptr(), ws.data_ptr(), ws.numel(),
                                      _stream(g.device)))
+    return y
+
+
+def swiglu_w4_gemv_noalloc(g, u, W: W4Weight, out_scale=None, residual=None, out=None):
+    """swiglu_w4_gemv without a workspace: the library keeps the partial sums in its static
+    per-GPU scratch (fdec_swiglu_w4_gemv_noalloc).  Allocates nothing when `out` is given;
+    calls that may overlap in time on one GPU must not be issued."""
+    M = g.shape[0]
+    ld = _rows(g, "g", M, W.K)
+    ldu = _rows(u, "u", M, W.K)
+    if M > 1 and ldu != ld:
+        raise ValueError("g and u must share a row stride")
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=g.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    cw = W.c()
+    _check(lib().fdec_swiglu_w4_gemv_noalloc(g.data_ptr(), u.data_ptr(), ld, ctypes.byref(cw), _ptr(out_scale),
+                                             _ptr(residual), M, y.data_ptr(), _stream(g.device)))
     return y
 
 

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -581,6 +582,74 @@ FDEC_API int fdec_swiglu_w4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t
     if (g_fail_launches.load()) return injected();
     return hip_status(launch_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual,
                                   y, ws, p, static_cast<hipStream_t>(stream)),
+                      "gemv launch");
+}
+
+}  // extern "C"
+
+// ---- the allocation-free SwiGLU GEMV: its K-slice partial sums live in a static device
+// array instead of a caller workspace ----
+namespace {
+
+constexpr size_t kScratchBytes = FDEC_NOALLOC_SCRATCH_BYTES;
+// Every GPU the library runs on holds its own copy until the process ends.  In host code
+// the name `scratch` is only a host-side stand-in: the device address of this GPU's copy
+// comes from hipGetSymbolAddress, taken once per device and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on device `dev`, which must be the current device.
+hipError_t scratch_address(int dev, void** out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+FDEC_API int fdec_swiglu_w4_gemv_noalloc(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_w4* W,
+                                         const float* out_scale, const fdec_bf16* residual, int32_t M,
+                                         fdec_bf16* y, fdec_stream stream) {
+    if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
+    const bool shape_ok = w4_gemv_shape_ok(M, W->K, W->N);
+    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides()) : GemvPlan{};
+    // the same checks as fdec_swiglu_w4_gemv with no workspace, then the scratch limit
+    int st = check_gemv(g, u, ldgu, W, out_scale, residual, M, y, nullptr, 0, true, 0, kMaxGemvRows);
+    if (st != FDEC_OK) return st;
+    if (p.partial_bytes > kScratchBytes)
+        return fail(FDEC_ERR_WORKSPACE, "this shape needs %zu bytes of partial sums; the static scratch holds %zu",
+                    p.partial_bytes, kScratchBytes);
+    if (g_fail_launches.load()) return injected();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    if (p.partial_bytes > 0) {
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+        if (dev < 0 || dev >= kMaxDevices) return fail(FDEC_ERR_UNSUPPORTED, "device %d is beyond %d", dev, kMaxDevices);
+        if (s) {
+            hipDevice_t sdev = -1;
+            if ((e = hipStreamGetDevice(s, &sdev)) != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+            if (int(sdev) != dev)
+                return fail(FDEC_ERR_ARG, "the stream belongs to device %d, the current device is %d", int(sdev), dev);
+        }
+        if ((e = scratch_address(dev, &ws)) != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        // y and the inputs may not overlap the scratch (they cannot: it is the library's own)
+    }
+    return hip_status(launch_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual, y,
+                                  ws, p, s),
                       "gemv launch");
 }
 
