@@ -295,17 +295,42 @@ FDEC_API int fdec_graph_destroy(fdec_graph graph);
  *   (M <= 4 and H small enough for its register budget: H <= 16384 / ceil-pow2(M) and
  *   about I / 256 pairs per workgroup); otherwise FDEC_ERR_UNSUPPORTED.
  *
- * fdec_mlp_decode2: the layer of fdec_mlp_decode in two kernels, same results up to
- * the roundings the three-kernel form adds (y_norm and gate_up are not written):
- *   1. fdec_add_rmsnorm_w4_gemv_swiglu(x, residual) -> h (into ws), act;
- *   2. out = bf16(out_scale * act @ dequant(down) [+ h]); the same kernel copies h into
- *      residual, so afterwards residual = h as with fdec_mlp_decode.
+ * fdec_mlp_decode2: the layer of fdec_mlp_decode with SwiGLU as the gate_up GEMV's
+ * epilogue (the gate/up pair is never written; act [M][I] is), same results up to the
+ * roundings it leaves out.
+ *   M <= 4, two kernels (y_norm is not written either):
+ *     1. fdec_add_rmsnorm_w4_gemv_swiglu(x, residual) -> h (into ws), act;
+ *     2. out = bf16(out_scale * act @ dequant(down) [+ h]); the same kernel copies h into
+ *        residual, so afterwards residual = h as with fdec_mlp_decode.
+ *     FDEC_ERR_UNSUPPORTED where either projection does not fit the column GEMV.
+ *   5 <= M <= 16, three kernels (the matrix-core gate_up is split over K, so its
+ *   workgroups cannot each normalise whole rows):
+ *     1. fdec_add_rmsnorm(x, residual) -> residual = h (in place), y = bf16(...) into
+ *        the first M * H * 2 bytes of ws;
+ *     2. fdec_w4_gemv_swiglu(y, gate_up) -> act;
+ *     3. out = bf16(out_scale * act @ dequant(down) [+ h]).
  *   act: bf16 [M][I] (caller-owned scratch).  out may equal x.  ws: at least
- *   fdec_mlp2_workspace_bytes(M, H, I) bytes (it holds h between the kernels).
- *   FDEC_ERR_UNSUPPORTED where either projection does not fit the column GEMV.
+ *   fdec_mlp2_workspace_bytes(M, H, I) bytes.
  * fdec_mlp_chain2 / fdec_mlp_graph_create2: the chain of fdec_mlp_chain and
  * fdec_mlp_graph_create built from the two-kernel layer (2 * n_layers kernels).
  */
+/*
+ * fdec_w4_gemv_swiglu: the gate_up projection with SwiGLU as its epilogue ([P4]
+ * section 5, "the fusion boundary problem": the gate_up GEMM with a silu * up epilogue
+ * writing act; [P4] section 5, horizontal fusion: gate columns [0, I), up [I, 2I)):
+ *     g = x @ dequant(gate_up)[:, :I],  u = x @ dequant(gate_up)[:, I:]   (fp32, never written)
+ *     act = bf16(silu(g) * u)                                   -> act_out [M][I]
+ *   x: bf16 [M][K] (K = gate_up.K);  gate_up.N = 2I, I a multiple of 8;  1 <= M <= 64.
+ *   Matrix-core kernel; when K is split into slices the slices' fp32 sums go to ws and a
+ *   second kernel adds them (in slice order) and applies the epilogue.  ws: at least
+ *   fdec_w4_gemv_swiglu_workspace_bytes(M, K, I) bytes (0 when K is not split).
+ *   act_out may not overlap x, the weights or ws.
+ */
+FDEC_API size_t fdec_w4_gemv_swiglu_workspace_bytes(int32_t M, int32_t K, int32_t I);
+FDEC_API int fdec_w4_gemv_swiglu(const fdec_bf16* x, const fdec_w4* gate_up, int32_t M,
+                                 fdec_bf16* act_out, void* ws, size_t ws_bytes,
+                                 fdec_stream stream);
+
 FDEC_API int fdec_add_rmsnorm_w4_gemv_swiglu(const fdec_bf16* x, const fdec_bf16* residual,
                                              const fdec_bf16* norm_weight, float eps,
                                              const fdec_w4* gate_up, int32_t M, fdec_bf16* h_out,

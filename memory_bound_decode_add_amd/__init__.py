@@ -81,6 +81,8 @@ _SIGS = {
     "fdec_add_rmsnorm_w4_gemv_swiglu": (ctypes.c_int, [_c_p, _c_p, _c_p, ctypes.c_float, ctypes.POINTER(CW4), _i32,
                                                        _c_p, _c_p, _c_p]),
     "fdec_mlp2_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_w4_gemv_swiglu_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_w4_gemv_swiglu": (ctypes.c_int, [_c_p, ctypes.POINTER(CW4), _i32, _c_p, _c_p, _sz, _c_p]),
     "fdec_mlp_decode2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "fdec_mlp_chain2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "fdec_mlp_graph_create2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _sz,
@@ -523,6 +525,26 @@ def add_rmsnorm_w4_gemv_swiglu(x, residual, weight, W_gu: W4Weight, eps=1e-6, h_
                                                  ctypes.byref(cw), M, h.data_ptr(), act.data_ptr(),
                                                  _stream(x.device)))
     return h, act
+
+
+def w4_gemv_swiglu_workspace_bytes(M, K, I) -> int:
+    return int(lib().fdec_w4_gemv_swiglu_workspace_bytes(M, K, I))
+
+
+def w4_gemv_swiglu(x, gate_up: W4Weight, out=None, ws=None):
+    """act = bf16(silu(x @ W[:, :I]) * (x @ W[:, I:])): the gate_up projection with SwiGLU as
+    its epilogue (the matrix-core kernel, 1..64 rows); x [M, K], W [K, 2I]."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[1] != gate_up.K:
+        raise ValueError("x must be [M, K]")
+    M, I = x.shape[0], gate_up.N // 2
+    act = torch.empty((M, I), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(act, "out", torch.bfloat16, shape=(M, I))
+    ws = _ws(ws, w4_gemv_swiglu_workspace_bytes(M, gate_up.K, I), x.device)
+    cw = gate_up.c()
+    _check(lib().fdec_w4_gemv_swiglu(x.data_ptr(), ctypes.byref(cw), M, act.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream(x.device)))
+    return act
 
 
 def mlp2_workspace_bytes(M, H, I) -> int:

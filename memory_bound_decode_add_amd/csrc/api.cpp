@@ -280,11 +280,29 @@ int check_chain(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d)
 // ---- the two-kernel layer ----
 // Workspace: h (the new residual) staged between the two kernels.  The first kernel
 // cannot write h into the residual buffer itself: every workgroup of it reads that buffer.
-size_t mlp2_ws(int M, int H) { return align_up(size_t(M) * H * 2); }
+// Up to 4 rows the layer is two kernels (the norm runs as the gate_up GEMV's prologue),
+// and the workspace stages h.  From 5 rows the gate_up GEMV is the matrix-core kernel,
+// whose K-sliced workgroups cannot each normalise whole rows: the layer is the norm
+// (h into the residual buffer in place, y into the workspace), the gate_up GEMV with the
+// SwiGLU epilogue, and the down GEMV; the workspace holds y and then the K-slice partial
+// sums of whichever GEMV is running.
+bool layer2_fused_norm(int M) { return M <= 4; }
+size_t mlp2_ws(int M, int H, int I, const Overrides& ov) {
+    if (layer2_fused_norm(M)) return align_up(size_t(M) * H * 2);
+    GemvPlan pp;
+    if (!plan_mfma_pair(M, H, I, pp)) return 0;
+    return align_up(size_t(M) * H * 2) + std::max(pp.partial_bytes, plan_gemv(M, I, H, ov).partial_bytes);
+}
 
 int check_layer2(const fdec_mlp_layer* L, int M, LayerDims* d, const Overrides& ov) {
     int st = check_layer(L, M, d);
     if (st != FDEC_OK) return st;
+    if (!layer2_fused_norm(M)) {
+        GemvPlan pp;
+        if (!plan_mfma_pair(M, d->H, d->I, pp))
+            return fail(FDEC_ERR_UNSUPPORTED, "no matrix-core gate_up plan for M = %d, H = %d, I = %d", M, d->H, d->I);
+        return FDEC_OK;
+    }
     if (!norm_gemv_swiglu_supported(M, d->H, d->I) || !gemv_column_supported(M, d->I, d->H, ov))
         return fail(FDEC_ERR_UNSUPPORTED,
                     "the two-kernel layer needs the column GEMV for both projections (M = %d, H = %d, I = %d)", M,
@@ -317,6 +335,19 @@ int check_layer2_buffers(const fdec_mlp_layer* L, int M, LayerDims d, const fdec
 
 hipError_t enqueue_layer2(const fdec_mlp_layer* L, int M, LayerDims d, const Overrides& ov, const fdec_bf16* x,
                           fdec_bf16* residual, fdec_bf16* act, fdec_bf16* out, void* ws, hipStream_t s) {
+    if (!layer2_fused_norm(M)) {
+        uint16_t* y = static_cast<uint16_t*>(ws);
+        void* pws = static_cast<char*>(ws) + align_up(size_t(M) * d.H * 2);
+        GemvPlan pp;
+        if (!plan_mfma_pair(M, d.H, d.I, pp)) return hipErrorInvalidValue;
+        const GemvPlan dp = plan_gemv(M, d.I, d.H, ov);
+        hipError_t e = launch_add_rmsnorm(x, residual, L->norm_weight, L->eps, M, d.H, residual, y, s);
+        if (e != hipSuccess) return e;
+        e = launch_mfma_pair(y, L->gate_up.qweight, L->gate_up.scales, M, d.H, d.I, act, pws, pp, s);
+        if (e != hipSuccess) return e;
+        return launch_gemv(kIdentity, act, nullptr, d.I, L->down.qweight, L->down.scales, M, d.I, d.H, L->out_scale,
+                           L->residual_in_epilogue ? residual : nullptr, out, pws, dp, s);
+    }
     uint16_t* h = static_cast<uint16_t*>(ws);
     hipError_t e = launch_norm_gemv_swiglu(x, residual, L->norm_weight, L->eps, L->gate_up.qweight,
                                            L->gate_up.scales, M, d.H, d.I, h, act, s);
@@ -793,7 +824,39 @@ FDEC_API int fdec_add_rmsnorm_w4_gemv_swiglu(const fdec_bf16* x, const fdec_bf16
 
 FDEC_API size_t fdec_mlp2_workspace_bytes(int32_t M, int32_t H, int32_t I) {
     if (M < 1 || M > 16 || H <= 0 || H % 128 || I <= 0 || I % 128) return 0;
-    return mlp2_ws(M, H);
+    return mlp2_ws(M, H, I, Overrides{});
+}
+
+FDEC_API size_t fdec_w4_gemv_swiglu_workspace_bytes(int32_t M, int32_t K, int32_t I) {
+    GemvPlan p;
+    if (K <= 0 || K % 128 || !plan_mfma_pair(M, K, I, p)) return 0;
+    return p.partial_bytes;
+}
+
+FDEC_API int fdec_w4_gemv_swiglu(const fdec_bf16* x, const fdec_w4* gate_up, int32_t M, fdec_bf16* act_out,
+                                 void* ws, size_t ws_bytes, fdec_stream stream) {
+    int st;
+    if ((st = check_w4(gate_up, "gate_up")) != FDEC_OK) return st;
+    if ((st = check_m(M, kMaxGemvRows)) != FDEC_OK) return st;
+    if (gate_up->N % 16) return fail(FDEC_ERR_SHAPE, "gate_up.N = %d must be 2I with I a multiple of 8", gate_up->N);
+    const int K = gate_up->K, I = gate_up->N / 2;
+    if (!x || !act_out) return fail(FDEC_ERR_NULL, "x and act_out are required");
+    if (!aligned16(x) || !aligned16(act_out)) return fail(FDEC_ERR_ALIGN, "x and act_out must be 16-byte aligned");
+    GemvPlan p;
+    if (!plan_mfma_pair(M, K, I, p)) return fail(FDEC_ERR_UNSUPPORTED, "no plan for M = %d, K = %d, I = %d", M, K, I);
+    if (ws_bytes < p.partial_bytes)
+        return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, p.partial_bytes);
+    if (p.partial_bytes > 0 && !ws) return fail(FDEC_ERR_NULL, "workspace is NULL");
+    if (ws && !aligned16(ws)) return fail(FDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const Span X{x, size_t(M) * K * 2}, A{act_out, size_t(M) * I * 2}, WS{ws, p.partial_bytes};
+    const Span ins[] = {X, w4_qspan(gate_up), w4_sspan(gate_up)};
+    for (const Span& in : ins)
+        if (overlap(A, in) || overlap(WS, in)) return fail(FDEC_ERR_ALIAS, "act_out or the workspace overlaps an input");
+    if (overlap(A, WS)) return fail(FDEC_ERR_ALIAS, "act_out overlaps the workspace");
+    if (g_fail_launches.load()) return injected();
+    return hip_status(launch_mfma_pair(x, gate_up->qweight, gate_up->scales, M, K, I, act_out, ws, p,
+                                       static_cast<hipStream_t>(stream)),
+                      "gate_up SwiGLU launch");
 }
 
 FDEC_API int fdec_mlp_decode2(const fdec_mlp_layer* layer, int32_t M, const fdec_bf16* x, fdec_bf16* residual,
@@ -802,7 +865,7 @@ FDEC_API int fdec_mlp_decode2(const fdec_mlp_layer* layer, int32_t M, const fdec
     const Overrides ov = current_overrides();
     int st = check_layer2(layer, M, &d, ov);
     if (st != FDEC_OK) return st;
-    st = check_layer2_buffers(layer, M, d, x, residual, act, out, ws, ws_bytes, mlp2_ws(M, d.H));
+    st = check_layer2_buffers(layer, M, d, x, residual, act, out, ws, ws_bytes, mlp2_ws(M, d.H, d.I, ov));
     if (st != FDEC_OK) return st;
     if (g_fail_launches.load()) return injected();
     return hip_status(enqueue_layer2(layer, M, d, ov, x, residual, act, out, ws, static_cast<hipStream_t>(stream)),
@@ -815,9 +878,9 @@ FDEC_API int fdec_mlp_chain2(const fdec_mlp_layer* layers, int32_t n_layers, int
     const Overrides ov = current_overrides();
     int st = check_chain2(layers, n_layers, M, &d, ov);
     if (st != FDEC_OK) return st;
+    const size_t need = mlp2_ws(M, d.H, d.I, ov);
     for (int l = 0; l < n_layers; ++l)
-        if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, mlp2_ws(M, d.H))) !=
-            FDEC_OK)
+        if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, need)) != FDEC_OK)
             return st;
     if (g_fail_launches.load()) return injected();
     for (int l = 0; l < n_layers; ++l) {
@@ -838,9 +901,9 @@ FDEC_API int fdec_mlp_graph_create2(const fdec_mlp_layer* layers, int32_t n_laye
     cp.ov = current_overrides();
     int st = check_chain2(layers, n_layers, M, &d, cp.ov);
     if (st != FDEC_OK) return st;
+    const size_t need = mlp2_ws(M, d.H, d.I, cp.ov);
     for (int l = 0; l < n_layers; ++l)
-        if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, mlp2_ws(M, d.H))) !=
-            FDEC_OK)
+        if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, need)) != FDEC_OK)
             return st;
     if (g_fail_launches.load()) return injected();
     return make_graph(2, cp, layers, n_layers, M, d, x, residual, nullptr, nullptr, act, ws,
@@ -857,9 +920,9 @@ FDEC_API int fdec_mlp_graph_update2(fdec_graph graph, const fdec_mlp_layer* laye
     cp.ov = current_overrides();
     int st = check_chain2(layers, n_layers, M, &d, cp.ov);
     if (st != FDEC_OK) return st;
+    const size_t need = mlp2_ws(M, d.H, d.I, cp.ov);
     for (int l = 0; l < n_layers; ++l)
-        if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, mlp2_ws(M, d.H))) !=
-            FDEC_OK)
+        if ((st = check_layer2_buffers(&layers[l], M, d, x, residual, act, x, ws, ws_bytes, need)) != FDEC_OK)
             return st;
     if (g_fail_launches.load()) return injected();
     return update_graph(graph, 2, cp, layers, n_layers, M, d, x, residual, nullptr, nullptr, act, ws,

@@ -62,7 +62,12 @@ struct Overrides {
 Overrides current_overrides();
 
 GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov = Overrides{});
-bool plan_mfma(int M, int K, int N, GemvPlan& p);   // 5 <= M <= 16
+bool plan_mfma(int M, int K, int N, GemvPlan& p);   // 5 <= M <= 64
+// The gate_up projection [K, 2I] with the SwiGLU epilogue: act[m][i] = bf16(silu(g) u)
+// from the unrounded sums of columns i and I + i (matrix-core kernel, 1 <= M <= 64).
+bool plan_mfma_pair(int M, int K, int I, GemvPlan& p);
+hipError_t launch_mfma_pair(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
+                            uint16_t* act, void* ws, const GemvPlan& p, hipStream_t s);
 // Sums the fp32 partials of K slices (slice j of row m at partial + j * split_stride +
 // m * row_stride) in slice order and applies the epilogue; launched after the kernel
 // that wrote them, on the same stream.

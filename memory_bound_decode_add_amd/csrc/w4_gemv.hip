@@ -969,6 +969,48 @@ bool plan_mfma(int M, int K, int N, GemvPlan& p) {
     return true;
 }
 
+// The gate_up projection with the SwiGLU epilogue (pair mode of the matrix-core kernel,
+// 1..64 rows): even wave counts, P = 8 waves column pairs per workgroup.  The K slices
+// are kept whole (one slice, the epilogue in the kernel) when that already gives about
+// one workgroup per CU; otherwise split toward 256 workgroups, summed by the pair finish.
+bool plan_mfma_pair(int M, int K, int I, GemvPlan& p) {
+    p = GemvPlan{};
+    if (M < 1 || M > kMfmaMaxRows || K <= 0 || K % kGroup || I < 8 || I % 8) return false;
+    const int rb = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    const int max_slice = kMfmaMaxSliceGroups / rb;
+    p.kind = kMfma;
+    p.mr = 16 * rb;
+    p.groups = K / kGroup;
+    p.cpw = 1;
+    auto splits_for = [&](int ranges) {
+        const int S = std::max((p.groups + max_slice - 1) / max_slice,
+                               ranges >= 192 ? 1 : std::min(p.groups, (256 + ranges - 1) / ranges));
+        const int gps = (p.groups + S - 1) / S;
+        return (p.groups + gps - 1) / gps;
+    };
+    double best = 1e30;
+    p.waves = kMfmaWaves;
+    for (int w = kMfmaWaves; w >= 6; w -= 2) {
+        const int ranges = (I + 8 * w - 1) / (8 * w);
+        const int wgs = ranges * splits_for(ranges);
+        const double fill = double((wgs + 255) / 256 * 256) / wgs;
+        if (fill < best - 1e-9) {
+            best = fill;
+            p.waves = w;
+        }
+    }
+    const int P = 8 * p.waves;
+    p.tiles = (I + P - 1) / P;
+    const int S = splits_for(p.tiles);
+    p.gps = (p.groups + S - 1) / S;
+    p.splits = (p.groups + p.gps - 1) / p.gps;
+    if (p.splits > 1) p.partial_bytes = size_t(p.splits) * p.mr * p.tiles * 2 * P * 4;
+    const size_t stage = size_t(p.mr) * (size_t(p.gps) * 16 + 1) * 16 + size_t(p.mr) * p.gps * 4;
+    const size_t xchg = size_t(p.waves / 2) * rb * kWave * 16;
+    p.lds_bytes = std::max(stage, xchg);
+    return p.lds_bytes <= kMaxLds;
+}
+
 GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov) {
     GemvPlan p{};
     p.groups = K / kGroup;

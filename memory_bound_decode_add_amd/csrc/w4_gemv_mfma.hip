@@ -85,6 +85,9 @@ struct MfmaArgs {
     uint16_t* y;
     float* partial;         // [splits][16 RB][npad]
     uint32_t m_lo, m_hi;    // int4 decode field masks 0x000F000F and 0x00F000F0
+    // pair mode (the gate_up projection with the SwiGLU epilogue): N = 2 I, y is act [M][I]
+    int half_n;             // I
+    int pairs;              // P: gate/up column pairs per workgroup
 };
 
 // One packed word -> 8 fp16 values with their offsets, in pair order: the decode every
@@ -152,7 +155,11 @@ __device__ __forceinline__ f16x8_t fp4_operand(uint32_t w, _Float16 s) {
                                                   __builtin_bit_cast(uint32_t, q[3] * s2)));
 }
 
-template <int TPW, int PRO, int WF, int RB>
+// PAIR: the workgroup owns P = 16 TPW W / 2 column pairs (i, I + i): waves 0 .. W/2 - 1
+// take the gate columns cg P + ..., the other half the up columns I + cg P + ...; the
+// epilogue writes act[m][i] = bf16(silu(gate) * up) from the two fp32 sums (through LDS
+// when the slice is the whole K, else through the partial sums and the pair finish).
+template <int TPW, int PRO, int WF, int RB, bool PAIR = false>
 __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaArgs a) {
     constexpr int kRows = 16 * RB;                     // activation rows staged: RB blocks of 16
     // groups per batch of weight loads: several row blocks already give the matrix cores
@@ -168,7 +175,12 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     const int ng = min(a.kgroups, a.groups - g0);      // groups in this slice
     const int nkb = ng * 16;                           // 8-wide k-blocks in this slice
     const int ncol = W * TPW * 16;                     // columns per workgroup
-    const int nw0 = cg * ncol + wave * TPW * 16;       // first column of this wave's tiles
+    const int half = W >> 1;
+    const bool up = PAIR && wave >= half;              // pair mode: this wave holds up columns
+    const int wl = up ? wave - half : wave;
+    // the wave's first column, and its offset inside the workgroup's range of partial sums
+    const int col_local = PAIR ? (up ? a.pairs : 0) + wl * TPW * 16 : wave * TPW * 16;
+    const int nw0 = PAIR ? (up ? a.half_n : 0) + cg * a.pairs + wl * TPW * 16 : cg * ncol + col_local;
     const int rs = nkb + 1;                            // row stride of act_s, in 16-byte blocks
     uint4* act_s = reinterpret_cast<uint4*>(smem);     // [kRows][rs] of 8 fp16
     float* esc_s = reinterpret_cast<float*>(act_s + kRows * rs);   // [kRows][ng]
@@ -202,6 +214,8 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
+            rraw[r][t] = make_uint2(0u, 0u);
+            if (PAIR) continue;                                      // no residual (y is [M][I])
             const uint16_t* rsrc = a.residual ? a.residual : a.y;   // y: a readable stand-in, value unused
             rraw[r][t] = *reinterpret_cast<const uint2*>(rsrc + size_t(min(16 * r + lm, a.M - 1)) * a.N +
                                                          min(nw0 + t * 16 + 4 * ls, a.N - 4));
@@ -346,7 +360,39 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     }
 
     // ---- epilogue: lane holds D[column 4 ls + q][row 16 r + lm] of each tile ----
-    if (a.splits == 1) {
+    if (PAIR && a.splits == 1) {
+        // the up waves hand their sums to the gate waves through LDS (act_s is free once
+        // every wave has finished its main loop)
+        float4* xs = reinterpret_cast<float4*>(smem);      // [W/2][RB][TPW][64]
+        __syncthreads();
+        if (up) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+                    xs[((wl * RB + r) * TPW + t) * kWave + lane] =
+                        make_float4(out[r][t][0], out[r][t][1], out[r][t][2], out[r][t][3]);
+        }
+        __syncthreads();
+        if (!up) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const float4 u = xs[((wl * RB + r) * TPW + t) * kWave + lane];
+                    const int i = nw0 + t * 16 + 4 * ls;          // four pairs i .. i + 3 (I % 8 == 0)
+                    const int row = 16 * r + lm;
+                    if (row < a.M && i < a.half_n) {
+                        uint2 o;
+                        o.x = pack_bf16x2(silu_f32(out[r][t][0]) * u.x, silu_f32(out[r][t][1]) * u.y);
+                        o.y = pack_bf16x2(silu_f32(out[r][t][2]) * u.z, silu_f32(out[r][t][3]) * u.w);
+                        *reinterpret_cast<uint2*>(a.y + size_t(row) * a.half_n + i) = o;
+                    }
+                }
+        }
+        return;
+    }
+    if (!PAIR && a.splits == 1) {
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -371,7 +417,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const int nc = (nw0 - cg * ncol) + t * 16 + 4 * ls;          // column within the range
+            const int nc = col_local + t * 16 + 4 * ls;          // column within the range
             float* dst = a.partial + (size_t(split) * kRows + 16 * r + lm) * a.npad + cg * ncol + nc;
             *reinterpret_cast<float4*>(dst) = make_float4(out[r][t][0], out[r][t][1], out[r][t][2], out[r][t][3]);
         }
@@ -438,7 +484,66 @@ hipError_t launch_mfma_wf(Prologue pro, const uint16_t* a0, const uint16_t* a1, 
     return launch_splitk_finish(a.partial, p.splits, int64_t(p.mr) * a.npad, a.npad, M, N, out_scale, residual, y, s);
 }
 
+// act[m][i] = bf16(silu(g) * u), with g and u the sums over the K slices (in slice order)
+// of the pair's gate and up partials: pair i of column-pair range cg = i / P sits at
+// columns cg 2P + i % P (gate) and cg 2P + P + i % P (up) of a slice's [rows][npad]
+// partials.  Runs after the kernel that wrote them, on the same stream.
+__global__ __launch_bounds__(256) void splitk_finish_swiglu_kernel(const float* __restrict__ partial, int splits,
+                                                                  int64_t split_stride, int64_t row_stride, int M,
+                                                                  int I, int P, uint16_t* act) {
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= M * I) return;
+    const int m = o / I, i = o % I;
+    const float* pg = partial + m * row_stride + size_t(i / P) * 2 * P + i % P;
+    const float* pu = pg + P;
+    float g = 0.f, u = 0.f;
+    for (int sl = 0; sl < splits; ++sl) {
+        g += pg[sl * split_stride];
+        u += pu[sl * split_stride];
+    }
+    act[o] = f32_to_bf16(silu_f32(g) * u);
+}
+
 }  // namespace
+
+hipError_t launch_mfma_pair(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
+                            uint16_t* act, void* ws, const GemvPlan& p, hipStream_t s) {
+    MfmaArgs a{};
+    a.a0 = x;
+    a.lda = K;
+    a.qw = reinterpret_cast<const uint4*>(qw);
+    a.sc = sc;
+    a.M = M;
+    a.K = K;
+    a.N = 2 * I;
+    a.nch = K / 32;
+    a.groups = p.groups;
+    a.kgroups = p.gps;
+    a.splits = p.splits;
+    a.cgroups = p.tiles;
+    a.npad = p.tiles * p.waves * p.cpw * 16;
+    a.y = act;
+    a.partial = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
+    a.m_lo = kDecodeMaskLo;
+    a.m_hi = kDecodeMaskHi;
+    a.half_n = I;
+    a.pairs = p.waves / 2 * p.cpw * 16;
+    const dim3 grid(p.tiles * p.splits);
+    const int threads = p.waves * kWave;
+    const int rb = p.mr / 16;
+    if (M > p.mr || (rb != 1 && rb != 2 && rb != 4) || p.cpw != 1 || p.waves % 2) return hipErrorInvalidValue;
+    hipError_t e;
+    if (rb == 1)
+        e = launch_k(w4_gemv_mfma_kernel<1, kIdentity, kWInt4, 1, true>, grid, threads, p.lds_bytes, s, a);
+    else if (rb == 2)
+        e = launch_k(w4_gemv_mfma_kernel<1, kIdentity, kWInt4, 2, true>, grid, threads, p.lds_bytes, s, a);
+    else
+        e = launch_k(w4_gemv_mfma_kernel<1, kIdentity, kWInt4, 4, true>, grid, threads, p.lds_bytes, s, a);
+    if (e != hipSuccess || p.splits == 1) return e;
+    splitk_finish_swiglu_kernel<<<dim3((M * I + 255) / 256), 256, 0, s>>>(a.partial, p.splits, int64_t(p.mr) * a.npad,
+                                                                         a.npad, M, I, a.pairs, act);
+    return hipGetLastError();
+}
 
 hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,

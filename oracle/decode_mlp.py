@@ -58,7 +58,7 @@ __all__ = [
     "mlp_chain", "product_form_gemv", "factored_form_gemv",
     "product_buffer_bytes", "unfused_act_gemv", "unfused_product_gemv",
     "add_rmsnorm_eager",
-    "add_rmsnorm_gemv_swiglu", "mlp_decode2", "mlp_chain2",
+    "add_rmsnorm_gemv_swiglu", "w4_gemv_swiglu", "mlp_decode2", "mlp_chain2",
     "FP4_BLOCK", "e2m1_decode", "e4m3_decode", "fp4_unpack", "fp4_dequant", "swiglu_fp4_gemv", "fp4_gemv",
 ]
 
@@ -283,27 +283,47 @@ def add_rmsnorm_gemv_swiglu(x, r, norm_w, gu_q, gu_s, eps=1e-6, *, n_chunk=4096)
     return f64_to_bf16(hs), f64_to_bf16(act)
 
 
-def mlp_decode2(x, r, norm_w, gu_q, gu_s, d_q, d_s, out_scale=0.5, eps=1e-6,
-                residual_in_epilogue=True, *, n_chunk=4096):
-    """The layer of ``mlp_decode`` as two kernels' worth of work:
+def w4_gemv_swiglu(x, gu_q, gu_s, *, n_chunk=4096):
+    """The gate_up projection with SwiGLU as its epilogue ([P4] section 5, the gate_up GEMM
+    with a silu * up epilogue writing act): [g, u] = x @ dequant(W_gate_up), not rounded
+    (never written); act = bf16(silu(g) * u).  Columns [0, I) are gate, [I, 2I) up."""
+    gu = _chunked_gemv(bf16_to_f64(x), gu_q, gu_s, n_chunk)
+    I = gu.shape[1] // 2
+    return f64_to_bf16(silu_mul(gu[:, :I], gu[:, I:]))
 
-    1. (h, act) = add_rmsnorm_gemv_swiglu(x, r, norm_w, W_gate_up)
+
+def mlp_decode2(x, r, norm_w, gu_q, gu_s, d_q, d_s, out_scale=0.5, eps=1e-6,
+                residual_in_epilogue=True, *, y_rounded=False, n_chunk=4096):
+    """The layer of ``mlp_decode`` with SwiGLU as the gate_up epilogue (gate/up never
+    written, act written):
+
+    1. (h, act) = add_rmsnorm_gemv_swiglu(x, r, norm_w, W_gate_up)       (y never written)
+       or, with ``y_rounded`` (the norm as its own kernel, which writes y):
+       (h, y) = add_rmsnorm(x, r, norm_w); act = w4_gemv_swiglu(y, W_gate_up)
     2. out = bf16(out_scale * act @ dequant(W_down) [+ h])
     """
-    h, act = add_rmsnorm_gemv_swiglu(x, r, norm_w, gu_q, gu_s, eps, n_chunk=n_chunk)
+    if y_rounded:
+        h, y = add_rmsnorm(x, r, norm_w, eps)
+        act = w4_gemv_swiglu(y, gu_q, gu_s, n_chunk=n_chunk)
+    else:
+        h, act = add_rmsnorm_gemv_swiglu(x, r, norm_w, gu_q, gu_s, eps, n_chunk=n_chunk)
+        y = None
     acc = _chunked_gemv(bf16_to_f64(act), d_q, d_s, n_chunk)
     out = f64_to_bf16(_epilogue(acc, out_scale, h if residual_in_epilogue else None))
-    return {"h": h, "act": act, "out": out}
+    d = {"h": h, "act": act, "out": out}
+    if y is not None:
+        d["y"] = y
+    return d
 
 
-def mlp_chain2(x0, r0, layers, *, keep=False):
-    """``mlp_chain`` built from the two-kernel layer (residual add deferred)."""
+def mlp_chain2(x0, r0, layers, *, keep=False, y_rounded=False):
+    """``mlp_chain`` built from ``mlp_decode2`` (residual add deferred)."""
     x, r = x0, r0
     trace = []
     for L in layers:
         d = mlp_decode2(x, r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
                         L.down.qweight, L.down.scales, L.out_scale, L.eps,
-                        residual_in_epilogue=False)
+                        residual_in_epilogue=False, y_rounded=y_rounded)
         if keep:
             trace.append(d)
         x, r = d["out"], d["h"]

@@ -11,7 +11,7 @@ import memory_bound_decode_add_amd as F
 import synth
 from helpers import assert_bits_equal, say
 from test_gpu_mlp import check_layer, dev_layers
-from test_gpu_mlp2 import check_layer2
+from test_gpu_mlp2 import check_layer2, check_layer2_mc
 
 pytestmark = pytest.mark.gpu
 
@@ -37,10 +37,15 @@ def first_layer_parity(inp, layer, M, H, I, two_kernel):
         b = F.Mlp2Buffers.empty(M, H, I)
         b.x.copy_(F.from_bits(inp.x))
         b.residual.copy_(F.from_bits(inp.r))
-        F.mlp_decode2(layer, b)
+        ws = F.workspace(F.mlp2_workspace_bytes(M, H, I))
+        F.mlp_decode2(layer, b, ws)
         torch.cuda.synchronize()
         got = {"h": F.to_bits(b.residual), "act": F.to_bits(b.act), "out": F.to_bits(b.out)}
-        check_layer2(inp.layers[0], inp.x, inp.r, got, False)
+        if M <= 4:
+            check_layer2(inp.layers[0], inp.x, inp.r, got, False)
+        else:   # the matrix-core form: y is in the workspace
+            got["y"] = F.to_bits(ws[: M * H * 2].view(torch.int16).view(torch.bfloat16).reshape(M, H))
+            check_layer2_mc(inp.layers[0], inp.x, inp.r, got, False)
     else:
         b = F.MlpBuffers.empty(M, H, I)
         b.x.copy_(F.from_bits(inp.x))
@@ -64,7 +69,8 @@ def replay_and_check(graph, b, inp, want, tag):
 
 
 @pytest.mark.parametrize("two_kernel,M,H,I,n", [(False, 1, 256, 512, 4), (False, 16, 384, 256, 3),
-                                                (True, 1, 1536, 8960, 4), (True, 3, 512, 640, 3)])
+                                                (True, 1, 1536, 8960, 4), (True, 3, 512, 640, 3),
+                                                (True, 16, 384, 256, 3)])
 def test_graph_update_repoints_layers_and_buffers(two_kernel, M, H, I, n):
     say(f"[graph update] {'two' if two_kernel else 'three'}-kernel layers, M={M} H={H} I={I}, {n} layers")
     inp_a = synth.mlp_inputs(M, H, I, n_layers=n, seed=101 + M)

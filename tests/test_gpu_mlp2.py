@@ -1,6 +1,7 @@
-"""GPU parity of the two-kernel decode-MLP layer (add + RMSNorm as the gate_up GEMV's
-prologue, SwiGLU as its epilogue, then the down GEMV), its chain and its hipGraph,
-against the fp64 oracle."""
+"""GPU parity of the decode-MLP layer with SwiGLU as the gate_up GEMV's epilogue: up to 4
+rows two kernels (add + RMSNorm as the gate_up GEMV's prologue, then the down GEMV), from
+5 rows three (the norm, the matrix-core gate_up with the SwiGLU epilogue, the down GEMV);
+its chain and its hipGraph, against the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -142,3 +143,94 @@ def test_chain2_qwen2_5_1_5b_28_layers_graph():
     # chaining its own 28 layers would also measure how single-ulp differences in the
     # materialised bf16 tensors grow through the chain, which the per-call bound does
     # not cover.)
+
+
+# ----------------------------------------------------------------------------
+# the gate_up projection with the SwiGLU epilogue on the matrix cores, and the layer
+# built on it from 5 rows
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,I", [(16, 4096, 14336), (5, 1024, 520), (1, 1536, 8960), (8, 9216, 1032),
+                                   (16, 14336, 2048), (32, 2048, 776), (64, 4096, 1024), (3, 128, 8)])
+def test_w4_gemv_swiglu(M, K, I):
+    need = F.w4_gemv_swiglu_workspace_bytes(M, K, I)
+    say(f"[gate_up+swiglu] M={M} K={K} I={I} workspace {need} B")
+    inp = synth.swiglu_gemv_inputs(M, K, 2 * I, seed=M * 31 + K + I)
+    W = F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales)
+    x = F.from_bits(inp.g)
+    ws = torch.full((max(16, need),), 0xFF, dtype=torch.uint8, device="cuda")   # NaN patterns
+    act = F.to_bits(F.w4_gemv_swiglu(x, W, ws=ws))
+    ref = O.w4_gemv_swiglu(inp.g, inp.W.qweight, inp.W.scales)
+    say("  worst err/bound", assert_close(act, ref, "act"))
+    assert_bits_equal(F.to_bits(F.w4_gemv_swiglu(x, W, ws=ws)), act, "repeat")
+
+
+def check_layer2_mc(L, x, r, got, resid):
+    """The three kernels of the matrix-core form, each against the oracle fed the bf16
+    inputs that kernel read (y is read back from the workspace)."""
+    h, y = O.add_rmsnorm(x, r, L.norm_w, L.eps)
+    assert_bits_equal(got["h"], h, "h")
+    w = [assert_close(got["y"], y, "y")]
+    act = O.w4_gemv_swiglu(got["y"], L.gate_up.qweight, L.gate_up.scales)
+    w.append(assert_close(got["act"], act, "act"))
+    out = O.w4_gemv(got["act"], L.down.qweight, L.down.scales, L.out_scale, return_f64=True)[1]
+    if resid:
+        out = out + O.bf16_to_f64(got["h"])
+    w.append(assert_close(got["out"], O.f64_to_bf16(out), "out"))
+    return w
+
+
+@pytest.mark.parametrize("M,H,I", [(16, 4096, 14336), (5, 512, 640), (8, 1024, 2048), (16, 384, 256),
+                                   (12, 1536, 8960)])
+def test_mlp_decode2_matrix_core_both_residual_modes(M, H, I):
+    say(f"[mlp2, matrix cores] M={M} H={H} I={I}")
+    inp = synth.mlp_inputs(M, H, I, n_layers=1, seed=M + H + I + 2)
+    for resid in (True, False):
+        layer = dev_layers(inp, resid)[0]
+        b = F.Mlp2Buffers.empty(M, H, I)
+        b.x.copy_(F.from_bits(inp.x))
+        b.residual.copy_(F.from_bits(inp.r))
+        ws = F.workspace(F.mlp2_workspace_bytes(M, H, I))
+        F.mlp_decode2(layer, b, ws)
+        torch.cuda.synchronize()
+        y = ws[: M * H * 2].view(torch.int16).view(torch.bfloat16).reshape(M, H)
+        got = {"h": F.to_bits(b.residual), "y": F.to_bits(y), "act": F.to_bits(b.act), "out": F.to_bits(b.out)}
+        say(f"  resid={resid} worst err/bound (y, act, out)", check_layer2_mc(inp.layers[0], inp.x, inp.r, got, resid))
+
+
+def test_chain2_matrix_core_graph():
+    M, H, I, n = 16, 512, 1024, 4
+    say(f"[chain2, matrix cores] M={M} H={H} I={I}, {n} layers: every layer, graph == eager")
+    inp = synth.mlp_inputs(M, H, I, n_layers=n, seed=77)
+    layers = dev_layers(inp, False)
+    b = F.Mlp2Buffers.empty(M, H, I, out_is_x=True)
+    ws = F.workspace(F.mlp2_workspace_bytes(M, H, I))
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    trace = []
+    for L in layers:
+        xin, rin = F.to_bits(b.x), F.to_bits(b.residual)
+        F.mlp_decode2(L, b, ws)
+        torch.cuda.synchronize()
+        y = ws[: M * H * 2].view(torch.int16).view(torch.bfloat16).reshape(M, H)
+        trace.append({"x": xin, "r": rin, "h": F.to_bits(b.residual), "y": F.to_bits(y), "act": F.to_bits(b.act),
+                      "out": F.to_bits(b.x)})
+    for l, t in enumerate(trace):
+        check_layer2_mc(inp.layers[l], t["x"], t["r"], t, False)
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    F.mlp_chain2(layers, b, ws)
+    torch.cuda.synchronize()
+    assert_bits_equal(F.to_bits(b.x), trace[-1]["out"], "chain x")
+    assert_bits_equal(F.to_bits(b.residual), trace[-1]["h"], "chain r")
+    graph = F.Mlp2Graph(layers, b, ws)
+    # three kernels per layer, plus a slice-summing kernel after each K-split GEMV
+    assert 3 * n <= graph.kernel_count <= 5 * n
+    for rep in range(3):
+        b.x.copy_(F.from_bits(inp.x))
+        b.residual.copy_(F.from_bits(inp.r))
+        graph.launch()
+        torch.cuda.synchronize()
+        assert_bits_equal(F.to_bits(b.x), trace[-1]["out"], f"graph replay {rep} x")
+        assert_bits_equal(F.to_bits(b.residual), trace[-1]["h"], f"graph replay {rep} r")
+        torch.randn(1 << 20, device="cuda").sum().item()
+    graph.close()

@@ -411,8 +411,9 @@ def test_mlp_chain_defers_residual():
 # ----------------------------------------------------------------------------
 # the two-kernel layer (norm as the gate_up prologue, SwiGLU as its epilogue)
 # ----------------------------------------------------------------------------
-def _py_layer2(x, r, nw, guq, gus, dq, ds, s, eps, residual_in_epilogue):
-    """Pure-Python loops: y and gate/up are not rounded (never written), act is."""
+def _py_layer2(x, r, nw, guq, gus, dq, ds, s, eps, residual_in_epilogue, round_y=False):
+    """Pure-Python loops: gate/up are not rounded (never written), act is; y is rounded only
+    with round_y (the form whose norm runs as its own kernel and writes y)."""
     M, H = x.shape
     I = guq.shape[0] // 2
 
@@ -425,6 +426,8 @@ def _py_layer2(x, r, nw, guq, gus, dq, ds, s, eps, residual_in_epilogue):
         h = [_py_round(bf16_bits_to_float(x[m, j]) + bf16_bits_to_float(r[m, j])) for j in range(H)]
         inv = 1.0 / math.sqrt(sum(v * v for v in h) / H + eps)
         y = [h[j] * inv * bf16_bits_to_float(nw[j]) for j in range(H)]
+        if round_y:
+            y = [_py_round(v) for v in y]
         g = [sum(y[k] * wq(guq, gus, k, n) for k in range(H)) for n in range(I)]
         u = [sum(y[k] * wq(guq, gus, k, I + n) for k in range(H)) for n in range(I)]
         act = [_py_round(g[n] / (1.0 + math.exp(-g[n])) * u[n]) for n in range(I)]
@@ -436,14 +439,16 @@ def _py_layer2(x, r, nw, guq, gus, dq, ds, s, eps, residual_in_epilogue):
     return {k: np.array(v) for k, v in outs.items()}
 
 
+@pytest.mark.parametrize("round_y", [False, True])
 @pytest.mark.parametrize("resid", [True, False])
-def test_mlp_layer2_matches_brute_force(resid):
+def test_mlp_layer2_matches_brute_force(resid, round_y):
     inp = synth.mlp_inputs(2, 128, 128, n_layers=1, seed=17, out_scale=0.5)
     L = inp.layers[0]
     d = O.mlp_decode2(inp.x, inp.r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
-                      L.down.qweight, L.down.scales, L.out_scale, L.eps, residual_in_epilogue=resid)
+                      L.down.qweight, L.down.scales, L.out_scale, L.eps, residual_in_epilogue=resid,
+                      y_rounded=round_y)
     ref = _py_layer2(inp.x, inp.r, L.norm_w, L.gate_up.qweight, L.gate_up.scales,
-                     L.down.qweight, L.down.scales, L.out_scale, L.eps, resid)
+                     L.down.qweight, L.down.scales, L.out_scale, L.eps, resid, round_y)
     for k in ("h", "act", "out"):
         ours = O.bf16_to_f64(d[k])
         mism = ours != ref[k]

@@ -198,3 +198,25 @@ def test_two_valid_chains_diverge_while_every_layer_is_within_the_bound():
         free.append(ratio(xb, xa))
     assert max(per_layer) <= 1.0, per_layer
     assert max(free) > 2.0, free
+
+
+# ----------------------------------------------------------------------------
+# the gate_up projection with the SwiGLU epilogue
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,I", [(1, 128, 8), (3, 256, 16)])
+def test_w4_gemv_swiglu_matches_brute_force(M, K, I):
+    inp = synth.swiglu_gemv_inputs(M, K, 2 * I, seed=K + I)
+    x = bf16_by_torch(inp.g)
+    act = O.w4_gemv_swiglu(inp.g, inp.W.qweight, inp.W.scales)
+    g = np.stack([brute_column(x, inp.W.qweight, inp.W.scales, n) for n in range(I)], axis=1)
+    u = np.stack([brute_column(x, inp.W.qweight, inp.W.scales, I + n) for n in range(I)], axis=1)
+    want = np.array([[g[m, i] / (1.0 + math.exp(-g[m, i])) * u[m, i] for i in range(I)] for m in range(M)])
+    ref = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # one rounding of the exact value: equal except within 1e-12 of a tie
+    assert np.mean(act == ref) > 0.95
+    assert np.all(np.abs(O.bf16_to_f64(act) - want) <= 2.0 ** -8 * np.abs(want) + 1e-300)
+    # gate and up are not rounded on the way: the three-kernel layer's act, which reads the
+    # rounded gate_up, differs from it
+    gu_r = O.w4_gemv(inp.g, inp.W.qweight, inp.W.scales)
+    act_r = O.f64_to_bf16(O.silu_mul(O.bf16_to_f64(gu_r[:, :I]), O.bf16_to_f64(gu_r[:, I:])))
+    assert not np.array_equal(act, act_r)
