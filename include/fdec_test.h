@@ -34,6 +34,12 @@ extern "C" {
 FDEC_API void fdec_set_gemv_split(int32_t k);
 FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_workgroup);
 FDEC_API void fdec_test_fail_launches(int32_t on);
+/* fdec_set_mfma_plan(kernel, tiles, groups_per_wave): the matrix-core kernel GEMVs of
+ *   5..16 rows run.  kernel 0: the built-in choice; 1: the row-block kernel (its
+ *   activation staged in LDS); 2: the kernel whose waves split K, with `tiles` 16-column
+ *   tiles per workgroup (4 or 8) and `groups_per_wave` 128-wide groups per wave (1..4; at
+ *   most 2 with the SwiGLU prologue), 0 for either leaving the built-in choice. */
+FDEC_API void fdec_set_mfma_plan(int32_t kernel, int32_t tiles, int32_t groups_per_wave);
 
 /* Workspace sizes under the overrides active now (equal to the fdec.h queries when none
  * is): fdec_test_gemv_workspace_bytes for fdec_swiglu_w4_gemv / fdec_w4_gemv,

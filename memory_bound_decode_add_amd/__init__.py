@@ -114,6 +114,7 @@ _SIGS = {
     "fdec_set_gemv_split": (None, [_i32]),
     "fdec_set_gemv_tiling": (None, [_i32, _i32]),
     "fdec_test_fail_launches": (None, [_i32]),
+    "fdec_set_mfma_plan": (None, [_i32, _i32, _i32]),
     "fdec_test_gemv_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "fdec_test_mlp_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "fdec_test_empty_kernel": (ctypes.c_int, [_i32, _i32, _c_p]),
@@ -768,12 +769,19 @@ def fp4_dequant(W: FP4Weight) -> torch.Tensor:
 # test, tuning and measurement controls (include/fdec_test.h; not for production use)
 # ----------------------------------------------------------------------------
 _overrides_active = False
-_override_state = {"split": 0, "tiling": (0, 0)}
+_override_state = {"split": 0, "tiling": (0, 0), "mfma": (0, 0, 0)}
 
 
 def _note_overrides():
     global _overrides_active
-    _overrides_active = _override_state["split"] != 0 or _override_state["tiling"] != (0, 0)
+    _overrides_active = (_override_state["split"] != 0 or _override_state["tiling"] != (0, 0)
+                         or _override_state["mfma"] != (0, 0, 0))
+
+
+def set_mfma_plan(kernel: int, tiles: int = 0, groups_per_wave: int = 0):
+    lib().fdec_set_mfma_plan(int(kernel), int(tiles), int(groups_per_wave))
+    _override_state["mfma"] = (int(kernel), int(tiles), int(groups_per_wave))
+    _note_overrides()
 
 
 def set_gemv_split(k: int):

@@ -27,6 +27,9 @@ std::atomic<int> g_fail_launches{0};
 std::atomic<int> g_forced_split{0};
 std::atomic<int> g_col_waves{0};
 std::atomic<int> g_col_cols{0};
+std::atomic<int> g_mfma_kernel{0};
+std::atomic<int> g_mfma_tiles{0};
+std::atomic<int> g_mfma_gw{0};
 
 constexpr size_t kAlign = 256;   // sub-buffer alignment inside workspaces
 
@@ -218,8 +221,8 @@ struct LayerPlan {
 };
 LayerPlan plan_layer(int M, int H, int I, const Overrides& ov) {
     LayerPlan lp;
-    lp.gu = plan_gemv(M, H, 2 * I, ov);
-    lp.dn = plan_gemv(M, I, H, ov);
+    lp.gu = plan_gemv(M, H, 2 * I, ov, kIdentity);
+    lp.dn = plan_gemv(M, I, H, ov, kSwiGLU);
     lp.ws = std::max(lp.gu.partial_bytes, lp.dn.partial_bytes);
     return lp;
 }
@@ -291,7 +294,7 @@ size_t mlp2_ws(int M, int H, int I, const Overrides& ov) {
     if (layer2_fused_norm(M)) return align_up(size_t(M) * H * 2);
     GemvPlan pp;
     if (!plan_mfma_pair(M, H, I, pp)) return 0;
-    return align_up(size_t(M) * H * 2) + std::max(pp.partial_bytes, plan_gemv(M, I, H, ov).partial_bytes);
+    return align_up(size_t(M) * H * 2) + std::max(pp.partial_bytes, plan_gemv(M, I, H, ov, kIdentity).partial_bytes);
 }
 
 int check_layer2(const fdec_mlp_layer* L, int M, LayerDims* d, const Overrides& ov) {
@@ -340,7 +343,7 @@ hipError_t enqueue_layer2(const fdec_mlp_layer* L, int M, LayerDims d, const Ove
         void* pws = static_cast<char*>(ws) + align_up(size_t(M) * d.H * 2);
         GemvPlan pp;
         if (!plan_mfma_pair(M, d.H, d.I, pp)) return hipErrorInvalidValue;
-        const GemvPlan dp = plan_gemv(M, d.I, d.H, ov);
+        const GemvPlan dp = plan_gemv(M, d.I, d.H, ov, kIdentity);
         hipError_t e = launch_add_rmsnorm(x, residual, L->norm_weight, L->eps, M, d.H, residual, y, s);
         if (e != hipSuccess) return e;
         e = launch_mfma_pair(y, L->gate_up.qweight, L->gate_up.scales, M, d.H, d.I, act, pws, pp, s);
@@ -403,6 +406,9 @@ Overrides current_overrides() {
     ov.split = g_forced_split.load();
     ov.col_waves = g_col_waves.load();
     ov.col_cols = g_col_cols.load();
+    ov.mfma_kernel = g_mfma_kernel.load();
+    ov.mfma_tiles = g_mfma_tiles.load();
+    ov.mfma_gw = g_mfma_gw.load();
     return ov;
 }
 }  // namespace fdec
@@ -539,9 +545,16 @@ FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_workgroup) {
     g_col_cols.store(cols_per_workgroup > 0 ? cols_per_workgroup : 0);
 }
 FDEC_API void fdec_test_fail_launches(int32_t on) { g_fail_launches.store(on ? 1 : 0); }
+FDEC_API void fdec_set_mfma_plan(int32_t kernel, int32_t tiles, int32_t groups_per_wave) {
+    g_mfma_kernel.store(kernel == 1 || kernel == 2 ? kernel : 0);
+    g_mfma_tiles.store(tiles == 4 || tiles == 8 ? tiles : 0);
+    g_mfma_gw.store(groups_per_wave >= 1 && groups_per_wave <= 4 ? groups_per_wave : 0);
+}
 
 FDEC_API size_t fdec_test_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
-    return w4_gemv_shape_ok(M, K, N) ? plan_gemv(M, K, N, current_overrides()).partial_bytes : 0;
+    if (!w4_gemv_shape_ok(M, K, N)) return 0;
+    const Overrides ov = current_overrides();
+    return std::max(plan_gemv(M, K, N, ov, kSwiGLU).partial_bytes, plan_gemv(M, K, N, ov, kIdentity).partial_bytes);
 }
 
 FDEC_API size_t fdec_test_mlp_workspace_bytes(int32_t M, int32_t H, int32_t I) {
@@ -606,7 +619,7 @@ FDEC_API int fdec_swiglu_w4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t
                                  void* ws, size_t ws_bytes, fdec_stream stream) {
     if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
     const bool shape_ok = w4_gemv_shape_ok(M, W->K, W->N);
-    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides()) : GemvPlan{};
+    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides(), kSwiGLU) : GemvPlan{};
     const int st = check_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true, p.partial_bytes,
                               kMaxGemvRows);
     if (st != FDEC_OK) return st;
@@ -655,7 +668,7 @@ FDEC_API int fdec_swiglu_w4_gemv_noalloc(const fdec_bf16* g, const fdec_bf16* u,
                                          fdec_bf16* y, fdec_stream stream) {
     if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
     const bool shape_ok = w4_gemv_shape_ok(M, W->K, W->N);
-    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides()) : GemvPlan{};
+    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides(), kSwiGLU) : GemvPlan{};
     // the same checks as fdec_swiglu_w4_gemv with no workspace, then the scratch limit
     int st = check_gemv(g, u, ldgu, W, out_scale, residual, M, y, nullptr, 0, true, 0, kMaxGemvRows);
     if (st != FDEC_OK) return st;
@@ -688,7 +701,7 @@ FDEC_API int fdec_w4_gemv(const fdec_bf16* x, const fdec_w4* W, const float* out
                           void* ws, size_t ws_bytes, fdec_stream stream) {
     if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
     const bool shape_ok = w4_gemv_shape_ok(M, W->K, W->N);
-    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides()) : GemvPlan{};
+    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides(), kIdentity) : GemvPlan{};
     const int st = check_gemv(x, nullptr, W->K, W, out_scale, nullptr, M, y, ws, ws_bytes, false, p.partial_bytes,
                               kMaxGemvRows);
     if (st != FDEC_OK) return st;
@@ -932,7 +945,7 @@ FDEC_API int fdec_mlp_graph_update2(fdec_graph graph, const fdec_mlp_layer* laye
 FDEC_API size_t fdec_unfused_gemv_workspace_bytes(int32_t mode, int32_t M, int32_t K, int32_t N) {
     if (M < 1 || M > 16 || K <= 0 || K % 128 || N <= 0 || N % 8) return 0;
     if (mode == FDEC_UNFUSED_PRODUCT) return M == 1 ? size_t(M) * K * N * 4 : 0;
-    if (mode == FDEC_UNFUSED_ACT) return unfused_act_ws(M, K, plan_gemv(M, K, N, Overrides{}));
+    if (mode == FDEC_UNFUSED_ACT) return unfused_act_ws(M, K, plan_gemv(M, K, N, Overrides{}, kIdentity));
     return 0;
 }
 
@@ -944,7 +957,7 @@ FDEC_API int fdec_unfused_swiglu_w4_gemv(int32_t mode, const fdec_bf16* g, const
     if (mode == FDEC_UNFUSED_PRODUCT && M != 1)
         return fail(FDEC_ERR_UNSUPPORTED, "the materialised-product sequence is defined for M == 1 only (M = %d)", M);
     const bool shape_ok = M >= 1 && M <= 16 && W->K > 0 && W->K % 128 == 0 && W->N > 0 && W->N % 8 == 0;
-    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides()) : GemvPlan{};
+    const GemvPlan p = shape_ok ? plan_gemv(M, W->K, W->N, current_overrides(), kIdentity) : GemvPlan{};
     const size_t need = !shape_ok ? 0
                         : mode == FDEC_UNFUSED_PRODUCT ? size_t(M) * W->K * W->N * 4
                                                        : unfused_act_ws(M, W->K, p);

@@ -969,8 +969,8 @@ bool plan_mfma(int M, int K, int N, GemvPlan& p) {
     return true;
 }
 
-// The gate_up projection with the SwiGLU epilogue (pair mode of the matrix-core kernel,
-// 1..64 rows): even wave counts, P = 8 waves column pairs per workgroup.  The K slices
+// The gate_up projection with the SwiGLU epilogue (pair mode of the row-block matrix-core
+// kernel, 1..64 rows): even wave counts, P = 8 waves column pairs per workgroup.  The K slices
 // are kept whole (one slice, the epilogue in the kernel) when that already gives about
 // one workgroup per CU; otherwise split toward 256 workgroups, summed by the pair finish.
 bool plan_mfma_pair(int M, int K, int I, GemvPlan& p) {
@@ -1011,7 +1011,7 @@ bool plan_mfma_pair(int M, int K, int I, GemvPlan& p) {
     return p.lds_bytes <= kMaxLds;
 }
 
-GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov) {
+GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov, Prologue pro) {
     GemvPlan p{};
     p.groups = K / kGroup;
     if (M > 16) {                 // only the matrix-core kernel takes more than 16 rows
@@ -1019,6 +1019,14 @@ GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov) {
         return p;
     }
     if (ov.split == 0 && plan_column(M, K, N, p, ov)) return p;
+    p = GemvPlan{};
+    // the kernel whose waves split K: one group per wave, SwiGLU prologue, up to about
+    // 12 MB of weights (measured faster there, slower elsewhere), or when forced
+    const bool kmfma = ov.mfma_kernel == 2 || (ov.mfma_kernel == 0 && pro == kSwiGLU && M > 4 &&
+                                                int64_t(K) * N / 2 <= (int64_t(12) << 20));
+    Overrides ovk = ov;
+    if (ov.mfma_kernel == 0) ovk.mfma_gw = 1;
+    if (ov.split == 0 && kmfma && plan_kmfma(M, K, N, pro == kSwiGLU ? 2 : 4, p, ovk)) return p;
     p = GemvPlan{};
     if (ov.split == 0 && plan_mfma(M, K, N, p)) return p;
     p = GemvPlan{};
@@ -1047,8 +1055,8 @@ GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov) {
 }
 
 size_t gemv_workspace_bytes(int M, int K, int N) {
-    const GemvPlan p = plan_gemv(M, K, N, Overrides{});
-    return p.partial_bytes;
+    return std::max(plan_gemv(M, K, N, Overrides{}, kSwiGLU).partial_bytes,
+                    plan_gemv(M, K, N, Overrides{}, kIdentity).partial_bytes);
 }
 
 hipError_t launch_splitk_finish(const float* partial, int splits, int64_t split_stride, int64_t row_stride, int M,
@@ -1086,6 +1094,7 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
             default: return launch_col<4>(pro, a, p, s);
         }
     }
+    if (p.kind == kKMfma) return launch_kmfma(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
     if (p.kind == kMfma) return launch_mfma(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
     SplitArgs a{};
     a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};

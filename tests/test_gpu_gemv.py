@@ -271,3 +271,34 @@ def test_gemv_graph_replays_match_eager(M, K, N):
         F.swiglu_w4_gemv(g, u, W, s, res, ws=ws)                  # eager work between replays
         torch.cuda.synchronize()
     assert_close(ref, O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 0.5, inp.residual), "eager vs oracle")
+
+
+# ---------------------------------------------------------------------------
+# the matrix-core kernel whose waves split K: every tile and groups-per-wave variant,
+# forced (the built-in plan takes it with one group per wave and the SwiGLU prologue)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("pro", ["swiglu", "identity"])
+@pytest.mark.parametrize("tiles,gw", [(8, 1), (8, 2), (4, 1), (4, 2), (8, 3), (4, 4)])
+def test_kmfma_kernel_every_variant(pro, tiles, gw):
+    if pro == "swiglu" and gw > 2:
+        pytest.skip("the SwiGLU prologue takes at most 2 groups per wave")
+    M, K, N = 12, 4224, 1000            # 33 groups: a ragged last slice; 1000 columns: a ragged tile
+    say(f"[kmfma] {pro} tiles={tiles} groups/wave={gw} M={M} K={K} N={N}")
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=tiles * 10 + gw, out_scale=0.5, with_residual=True)
+    g, u, W, res = to_dev(inp)
+    s = F.scalar(0.5)
+    F.set_mfma_plan(2, tiles, gw)
+    try:
+        ws = torch.full((max(16, F.gemv_workspace_bytes(M, K, N)),), 0xFF, dtype=torch.uint8, device=DEV)
+        if pro == "swiglu":
+            y = F.to_bits(F.swiglu_w4_gemv(g, u, W, s, res, ws=ws))
+            y2 = F.to_bits(F.swiglu_w4_gemv(g, u, W, s, res, ws=ws))
+            ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 0.5, inp.residual)
+        else:
+            y = F.to_bits(F.w4_gemv(g, W, s, ws=ws))
+            y2 = F.to_bits(F.w4_gemv(g, W, s, ws=ws))
+            ref = O.w4_gemv(inp.g, inp.W.qweight, inp.W.scales, 0.5)
+    finally:
+        F.set_mfma_plan(0)
+    say("  worst err/bound", assert_close(y, ref, "y"))
+    assert_bits_equal(y, y2, "repeat")
