@@ -352,6 +352,35 @@ FDEC_API int fdec_mlp_graph_update2(fdec_graph graph, const fdec_mlp_layer* laye
                                     size_t ws_bytes, fdec_stream stream);
 
 /*
+ * Prefill sizes ([P5] "Kernel Fusion, torch.compile and CUDA Graphs, Measured": at a
+ * 2,048-token prefill the MLP half is compute-bound and the fusion win shrinks).  A tiled
+ * GEMM would recompute a fused SwiGLU prologue once per column tile, so at these sizes the
+ * activation is formed once by its own elementwise kernel and the GEMM reads it as stored.
+ *
+ * fdec_swiglu: act[m][k] = bf16(silu(g[m][k]) * u[m][k]), one rounding ([P5] Step 1: the
+ *   fused SwiGLU, 6 bytes per element).  g, u: bf16 [M][ldgu] (ldgu >= K, % 8 == 0);
+ *   act: bf16 [M][K], K % 8 == 0; act may not overlap g or u.  M == 0 enqueues nothing.
+ * fdec_w4_gemm: y = bf16(s * x @ dequant(W) (+ residual)), s = *out_scale or 1, for any
+ *   number of rows 1 <= M <= 2^24 (matrix cores, bf16 operands: the int4 weights are exact
+ *   in bf16 and x is used as stored; fp32 accumulation, the group scales applied to each
+ *   group's fp32 sum).  x: bf16 [M][K];  y: bf16 [M][N], may equal residual, no other
+ *   overlap.  No workspace.
+ * fdec_swiglu_w4_gemm: fdec_swiglu into the workspace (act, M * K * 2 bytes =
+ *   fdec_swiglu_w4_gemm_workspace_bytes(M, K)), then fdec_w4_gemm on it:
+ *   y = bf16(s * bf16(silu(g) * u) @ dequant(W) (+ residual)).
+ */
+FDEC_API int fdec_swiglu(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, int32_t M,
+                         int32_t K, fdec_bf16* act, fdec_stream stream);
+FDEC_API int fdec_w4_gemm(const fdec_bf16* x, const fdec_w4* W, const float* out_scale,
+                          const fdec_bf16* residual, int32_t M, fdec_bf16* y,
+                          fdec_stream stream);
+FDEC_API size_t fdec_swiglu_w4_gemm_workspace_bytes(int32_t M, int32_t K);
+FDEC_API int fdec_swiglu_w4_gemm(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu,
+                                 const fdec_w4* W, const float* out_scale,
+                                 const fdec_bf16* residual, int32_t M, fdec_bf16* y,
+                                 void* ws, size_t ws_bytes, fdec_stream stream);
+
+/*
  * FP4 weights: [P3] ("PyTorch folds NVFP4 output scaling into NVGEMM candidates for
  * decode workloads") restricts its fold to packed FP4 inputs with E4M3 1x16 block scales
  * and a zero-dimensional fp32 multiplier.  Read here as weight-only quantisation behind

@@ -82,6 +82,11 @@ _SIGS = {
                                                        _c_p, _c_p, _c_p]),
     "fdec_mlp2_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "fdec_w4_gemv_swiglu_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_swiglu": (ctypes.c_int, [_c_p, _c_p, _i64, _i32, _i32, _c_p, _c_p]),
+    "fdec_w4_gemm": (ctypes.c_int, [_c_p, ctypes.POINTER(CW4), _c_p, _c_p, _i32, _c_p, _c_p]),
+    "fdec_swiglu_w4_gemm_workspace_bytes": (_sz, [_i32, _i32]),
+    "fdec_swiglu_w4_gemm": (ctypes.c_int, [_c_p, _c_p, _i64, ctypes.POINTER(CW4), _c_p, _c_p, _i32, _c_p, _c_p,
+                                           _sz, _c_p]),
     "fdec_w4_gemv_swiglu": (ctypes.c_int, [_c_p, ctypes.POINTER(CW4), _i32, _c_p, _c_p, _sz, _c_p]),
     "fdec_mlp_decode2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "fdec_mlp_chain2": (ctypes.c_int, [ctypes.POINTER(CLayer), _i32, _i32, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
@@ -546,6 +551,63 @@ def w4_gemv_swiglu(x, gate_up: W4Weight, out=None, ws=None):
     _check(lib().fdec_w4_gemv_swiglu(x.data_ptr(), ctypes.byref(cw), M, act.data_ptr(), ws.data_ptr(), ws.numel(),
                                      _stream(x.device)))
     return act
+
+
+# ----------------------------------------------------------------------------
+# prefill sizes
+# ----------------------------------------------------------------------------
+def swiglu(g, u, out=None):
+    """act = bf16(silu(g) * u), one rounding; g, u are [M, K] views with one row stride."""
+    M, K = g.shape
+    ld = _rows(g, "g", M, K)
+    if M > 1 and _rows(u, "u", M, K) != ld:
+        raise ValueError("g and u must share a row stride")
+    act = torch.empty((M, K), dtype=torch.bfloat16, device=g.device) if out is None else out
+    _need(act, "out", torch.bfloat16, shape=(M, K))
+    _check(lib().fdec_swiglu(g.data_ptr(), u.data_ptr(), ld, M, K, act.data_ptr(), _stream(g.device)))
+    return act
+
+
+def w4_gemm(x, W: W4Weight, out_scale=None, residual=None, out=None):
+    """y = bf16(s * x @ dequant(W) (+ residual)) for any number of rows (matrix-core GEMM)."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[1] != W.K:
+        raise ValueError("x must be [M, K]")
+    M = x.shape[0]
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    cw = W.c()
+    _check(lib().fdec_w4_gemm(x.data_ptr(), ctypes.byref(cw), _ptr(out_scale), _ptr(residual), M, y.data_ptr(),
+                              _stream(x.device)))
+    return y
+
+
+def swiglu_w4_gemm_workspace_bytes(M, K) -> int:
+    return int(lib().fdec_swiglu_w4_gemm_workspace_bytes(M, K))
+
+
+def swiglu_w4_gemm(g, u, W: W4Weight, out_scale=None, residual=None, out=None, ws=None):
+    """y = bf16(s * bf16(silu(g) * u) @ dequant(W) (+ residual)): the prefill-size path
+    (the SwiGLU pass into the workspace, then the GEMM)."""
+    M = g.shape[0]
+    ld = _rows(g, "g", M, W.K)
+    if M > 1 and _rows(u, "u", M, W.K) != ld:
+        raise ValueError("g and u must share a row stride")
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=g.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    ws = _ws(ws, swiglu_w4_gemm_workspace_bytes(M, W.K), g.device)
+    cw = W.c()
+    _check(lib().fdec_swiglu_w4_gemm(g.data_ptr(), u.data_ptr(), ld, ctypes.byref(cw), _ptr(out_scale),
+                                     _ptr(residual), M, y.data_ptr(), ws.data_ptr(), ws.numel(), _stream(g.device)))
+    return y
 
 
 def mlp2_workspace_bytes(M, H, I) -> int:

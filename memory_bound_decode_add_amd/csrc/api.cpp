@@ -1038,6 +1038,85 @@ FDEC_API int fdec_unfused_mlp_decode(const fdec_mlp_layer* layer, int32_t M, con
     return hip_status(e, "unfused layer launch");
 }
 
+// ---- prefill sizes: the fused SwiGLU elementwise pass and the W4 GEMM ----
+namespace {
+int check_prefill_gemm(const fdec_bf16* x, const fdec_w4* W, const float* out_scale, const fdec_bf16* residual,
+                       int M, const fdec_bf16* y) {
+    int st;
+    if ((st = check_w4(W, "W")) != FDEC_OK) return st;
+    if (M < 1 || M > (1 << 24)) return fail(FDEC_ERR_SHAPE, "M = %d must be in [1, 2^24]", M);
+    if (!x || !y) return fail(FDEC_ERR_NULL, "x and y are required");
+    if (!aligned16(x) || !aligned16(y) || (residual && !aligned16(residual)))
+        return fail(FDEC_ERR_ALIGN, "x, y and residual must be 16-byte aligned");
+    if (out_scale && !aligned4(out_scale)) return fail(FDEC_ERR_ALIGN, "out_scale must be 4-byte aligned");
+    const Span X{x, size_t(M) * W->K * 2}, Y{y, size_t(M) * W->N * 2};
+    const Span ins[] = {X, w4_qspan(W), w4_sspan(W), {out_scale, 4}};
+    for (const Span& in : ins)
+        if (overlap(Y, in)) return fail(FDEC_ERR_ALIAS, "y overlaps an input");
+    if (residual && overlap(Y, Span{residual, Y.bytes}) && residual != y)
+        return fail(FDEC_ERR_ALIAS, "y may only alias residual exactly");
+    return FDEC_OK;
+}
+}  // namespace
+
+FDEC_API int fdec_w4_gemm(const fdec_bf16* x, const fdec_w4* W, const float* out_scale, const fdec_bf16* residual,
+                          int32_t M, fdec_bf16* y, fdec_stream stream) {
+    const int st = check_prefill_gemm(x, W, out_scale, residual, M, y);
+    if (st != FDEC_OK) return st;
+    if (g_fail_launches.load()) return injected();
+    return hip_status(launch_w4_gemm(x, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale, residual, y,
+                                     static_cast<hipStream_t>(stream)),
+                      "gemm launch");
+}
+
+FDEC_API int fdec_swiglu(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, int32_t M, int32_t K,
+                         fdec_bf16* act, fdec_stream stream) {
+    if (M < 0 || K <= 0 || K % 8) return fail(FDEC_ERR_SHAPE, "M = %d, K = %d: M >= 0, K a positive multiple of 8", M, K);
+    if (M == 0) return ok();
+    if (!g || !u || !act) return fail(FDEC_ERR_NULL, "g, u and act are required");
+    if (ldgu < K || ldgu % 8) return fail(FDEC_ERR_SHAPE, "ld = %lld must be >= K and a multiple of 8", (long long)ldgu);
+    if (!aligned16(g) || !aligned16(u) || !aligned16(act)) return fail(FDEC_ERR_ALIGN, "every tensor must be 16-byte aligned");
+    const size_t in_bytes = (size_t(M - 1) * ldgu + K) * 2;
+    const Span A{act, size_t(M) * K * 2};
+    if (overlap(A, {g, in_bytes}) || overlap(A, {u, in_bytes})) return fail(FDEC_ERR_ALIAS, "act overlaps g or u");
+    if (g_fail_launches.load()) return injected();
+    return hip_status(launch_swiglu_act(g, u, ldgu, M, K, act, static_cast<hipStream_t>(stream)), "swiglu launch");
+}
+
+FDEC_API size_t fdec_swiglu_w4_gemm_workspace_bytes(int32_t M, int32_t K) {
+    if (M < 1 || K <= 0 || K % 128) return 0;
+    return size_t(M) * K * 2;
+}
+
+FDEC_API int fdec_swiglu_w4_gemm(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_w4* W,
+                                 const float* out_scale, const fdec_bf16* residual, int32_t M, fdec_bf16* y,
+                                 void* ws, size_t ws_bytes, fdec_stream stream) {
+    if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
+    int st = check_prefill_gemm(g, W, out_scale, residual, M, y);
+    if (st != FDEC_OK) return st;
+    if (!u) return fail(FDEC_ERR_NULL, "u is required");
+    if (ldgu < W->K || ldgu % 8) return fail(FDEC_ERR_SHAPE, "ld = %lld must be >= K and a multiple of 8", (long long)ldgu);
+    if (!aligned16(u)) return fail(FDEC_ERR_ALIGN, "u must be 16-byte aligned");
+    const size_t need = size_t(M) * W->K * 2;
+    if (ws_bytes < need) return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);
+    if (!ws) return fail(FDEC_ERR_NULL, "workspace is NULL");
+    if (!aligned16(ws)) return fail(FDEC_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t in_bytes = (size_t(M - 1) * ldgu + W->K) * 2;
+    const Span WS{ws, need};
+    const Span others[] = {{g, in_bytes}, {u, in_bytes}, w4_qspan(W), w4_sspan(W), {out_scale, 4},
+                           {residual, size_t(M) * W->N * 2}, {y, size_t(M) * W->N * 2}};
+    for (const Span& o : others)
+        if (overlap(WS, o)) return fail(FDEC_ERR_ALIAS, "the workspace overlaps an input or y");
+    if (overlap({y, size_t(M) * W->N * 2}, {u, in_bytes})) return fail(FDEC_ERR_ALIAS, "y overlaps u");
+    if (g_fail_launches.load()) return injected();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint16_t* act = static_cast<uint16_t*>(ws);
+    hipError_t e = launch_swiglu_act(g, u, ldgu, M, W->K, act, s);
+    if (e == hipSuccess)
+        e = launch_w4_gemm(act, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale, residual, y, s);
+    return hip_status(e, "swiglu gemm launch");
+}
+
 FDEC_API size_t fdec_fp4_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
     if (M < 1 || M > kMaxGemvRows || K <= 0 || K % 32 || N <= 0 || N % 8) return 0;
     return fp4_gemv_workspace_bytes(M, K, N);

@@ -147,6 +147,13 @@ hipError_t launch_eager_rmsnorm(const uint16_t* x, const uint16_t* r, const uint
                                 float eps, int M, int H, uint16_t* h, uint16_t* y,
                                 float* f32a, float* f32b, float* rowbuf, hipStream_t s);
 
+// Prefill-sized GEMM (any M, bf16 activation as stored) and the fused SwiGLU elementwise
+// kernel that precedes it at prefill sizes.
+size_t w4_gemm_lds_bytes();
+hipError_t launch_w4_gemm(const uint16_t* x, int64_t lda, const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
+                          const float* out_scale, const uint16_t* residual, uint16_t* y, hipStream_t s);
+hipError_t launch_swiglu_act(const uint16_t* g, const uint16_t* u, int64_t ldgu, int M, int K, uint16_t* act,
+                             hipStream_t s);
 // measurement probes
 hipError_t launch_empty(int wgs, int threads, hipStream_t s);
 bool read_ceiling_fits(int per_wg, int bcast16, int rows, int piece_bytes);

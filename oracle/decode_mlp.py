@@ -59,6 +59,7 @@ __all__ = [
     "product_buffer_bytes", "unfused_act_gemv", "unfused_product_gemv",
     "add_rmsnorm_eager",
     "add_rmsnorm_gemv_swiglu", "w4_gemv_swiglu", "mlp_decode2", "mlp_chain2",
+    "swiglu_act", "w4_gemm", "swiglu_w4_gemm",
     "FP4_BLOCK", "e2m1_decode", "e4m3_decode", "fp4_unpack", "fp4_dequant", "swiglu_fp4_gemv", "fp4_gemv",
 ]
 
@@ -328,6 +329,28 @@ def mlp_chain2(x0, r0, layers, *, keep=False, y_rounded=False):
             trace.append(d)
         x, r = d["out"], d["h"]
     return (x, r, trace) if keep else (x, r)
+
+
+# ----------------------------------------------------------------------------
+# prefill sizes ([P5]: at 2,048 tokens the MLP half is compute-bound and the fusion win
+# shrinks): the activation is formed once, rounded to bf16, then multiplied
+# ----------------------------------------------------------------------------
+def swiglu_act(g, u):
+    """act = bf16(silu(g) * u): the fused SwiGLU elementwise pass ([P5] Step 1), one rounding."""
+    return f64_to_bf16(silu_mul(bf16_to_f64(g), bf16_to_f64(u)))
+
+
+def w4_gemm(x, qweight, scales, out_scale=None, residual=None, *, return_f64=False):
+    """y = bf16([out_scale *] x @ dequant(W) (+ residual)) for any number of rows."""
+    acc = _chunked_gemv(bf16_to_f64(x), qweight, scales)
+    y = _epilogue(acc, out_scale, residual)
+    return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)
+
+
+def swiglu_w4_gemm(g, u, qweight, scales, out_scale=1.0, residual=None, *, return_f64=False):
+    """The prefill path: y = bf16(out_scale * bf16(silu(g) * u) @ dequant(W) (+ residual)),
+    the activation rounded once where the elementwise pass writes it."""
+    return w4_gemm(swiglu_act(g, u), qweight, scales, out_scale, residual, return_f64=return_f64)
 
 
 # ----------------------------------------------------------------------------

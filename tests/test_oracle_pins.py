@@ -220,3 +220,34 @@ def test_w4_gemv_swiglu_matches_brute_force(M, K, I):
     gu_r = O.w4_gemv(inp.g, inp.W.qweight, inp.W.scales)
     act_r = O.f64_to_bf16(O.silu_mul(O.bf16_to_f64(gu_r[:, :I]), O.bf16_to_f64(gu_r[:, I:])))
     assert not np.array_equal(act, act_r)
+
+
+# ----------------------------------------------------------------------------
+# the prefill path: the SwiGLU pass (one rounding) and the GEMM
+# ----------------------------------------------------------------------------
+def test_swiglu_act_is_one_rounding_of_the_exact_value():
+    from test_oracle import f64_to_bf16_bits_bitwise
+    inp = synth.swiglu_gemv_inputs(3, 256, 8, seed=41)
+    act = O.swiglu_act(inp.g, inp.u)
+    g, u = bf16_by_torch(inp.g), bf16_by_torch(inp.u)
+    for m in range(3):
+        for k in range(256):
+            v = g[m, k] / (1.0 + math.exp(-g[m, k])) * u[m, k]
+            if v != 0.0 and abs(v) >= 2.0 ** -126:
+                assert int(act[m, k]) == f64_to_bf16_bits_bitwise(v), (m, k)
+
+
+@pytest.mark.parametrize("M,K,N", [(3, 128, 8), (5, 256, 24)])
+def test_w4_gemm_matches_brute_force(M, K, N):
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=M + K + N, with_residual=True)
+    _, f = O.w4_gemm(inp.g, inp.W.qweight, inp.W.scales, 0.75, inp.residual, return_f64=True)
+    x = bf16_by_torch(inp.g)
+    want = np.stack([brute_column(x, inp.W.qweight, inp.W.scales, n) for n in range(N)], axis=1) * 0.75 \
+        + bf16_by_torch(inp.residual)
+    assert np.max(np.abs(f - want)) <= 1e-12 * np.max(np.abs(want))
+    # the prefill path rounds the activation where the SwiGLU pass writes it
+    _, p = O.swiglu_w4_gemm(inp.g, inp.u, inp.W.qweight, inp.W.scales, 0.75, inp.residual, return_f64=True)
+    act = bf16_by_torch(O.swiglu_act(inp.g, inp.u))
+    want2 = np.stack([brute_column(act, inp.W.qweight, inp.W.scales, n) for n in range(N)], axis=1) * 0.75 \
+        + bf16_by_torch(inp.residual)
+    assert np.max(np.abs(p - want2)) <= 1e-12 * np.max(np.abs(want2))
