@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/call + achieved HBM GB/s (% of peak), SwiGLU→W4 GEMV M=1 K=9216 N=2560"
 PEAK_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak
 WORKLOAD = "swiglu_w4_gemv_1x9216x2560"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_w4_gemv_1x9216x2560.json")
 CALIB_FLOATS = 1 << 27          # calibration copy: 512 MiB read, 512 MiB written per launch (beyond every cache)
@@ -287,7 +288,7 @@ def bench_extras(torch, F, synth, n_sets_gemv):
         t = bench_repeat(torch, timer, fns, 5) / len(gsets)
         b = T.swiglu_w4_gemv_bytes(Mb, K, N)
         sweep[f"M{Mb}"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS,
-                           "kernel": "column" if Mb <= 4 else "matrix-core" if Mb <= 16 else
+                           "kernel": "column" if Mb <= 4 else "matrix-core, waves split K" if Mb <= 16 else
                            f"matrix-core, {(Mb + 15) // 16} row blocks"}
         del gb, ub, ys, wsb
     out["batch_sweep_swiglu_w4_gemv_9216x2560"] = sweep
@@ -322,6 +323,32 @@ def bench_extras(torch, F, synth, n_sets_gemv):
         del gb, ub, ys, wsb
     del fsets
 
+    # the prefill point: 2,048 tokens through the SwiGLU pass and the matrix-core GEMM at
+    # the metric's K and N (4 rotating weight sets; the activation is 75 MB per call anyway)
+    log("[bench] prefill 2048x9216x2560")
+    Mp = 2048
+    psets = [F.W4Weight.from_numpy(*(lambda w: (w.qweight, w.scales))(
+        synth.swiglu_gemv_inputs(1, K, N, seed=100 + i).W)) for i in range(4)]
+    gen = torch.Generator().manual_seed(2048)
+    gp = torch.randn(Mp, K, generator=gen).to(torch.bfloat16).cuda()
+    up = torch.randn(Mp, K, generator=gen).to(torch.bfloat16).cuda()
+    actp = torch.empty((Mp, K), dtype=torch.bfloat16, device="cuda")
+    yps = [torch.empty((Mp, N), dtype=torch.bfloat16, device="cuda") for _ in psets]
+    wsp = F.workspace(F.swiglu_w4_gemm_workspace_bytes(Mp, K))
+    t_act = bench_repeat(torch, timer, [lambda: F.swiglu(gp, up, out=actp)], 10)
+    t_gemm = bench_repeat(torch, timer, [lambda W=W, y=y: F.w4_gemm(actp, W, scale, out=y) for W, y in zip(psets, yps)],
+                          5) / len(psets)
+    t_all = bench_repeat(torch, timer, [lambda W=W, y=y: F.swiglu_w4_gemm(gp, up, W, scale, out=y, ws=wsp)
+                                        for W, y in zip(psets, yps)], 5) / len(psets)
+    flops = 2.0 * Mp * K * N
+    out["prefill_swiglu_w4_gemm_2048x9216x2560"] = {
+        "us_per_call": t_all * 1e6, "swiglu_pass_us": t_act * 1e6, "gemm_us": t_gemm * 1e6,
+        "swiglu_pass_gbps": 3 * Mp * K * 2 / t_act / 1e9,
+        "gemm_roofline": {"bound": "mfma", "achieved": flops / t_gemm / 1e12, "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": flops / t_gemm / 1e12 / PEAK_BF16_TFLOPS},
+        "kernels": 2}
+    del psets, gp, up, actp, yps, wsp
+
     # Llama-3-8B-sized MLP layer at M=16, 6 rotating weight sets
     c = synth.CONFIGS["mlp_llama3_8b_m16"]
     M, H, I = c["M"], c["H"], c["I"]
@@ -343,7 +370,24 @@ def bench_extras(torch, F, synth, n_sets_gemv):
     wsu = F.workspace(F.unfused_mlp_workspace_bytes(M, H, I))
     t = bench_repeat(torch, timer, [lambda L=L: F.unfused_mlp_decode(L, bufs, wsu) for L in layers[:2]], 3) / 2
     out["unfused_mlp_llama3_8b_m16"] = {"us_per_call": t * 1e6}
-    del layers, bufs, wsm, wsu
+    # the same layer with SwiGLU as the gate_up epilogue (norm; gate_up + SwiGLU writing act
+    # [16, I]; down with the residual), and its gate_up kernel alone
+    b2 = F.Mlp2Buffers.empty(M, H, I)
+    b2.x.copy_(bufs.x)
+    b2.residual.copy_(bufs.residual)
+    ws2 = F.workspace(F.mlp2_workspace_bytes(M, H, I))
+    t = bench_repeat(torch, timer, [lambda L=L: F.mlp_decode2(L, b2, ws2) for L in layers], 5) / len(layers)
+    b = T.mlp2_layer_bytes(M, H, I, True)
+    out["mlp2_llama3_8b_m16"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS,
+                                 "bytes_per_call": b, "kernels": 3}
+    yb = torch.empty((M, H), dtype=torch.bfloat16, device="cuda").normal_()
+    wsp = F.workspace(F.w4_gemv_swiglu_workspace_bytes(M, H, I))
+    t = bench_repeat(torch, timer, [lambda L=L: F.w4_gemv_swiglu(yb, L.gate_up, out=b2.act, ws=wsp)
+                                    for L in layers], 5) / len(layers)
+    b = T.w4_gemv_swiglu_bytes(M, H, I)
+    out["w4_gemv_swiglu_16x4096x14336"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9,
+                                            "frac_of_peak": b / t / 1e9 / PEAK_GBPS, "bytes_per_call": b}
+    del layers, bufs, wsm, wsu, b2, ws2, yb, wsp
 
     # Qwen2.5-1.5B-sized MLP chain, 28 layers: eager chain vs one hipGraph
     c = synth.CONFIGS["mlp_qwen2_5_1_5b_28l"]

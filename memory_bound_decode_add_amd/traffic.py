@@ -79,10 +79,23 @@ def mlp_layer_bytes(M: int, H: int, I: int, residual_in_epilogue: bool) -> int:
             + swiglu_w4_gemv_bytes(M, I, H, residual=residual_in_epilogue))
 
 
+def w4_gemv_swiglu_bytes(M: int, K: int, I: int) -> int:
+    """The gate_up projection with the SwiGLU epilogue: x in, gate_up weights [K, 2I],
+    act [M, I] out (the gate/up pair is never written)."""
+    return w4_weight_bytes(K, 2 * I) + M * K * BF16 + M * I * BF16
+
+
 def mlp2_layer_bytes(M: int, H: int, I: int, residual_in_epilogue: bool) -> int:
-    """The two-kernel layer.  Kernel 1: x, residual and the norm weight in, gate_up
+    """The layer with SwiGLU as the gate_up epilogue.
+
+    Up to 4 rows, two kernels.  Kernel 1: x, residual and the norm weight in, gate_up
     weights, h and act out.  Kernel 2: act in, down weights, out out (+ h in for the
-    residual add), the fp32 scalar, and the residual update (h in, residual out)."""
+    residual add), the fp32 scalar, and the residual update (h in, residual out).
+    From 5 rows, three kernels: add_rmsnorm; the gate_up GEMV with the SwiGLU epilogue;
+    the down GEMV on act (+ the residual, which the norm updated in place)."""
+    if M > 4:
+        down = w4_gemv_bytes(M, I, H, out_scale=True) + (M * H * BF16 if residual_in_epilogue else 0)
+        return add_rmsnorm_bytes(M, H) + w4_gemv_swiglu_bytes(M, H, I) + down
     k1 = 2 * M * H * BF16 + H * BF16 + w4_weight_bytes(H, 2 * I) + M * H * BF16 + M * I * BF16
     k2 = M * I * BF16 + w4_weight_bytes(I, H) + M * H * BF16 + F32 + 2 * M * H * BF16
     if residual_in_epilogue:

@@ -302,3 +302,44 @@ def test_kmfma_kernel_every_variant(pro, tiles, gw):
         F.set_mfma_plan(0)
     say("  worst err/bound", assert_close(y, ref, "y"))
     assert_bits_equal(y, y2, "repeat")
+
+
+# ---------------------------------------------------------------------------
+# outputs that should be exactly zero: the kernels keep a known offset in every decoded
+# weight (1032 + q or 1152 + 16 q in fp16) and remove it once per chunk or group, so a
+# zero weight column leaves the rounding of those offset sums.  The offsets are summed
+# from the same fp16 activation values the dot uses, so what is left is bounded by fp32
+# rounding of sums of about 1152 * |a| per k: below 2^-10 of sum_k |act| * scale.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N,split", [(1, 9216, 2560, 0), (3, 4096, 520, 0), (8, 9216, 2560, 0),
+                                         (16, 14336, 4096, 0), (32, 2048, 776, 0), (1, 4096, 520, 4)])
+def test_zero_weight_columns_give_zero(M, K, N, split):
+    say(f"[zero columns] M={M} K={K} N={N} forced split={split}")
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=M + K + N, out_scale=1.0, with_residual=True)
+    q = O.w4_unpack(inp.W.qweight).astype(np.int64)
+    zero_cols = np.arange(0, N, 7)
+    q[:, zero_cols] = 0
+    qw = synth.pack_int4(q)
+    W = F.W4Weight.from_numpy(qw, inp.W.scales)
+    g, u, res = F.from_bits(inp.g), F.from_bits(inp.u), F.from_bits(inp.residual)
+    if split:
+        F.set_gemv_split(split)
+    try:
+        ws = F.workspace(F.gemv_workspace_bytes(M, K, N))
+        y = F.to_bits(F.swiglu_w4_gemv(g, u, W, F.scalar(1.0), None, ws=ws))
+        yr = F.to_bits(F.swiglu_w4_gemv(g, u, W, F.scalar(1.0), res, ws=ws))
+    finally:
+        F.set_gemv_split(0)
+    act = np.abs(O.silu_mul(O.bf16_to_f64(inp.g), O.bf16_to_f64(inp.u)))
+    smax = O.bf16_to_f64(inp.W.scales).max()
+    bound = 2.0 ** -10 * act.sum(axis=1, keepdims=True) * smax           # per row
+    z = O.bf16_to_f64(y)[:, zero_cols]
+    assert np.all(np.abs(z) <= bound), f"worst |y| / bound = {np.max(np.abs(z) / bound):.3f}"
+    say(f"  largest |y| on a zero column: {np.abs(z).max():.3e} (bound {bound.min():.3e} .. {bound.max():.3e})")
+    # with the residual in the epilogue, y is the residual to within that bound plus one rounding
+    r = O.bf16_to_f64(inp.residual)[:, zero_cols]
+    zr = O.bf16_to_f64(yr)[:, zero_cols]
+    assert np.all(np.abs(zr - r) <= bound + np.abs(r) * 2.0 ** -8)
+    # the other columns are unaffected
+    ref = O.swiglu_w4_gemv(inp.g, inp.u, qw, inp.W.scales, 1.0)
+    assert_close(y, ref, "y")

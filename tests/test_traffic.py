@@ -71,3 +71,11 @@ def test_fp4_gemv_bytes():
     assert T.fp4_weight_bytes(9216, 2560) == 11_796_480 + 1_474_560
     assert T.swiglu_fp4_gemv_bytes(1, 9216, 2560) == 11_796_480 + 1_474_560 + 36_864 + 5_120 + 4
     assert T.swiglu_fp4_gemv_bytes(1, 9216, 2560) - T.swiglu_w4_gemv_bytes(1, 9216, 2560) == 1_474_560 - 368_640
+
+
+def test_swiglu_epilogue_layer_bytes():
+    # the form with SwiGLU as the gate_up epilogue writes act [M, I] where the three-kernel
+    # form writes the gate/up pair [M, 2I] and reads it back: 2 * M * I * 2 bytes fewer
+    M, H, I = 16, 4096, 14336
+    assert T.mlp_layer_bytes(M, H, I, True) - T.mlp2_layer_bytes(M, H, I, True) == 2 * M * I * 2
+    assert T.w4_gemv_swiglu_bytes(M, H, I) == H * 2 * I // 2 + (H // 128) * 2 * I * 2 + M * H * 2 + M * I * 2
