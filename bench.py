@@ -528,11 +528,17 @@ def cpu_baseline(synth, seconds):
 
 
 def profile_calls(torch, F, synth):
-    """A few eager calls of each GEMV kernel family, for hardware-counter runs: the column
-    kernel at the metric's shape, the matrix-core kernel on the Llama-3-8B-sized M=16
-    projections (gate_up identity, down SwiGLU with its finish kernel), and the FP4 kernels."""
+    """A few eager calls of each kernel family, for hardware-counter runs:
+    - the column kernel at the metric's shape (M=1, K=9216, N=2560, SwiGLU);
+    - the matrix-core kernels at 16 rows: the kernel whose waves split K (K=9216, N=2560,
+      SwiGLU) and the row-block kernel on the Llama-3-8B-sized projections (gate_up
+      K=4096, N=28672, identity; down K=14336, N=4096, SwiGLU, with its finish kernel);
+    - the gate_up projection with the SwiGLU epilogue (M=16, K=4096, I=14336, pair mode);
+    - the FP4 kernels at M=1 and 16 (K=9216, N=2560);
+    - the prefill point: the SwiGLU pass and the W4 GEMM at 2048 x 9216 x 2560."""
     sc = F.scalar(0.5)
-    for M, K, N, pro, n in ((1, 9216, 2560, "swiglu", 24), (16, 4096, 28672, "id", 4), (16, 14336, 4096, "swiglu", 4)):
+    for M, K, N, pro, n in ((1, 9216, 2560, "swiglu", 24), (16, 9216, 2560, "swiglu", 24),
+                            (16, 4096, 28672, "id", 4), (16, 14336, 4096, "swiglu", 4)):
         sets = []
         for i in range(n):
             inp = synth.swiglu_gemv_inputs(M, K, N, seed=i)
@@ -547,6 +553,18 @@ def profile_calls(torch, F, synth):
                     F.w4_gemv(g, W, sc, out=y, ws=ws)
         torch.cuda.synchronize()
         del sets, ws
+    M, K, I = 16, 4096, 14336
+    sets = []
+    for i in range(4):
+        inp = synth.swiglu_gemv_inputs(M, K, 2 * I, seed=i)
+        sets.append((F.from_bits(inp.g), F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales),
+                     torch.empty((M, I), dtype=torch.bfloat16, device="cuda")))
+    ws = F.workspace(F.w4_gemv_swiglu_workspace_bytes(M, K, I))
+    for _ in range(2):
+        for x, W, act in sets:
+            F.w4_gemv_swiglu(x, W, out=act, ws=ws)
+    torch.cuda.synchronize()
+    del sets, ws
     for M in (1, 16):
         inp = synth.swiglu_fp4_gemv_inputs(M, 9216, 2560, seed=M)
         g, u = F.from_bits(inp.g), F.from_bits(inp.u)
@@ -555,6 +573,17 @@ def profile_calls(torch, F, synth):
         ws = F.workspace(F.fp4_gemv_workspace_bytes(M, 9216, 2560))
         for _ in range(8):
             F.swiglu_fp4_gemv(g, u, W, sc, out=y, ws=ws)
+    torch.cuda.synchronize()
+    M, K, N = 2048, 9216, 2560
+    inp = synth.swiglu_gemv_inputs(1, K, N, seed=0)
+    W = F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales)
+    gen = torch.Generator().manual_seed(2048)
+    g = torch.randn(M, K, generator=gen).to(torch.bfloat16).cuda()
+    u = torch.randn(M, K, generator=gen).to(torch.bfloat16).cuda()
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = F.workspace(F.swiglu_w4_gemm_workspace_bytes(M, K))
+    for _ in range(4):
+        F.swiglu_w4_gemm(g, u, W, F.scalar(1.0), out=y, ws=ws)
     torch.cuda.synchronize()
     log("[bench] profile calls done")
 

@@ -10,29 +10,38 @@
 //                                               per element, as the fused SwiGLU of Step 1)
 //     y   = bf16(s * act @ dequant(W) (+ res)) (this GEMM; act is used as stored)
 //
-// GEMM tiling.  A workgroup of 8 waves (two per SIMD) computes a 128-row x 160-column tile of y (at
-// M = 2048, N = 2560: 16 x 16 = 256 workgroups, one per CU), looping over K one 128-wide
-// group at a time with two LDS buffers: while the matrix cores work on group g, the
-// global loads of group g + 1 are in flight, and their values are then written to the
-// other buffer.  Per group the workgroup stages
-//   - the 128 x 128 bf16 activation block, each 8-value block stored in the int4 pair
-//     order (e0, e4, e1, e5, e2, e6, e3, e7) -- four byte permutes per 16 bytes;
-//   - the 160 x 128 weights, each packed word decoded once into eight exact bf16 values
-//     136 + q in pair order: a 4-bit field of offset-binary q + 8 in the mantissa of bf16
-//     128 (0x4300), field j of the word shifted to bits 0..3 and 16..19 (three shifts and
-//     four v_bitop3_b32 per word);
-//   - the group's 160 column scales.
+// GEMM tiling.  A workgroup of 8 waves (two per SIMD) computes a 128-row x 160-column
+// tile of y (at M = 2048, N = 2560: 16 x 16 = 256 workgroups, one per CU), looping over K
+// one 128-wide group at a time.  Each group's raw bytes -- the 128 x 128 bf16 activation
+// block in k order, the 160 columns' packed words and their 160 scales -- go straight from
+// global memory into one of three LDS slots with global_load_lds_dwordx4 (a lane's 16
+// bytes land at the wave load's slot address plus 16 x lane).  No register holds them in
+// flight, and the loads of groups g + 1 and g + 2 stay outstanding while group g is
+// multiplied.  Rows and columns are padded by one 16-byte chunk (lanes that land on a pad
+// re-read a chunk of their row), which keeps the operand reads free of bank conflicts.
+// Per group, after one barrier, a wave reads all its operands from the slot in one batch
+// and issues the loads of group g + 2 into the slot every wave has finished with.
 // Wave (wr, wc), wr = 0..3, wc = 0..1, owns rows 32 wr .. 32 wr + 31 (2 row tiles of 16)
-// and columns 80 wc .. 80 wc + 79 (5 column tiles); per group and k-step it reads its 2
-// activation and 5 weight operands from LDS and issues 10 v_mfma_f32_16x16x32_bf16, plus one MFMA per
-// row tile with a constant -136 operand that removes the weights' offset (shared by the
-// 5 column tiles).  The group's fp32 sums are scaled by the group scale once and added to
-// the running tile (fp32).  The epilogue applies the output scale and residual and rounds
-// to bf16 once.  The MFMA operand layout is that of the GEMV kernels: lane l supplies
-// A[l%16][8(l/16)+e] (weights, row = column n), B[8(l/16)+e][l%16] (activation, column =
-// row m), and holds D[4(l/16)+r][l%16].  Two waves per SIMD (210 VGPRs each) hide each
-// other's LDS latency: at 2048 x 9216 x 2560 this runs 12 % faster than 4 waves with
-// 64 x 80 wave tiles (one wave per SIMD, 384 VGPRs), although it reads more from LDS.
+// and columns 80 wc .. 80 wc + 79 (5 column tiles).  Per group and k-step it
+//   - permutes its 2 activation operands to the int4 pair order (e0, e4, e1, e5, e2, e6,
+//     e3, e7): four byte permutes per 16 bytes;
+//   - decodes its 5 weight words into eight exact bf16 values 136 + q each, in pair order:
+//     a 4-bit field of offset-binary q + 8 in the mantissa of bf16 128 (0x4300), field j
+//     of the word shifted to bits 0..3 and 16..19 (three shifts and four v_bitop3_b32 per
+//     word);
+//   - issues 10 v_mfma_f32_16x16x32_bf16.
+// The offset is removed inside the matrix cores: per row tile, a chain of four MFMAs with
+// a constant -136 operand forms -136 * sum_k act, which starts each product chain of the
+// group.  The group's fp32 sums are scaled by the group scale once and added to the
+// running tile (fp32); the epilogue applies the output scale and residual and rounds to
+// bf16 once.  The MFMA k-slots are permuted so that lane (lm, ls) takes word 4 ls + ks of
+// its column in k-step ks (one 16-byte chunk per column and group) against activation
+// k = 32 ls + 8 ks .. + 7.  The operand layout is that of the GEMV kernels: lane l
+// supplies A[l%16][8(l/16)+e] (weights, row = column n), B[8(l/16)+e][l%16] (activation,
+// column = row m), and holds D[4(l/16)+r][l%16].
+// Measured at 2048 x 9216 x 2560: 147-151 us.  The same tiling staged through registers
+// (one group ahead, decoded once per workgroup into LDS) took 162 us, and with 4 waves of
+// 64 x 80 (one per SIMD) 184 us; this ring with 4 waves of 64 x 80 took 154 us.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -47,13 +56,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kGBM = 128;               // rows per workgroup
 constexpr int kGBN = 160;               // columns per workgroup
 constexpr int kGThreads = 512;          // 8 waves, 4 x 2, two per SIMD
-constexpr int kGRowTiles = 2;           // per wave (32 rows)
+constexpr int kRT = 2;                  // row tiles of 16 per wave (32 rows)
 constexpr int kGColTiles = 5;           // per wave (80 columns)
-constexpr int kGActChunks = kGBM * 16 / kGThreads;                     // 16-byte pieces per thread: 4
-constexpr int kGWChunks = (kGBN * 4 + kGThreads - 1) / kGThreads;      // 16-byte weight chunks: 2
-constexpr int kGStride = 128 + 8;       // LDS row stride of a staged block, in bf16
-constexpr size_t kGBufBytes = size_t(kGBM + kGBN) * kGStride * 2 + size_t(kGBN) * 4;
-constexpr size_t kGLdsBytes = 2 * kGBufBytes;
 
 struct GemmArgs {
     const uint16_t* x;      // bf16 [M][lda]
@@ -85,121 +89,187 @@ __device__ __forceinline__ uint4 to_pair_order(uint4 v) {
                       __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));  // e3 = y.hi, e7 = w.hi
 }
 
-__global__ __launch_bounds__(kGThreads) void w4_gemm_kernel(GemmArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+constexpr int kRActCPR = 17;                          // 16-byte chunks per padded activation row
+constexpr int kRActLoads = kGBM * kRActCPR / 64;      // wave loads of a slot's activation: 34
+constexpr int kRWCPC = 5;                             // 16-byte chunks per padded weight column
+constexpr int kRWLoads = (kGBN * kRWCPC + 63) / 64;   // 13 (the last one partly past the 800 chunks)
+constexpr int kRActBytes = kRActLoads * 1024;
+constexpr int kRWBytes = kRWLoads * 1024;
+constexpr int kRSlotBytes = kRActBytes + kRWBytes + 1024;          // + the scales' wave load
+constexpr int kRSlots = 3;
+constexpr size_t kRLdsBytes = size_t(kRSlots) * kRSlotBytes;
+constexpr int kRLoads = kRActLoads + kRWLoads + 1;    // 48 wave loads per group ...
+constexpr int kRLoadsPerWave = kRLoads / 8;           // ... six per wave
+static_assert(kRLoads % 8 == 0 && kGBM * kRActCPR % 64 == 0, "every wave issues the same loads per group");
+static_assert(kRLdsBytes <= 160 * 1024, "three slots fit LDS");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding: vmcnt in bits 3..0
+// and 15..14, expcnt 6..4 and lgkmcnt 11..8 left at their maxima)
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// The wave loads of a group: wave load q = wave + 8 j; q < 34 the activation, then 13
+// of weights, then the scales; lane l covers chunk 64 q' + l of its region (addresses
+// clamped inside the tensors; what lands on a pad or past the 160 columns is never read).
+// A lane's byte offset from its region's base is the same for every group, so it is
+// computed once; the bases are workgroup-uniform and advance by one group per step.
+struct RingLoads {
+    static constexpr int kPerWave = kRLoadsPerWave;
+    uint32_t off[kPerWave];      // the lane's byte offset from its region's base, per load
+    __device__ __forceinline__ RingLoads(const GemmArgs& a, int m0, int n0, int wave, int lane) {
+#pragma unroll
+        for (int j = 0; j < kPerWave; ++j) {
+            const int q = wave + 8 * j;
+            if (q < kRActLoads) {
+                const int p = 64 * q + lane, r = p / kRActCPR, c = min(p % kRActCPR, 15);
+                off[j] = uint32_t((min(m0 + r, a.M - 1) - m0) * uint32_t(a.lda) * 2u + uint32_t(c) * 16u);
+            } else if (q < kRActLoads + kRWLoads) {
+                const int p = 64 * (q - kRActLoads) + lane;
+                const int col = min(p / kRWCPC, kGBN - 1), c = min(p % kRWCPC, 3);
+                off[j] = uint32_t((min(n0 + col, a.N - 1) - n0) * uint32_t(a.nch) * 16u + uint32_t(c) * 16u);
+            } else {
+                off[j] = uint32_t((min(n0 + 8 * min(lane, kGBN / 8 - 1), a.N - 8) - n0) * 2);
+            }
+        }
+    }
+    __device__ __forceinline__ void issue(const GemmArgs& a, unsigned char* dst_slot, int g, int m0, int n0,
+                                          int wave) const {
+        const char* xb = reinterpret_cast<const char*>(a.x + size_t(m0) * a.lda) + size_t(g) * 256;
+        const char* wb = reinterpret_cast<const char*>(a.qw + size_t(n0) * a.nch) + size_t(g) * 64;
+        const char* sb = reinterpret_cast<const char*>(a.sc + size_t(g) * a.N + n0);
+#pragma unroll
+        for (int j = 0; j < kPerWave; ++j) {
+            const int q = wave + 8 * j;
+            const char* base;
+            unsigned char* dst;
+            if (q < kRActLoads) {
+                base = xb;
+                dst = dst_slot + q * 1024;
+            } else if (q < kRActLoads + kRWLoads) {
+                base = wb;
+                dst = dst_slot + kRActBytes + (q - kRActLoads) * 1024;
+            } else {
+                base = sb;
+                dst = dst_slot + kRActBytes + kRWBytes;
+            }
+            __builtin_amdgcn_global_load_lds(base + off[j], (lds_void_t*)dst, 16, 0, 0);
+        }
+    }
+};
+
+// One step of the ring: the loads of group g_next (if >= 0) into nxt, then the products of
+// the group in cur.  cur and nxt are distinct slots; declaring them restrict lets the
+// compiler see that the reads of cur need not wait for the loads into nxt.
+__device__ __forceinline__ void ring_step(const GemmArgs& a, const RingLoads& ld,
+                                          const unsigned char* __restrict__ cur, unsigned char* __restrict__ nxt,
+                                          int g_next, int m0, int n0, int wave, int lane,
+                                          f32x4_t (&out)[kRT][kGColTiles]) {
     const int ls = lane >> 4, lm = lane & 15;
     const int wr = wave >> 1, wc = wave & 1;
-    // workgroups of one row block are consecutive on an XCD (they share its activation)
+    // MFMA k-slot order: lane (lm, ls) takes word 4 ls + ks of its column in k-step ks, so
+    // its four weight words are one 16-byte chunk and its activation operands are the 32
+    // consecutive values from k = 32 ls
+    const uint16_t* as = reinterpret_cast<const uint16_t*>(cur) + (16 * kRT * wr + lm) * (kRActCPR * 8) + 32 * ls;
+    const uint4* wsp = reinterpret_cast<const uint4*>(cur + kRActBytes) + (80 * wc + lm) * kRWCPC + ls;
+    const uint16_t* ssp = reinterpret_cast<const uint16_t*>(cur + kRActBytes + kRWBytes) + 80 * wc + 4 * ls;
+    // every LDS read of the group in one batch, then the next loads, then the arithmetic
+    uint4 wq[kGColTiles], araw[4][kRT];
+    uint2 sq[kGColTiles];
+#pragma unroll
+    for (int c = 0; c < kGColTiles; ++c) wq[c] = wsp[c * 16 * kRWCPC];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int r = 0; r < kRT; ++r) araw[ks][r] = *reinterpret_cast<const uint4*>(as + r * 16 * (kRActCPR * 8) + 8 * ks);
+#pragma unroll
+    for (int c = 0; c < kGColTiles; ++c) sq[c] = *reinterpret_cast<const uint2*>(ssp + 16 * c);
+    if (g_next >= 0) ld.issue(a, nxt, g_next, m0, n0, wave);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const uint32_t m136 = 0xC308C308u;                  // bf16 -136 in each half
+    const bf16x8_t negoff = __builtin_bit_cast(bf16x8_t, make_uint4(m136, m136, m136, m136));
+    // the offset sums -136 * sum_k act (one chain per row tile) start the products' chains:
+    // no separate add per output element
+    bf16x8_t bop[4][kRT];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int r = 0; r < kRT; ++r) bop[ks][r] = __builtin_bit_cast(bf16x8_t, to_pair_order(araw[ks][r]));
+    f32x4_t bias[kRT];
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) {
+        bias[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            bias[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(negoff, bop[ks][r], bias[r], 0, 0, 0);
+    }
+    f32x4_t d[kRT][kGColTiles];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int c = 0; c < kGColTiles; ++c) {
+            const uint32_t w = ks == 0 ? wq[c].x : ks == 1 ? wq[c].y : ks == 2 ? wq[c].z : wq[c].w;
+            const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, decode_bf16x8_biased(w, a.dm.lo));
+#pragma unroll
+            for (int r = 0; r < kRT; ++r)
+                d[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[ks][r], ks == 0 ? bias[r] : d[r][c], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < kGColTiles; ++c) {
+        const float s0 = bf16_lo(sq[c].x), s1 = bf16_hi(sq[c].x), s2 = bf16_lo(sq[c].y), s3 = bf16_hi(sq[c].y);
+#pragma unroll
+        for (int r = 0; r < kRT; ++r) {
+            out[r][c][0] = fmaf(s0, d[r][c][0], out[r][c][0]);
+            out[r][c][1] = fmaf(s1, d[r][c][1], out[r][c][1]);
+            out[r][c][2] = fmaf(s2, d[r][c][2], out[r][c][2]);
+            out[r][c][3] = fmaf(s3, d[r][c][3], out[r][c][3]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kGThreads) void w4_gemm_kernel(GemmArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    // the wave index as a scalar, so that everything derived from it (which loads a wave
+    // issues, where they land) is computed once per wave
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int ls = lane >> 4, lm = lane & 15;
+    const int wr = wave >> 1, wc = wave & 1;
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
     const int nt = lb % a.ntiles, mt = lb / a.ntiles;
     const int m0 = mt * kGBM, n0 = nt * kGBN;
 
-    auto act_s = [&](int b) { return reinterpret_cast<uint16_t*>(smem + b * kGBufBytes); };
-    auto w_s = [&](int b) { return act_s(b) + kGBM * kGStride; };
-    auto sc_s = [&](int b) { return reinterpret_cast<float*>(w_s(b) + kGBN * kGStride); };
-
-    // ---- staging: global loads of group g into registers, then stores into buffer b ----
-    uint4 av[kGActChunks], wv[kGWChunks];
-    uint16_t sv = 0;
-    auto stage_load = [&](int g) {
+    f32x4_t out[kRT][kGColTiles];
 #pragma unroll
-        for (int i = 0; i < kGActChunks; ++i) {
-            const int c = tid + kGThreads * i;                 // 16 chunks of 8 values per row
-            const int row = min(m0 + (c >> 4), a.M - 1);
-            av[i] = *reinterpret_cast<const uint4*>(a.x + size_t(row) * a.lda + g * 128 + (c & 15) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < kGWChunks; ++i) {
-            const int c = min(tid + kGThreads * i, kGBN * 4 - 1);   // 4 chunks of 32 k per column
-            const int n = min(n0 + (c >> 2), a.N - 1);
-            wv[i] = nt_load(a.qw + size_t(n) * a.nch + 4 * g + (c & 3));
-        }
-        if (tid < kGBN) sv = a.sc[size_t(g) * a.N + min(n0 + tid, a.N - 1)];
-    };
-    auto stage_store = [&](int b) {
-        uint16_t* as = act_s(b);
-        uint16_t* ws = w_s(b);
-#pragma unroll
-        for (int i = 0; i < kGActChunks; ++i) {
-            const int c = tid + kGThreads * i;
-            *reinterpret_cast<uint4*>(as + (c >> 4) * kGStride + (c & 15) * 8) = to_pair_order(av[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < kGWChunks; ++i) {
-            const int c = tid + kGThreads * i;
-            if (c < kGBN * 4) {
-                uint16_t* dst = ws + (c >> 2) * kGStride + (c & 3) * 32;
-                const uint32_t wd[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<uint4*>(dst + 8 * j) = decode_bf16x8_biased(wd[j], a.dm.lo);
-            }
-        }
-        if (tid < kGBN) sc_s(b)[tid] = bf16_to_f32(sv);
-    };
-
-    const uint32_t m136 = 0xC308C308u;                  // bf16 -136 in each half
-    const bf16x8_t negoff = __builtin_bit_cast(bf16x8_t, make_uint4(m136, m136, m136, m136));
-    f32x4_t out[kGRowTiles][kGColTiles];
-#pragma unroll
-    for (int r = 0; r < kGRowTiles; ++r)
+    for (int r = 0; r < kRT; ++r)
 #pragma unroll
         for (int c = 0; c < kGColTiles; ++c) out[r][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    stage_load(0);
-    stage_store(0);
-    __syncthreads();
+    const RingLoads ld(a, m0, n0, wave, lane);
+    ld.issue(a, smem, 0, m0, n0, wave);
+    if (a.groups > 1) ld.issue(a, smem + kRSlotBytes, 1, m0, n0, wave);
     for (int g = 0; g < a.groups; ++g) {
-        const int b = g & 1;
-        if (g + 1 < a.groups) stage_load(g + 1);
-        const uint16_t* as = act_s(b) + (16 * kGRowTiles * wr + lm) * kGStride + ls * 8;
-        const uint16_t* ws = w_s(b) + (80 * wc + lm) * kGStride + ls * 8;
-        f32x4_t d[kGRowTiles][kGColTiles], bias[kGRowTiles];
-#pragma unroll
-        for (int r = 0; r < kGRowTiles; ++r) {
-            bias[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < kGColTiles; ++c) d[r][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8_t bop[kGRowTiles], aop[kGColTiles];
-#pragma unroll
-            for (int r = 0; r < kGRowTiles; ++r)
-                bop[r] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(as + r * 16 * kGStride + ks * 32));
-#pragma unroll
-            for (int c = 0; c < kGColTiles; ++c)
-                aop[c] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ws + c * 16 * kGStride + ks * 32));
-#pragma unroll
-            for (int r = 0; r < kGRowTiles; ++r) {
-                bias[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(negoff, bop[r], bias[r], 0, 0, 0);
-#pragma unroll
-                for (int c = 0; c < kGColTiles; ++c)
-                    d[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[c], bop[r], d[r][c], 0, 0, 0);
-            }
-        }
-        const float* ss = sc_s(b) + 80 * wc + 4 * ls;
-#pragma unroll
-        for (int c = 0; c < kGColTiles; ++c) {
-            const float4 s4 = *reinterpret_cast<const float4*>(ss + c * 16);
-#pragma unroll
-            for (int r = 0; r < kGRowTiles; ++r) {
-                out[r][c][0] = fmaf(s4.x, d[r][c][0] + bias[r][0], out[r][c][0]);
-                out[r][c][1] = fmaf(s4.y, d[r][c][1] + bias[r][1], out[r][c][1]);
-                out[r][c][2] = fmaf(s4.z, d[r][c][2] + bias[r][2], out[r][c][2]);
-                out[r][c][3] = fmaf(s4.w, d[r][c][3] + bias[r][3], out[r][c][3]);
-            }
-        }
-        if (g + 1 < a.groups) stage_store(b ^ 1);
-        __syncthreads();
+        // this wave's loads of group g have landed (those of g + 1 may still be in flight);
+        // the barrier makes every wave's visible, and it follows every wave's reads of the
+        // slot that group g + 2 reuses.  A plain s_barrier: a fence here would also wait
+        // for the loads still in flight.  The signal fences (compiler-only, no instruction)
+        // keep the compiler from moving LDS accesses across it.
+        if (g + 1 < a.groups)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRLoadsPerWave));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        ring_step(a, ld, smem + (g % kRSlots) * kRSlotBytes, smem + ((g + 2) % kRSlots) * kRSlotBytes,
+                  g + 2 < a.groups ? g + 2 : -1, m0, n0, wave, lane, out);
     }
 
-    // ---- epilogue: lane holds columns 4 ls .. 4 ls + 3 of row lm of each tile ----
     const float os = a.out_scale ? *a.out_scale : 1.0f;
 #pragma unroll
-    for (int r = 0; r < kGRowTiles; ++r) {
-        const int m = m0 + 16 * kGRowTiles * wr + 16 * r + lm;
+    for (int r = 0; r < kRT; ++r) {
+        const int m = m0 + 16 * kRT * wr + 16 * r + lm;
         if (m >= a.M) continue;
 #pragma unroll
         for (int c = 0; c < kGColTiles; ++c) {
@@ -240,7 +310,7 @@ __global__ __launch_bounds__(256) void swiglu_act_kernel(const uint16_t* __restr
 
 }  // namespace
 
-size_t w4_gemm_lds_bytes() { return kGLdsBytes; }
+size_t w4_gemm_lds_bytes() { return kRLdsBytes; }
 
 hipError_t launch_w4_gemm(const uint16_t* x, int64_t lda, const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                           const float* out_scale, const uint16_t* residual, uint16_t* y, hipStream_t s) {
@@ -261,9 +331,9 @@ hipError_t launch_w4_gemm(const uint16_t* x, int64_t lda, const uint32_t* qw, co
     const int64_t wgs = int64_t((M + kGBM - 1) / kGBM) * a.ntiles;
     if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(w4_gemm_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kGLdsBytes));
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kRLdsBytes));
     if (e != hipSuccess) return e;
-    w4_gemm_kernel<<<dim3(unsigned(wgs)), kGThreads, kGLdsBytes, s>>>(a);
+    w4_gemm_kernel<<<dim3(unsigned(wgs)), kGThreads, kRLdsBytes, s>>>(a);
     return hipGetLastError();
 }
 

@@ -965,7 +965,7 @@ bool plan_mfma(int M, int K, int N, GemvPlan& p) {
     p.gps = (p.groups + S - 1) / S;
     p.splits = (p.groups + p.gps - 1) / p.gps;
     if (p.splits > 1) p.partial_bytes = size_t(p.splits) * p.mr * p.tiles * ncol * 4;
-    p.lds_bytes = size_t(p.mr) * (size_t(p.gps) * 16 + 1) * 16 + size_t(p.mr) * p.gps * 4;
+    p.lds_bytes = size_t(p.mr) * (size_t(p.gps) * 16 + 1) * 16 + size_t(p.mr) * (p.gps | 1) * 4;
     return true;
 }
 
@@ -1005,7 +1005,7 @@ bool plan_mfma_pair(int M, int K, int I, GemvPlan& p) {
     p.gps = (p.groups + S - 1) / S;
     p.splits = (p.groups + p.gps - 1) / p.gps;
     if (p.splits > 1) p.partial_bytes = size_t(p.splits) * p.mr * p.tiles * 2 * P * 4;
-    const size_t stage = size_t(p.mr) * (size_t(p.gps) * 16 + 1) * 16 + size_t(p.mr) * p.gps * 4;
+    const size_t stage = size_t(p.mr) * (size_t(p.gps) * 16 + 1) * 16 + size_t(p.mr) * (p.gps | 1) * 4;
     const size_t xchg = size_t(p.waves / 2) * rb * kWave * 16;
     p.lds_bytes = std::max(stage, xchg);
     return p.lds_bytes <= kMaxLds;

@@ -183,7 +183,10 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     const int nw0 = PAIR ? (up ? a.half_n : 0) + cg * a.pairs + wl * TPW * 16 : cg * ncol + col_local;
     const int rs = nkb + 1;                            // row stride of act_s, in 16-byte blocks
     uint4* act_s = reinterpret_cast<uint4*>(smem);     // [kRows][rs] of 8 fp16
-    float* esc_s = reinterpret_cast<float*>(act_s + kRows * rs);   // [kRows][ng]
+    // [kRows][es]: an odd row stride puts the 16 rows a wave reads at once in 16 different
+    // banks (a stride of 32 groups put them all in one)
+    const int es = a.kgroups | 1;
+    float* esc_s = reinterpret_cast<float*>(act_s + kRows * rs);
 
     // ---- weight and scale loads of one batch of groups (addresses clamped) ----
     auto load_batch = [&](int b, uint4 (&w)[kP][TPW], uint2 (&sv)[kP][TPW]) {
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
             const uint4 h = stage_item_mfma<PRO, WF>(gv[u], uv[u], &esc);
             if (base + u * nthr + tid < nitems) {
                 act_s[m * rs + kb] = h;
-                if ((kb & 15) == 0) esc_s[m * ng + (kb >> 4)] = esc;
+                if ((kb & 15) == 0) esc_s[m * es + (kb >> 4)] = esc;
             }
             advance(m, kb);
         }
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
             const int gl = min(b * kP + p, ng - 1);
 #pragma unroll
             for (int j = 0; j < 4; ++j) bop[p][j] = __builtin_bit_cast(f16x8_t, act_s[row * rs + 16 * gl + 4 * ls + j]);
-            e[p] = b * kP + p < ng ? esc_s[row * ng + gl] : 0.f;
+            e[p] = b * kP + p < ng ? esc_s[row * es + gl] : 0.f;
         }
         f32x4_t bias[kP];
 #pragma unroll
