@@ -47,6 +47,10 @@ Readings where the pages are silent (each is also listed in the design notes):
   SwiGLU prologue value.  E2M1 codes are packed like the int4 nibbles (code of k = 8*kb
   + j in bits [4j, 4j+4) of word (n, kb)); block scales are E4M3 ('fn': no infinities)
   bytes [N, K/16], scale (n, b) applying to k in [16 b, 16 b + 16) of column n.
+* FP4 activations (both operands FP4, as [P3]'s scaled matmul takes them): quantised at
+  run time with a given per-tensor scale G, one E4M3 scale per 16 values, every step in
+  fp32 with round-to-nearest-even and saturation (see nvfp4_quantize); the per-tensor
+  scale travels in the output multiplier.
 """
 from __future__ import annotations
 
@@ -61,6 +65,7 @@ __all__ = [
     "add_rmsnorm_gemv_swiglu", "w4_gemv_swiglu", "mlp_decode2", "mlp_chain2",
     "swiglu_act", "w4_gemm", "swiglu_w4_gemm",
     "FP4_BLOCK", "e2m1_decode", "e4m3_decode", "fp4_unpack", "fp4_dequant", "swiglu_fp4_gemv", "fp4_gemv",
+    "e4m3_encode", "e2m1_encode", "nvfp4_quantize", "nvfp4_dequant", "fp4a4_gemv", "swiglu_fp4a4_gemv",
 ]
 
 GROUP = 128   # weights per scale group along K (one scale per group per column)
@@ -496,5 +501,89 @@ def swiglu_fp4_gemv(g, u, qweight, scales, out_scale=1.0, residual=None, *, retu
 def fp4_gemv(x, qweight, scales, out_scale=None, residual=None, *, return_f64=False):
     """The same GEMV with the identity prologue: y = bf16([out_scale *] x @ W (+ residual))."""
     acc = _chunked_fp4_gemv(bf16_to_f64(x), qweight, scales)
+    y = _epilogue(acc, out_scale, residual)
+    return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)
+
+
+# ----------------------------------------------------------------------------
+# FP4 activations ([P3]: the scaled matmul takes packed FP4 for both of its inputs, each
+# with E4M3 1x16 block scales; the zero-dimensional fp32 multiplier carries what the
+# block scales do not, here the activation's per-tensor scale G times the weights').
+# The activation is quantised at run time with a given per-tensor scale G (a calibrated
+# constant), one E4M3 scale per 16 values along K:
+#     s_b = e4m3(amax_b / (6 G))                 amax_b: the block's largest magnitude
+#     q_k = e2m1(x_k / (s_b G)), 0 where s_b = 0
+# each step an fp32 operation (the precision the kernels decide in), both roundings to
+# nearest with ties to the even code, saturating (E4M3 at 448, E2M1 at 6).  The GEMM
+# then multiplies the exact values q_k s_b by the FP4 weights.
+# ----------------------------------------------------------------------------
+_E4M3_FINITE = e4m3_decode(np.arange(127))      # codes 0..126: 0 .. 448, increasing
+
+
+def e4m3_encode(t) -> np.ndarray:
+    """Non-negative values -> E4M3 codes 0..126: the nearest finite E4M3 value, ties to
+    the even code, 448 for everything above it."""
+    t = np.asarray(t, dtype=np.float64)
+    i = np.clip(np.searchsorted(_E4M3_FINITE, t), 1, 126)         # _E4M3_FINITE[i - 1] < t <= [i]
+    lo, hi = _E4M3_FINITE[i - 1], _E4M3_FINITE[i]
+    up = (hi - t < t - lo) | ((hi - t == t - lo) & (i % 2 == 0))
+    code = np.where(up, i, i - 1)
+    code = np.where(t >= 448.0, 126, np.where(t <= 0.0, 0, code))
+    return code.astype(np.uint8)
+
+
+def e2m1_encode(y) -> np.ndarray:
+    """Values -> E2M1 codes 0..15: the magnitude to the nearest E2M1 magnitude, ties to the
+    even code, 6 for everything above it; bit 3 is the value's sign bit."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    i = np.clip(np.searchsorted(_E2M1_MAGNITUDE, a), 1, 7)
+    lo, hi = _E2M1_MAGNITUDE[i - 1], _E2M1_MAGNITUDE[i]
+    up = (hi - a < a - lo) | ((hi - a == a - lo) & (i % 2 == 0))
+    code = np.where(a >= 6.0, 7, np.where(up, i, i - 1))
+    return (code | np.where(np.signbit(y), 8, 0)).astype(np.uint8)
+
+
+def nvfp4_quantize(x, global_scale):
+    """x float32 [M, K] (K % 16 == 0), per-tensor scale G > 0 -> (E2M1 codes uint8 [M, K],
+    E4M3 block-scale codes uint8 [M, K/16]), every step in fp32 as described above."""
+    x = np.asarray(x, dtype=np.float32)
+    G = np.float32(global_scale)
+    M, K = x.shape
+    if K % FP4_BLOCK:
+        raise ValueError("K must be a multiple of 16")
+    xb = x.reshape(M, K // FP4_BLOCK, FP4_BLOCK)
+    amax = np.max(np.abs(xb), axis=-1)                      # float32
+    sc = e4m3_encode(amax / (np.float32(6.0) * G))           # float32 quotient, then E4M3
+    s = e4m3_decode(sc).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = xb / (s * G)[..., None]                          # float32 product, float32 quotient
+    codes = np.where(s[..., None] > 0, e2m1_encode(y), 0)
+    return codes.reshape(M, K).astype(np.uint8), sc
+
+
+def nvfp4_dequant(codes, scale_codes) -> np.ndarray:
+    """float64 [M, K]: e2m1(code[m, k]) * e4m3(scale[m, k // 16]) (exact)."""
+    s = e4m3_decode(scale_codes)
+    return e2m1_decode(codes) * np.repeat(s, FP4_BLOCK, axis=-1)
+
+
+def fp4a4_gemv(x, qweight, scales, act_global_scale, out_scale=None, residual=None, *, return_f64=False):
+    """Both operands FP4 ([P3]'s scaled matmul): x (bf16 [M, K]) quantised with
+    nvfp4_quantize, then y = bf16([out_scale *] sum_k xq[m, k] w[k, n] (+ residual)) with
+    xq = e2m1 * e4m3 (without G: the output multiplier carries it) and the FP4 weights."""
+    codes, sc = nvfp4_quantize(bf16_to_f64(x).astype(np.float32), act_global_scale)
+    acc = _chunked_fp4_gemv(nvfp4_dequant(codes, sc), qweight, scales)
+    y = _epilogue(acc, out_scale, residual)
+    return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)
+
+
+def swiglu_fp4a4_gemv(g, u, qweight, scales, act_global_scale, out_scale=1.0, residual=None, *,
+                      return_f64=False):
+    """The same with the SwiGLU prologue: act = silu(g) * u, rounded to fp32 (the
+    precision the quantisation decides in), then quantised and multiplied as above."""
+    act = silu_mul(bf16_to_f64(g), bf16_to_f64(u)).astype(np.float32)
+    codes, sc = nvfp4_quantize(act, act_global_scale)
+    acc = _chunked_fp4_gemv(nvfp4_dequant(codes, sc), qweight, scales)
     y = _epilogue(acc, out_scale, residual)
     return (f64_to_bf16(y), y) if return_f64 else f64_to_bf16(y)
