@@ -419,6 +419,38 @@ FDEC_API int fdec_fp4_gemv(const fdec_bf16* x, const fdec_fp4* W, const float* o
 FDEC_API int fdec_fp4_dequant(const fdec_fp4* W, float* w_out, fdec_stream stream);
 
 /*
+ * FP4 activations as well ("PyTorch folds NVFP4 output scaling into NVGEMM candidates for
+ * decode workloads": the scaled matmul takes packed FP4 for both of its inputs, each with
+ * E4M3 1x16 block scales, and a zero-dimensional fp32 output multiplier).  The
+ * activation is quantised while it is formed, with its per-tensor scale G (act_scale: a
+ * device fp32 > 0, a calibrated constant), one E4M3 block scale per 16 values along K:
+ *     s_b = e4m3(amax_b / (6 G)),   q_k = e2m1(x_k / (s_b G))   (q_k = 0 where s_b = 0),
+ * each step an fp32 operation, both roundings to nearest with ties to the even code and
+ * saturating (E4M3 at 448, E2M1 at 6).  The products use the exact values q_k s_b (G is
+ * not applied: out_scale carries it, with the weights' per-tensor scale):
+ *     y[m, n] = bf16(out_scale * sum_k q[m,k] s[m,k/16] w[k,n] (+ residual[m, n])).
+ *
+ * fdec_swiglu_fp4a4_gemv: act = silu(g) * u (fp32), quantised as above; arguments, shapes,
+ *   kernels, workspace and errors as fdec_swiglu_fp4_gemv, plus act_scale (required,
+ *   4-byte aligned, overlapping neither y nor the workspace).
+ * fdec_fp4a4_gemv: the identity prologue (x [M][K] bf16).
+ * fdec_nvfp4_quantize: test hook; the same quantisation of x [M][ldx] bf16 (K % 16 == 0,
+ *   ldx >= K, ldx % 8 == 0, x 16-byte aligned): codes [M][K/8] words, the code of k =
+ *   8 kb + j in bits [4j, 4j+4) of word (m, kb) (as the weights are packed); scales
+ *   [M][K/16] E4M3 bytes.  codes and scales may overlap nothing.
+ */
+FDEC_API int fdec_swiglu_fp4a4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu,
+                                    const fdec_fp4* W, const float* act_scale,
+                                    const float* out_scale, const fdec_bf16* residual, int32_t M,
+                                    fdec_bf16* y, void* ws, size_t ws_bytes, fdec_stream stream);
+FDEC_API int fdec_fp4a4_gemv(const fdec_bf16* x, const fdec_fp4* W, const float* act_scale,
+                             const float* out_scale, const fdec_bf16* residual, int32_t M,
+                             fdec_bf16* y, void* ws, size_t ws_bytes, fdec_stream stream);
+FDEC_API int fdec_nvfp4_quantize(const fdec_bf16* x, int64_t ldx, int32_t M, int32_t K,
+                                 const float* act_scale, uint32_t* codes, uint8_t* scales,
+                                 fdec_stream stream);
+
+/*
  * The unfused sequences the fused kernels replace, kept for comparison.
  *
  * FDEC_UNFUSED_PRODUCT ([P1], the materialised broadcast product; M == 1 only,

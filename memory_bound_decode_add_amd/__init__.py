@@ -115,6 +115,10 @@ _SIGS = {
                                             _c_p, _sz, _c_p]),
     "fdec_fp4_gemv": (ctypes.c_int, [_c_p, ctypes.POINTER(CFP4), _c_p, _c_p, _i32, _c_p, _c_p, _sz, _c_p]),
     "fdec_fp4_dequant": (ctypes.c_int, [ctypes.POINTER(CFP4), _c_p, _c_p]),
+    "fdec_swiglu_fp4a4_gemv": (ctypes.c_int, [_c_p, _c_p, _i64, ctypes.POINTER(CFP4), _c_p, _c_p, _c_p, _i32, _c_p,
+                                              _c_p, _sz, _c_p]),
+    "fdec_fp4a4_gemv": (ctypes.c_int, [_c_p, ctypes.POINTER(CFP4), _c_p, _c_p, _c_p, _i32, _c_p, _c_p, _sz, _c_p]),
+    "fdec_nvfp4_quantize": (ctypes.c_int, [_c_p, _i64, _i32, _i32, _c_p, _c_p, _c_p, _c_p]),
     # include/fdec_test.h
     "fdec_set_gemv_split": (None, [_i32]),
     "fdec_set_gemv_tiling": (None, [_i32, _i32]),
@@ -818,6 +822,64 @@ def fp4_gemv(x, W: FP4Weight, out_scale=None, residual=None, out=None, ws=None):
     _check(lib().fdec_fp4_gemv(x.data_ptr(), ctypes.byref(cw), _ptr(out_scale), _ptr(residual), M, y.data_ptr(),
                                ws.data_ptr(), ws.numel(), _stream(x.device)))
     return y
+
+
+def swiglu_fp4a4_gemv(g, u, W: FP4Weight, act_scale, out_scale=None, residual=None, out=None, ws=None):
+    """Both operands FP4: act = silu(g) * u quantised with its per-tensor scale act_scale
+    (device fp32 scalar; E4M3 block scales of 16), times the FP4 weights:
+    y = bf16(s * sum_k q s_b w (+ residual))."""
+    M = g.shape[0]
+    ld = _rows(g, "g", M, W.K)
+    ldu = _rows(u, "u", M, W.K)
+    if M > 1 and ldu != ld:
+        raise ValueError("g and u must share a row stride")
+    _need(act_scale, "act_scale", torch.float32, numel=1)
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=g.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    ws = _ws(ws, fp4_gemv_workspace_bytes(M, W.K, W.N), g.device)
+    cw = W.c()
+    _check(lib().fdec_swiglu_fp4a4_gemv(g.data_ptr(), u.data_ptr(), ld, ctypes.byref(cw), act_scale.data_ptr(),
+                                        _ptr(out_scale), _ptr(residual), M, y.data_ptr(), ws.data_ptr(), ws.numel(),
+                                        _stream(g.device)))
+    return y
+
+
+def fp4a4_gemv(x, W: FP4Weight, act_scale, out_scale=None, residual=None, out=None, ws=None):
+    """Both operands FP4 with the identity prologue: x [M, K] bf16 quantised, then times W."""
+    _need(x, "x", torch.bfloat16)
+    M = x.shape[0]
+    _need(x, "x", torch.bfloat16, shape=(M, W.K))
+    _need(act_scale, "act_scale", torch.float32, numel=1)
+    if out_scale is not None:
+        _need(out_scale, "out_scale", torch.float32, numel=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, shape=(M, W.N))
+    y = torch.empty((M, W.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(y, "out", torch.bfloat16, shape=(M, W.N))
+    ws = _ws(ws, fp4_gemv_workspace_bytes(M, W.K, W.N), x.device)
+    cw = W.c()
+    _check(lib().fdec_fp4a4_gemv(x.data_ptr(), ctypes.byref(cw), act_scale.data_ptr(), _ptr(out_scale),
+                                 _ptr(residual), M, y.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)))
+    return y
+
+
+def nvfp4_quantize(x, act_scale):
+    """The activation quantiser alone (test hook): x [M, K] bf16 -> (codes int32 [M, K/8]
+    packed words, E4M3 scale codes uint8 [M, K/16]); x may be a row-strided view."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise TypeError("x must be a 2-D bf16 GPU tensor")
+    M, K = x.shape
+    ld = _rows(x, "x", M, K)
+    _need(act_scale, "act_scale", torch.float32, numel=1)
+    codes = torch.empty((M, K // 8), dtype=torch.int32, device=x.device)
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
+    _check(lib().fdec_nvfp4_quantize(x.data_ptr(), ld, M, K, act_scale.data_ptr(), codes.data_ptr(),
+                                     scales.data_ptr(), _stream(x.device)))
+    return codes, scales
 
 
 def fp4_dequant(W: FP4Weight) -> torch.Tensor:

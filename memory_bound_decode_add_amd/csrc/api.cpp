@@ -175,7 +175,7 @@ int check_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const f
         return fail(FDEC_ERR_ALIAS, "y may only alias residual exactly");
     if (!fp4_gemv_supported(M, W->K, W->N))
         return fail(FDEC_ERR_UNSUPPORTED,
-                    "the FP4 GEMV takes M <= 4 with K <= 16384, or M <= 16 with K %% 128 == 0 (M = %d, K = %d)", M,
+                    "the FP4 GEMV takes M <= 4 with K <= 16384, or M <= 64 with K %% 128 == 0 (M = %d, K = %d)", M,
                     W->K);
     const size_t need = fp4_gemv_workspace_bytes(M, W->K, W->N);
     if (ws_bytes < need) return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);
@@ -1129,7 +1129,7 @@ FDEC_API int fdec_swiglu_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_
     if (st != FDEC_OK) return st;
     if (g_fail_launches.load()) return injected();
     return hip_status(launch_fp4_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual,
-                                      y, ws, static_cast<hipStream_t>(stream)),
+                                      y, ws, nullptr, static_cast<hipStream_t>(stream)),
                       "fp4 gemv launch");
 }
 
@@ -1140,8 +1140,63 @@ FDEC_API int fdec_fp4_gemv(const fdec_bf16* x, const fdec_fp4* W, const float* o
     if (st != FDEC_OK) return st;
     if (g_fail_launches.load()) return injected();
     return hip_status(launch_fp4_gemv(kIdentity, x, nullptr, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale,
-                                      residual, y, ws, static_cast<hipStream_t>(stream)),
+                                      residual, y, ws, nullptr, static_cast<hipStream_t>(stream)),
                       "fp4 gemv launch");
+}
+
+namespace {
+// The activation's per-tensor scale of the FP4-activation GEMVs: a device fp32, read by
+// every workgroup, never written.
+int check_act_scale(const float* act_scale, const fdec_bf16* y, int M, const fdec_fp4* W, const void* ws, size_t ws_bytes) {
+    if (!act_scale) return fail(FDEC_ERR_NULL, "act_scale is required");
+    if (!aligned4(act_scale)) return fail(FDEC_ERR_ALIGN, "act_scale must be 4-byte aligned");
+    const Span A{act_scale, 4};
+    if (overlap(A, {y, size_t(M) * W->N * 2}) || overlap(A, {ws, ws_bytes}))
+        return fail(FDEC_ERR_ALIAS, "act_scale overlaps y or the workspace");
+    return FDEC_OK;
+}
+}  // namespace
+
+FDEC_API int fdec_swiglu_fp4a4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const fdec_fp4* W,
+                                    const float* act_scale, const float* out_scale, const fdec_bf16* residual,
+                                    int32_t M, fdec_bf16* y, void* ws, size_t ws_bytes, fdec_stream stream) {
+    int st = check_fp4_gemv(g, u, ldgu, W, out_scale, residual, M, y, ws, ws_bytes, true);
+    if (st != FDEC_OK) return st;
+    if ((st = check_act_scale(act_scale, y, M, W, ws, ws_bytes)) != FDEC_OK) return st;
+    if (g_fail_launches.load()) return injected();
+    return hip_status(launch_fp4_gemv(kSwiGLU, g, u, ldgu, W->qweight, W->scales, M, W->K, W->N, out_scale, residual,
+                                      y, ws, act_scale, static_cast<hipStream_t>(stream)),
+                      "fp4a4 gemv launch");
+}
+
+FDEC_API int fdec_fp4a4_gemv(const fdec_bf16* x, const fdec_fp4* W, const float* act_scale, const float* out_scale,
+                             const fdec_bf16* residual, int32_t M, fdec_bf16* y, void* ws, size_t ws_bytes,
+                             fdec_stream stream) {
+    if (!W) return fail(FDEC_ERR_NULL, "W is NULL");
+    int st = check_fp4_gemv(x, nullptr, W->K, W, out_scale, residual, M, y, ws, ws_bytes, false);
+    if (st != FDEC_OK) return st;
+    if ((st = check_act_scale(act_scale, y, M, W, ws, ws_bytes)) != FDEC_OK) return st;
+    if (g_fail_launches.load()) return injected();
+    return hip_status(launch_fp4_gemv(kIdentity, x, nullptr, W->K, W->qweight, W->scales, M, W->K, W->N, out_scale,
+                                      residual, y, ws, act_scale, static_cast<hipStream_t>(stream)),
+                      "fp4a4 gemv launch");
+}
+
+FDEC_API int fdec_nvfp4_quantize(const fdec_bf16* x, int64_t ldx, int32_t M, int32_t K, const float* act_scale,
+                                 uint32_t* codes, uint8_t* scales, fdec_stream stream) {
+    if (M < 0 || K <= 0 || K % 16) return fail(FDEC_ERR_SHAPE, "M = %d, K = %d: M >= 0, K a positive multiple of 16", M, K);
+    if (M == 0) return ok();
+    if (!x || !act_scale || !codes || !scales) return fail(FDEC_ERR_NULL, "x, act_scale, codes and scales are required");
+    if (ldx < K || ldx % 8) return fail(FDEC_ERR_SHAPE, "ldx = %lld must be >= K and a multiple of 8", (long long)ldx);
+    if (!aligned16(x) || !aligned4(codes) || !aligned4(act_scale))
+        return fail(FDEC_ERR_ALIGN, "x must be 16-byte aligned, codes and act_scale 4-byte aligned");
+    const Span X{x, (size_t(M - 1) * ldx + K) * 2}, C{codes, size_t(M) * (K / 8) * 4}, S{scales, size_t(M) * (K / 16)},
+        A{act_scale, 4};
+    if (overlap(C, X) || overlap(C, A) || overlap(S, X) || overlap(S, A) || overlap(C, S))
+        return fail(FDEC_ERR_ALIAS, "codes and scales may overlap nothing");
+    if (g_fail_launches.load()) return injected();
+    return hip_status(launch_nvfp4_quantize(x, ldx, M, K, act_scale, codes, scales, static_cast<hipStream_t>(stream)),
+                      "fp4 quantize launch");
 }
 
 FDEC_API int fdec_fp4_dequant(const fdec_fp4* W, float* w_out, fdec_stream stream) {

@@ -136,6 +136,59 @@ __device__ __forceinline__ void fp4x8(uint32_t w, half2_t* q) {
     q[3] = fp4x2<3>(w);
 }
 
+// ---------------------------------------------------------------------------
+// FP4 activations (the scaled matmul with both operands FP4): a block of 16 values along
+// K is quantised with the per-tensor scale G, every step an fp32 operation rounding to
+// nearest with ties to even:
+//     s = e4m3(amax / (6 G)),   q_k = e2m1(x_k / (s G))   (q_k = 0 where s = 0),
+// and the exact values q_k s are what the dot products use: an E2M1 value has 2
+// significant bits and an E4M3 value 4, so q s is an fp16 number (2^-10 <= |q s| <= 2688).
+// ---------------------------------------------------------------------------
+// Non-negative fp32 -> E4M3 code: the nearest E4M3 value, ties to the even code, 448
+// (code 126) for everything above it.
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+    if (!(t > 0.0f)) return 0u;
+    if (t >= 448.0f) return 126u;
+    if (t < 0.015625f) return uint32_t(__builtin_rintf(t * 512.0f));   // steps of 2^-9; code 8 is 2^-6
+    const uint32_t b = __float_as_uint(t);
+    const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);                 // 3 mantissa bits, ties to even
+    return (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);                 // exponent bias 127 -> 7
+}
+
+// fp32 -> E2M1 code: the magnitude to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 (a
+// midpoint goes to the even code), 6 for everything above; bit 3 is the sign bit.
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+    const float a = fabsf(y);
+    const uint32_t c = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+                       uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+    return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// N (8 or 16) values of one block, given the block's largest magnitude (taken over the
+// whole block, which may span two lanes): their codes packed 8 to a word in k order
+// (code of value i in bits 4 (i % 8) of word i / 8), and the fp16 pairs q s in k order.
+// Returns the block's E4M3 scale code.
+template <int N>
+__device__ __forceinline__ uint32_t nvfp4_quantize_block(const float (&v)[N], float amax, float G,
+                                                         uint32_t (&words)[N / 8], uint32_t (&xq)[N / 2]) {
+    const uint32_t sc = e4m3_encode(amax / (6.0f * G));
+    const float s = e4m3_to_f32(sc);
+    const float d = s * G;
+#pragma unroll
+    for (int w = 0; w < N / 8; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) word |= (s > 0.0f ? e2m1_encode(v[8 * w + j] / d) : 0u) << (4 * j);
+        words[w] = word;
+        half2_t q[4];
+        fp4x8(word, q);
+        const half2_t sh = {(_Float16)s, (_Float16)s};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) xq[4 * w + p] = __builtin_bit_cast(uint32_t, q[p] * sh);
+    }
+    return sc;
+}
+
 // Position of weight j (0..7) of a word in the pair order above.
 __host__ __device__ constexpr int pair_slot(int j) { return 2 * (j & 3) + (j >> 2); }
 

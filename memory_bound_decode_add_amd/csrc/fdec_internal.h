@@ -116,16 +116,22 @@ hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
                        void* ws, const GemvPlan& p, hipStream_t s);
 // FP4 (E2M1) weights with E4M3 1x16 block scales: M = 1..4 (K % 32 == 0, K <= 16384)
-// on the chunk-owning kernel, M = 5..16 (K % 128 == 0) on the matrix-core kernel.
+// on the chunk-owning kernel, M = 5..64 (K % 128 == 0) on the matrix-core kernel.  With
+// gscale (the activation's per-tensor scale, device fp32) the activation is quantised to
+// FP4 as well (both operands FP4); NULL keeps it unquantised.
 bool fp4_gemv_supported(int M, int K, int N);
 size_t fp4_gemv_workspace_bytes(int M, int K, int N);
 hipError_t launch_fp4_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
                            const uint8_t* sc, int M, int K, int N, const float* out_scale, const uint16_t* residual,
-                           uint16_t* y, void* ws, hipStream_t s);
+                           uint16_t* y, void* ws, const float* gscale, hipStream_t s);
 hipError_t launch_mfma_fp4(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                            const uint32_t* qw, const uint8_t* sc8, int M, int K, int N,
                            const float* out_scale, const uint16_t* residual, uint16_t* y,
-                           void* ws, const GemvPlan& p, hipStream_t s);
+                           void* ws, const GemvPlan& p, const float* gscale, hipStream_t s);
+// Test hook: FP4 quantisation of a bf16 activation x [M][ldx] (K % 16 == 0): codes
+// [M][K/8] packed words, E4M3 scale codes [M][K/16].
+hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t ldx, int M, int K, const float* gscale, uint32_t* codes,
+                                 uint8_t* scales, hipStream_t s);
 hipError_t launch_fp4_dequant(const uint32_t* qw, const uint8_t* sc, int K, int N, float* w, hipStream_t s);
 hipError_t launch_w4_unpack(const uint32_t* qw, int K, int N, int8_t* q, hipStream_t s);
 hipError_t launch_w4_dequant(const uint32_t* qw, const uint16_t* sc, int K, int N,

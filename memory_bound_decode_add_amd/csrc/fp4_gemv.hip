@@ -29,6 +29,12 @@
 // A column's 32-lane sums are reduced with DPP and lane reads, the per-wave results meet
 // in LDS, and one lane per output sums them in wave order and applies the epilogue.  No
 // workspace, no cross-workgroup step; results do not depend on scheduling.
+//
+// FP4 activations (A4: both operands FP4, as the page's scaled matmul takes them).  A
+// lane's 16 activation values are exactly one block of 16 along K, so it quantises them
+// on its own (nvfp4_quantize_block: E4M3 block scale from the block's largest magnitude
+// and the per-tensor scale G, E2M1 codes) and exchanges the exact fp16 values q s instead
+// of the block-scaled activation; the chunk's power of two is then 1.
 #include "device_common.h"
 #include "fdec_internal.h"
 
@@ -59,9 +65,10 @@ struct Fp4Args {
     const float* out_scale;
     const uint16_t* residual;
     uint16_t* y;
+    const float* gscale;    // A4: the activation's per-tensor scale G (device fp32)
 };
 
-template <int MR, int CH, int PRO>
+template <int MR, int CH, int PRO, bool A4>
 __global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args a) {
     __shared__ float red[kFp4MaxWaves][MR][2 * CH];
     __shared__ __align__(16) unsigned char sc_s[kFp4ScBytes];
@@ -139,16 +146,23 @@ __global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args 
             v[i] = live ? v[i] : 0.f;
             mx = fmaxf(mx, fabsf(v[i]));
         }
-        mx = fmaxf(mx, xchg32(mx));            // the chunk's largest magnitude
-        int e = 0;
-        (void)__builtin_frexpf(mx, &e);
-        const int E = min(max(e - 15, -126), 127);
-        const float down = __builtin_ldexpf(1.0f, -E);
-        e2[m] = __builtin_ldexpf(1.0f, E);
         uint32_t own[8];
+        if (A4) {
+            // the lane's 16 values are one block: its codes and the exact values q s
+            uint32_t words[2];
+            (void)nvfp4_quantize_block<16>(v, mx, *a.gscale, words, own);
+            e2[m] = 1.0f;
+        } else {
+            mx = fmaxf(mx, xchg32(mx));            // the chunk's largest magnitude
+            int e = 0;
+            (void)__builtin_frexpf(mx, &e);
+            const int E = min(max(e - 15, -126), 127);
+            const float down = __builtin_ldexpf(1.0f, -E);
+            e2[m] = __builtin_ldexpf(1.0f, E);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            own[i] = __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2 * i] * down, v[2 * i + 1] * down));
+            for (int i = 0; i < 8; ++i)
+                own[i] = __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2 * i] * down, v[2 * i + 1] * down));
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t oth = xchg32u(own[i]);
@@ -240,6 +254,32 @@ __global__ void fp4_dequant_kernel(const uint32_t* __restrict__ qw, const uint8_
     }
 }
 
+// Test hook: FP4 quantisation of a bf16 activation, one thread per block of 16 values:
+// codes [M][K/8] packed words (k order), E4M3 scale codes [M][K/16].
+__global__ void nvfp4_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M, int nblk,
+                                      const float* __restrict__ gscale, uint32_t* __restrict__ codes,
+                                      uint8_t* __restrict__ scales) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;   // block (m, b)
+    if (i >= int64_t(M) * nblk) return;
+    const int64_t m = i / nblk, b = i % nblk;
+    const uint4* src = reinterpret_cast<const uint4*>(x + m * ldx + b * 16);
+    const uint4 p0 = src[0], p1 = src[1];
+    const uint32_t wd[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    float v[16], mx = 0.f;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+        v[2 * h] = bf16_lo(wd[h]);
+        v[2 * h + 1] = bf16_hi(wd[h]);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fabsf(v[k]));
+    uint32_t words[2], xq[8];
+    const uint32_t sc = nvfp4_quantize_block<16>(v, mx, *gscale, words, xq);
+    codes[m * (nblk * 2) + 2 * b] = words[0];
+    codes[m * (nblk * 2) + 2 * b + 1] = words[1];
+    scales[m * nblk + b] = uint8_t(sc);
+}
+
 struct Fp4Plan {
     int mr, ch, cols, waves, wgs;
 };
@@ -264,10 +304,17 @@ bool fp4_plan(int M, int K, int N, Fp4Plan& p) {
 
 template <int MR, int CH>
 hipError_t launch_fp4_2(Prologue pro, const Fp4Args& a, const Fp4Plan& p, hipStream_t s) {
-    if (pro == kSwiGLU)
-        fp4_gemv_kernel<MR, CH, kSwiGLU><<<dim3(p.wgs), p.waves * kWave, 0, s>>>(a);
-    else
-        fp4_gemv_kernel<MR, CH, kIdentity><<<dim3(p.wgs), p.waves * kWave, 0, s>>>(a);
+    const dim3 grid(p.wgs), block(p.waves * kWave);
+    if (a.gscale) {
+        if (pro == kSwiGLU)
+            fp4_gemv_kernel<MR, CH, kSwiGLU, true><<<grid, block, 0, s>>>(a);
+        else
+            fp4_gemv_kernel<MR, CH, kIdentity, true><<<grid, block, 0, s>>>(a);
+    } else if (pro == kSwiGLU) {
+        fp4_gemv_kernel<MR, CH, kSwiGLU, false><<<grid, block, 0, s>>>(a);
+    } else {
+        fp4_gemv_kernel<MR, CH, kIdentity, false><<<grid, block, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -315,12 +362,12 @@ size_t fp4_gemv_workspace_bytes(int M, int K, int N) {
 
 hipError_t launch_fp4_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
                            const uint8_t* sc, int M, int K, int N, const float* out_scale, const uint16_t* residual,
-                           uint16_t* y, void* ws, hipStream_t s) {
+                           uint16_t* y, void* ws, const float* gscale, hipStream_t s) {
     if (M > 4) {
         GemvPlan g{};
         g.groups = K / kGroup;
         if (!fp4_gemv_supported(M, K, N) || !plan_mfma(M, K, N, g)) return hipErrorInvalidValue;
-        return launch_mfma_fp4(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, g, s);
+        return launch_mfma_fp4(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, g, gscale, s);
     }
     Fp4Plan p;
     if (!fp4_plan(M, K, N, p)) return hipErrorInvalidValue;
@@ -338,11 +385,20 @@ hipError_t launch_fp4_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1,
     a.out_scale = out_scale;
     a.residual = residual;
     a.y = y;
+    a.gscale = gscale;
     switch (p.mr) {
         case 1: return launch_fp4_1<1>(pro, a, p, s);
         case 2: return launch_fp4_1<2>(pro, a, p, s);
         default: return launch_fp4_1<4>(pro, a, p, s);
     }
+}
+
+hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t ldx, int M, int K, const float* gscale, uint32_t* codes,
+                                 uint8_t* scales, hipStream_t s) {
+    const int64_t n = int64_t(M) * (K / 16);
+    if (n == 0) return hipSuccess;
+    nvfp4_quantize_kernel<<<dim3(unsigned((n + 255) / 256)), 256, 0, s>>>(x, ldx, M, K / 16, gscale, codes, scales);
+    return hipGetLastError();
 }
 
 hipError_t launch_fp4_dequant(const uint32_t* qw, const uint8_t* sc, int K, int N, float* w, hipStream_t s) {

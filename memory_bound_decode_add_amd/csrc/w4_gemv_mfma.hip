@@ -65,6 +65,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMfmaP = 4;          // groups per batch of weight loads
 constexpr int kWInt4 = 0;          // weight formats
 constexpr int kWFp4 = 1;
+constexpr int kWFp4A4 = 2;         // FP4 weights and FP4 activations (quantised while staged)
 
 struct MfmaArgs {
     const uint16_t* a0;     // g (SwiGLU) or x (identity), row stride lda
@@ -73,6 +74,7 @@ struct MfmaArgs {
     const uint4* qw;        // [N][K/32] chunks of 4 words
     const uint16_t* sc;     // bf16 scales [K/128][N] (int4)
     const uint8_t* sc8;     // E4M3 block scales [N][K/16] (FP4)
+    const float* gscale;    // FP4 activations: their per-tensor scale G (device fp32)
     int M, K, N;
     int nch;                // K / 32
     int groups;             // K / 128
@@ -101,9 +103,13 @@ __device__ __forceinline__ f16x8_t decode_f16x8_biased(uint32_t w, DecodeMasks d
 // DPP row hold the 16 k-blocks of one 128-wide group of that row and share its scale.
 // Must be called with the whole wave active.  Returns the fp16 words in pair order;
 // *esc = 2^E of the group.  Rows past M need no zeroing: row m of the activation only
-// reaches output row m, which is never stored.
+// reaches output row m, which is never stored.  With FP4 activations (kWFp4A4) the two
+// items of a 16-value block sit in lanes 2i and 2i + 1 (k-blocks 2b and 2b + 1; a row has
+// an even number of k-blocks and a workgroup an even number of threads); they take the
+// block's largest magnitude from each other and return the exact values q s in k order,
+// with *esc = 1.
 template <int PRO, int WF>
-__device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, float* esc) {
+__device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, float* esc, float G) {
     const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
     const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
     float v[8];
@@ -120,6 +126,13 @@ __device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, float* esc)
     float mx = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+    if (WF == kWFp4A4) {
+        mx = fmaxf(mx, dpp<kQuadSwap1>(mx));           // the block's other half (lane ^ 1)
+        uint32_t words[1], xq[4];
+        (void)nvfp4_quantize_block<8>(v, mx, G, words, xq);
+        *esc = 1.0f;
+        return make_uint4(xq[0], xq[1], xq[2], xq[3]);
+    }
     // magnitudes order as their bit patterns do, so the group max is an unsigned max
     uint32_t mb = __builtin_bit_cast(uint32_t, mx);
     mb = max(mb, dpp_u32<kQuadSwap1>(mb));
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
             for (int t = 0; t < TPW; ++t) {
                 const int n = min(nw0 + t * 16 + lm, a.N - 1);
                 w[p][t] = a.qw[size_t(n) * a.nch + 4 * g + ls];
-                if (WF == kWFp4) {
+                if (WF != kWInt4) {
                     // the two E4M3 scales of this lane's chunk (column n, chunk 4g + ls)
                     sv[p][t].x = *reinterpret_cast<const uint16_t*>(a.sc8 + size_t(n) * (a.K / 16) + 2 * (4 * g + ls));
                     sv[p][t].y = 0;
@@ -230,6 +243,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     // converted, so the staging waits for one L2 round trip, not one per item.
     const int nitems = nkb * kRows;
     const int kbase = g0 * 128;
+    const float G = WF == kWFp4A4 ? *a.gscale : 0.0f;
     constexpr int UMAX = PRO == kSwiGLU ? 12 : 24;
     const int nthr = blockDim.x;
     // Item it has row it / nkb and k-block it % nkb.  A thread's items are nthr apart, so
@@ -263,7 +277,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
         for (int u = 0; u < UMAX; ++u) {
             if (base + u * nthr >= nitems) break;                   // uniform: the whole wave stays active
             float esc;
-            const uint4 h = stage_item_mfma<PRO, WF>(gv[u], uv[u], &esc);
+            const uint4 h = stage_item_mfma<PRO, WF>(gv[u], uv[u], &esc, G);
             if (base + u * nthr + tid < nitems) {
                 act_s[m * rs + kb] = h;
                 if ((kb & 15) == 0) esc_s[m * es + (kb >> 4)] = esc;
@@ -323,7 +337,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
 #pragma unroll
             for (int p = 0; p < kP; ++p) d[p] = bias[p];
             _Float16 fs[kP][2];
-            if (WF == kWFp4) {
+            if (WF != kWInt4) {
 #pragma unroll
                 for (int p = 0; p < kP; ++p) {
                     fs[p][0] = (_Float16)e4m3_to_f32(sv[p][t].x & 0xFFu);
@@ -335,12 +349,12 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
 #pragma unroll
                 for (int p = 0; p < kP; ++p) {
                     const uint32_t wd = j == 0 ? w[p][t].x : j == 1 ? w[p][t].y : j == 2 ? w[p][t].z : w[p][t].w;
-                    const f16x8_t aop = WF == kWFp4 ? fp4_operand(wd, fs[p][j >> 1]) : decode_f16x8_biased(wd, DecodeMasks{a.m_lo, a.m_hi});
+                    const f16x8_t aop = WF != kWInt4 ? fp4_operand(wd, fs[p][j >> 1]) : decode_f16x8_biased(wd, DecodeMasks{a.m_lo, a.m_hi});
                     d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[p][j], d[p], 0, 0, 0);
                 }
 #pragma unroll
             for (int p = 0; p < kP; ++p) {
-                if (WF == kWFp4) {
+                if (WF != kWInt4) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) out[r][t][q] = fmaf(e[p], d[p][q], out[r][t][q]);
                 } else {
@@ -444,8 +458,10 @@ namespace {
 template <int WF>
 hipError_t launch_mfma_wf(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
                           const uint16_t* sc, const uint8_t* sc8, int M, int K, int N, const float* out_scale,
-                          const uint16_t* residual, uint16_t* y, void* ws, const GemvPlan& p, hipStream_t s) {
+                          const uint16_t* residual, uint16_t* y, void* ws, const GemvPlan& p, hipStream_t s,
+                          const float* gscale = nullptr) {
     MfmaArgs a{};
+    a.gscale = gscale;
     a.a0 = a0;
     a.a1 = a1;
     a.lda = lda;
@@ -558,7 +574,10 @@ hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
 hipError_t launch_mfma_fp4(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                            const uint32_t* qw, const uint8_t* sc8, int M, int K, int N,
                            const float* out_scale, const uint16_t* residual, uint16_t* y,
-                           void* ws, const GemvPlan& p, hipStream_t s) {
+                           void* ws, const GemvPlan& p, const float* gscale, hipStream_t s) {
+    if (gscale)
+        return launch_mfma_wf<kWFp4A4>(pro, a0, a1, lda, qw, nullptr, sc8, M, K, N, out_scale, residual, y, ws, p, s,
+                                       gscale);
     return launch_mfma_wf<kWFp4>(pro, a0, a1, lda, qw, nullptr, sc8, M, K, N, out_scale, residual, y, ws, p, s);
 }
 

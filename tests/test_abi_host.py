@@ -232,6 +232,37 @@ def test_fp4_gemv_validation(L, inject):
     assert L.fdec_fp4_dequant(ctypes.byref(W), f(), None) == HIP
 
 
+def test_fp4a4_validation(L, inject):
+    f = Fake()
+    W = _fp4(f, K=1024, N=512)
+    act, y = f(4), f()
+
+    def call(g=None, u=None, a=act, scale=None, res=None, M=1, yy=y, ws=0, wsb=0):
+        return L.fdec_swiglu_fp4a4_gemv(f() if g is None else g, f() if u is None else u, W.K, ctypes.byref(W), a,
+                                        scale, res, M, yy, ws, wsb, None)
+
+    assert call() == HIP
+    assert call(a=0) == NULL                             # the per-tensor scale is required
+    assert call(a=act + 2) == ALIGN
+    assert call(a=y + 64) == ALIAS                       # y would overwrite it
+    assert call(u=0) == NULL
+    assert call(M=0) == SHAPE
+    assert L.fdec_fp4a4_gemv(f(), ctypes.byref(W), act, None, None, 1, y, 0, 0, None) == HIP
+    assert L.fdec_fp4a4_gemv(f(), ctypes.byref(W), 0, None, None, 1, y, 0, 0, None) == NULL
+    assert L.fdec_fp4a4_gemv(f(), None, act, None, None, 1, y, 0, 0, None) == NULL
+    # the quantiser hook
+    x, c, sc = f(), f(), f()
+    assert L.fdec_nvfp4_quantize(x, 1024, 4, 1024, act, c, sc, None) == HIP
+    assert L.fdec_nvfp4_quantize(x, 1024, 0, 1024, act, c, sc, None) == OK      # nothing to do
+    assert L.fdec_nvfp4_quantize(x, 1024, 4, 1000, act, c, sc, None) == SHAPE   # K % 16
+    assert L.fdec_nvfp4_quantize(x, 1000, 4, 1024, act, c, sc, None) == SHAPE   # ldx < K
+    assert L.fdec_nvfp4_quantize(x, 1028, 4, 1024, act, c, sc, None) == SHAPE   # ldx % 8
+    assert L.fdec_nvfp4_quantize(x + 8, 1024, 4, 1024, act, c, sc, None) == ALIGN
+    assert L.fdec_nvfp4_quantize(x, 1024, 4, 1024, 0, c, sc, None) == NULL
+    assert L.fdec_nvfp4_quantize(x, 1024, 4, 1024, act, x + 64, sc, None) == ALIAS
+    assert L.fdec_nvfp4_quantize(x, 1024, 4, 1024, act, c, c + 16, None) == ALIAS
+
+
 def test_gemv_split_override_changes_only_the_test_queries(L):
     base = L.fdec_w4_gemv_workspace_bytes(1, 9216, 2560)
     mlp = L.fdec_mlp_workspace_bytes(1, 1536, 8960)
