@@ -321,6 +321,25 @@ def bench_extras(torch, F, synth, n_sets_gemv):
         out[f"swiglu_fp4_gemv_{Mb}x9216x2560"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9,
                                                   "frac_of_peak": b / t / 1e9 / PEAK_GBPS, "bytes_per_call": b}
         del gb, ub, ys, wsb
+
+    # both operands FP4: the SwiGLU activation quantised to E2M1 with E4M3 1x16 block scales
+    # in the prologue, over a per-tensor scale calibrated once from one set's activation
+    # (largest magnitude / (6 * 448)); the HBM bytes are those of the FP4-weight GEMV
+    log("[bench] FP4-activation SwiGLU GEMV 1/16/64 x 9216x2560")
+    gen = torch.Generator().manual_seed(4444)
+    for Mb in (1, 16, 64):
+        gb = torch.randn(Mb, K, generator=gen).to(torch.bfloat16).cuda()
+        ub = torch.randn(Mb, K, generator=gen).to(torch.bfloat16).cuda()
+        gsc = F.scalar(F.swiglu(gb, ub).float().abs().max().item() / (6.0 * 448.0))
+        ys = [torch.empty((Mb, N), dtype=torch.bfloat16, device="cuda") for _ in fsets]
+        wsb = F.workspace(max(1, F.fp4_gemv_workspace_bytes(Mb, K, N)))
+        fns = [lambda s=s, y=y: F.swiglu_fp4a4_gemv(gb, ub, s[2], gsc, scale, out=y, ws=wsb)
+               for s, y in zip(fsets, ys)]
+        t = bench_repeat(torch, timer, fns, 5) / len(fsets)
+        b = T.swiglu_fp4_gemv_bytes(Mb, K, N)
+        out[f"swiglu_fp4a4_gemv_{Mb}x9216x2560"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9,
+                                                    "frac_of_peak": b / t / 1e9 / PEAK_GBPS, "bytes_per_call": b}
+        del gb, ub, ys, wsb
     del fsets
 
     # the prefill point: 2,048 tokens through the SwiGLU pass and the matrix-core GEMM at

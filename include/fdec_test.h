@@ -38,7 +38,9 @@ FDEC_API void fdec_test_fail_launches(int32_t on);
  *   5..16 rows run.  kernel 0: the built-in choice; 1: the row-block kernel (its
  *   activation staged in LDS); 2: the kernel whose waves split K, with `tiles` 16-column
  *   tiles per workgroup (4 or 8) and `groups_per_wave` 128-wide groups per wave (1..4; at
- *   most 2 with the SwiGLU prologue), 0 for either leaving the built-in choice. */
+ *   most 2 with the SwiGLU prologue), 0 for either leaving the built-in choice; 3: the
+ *   kernel fed by direct-to-LDS loads of every operand (also the pair-mode gate_up of
+ *   fdec_w4_gemv_swiglu and of the 16-row layer). */
 FDEC_API void fdec_set_mfma_plan(int32_t kernel, int32_t tiles, int32_t groups_per_wave);
 
 /* Workspace sizes under the overrides active now (equal to the fdec.h queries when none

@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfdec.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "add_rmsnorm.hip", "w4_gemv.hip", "w4_gemv_mfma.hip", "unfused.hip", "fp4_gemv.hip", "probes.hip", "w4_gemv_kmfma.hip", "w4_gemm.hip"]
+SOURCES = ["api.cpp", "add_rmsnorm.hip", "w4_gemv.hip", "w4_gemv_mfma.hip", "unfused.hip", "fp4_gemv.hip", "probes.hip", "w4_gemv_kmfma.hip", "w4_gemv_ring.hip", "w4_gemm.hip"]
 
 
 def hipcc() -> str:

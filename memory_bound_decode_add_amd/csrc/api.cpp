@@ -293,7 +293,7 @@ bool layer2_fused_norm(int M) { return M <= 4; }
 size_t mlp2_ws(int M, int H, int I, const Overrides& ov) {
     if (layer2_fused_norm(M)) return align_up(size_t(M) * H * 2);
     GemvPlan pp;
-    if (!plan_mfma_pair(M, H, I, pp)) return 0;
+    if (!plan_pair(M, H, I, ov, pp)) return 0;
     return align_up(size_t(M) * H * 2) + std::max(pp.partial_bytes, plan_gemv(M, I, H, ov, kIdentity).partial_bytes);
 }
 
@@ -302,7 +302,7 @@ int check_layer2(const fdec_mlp_layer* L, int M, LayerDims* d, const Overrides& 
     if (st != FDEC_OK) return st;
     if (!layer2_fused_norm(M)) {
         GemvPlan pp;
-        if (!plan_mfma_pair(M, d->H, d->I, pp))
+        if (!plan_pair(M, d->H, d->I, ov, pp))
             return fail(FDEC_ERR_UNSUPPORTED, "no matrix-core gate_up plan for M = %d, H = %d, I = %d", M, d->H, d->I);
         return FDEC_OK;
     }
@@ -342,7 +342,7 @@ hipError_t enqueue_layer2(const fdec_mlp_layer* L, int M, LayerDims d, const Ove
         uint16_t* y = static_cast<uint16_t*>(ws);
         void* pws = static_cast<char*>(ws) + align_up(size_t(M) * d.H * 2);
         GemvPlan pp;
-        if (!plan_mfma_pair(M, d.H, d.I, pp)) return hipErrorInvalidValue;
+        if (!plan_pair(M, d.H, d.I, ov, pp)) return hipErrorInvalidValue;
         const GemvPlan dp = plan_gemv(M, d.I, d.H, ov, kIdentity);
         hipError_t e = launch_add_rmsnorm(x, residual, L->norm_weight, L->eps, M, d.H, residual, y, s);
         if (e != hipSuccess) return e;
@@ -546,7 +546,7 @@ FDEC_API void fdec_set_gemv_tiling(int32_t waves, int32_t cols_per_workgroup) {
 }
 FDEC_API void fdec_test_fail_launches(int32_t on) { g_fail_launches.store(on ? 1 : 0); }
 FDEC_API void fdec_set_mfma_plan(int32_t kernel, int32_t tiles, int32_t groups_per_wave) {
-    g_mfma_kernel.store(kernel == 1 || kernel == 2 ? kernel : 0);
+    g_mfma_kernel.store(kernel >= 1 && kernel <= 3 ? kernel : 0);
     g_mfma_tiles.store(tiles == 4 || tiles == 8 ? tiles : 0);
     g_mfma_gw.store(groups_per_wave >= 1 && groups_per_wave <= 4 ? groups_per_wave : 0);
 }
@@ -842,7 +842,7 @@ FDEC_API size_t fdec_mlp2_workspace_bytes(int32_t M, int32_t H, int32_t I) {
 
 FDEC_API size_t fdec_w4_gemv_swiglu_workspace_bytes(int32_t M, int32_t K, int32_t I) {
     GemvPlan p;
-    if (K <= 0 || K % 128 || !plan_mfma_pair(M, K, I, p)) return 0;
+    if (K <= 0 || K % 128 || !plan_pair(M, K, I, Overrides{}, p)) return 0;
     return p.partial_bytes;
 }
 
@@ -856,7 +856,7 @@ FDEC_API int fdec_w4_gemv_swiglu(const fdec_bf16* x, const fdec_w4* gate_up, int
     if (!x || !act_out) return fail(FDEC_ERR_NULL, "x and act_out are required");
     if (!aligned16(x) || !aligned16(act_out)) return fail(FDEC_ERR_ALIGN, "x and act_out must be 16-byte aligned");
     GemvPlan p;
-    if (!plan_mfma_pair(M, K, I, p)) return fail(FDEC_ERR_UNSUPPORTED, "no plan for M = %d, K = %d, I = %d", M, K, I);
+    if (!plan_pair(M, K, I, current_overrides(), p)) return fail(FDEC_ERR_UNSUPPORTED, "no plan for M = %d, K = %d, I = %d", M, K, I);
     if (ws_bytes < p.partial_bytes)
         return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, p.partial_bytes);
     if (p.partial_bytes > 0 && !ws) return fail(FDEC_ERR_NULL, "workspace is NULL");

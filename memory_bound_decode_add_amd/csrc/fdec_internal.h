@@ -26,7 +26,7 @@ constexpr int kColMaxChunks = 8;
 constexpr int kColScLoads = 4;       // 16-byte scale loads per thread, column kernel     // 32-wide K chunks per lane, column kernel
 constexpr size_t kMaxLds = 160 * 1024;
 
-enum GemvKind { kColumnOwning = 0, kSplitK = 1, kMfma = 2, kKMfma = 3 };
+enum GemvKind { kColumnOwning = 0, kSplitK = 1, kMfma = 2, kKMfma = 3, kRing = 4 };
 constexpr int kMfmaWaves = 8;       // waves per workgroup, matrix-core kernel
 constexpr int kMfmaMaxSliceGroups = 36;   // 128-wide groups per K slice at 16 rows (LDS: 4 KB each)
 constexpr int kMfmaMaxRows = 64;          // four row blocks of 16
@@ -65,6 +65,9 @@ struct Overrides {
 Overrides current_overrides();
 
 
+// kAddRmsNorm: the activation is rmsnorm(x + r) * w over the whole row (the fused
+// layer's gate_up), and the epilogue writes silu(gate) * up of column pairs (i, I + i).
+enum Prologue { kIdentity = 0, kSwiGLU = 1, kAddRmsNorm = 2 };
 bool plan_mfma(int M, int K, int N, GemvPlan& p);   // 5 <= M <= 64
 // The gate_up projection [K, 2I] with the SwiGLU epilogue: act[m][i] = bf16(silu(g) u)
 // from the unrounded sums of columns i and I + i (matrix-core kernel, 1 <= M <= 64).
@@ -72,7 +75,23 @@ bool plan_mfma_pair(int M, int K, int I, GemvPlan& p);
 // The matrix-core kernel whose waves split K (5..16 rows).  max_gw: most 128-wide groups
 // per wave (at most 2 with the SwiGLU prologue).
 bool plan_kmfma(int M, int K, int N, int max_gw, GemvPlan& p, const Overrides& ov = Overrides{});
+// The pair plan GEMVs run: plan_mfma_pair, or the ring kernel's when chosen (5..16 rows).
+bool plan_pair(int M, int K, int I, const Overrides& ov, GemvPlan& p);
+// Launches a pair plan of either kind.
 hipError_t launch_mfma_pair(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
+                            uint16_t* act, void* ws, const GemvPlan& p, hipStream_t s);
+// act[m][i] = bf16(silu(g) * u) from the K slices' fp32 partials of the pairs' gate and
+// up columns (P pairs per column range: gate at range * 2P + i % P, up P further).
+hipError_t launch_splitk_finish_swiglu(const float* partial, int splits, int64_t split_stride, int64_t row_stride,
+                                       int M, int I, int P, uint16_t* act, hipStream_t s);
+// The matrix-core kernel fed by direct-to-LDS loads of every operand (5..16 rows; pair
+// mode with the identity prologue).
+bool plan_ring(int M, int K, int N, Prologue pro, GemvPlan& p);
+bool plan_ring_pair(int M, int K, int I, GemvPlan& p);
+hipError_t launch_ring(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
+                       const uint16_t* sc, int M, int K, int N, const float* out_scale, const uint16_t* residual,
+                       uint16_t* y, void* ws, const GemvPlan& p, hipStream_t s);
+hipError_t launch_ring_pair(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
                             uint16_t* act, void* ws, const GemvPlan& p, hipStream_t s);
 // Sums the fp32 partials of K slices (slice j of row m at partial + j * split_stride +
 // m * row_stride) in slice order and applies the epilogue; launched after the kernel
@@ -82,9 +101,6 @@ hipError_t launch_splitk_finish(const float* partial, int splits, int64_t split_
 // the larger workspace of the two prologues' built-in plans (no overrides)
 size_t gemv_workspace_bytes(int M, int K, int N);
 
-// kAddRmsNorm: the activation is rmsnorm(x + r) * w over the whole row (the fused
-// layer's gate_up), and the epilogue writes silu(gate) * up of column pairs (i, I + i).
-enum Prologue { kIdentity = 0, kSwiGLU = 1, kAddRmsNorm = 2 };
 // The plan of a GEMV with prologue pro (kSwiGLU or kIdentity; the matrix-core kernel whose
 // waves split K holds fewer groups per wave with the SwiGLU prologue's raw g and u).
 GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov, Prologue pro);

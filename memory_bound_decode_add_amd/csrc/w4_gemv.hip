@@ -1011,6 +1011,21 @@ bool plan_mfma_pair(int M, int K, int I, GemvPlan& p) {
     return p.lds_bytes <= kMaxLds;
 }
 
+// The ring kernel's plan where it measured faster than the row-block kernel (5..16 rows,
+// identity prologue and pair mode): K slices of at most 16 groups in at most 256
+// workgroups.  Longer slices favour the row-block kernel, whose main loop runs without a
+// barrier once its activation is staged (16 x 4096 x 28672: 19.0 against 21.8 us), and
+// shorter ones the ring, which has no staging pass (16 x 1536 x 17920: 9.1 against
+// 14.1 us; 16 x 4096 x 11008: 14.1 against 19.1; 16 x 1024 x 512: 5.5 against 7.5).
+bool ring_preferred(const GemvPlan& r) { return r.gps <= 16 && r.tiles * r.splits <= 256; }
+
+bool plan_pair(int M, int K, int I, const Overrides& ov, GemvPlan& p) {
+    if ((ov.mfma_kernel == 3 || ov.mfma_kernel == 0) && M > 4 && plan_ring_pair(M, K, I, p) &&
+        (ov.mfma_kernel == 3 || ring_preferred(p)))
+        return true;
+    return plan_mfma_pair(M, K, I, p);
+}
+
 GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov, Prologue pro) {
     GemvPlan p{};
     p.groups = K / kGroup;
@@ -1019,6 +1034,14 @@ GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov, Prologue pro) {
         return p;
     }
     if (ov.split == 0 && plan_column(M, K, N, p, ov)) return p;
+    p = GemvPlan{};
+    // the ring kernel: forced, or built in where it measured faster -- the SwiGLU prologue
+    // above about 12 MB of weights (16 x 14336 x 4096: 15.5 against 16.4 us; 16 x 4096 x 11008:
+    // 15.7 against 23.9), the identity prologue by ring_preferred
+    if (ov.split == 0 && (ov.mfma_kernel == 3 || (ov.mfma_kernel == 0 && M > 4)) && plan_ring(M, K, N, pro, p)) {
+        const bool big = int64_t(K) * N / 2 > (int64_t(12) << 20);
+        if (ov.mfma_kernel == 3 || (pro == kSwiGLU && big) || (pro == kIdentity && ring_preferred(p))) return p;
+    }
     p = GemvPlan{};
     // the kernel whose waves split K: one group per wave, SwiGLU prologue, up to about
     // 12 MB of weights (measured faster there, slower elsewhere), or when forced
@@ -1094,6 +1117,7 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
             default: return launch_col<4>(pro, a, p, s);
         }
     }
+    if (p.kind == kRing) return launch_ring(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
     if (p.kind == kKMfma) return launch_kmfma(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
     if (p.kind == kMfma) return launch_mfma(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
     SplitArgs a{};

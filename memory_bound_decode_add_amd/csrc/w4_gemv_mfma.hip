@@ -525,8 +525,16 @@ __global__ __launch_bounds__(256) void splitk_finish_swiglu_kernel(const float* 
 
 }  // namespace
 
+hipError_t launch_splitk_finish_swiglu(const float* partial, int splits, int64_t split_stride, int64_t row_stride,
+                                       int M, int I, int P, uint16_t* act, hipStream_t s) {
+    splitk_finish_swiglu_kernel<<<dim3((M * I + 255) / 256), 256, 0, s>>>(partial, splits, split_stride, row_stride, M,
+                                                                         I, P, act);
+    return hipGetLastError();
+}
+
 hipError_t launch_mfma_pair(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
                             uint16_t* act, void* ws, const GemvPlan& p, hipStream_t s) {
+    if (p.kind == kRing) return launch_ring_pair(x, qw, sc, M, K, I, act, ws, p, s);
     MfmaArgs a{};
     a.a0 = x;
     a.lda = K;
@@ -559,9 +567,7 @@ hipError_t launch_mfma_pair(const uint16_t* x, const uint32_t* qw, const uint16_
     else
         e = launch_k(w4_gemv_mfma_kernel<1, kIdentity, kWInt4, 4, true>, grid, threads, p.lds_bytes, s, a);
     if (e != hipSuccess || p.splits == 1) return e;
-    splitk_finish_swiglu_kernel<<<dim3((M * I + 255) / 256), 256, 0, s>>>(a.partial, p.splits, int64_t(p.mr) * a.npad,
-                                                                         a.npad, M, I, a.pairs, act);
-    return hipGetLastError();
+    return launch_splitk_finish_swiglu(a.partial, p.splits, int64_t(p.mr) * a.npad, a.npad, M, I, a.pairs, act, s);
 }
 
 hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
