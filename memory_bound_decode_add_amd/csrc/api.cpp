@@ -290,11 +290,16 @@ int check_chain(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d)
 // SwiGLU epilogue, and the down GEMV; the workspace holds y and then the K-slice partial
 // sums of whichever GEMV is running.
 bool layer2_fused_norm(int M) { return M <= 4; }
+// From 5 rows the workspace holds y (bf16), y as the matrix-core GEMVs stage it (written by
+// the norm kernel, copied by the row-block gate_up: fp16 [M][H] and the [M][H/128] powers of
+// two), then the K-slice partial sums of whichever GEMV is running.
+size_t staged_bytes(int M, int H) { return align_up(size_t(M) * H * 2) + align_up(size_t(M) * (H / 128) * 4); }
 size_t mlp2_ws(int M, int H, int I, const Overrides& ov) {
     if (layer2_fused_norm(M)) return align_up(size_t(M) * H * 2);
     GemvPlan pp;
     if (!plan_pair(M, H, I, ov, pp)) return 0;
-    return align_up(size_t(M) * H * 2) + std::max(pp.partial_bytes, plan_gemv(M, I, H, ov, kIdentity).partial_bytes);
+    return align_up(size_t(M) * H * 2) + staged_bytes(M, H) +
+           std::max(pp.partial_bytes, plan_gemv(M, I, H, ov, kIdentity).partial_bytes);
 }
 
 int check_layer2(const fdec_mlp_layer* L, int M, LayerDims* d, const Overrides& ov) {
@@ -340,13 +345,19 @@ hipError_t enqueue_layer2(const fdec_mlp_layer* L, int M, LayerDims d, const Ove
                           fdec_bf16* residual, fdec_bf16* act, fdec_bf16* out, void* ws, hipStream_t s) {
     if (!layer2_fused_norm(M)) {
         uint16_t* y = static_cast<uint16_t*>(ws);
-        void* pws = static_cast<char*>(ws) + align_up(size_t(M) * d.H * 2);
+        char* ys = static_cast<char*>(ws) + align_up(size_t(M) * d.H * 2);
+        float* yesc = reinterpret_cast<float*>(ys + align_up(size_t(M) * d.H * 2));
+        void* pws = static_cast<char*>(ws) + align_up(size_t(M) * d.H * 2) + staged_bytes(M, d.H);
         GemvPlan pp;
         if (!plan_pair(M, d.H, d.I, ov, pp)) return hipErrorInvalidValue;
         const GemvPlan dp = plan_gemv(M, d.I, d.H, ov, kIdentity);
-        hipError_t e = launch_add_rmsnorm(x, residual, L->norm_weight, L->eps, M, d.H, residual, y, s);
+        // the norm also writes y staged when the row-block gate_up will read it that way
+        const bool staged = pp.kind == kMfma && pp.mr == 16;
+        hipError_t e = launch_add_rmsnorm_staged(x, residual, L->norm_weight, L->eps, M, d.H, residual, y,
+                                                 staged ? ys : nullptr, staged ? yesc : nullptr, s);
         if (e != hipSuccess) return e;
-        e = launch_mfma_pair(y, L->gate_up.qweight, L->gate_up.scales, M, d.H, d.I, act, pws, pp, s);
+        e = launch_mfma_pair(y, L->gate_up.qweight, L->gate_up.scales, M, d.H, d.I, act, pws, pp, s,
+                             staged ? ys : nullptr, staged ? yesc : nullptr);
         if (e != hipSuccess) return e;
         return launch_gemv(kIdentity, act, nullptr, d.I, L->down.qweight, L->down.scales, M, d.I, d.H, L->out_scale,
                            L->residual_in_epilogue ? residual : nullptr, out, pws, dp, s);

@@ -251,4 +251,54 @@ __device__ __forceinline__ float silu_f32(float v) {
     return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
 }
 
+// ---------------------------------------------------------------------------
+// Block-scaled fp16 staging of the activation for the matrix-core GEMVs.  A k-block is 8
+// consecutive values of one row; the 16 lanes of a DPP row hold the 16 k-blocks of one
+// 128-wide group.  The group's largest magnitude mx sets a power of two 2^E that puts it
+// in [2^14, 2^15); the values are stored times 2^-E in fp16, rounded toward zero, and 2^E
+// is folded back in with the group's weight scale.  Every staging site (the GEMV kernels'
+// own, and the norm kernel writing a staged copy of its output) runs these two functions,
+// so a pre-staged activation is bit-identical to one staged by the GEMV.
+// ---------------------------------------------------------------------------
+// The group's power of two from this lane's largest magnitude: *esc = 2^E, returns 2^-E.
+// Whole wave active, the 16 lanes of each DPP row one group.
+__device__ __forceinline__ float stage_group_scale(float mx, float* esc) {
+    // magnitudes order as their bit patterns do, so the group max is an unsigned max
+    uint32_t mb = __builtin_bit_cast(uint32_t, mx);
+    mb = max(mb, dpp_u32<kQuadSwap1>(mb));
+    mb = max(mb, dpp_u32<kQuadSwap2>(mb));
+    mb = max(mb, dpp_u32<kRowRor4>(mb));
+    mb = max(mb, dpp_u32<kRowRor8>(mb));
+    int e = 0;
+    (void)__builtin_frexpf(__builtin_bit_cast(float, mb), &e);
+    const int E = min(max(e - 15, -126), 127);
+    *esc = __builtin_ldexpf(1.0f, E);
+    return __builtin_ldexpf(1.0f, -E);
+}
+
+// One k-block staged for the int4 kernels: pair order (k0, k4), (k1, k5), (k2, k6),
+// (k3, k7), the odd positions also divided by 16, matching decode_int4x8_biased.
+__device__ __forceinline__ uint4 stage_pair_order(const float (&v)[8], float down) {
+    const float down16 = down * 0.0625f;
+    return make_uint4(__builtin_bit_cast(uint32_t, pk_f16_rtz(v[0] * down, v[4] * down)),
+                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[1] * down16, v[5] * down16)),
+                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2] * down, v[6] * down)),
+                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[3] * down16, v[7] * down16)));
+}
+
+// A k-block of 8 bf16 values (one 16-byte word) staged for the int4 kernels.
+__device__ __forceinline__ uint4 stage_bf16_kblock(uint4 w, float* esc) {
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        v[2 * h] = bf16_lo(a[h]);
+        v[2 * h + 1] = bf16_hi(a[h]);
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+    return stage_pair_order(v, stage_group_scale(mx, esc));
+}
+
 }  // namespace fdec

@@ -77,9 +77,12 @@ bool plan_mfma_pair(int M, int K, int I, GemvPlan& p);
 bool plan_kmfma(int M, int K, int N, int max_gw, GemvPlan& p, const Overrides& ov = Overrides{});
 // The pair plan GEMVs run: plan_mfma_pair, or the ring kernel's when chosen (5..16 rows).
 bool plan_pair(int M, int K, int I, const Overrides& ov, GemvPlan& p);
-// Launches a pair plan of either kind.
+// Launches a pair plan of either kind.  xs / xesc: x already staged (launch_add_rmsnorm_staged's
+// layout), which the row-block kernel copies instead of staging x itself; the ring
+// kernel ignores them.
 hipError_t launch_mfma_pair(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
-                            uint16_t* act, void* ws, const GemvPlan& p, hipStream_t s);
+                            uint16_t* act, void* ws, const GemvPlan& p, hipStream_t s, const void* xs = nullptr,
+                            const float* xesc = nullptr);
 // act[m][i] = bf16(silu(g) * u) from the K slices' fp32 partials of the pairs' gate and
 // up columns (P pairs per column range: gate at range * 2P + i % P, up P further).
 hipError_t launch_splitk_finish_swiglu(const float* partial, int splits, int64_t split_stride, int64_t row_stride,
@@ -113,6 +116,10 @@ hipError_t launch_kmfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, in
 hipError_t launch_add_rmsnorm(const uint16_t* x, const uint16_t* r, const uint16_t* w,
                               float eps, int M, int H, uint16_t* h, uint16_t* y,
                               hipStream_t s);
+// The same, also writing y staged for the matrix-core GEMVs (H % 128 == 0): ys [M][H/8]
+// 16-byte k-blocks of block-scaled fp16 in pair order, yesc [M][H/128] powers of two.
+hipError_t launch_add_rmsnorm_staged(const uint16_t* x, const uint16_t* r, const uint16_t* w, float eps, int M,
+                                     int H, uint16_t* h, uint16_t* y, void* ys, float* yesc, hipStream_t s);
 // Launches plan p, which the caller made with plan_gemv(M, K, N, ...) and checked ws for.
 hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,

@@ -90,6 +90,10 @@ struct MfmaArgs {
     // pair mode (the gate_up projection with the SwiGLU epilogue): N = 2 I, y is act [M][I]
     int half_n;             // I
     int pairs;              // P: gate/up column pairs per workgroup
+    // identity prologue, int4 weights, one row block: the activation already staged by its
+    // producer ([M][K/8] k-blocks, [M][K/128] powers of two), or null
+    const uint4* st;
+    const float* stesc;
 };
 
 // One packed word -> 8 fp16 values with their offsets, in pair order: the decode every
@@ -133,27 +137,13 @@ __device__ __forceinline__ uint4 stage_item_mfma(uint4 gv, uint4 uv, float* esc,
         *esc = 1.0f;
         return make_uint4(xq[0], xq[1], xq[2], xq[3]);
     }
-    // magnitudes order as their bit patterns do, so the group max is an unsigned max
-    uint32_t mb = __builtin_bit_cast(uint32_t, mx);
-    mb = max(mb, dpp_u32<kQuadSwap1>(mb));
-    mb = max(mb, dpp_u32<kQuadSwap2>(mb));
-    mb = max(mb, dpp_u32<kRowRor4>(mb));
-    mb = max(mb, dpp_u32<kRowRor8>(mb));           // the group's largest magnitude
-    int e = 0;
-    (void)__builtin_frexpf(__builtin_bit_cast(float, mb), &e);
-    const int E = min(max(e - 15, -126), 127);
-    const float down = __builtin_ldexpf(1.0f, -E);
-    const float down16 = down * 0.0625f;
-    *esc = __builtin_ldexpf(1.0f, E);
+    const float down = stage_group_scale(mx, esc);
     if (WF == kWFp4)   // k order, as v_cvt_scalef32_pk_f16_fp4 produces the weights
         return make_uint4(__builtin_bit_cast(uint32_t, pk_f16_rtz(v[0] * down, v[1] * down)),
                           __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2] * down, v[3] * down)),
                           __builtin_bit_cast(uint32_t, pk_f16_rtz(v[4] * down, v[5] * down)),
                           __builtin_bit_cast(uint32_t, pk_f16_rtz(v[6] * down, v[7] * down)));
-    return make_uint4(__builtin_bit_cast(uint32_t, pk_f16_rtz(v[0] * down, v[4] * down)),
-                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[1] * down16, v[5] * down16)),
-                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2] * down, v[6] * down)),
-                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[3] * down16, v[7] * down16)));
+    return stage_pair_order(v, down);
 }
 
 // The A operand of one MFMA for FP4 weights: the eight values of word w times the
@@ -200,6 +190,10 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
     // banks (a stride of 32 groups put them all in one)
     const int es = a.kgroups | 1;
     float* esc_s = reinterpret_cast<float*>(act_s + kRows * rs);
+
+    // the activation already staged by its producer: identity prologue, int4 weights, one
+    // row block
+    const bool prestaged = PRO == kIdentity && WF == kWInt4 && RB == 1 && a.st != nullptr;
 
     // ---- weight and scale loads of one batch of groups (addresses clamped) ----
     auto load_batch = [&](int b, uint4 (&w)[kP][TPW], uint2 (&sv)[kP][TPW]) {
@@ -285,14 +279,56 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void w4_gemv_mfma_kernel(MfmaAr
             advance(m, kb);
         }
     };
-    for (int base = 0; base < nitems; base += UMAX * nthr) {       // uniform trip count
-        load_items(base);
-        stage_items(base);
+    if (prestaged && nkb % 64 == 0) {
+        // a pre-staged slice whose rows are whole 1 KB pieces: the first weights, the
+        // slice's powers of two (into registers), then direct-to-LDS loads of the slice (wave
+        // load q copies k-blocks 64 q .. 64 q + 63 of the flattened [row][k-block] slice,
+        // which stay inside one row): all in flight together, one barrier after them all.
+        // (Loading the powers of two with each weight batch instead, straight into
+        // registers, measured 8 us slower on the 16-row layer's gate_up.)
+        load_batch(0, wA, sA);
+        float ev[2];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {                // kRows * ng <= 16 * 36 <= 2 * 384
+            const int i = tid + it * nthr, m = i / ng, g = i - m * ng;
+            ev[it] = i < kRows * ng ? a.stesc[size_t(min(m, a.M - 1)) * (a.K / 128) + g0 + g] : 0.f;
+        }
+        const int W = blockDim.x >> 6;
+        const int rows_per = nkb / 64;                 // 1 KB loads per row
+        for (int q = __builtin_amdgcn_readfirstlane(wave); q < kRows * rows_per; q += W) {
+            const int m = q / rows_per, kb0 = 64 * (q - m * rows_per);
+            __builtin_amdgcn_global_load_lds(a.st + size_t(min(m, a.M - 1)) * (a.K / 8) + g0 * 16 + kb0 + lane,
+                                             (__attribute__((address_space(3))) void*)(act_s + m * rs + kb0), 16, 0,
+                                             0);
+        }
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int i = tid + it * nthr, m = i / ng, g = i - m * ng;
+            if (i < kRows * ng) esc_s[m * es + g] = ev[it];
+        }
+        __syncthreads();
+    } else if (prestaged) {
+        // a pre-staged slice of any length: copied through registers
+        for (int i = tid; i < nitems; i += nthr) {
+            const int m = i / nkb, kb = i - m * nkb;
+            act_s[m * rs + kb] = a.st[size_t(min(m, a.M - 1)) * (a.K / 8) + g0 * 16 + kb];
+        }
+        for (int i = tid; i < kRows * ng; i += nthr) {
+            const int m = i / ng, g = i - m * ng;
+            esc_s[m * es + g] = a.stesc[size_t(min(m, a.M - 1)) * (a.K / 128) + g0 + g];
+        }
+        load_batch(0, wA, sA);
+        __syncthreads();
+    } else {
+        for (int base = 0; base < nitems; base += UMAX * nthr) {       // uniform trip count
+            load_items(base);
+            stage_items(base);
+        }
+        // the first weights are requested only now: issued earlier, they would sit ahead of
+        // the activation loads in the CU's memory queue and every staging wait would cover them
+        load_batch(0, wA, sA);
+        __syncthreads();
     }
-    // the first weights are requested only now: issued earlier, they would sit ahead of
-    // the activation loads in the CU's memory queue and every staging wait would cover them
-    load_batch(0, wA, sA);
-    __syncthreads();
 
     // ---- main loop: batches of kP groups, next batch's loads in flight ----
     f32x4_t out[RB][TPW];
@@ -533,9 +569,12 @@ hipError_t launch_splitk_finish_swiglu(const float* partial, int splits, int64_t
 }
 
 hipError_t launch_mfma_pair(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, int M, int K, int I,
-                            uint16_t* act, void* ws, const GemvPlan& p, hipStream_t s) {
+                            uint16_t* act, void* ws, const GemvPlan& p, hipStream_t s, const void* xs,
+                            const float* xesc) {
     if (p.kind == kRing) return launch_ring_pair(x, qw, sc, M, K, I, act, ws, p, s);
     MfmaArgs a{};
+    a.st = p.mr == 16 ? static_cast<const uint4*>(xs) : nullptr;
+    a.stesc = xesc;
     a.a0 = x;
     a.lda = K;
     a.qw = reinterpret_cast<const uint4*>(qw);

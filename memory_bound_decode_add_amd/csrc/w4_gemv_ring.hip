@@ -149,22 +149,7 @@ __device__ __forceinline__ uint4 stage8(uint4 gv, uint4 uv, float* esc) {
     float mx = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
-    // magnitudes order as their bit patterns do: the group max is an unsigned max
-    uint32_t mb = __builtin_bit_cast(uint32_t, mx);
-    mb = max(mb, dpp_u32<kQuadSwap1>(mb));
-    mb = max(mb, dpp_u32<kQuadSwap2>(mb));
-    mb = max(mb, dpp_u32<kRowRor4>(mb));
-    mb = max(mb, dpp_u32<kRowRor8>(mb));
-    int e = 0;
-    (void)__builtin_frexpf(__builtin_bit_cast(float, mb), &e);
-    const int E = min(max(e - 15, -126), 127);
-    const float down = __builtin_ldexpf(1.0f, -E);
-    const float down16 = down * 0.0625f;
-    *esc = __builtin_ldexpf(1.0f, E);
-    return make_uint4(__builtin_bit_cast(uint32_t, pk_f16_rtz(v[0] * down, v[4] * down)),
-                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[1] * down16, v[5] * down16)),
-                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[2] * down, v[6] * down)),
-                      __builtin_bit_cast(uint32_t, pk_f16_rtz(v[3] * down16, v[7] * down16)));
+    return stage_pair_order(v, stage_group_scale(mx, esc));
 }
 
 // The lane's fixed parts of its loads: byte offsets from per-step bases.

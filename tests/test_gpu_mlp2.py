@@ -197,6 +197,26 @@ def test_mlp_decode2_matrix_core_both_residual_modes(M, H, I):
         say(f"  resid={resid} worst err/bound (y, act, out)", check_layer2_mc(inp.layers[0], inp.x, inp.r, got, resid))
 
 
+@pytest.mark.parametrize("M,H,I", [(16, 4096, 14336), (5, 4096, 1152), (12, 3584, 2048), (8, 1024, 2048)])
+def test_mlp_decode2_gate_up_reads_the_norms_staged_copy(M, H, I):
+    # From 5 rows the norm kernel also writes y as the matrix-core GEMVs stage it, and the
+    # row-block gate_up copies that instead of staging y itself; its act must be bit-identical
+    # to the standalone gate_up's on the same y (which stages y itself).  At H = 1024 the
+    # gate_up runs on the ring kernel, which stages from y either way.
+    say(f"[mlp2, staged y] M={M} H={H} I={I}")
+    inp = synth.mlp_inputs(M, H, I, n_layers=1, seed=M * 5 + H + I)
+    layer = dev_layers(inp, True)[0]
+    b = F.Mlp2Buffers.empty(M, H, I)
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    ws = torch.full((F.mlp2_workspace_bytes(M, H, I),), 0xFF, dtype=torch.uint8, device="cuda")
+    F.mlp_decode2(layer, b, ws)
+    torch.cuda.synchronize()
+    y = ws[: M * H * 2].view(torch.int16).view(torch.bfloat16).reshape(M, H).clone()
+    act = F.to_bits(F.w4_gemv_swiglu(y, layer.gate_up))
+    assert_bits_equal(F.to_bits(b.act), act, "act: staged copy vs staged by the gate_up itself")
+
+
 def test_chain2_matrix_core_graph():
     M, H, I, n = 16, 512, 1024, 4
     say(f"[chain2, matrix cores] M={M} H={H} I={I}, {n} layers: every layer, graph == eager")
