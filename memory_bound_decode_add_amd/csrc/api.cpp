@@ -215,15 +215,23 @@ int check_layer(const fdec_mlp_layer* L, int M, LayerDims* d) {
 
 // The two GEMV plans of a layer, made once per call: the workspace is checked against
 // them and they are what gets launched.
+// y as the matrix-core GEMVs stage it (written by the norm kernel, copied by a row-block
+// gate_up): fp16 [M][H] and the [M][H/128] powers of two.
+size_t staged_bytes(int M, int H) { return align_up(size_t(M) * H * 2) + align_up(size_t(M) * (H / 128) * 4); }
+
+// Workspace of the three-kernel layer: y staged (when the gate_up runs on the row-block
+// kernel at 5..16 rows), then the K-slice partial sums of whichever GEMV is running.
 struct LayerPlan {
     GemvPlan gu, dn;
+    bool staged;
     size_t ws;
 };
 LayerPlan plan_layer(int M, int H, int I, const Overrides& ov) {
     LayerPlan lp;
     lp.gu = plan_gemv(M, H, 2 * I, ov, kIdentity);
     lp.dn = plan_gemv(M, I, H, ov, kSwiGLU);
-    lp.ws = std::max(lp.gu.partial_bytes, lp.dn.partial_bytes);
+    lp.staged = lp.gu.kind == kMfma && lp.gu.mr == 16 && M > 4;
+    lp.ws = (lp.staged ? staged_bytes(M, H) : 0) + std::max(lp.gu.partial_bytes, lp.dn.partial_bytes);
     return lp;
 }
 size_t mlp_ws(int M, int H, int I) { return plan_layer(M, H, I, Overrides{}).ws; }
@@ -256,13 +264,17 @@ int check_layer_buffers(const fdec_mlp_layer* L, int M, LayerDims d, const fdec_
 hipError_t enqueue_layer(const fdec_mlp_layer* L, int M, LayerDims d, const LayerPlan& lp, const fdec_bf16* x,
                          fdec_bf16* residual, fdec_bf16* y_norm, fdec_bf16* gate_up, fdec_bf16* out,
                          void* ws, hipStream_t s) {
-    hipError_t e = launch_add_rmsnorm(x, residual, L->norm_weight, L->eps, M, d.H, residual, y_norm, s);
+    char* ys = lp.staged ? static_cast<char*>(ws) : nullptr;
+    float* yesc = lp.staged ? reinterpret_cast<float*>(ys + align_up(size_t(M) * d.H * 2)) : nullptr;
+    void* pws = lp.staged ? static_cast<void*>(static_cast<char*>(ws) + staged_bytes(M, d.H)) : ws;
+    hipError_t e = launch_add_rmsnorm_staged(x, residual, L->norm_weight, L->eps, M, d.H, residual, y_norm, ys,
+                                             yesc, s);
     if (e != hipSuccess) return e;
     e = launch_gemv(kIdentity, y_norm, nullptr, d.H, L->gate_up.qweight, L->gate_up.scales, M, d.H, 2 * d.I,
-                    nullptr, nullptr, gate_up, ws, lp.gu, s);
+                    nullptr, nullptr, gate_up, pws, lp.gu, s, ys, yesc);
     if (e != hipSuccess) return e;
     return launch_gemv(kSwiGLU, gate_up, gate_up + d.I, 2 * int64_t(d.I), L->down.qweight, L->down.scales, M,
-                       d.I, d.H, L->out_scale, L->residual_in_epilogue ? residual : nullptr, out, ws, lp.dn, s);
+                       d.I, d.H, L->out_scale, L->residual_in_epilogue ? residual : nullptr, out, pws, lp.dn, s);
 }
 
 int check_chain(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d) {
@@ -290,10 +302,8 @@ int check_chain(const fdec_mlp_layer* layers, int n_layers, int M, LayerDims* d)
 // SwiGLU epilogue, and the down GEMV; the workspace holds y and then the K-slice partial
 // sums of whichever GEMV is running.
 bool layer2_fused_norm(int M) { return M <= 4; }
-// From 5 rows the workspace holds y (bf16), y as the matrix-core GEMVs stage it (written by
-// the norm kernel, copied by the row-block gate_up: fp16 [M][H] and the [M][H/128] powers of
-// two), then the K-slice partial sums of whichever GEMV is running.
-size_t staged_bytes(int M, int H) { return align_up(size_t(M) * H * 2) + align_up(size_t(M) * (H / 128) * 4); }
+// From 5 rows the workspace holds y (bf16), y staged (as above), then the K-slice partial
+// sums of whichever GEMV is running.
 size_t mlp2_ws(int M, int H, int I, const Overrides& ov) {
     if (layer2_fused_norm(M)) return align_up(size_t(M) * H * 2);
     GemvPlan pp;

@@ -121,10 +121,14 @@ hipError_t launch_add_rmsnorm(const uint16_t* x, const uint16_t* r, const uint16
 hipError_t launch_add_rmsnorm_staged(const uint16_t* x, const uint16_t* r, const uint16_t* w, float eps, int M,
                                      int H, uint16_t* h, uint16_t* y, void* ys, float* yesc, hipStream_t s);
 // Launches plan p, which the caller made with plan_gemv(M, K, N, ...) and checked ws for.
+// xs / xesc: with the identity prologue, a0 already staged (launch_add_rmsnorm_staged's
+// layout), which a row-block plan at 5..16 rows copies instead of staging a0 itself;
+// other plans ignore them.
 hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
-                       void* ws, const GemvPlan& p, hipStream_t s);
+                       void* ws, const GemvPlan& p, hipStream_t s, const void* xs = nullptr,
+                       const float* xesc = nullptr);
 // The fused layer's two kernels (column kernel only).
 bool norm_gemv_swiglu_supported(int M, int K, int I);
 hipError_t launch_norm_gemv_swiglu(const uint16_t* x, const uint16_t* r, const uint16_t* nw, float eps,
@@ -137,7 +141,8 @@ hipError_t launch_gemv_copy(Prologue pro, const uint16_t* a0, int64_t lda, const
 hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
-                       void* ws, const GemvPlan& p, hipStream_t s);
+                       void* ws, const GemvPlan& p, hipStream_t s, const void* xs = nullptr,
+                       const float* xesc = nullptr);
 // FP4 (E2M1) weights with E4M3 1x16 block scales: M = 1..4 (K % 32 == 0, K <= 16384)
 // on the chunk-owning kernel, M = 5..64 (K % 128 == 0) on the matrix-core kernel.  With
 // gscale (the activation's per-tensor scale, device fp32) the activation is quantised to

@@ -1092,7 +1092,7 @@ hipError_t launch_splitk_finish(const float* partial, int splits, int64_t split_
 hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
-                       void* ws, const GemvPlan& p, hipStream_t s) {
+                       void* ws, const GemvPlan& p, hipStream_t s, const void* xs, const float* xesc) {
     if (p.kind == kColumnOwning) {
         ColArgs a{};
         a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};
@@ -1119,7 +1119,8 @@ hipError_t launch_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int
     }
     if (p.kind == kRing) return launch_ring(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
     if (p.kind == kKMfma) return launch_kmfma(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
-    if (p.kind == kMfma) return launch_mfma(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s);
+    if (p.kind == kMfma)
+        return launch_mfma(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, p, s, xs, xesc);
     SplitArgs a{};
     a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};
     a.a0 = a0;

@@ -495,9 +495,12 @@ template <int WF>
 hipError_t launch_mfma_wf(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
                           const uint16_t* sc, const uint8_t* sc8, int M, int K, int N, const float* out_scale,
                           const uint16_t* residual, uint16_t* y, void* ws, const GemvPlan& p, hipStream_t s,
-                          const float* gscale = nullptr) {
+                          const float* gscale = nullptr, const void* xs = nullptr, const float* xesc = nullptr) {
     MfmaArgs a{};
     a.gscale = gscale;
+    // a pre-staged activation: identity prologue, int4 weights, one row block
+    a.st = WF == kWInt4 && pro == kIdentity && p.mr == 16 ? static_cast<const uint4*>(xs) : nullptr;
+    a.stesc = xesc;
     a.a0 = a0;
     a.a1 = a1;
     a.lda = lda;
@@ -612,8 +615,9 @@ hipError_t launch_mfma_pair(const uint16_t* x, const uint32_t* qw, const uint16_
 hipError_t launch_mfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,
                        const uint32_t* qw, const uint16_t* sc, int M, int K, int N,
                        const float* out_scale, const uint16_t* residual, uint16_t* y,
-                       void* ws, const GemvPlan& p, hipStream_t s) {
-    return launch_mfma_wf<kWInt4>(pro, a0, a1, lda, qw, sc, nullptr, M, K, N, out_scale, residual, y, ws, p, s);
+                       void* ws, const GemvPlan& p, hipStream_t s, const void* xs, const float* xesc) {
+    return launch_mfma_wf<kWInt4>(pro, a0, a1, lda, qw, sc, nullptr, M, K, N, out_scale, residual, y, ws, p, s,
+                                  nullptr, xs, xesc);
 }
 
 hipError_t launch_mfma_fp4(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda,

@@ -51,6 +51,25 @@ def test_mlp_layer_llama3_8b_m16():
     say("  worst err/bound (y, gu, out)", check_layer(inp.layers[0], inp.x, inp.r, got, True))
 
 
+@pytest.mark.parametrize("M,H,I", [(16, 4096, 14336), (5, 4096, 1152), (12, 3584, 2048), (8, 1024, 2048)])
+def test_mlp_layer_gate_up_reads_the_norms_staged_copy(M, H, I):
+    # From 5 rows the norm kernel also writes y staged for the matrix cores, and a row-block
+    # gate_up copies that instead of staging y itself: gate_up must be bit-identical to the
+    # standalone GEMV's on the same y_norm (which stages it itself).  At H = 1024 the
+    # gate_up runs on the ring kernel, which stages from y_norm either way.
+    say(f"[mlp, staged y] M={M} H={H} I={I}")
+    inp = synth.mlp_inputs(M, H, I, n_layers=1, seed=M * 7 + H + I)
+    layer = dev_layers(inp, True)[0]
+    b = F.MlpBuffers.empty(M, H, I)
+    b.x.copy_(F.from_bits(inp.x))
+    b.residual.copy_(F.from_bits(inp.r))
+    ws = torch.full((max(16, F.mlp_workspace_bytes(M, H, I)),), 0xFF, dtype=torch.uint8, device="cuda")
+    F.mlp_decode(layer, b, ws)
+    torch.cuda.synchronize()
+    gu = F.to_bits(F.w4_gemv(b.y_norm.clone(), layer.gate_up))
+    assert_bits_equal(F.to_bits(b.gate_up), gu, "gate_up: staged copy vs staged by the GEMV itself")
+
+
 @pytest.mark.parametrize("M,H,I", [(1, 256, 384), (3, 512, 640), (16, 384, 256)])
 def test_mlp_layer_small_shapes_both_residual_modes(M, H, I):
     say(f"[mlp] M={M} H={H} I={I}")
