@@ -13,9 +13,9 @@ rotation of the sets) and timed with HIP events on the stream they run on.
 The JSON line on stdout reports achieved algorithmic GB/s (the job's bytes over the
 time) and its fraction of MI355X's 8 TB/s HBM peak, the fp64 CPU oracle timed on this
 host on a bounded sample, and, unless --only gemv, the other workloads: residual add +
-RMSNorm at 8192 x 4096, the 16-row Llama-3-8B-sized MLP layer, the 28-layer
-Qwen2.5-1.5B-sized MLP chain (eager and as one hipGraph), the unfused sequences and a
-plain copy kernel.
+RMSNorm at 8192 x 4096, the 16-row Llama-3-8B-sized MLP layer, a 16-row
+Qwen2.5-1.5B-shaped layer, the 28-layer Qwen2.5-1.5B-sized MLP chain (eager and as one
+hipGraph), the unfused sequences and a plain copy kernel.
 """
 from __future__ import annotations
 
@@ -407,6 +407,34 @@ def bench_extras(torch, F, synth, n_sets_gemv):
     out["w4_gemv_swiglu_16x4096x14336"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9,
                                             "frac_of_peak": b / t / 1e9 / PEAK_GBPS, "bytes_per_call": b}
     del layers, bufs, wsm, wsu, b2, ws2, yb, wsp
+
+    # one Qwen2.5-1.5B-shaped layer at 16 rows (H=1536, I=8960: short K, where the GEMVs run
+    # on the kernel fed by direct-to-LDS loads), both layer forms, 6 rotating weight sets
+    M16, H16, I16 = 16, 1536, 8960
+    log(f"[bench] MLP layer M={M16} H={H16} I={I16}")
+    layers = []
+    for i in range(6):
+        L = synth.mlp_inputs(M16, H16, I16, 1, seed=50 + i, out_scale=1.0).layers[0]
+        layers.append(F.MlpLayer(F.from_bits(L.norm_w), F.W4Weight.from_numpy(L.gate_up.qweight, L.gate_up.scales),
+                                 F.W4Weight.from_numpy(L.down.qweight, L.down.scales), F.scalar(L.out_scale),
+                                 L.eps, True))
+    gen = torch.Generator().manual_seed(16)
+    xq = torch.randn(M16, H16, generator=gen).to(torch.bfloat16).cuda()
+    bufs = F.MlpBuffers.empty(M16, H16, I16)
+    bufs.x.copy_(xq)
+    bufs.residual.copy_(xq)
+    wsm = F.workspace(F.mlp_workspace_bytes(M16, H16, I16))
+    t = bench_repeat(torch, timer, [lambda L=L: F.mlp_decode(L, bufs, wsm) for L in layers], 10) / len(layers)
+    b = T.mlp_layer_bytes(M16, H16, I16, True)
+    out["mlp_qwen2_5_1_5b_m16"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS}
+    b2 = F.Mlp2Buffers.empty(M16, H16, I16)
+    b2.x.copy_(xq)
+    b2.residual.copy_(xq)
+    ws2 = F.workspace(F.mlp2_workspace_bytes(M16, H16, I16))
+    t = bench_repeat(torch, timer, [lambda L=L: F.mlp_decode2(L, b2, ws2) for L in layers], 10) / len(layers)
+    b = T.mlp2_layer_bytes(M16, H16, I16, True)
+    out["mlp2_qwen2_5_1_5b_m16"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS}
+    del layers, bufs, wsm, b2, ws2, xq
 
     # Qwen2.5-1.5B-sized MLP chain, 28 layers: eager chain vs one hipGraph
     c = synth.CONFIGS["mlp_qwen2_5_1_5b_28l"]

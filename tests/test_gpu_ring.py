@@ -35,7 +35,7 @@ def nan_ws(nbytes=BIG_WS):
 # N = 1000 and 264 end in a partial tile, 520 in a partial column range; 9216 x 2560 is
 # the metric's shape at 16 rows (12 slices); 14336 x 4096 the 16-row layer's down (8).
 SHAPES = [(5, 4224, 1000), (8, 1024, 264), (12, 4224, 520), (16, 9216, 2560), (16, 14336, 4096), (16, 256, 128),
-          (7, 128, 1032), (16, 4096, 28672)]
+          (7, 128, 1032), (16, 4096, 28672), (1, 2048, 776), (3, 4224, 264)]   # forced below 5 rows too
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
