@@ -578,14 +578,16 @@ def profile_calls(torch, F, synth):
     """A few eager calls of each kernel family, for hardware-counter runs:
     - the column kernel at the metric's shape (M=1, K=9216, N=2560, SwiGLU);
     - the matrix-core kernels at 16 rows: the kernel whose waves split K (K=9216, N=2560,
-      SwiGLU) and the row-block kernel on the Llama-3-8B-sized projections (gate_up
-      K=4096, N=28672, identity; down K=14336, N=4096, SwiGLU, with its finish kernel);
+      SwiGLU), the row-block kernel on the Llama-3-8B-sized gate_up (K=4096, N=28672,
+      identity) and the ring kernel on its down projection (K=14336, N=4096, SwiGLU, with
+      its finish kernel) and on the Qwen2.5-1.5B-sized gate_up (K=1536, N=17920, identity);
     - the gate_up projection with the SwiGLU epilogue (M=16, K=4096, I=14336, pair mode);
-    - the FP4 kernels at M=1 and 16 (K=9216, N=2560);
+    - the FP4 kernels at M=1 and 16 (K=9216, N=2560), with FP4 weights and with both
+      operands FP4;
     - the prefill point: the SwiGLU pass and the W4 GEMM at 2048 x 9216 x 2560."""
     sc = F.scalar(0.5)
     for M, K, N, pro, n in ((1, 9216, 2560, "swiglu", 24), (16, 9216, 2560, "swiglu", 24),
-                            (16, 4096, 28672, "id", 4), (16, 14336, 4096, "swiglu", 4)):
+                            (16, 4096, 28672, "id", 4), (16, 14336, 4096, "swiglu", 4), (16, 1536, 17920, "id", 8)):
         sets = []
         for i in range(n):
             inp = synth.swiglu_gemv_inputs(M, K, N, seed=i)
@@ -618,8 +620,11 @@ def profile_calls(torch, F, synth):
         W = F.FP4Weight.from_numpy(inp.W.qweight, inp.W.scales)
         y = torch.empty((M, 2560), dtype=torch.bfloat16, device="cuda")
         ws = F.workspace(F.fp4_gemv_workspace_bytes(M, 9216, 2560))
+        gsc = F.scalar(F.swiglu(g, u).float().abs().max().item() / (6.0 * 448.0))
         for _ in range(8):
             F.swiglu_fp4_gemv(g, u, W, sc, out=y, ws=ws)
+        for _ in range(8):
+            F.swiglu_fp4a4_gemv(g, u, W, gsc, sc, out=y, ws=ws)
     torch.cuda.synchronize()
     M, K, N = 2048, 9216, 2560
     inp = synth.swiglu_gemv_inputs(1, K, N, seed=0)
