@@ -244,7 +244,7 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     const int W = (blockDim.x >> 6) - S;           // dot waves
     const int C = a.cols;                          // columns per workgroup (2 * pairs with PAIR)
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: slot tests branch on scalars
     const int lane = tid & 63;
     const int nblk = (a.K + 511) >> 9;             // 512-wide staging blocks
     const int qs = col_quarter_stride(a.nch);      // halves
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int c = lane + kWave * i;
-        if (c < a.nch) {
+        if (i < NI - 1 || c < a.nch) {             // only the last range can pass K (NI = ceil(nch / 64))
             uint4 av[MR][4];
             float2 eb[MR];
 #pragma unroll
@@ -701,8 +701,10 @@ hipError_t launch(Kern k, dim3 grid, int threads, size_t lds, hipStream_t s, con
     return hipGetLastError();
 }
 
+// The kernels take every chunk range but the last as inside K: NI must be ceil(nch / 64).
 template <int MR, int CPW, int NI>
 hipError_t launch_col3(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStream_t s) {
+    if (p.ni != NI) return hipErrorInvalidValue;
     if (pro == kSwiGLU)
         return launch(w4_gemv_col_kernel<MR, CPW, NI, kSwiGLU>, dim3(p.wgs), (p.stagers + p.waves) * kWave, p.lds_bytes,
                       s, a);
@@ -755,6 +757,7 @@ hipError_t launch_col(Prologue pro, const ColArgs& a, const GemvPlan& p, hipStre
 // Pair mode (add + RMSNorm prologue, SwiGLU pair epilogue): even slot counts only.
 template <int MR, int CPW, int NI>
 hipError_t launch_pair3(const ColArgs& a, const GemvPlan& p, hipStream_t s) {
+    if (p.ni != NI) return hipErrorInvalidValue;
     return launch(w4_gemv_col_kernel<MR, CPW, NI, kAddRmsNorm>, dim3(p.wgs), (p.stagers + p.waves) * kWave,
                   p.lds_bytes, s, a);
 }
