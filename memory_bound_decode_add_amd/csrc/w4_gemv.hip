@@ -157,14 +157,13 @@ struct ColArgs {
 __device__ __forceinline__ int col_quarter_stride(int nch) { return nch * 8 + 32; }
 
 // Eight activation values k = 8w + j (j = 0..7) of one lane -> LDS (see above).
-__device__ __forceinline__ void stage_values_col(float (&v)[8], bool live, bool in_k, bool quad_lead,
+// Lanes past K (a quad is wholly inside or outside) store nothing; rows past M stage
+// copies of row M - 1 (clamped loads), whose sums no lane stores: neither is zeroed.
+__device__ __forceinline__ void stage_values_col(float (&v)[8], bool in_k, bool quad_lead,
                                                  _Float16* dst, float2* eb_dst) {
     float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        v[j] = live ? v[j] : 0.f;
-        mx = fmaxf(mx, fabsf(v[j]));
-    }
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
     mx = fmaxf(mx, dpp<kQuadSwap1>(mx));
     mx = fmaxf(mx, dpp<kQuadSwap2>(mx));           // the chunk's largest magnitude
     int e = 0;
@@ -192,8 +191,8 @@ __device__ __forceinline__ void stage_values_col(float (&v)[8], bool live, bool 
 }
 
 template <int PRO>
-__device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, bool live, bool in_k,
-                                               bool quad_lead, _Float16* dst, float2* eb_dst) {
+__device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, bool in_k, bool quad_lead,
+                                               _Float16* dst, float2* eb_dst) {
     float v[8];                                    // k = 8w + j, j = 0..7
     const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
     const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
@@ -207,7 +206,7 @@ __device__ __forceinline__ void stage_word_col(const uint4 gv, const uint4 uv, b
             v[2 * h + 1] = bf16_hi(gw[h]);
         }
     }
-    stage_values_col(v, live, in_k, quad_lead, dst, eb_dst);
+    stage_values_col(v, in_k, quad_lead, dst, eb_dst);
 }
 
 // Sum over a full wave (all 64 lanes active), returned uniform, in a fixed order.
@@ -360,7 +359,7 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
                     v[2 * h] = bf16_lo(hw[h]) * rs * bf16_lo(ww[h]);
                     v[2 * h + 1] = bf16_hi(hw[h]) * rs * bf16_hi(ww[h]);
                 }
-                stage_values_col(v, in_k && m < a.M, in_k, (lane & 3) == 0,
+                stage_values_col(v, in_k, (lane & 3) == 0,
                                  act_s + size_t(m) * 4 * qs + lofs + b * 128,
                                  eb_s + m * a.nch + b * 16 + (lane >> 2));
             }
@@ -371,7 +370,7 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
                 if (t >= ntask) break;             // uniform across the wave
                 const int m = t % MR, b = t / MR;
                 const bool in_k = b * 64 + lane < kw;  // a chunk lies wholly inside or outside K
-                stage_word_col<PRO>(ga[ti], ua[ti], in_k && m < a.M, in_k, (lane & 3) == 0,
+                stage_word_col<PRO>(ga[ti], ua[ti], in_k, (lane & 3) == 0,
                                     act_s + size_t(m) * 4 * qs + lofs + b * 128,
                                     eb_s + m * a.nch + b * 16 + (lane >> 2));
             }
@@ -435,19 +434,27 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int j = 0; j < CPW; ++j) acc[m][j] = 0.f;
+    // the activation of range i + 1 is read from LDS while range i is worked
+    uint4 avb[2][MR][4];
+    float2 ebb[2][MR];
+    auto read_act = [&](int i, int b) {
+        const int c = min(lane + kWave * i, a.nch - 1);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const _Float16* arow = act_s + size_t(m) * 4 * qs + c * 8;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) avb[b][m][h] = *reinterpret_cast<const uint4*>(arow + h * qs);
+            ebb[b][m] = eb_s[m * a.nch + c];
+        }
+    };
+    read_act(0, 0);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+        if (i + 1 < NI) read_act(i + 1, (i + 1) & 1);
         const int c = lane + kWave * i;
         if (i < NI - 1 || c < a.nch) {             // only the last range can pass K (NI = ceil(nch / 64))
-            uint4 av[MR][4];
-            float2 eb[MR];
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                const _Float16* arow = act_s + size_t(m) * 4 * qs + c * 8;
-#pragma unroll
-                for (int h = 0; h < 4; ++h) av[m][h] = *reinterpret_cast<const uint4*>(arow + h * qs);
-                eb[m] = eb_s[m * a.nch + c];
-            }
+            const uint4 (&av)[MR][4] = avb[i & 1];
+            const float2 (&eb)[MR] = ebb[i & 1];
 #pragma unroll
             for (int j = 0; j < CPW; ++j) {
                 if (!slot_ok(j)) break;            // uniform
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(256) void w4_gemv_split_kernel(SplitArgs a) {
     float* red_s = esc_s + GPS * MR;                                      // [4][MR][64]
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int tile = blockIdx.x % a.tiles;
     const int split = blockIdx.x / a.tiles;
