@@ -25,6 +25,7 @@ constexpr int kColMaxWaves = 14;     // dot waves per workgroup, column kernel (
 constexpr int kColMaxChunks = 8;
 constexpr int kColScLoads = 4;       // 16-byte scale loads per thread, column kernel     // 32-wide K chunks per lane, column kernel
 constexpr size_t kMaxLds = 160 * 1024;
+constexpr int kFinishBatch = 16;     // K slices a finish kernel requests at once
 
 enum GemvKind { kColumnOwning = 0, kSplitK = 1, kMfma = 2, kKMfma = 3, kRing = 4 };
 constexpr int kMfmaWaves = 8;       // waves per workgroup, matrix-core kernel

@@ -554,10 +554,21 @@ __global__ __launch_bounds__(256) void splitk_finish_swiglu_kernel(const float* 
     const int m = o / I, i = o % I;
     const float* pg = partial + m * row_stride + size_t(i / P) * 2 * P + i % P;
     const float* pu = pg + P;
+    // every slice of a batch requested before the first is used (one memory round trip
+    // per kFinishBatch slices, not one per slice); sums in slice order
     float g = 0.f, u = 0.f;
-    for (int sl = 0; sl < splits; ++sl) {
-        g += pg[sl * split_stride];
-        u += pu[sl * split_stride];
+    for (int s0 = 0; s0 < splits; s0 += kFinishBatch) {
+        float tg[kFinishBatch], tu[kFinishBatch];
+#pragma unroll
+        for (int b = 0; b < kFinishBatch; ++b) {
+            tg[b] = s0 + b < splits ? pg[(s0 + b) * split_stride] : 0.f;
+            tu[b] = s0 + b < splits ? pu[(s0 + b) * split_stride] : 0.f;
+        }
+#pragma unroll
+        for (int b = 0; b < kFinishBatch; ++b) {
+            g += tg[b];
+            u += tu[b];
+        }
     }
     act[o] = f32_to_bf16(silu_f32(g) * u);
 }
