@@ -42,6 +42,10 @@ FDEC_API void fdec_test_fail_launches(int32_t on);
  *   kernel fed by direct-to-LDS loads of every operand (also the pair-mode gate_up of
  *   fdec_w4_gemv_swiglu and of the 16-row layer). */
 FDEC_API void fdec_set_mfma_plan(int32_t kernel, int32_t tiles, int32_t groups_per_wave);
+/* fdec_set_kmfma_waves(waves): waves per workgroup (6..8) of the kernel whose waves split
+ *   K, each wave taking its own groups of the workgroup's K slice; 0 (or any other value)
+ *   leaves the built-in choice. */
+FDEC_API void fdec_set_kmfma_waves(int32_t waves);
 
 /* Workspace sizes under the overrides active now (equal to the fdec.h queries when none
  * is): fdec_test_gemv_workspace_bytes for fdec_swiglu_w4_gemv / fdec_w4_gemv,

@@ -124,6 +124,7 @@ _SIGS = {
     "fdec_set_gemv_tiling": (None, [_i32, _i32]),
     "fdec_test_fail_launches": (None, [_i32]),
     "fdec_set_mfma_plan": (None, [_i32, _i32, _i32]),
+    "fdec_set_kmfma_waves": (None, [_i32]),
     "fdec_test_gemv_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "fdec_test_mlp_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "fdec_test_empty_kernel": (ctypes.c_int, [_i32, _i32, _c_p]),
@@ -893,18 +894,25 @@ def fp4_dequant(W: FP4Weight) -> torch.Tensor:
 # test, tuning and measurement controls (include/fdec_test.h; not for production use)
 # ----------------------------------------------------------------------------
 _overrides_active = False
-_override_state = {"split": 0, "tiling": (0, 0), "mfma": (0, 0, 0)}
+_override_state = {"split": 0, "tiling": (0, 0), "mfma": (0, 0, 0), "kmfma_waves": 0}
 
 
 def _note_overrides():
     global _overrides_active
     _overrides_active = (_override_state["split"] != 0 or _override_state["tiling"] != (0, 0)
-                         or _override_state["mfma"] != (0, 0, 0))
+                         or _override_state["mfma"] != (0, 0, 0) or _override_state["kmfma_waves"] != 0)
 
 
 def set_mfma_plan(kernel: int, tiles: int = 0, groups_per_wave: int = 0):
     lib().fdec_set_mfma_plan(int(kernel), int(tiles), int(groups_per_wave))
     _override_state["mfma"] = (int(kernel), int(tiles), int(groups_per_wave))
+    _note_overrides()
+
+
+def set_kmfma_waves(waves: int):
+    """Waves per workgroup (6..8) of the matrix-core kernel whose waves split K; 0: built in."""
+    lib().fdec_set_kmfma_waves(int(waves))
+    _override_state["kmfma_waves"] = int(waves) if 6 <= int(waves) <= 8 else 0
     _note_overrides()
 
 

@@ -30,6 +30,7 @@ std::atomic<int> g_col_cols{0};
 std::atomic<int> g_mfma_kernel{0};
 std::atomic<int> g_mfma_tiles{0};
 std::atomic<int> g_mfma_gw{0};
+std::atomic<int> g_mfma_waves{0};
 
 constexpr size_t kAlign = 256;   // sub-buffer alignment inside workspaces
 
@@ -430,6 +431,7 @@ Overrides current_overrides() {
     ov.mfma_kernel = g_mfma_kernel.load();
     ov.mfma_tiles = g_mfma_tiles.load();
     ov.mfma_gw = g_mfma_gw.load();
+    ov.mfma_waves = g_mfma_waves.load();
     return ov;
 }
 }  // namespace fdec
@@ -571,6 +573,8 @@ FDEC_API void fdec_set_mfma_plan(int32_t kernel, int32_t tiles, int32_t groups_p
     g_mfma_tiles.store(tiles == 4 || tiles == 8 ? tiles : 0);
     g_mfma_gw.store(groups_per_wave >= 1 && groups_per_wave <= 4 ? groups_per_wave : 0);
 }
+
+FDEC_API void fdec_set_kmfma_waves(int32_t waves) { g_mfma_waves.store(waves >= 6 && waves <= 8 ? waves : 0); }
 
 FDEC_API size_t fdec_test_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) {
     if (!w4_gemv_shape_ok(M, K, N)) return 0;

@@ -62,6 +62,7 @@ struct Overrides {
     int mfma_kernel = 0;  // fdec_set_mfma_plan
     int mfma_tiles = 0;
     int mfma_gw = 0;
+    int mfma_waves = 0;   // fdec_set_kmfma_waves
 };
 Overrides current_overrides();
 

@@ -7,8 +7,8 @@
 //     y[m, n] = bf16( s * sum_k act[m, k] * q[k, n] * scale[k/128, n]  (+ res[m, n]) )
 // with act = silu(g) * u (SwiGLU prologue) or act = x (identity prologue).
 //
-// Work assignment.  A workgroup of 8 waves owns T tiles of 16 columns over a K slice of
-// 8 GW whole 128-wide groups;
+// Work assignment.  A workgroup of W waves (6..8) owns T tiles of 16 columns over a K
+// slice of W GW whole 128-wide groups;
 // wave w takes GW consecutive groups of the slice for all T tiles.  So a wave needs the
 // activation of its own GW groups only (16 rows x 128 GW values), which it loads straight
 // into the registers that are its MFMA B operands: there is no activation staging in LDS
@@ -53,7 +53,7 @@ namespace {
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kKWaves = 8;
+constexpr int kKWaves = 8;          // waves per workgroup, at most (KArgs::nw)
 
 struct KArgs {
     const uint16_t* a0;     // g (SwiGLU) or x (identity), row stride lda
@@ -65,7 +65,8 @@ struct KArgs {
     int nch;                // K / 32
     int groups;             // K / 128
     int cgroups;            // column ranges (workgroups per K slice)
-    int splits;             // K slices of 8 GW groups
+    int splits;             // K slices of nw GW groups
+    int nw;                 // waves per workgroup (the kernel's W)
     int npad;               // cgroups * 16 T: columns of a slice's partial sums
     const float* out_scale;
     const uint16_t* residual;
@@ -74,14 +75,15 @@ struct KArgs {
     DecodeMasks dm;
 };
 
-template <int PRO, int T, int GW>
+template <int PRO, int T, int GW, int W>
 __global__ __launch_bounds__(kKWaves * kWave) void w4_gemv_kmfma_kernel(KArgs a) {
+    static_assert(W >= 6 && W <= kKWaves, "6..8 waves");
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ls = lane >> 4, lm = lane & 15;
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
     const int cg = lb % a.cgroups, split = lb / a.cgroups;
-    const int gw0 = (split * kKWaves + wave) * GW;     // this wave's first group
+    const int gw0 = (split * W + wave) * GW;           // this wave's first group
     auto tile_col = [&](int t) { return cg * 16 * T + 16 * t; };   // first column of tile t
 
     // ---- activation: rows past M read row M - 1 (never stored); groups past K read the
@@ -196,13 +198,13 @@ __global__ __launch_bounds__(kKWaves * kWave) void w4_gemv_kmfma_kernel(KArgs a)
 #pragma unroll
     for (int t = 0; t < T; ++t) red[(wave * T + t) * kWave + lane] = make_float4(out[t][0], out[t][1], out[t][2], out[t][3]);
     __syncthreads();
-    // thread (t, ln) = (tid / 64, tid % 64) sums the waves' values for its quad, in wave order
-    const int t = tid >> 6, ln = tid & 63;
-    if (t >= T) return;
+    // wave w sums the waves' values of tiles w, w + W, ..., lane ln = (ls, lm) its quad,
+    // in wave order
+    const int ln = lane;
     auto wave_sum = [&](int tt) {
         float4 acc = red[tt * kWave + ln];
 #pragma unroll
-        for (int w = 1; w < kKWaves; ++w) {
+        for (int w = 1; w < W; ++w) {
             const float4 v = red[(w * T + tt) * kWave + ln];
             acc.x += v.x;
             acc.y += v.y;
@@ -212,42 +214,55 @@ __global__ __launch_bounds__(kKWaves * kWave) void w4_gemv_kmfma_kernel(KArgs a)
         return acc;
     };
     const int orow = ln & 15, oc = 4 * (ln >> 4);        // row, column offset in the tile
-    if (a.splits > 1) {
+#pragma unroll
+    for (int t0 = 0; t0 < T; t0 += W) {
+        const int t = t0 + wave;
+        if (t >= T) break;                                 // uniform across the wave
+        if (a.splits > 1) {
+            const float4 v = wave_sum(t);
+            float* dst = a.partial + (size_t(split) * 16 + orow) * a.npad + cg * 16 * T + 16 * t + oc;
+            *reinterpret_cast<float4*>(dst) = v;
+            continue;
+        }
+        const int n = tile_col(t) + oc;
+        if (orow >= a.M || n >= a.N) continue;
         const float4 v = wave_sum(t);
-        float* dst = a.partial + (size_t(split) * 16 + orow) * a.npad + cg * 16 * T + 16 * t + oc;
-        *reinterpret_cast<float4*>(dst) = v;
-        return;
+        const float os = a.out_scale ? *a.out_scale : 1.0f;
+        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+        if (a.residual) {
+            const uint2 rr = *reinterpret_cast<const uint2*>(a.residual + size_t(orow) * a.N + n);
+            r0 = bf16_lo(rr.x);
+            r1 = bf16_hi(rr.x);
+            r2 = bf16_lo(rr.y);
+            r3 = bf16_hi(rr.y);
+        }
+        uint2 o;
+        o.x = pack_bf16x2(fmaf(v.x, os, r0), fmaf(v.y, os, r1));
+        o.y = pack_bf16x2(fmaf(v.z, os, r2), fmaf(v.w, os, r3));
+        *reinterpret_cast<uint2*>(a.y + size_t(orow) * a.N + n) = o;
     }
-    if (orow >= a.M) return;
-    const int n = tile_col(t) + oc;
-    if (n >= a.N) return;
-    const float4 v = wave_sum(t);
-    const float os = a.out_scale ? *a.out_scale : 1.0f;
-    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-    if (a.residual) {
-        const uint2 rr = *reinterpret_cast<const uint2*>(a.residual + size_t(orow) * a.N + n);
-        r0 = bf16_lo(rr.x);
-        r1 = bf16_hi(rr.x);
-        r2 = bf16_lo(rr.y);
-        r3 = bf16_hi(rr.y);
-    }
-    uint2 o;
-    o.x = pack_bf16x2(fmaf(v.x, os, r0), fmaf(v.y, os, r1));
-    o.y = pack_bf16x2(fmaf(v.z, os, r2), fmaf(v.w, os, r3));
-    *reinterpret_cast<uint2*>(a.y + size_t(orow) * a.N + n) = o;
 }
 
-template <int PRO, int T, int GW>
-hipError_t launch_kmfma4(const KArgs& a, const GemvPlan& p, hipStream_t s) {
-    const auto k = w4_gemv_kmfma_kernel<PRO, T, GW>;
-    const size_t lds = size_t(kKWaves) * T * kWave * 16;
+template <int PRO, int T, int GW, int W>
+hipError_t launch_kmfma5(const KArgs& a, const GemvPlan& p, hipStream_t s) {
+    const auto k = w4_gemv_kmfma_kernel<PRO, T, GW, W>;
+    const size_t lds = size_t(W) * T * kWave * 16;
     if (lds > 65536) {
         const hipError_t e =
             hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
         if (e != hipSuccess) return e;
     }
-    k<<<dim3(p.tiles * p.splits), dim3(kKWaves * kWave), lds, s>>>(a);
+    k<<<dim3(p.tiles * p.splits), dim3(W * kWave), lds, s>>>(a);
     return hipGetLastError();
+}
+
+template <int PRO, int T, int GW>
+hipError_t launch_kmfma4(const KArgs& a, const GemvPlan& p, hipStream_t s) {
+    switch (a.nw) {
+        case 6: return launch_kmfma5<PRO, T, GW, 6>(a, p, s);
+        case 7: return launch_kmfma5<PRO, T, GW, 7>(a, p, s);
+        default: return launch_kmfma5<PRO, T, GW, 8>(a, p, s);
+    }
 }
 
 template <int PRO, int T>
@@ -267,41 +282,48 @@ hipError_t launch_kmfma2(const KArgs& a, const GemvPlan& p, hipStream_t s) {
 
 }  // namespace
 
-// T (tiles of 16 columns per workgroup, 8 or 4; p.cpw) and GW (groups per wave, 1..max_gw;
-// the SwiGLU prologue takes at most 2, its raw g and u needing twice the registers; p.gw): the
-// pair with the least estimated time, counted in (16-column, 128-k) weight blocks per
-// workgroup times rounds of workgroups over 256 CUs, plus about 75 such blocks for the
-// slice-summing kernel when K is split.
+// T (tiles of 16 columns per workgroup, 8 or 4; p.cpw), GW (groups per wave, 1..max_gw;
+// the SwiGLU prologue takes at most 2, its raw g and u needing twice the registers; p.gw)
+// and W (waves per workgroup, 8 down to 6; p.waves): the choice with the least estimated
+// time, counted in (16-column, 128-k) weight blocks per workgroup times rounds of
+// workgroups over 256 CUs, plus about 75 such blocks for the slice-summing kernel when K
+// is split; ties go to more waves.  Fewer than 8 waves make thinner K slices, hence more
+// workgroups: measured on MI355X at 16 rows, 9216 x 2560 takes 8 tiles and 6 waves (240
+// workgroups; 10.7 against 11.0 us with 8 waves), 8960 x 1536 4 tiles and 7 waves (240;
+// 8.7 against 9.3 us), while 4096 x 4096 and 8192 x 2048 keep 4 tiles and 8 waves (256).
 bool plan_kmfma(int M, int K, int N, int max_gw, GemvPlan& p, const Overrides& ov) {
     p = GemvPlan{};
     if (M < 1 || M > 16 || K <= 0 || K % kGroup || N <= 0 || N % 8) return false;
     p.kind = kKMfma;
     p.mr = 16;
     p.groups = K / kGroup;
-    p.waves = kKWaves;
     double best = 1e30;
-    for (int T : {8, 4}) {
-        if (ov.mfma_tiles && T != ov.mfma_tiles) continue;
-        const int ranges = (N + 16 * T - 1) / (16 * T);
-        for (int gw = std::min(max_gw, 4); gw >= 1; --gw) {
-            if (ov.mfma_gw && gw != ov.mfma_gw) continue;
-            const int slice = kKWaves * gw;
-            const int S = (p.groups + slice - 1) / slice;
-            const int wgs = ranges * S;
-            const double cost = double((wgs + 255) / 256) * T * std::min(slice, p.groups) + (S > 1 ? 75.0 : 0.0);
-            if (cost < best - 1e-9) {
-                best = cost;
-                p.cpw = T;
-                p.gw = gw;
-                p.tiles = ranges;
-                p.splits = S;
+    for (int W = kKWaves; W >= 6; --W) {
+        if (ov.mfma_waves && W != ov.mfma_waves) continue;
+        for (int T : {8, 4}) {
+            if (ov.mfma_tiles && T != ov.mfma_tiles) continue;
+            const int ranges = (N + 16 * T - 1) / (16 * T);
+            for (int gw = std::min(max_gw, 4); gw >= 1; --gw) {
+                if (ov.mfma_gw && gw != ov.mfma_gw) continue;
+                const int slice = W * gw;
+                const int S = (p.groups + slice - 1) / slice;
+                const int wgs = ranges * S;
+                const double cost = double((wgs + 255) / 256) * T * std::min(slice, p.groups) + (S > 1 ? 75.0 : 0.0);
+                if (cost < best - 1e-9) {
+                    best = cost;
+                    p.cpw = T;
+                    p.gw = gw;
+                    p.waves = W;
+                    p.tiles = ranges;
+                    p.splits = S;
+                }
             }
         }
     }
     if (best >= 1e29) return false;
-    p.gps = kKWaves * p.gw;
+    p.gps = p.waves * p.gw;
     if (p.splits > 1) p.partial_bytes = size_t(p.splits) * 16 * p.tiles * 16 * p.cpw * 4;
-    p.lds_bytes = size_t(kKWaves) * p.cpw * kWave * 16;
+    p.lds_bytes = size_t(p.waves) * p.cpw * kWave * 16;
     return true;
 }
 
@@ -320,13 +342,16 @@ hipError_t launch_kmfma(Prologue pro, const uint16_t* a0, const uint16_t* a1, in
     a.groups = p.groups;
     a.cgroups = p.tiles;
     a.splits = p.splits;
+    a.nw = p.waves;
     a.npad = p.tiles * 16 * p.cpw;
     a.out_scale = out_scale;
     a.residual = residual;
     a.y = y;
     a.partial = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
     a.dm = DecodeMasks{kDecodeMaskLo, kDecodeMaskHi};
-    if (p.kind != kKMfma || M > 16 || (p.cpw != 4 && p.cpw != 8) || p.gw < 1 || p.gw > 4) return hipErrorInvalidValue;
+    if (p.kind != kKMfma || M > 16 || (p.cpw != 4 && p.cpw != 8) || p.gw < 1 || p.gw > 4 || p.waves < 6 ||
+        p.waves > kKWaves)
+        return hipErrorInvalidValue;
     const hipError_t e = pro == kSwiGLU ? launch_kmfma2<kSwiGLU>(a, p, s) : launch_kmfma2<kIdentity>(a, p, s);
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_splitk_finish(a.partial, p.splits, int64_t(16) * a.npad, a.npad, M, N, out_scale, residual, y, s);

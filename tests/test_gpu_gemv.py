@@ -304,6 +304,31 @@ def test_kmfma_kernel_every_variant(pro, tiles, gw):
     assert_bits_equal(y, y2, "repeat")
 
 
+@pytest.mark.parametrize("waves", [6, 7, 8])
+@pytest.mark.parametrize("tiles,gw", [(8, 1), (4, 2)])
+def test_kmfma_kernel_wave_counts(waves, tiles, gw):
+    # fewer waves than 8 tiles: some waves sum and store two tiles
+    M, K, N = 16, 4224, 1000
+    say(f"[kmfma] SwiGLU waves={waves} tiles={tiles} groups/wave={gw} M={M} K={K} N={N}")
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=waves * 100 + tiles * 10 + gw, out_scale=0.5, with_residual=True)
+    g, u, W, res = to_dev(inp)
+    s = F.scalar(0.5)
+    F.set_mfma_plan(2, tiles, gw)
+    F.set_kmfma_waves(waves)
+    try:
+        ws = torch.full((max(16, F.gemv_workspace_bytes(M, K, N)),), 0xFF, dtype=torch.uint8, device=DEV)
+        y = F.to_bits(F.swiglu_w4_gemv(g, u, W, s, res, ws=ws))
+        y2 = F.to_bits(F.swiglu_w4_gemv(g, u, W, s, res, ws=ws))
+        xi = F.to_bits(F.w4_gemv(g, W, s, ws=ws))
+    finally:
+        F.set_kmfma_waves(0)
+        F.set_mfma_plan(0)
+    say("  worst err/bound", assert_close(y, O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, 0.5,
+                                                               inp.residual), "y"))
+    assert_bits_equal(y, y2, "repeat")
+    say("  identity worst err/bound", assert_close(xi, O.w4_gemv(inp.g, inp.W.qweight, inp.W.scales, 0.5), "x"))
+
+
 # ---------------------------------------------------------------------------
 # outputs that should be exactly zero: the kernels keep a known offset in every decoded
 # weight (1032 + q or 1152 + 16 q in fp16) and remove it once per chunk or group, so a
