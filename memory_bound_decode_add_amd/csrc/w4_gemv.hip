@@ -434,9 +434,11 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int j = 0; j < CPW; ++j) acc[m][j] = 0.f;
-    // the activation of range i + 1 is read from LDS while range i is worked
-    uint4 avb[2][MR][4];
-    float2 ebb[2][MR];
+    // One row: the activation of range i + 1 is read from LDS while range i is worked (a
+    // second buffer; with more rows its registers would spill).
+    constexpr int NB = MR == 1 ? 2 : 1;
+    uint4 avb[NB][MR][4];
+    float2 ebb[NB][MR];
     auto read_act = [&](int i, int b) {
         const int c = min(lane + kWave * i, a.nch - 1);
 #pragma unroll
@@ -447,14 +449,15 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
             ebb[b][m] = eb_s[m * a.nch + c];
         }
     };
-    read_act(0, 0);
+    if (NB == 2) read_act(0, 0);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        if (i + 1 < NI) read_act(i + 1, (i + 1) & 1);
+        if (NB == 2 && i + 1 < NI) read_act(i + 1, (i + 1) % NB);
         const int c = lane + kWave * i;
         if (i < NI - 1 || c < a.nch) {             // only the last range can pass K (NI = ceil(nch / 64))
-            const uint4 (&av)[MR][4] = avb[i & 1];
-            const float2 (&eb)[MR] = ebb[i & 1];
+            if (NB == 1) read_act(i, 0);
+            const uint4 (&av)[MR][4] = avb[i % NB];
+            const float2 (&eb)[MR] = ebb[i % NB];
 #pragma unroll
             for (int j = 0; j < CPW; ++j) {
                 if (!slot_ok(j)) break;            // uniform
