@@ -440,7 +440,8 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     uint4 avb[NB][MR][4];
     float2 ebb[NB][MR];
     auto read_act = [&](int i, int b) {
-        const int c = min(lane + kWave * i, a.nch - 1);
+        // only the last range can pass K: the others need no clamp (constant LDS offsets)
+        const int c = i < NI - 1 ? lane + kWave * i : min(lane + kWave * i, a.nch - 1);
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             const _Float16* arow = act_s + size_t(m) * 4 * qs + c * 8;
@@ -449,6 +450,12 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
             ebb[b][m] = eb_s[m * a.nch + c];
         }
     };
+    const float* sc_row = sc_s + (lane >> 2) * C;    // chunk lane + 64 i is in group lane / 4 + 16 i
+    // The decode masks as vector registers, set once: a VALU instruction takes one scalar
+    // operand, so with the masks in scalars every block of the dot re-copied them (an
+    // identity DPP move, which the compiler does not re-materialise).
+    const DecodeMasks dmv{uint32_t(__builtin_amdgcn_update_dpp(0, int(a.dm.lo), 0xE4, 0xF, 0xF, false)),
+                          uint32_t(__builtin_amdgcn_update_dpp(0, int(a.dm.hi), 0xE4, 0xF, 0xF, false))};
     if (NB == 2) read_act(0, 0);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -461,11 +468,11 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
 #pragma unroll
             for (int j = 0; j < CPW; ++j) {
                 if (!slot_ok(j)) break;            // uniform
-                const float s = sc_s[(c >> 2) * C + slot_cj(j)];
+                const float s = sc_row[16 * C * i + slot_cj(j)];
                 const uint32_t wd[4] = {wv[i][j].x, wv[i][j].y, wv[i][j].z, wv[i][j].w};
                 Q4x2 q[4];
 #pragma unroll
-                for (int h = 0; h < 4; ++h) q[h] = decode_int4x8_biased(wd[h], a.dm);
+                for (int h = 0; h < 4; ++h) q[h] = decode_int4x8_biased(wd[h], dmv);
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     float d = -eb[m].y;
