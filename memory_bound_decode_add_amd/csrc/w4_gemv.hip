@@ -156,6 +156,10 @@ struct ColArgs {
 // summed from the rounded values, so they cancel exactly whatever the rounding.
 __device__ __forceinline__ int col_quarter_stride(int nch) { return nch * 8 + 32; }
 
+// Which waves load the group scales: the dot waves with three or more 64-chunk ranges per
+// lane (long K), the staging waves otherwise (see the kernel).
+__host__ __device__ constexpr bool col_dot_scales(int ni) { return ni >= 3; }
+
 // Eight activation values k = 8w + j (j = 0..7) of one lane -> LDS (see above).
 // Lanes past K (a quad is wholly inside or outside) store nothing; rows past M stage
 // copies of row M - 1 (clamped loads), whose sums no lane stores: neither is zeroed.
@@ -260,9 +264,54 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
         return cbase + cj;
     };
 
+    // ---- group scales of the workgroup's columns, as aligned 8-column pieces of each
+    // group's row.  One column range, or two with PAIR (gate i.., up I + i..): range r
+    // covers columns [cb_r, cb_r + n_r) and LDS slots [o_r, o_r + n_r).  Loaded into
+    // registers by thread tid0 + r nthr, then written to LDS.  With long K (kDotScales)
+    // the dot waves load them ahead of their own weights: cold like the weights, they then
+    // land while the activation is staged, where behind the staging waves' activation
+    // loads they held the barrier (measured on MI355X at K = 9216, N = 2560: landing
+    // ≈ 0.9 us after the staged activation).  With short K the staging waves do it, the
+    // dot waves having many columns' weights to request. ----
+    const int n0 = PAIR ? a.pairs : C;
+    const int cb0 = cbase, cb1 = PAIR ? a.half_n + cbase : 0;
+    const int p00 = cb0 >> 3, npc0 = ((min(cb0 + n0, a.N) - 1) >> 3) - p00 + 1;
+    const int p01 = cb1 >> 3, npc1 = PAIR ? ((min(cb1 + n0, a.N) - 1) >> 3) - p01 + 1 : 0;
+    const int nsc0 = a.groups * npc0, nsc = nsc0 + a.groups * npc1;
+    constexpr bool kDotScales = col_dot_scales(NI);
+    auto load_scales = [&](uint4 (&sraw)[kColScLoads], int tid0, int nthr) {
+#pragma unroll
+        for (int r = 0; r < kColScLoads; ++r) {
+            if (r * nthr >= nsc) break;            // uniform
+            const int idx = min(tid0 + r * nthr, nsc - 1);
+            const bool hi = idx >= nsc0;
+            const int j = hi ? idx - nsc0 : idx, npc = hi ? npc1 : npc0;
+            const int g = j / npc, pc = (hi ? p01 : p00) + j % npc;
+            sraw[r] = *reinterpret_cast<const uint4*>(a.sc + size_t(g) * a.N + pc * 8);
+        }
+    };
+    auto write_scales = [&](const uint4 (&sraw)[kColScLoads], int tid0, int nthr) {
+#pragma unroll
+        for (int r = 0; r < kColScLoads; ++r) {
+            if (r * nthr >= nsc) break;
+            const int idx = tid0 + r * nthr;
+            if (idx < nsc) {
+                const bool hi = idx >= nsc0;
+                const int j = hi ? idx - nsc0 : idx, npc = hi ? npc1 : npc0;
+                const int g = j / npc;
+                const int cc0 = ((hi ? p01 : p00) + j % npc) * 8 - (hi ? cb1 : cb0), o = hi ? n0 : 0;
+                const uint32_t wd[4] = {sraw[r].x, sraw[r].y, sraw[r].z, sraw[r].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int cc = cc0 + e;
+                    if (cc >= 0 && cc < n0) sc_s[g * C + o + cc] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+                }
+            }
+        }
+    };
     if (wave < S) {
         // ================= staging waves =================
-        const int sw = wave, stid = tid, nst = S * kWave;
+        const int sw = wave;
         // ---- activation inputs: task t = sw + S * ti -> (row t % MR, block t / MR) ----
         const int ntask = MR * nblk;
         uint4 ga[TMAX], ua[TMAX], wa[PAIR ? TMAX : 1];
@@ -277,25 +326,9 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
                                       : make_uint4(0, 0, 0, 0);
             if (PAIR) wa[ti] = *reinterpret_cast<const uint4*>(a.nw + k);
         }
-        // ---- group scales of the workgroup's columns, as aligned 8-column pieces of
-        // each group's row.  One column range, or two with PAIR (gate i.., up I + i..):
-        // range r covers columns [cb_r, cb_r + n_r) and LDS slots [o_r, o_r + n_r). ----
-        const int n0 = PAIR ? a.pairs : C;
-        const int cb0 = cbase, cb1 = PAIR ? a.half_n + cbase : 0;
-        const int p00 = cb0 >> 3, npc0 = ((min(cb0 + n0, a.N) - 1) >> 3) - p00 + 1;
-        const int p01 = cb1 >> 3, npc1 = PAIR ? ((min(cb1 + n0, a.N) - 1) >> 3) - p01 + 1 : 0;
-        const int nsc0 = a.groups * npc0, nsc = nsc0 + a.groups * npc1;
         uint4 sraw[kColScLoads];
-#pragma unroll
-        for (int r = 0; r < kColScLoads; ++r) {
-            if (r * nst >= nsc) break;             // uniform
-            const int idx = min(stid + r * nst, nsc - 1);
-            const bool hi = idx >= nsc0;
-            const int j = hi ? idx - nsc0 : idx, npc = hi ? npc1 : npc0;
-            const int g = j / npc, pc = (hi ? p01 : p00) + j % npc;
-            sraw[r] = *reinterpret_cast<const uint4*>(a.sc + size_t(g) * a.N + pc * 8);
-        }
-        // ---- activations, per-chunk scale and offsets, group scales to LDS ----
+        if (!kDotScales) load_scales(sraw, tid, S * kWave);
+        // ---- activations, per-chunk scale and offsets to LDS ----
         // word wi = 64 b + lane: chunk wi / 4, quarter wi % 4
         const int lofs = (lane & 3) * qs + (lane >> 2) * 8;
         if (PAIR) {
@@ -375,23 +408,7 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
                                     eb_s + m * a.nch + b * 16 + (lane >> 2));
             }
         }
-#pragma unroll
-        for (int r = 0; r < kColScLoads; ++r) {
-            if (r * nst >= nsc) break;
-            const int idx = stid + r * nst;
-            if (idx < nsc) {
-                const bool hi = idx >= nsc0;
-                const int j = hi ? idx - nsc0 : idx, npc = hi ? npc1 : npc0;
-                const int g = j / npc;
-                const int cc0 = ((hi ? p01 : p00) + j % npc) * 8 - (hi ? cb1 : cb0), o = hi ? n0 : 0;
-                const uint32_t wd[4] = {sraw[r].x, sraw[r].y, sraw[r].z, sraw[r].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int cc = cc0 + e;
-                    if (cc >= 0 && cc < n0) sc_s[g * C + o + cc] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
-                }
-            }
-        }
+        if (!kDotScales) write_scales(sraw, tid, S * kWave);
         __syncthreads();
         return;
     }
@@ -416,6 +433,9 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     // weight chunks: lane l takes chunks l, l+64, ... of each of the wave's columns (a
     // slot the wave does not own re-reads its first column: the loads stay unconditional,
     // so every wait in the dot is exact; skipping them measured slower)
+    // the group scales first (long K), ahead of this wave's weights
+    uint4 sraw[kColScLoads];
+    if (kDotScales) load_scales(sraw, tid - S * kWave, W * kWave);
     uint4 wv[NI][CPW];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
@@ -424,6 +444,7 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) wv[i][j] = nt_load(colp + min(lane + kWave * i, a.nch - 1));
     }
+    if (kDotScales) write_scales(sraw, tid - S * kWave, W * kWave);
     if (PAIR) __syncthreads();                     // the staging waves' row sums
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
@@ -909,7 +930,7 @@ bool plan_column(int M, int K, int N, GemvPlan& p, const Overrides& ov) {
     p.cpw = col_cpw_round((C + p.waves - 1) / p.waves);
     if (p.cpw < 1 || p.cpw > cmax || p.stagers * kColMaxTasks < ntask) return false;
     const int pieces = (C + 7) / 8 + 1;                       // 8-column scale pieces per group, at most
-    if (p.groups * pieces > kColScLoads * p.stagers * kWave) return false;   // staging waves' scale capacity
+    if (p.groups * pieces > kColScLoads * (col_dot_scales(p.ni) ? p.waves : p.stagers) * kWave) return false;
     p.wgs = (N + C - 1) / C;
     p.lds_bytes = size_t(p.mr) * 4 * (nch * 8 + 32) * 2 + size_t(p.mr) * nch * 8 + size_t(p.groups) * C * 4;
     if (p.lds_bytes > kMaxLds) return false;
@@ -944,7 +965,7 @@ bool plan_column_pair(int M, int K, int I, GemvPlan& p) {
     if (p.cpw > cmax) return false;
     p.cols = 2 * pairs;
     const int pieces = 2 * ((pairs + 7) / 8 + 1);
-    if (p.groups * pieces > kColScLoads * p.stagers * kWave) return false;
+    if (p.groups * pieces > kColScLoads * (col_dot_scales(p.ni) ? p.waves : p.stagers) * kWave) return false;
     p.wgs = (I + pairs - 1) / pairs;
     p.lds_bytes = size_t(p.mr) * 4 * (nch * 8 + 32) * 2 + size_t(p.mr) * nch * 8 + size_t(p.groups) * p.cols * 4 +
                   size_t(p.stagers) * p.mr * 4;
