@@ -893,6 +893,26 @@ int col_cpw_max(int ni, int mr) {
 // per lane); the extra slots are skipped.
 int col_cpw_round(int cpw) { return cpw <= 4 ? cpw : cpw <= 6 ? 6 : 8; }
 
+// Dot waves for `units` columns (or column pairs) of a workgroup, unit u on wave u % W,
+// at most `per_max` per wave, with S staging waves ahead of them (waves go to the SIMDs
+// round robin): the W in [8, 16 - S] whose busiest SIMD holds the fewest units, ties to
+// fewer waves.  The dot is VALU work, so the busiest SIMD sets its time; measured on
+// MI355X at K = 1536 (one chunk range per lane), 12 dot waves against 9.
+int col_dot_waves(int S, int units, int per_max) {
+    int best_w = 0, best_load = 1 << 30;
+    for (int W = 8; W <= 16 - S; ++W) {
+        if ((units + W - 1) / W > per_max) continue;
+        int load[4] = {0, 0, 0, 0};
+        for (int w = 0; w < W && w < units; ++w) load[(S + w) % 4] += (units - w + W - 1) / W;
+        const int mx = std::max(std::max(load[0], load[1]), std::max(load[2], load[3]));
+        if (mx < best_load) {
+            best_load = mx;
+            best_w = W;
+        }
+    }
+    return best_w;
+}
+
 bool plan_column(int M, int K, int N, GemvPlan& p, const Overrides& ov) {
     if (M > 4 || K > 32 * kColMaxChunks * kWave) return false;
     const int nch = K / 32;
@@ -911,8 +931,17 @@ bool plan_column(int M, int K, int N, GemvPlan& p, const Overrides& ov) {
     const int cwant = std::max(1, (N + 255) / 256);
     p.waves = 8;
     if (cwant > 8 * cmax) {
-        const int cpw = std::min(cmax, col_cpw_round((cwant + 15 - p.stagers) / (16 - p.stagers)));
-        p.waves = std::max(8, std::min(16 - p.stagers, (cwant + cpw - 1) / cpw));
+        // the wave count whose busiest SIMD holds the fewest columns, at most cmax per wave
+        // after rounding to an instantiated variant; else the fewest waves that reach cmax
+        int w = 0;
+        for (int cap = cmax; cap >= 1 && !w; --cap)
+            if (col_cpw_round(cap) <= cmax) w = col_dot_waves(p.stagers, cwant, cap);
+        if (w) {
+            p.waves = w;
+        } else {
+            const int cpw = std::min(cmax, col_cpw_round((cwant + 15 - p.stagers) / (16 - p.stagers)));
+            p.waves = std::max(8, std::min(16 - p.stagers, (cwant + cpw - 1) / cpw));
+        }
     }
     int C = std::min(cwant, p.waves * cmax);
     // a forced shape replaces the choice when the kernel has a variant for it; more dot
@@ -959,7 +988,10 @@ bool plan_column_pair(int M, int K, int I, GemvPlan& p) {
     const int ppw = cmax / 2;                                  // pairs per wave, at most
     const int pwant = std::max(1, (I + 255) / 256);
     p.waves = 8;
-    if (pwant > 8 * ppw) p.waves = std::min(16 - p.stagers, (pwant + ppw - 1) / ppw);
+    if (pwant > 8 * ppw) {
+        const int w = col_dot_waves(p.stagers, pwant, ppw);
+        p.waves = w ? w : std::min(16 - p.stagers, (pwant + ppw - 1) / ppw);
+    }
     const int pairs = std::min(pwant, p.waves * ppw);
     p.cpw = 2 * ((pairs + p.waves - 1) / p.waves);
     if (p.cpw > cmax) return false;
