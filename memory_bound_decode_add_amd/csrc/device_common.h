@@ -276,6 +276,25 @@ __device__ __forceinline__ float stage_group_scale(float mx, float* esc) {
     return __builtin_ldexpf(1.0f, -E);
 }
 
+// The offset terms of a staged 128-wide group for the int4 matrix-core kernels: a lane
+// holds one staged k-block (pair order, odd positions / 16) and the 16 lanes of its DPP
+// row the group's 16 k-blocks.  Returns, in every lane of the row, the sum over the group
+// of -1032 * (even slot) - 1152 * (odd slot): what the MFMA of the constant offset matrix
+// with these values gives in every column, so a product chain can start from it instead.
+__device__ __forceinline__ float staged_offset_sum16(uint4 h) {
+    const half2_t ne = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half2_t no = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    float b = dot2(__builtin_bit_cast(half2_t, h.x), ne, 0.f);
+    b = dot2(__builtin_bit_cast(half2_t, h.z), ne, b);
+    b = dot2(__builtin_bit_cast(half2_t, h.y), no, b);
+    b = dot2(__builtin_bit_cast(half2_t, h.w), no, b);
+    b += dpp<kQuadSwap1>(b);
+    b += dpp<kQuadSwap2>(b);
+    b += dpp<kRowRor4>(b);
+    b += dpp<kRowRor8>(b);
+    return b;
+}
+
 // One k-block staged for the int4 kernels: pair order (k0, k4), (k1, k5), (k2, k6),
 // (k3, k7), the odd positions also divided by 16, matching decode_int4x8_biased.
 __device__ __forceinline__ uint4 stage_pair_order(const float (&v)[8], float down) {

@@ -39,10 +39,12 @@
 // of operands and three steps of staged activation, not the slice's activation, so a
 // 16-row, 4096-wide slice needs no K split.
 //
-// Products (as the row-block kernel).  v_mfma_f32_16x16x32_f16 with A = the decoded
-// weights (fp16 1032 + q / 1152 + 16 q in pair order), B = the staged activation; each
-// group's chain starts from the product of the constant -1032 / -1152 matrix with the
-// same B operands, which removes the offsets.  The group's bf16 scale times the row's
+// Products.  v_mfma_f32_16x16x32_f16 with A = the decoded weights (fp16 1032 + q /
+// 1152 + 16 q in pair order), B = the staged activation; each group's chain starts from
+// the group's offset sum per row (-1032 / -1152 times the staged values, summed when the
+// step is converted and published with its power of two), which removes the offsets.
+// (That sum is the same for every column: formed once per step instead of by four MFMAs
+// of a constant matrix in every wave, which were half of the kernel's MFMAs.)  The group's bf16 scale times the row's
 // power of two multiplies the group's result once.
 //
 // Epilogue.  One K slice: the output (residual and scale) or, in pair mode, the up waves
@@ -65,7 +67,7 @@ constexpr int kRgThreads = kRgWaves * kWave;
 constexpr int kRgPairs = kRgWaves / 2 * 16;            // column pairs per workgroup, pair mode
 constexpr int kRgRowBlocks = 33;                        // 16-byte blocks per staged row: 32 + a pad
 constexpr int kRgActBytes = 16 * kRgRowBlocks * 16;     // one staged step: 16 rows
-constexpr int kRgActSlot = kRgActBytes + 16 * 2 * 4;    // + the (row, group) powers of two
+constexpr int kRgActSlot = kRgActBytes + 2 * 16 * 2 * 4;   // + per (row, group): power of two, offset sum
 constexpr int kRgActSlots = 3;
 
 // s_waitcnt with only one count limited (gfx9 encoding: vmcnt in bits 3..0 and 15..14,
@@ -200,9 +202,10 @@ __device__ __forceinline__ void rg_step(const RgArgs& a, const RgLane& ln, int t
         const uint4 uv = PRO == kSwiGLU ? reinterpret_cast<const uint4*>(rnext + 1024)[lane] : make_uint4(0, 0, 0, 0);
         float esc;
         const uint4 h = stage8<PRO>(gv, uv, &esc);
+        const float off = staged_offset_sum16(h);
         const int row = tid >> 5, kb = tid & 31;
         reinterpret_cast<uint4*>(anext)[row * kRgRowBlocks + kb] = h;
-        if ((kb & 15) == 0) reinterpret_cast<float*>(anext + kRgActBytes)[row * 2 + (kb >> 4)] = esc;
+        if ((kb & 15) == 0) reinterpret_cast<float2*>(anext + kRgActBytes)[row * 2 + (kb >> 4)] = make_float2(esc, off);
     }
     const unsigned char* wq = wcur + RgShape<PRO>::kActLoads * 1024;
     const uint4 w0 = *reinterpret_cast<const uint4*>(wq + ln.rd[0]);
@@ -221,17 +224,9 @@ __device__ __forceinline__ void rg_step(const RgArgs& a, const RgLane& ln, int t
         b0[j] = __builtin_bit_cast(f16x8_t, as[j]);
         b1[j] = __builtin_bit_cast(f16x8_t, as[16 + j]);
     }
-    const float* es = reinterpret_cast<const float*>(acur + kRgActBytes) + lm * 2;
-    const float e0 = es[0] * e_valid0, e1 = es[1] * e_valid1;
-
-    const uint32_t o_even = 0xE408E408u, o_odd = 0xE480E480u;    // -1032, -1152 in each half
-    const f16x8_t negoff = __builtin_bit_cast(f16x8_t, make_uint4(o_even, o_odd, o_even, o_odd));
-    f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(negoff, b0[j], d0, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(negoff, b1[j], d1, 0, 0, 0);
-    }
+    const float4 es = reinterpret_cast<const float4*>(acur + kRgActBytes)[lm];   // (esc, off) of groups 0, 1
+    const float e0 = es.x * e_valid0, e1 = es.z * e_valid1;
+    f32x4_t d0 = {es.y, es.y, es.y, es.y}, d1 = {es.w, es.w, es.w, es.w};
     const uint32_t wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -266,9 +261,10 @@ __device__ __forceinline__ void rg_prologue(const RgArgs& a, const RgLane& ln, i
     const uint4 uv = PRO == kSwiGLU ? reinterpret_cast<const uint4*>(slot0 + 1024)[lane] : make_uint4(0, 0, 0, 0);
     float esc;
     const uint4 h = stage8<PRO>(gv, uv, &esc);
+    const float off = staged_offset_sum16(h);
     const int row = tid >> 5, kb = tid & 31;
     reinterpret_cast<uint4*>(act0)[row * kRgRowBlocks + kb] = h;
-    if ((kb & 15) == 0) reinterpret_cast<float*>(act0 + kRgActBytes)[row * 2 + (kb >> 4)] = esc;
+    if ((kb & 15) == 0) reinterpret_cast<float2*>(act0 + kRgActBytes)[row * 2 + (kb >> 4)] = make_float2(esc, off);
 }
 
 template <int PRO, bool PAIR>
