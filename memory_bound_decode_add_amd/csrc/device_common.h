@@ -251,6 +251,36 @@ __device__ __forceinline__ float silu_f32(float v) {
     return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
 }
 
+// gfx950 lane swaps (v_permlane32_swap, v_permlane16_swap), both results as floats.
+//   swap32(x, y) = {x lanes 0..31 then y lanes 0..31,  x lanes 32..63 then y lanes 32..63};
+//   swap16(x, y), in rows of 16 lanes = {x0 y0 x2 y2,  x1 y1 x3 y3}.
+// The builtin's two-element result is cast as a whole: with this compiler a cast of one
+// element of it on its own read element 0 for both.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2_t swap32(float x, float y) {
+    return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                                        __builtin_bit_cast(uint32_t, y), false, false));
+}
+__device__ __forceinline__ f32x2_t swap16(float x, float y) {
+    return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                                        __builtin_bit_cast(uint32_t, y), false, false));
+}
+
+// Sums a, b, c and d over a full wave (all 64 lanes active), four values in one register:
+// the half-wave swaps fold lanes 32..63 onto 0..31 for two values each, the row swap folds
+// the odd rows onto the even ones, and four DPP steps sum within each row of 16 lanes.
+// Every lane of row r then holds the total of {a, c, b, d}[r].
+__device__ __forceinline__ float wave_sum4_rows(float a, float b, float c, float d) {
+    const f32x2_t x = swap32(a, b), y = swap32(c, d);
+    const f32x2_t z = swap16(x[0] + x[1], y[0] + y[1]);   // rows a a b b | c c d d
+    float u = z[0] + z[1];                                 // rows a c b d
+    u += dpp<kQuadSwap1>(u);
+    u += dpp<kQuadSwap2>(u);
+    u += dpp<kRowRor4>(u);
+    u += dpp<kRowRor8>(u);
+    return u;
+}
+
 // ---------------------------------------------------------------------------
 // Block-scaled fp16 staging of the activation for the matrix-core GEMVs.  A k-block is 8
 // consecutive values of one row; the 16 lanes of a DPP row hold the 16 k-blocks of one

@@ -422,13 +422,32 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     auto slot_unit = [&](int j) { return wave + W * (PAIR ? (j >> 1) : j); };
     auto slot_ok = [&](int j) { return slot_unit(j) < (PAIR ? a.pairs : C); };
     auto slot_cj = [&](int j) { return PAIR && (j & 1) ? a.pairs + slot_unit(j) : slot_unit(j); };
-    // output of lane l < MR * OPW: row l / OPW, unit (column or pair) wave + W * (l % OPW)
+    // The wave's outputs n = m * OPW + o: row m, unit o (a column, or with PAIR a pair).
+    // kRowSums (two or more plain outputs): they are summed four to a register, output n of
+    // group g ends in row r of it, n = 4 g + {0, 2, 1, 3}[r], and lane 16 r stores it.
+    // Otherwise each output is summed on its own and lane n stores it.  (Four to a register
+    // measured faster there; with one output, and for the SwiGLU pairs, the per-output sums
+    // measured as fast or faster.)
     constexpr int OPW = PAIR ? CPW / 2 : CPW;
+    constexpr int NO = MR * OPW;
+    constexpr bool kRowSums = !PAIR && NO >= 2;
+    constexpr int NG = kRowSums ? (NO + 3) / 4 : 1;
     const int ldy = PAIR ? a.half_n : a.N;
-    const int em = lane / OPW, eu = wave + W * (lane % OPW), en = cbase + eu;
-    const bool owner = lane < MR * OPW && em < a.M && eu < (PAIR ? a.pairs : C) && en < ldy;
+    const int orow = lane >> 4;
+    const bool lead = !kRowSums || (lane & 15) == 0;
     const uint16_t* rsrc = a.residual ? a.residual : a.y;   // y: a readable stand-in, value unused
-    const uint16_t rraw = rsrc[size_t(min(em, a.M - 1)) * ldy + min(en, ldy - 1)];
+    int o_m[NG], o_n[NG];
+    bool o_ok[NG];
+    uint16_t o_r[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int n = kRowSums ? 4 * g + (((orow & 1) << 1) | (orow >> 1)) : lane;
+        const int m = n / OPW, u = wave + W * (n % OPW);
+        o_m[g] = m;
+        o_n[g] = cbase + u;
+        o_ok[g] = lead && n < NO && m < a.M && u < (PAIR ? a.pairs : C) && cbase + u < ldy;
+        o_r[g] = rsrc[size_t(min(m, a.M - 1)) * ldy + min(cbase + u, ldy - 1)];
+    }
     const float os = a.out_scale ? *a.out_scale : 1.0f;
     // weight chunks: lane l takes chunks l, l+64, ... of each of the wave's columns (a
     // slot the wave does not own re-reads its first column: the loads stay unconditional,
@@ -510,6 +529,19 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
         }
     }
 
+    if constexpr (kRowSums) {
+    // ---- sum the outputs over the wave, four to a register; the epilogue in every row ----
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        if (MR == 1 && !slot_ok(4 * g)) break;     // uniform: no owned column left
+        const int n0 = min(4 * g, NO - 1), n1 = min(4 * g + 1, NO - 1);
+        const int n2 = min(4 * g + 2, NO - 1), n3 = min(4 * g + 3, NO - 1);
+        const float v = wave_sum4_rows(acc[n0 / CPW][n0 % CPW], acc[n1 / CPW][n1 % CPW],
+                                       acc[n2 / CPW][n2 % CPW], acc[n3 / CPW][n3 % CPW]);
+        const float res = a.residual ? bf16_to_f32(o_r[g]) : 0.f;
+        if (o_ok[g]) a.y[size_t(o_m[g]) * ldy + o_n[g]] = f32_to_bf16(fmaf(v, os, res));
+    }
+    } else {
     // ---- reduce each column over the wave; the owning lane applies the epilogue ----
     float tot[MR][CPW];
 #pragma unroll
@@ -540,10 +572,11 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
             mine = lane == m * OPW + o ? v : mine;
         }
     if (PAIR) {
-        if (owner) a.y[size_t(em) * ldy + en] = f32_to_bf16(mine);
+        if (o_ok[0]) a.y[size_t(o_m[0]) * ldy + o_n[0]] = f32_to_bf16(mine);
     } else {
-        const float res = a.residual ? bf16_to_f32(rraw) : 0.f;
-        if (owner) a.y[size_t(em) * ldy + en] = f32_to_bf16(fmaf(mine, os, res));
+        const float res = a.residual ? bf16_to_f32(o_r[0]) : 0.f;
+        if (o_ok[0]) a.y[size_t(o_m[0]) * ldy + o_n[0]] = f32_to_bf16(fmaf(mine, os, res));
+    }
     }
     // ---- side copy (the fused layer's residual update), spread over the grid ----
     if (a.cp_n16 > 0) {
