@@ -25,9 +25,10 @@ extern "C" {
  *   that do not fit the shape are clamped).  Calls with more than 16 rows ignore it:
  *   only the matrix-core kernel takes them.
  * fdec_set_gemv_tiling(waves, cols_per_workgroup): force the column-owning GEMV
- *   kernel's workgroup shape (1..14 dot waves, each owning at most 4 columns, next to
- *   the staging waves, 16 waves in all); (0, 0) restores the built-in choice.  Shapes
- *   the kernel cannot take fall back to it.
+ *   kernel's workgroup shape (1..14 dot waves next to the staging waves, 16 waves in
+ *   all; each dot wave owns at most 8 columns with K <= 2048, fewer with longer K or with
+ *   3..4 rows); (0, 0) restores the built-in choice.  Shapes the kernel cannot take fall
+ *   back to it.
  * fdec_test_fail_launches(on): while on, every compute call validates its arguments
  *   and then returns FDEC_ERR_HIP without touching the GPU (exercises the error path
  *   on machines without a GPU). */

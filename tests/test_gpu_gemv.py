@@ -188,6 +188,55 @@ def test_swiglu_gemv_exact_special_cases_bit_exact(M, K, N):
 
 
 # ---------------------------------------------------------------------------
+# the column kernel at every columns-per-wave variant (forced workgroup shapes)
+# ---------------------------------------------------------------------------
+def _column_plan_accepts(M, K, waves, cols):
+    """The column planner's conditions for taking a forced (waves, cols) shape: at most
+    the variant's columns per wave for this chunk count and row count, and staging waves
+    (those the dot waves leave of 16) for every (row, 512-wide block) task."""
+    nch = K // 32
+    ni = -(-nch // 64)
+    mr = 1 if M <= 1 else 2 if M <= 2 else 4
+    if mr >= 4:
+        cmax = 4 if ni <= 1 else 2 if ni <= 3 else 1
+    else:
+        cmax = 8 if ni <= 1 else 4 if ni <= 3 else 3 if ni <= 4 else 2 if ni <= 6 else 1
+    ntask = mr * -(-K // 512)
+    stagers = min(min(8, max(2, ntask)), 16 - waves)
+    return -(-cols // waves) <= cmax and stagers * 8 >= ntask and stagers >= 1
+
+
+# (M, K, dot waves, columns per workgroup): columns per wave 1, 2, 3, 4, 5 -> 6, 6, 7 -> 8
+# and 8, at one to four rows, so the outputs per wave (rows x columns) run over 1..16 and
+# fill the last group of four partly and wholly; N leaves a ragged last workgroup.
+FORCED = [(1, 1024, 8, 8), (1, 9216, 8, 16), (1, 8192, 8, 24), (1, 1024, 10, 36), (1, 1024, 8, 40),
+          (1, 1024, 8, 48), (1, 1024, 8, 56), (1, 1024, 8, 64), (2, 1024, 8, 64), (2, 6144, 8, 32),
+          (3, 1024, 8, 32), (4, 1024, 8, 24), (4, 4096, 8, 16), (2, 9216, 8, 8)]
+
+
+@pytest.mark.parametrize("M,K,waves,cols", FORCED)
+@pytest.mark.parametrize("pro", ["swiglu", "identity"])
+def test_column_kernel_forced_tilings(M, K, waves, cols, pro):
+    assert _column_plan_accepts(M, K, waves, cols)
+    N = -(-(3 * cols + 12) // 8) * 8
+    say(f"[gemv forced tiling] {pro} M={M} K={K} N={N} waves={waves} cols={cols}")
+    inp = synth.swiglu_gemv_inputs(M, K, N, seed=M * 7 + cols, out_scale=0.75, with_residual=True)
+    F.set_gemv_tiling(waves, cols)
+    try:
+        if pro == "swiglu":
+            y = run_gemv(inp, inp.out_scale)
+            ref = O.swiglu_w4_gemv(inp.g, inp.u, inp.W.qweight, inp.W.scales, inp.out_scale, inp.residual)
+        else:
+            y = F.to_bits(F.w4_gemv(F.from_bits(inp.g), F.W4Weight.from_numpy(inp.W.qweight, inp.W.scales),
+                                    F.scalar(inp.out_scale)))
+            torch.cuda.synchronize()
+            ref = O.w4_gemv(inp.g, inp.W.qweight, inp.W.scales, inp.out_scale)
+    finally:
+        F.set_gemv_tiling(0, 0)
+    assert_close(y, ref, f"forced tiling {pro} M={M} K={K} waves={waves} cols={cols}")
+
+
+# ---------------------------------------------------------------------------
 # the identity-prologue GEMV (gate_up)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("M,K,N", [(1, 1536, 17920), (16, 4096, 28672), (3, 640, 392), (64, 1024, 2056),
