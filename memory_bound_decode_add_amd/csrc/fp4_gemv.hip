@@ -204,25 +204,23 @@ __global__ __launch_bounds__(kFp4MaxWaves * kWave) void fp4_gemv_kernel(Fp4Args 
         }
     }
 
-    // ---- per column: the 32 lanes of each half, then the waves ----
+    // ---- per column: the row swap folds the two rows of each half for two columns at
+    // once (rows then hold column j0 and j1 of half 0, j0 and j1 of half 1), four DPP steps
+    // sum each row, and each row's first lane writes its column's wave sum ----
+    const int orow = lane >> 4;
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            float t = part[m][j];
+        for (int p = 0; p < (CH + 1) / 2; ++p) {
+            const int j0 = 2 * p, j1 = min(2 * p + 1, CH - 1);
+            const f32x2_t z = swap16(part[m][j0], part[m][j1]);
+            float t = z[0] + z[1];
             t += dpp<kQuadSwap1>(t);
             t += dpp<kQuadSwap2>(t);
             t += dpp<kRowRor4>(t);
-            t += dpp<kRowRor8>(t);             // every lane holds its row-of-16 sum
-            const int b = __builtin_bit_cast(int, t);
-            const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
-                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-            const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
-                             __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-            if (lane == 0) {
-                red[wave][m][j] = s0;
-                red[wave][m][CH + j] = s1;
-            }
+            t += dpp<kRowRor8>(t);
+            if ((lane & 15) == 0 && 2 * p + (orow & 1) < CH)
+                red[wave][m][(orow >> 1) * CH + ((orow & 1) ? j1 : j0)] = t;
         }
     __syncthreads();
     if (wave == 0 && lane < MR * 2 * CH) {
