@@ -425,9 +425,9 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
     // The wave's outputs n = m * OPW + o: row m, unit o (a column, or with PAIR a pair).
     // kRowSums (two or more plain outputs): they are summed four to a register, output n of
     // group g ends in row r of it, n = 4 g + {0, 2, 1, 3}[r], and lane 16 r stores it.
-    // Otherwise each output is summed on its own and lane n stores it.  (Four to a register
-    // measured faster there; with one output, and for the SwiGLU pairs, the per-output sums
-    // measured as fast or faster.)
+    // Otherwise lane n stores output n, its sums read as scalars.  (The per-row stores
+    // measured faster for plain outputs; for the SwiGLU pairs, where one lane needs both
+    // sums of a pair, the scalar reads did.)
     constexpr int OPW = PAIR ? CPW / 2 : CPW;
     constexpr int NO = MR * OPW;
     constexpr bool kRowSums = !PAIR && NO >= 2;
@@ -542,26 +542,39 @@ __global__ __launch_bounds__(16 * kWave) void w4_gemv_col_kernel(ColArgs a) {
         if (o_ok[g]) a.y[size_t(o_m[g]) * ldy + o_n[g]] = f32_to_bf16(fmaf(v, os, res));
     }
     } else {
-    // ---- reduce each column over the wave; the owning lane applies the epilogue ----
+    // ---- reduce each column over the wave, read the totals as scalars; the owning lane
+    // applies the epilogue.  Two or more slots (the SwiGLU pairs): four slots to a
+    // register, then one lane read per slot (C5-shaped layer 11.03 -> 10.76 us, same-run
+    // A/B); one slot: DPP within the rows, then the four row sums ----
     float tot[MR][CPW];
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) {
+    for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            tot[m][j] = 0.f;
-            if (!slot_ok(j)) continue;             // uniform
-            float v = acc[m][j];
-            v += dpp<kQuadSwap1>(v);
-            v += dpp<kQuadSwap2>(v);
-            v += dpp<kRowRor4>(v);
-            v += dpp<kRowRor8>(v);                 // every lane holds its row-of-16 sum
-            const int b = __builtin_bit_cast(int, v);
-            tot[m][j] = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
-                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
-                        (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
-                         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+        for (int j0 = 0; j0 < CPW; j0 += 4) {
+#pragma unroll
+            for (int j = j0; j < j0 + 4 && j < CPW; ++j) tot[m][j] = 0.f;
+            if (!slot_ok(j0)) continue;            // uniform
+            if (CPW >= 2) {
+                const float t = wave_sum4_rows(acc[m][j0], acc[m][min(j0 + 1, CPW - 1)],
+                                               acc[m][min(j0 + 2, CPW - 1)], acc[m][min(j0 + 3, CPW - 1)]);
+                const int b = __builtin_bit_cast(int, t);    // rows: slots j0, j0 + 2, j0 + 1, j0 + 3
+                tot[m][j0] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+                if (j0 + 1 < CPW) tot[m][j0 + 1] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+                if (j0 + 2 < CPW) tot[m][j0 + 2] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+                if (j0 + 3 < CPW) tot[m][j0 + 3] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+            } else {
+                float v = acc[m][j0];
+                v += dpp<kQuadSwap1>(v);
+                v += dpp<kQuadSwap2>(v);
+                v += dpp<kRowRor4>(v);
+                v += dpp<kRowRor8>(v);             // every lane holds its row-of-16 sum
+                const int b = __builtin_bit_cast(int, v);
+                tot[m][j0] = (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+                              __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+                             (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+                              __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+            }
         }
-    }
     float mine = 0.f;
 #pragma unroll
     for (int m = 0; m < MR; ++m)
