@@ -37,9 +37,11 @@
 // Decode and offsets as in the other int4 kernels: decode_int4x8_biased gives fp16
 // 1032 + q (even positions) and 1152 + 16 q (odd), the activation is stored with odd
 // positions divided by 16 in the pair order (j0, j4, j1, j5, j2, j6, j3, j7), and the
-// offsets are removed inside the matrix core by starting each group's accumulation from a
-// constant -1032 / -1152 matrix times the group's B operands (four MFMAs per wave and
-// group, shared by all T tiles).  The activation is block-scaled fp16: per (row, group) a
+// offsets are removed by starting each group's accumulation from what a constant
+// -1032 / -1152 matrix times the group's B operands gives: per row, the offsets summed
+// against the row's staged values (16 dot2 per lane and two lane swaps per wave and group,
+// shared by all T tiles; four MFMAs of that matrix measured 0.27 us slower at 8 and 16
+// rows, K = 9216, N = 2560).  The activation is block-scaled fp16: per (row, group) a
 // power of two puts the group's largest magnitude in [2^14, 2^15), folded back in with
 // the group scale; fp32 -> fp16 rounds toward zero.
 #include "device_common.h"
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(kKWaves * kWave) void w4_gemv_kmfma_kernel(KArgs a)
 
     // ---- the B operands: block-scaled fp16 in pair order, odd positions / 16 ----
     f16x8_t bop[GW][4];
-    float esc[GW];
+    float esc[GW], off[GW];
 #pragma unroll
     for (int gi = 0; gi < GW; ++gi) {
         float v[4][8];
@@ -162,20 +164,34 @@ __global__ __launch_bounds__(kKWaves * kWave) void w4_gemv_kmfma_kernel(KArgs a)
                                     __builtin_bit_cast(uint32_t, pk_f16_rtz(v[j][1] * down16, v[j][5] * down16)),
                                     __builtin_bit_cast(uint32_t, pk_f16_rtz(v[j][2] * down, v[j][6] * down)),
                                     __builtin_bit_cast(uint32_t, pk_f16_rtz(v[j][3] * down16, v[j][7] * down16))));
+        // The decode's offsets: -1032 at the even pair slots and -1152 at the odd ones,
+        // summed against the group's 128 staged values of row lm (what the constant offset
+        // matrix times these B operands gives in every column).  The row's four lanes
+        // (lm + 16 ls) meet through the half-wave and row swaps.
+        const half2_t ne = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+        const half2_t no = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+        float ob = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 h = __builtin_bit_cast(uint4, bop[gi][j]);
+            ob = dot2(__builtin_bit_cast(half2_t, h.x), ne, ob);
+            ob = dot2(__builtin_bit_cast(half2_t, h.z), ne, ob);
+            ob = dot2(__builtin_bit_cast(half2_t, h.y), no, ob);
+            ob = dot2(__builtin_bit_cast(half2_t, h.w), no, ob);
+        }
+        const f32x2_t oh = swap32(ob, ob);
+        const f32x2_t orw = swap16(oh[0] + oh[1], oh[0] + oh[1]);
+        off[gi] = orw[0] + orw[1];
     }
 
     // ---- main loop over the wave's groups, the next group's loads in flight ----
-    const uint32_t o_even = 0xE408E408u, o_odd = 0xE480E480u;    // -1032, -1152 in each half
-    const f16x8_t negoff = __builtin_bit_cast(f16x8_t, make_uint4(o_even, o_odd, o_even, o_odd));
     f32x4_t out[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) out[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int gi = 0; gi < GW; ++gi) {
         const int buf = gi & 1;
-        f32x4_t bias = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bias = __builtin_amdgcn_mfma_f32_16x16x32_f16(negoff, bop[gi][j], bias, 0, 0, 0);
+        const f32x4_t bias = f32x4_t{off[gi], off[gi], off[gi], off[gi]};
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             const uint32_t wd[4] = {wv[buf][t].x, wv[buf][t].y, wv[buf][t].z, wv[buf][t].w};
