@@ -288,8 +288,7 @@ def bench_extras(torch, F, synth, n_sets_gemv):
         t = bench_repeat(torch, timer, fns, 5) / len(gsets)
         b = T.swiglu_w4_gemv_bytes(Mb, K, N)
         sweep[f"M{Mb}"] = {"us_per_call": t * 1e6, "gbps": b / t / 1e9, "frac_of_peak": b / t / 1e9 / PEAK_GBPS,
-                           "kernel": "column" if Mb <= 4 else "matrix-core, waves split K" if Mb <= 16 else
-                           f"matrix-core, {(Mb + 15) // 16} row blocks"}
+                           "kernel": F.gemv_kernel(Mb, K, N)}
         del gb, ub, ys, wsb
     out["batch_sweep_swiglu_w4_gemv_9216x2560"] = sweep
     del gsets

@@ -52,6 +52,12 @@ FDEC_API void fdec_set_kmfma_waves(int32_t waves);
  * is): fdec_test_gemv_workspace_bytes for fdec_swiglu_w4_gemv / fdec_w4_gemv,
  * fdec_test_mlp_workspace_bytes for fdec_mlp_decode / _chain / _graph_create / _update. */
 FDEC_API size_t fdec_test_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N);
+/* fdec_test_gemv_kernel(M, K, N, swiglu): the kernel fdec_swiglu_w4_gemv (swiglu != 0) or
+ *   fdec_w4_gemv (swiglu == 0) launches for this shape under the current switches:
+ *   0 column-owning (VALU), 1 split-K (VALU, with the finish kernel), 2 matrix-core row
+ *   blocks, 3 matrix-core with the waves splitting K, 4 matrix-core fed by direct-to-LDS
+ *   loads; -1 for a shape the entry points reject.  Host-side planning only: no GPU. */
+FDEC_API int32_t fdec_test_gemv_kernel(int32_t M, int32_t K, int32_t N, int32_t swiglu);
 FDEC_API size_t fdec_test_mlp_workspace_bytes(int32_t M, int32_t H, int32_t I);
 
 /*

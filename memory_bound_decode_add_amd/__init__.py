@@ -126,6 +126,7 @@ _SIGS = {
     "fdec_set_mfma_plan": (None, [_i32, _i32, _i32]),
     "fdec_set_kmfma_waves": (None, [_i32]),
     "fdec_test_gemv_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "fdec_test_gemv_kernel": (_i32, [_i32, _i32, _i32, _i32]),
     "fdec_test_mlp_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "fdec_test_empty_kernel": (ctypes.c_int, [_i32, _i32, _c_p]),
     "fdec_test_read_ceiling": (ctypes.c_int, [_c_p, _sz, _i32, _c_p, _c_p, _sz, _c_p, _sz, _i32, _i32, _i32, _i32,
@@ -274,6 +275,18 @@ def scalar(v: float, device="cuda") -> torch.Tensor:
 # ----------------------------------------------------------------------------
 # workspaces
 # ----------------------------------------------------------------------------
+GEMV_KERNELS = {0: "column", 1: "split-K", 2: "matrix-core, row blocks", 3: "matrix-core, waves split K",
+                4: "matrix-core, direct-to-LDS ring"}
+
+
+def gemv_kernel(M, K, N, swiglu=True) -> str:
+    """The kernel the GEMV entry point launches for this shape (host-side plan)."""
+    k = int(lib().fdec_test_gemv_kernel(int(M), int(K), int(N), 1 if swiglu else 0))
+    if k < 0:
+        raise FdecError(f"gemv shape M={M} K={K} N={N} rejected")
+    return GEMV_KERNELS[k]
+
+
 def gemv_workspace_bytes(M, K, N) -> int:
     """Workspace of fdec_swiglu_w4_gemv / fdec_w4_gemv.  While a test override set through
     this module (set_gemv_split, set_gemv_tiling) is active, the size under it."""

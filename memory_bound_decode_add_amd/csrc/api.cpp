@@ -582,6 +582,11 @@ FDEC_API size_t fdec_test_gemv_workspace_bytes(int32_t M, int32_t K, int32_t N) 
     return std::max(plan_gemv(M, K, N, ov, kSwiGLU).partial_bytes, plan_gemv(M, K, N, ov, kIdentity).partial_bytes);
 }
 
+FDEC_API int32_t fdec_test_gemv_kernel(int32_t M, int32_t K, int32_t N, int32_t swiglu) {
+    if (!w4_gemv_shape_ok(M, K, N)) return -1;
+    return int32_t(plan_gemv(M, K, N, current_overrides(), swiglu ? kSwiGLU : kIdentity).kind);
+}
+
 FDEC_API size_t fdec_test_mlp_workspace_bytes(int32_t M, int32_t H, int32_t I) {
     if (M < 1 || M > 16 || H <= 0 || H % 128 || I <= 0 || I % 128) return 0;
     return plan_layer(M, H, I, current_overrides()).ws;

@@ -284,6 +284,34 @@ def test_gemv_split_override_changes_only_the_test_queries(L):
     assert L.fdec_test_gemv_workspace_bytes(1, 9216, 2560) == base
 
 
+def test_planned_kernel_per_shape(L):
+    """The planner's choice (host code, no GPU): one row and the short-K 1536 x 17920 on the
+    column kernel; three and four rows at K = 9216 exceed the column kernel's staging slots
+    (4 rows x 18 blocks > 64 tasks) and run split-K; 5..16 rows with the SwiGLU prologue and
+    at most about 12 MB of weights on the matrix cores with the waves splitting K; more
+    than 12 MB on the ring; more than 16 rows on row blocks; rejected shapes -1."""
+    k = L.fdec_test_gemv_kernel
+    assert k(1, 9216, 2560, 1) == 0
+    assert k(2, 9216, 2560, 1) == 0
+    assert k(1, 1536, 17920, 0) == 0
+    assert k(3, 9216, 2560, 1) == 1
+    assert k(4, 9216, 2560, 1) == 1
+    assert k(4, 4096, 2560, 1) == 0
+    assert k(8, 9216, 2560, 1) == 3
+    assert k(16, 9216, 2560, 1) == 3
+    assert k(16, 14336, 4096, 1) == 4
+    assert k(32, 9216, 2560, 1) == 2
+    assert k(64, 9216, 2560, 1) == 2
+    assert k(1, 9216, 2555, 1) == -1          # N % 8
+    assert k(1, 9200, 2560, 1) == -1          # K % 128
+    try:
+        L.fdec_set_gemv_split(18)
+        assert k(1, 9216, 2560, 1) == 1       # a forced split leaves the column kernel
+    finally:
+        L.fdec_set_gemv_split(0)
+    assert k(1, 9216, 2560, 1) == 0
+
+
 def test_forced_split_needs_the_larger_workspace(L, fake, inject):
     # planned once at entry: a call under an override is checked against that plan's workspace
     W = CW4(fake(1 << 24), fake(1 << 20), 9216, 2560)
