@@ -395,11 +395,11 @@ FDEC_API int fdec_swiglu_w4_gemm(const fdec_bf16* g, const fdec_bf16* u, int64_t
  *
  * fdec_swiglu_fp4_gemv: y[m, n] = bf16(s * sum_k silu(g[m,k]) u[m,k] w[k,n] (+ residual)),
  *   w = e2m1 * e4m3 block scale; arguments, aliasing and errors as fdec_swiglu_w4_gemv.
- *   Implemented for M <= 4 with K <= 16384 (a chunk-owning VALU kernel, no workspace),
- *   and for 5 <= M <= 64 with K % 128 == 0 (the matrix-core kernel, past 16 rows with
- *   two or four 16-row blocks per weight load; its K slices use a workspace of
- *   fdec_fp4_gemv_workspace_bytes(M, K, N) bytes, 0 when not needed);
- *   FDEC_ERR_UNSUPPORTED otherwise, FDEC_ERR_SHAPE outside [1, 64].
+ *   Implemented for 3 <= M <= 64 with K % 128 == 0 (the matrix-core kernel, past 16
+ *   rows with two or four 16-row blocks per weight load; its K slices use a workspace
+ *   of fdec_fp4_gemv_workspace_bytes(M, K, N) bytes, 0 when not needed), and otherwise
+ *   for M <= 4 with K <= 16384 (a chunk-owning VALU kernel, no workspace; always at
+ *   M <= 2); FDEC_ERR_UNSUPPORTED otherwise, FDEC_ERR_SHAPE outside [1, 64].
  * fdec_fp4_gemv: the identity prologue, y = bf16(s * x @ w (+ residual)); x [M][K].
  * fdec_fp4_dequant: test hook; writes w as fp32 [K][N] (exact).
  */

@@ -176,7 +176,7 @@ int check_fp4_gemv(const fdec_bf16* g, const fdec_bf16* u, int64_t ldgu, const f
         return fail(FDEC_ERR_ALIAS, "y may only alias residual exactly");
     if (!fp4_gemv_supported(M, W->K, W->N))
         return fail(FDEC_ERR_UNSUPPORTED,
-                    "the FP4 GEMV takes M <= 4 with K <= 16384, or M <= 64 with K %% 128 == 0 (M = %d, K = %d)", M,
+                    "the FP4 GEMV takes M <= 4 with K <= 16384, or 3 <= M <= 64 with K %% 128 == 0 (M = %d, K = %d)", M,
                     W->K);
     const size_t need = fp4_gemv_workspace_bytes(M, W->K, W->N);
     if (ws_bytes < need) return fail(FDEC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);

@@ -70,7 +70,7 @@ Overrides current_overrides();
 // kAddRmsNorm: the activation is rmsnorm(x + r) * w over the whole row (the fused
 // layer's gate_up), and the epilogue writes silu(gate) * up of column pairs (i, I + i).
 enum Prologue { kIdentity = 0, kSwiGLU = 1, kAddRmsNorm = 2 };
-bool plan_mfma(int M, int K, int N, GemvPlan& p);   // 5 <= M <= 64
+bool plan_mfma(int M, int K, int N, GemvPlan& p, int min_rows = 5);   // min_rows <= M <= 64
 // The gate_up projection [K, 2I] with the SwiGLU epilogue: act[m][i] = bf16(silu(g) u)
 // from the unrounded sums of columns i and I + i (matrix-core kernel, 1 <= M <= 64).
 bool plan_mfma_pair(int M, int K, int I, GemvPlan& p);

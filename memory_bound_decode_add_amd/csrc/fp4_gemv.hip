@@ -340,31 +340,35 @@ hipError_t launch_fp4_1(Prologue pro, const Fp4Args& a, const Fp4Plan& p, hipStr
 
 }  // namespace
 
-// 1..4 rows: the chunk-owning kernel above.  5..64 rows: the matrix-core kernel with
-// the FP4 weight format (K % 128 == 0; two or four 16-row blocks past 16 rows), whose K
-// slices need a workspace.
+// One or two rows: the chunk-owning kernel above; also three or four where K % 128 != 0.
+// Otherwise the matrix-core kernel with the FP4 weight format (K % 128 == 0; two or four
+// 16-row blocks past 16 rows), whose K slices need a workspace.  At three and four rows
+// the chunk-owning kernel holds two columns per lane half (its registers), so some 640
+// workgroups each recompute the whole activation's SiLU.
+bool fp4_on_lanes(int M, int K) { return M <= 2 || (M <= 4 && K % 128 != 0); }
+
 bool fp4_gemv_supported(int M, int K, int N) {
     Fp4Plan p;
-    if (M <= 4) return fp4_plan(M, K, N, p);
+    if (fp4_on_lanes(M, K)) return fp4_plan(M, K, N, p);
     GemvPlan g{};
-    return M <= kMfmaMaxRows && K > 0 && K % 128 == 0 && N > 0 && N % 8 == 0 && plan_mfma(M, K, N, g);
+    return M <= kMfmaMaxRows && K > 0 && K % 128 == 0 && N > 0 && N % 8 == 0 && plan_mfma(M, K, N, g, 3);
 }
 
 size_t fp4_gemv_workspace_bytes(int M, int K, int N) {
-    if (M <= 4 || !fp4_gemv_supported(M, K, N)) return 0;
+    if (fp4_on_lanes(M, K) || !fp4_gemv_supported(M, K, N)) return 0;
     GemvPlan g{};
     g.groups = K / kGroup;
-    plan_mfma(M, K, N, g);
+    plan_mfma(M, K, N, g, 3);
     return g.partial_bytes;
 }
 
 hipError_t launch_fp4_gemv(Prologue pro, const uint16_t* a0, const uint16_t* a1, int64_t lda, const uint32_t* qw,
                            const uint8_t* sc, int M, int K, int N, const float* out_scale, const uint16_t* residual,
                            uint16_t* y, void* ws, const float* gscale, hipStream_t s) {
-    if (M > 4) {
+    if (!fp4_on_lanes(M, K)) {
         GemvPlan g{};
         g.groups = K / kGroup;
-        if (!fp4_gemv_supported(M, K, N) || !plan_mfma(M, K, N, g)) return hipErrorInvalidValue;
+        if (!fp4_gemv_supported(M, K, N) || !plan_mfma(M, K, N, g, 3)) return hipErrorInvalidValue;
         return launch_mfma_fp4(pro, a0, a1, lda, qw, sc, M, K, N, out_scale, residual, y, ws, g, gscale, s);
     }
     Fp4Plan p;

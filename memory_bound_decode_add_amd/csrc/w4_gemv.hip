@@ -1065,8 +1065,8 @@ int mfma_splits(int groups, int tiles, int max_slice = kMfmaMaxSliceGroups) {
     return (groups + gps - 1) / gps;
 }
 
-bool plan_mfma(int M, int K, int N, GemvPlan& p) {
-    if (M <= 4 || M > kMfmaMaxRows) return false;
+bool plan_mfma(int M, int K, int N, GemvPlan& p, int min_rows) {
+    if (M < std::max(min_rows, 1) || M > kMfmaMaxRows) return false;
     const int rb = M <= 16 ? 1 : M <= 32 ? 2 : 4;     // row blocks of 16
     const int max_slice = kMfmaMaxSliceGroups / rb;   // LDS holds 16 rb rows of the slice
     p.kind = kMfma;
