@@ -1166,8 +1166,9 @@ GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov, Prologue pro) {
     }
     p = GemvPlan{};
     // the kernel whose waves split K: one group per wave, SwiGLU prologue, up to about
-    // 12 MB of weights (measured faster there, slower elsewhere), or when forced
-    const bool kmfma = ov.mfma_kernel == 2 || (ov.mfma_kernel == 0 && pro == kSwiGLU && M > 4 &&
+    // 12 MB of weights (measured faster there, slower elsewhere), or when forced; also 3..4
+    // rows the column kernel cannot stage (K = 9216: 11.9 -> 11.65 us against split-K)
+    const bool kmfma = ov.mfma_kernel == 2 || (ov.mfma_kernel == 0 && pro == kSwiGLU && M > 2 &&
                                                 int64_t(K) * N / 2 <= (int64_t(12) << 20));
     Overrides ovk = ov;
     if (ov.mfma_kernel == 0) ovk.mfma_gw = 1;

@@ -287,15 +287,17 @@ def test_gemv_split_override_changes_only_the_test_queries(L):
 def test_planned_kernel_per_shape(L):
     """The planner's choice (host code, no GPU): one row and the short-K 1536 x 17920 on the
     column kernel; three and four rows at K = 9216 exceed the column kernel's staging slots
-    (4 rows x 18 blocks > 64 tasks) and run split-K; 5..16 rows with the SwiGLU prologue and
-    at most about 12 MB of weights on the matrix cores with the waves splitting K; more
-    than 12 MB on the ring; more than 16 rows on row blocks; rejected shapes -1."""
+    (4 rows x 18 blocks > 64 tasks) and, with the SwiGLU prologue, run on the matrix cores
+    with the waves splitting K, as 5..16 rows with at most about 12 MB of weights do (the
+    identity prologue there: split-K); more than 12 MB on the ring; more than 16 rows on
+    row blocks; rejected shapes -1."""
     k = L.fdec_test_gemv_kernel
     assert k(1, 9216, 2560, 1) == 0
     assert k(2, 9216, 2560, 1) == 0
     assert k(1, 1536, 17920, 0) == 0
-    assert k(3, 9216, 2560, 1) == 1
-    assert k(4, 9216, 2560, 1) == 1
+    assert k(3, 9216, 2560, 1) == 3
+    assert k(4, 9216, 2560, 1) == 3
+    assert k(4, 9216, 2560, 0) == 1
     assert k(4, 4096, 2560, 1) == 0
     assert k(8, 9216, 2560, 1) == 3
     assert k(16, 9216, 2560, 1) == 3
