@@ -1159,19 +1159,24 @@ GemvPlan plan_gemv(int M, int K, int N, const Overrides& ov, Prologue pro) {
     p = GemvPlan{};
     // the ring kernel: forced, or built in where it measured faster -- the SwiGLU prologue
     // above about 12 MB of weights (16 x 14336 x 4096: 15.5 against 16.4 us; 16 x 4096 x 11008:
-    // 15.7 against 23.9), the identity prologue by ring_preferred
+    // 15.7 against 23.9), the identity prologue by ring_preferred where the kernel whose
+    // waves split K is not taken (short K or above about 12 MB: 16 x 1536 x 17920 9.8
+    // against 18.3 us, 16 x 14336 x 4096 14.9 against 18.0)
+    const bool small = int64_t(K) * N / 2 <= (int64_t(12) << 20);
+    const bool kmfma_ident = pro == kIdentity && M > 4 && K >= 4096 && small;
     if (ov.split == 0 && (ov.mfma_kernel == 3 || (ov.mfma_kernel == 0 && M > 4)) && plan_ring(M, K, N, pro, p)) {
-        const bool big = int64_t(K) * N / 2 > (int64_t(12) << 20);
-        if (ov.mfma_kernel == 3 || (pro == kSwiGLU && big) || (pro == kIdentity && ring_preferred(p))) return p;
+        if (ov.mfma_kernel == 3 || (pro == kSwiGLU && !small) || (pro == kIdentity && !kmfma_ident && ring_preferred(p)))
+            return p;
     }
     p = GemvPlan{};
-    // the kernel whose waves split K: one group per wave, SwiGLU prologue, up to about
-    // 12 MB of weights (measured faster there, slower elsewhere), or when forced; also 3..4
-    // rows the column kernel cannot stage (K = 9216: 11.9 -> 11.65 us against split-K)
-    const bool kmfma = ov.mfma_kernel == 2 || (ov.mfma_kernel == 0 && pro == kSwiGLU && M > 2 &&
-                                                int64_t(K) * N / 2 <= (int64_t(12) << 20));
+    // the kernel whose waves split K: the SwiGLU prologue up to about 12 MB of weights, one
+    // group per wave (measured faster there, slower elsewhere), also 3..4 rows the column
+    // kernel cannot stage (K = 9216: 11.9 -> 11.65 us against split-K); the identity
+    // prologue at K >= 4096 up to about 12 MB, groups per wave by its cost (16 x 8960 x 1536:
+    // 8.61 -> 7.25 us, 16 x 4096 x 4096: 8.46 -> 7.55 us against the ring); or when forced
+    const bool kmfma = ov.mfma_kernel == 2 || (ov.mfma_kernel == 0 && ((pro == kSwiGLU && M > 2 && small) || kmfma_ident));
     Overrides ovk = ov;
-    if (ov.mfma_kernel == 0) ovk.mfma_gw = 1;
+    if (ov.mfma_kernel == 0) ovk.mfma_gw = pro == kSwiGLU ? 1 : 0;
     if (ov.split == 0 && kmfma && plan_kmfma(M, K, N, pro == kSwiGLU ? 2 : 4, p, ovk)) return p;
     p = GemvPlan{};
     if (ov.split == 0 && plan_mfma(M, K, N, p)) return p;

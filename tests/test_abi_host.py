@@ -289,8 +289,9 @@ def test_planned_kernel_per_shape(L):
     column kernel; three and four rows at K = 9216 exceed the column kernel's staging slots
     (4 rows x 18 blocks > 64 tasks) and, with the SwiGLU prologue, run on the matrix cores
     with the waves splitting K, as 5..16 rows with at most about 12 MB of weights do (the
-    identity prologue there: split-K); more than 12 MB on the ring; more than 16 rows on
-    row blocks; rejected shapes -1."""
+    identity prologue there: split-K; at 5..16 rows with K >= 4096 the waves-split-K
+    kernel too); more than 12 MB, or identity at short K, on the ring; more than 16 rows
+    on row blocks; rejected shapes -1."""
     k = L.fdec_test_gemv_kernel
     assert k(1, 9216, 2560, 1) == 0
     assert k(2, 9216, 2560, 1) == 0
@@ -302,6 +303,10 @@ def test_planned_kernel_per_shape(L):
     assert k(8, 9216, 2560, 1) == 3
     assert k(16, 9216, 2560, 1) == 3
     assert k(16, 14336, 4096, 1) == 4
+    assert k(16, 8960, 1536, 0) == 3          # identity, K >= 4096, <= 12 MB
+    assert k(8, 4096, 4096, 0) == 3
+    assert k(16, 1536, 17920, 0) == 4         # identity at short K: the ring
+    assert k(16, 14336, 4096, 0) == 4         # identity above 12 MB: the ring
     assert k(32, 9216, 2560, 1) == 2
     assert k(64, 9216, 2560, 1) == 2
     assert k(1, 9216, 2555, 1) == -1          # N % 8
